@@ -1,0 +1,198 @@
+"""Seeded synthetic inputs for the W4A8 linear layer (numpy only).
+
+This module is shared by the tests, the benchmark and the smoke check.  It draws random
+numbers and lays them out in the canonical input format; it contains none of the layer's own
+arithmetic (no rotation, no activation quantization, no integer dot products, no rescale).
+The weight codes it produces stand in for a quantized checkpoint: the offline weight quantizer
+below (symmetric ``s = f16(max|w|/7)``, affine ``s = f16((max-min)/15), b = f16(min)``) only
+turns Gaussian draws into plausible codes and scales.
+
+Canonical formats (consumed by both the HIP library and the oracle):
+  x          float32 [m, k]                   activations, row-major
+  codes      uint8   [n, k/2]                 two 4-bit codes per byte, low nibble = even k
+             sym:      two's-complement q in [-8, 7]
+             affine:   unsigned u in [0, 15]
+             codebook: index j in [0, 15] into the row's 16-entry int8 codebook
+  scales     float16 [n, k/group]
+  bias       float16 [n, k/group]            affine only
+  codebook   int8    [n, 16]                 codebook only
+
+Shapes and distributions follow the workloads the pages measure: Gemma-style decode GEMVs
+(K=2048, gate_up N=16384, o_proj N=2048), a 128-row prefill chunk of a 5120-wide model's fused
+gate|up (N=34816) with 4-bit affine group-64 weights, a 128-block rotated codebook layer
+(K=1536, N=6144), and a K=1536 x 262144 vocabulary head.  Seeds: every array has its own
+stream, ``PCG64(SeedSequence([2026, cfg, variant, stream]))`` with streams 0 = X, 1 = outlier
+channels, 2 = W, 3 = codebook entries, 4 = codebook indices, 5 = codebook scales.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+import numpy as np
+
+FMT_SYM, FMT_AFFINE, FMT_CODEBOOK = 0, 1, 2
+FORMAT_NAMES = {FMT_SYM: "sym", FMT_AFFINE: "affine", FMT_CODEBOOK: "codebook"}
+
+_W_CHUNK_ROWS = 8192  # W is drawn in fixed row chunks so large heads stay within memory
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    m: int
+    k: int
+    n: int
+    group: int
+    fmt: int
+    hadamard: int            # 0 or the rotation block width
+    x_outliers: int          # number of outlier input channels
+    x_outlier_scale: float
+    w_sigma: float
+    cfg_id: int              # seed component for X
+    x_variant: int
+    w_variant: int           # configs that share W share this and cfg_id
+    note: str = ""
+    extra: dict = field(default_factory=dict)
+
+
+CONFIGS = {
+    "C1": LayerConfig("C1", 1, 1024, 1024, 64, FMT_SYM, 0, 0, 1.0, 0.02, 1, 0, 0,
+                      "tiny decode GEMV"),
+    "C2a": LayerConfig("C2a", 1, 2048, 16384, 64, FMT_SYM, 0, 8, 20.0, 0.02, 2, 0, 0,
+                       "decode GEMV, gate_up-shaped"),
+    "C2b": LayerConfig("C2b", 1, 2048, 2048, 64, FMT_SYM, 0, 8, 20.0, 0.02, 2, 1, 1,
+                       "decode GEMV, o_proj-shaped"),
+    "C3a": LayerConfig("C3a", 128, 5120, 34816, 64, FMT_AFFINE, 0, 0, 1.0, 0.015, 3, 0, 0,
+                       "prefill GEMM, fused gate|up, affine 4-bit"),
+    "C3b": LayerConfig("C3b", 65, 5120, 34816, 64, FMT_AFFINE, 0, 0, 1.0, 0.015, 3, 1, 0,
+                       "prefill GEMM, odd M"),
+    "C4": LayerConfig("C4", 1024, 1536, 6144, 128, FMT_CODEBOOK, 128, 0, 1.0, 0.0, 4, 0, 0,
+                      "rotated codebook GEMM"),
+    "C5a": LayerConfig("C5a", 1, 1536, 262144, 64, FMT_SYM, 0, 15, 15.0, 0.02, 5, 0, 0,
+                       "vocabulary head, decode GEMV"),
+    "C5b": LayerConfig("C5b", 64, 1536, 262144, 64, FMT_SYM, 0, 15, 15.0, 0.02, 5, 1, 0,
+                       "vocabulary head, chunked prefill"),
+}
+
+
+def rng(cfg_id: int, variant: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([2026, cfg_id, variant,
+                                                                       stream])))
+
+
+def config(name: str, **overrides) -> LayerConfig:
+    """A named config, optionally with shape overrides (m, k, n, ...) for small test cases."""
+    return replace(CONFIGS[name], **overrides)
+
+
+def pack_nibbles(c: np.ndarray) -> np.ndarray:
+    """[n, k] codes in 0..15 -> [n, k/2] bytes, low nibble = even k."""
+    c = np.asarray(c, dtype=np.uint8)
+    return (c[:, 0::2] & 0x0F) | ((c[:, 1::2] & 0x0F) << 4)
+
+
+def unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    """[n, k/2] bytes -> [n, k] codes 0..15 (inverse of pack_nibbles)."""
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty((b.shape[0], b.shape[1] * 2), np.uint8)
+    out[:, 0::2] = b & 0x0F
+    out[:, 1::2] = b >> 4
+    return out
+
+
+def make_x(cfg: LayerConfig) -> np.ndarray:
+    """float32 [m, k]: standard normal, with whole outlier columns scaled."""
+    x = rng(cfg.cfg_id, cfg.x_variant, 0).standard_normal((cfg.m, cfg.k), dtype=np.float32)
+    if cfg.x_outliers:
+        cols = rng(cfg.cfg_id, cfg.x_variant, 1).choice(cfg.k, size=cfg.x_outliers,
+                                                        replace=False)
+        x[:, np.sort(cols)] *= np.float32(cfg.x_outlier_scale)
+    return x
+
+
+def _quantize_weights_sym(w: np.ndarray, group: int):
+    n, k = w.shape
+    wg = w.reshape(n, k // group, group)
+    s16 = (np.abs(wg).max(axis=2) / np.float32(7.0)).astype(np.float16)
+    s32 = s16.astype(np.float32)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s32 > 0, np.rint(wg / np.where(s32 > 0, s32, 1)), 0)
+    q = np.clip(q, -8, 7).astype(np.int8).reshape(n, k)
+    return (q.astype(np.uint8) & 0x0F), s16, None
+
+
+def _quantize_weights_affine(w: np.ndarray, group: int):
+    n, k = w.shape
+    wg = w.reshape(n, k // group, group)
+    lo = wg.min(axis=2)
+    hi = wg.max(axis=2)
+    s16 = ((hi - lo) / np.float32(15.0)).astype(np.float16)
+    b16 = lo.astype(np.float16)
+    s32 = s16.astype(np.float32)[:, :, None]
+    b32 = b16.astype(np.float32)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = np.where(s32 > 0, np.rint((wg - b32) / np.where(s32 > 0, s32, 1)), 0)
+    u = np.clip(u, 0, 15).astype(np.uint8).reshape(n, k)
+    return u, s16, b16
+
+
+def make_weights(cfg: LayerConfig, full_range: bool = False):
+    """Canonical (codes [n,k/2] u8, scales [n,k/g] f16, bias f16|None, codebook i8|None)."""
+    n, k, g = cfg.n, cfg.k, cfg.group
+    ng = k // g
+    if cfg.fmt == FMT_CODEBOOK:
+        cb = np.clip(np.rint(40.0 * rng(cfg.cfg_id, cfg.w_variant, 3).standard_normal((n, 16))),
+                     -127, 127).astype(np.int8)
+        idx = rng(cfg.cfg_id, cfg.w_variant, 4).integers(0, 16, size=(n, k), dtype=np.uint8)
+        sc = (rng(cfg.cfg_id, cfg.w_variant, 5).uniform(0.5, 1.5, size=(n, ng))
+              * 5e-4).astype(np.float16)
+        return pack_nibbles(idx), sc, None, cb
+    r = rng(cfg.cfg_id, cfg.w_variant, 2)
+    if full_range:
+        c = r.integers(0, 16, size=(n, k), dtype=np.uint8)
+        sc = (r.uniform(0.5, 1.5, size=(n, ng)) * cfg.w_sigma / 3.0).astype(np.float16)
+        bias = None
+        if cfg.fmt == FMT_AFFINE:
+            bias = (-7.5 * sc.astype(np.float32)
+                    + r.normal(0, cfg.w_sigma / 10, size=(n, ng))).astype(np.float16)
+        return pack_nibbles(c), sc, bias, None
+    codes = np.empty((n, k // 2), np.uint8)
+    scales = np.empty((n, ng), np.float16)
+    bias = np.empty((n, ng), np.float16) if cfg.fmt == FMT_AFFINE else None
+    quant = _quantize_weights_sym if cfg.fmt == FMT_SYM else _quantize_weights_affine
+    for r0 in range(0, n, _W_CHUNK_ROWS):
+        rows = min(_W_CHUNK_ROWS, n - r0)
+        w = r.standard_normal((rows, k), dtype=np.float32) * np.float32(cfg.w_sigma)
+        c, s, b = quant(w, g)
+        codes[r0:r0 + rows] = pack_nibbles(c)
+        scales[r0:r0 + rows] = s
+        if bias is not None:
+            bias[r0:r0 + rows] = b
+    return codes, scales, bias, None
+
+
+def make(name_or_cfg, full_range: bool = False, **overrides):
+    """All inputs of one layer: dict(cfg, x, codes, scales, bias, codebook)."""
+    cfg = name_or_cfg if isinstance(name_or_cfg, LayerConfig) else config(name_or_cfg,
+                                                                          **overrides)
+    codes, scales, bias, cb = make_weights(cfg, full_range=full_range)
+    return dict(cfg=cfg, x=make_x(cfg), codes=codes, scales=scales, bias=bias, codebook=cb)
+
+
+def weight_bytes(cfg: LayerConfig) -> int:
+    """Algorithmic weight bytes: nibbles + fp16 scales (+ fp16 bias) (+ int8 codebook)."""
+    b = cfg.n * cfg.k // 2 + 2 * cfg.n * (cfg.k // cfg.group)
+    if cfg.fmt == FMT_AFFINE:
+        b += 2 * cfg.n * (cfg.k // cfg.group)
+    if cfg.fmt == FMT_CODEBOOK:
+        b += 16 * cfg.n
+    return b
+
+
+def algorithmic_bytes(cfg: LayerConfig) -> int:
+    """Bytes one linear call must move: weights + xq + xs + xsum + fp32 y."""
+    ng = cfg.k // cfg.group
+    return weight_bytes(cfg) + cfg.m * cfg.k + 8 * cfg.m * ng + 4 * cfg.m * cfg.n
+
+
+def int_ops(cfg: LayerConfig) -> int:
+    return 2 * cfg.m * cfg.n * cfg.k

@@ -1,0 +1,160 @@
+"""CPU oracle of the W4A8 linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import this package.  The product path (the HIP library and its Python binding) never imports,
+links or calls it, and the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C loops, built with ``-O2 -ffp-contract=off`` and no
+fast-math); this module only builds that file with gcc, loads it with ctypes and marshals numpy
+arrays.  See the header of ``oracle.c`` for what each step computes and which passage of the
+pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+FORMAT_SYM, FORMAT_AFFINE, FORMAT_CODEBOOK = 0, 1, 2
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so next to it (gcc, OpenMP, strict IEEE fp32)."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+           "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_half_to_double.restype = ctypes.c_double
+    lib.oracle_wht_block.argtypes = [P, ctypes.c_int]
+    lib.oracle_wht_block.restype = None
+    lib.oracle_rotate.argtypes = [P, i64, i64, i32]
+    lib.oracle_quantize.argtypes = [P, i64, i64, i32, P, P, P]
+    lib.oracle_prep.argtypes = [P, i64, i64, i32, i32, P, P, P]
+    lib.oracle_partials.argtypes = [i32, P, P, i64, i64, i32, P, i64, P]
+    lib.oracle_linear.argtypes = [i32, P, P, P, P, i64, i64, i32, P, P, P, i64, P, P]
+    for f in ("oracle_rotate", "oracle_quantize", "oracle_prep", "oracle_partials",
+              "oracle_linear", "oracle_num_threads"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc == 1:
+        raise ValueError(f"{what}: invalid arguments")
+    if rc == 2:
+        raise OverflowError(f"{what}: an integer partial does not fit int32")
+    if rc != 0:
+        raise RuntimeError(f"{what}: status {rc}")
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def half_to_double(h: int) -> float:
+    return float(_load().oracle_half_to_double(int(h)))
+
+
+def wht(x: np.ndarray, block: int = 128) -> np.ndarray:
+    """Normalized Walsh-Hadamard transform of every `block`-wide block of each row (fp32)."""
+    x = np.array(x, dtype=np.float32, order="C", copy=True)
+    if x.ndim == 1:
+        x = x[None, :]
+    m, k = x.shape
+    _check(_load().oracle_rotate(_ptr(x), m, k, block), "rotate")
+    return x
+
+
+def quantize(x: np.ndarray, group: int):
+    """Per-row per-group int8 quantization: returns (xq int8 [m,k], xs f32 [m,k/g], xsum i32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    m, k = x.shape
+    xq = np.empty((m, k), np.int8)
+    xs = np.empty((m, k // group), np.float32)
+    xsum = np.empty((m, k // group), np.int32)
+    _check(_load().oracle_quantize(_ptr(x), m, k, group, _ptr(xq), _ptr(xs), _ptr(xsum)),
+           "quantize")
+    return xq, xs, xsum
+
+
+def prep(x: np.ndarray, group: int, hadamard_block: int = 0):
+    """The activation prepass: optional rotation, then quantize.  Returns (xq, xs, xsum)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    m, k = x.shape
+    xq = np.empty((m, k), np.int8)
+    xs = np.empty((m, k // group), np.float32)
+    xsum = np.empty((m, k // group), np.int32)
+    _check(_load().oracle_prep(_ptr(x), m, k, group, hadamard_block,
+                               _ptr(xq), _ptr(xs), _ptr(xsum)), "prep")
+    return xq, xs, xsum
+
+
+def partials(fmt: int, codes: np.ndarray, xq: np.ndarray, group: int, codebook=None):
+    """Integer per-group partials D [m, n, k/group] (int32)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    if xq.ndim == 1:
+        xq = xq[None, :]
+    n = codes.shape[0]
+    m, k = xq.shape
+    assert codes.shape[1] * 2 == k
+    cb = None if codebook is None else np.ascontiguousarray(codebook, dtype=np.int8)
+    d = np.empty((m, n, k // group), np.int32)
+    _check(_load().oracle_partials(fmt, _ptr(codes), _ptr(cb), n, k, group, _ptr(xq), m,
+                                   _ptr(d)), "partials")
+    return d
+
+
+def linear(fmt: int, codes, scales_f16, xq, xs, xsum, group: int, bias_f16=None,
+           codebook=None, with_terms: bool = True):
+    """fp64 output y [m, n] (and the term magnitude T [m, n] if with_terms)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales_f16, dtype=np.float16).view(np.uint16)
+    bias = None if bias_f16 is None else \
+        np.ascontiguousarray(bias_f16, dtype=np.float16).view(np.uint16)
+    cb = None if codebook is None else np.ascontiguousarray(codebook, dtype=np.int8)
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    xs = np.ascontiguousarray(xs, dtype=np.float32)
+    xsum = np.ascontiguousarray(xsum, dtype=np.int32)
+    if xq.ndim == 1:
+        xq, xs, xsum = xq[None, :], xs[None, :], xsum[None, :]
+    n = codes.shape[0]
+    m, k = xq.shape
+    y = np.empty((m, n), np.float64)
+    t = np.empty((m, n), np.float64) if with_terms else None
+    _check(_load().oracle_linear(fmt, _ptr(codes), _ptr(scales), _ptr(bias), _ptr(cb), n, k,
+                                 group, _ptr(xq), _ptr(xs), _ptr(xsum), m, _ptr(y), _ptr(t)),
+           "linear")
+    return (y, t) if with_terms else y

@@ -1,0 +1,296 @@
+/*
+ * oracle.c -- plain, slow, obviously-correct CPU definition of the W4A8 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call this
+ * file: only the tests, the smoke check and the benchmark's CPU-baseline leg do.  It shares
+ * no code, header, table or constant with the HIP library, and includes nothing from it.
+ *
+ * What it computes (sources are the four pages this project is written from):
+ *
+ *   rotation   "cactus PR #697, SME2 acceleration for CQ4 matmul, prefill attention, and
+ *              orthogonal embeddings", section "What's in here / Quantized matmul": the fused
+ *              GEMV's first phase applies a Hadamard transform to the activations before their
+ *              int8 quantization; the 128-wide virtual groups of the orthogonal lm_head keep the
+ *              rotation aligned with quantization groups.  Reading taken here: the normalized
+ *              Sylvester-order Walsh-Hadamard transform on independent 128-wide blocks, fp32
+ *              add/sub butterflies with the span doubling 1,2,...,64, then one multiply by
+ *              fp32(1/sqrt(128)).
+ *   quantize   same section (int8 per-group activation quantization) and the review snippet of
+ *              the per-group SMOPA leaf contract (per-group int8 activations, one activation
+ *              scale per group).  Reading: per row and group, amax = max|x| (exact),
+ *              xs = amax / 127 as an IEEE fp32 divide, xq = round-half-even(x / xs) as an IEEE
+ *              fp32 divide then rint, so codes lie in [-127, 127]; amax == 0 gives xs = 0 and
+ *              xq = 0.
+ *   group sums "TensorFold PR #3215, simd_qmm on Metal: X's group sums and half operands from a
+ *              prepass", section "What this changes": the prepass writes each row's per-group
+ *              sums once, for the affine bias term.  Reading: the int32 sum of the int8 codes of
+ *              the group (the only reading under which x_hat = xs*xq makes the bias term
+ *              sum_k x_hat*bw equal xs*bw*xsum exactly).
+ *   partials   PR #697's leaf contract (review snippet): a raw int32 dot product per group and
+ *              output channel, partials[g][c] = sum over the group of act[k]*weight[c][k], with
+ *              the activation-scale and weight-scale rescale applied by the caller.
+ *   output     y[m][n] = sum over groups g of xs[m][g]*( sw[n][g]*D[m][n][g]
+ *                                                      + bw[n][g]*xsum[m][g] )
+ *              evaluated here in fp64 with g ascending; bw = 0 except for the affine format
+ *              ("TensorFold PR #3215": 4-bit affine g64 weights, scale and bias per group,
+ *              dequantized weight = scale*u + bias).
+ *
+ * Weight formats (canonical input, one byte holds two 4-bit codes, low nibble = even k):
+ *   format 0 (symmetric):  code is a two's-complement q in [-8, 7]; w_int = q
+ *   format 1 (affine):     code is an unsigned u in [0, 15];        w_int = u
+ *   format 2 (codebook):   code is an index j in [0, 15];           w_int = codebook[n][j]
+ *                          (PR #697's CQ4: 4-bit codebook indices expanded to int8 by lookup)
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared (no fast-math), so that every fp32
+ * operation is a single IEEE-rounded operation in program order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARGS 1
+#define ORACLE_OVERFLOW 2
+
+/* ---------------------------------------------------------------- fp16 decoding -------- */
+
+/* IEEE binary16 bit pattern -> double, exactly (every binary16 value is a double). */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int mant = h & 0x3ff;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)mant, -24);               /* subnormal: mant * 2^-24 */
+    } else if (expo == 31) {
+        v = mant ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(mant | 0x400), expo - 25); /* (1024 + mant) * 2^(e-15-10) */
+    }
+    return sign ? -v : v;
+}
+
+/* ---------------------------------------------------------------- rotation ------------- */
+
+/* The normalizing constant, fp32(1/sqrt(128)), computed in double and rounded once. */
+static float oracle_wht_scale(int block)
+{
+    return (float)(1.0 / sqrt((double)block));
+}
+
+/*
+ * In-place normalized Walsh-Hadamard transform of one block of `block` floats (a power of two).
+ * Butterfly on pairs (j, j+h): new x[j] = x[j] + x[j+h], new x[j+h] = x[j] - x[j+h], for
+ * h = 1, 2, 4, ..., block/2, then every element is multiplied by fp32(1/sqrt(block)).
+ */
+void oracle_wht_block(float *v, int block)
+{
+    for (int h = 1; h < block; h *= 2) {
+        for (int i = 0; i < block; i += 2 * h) {
+            for (int j = i; j < i + h; ++j) {
+                float a = v[j];
+                float b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+        }
+    }
+    float c = oracle_wht_scale(block);
+    for (int j = 0; j < block; ++j)
+        v[j] = v[j] * c;
+}
+
+/* Rotate every `block`-wide block of every row of x[m][k] in place. */
+int oracle_rotate(float *x, int64_t m, int64_t k, int32_t block)
+{
+    if (block <= 0 || (block & (block - 1)) != 0 || k % block != 0 || m < 0)
+        return ORACLE_BAD_ARGS;
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t b = 0; b < k / block; ++b)
+            oracle_wht_block(x + r * k + b * block, block);
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- quantization --------- */
+
+/*
+ * Per row r and group g of `group` consecutive k:
+ *   amax = max |x|;  xs = amax / 127 (fp32 divide);  xq = rint(x / xs) (fp32 divide, ties to even)
+ *   xsum = sum of the group's codes (int32).
+ */
+int oracle_quantize(const float *x, int64_t m, int64_t k, int32_t group,
+                    int8_t *xq, float *xs, int32_t *xsum)
+{
+    if (group <= 0 || k % group != 0 || m < 0)
+        return ORACLE_BAD_ARGS;
+    int64_t ng = k / group;
+    for (int64_t r = 0; r < m; ++r) {
+        for (int64_t g = 0; g < ng; ++g) {
+            const float *xg = x + r * k + g * group;
+            int8_t *qg = xq + r * k + g * group;
+            float amax = 0.0f;
+            for (int i = 0; i < group; ++i) {
+                float a = fabsf(xg[i]);
+                if (a > amax)
+                    amax = a;
+            }
+            float scale = amax / 127.0f;
+            int32_t sum = 0;
+            for (int i = 0; i < group; ++i) {
+                int32_t q = 0;
+                if (amax > 0.0f) {
+                    float t = xg[i] / scale;
+                    float rq = rintf(t);          /* round to nearest, ties to even */
+                    if (rq > 127.0f) rq = 127.0f;   /* unreachable: |x| <= amax          */
+                    if (rq < -127.0f) rq = -127.0f;
+                    q = (int32_t)rq;
+                }
+                qg[i] = (int8_t)q;
+                sum += q;
+            }
+            xs[r * ng + g] = scale;
+            xsum[r * ng + g] = sum;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The whole activation prepass: copy, optional rotation, quantization. */
+int oracle_prep(const float *x, int64_t m, int64_t k, int32_t group, int32_t hadamard_block,
+                int8_t *xq, float *xs, int32_t *xsum)
+{
+    if (hadamard_block != 0 && (hadamard_block <= 0 || k % hadamard_block != 0))
+        return ORACLE_BAD_ARGS;
+    float *tmp = (float *)malloc((size_t)(m * k > 0 ? m * k : 1) * sizeof(float));
+    if (!tmp)
+        return ORACLE_BAD_ARGS;
+    memcpy(tmp, x, (size_t)(m * k) * sizeof(float));
+    int rc = ORACLE_OK;
+    if (hadamard_block != 0)
+        rc = oracle_rotate(tmp, m, k, hadamard_block);
+    if (rc == ORACLE_OK)
+        rc = oracle_quantize(tmp, m, k, group, xq, xs, xsum);
+    free(tmp);
+    return rc;
+}
+
+/* ---------------------------------------------------------------- weights -------------- */
+
+/* The 4-bit code of weight (n, k) from the canonical byte array codes[n][k/2]. */
+static int oracle_code(const uint8_t *codes, int64_t k_total, int64_t n, int64_t k)
+{
+    uint8_t byte = codes[n * (k_total / 2) + k / 2];
+    return (k % 2 == 0) ? (byte & 0x0f) : (byte >> 4);
+}
+
+/* The integer weight of (n, k) for each format (see the file header). */
+static int32_t oracle_weight_int(int format, const uint8_t *codes, const int8_t *codebook,
+                                 int64_t k_total, int64_t n, int64_t k)
+{
+    int c = oracle_code(codes, k_total, n, k);
+    if (format == 0)
+        return c >= 8 ? c - 16 : c;                 /* two's-complement nibble */
+    if (format == 1)
+        return c;                                   /* unsigned code */
+    return (int32_t)codebook[n * 16 + c];           /* codebook lookup */
+}
+
+/* ---------------------------------------------------------------- partials, output ----- */
+
+/*
+ * D[r][n][g] = sum over k in group g of xq[r][k] * w_int[n][k], accumulated in int64 and
+ * checked to fit int32.  Output layout d[m][n][k/group].
+ */
+int oracle_partials(int32_t format, const uint8_t *codes, const int8_t *codebook,
+                    int64_t n, int64_t k, int32_t group, const int8_t *xq, int64_t m,
+                    int32_t *d)
+{
+    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 2)
+        return ORACLE_BAD_ARGS;
+    if (format == 2 && codebook == NULL)
+        return ORACLE_BAD_ARGS;
+    int64_t ng = k / group;
+    int overflow = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : overflow)
+    for (int64_t c = 0; c < n; ++c) {
+        int32_t *w = (int32_t *)malloc((size_t)k * sizeof(int32_t));
+        for (int64_t kk = 0; kk < k; ++kk)
+            w[kk] = oracle_weight_int(format, codes, codebook, k, c, kk);
+        for (int64_t r = 0; r < m; ++r) {
+            for (int64_t g = 0; g < ng; ++g) {
+                int64_t acc = 0;
+                for (int64_t kk = g * group; kk < (g + 1) * group; ++kk)
+                    acc += (int64_t)xq[r * k + kk] * (int64_t)w[kk];
+                if (acc > INT32_MAX || acc < INT32_MIN)
+                    overflow = 1;
+                d[(r * n + c) * ng + g] = (int32_t)acc;
+            }
+        }
+        free(w);
+    }
+    return overflow ? ORACLE_OVERFLOW : ORACLE_OK;
+}
+
+/*
+ * y[r][n] = sum_g xs[r][g] * ( sw[n][g]*D[r][n][g] + bw[n][g]*xsum[r][g] )    (fp64, g ascending)
+ * t[r][n] = sum_g |xs*sw*D| + |xs*bw*xsum|      (the magnitude of the terms, for error bounds)
+ * bias_f16 is used only for format 1 (affine); it may be NULL otherwise.
+ * t may be NULL.
+ */
+int oracle_linear(int32_t format, const uint8_t *codes, const uint16_t *scales_f16,
+                  const uint16_t *bias_f16, const int8_t *codebook,
+                  int64_t n, int64_t k, int32_t group,
+                  const int8_t *xq, const float *xs, const int32_t *xsum, int64_t m,
+                  double *y, double *t)
+{
+    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 2)
+        return ORACLE_BAD_ARGS;
+    if ((format == 1 && bias_f16 == NULL) || (format == 2 && codebook == NULL))
+        return ORACLE_BAD_ARGS;
+    int64_t ng = k / group;
+    int overflow = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : overflow)
+    for (int64_t c = 0; c < n; ++c) {
+        int32_t *w = (int32_t *)malloc((size_t)k * sizeof(int32_t));
+        for (int64_t kk = 0; kk < k; ++kk)
+            w[kk] = oracle_weight_int(format, codes, codebook, k, c, kk);
+        for (int64_t r = 0; r < m; ++r) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t g = 0; g < ng; ++g) {
+                int64_t dot = 0;
+                for (int64_t kk = g * group; kk < (g + 1) * group; ++kk)
+                    dot += (int64_t)xq[r * k + kk] * (int64_t)w[kk];
+                if (dot > INT32_MAX || dot < INT32_MIN)
+                    overflow = 1;
+                double a = (double)xs[r * ng + g];
+                double sw = oracle_half_to_double(scales_f16[c * ng + g]);
+                double bw = (format == 1) ? oracle_half_to_double(bias_f16[c * ng + g]) : 0.0;
+                double main_term = a * (sw * (double)dot);
+                double bias_term = a * (bw * (double)xsum[r * ng + g]);
+                acc += main_term + bias_term;
+                mag += fabs(main_term) + fabs(bias_term);
+            }
+            y[r * n + c] = acc;
+            if (t)
+                t[r * n + c] = mag;
+        }
+        free(w);
+    }
+    return overflow ? ORACLE_OVERFLOW : ORACLE_OK;
+}
+
+/* Number of OpenMP threads a parallel region here would use (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,408 @@
+"""Pins of the CPU oracle against things other than itself (closed forms, library routines,
+brute force, exact special cases, invariants), plus planted-mistake controls that show each pin
+would catch a plausible error.  CPU only."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_group_quantized_act_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- helpers (tests)
+
+def hadamard_dense(n: int) -> np.ndarray:
+    """Closed form of the normalized Sylvester Hadamard matrix: (-1)^popcount(i&j) / sqrt(n)."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    bits = np.bitwise_and(i, j)
+    pop = np.zeros_like(bits)
+    for b in range(16):
+        pop += (bits >> b) & 1
+    return np.where(pop % 2 == 0, 1.0, -1.0) / np.sqrt(n)
+
+
+def decode_weights(fmt, codes, codebook=None):
+    """Integer weights [n, k] decoded from canonical codes by the test itself."""
+    c = synth.unpack_nibbles(codes).astype(np.int64)
+    if fmt == synth.FMT_SYM:
+        return np.where(c >= 8, c - 16, c)
+    if fmt == synth.FMT_AFFINE:
+        return c
+    return np.take_along_axis(codebook.astype(np.int64), c, axis=1)
+
+
+def dequant_bruteforce(fmt, codes, scales, bias, codebook, xq, xs, group):
+    """fp64 dequantize-then-matmul: x_hat = xs*xq, w_hat = sw*w (+ bw), y = x_hat @ w_hat^T."""
+    m, k = xq.shape
+    rep = lambda a: np.repeat(a.astype(np.float64), group, axis=1)
+    x_hat = rep(xs) * xq.astype(np.float64)
+    w_hat = rep(scales) * decode_weights(fmt, codes, codebook).astype(np.float64)
+    if fmt == synth.FMT_AFFINE:
+        w_hat = w_hat + rep(bias)
+    return x_hat @ w_hat.T
+
+
+def small_layer(fmt, m=3, k=256, n=40, group=64, hadamard=0, seed=7, full_range=True):
+    name = {synth.FMT_SYM: "C1", synth.FMT_AFFINE: "C3a", synth.FMT_CODEBOOK: "C4"}[fmt]
+    cfg = synth.config(name, m=m, k=k, n=n, group=group, hadamard=hadamard, x_variant=seed,
+                       w_variant=seed)
+    return synth.make(cfg, full_range=full_range)
+
+
+def correctly_rounded_div(a, b):
+    """fp32 a/b correctly rounded, derived independently of fp32 hardware division: the double
+    quotient rounded to float32.  Double rounding through binary64 is innocuous for division of
+    binary32 operands (53 >= 2*24 + 2; Figueroa, 'When is double rounding innocuous?', 1995)."""
+    return (np.asarray(a, np.float64) / np.asarray(b, np.float64)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- fp16 decoding
+
+def test_half_to_double_all_patterns():
+    """The oracle's own binary16 decoder equals numpy's conversion for all 65536 patterns."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(int(b)) for b in bits[::1]])
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[np.isinf(ref)], ref[np.isinf(ref)])
+
+
+# ----------------------------------------------------------------------------- rotation
+
+def test_wht_matches_dense_closed_form():
+    x = np.random.default_rng(1).standard_normal((6, 128)).astype(np.float32)
+    got = oracle.wht(x, 128).astype(np.float64)
+    ref = x.astype(np.float64) @ hadamard_dense(128).T
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    assert err < 2e-6, err
+
+
+def test_wht_one_hot_is_exact():
+    """H e_i: every butterfly adds a value and an exact 0, so the output is exactly
+    +-fp32(1/sqrt(128)) with the closed-form sign (-1)^popcount(i&j)."""
+    c = np.float32(1.0 / np.sqrt(128.0))
+    signs = np.sign(hadamard_dense(128))
+    x = np.eye(128, dtype=np.float32)
+    got = oracle.wht(x, 128)
+    assert np.array_equal(got, (signs * c).astype(np.float32))
+
+
+def test_wht_ones_maps_to_scaled_e0():
+    got = oracle.wht(np.ones((1, 128), np.float32), 128)[0]
+    assert got[0] == np.float32(128.0) * np.float32(1.0 / np.sqrt(128.0))
+    assert np.all(got[1:] == 0.0)
+
+
+def test_wht_norm_preserved_and_involution():
+    x = np.random.default_rng(2).standard_normal((4, 512)).astype(np.float32) * 3
+    y = oracle.wht(x, 128)
+    for b in range(4):
+        blk = slice(128 * b, 128 * (b + 1))
+        nx = np.linalg.norm(x[:, blk].astype(np.float64), axis=1)
+        ny = np.linalg.norm(y[:, blk].astype(np.float64), axis=1)
+        assert np.allclose(nx, ny, rtol=2e-6)
+    z = oracle.wht(y, 128)
+    assert np.allclose(z, x, rtol=0, atol=3e-6 * np.abs(x).max())
+
+
+def test_wht_blocks_are_independent():
+    x = np.random.default_rng(3).standard_normal((2, 384)).astype(np.float32)
+    whole = oracle.wht(x, 128)
+    for b in range(3):
+        part = oracle.wht(x[:, 128 * b:128 * (b + 1)].copy(), 128)
+        assert np.array_equal(whole[:, 128 * b:128 * (b + 1)], part)
+
+
+# ----------------------------------------------------------------------------- quantization
+
+def _load_quant_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "quant_unit_scale.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                a, b = line.split()
+                rows.append((float(a), int(b)))
+    return rows
+
+
+def test_quant_unit_scale_golden():
+    rows = _load_quant_golden()
+    x = np.zeros((1, 64), np.float32)
+    x[0, :len(rows)] = [r[0] for r in rows]
+    xq, xs, xsum = oracle.quantize(x, 64)
+    assert xs[0, 0] == np.float32(1.0)
+    assert list(xq[0, :len(rows)]) == [r[1] for r in rows]
+    assert np.all(xq[0, len(rows):] == 0)
+    assert xsum[0, 0] == 129
+
+
+def test_quant_zero_groups():
+    x = np.zeros((2, 192), np.float32)
+    x[1, 64:128] = np.linspace(-3, 3, 64)
+    xq, xs, xsum = oracle.quantize(x, 64)
+    assert np.all(xs[0] == 0) and np.all(xq[0] == 0) and np.all(xsum[0] == 0)
+    assert xs[1, 0] == 0 and xs[1, 2] == 0 and xs[1, 1] > 0
+    assert np.abs(xq[1, 64:128]).max() == 127
+
+
+def _adversarial_rows(seed=4):
+    """Rows with outliers and values placed so that x/xs lands within an ulp of k + 0.5."""
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((64, 256)).astype(np.float32)
+    x[:, 5] *= 20
+    amax = np.abs(x.reshape(64, 4, 64)).max(axis=2)
+    xs = (amax.astype(np.float64) / 127).astype(np.float32)
+    # put some values at (j + 0.5) * xs, computed in fp32: the product's rounding moves the
+    # quotient either side of the tie, which separates exact division from other schemes
+    for row in range(64):
+        for g in range(4):
+            for t in range(8):
+                col = g * 64 + 8 + t * 7
+                if col % 64 == 5:
+                    continue
+                j = r.integers(-120, 120)
+                x[row, col] = np.float32(j + 0.5) * xs[row, g]
+    return x
+
+
+def test_quant_matches_independent_division():
+    """xs and xq equal an independent, correctly rounded derivation (see correctly_rounded_div)."""
+    x = _adversarial_rows()
+    xq, xs, xsum = oracle.quantize(x, 64)
+    xg = x.reshape(64, 4, 64)
+    amax = np.abs(xg).max(axis=2)
+    xs_ref = correctly_rounded_div(amax, np.float32(127))
+    assert np.array_equal(xs, xs_ref)
+    q_ref = np.rint(correctly_rounded_div(xg, xs_ref[:, :, None])).astype(np.int8)
+    assert np.array_equal(xq, q_ref.reshape(64, 256))
+    assert np.array_equal(xsum, q_ref.astype(np.int64).sum(axis=2))
+
+
+def test_quant_division_is_distinguishable_from_reciprocal():
+    """The adversarial set contains codes where x*fl(1/xs) rounds differently from x/xs, so the
+    previous test really pins division (a reciprocal-multiply oracle would fail it)."""
+    x = _adversarial_rows()
+    xg = x.reshape(64, 4, 64)
+    xs = correctly_rounded_div(np.abs(xg).max(axis=2), np.float32(127))[:, :, None]
+    by_div = np.rint(correctly_rounded_div(xg, xs))
+    recip = (np.float32(1) / xs).astype(np.float32)
+    by_mul = np.rint((xg * recip).astype(np.float32))
+    assert np.count_nonzero(by_div != by_mul) > 0
+
+
+def test_quant_rounding_bound_and_range():
+    x = synth.make_x(synth.config("C5a", k=1536))
+    xq, xs, xsum = oracle.quantize(x, 64)
+    xg = x.reshape(1, -1, 64).astype(np.float64)
+    rec = xs[:, :, None].astype(np.float64) * xq.reshape(1, -1, 64)
+    # |x - xs*q| <= xs/2 up to the two fp32 roundings of x/xs
+    assert np.all(np.abs(xg - rec) <= xs[:, :, None] * (0.5 + 1e-5))
+    assert np.abs(xq).max() <= 127
+    assert np.all(np.abs(xq.reshape(1, -1, 64)).max(axis=2) == 127)
+    assert np.array_equal(xsum, xq.reshape(1, -1, 64).astype(np.int64).sum(axis=2))
+
+
+def test_prep_composes_rotation_then_quantization():
+    x = synth.make_x(synth.config("C4", m=5))
+    a = oracle.prep(x, 128, hadamard_block=128)
+    b = oracle.quantize(oracle.wht(x, 128), 128)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+# ----------------------------------------------------------------------------- partials
+
+@pytest.mark.parametrize("fmt", [synth.FMT_SYM, synth.FMT_AFFINE, synth.FMT_CODEBOOK])
+@pytest.mark.parametrize("group", [64, 128])
+def test_partials_bruteforce_integer(fmt, group):
+    L = small_layer(fmt, m=3, k=256, n=24, group=group)
+    xq, xs, xsum = oracle.quantize(L["x"], group)
+    d = oracle.partials(fmt, L["codes"], xq, group, codebook=L["codebook"])
+    w = decode_weights(fmt, L["codes"], L["codebook"])
+    ng = 256 // group
+    ref = np.einsum("mgk,ngk->mng", xq.astype(np.int64).reshape(3, ng, group),
+                    w.reshape(24, ng, group))
+    assert np.array_equal(d, ref)
+
+
+def test_partials_python_bigint_spot():
+    L = small_layer(synth.FMT_CODEBOOK, m=2, k=128, n=4, group=64)
+    xq, _, _ = oracle.quantize(L["x"], 64)
+    d = oracle.partials(2, L["codes"], xq, 64, codebook=L["codebook"])
+    idx = synth.unpack_nibbles(L["codes"])
+    for r in range(2):
+        for c in range(4):
+            for g in range(2):
+                s = 0
+                for kk in range(64 * g, 64 * g + 64):
+                    s += int(xq[r, kk]) * int(L["codebook"][c, idx[c, kk]])
+                assert d[r, c, g] == s
+
+
+def test_codebook_sign_extended_identity_equals_sym():
+    L = small_layer(synth.FMT_SYM, m=2, k=128, n=16)
+    xq, _, _ = oracle.quantize(L["x"], 64)
+    ident = np.array([j if j < 8 else j - 16 for j in range(16)], np.int8)
+    cb = np.tile(ident, (16, 1))
+    d_sym = oracle.partials(0, L["codes"], xq, 64)
+    d_cb = oracle.partials(2, L["codes"], xq, 64, codebook=cb)
+    assert np.array_equal(d_sym, d_cb)
+
+
+# ----------------------------------------------------------------------------- output
+
+@pytest.mark.parametrize("fmt,group,had", [(0, 64, 0), (1, 64, 0), (2, 128, 128), (0, 128, 128),
+                                           (1, 128, 0), (2, 64, 0)])
+def test_linear_vs_fp64_dequant_matmul(fmt, group, had):
+    L = small_layer(fmt, m=4, k=512, n=48, group=group, hadamard=had)
+    xq, xs, xsum = oracle.prep(L["x"], group, hadamard_block=had)
+    y, t = oracle.linear(fmt, L["codes"], L["scales"], xq, xs, xsum, group, bias_f16=L["bias"],
+                         codebook=L["codebook"])
+    ref = dequant_bruteforce(fmt, L["codes"], L["scales"], L["bias"], L["codebook"], xq, xs,
+                             group)
+    assert np.all(np.abs(y - ref) <= 1e-12 * t + 1e-300)
+    assert np.all(t >= np.abs(y) * (1 - 1e-12))
+
+
+def test_tiny_linear_golden():
+    want = {}
+    with open(os.path.join(GOLDEN, "tiny_linear.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                fmtname, d, y = line.split()
+                want[fmtname] = (int(d), float(y))
+    x = np.zeros((1, 64), np.float32)
+    x[0, 0], x[0, 1] = 127.0, -64.0
+    xq, xs, xsum = oracle.quantize(x, 64)
+    assert xs[0, 0] == 1.0 and xsum[0, 0] == 63
+
+    def codes_of(vals):
+        c = np.zeros((1, 64), np.uint8)
+        c[0, :len(vals)] = vals
+        return synth.pack_nibbles(c)
+
+    half = lambda v: np.full((1, 1), v, np.float16)
+    cases = {
+        "sym": (0, codes_of([1, 2]), half(0.5), None, None),
+        "affine": (1, codes_of([3, 5]), half(0.25), half(-1.0), None),
+        "codebook": (2, codes_of([1, 2]), half(0.125), None,
+                     np.array([[10, -20, 30] + [0] * 13], np.int8)),
+    }
+    for name, (fmt, codes, s, b, cb) in cases.items():
+        d = oracle.partials(fmt, codes, xq, 64, codebook=cb)
+        y = oracle.linear(fmt, codes, s, xq, xs, xsum, 64, bias_f16=b, codebook=cb,
+                          with_terms=False)
+        assert d[0, 0, 0] == want[name][0], name
+        assert y[0, 0] == want[name][1], name
+
+
+def test_sym_equals_affine_shifted():
+    """sym(q, s) == affine(u = q + 8, s, b = -8 s); -8*s is exact in fp16 for these scales."""
+    L = small_layer(synth.FMT_SYM, m=3, k=256, n=32)
+    q = synth.unpack_nibbles(L["codes"]).astype(np.int16)
+    q = np.where(q >= 8, q - 16, q)
+    u_codes = synth.pack_nibbles((q + 8).astype(np.uint8))
+    b = (-8.0 * L["scales"].astype(np.float64)).astype(np.float16)
+    assert np.array_equal(b.astype(np.float64), -8.0 * L["scales"].astype(np.float64))
+    xq, xs, xsum = oracle.quantize(L["x"], 64)
+    y_s, t_s = oracle.linear(0, L["codes"], L["scales"], xq, xs, xsum, 64)
+    y_a, t_a = oracle.linear(1, u_codes, L["scales"], xq, xs, xsum, 64, bias_f16=b)
+    assert np.all(np.abs(y_s - y_a) <= 1e-12 * (t_s + t_a))
+    d_s = oracle.partials(0, L["codes"], xq, 64)
+    d_a = oracle.partials(1, u_codes, xq, 64)
+    assert np.array_equal(d_a, d_s + 8 * xsum[:, None, :])
+
+
+def test_group_permutation_invariance():
+    L = small_layer(synth.FMT_AFFINE, m=2, k=512, n=16)
+    xq, xs, xsum = oracle.quantize(L["x"], 64)
+    y, t = oracle.linear(1, L["codes"], L["scales"], xq, xs, xsum, 64, bias_f16=L["bias"])
+    perm = np.random.default_rng(5).permutation(8)
+    cidx = synth.unpack_nibbles(L["codes"]).reshape(16, 8, 64)[:, perm].reshape(16, 512)
+    xq_p = xq.reshape(2, 8, 64)[:, perm].reshape(2, 512)
+    y_p, _ = oracle.linear(1, synth.pack_nibbles(cidx), L["scales"][:, perm], xq_p,
+                           xs[:, perm], xsum[:, perm], 64, bias_f16=L["bias"][:, perm])
+    assert np.all(np.abs(y - y_p) <= 1e-12 * t)
+
+
+def test_unit_scales_reduce_to_integer_matmul():
+    """Groups whose amax is 127 and integer-valued x give xs = 1, xq = x; with weight scale 1 the
+    output is the exact integer matmul x @ w_int^T."""
+    r = np.random.default_rng(6)
+    x = r.integers(-126, 127, size=(3, 128)).astype(np.float32)
+    x[:, 0] = 127
+    x[:, 64] = -127
+    L = small_layer(synth.FMT_SYM, m=3, k=128, n=20)
+    ones = np.ones((20, 2), np.float16)
+    xq, xs, xsum = oracle.quantize(x, 64)
+    assert np.all(xs == 1.0) and np.array_equal(xq, x.astype(np.int8))
+    y = oracle.linear(0, L["codes"], ones, xq, xs, xsum, 64, with_terms=False)
+    ref = x.astype(np.int64) @ decode_weights(0, L["codes"]).T
+    assert np.array_equal(y, ref.astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- planted controls
+
+def test_control_zeroed_sums_break_affine_pin():
+    L = small_layer(synth.FMT_AFFINE, m=2, k=256, n=16)
+    xq, xs, xsum = oracle.quantize(L["x"], 64)
+    ref = dequant_bruteforce(1, L["codes"], L["scales"], L["bias"], None, xq, xs, 64)
+    y, t = oracle.linear(1, L["codes"], L["scales"], xq, xs, np.zeros_like(xsum), 64,
+                         bias_f16=L["bias"])
+    assert not np.all(np.abs(y - ref) <= 1e-4 * t)
+
+
+def test_control_scale_off_by_one_ulp_breaks_division_pin():
+    x = _adversarial_rows()
+    _, xs, _ = oracle.quantize(x, 64)
+    bad = np.nextafter(xs, np.float32(np.inf))
+    xs_ref = correctly_rounded_div(np.abs(x.reshape(64, 4, 64)).max(axis=2), np.float32(127))
+    assert not np.array_equal(bad, xs_ref)
+
+
+def test_control_skipped_rotation_breaks_rotated_layer():
+    L = small_layer(synth.FMT_CODEBOOK, m=2, k=256, n=16, group=128, hadamard=128)
+    xq_r, xs_r, xsum_r = oracle.prep(L["x"], 128, hadamard_block=128)
+    xq_n, xs_n, xsum_n = oracle.prep(L["x"], 128, hadamard_block=0)
+    y_r, t_r = oracle.linear(2, L["codes"], L["scales"], xq_r, xs_r, xsum_r, 128,
+                             codebook=L["codebook"])
+    y_n = oracle.linear(2, L["codes"], L["scales"], xq_n, xs_n, xsum_n, 128,
+                        codebook=L["codebook"], with_terms=False)
+    assert not np.all(np.abs(y_r - y_n) <= 1e-4 * t_r)
+
+
+# ----------------------------------------------------------------------------- generator
+
+def test_generator_is_deterministic():
+    a = synth.make("C2b", k=256, n=64)
+    b = synth.make("C2b", k=256, n=64)
+    for key in ("x", "codes", "scales"):
+        assert np.array_equal(a[key], b[key])
+    c = synth.make("C3a", m=4, k=256, n=32)
+    assert c["bias"] is not None and c["codebook"] is None
+    d = synth.make("C4", m=4, k=256, n=32)
+    assert d["codebook"].shape == (32, 16) and d["bias"] is None
+
+
+def test_generator_outliers_and_ranges():
+    cfg = synth.config("C2a")
+    x = synth.make_x(cfg)
+    raw = synth.rng(cfg.cfg_id, cfg.x_variant, 0).standard_normal((1, 2048), dtype=np.float32)
+    scaled = np.flatnonzero(x[0] != raw[0])
+    assert len(scaled) == 8
+    assert np.array_equal(x[0, scaled], raw[0, scaled] * np.float32(20.0))
+    cfg = synth.config("C3a", n=64)
+    codes, sc, bias, _ = synth.make_weights(cfg)
+    u = synth.unpack_nibbles(codes)
+    assert u.min() == 0 and u.max() == 15
+    fr = synth.make("C1", full_range=True, n=64)
+    assert set(np.unique(synth.unpack_nibbles(fr["codes"]))) == set(range(16))
+    assert synth.algorithmic_bytes(synth.config("C1")) == 562304
