@@ -1,0 +1,76 @@
+"""Build libw4a8.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc.
+
+Every translation unit is compiled in parallel, then linked into
+``bit_group_quantized_act_amd/libw4a8.so`` (replaced atomically).  Flags:
+  --offload-arch=gfx950                       MI355X only, no other targets
+  -fhip-fp32-correctly-rounded-divide-sqrt    IEEE fp32 division (the prepass is bit-exact)
+  -target-feature -packed-fp32-ops            no packed fp32 VALU instructions in device code
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
+LIB = os.path.join(HERE, "libw4a8.so")
+SOURCES = ["api.hip", "pack.hip", "prep.hip", "gemv.hip", "gemm.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libw4a8)")
+
+
+def _quiet(stderr: str) -> str:
+    # hipcc's host pass does not know the device-only target feature; that warning is noise.
+    return "\n".join(l for l in stderr.splitlines() if "packed-fp32-ops" not in l)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every HIP source and link libw4a8.so.  Always rebuilds.  Returns the path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+    flags = HIPCC_FLAGS + list(extra_flags or [])
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmd = [cc] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                            text=True)))
+    failed = []
+    for src, p in procs:
+        out, err = p.communicate()
+        err = _quiet(err)
+        if p.returncode != 0:
+            failed.append(f"{src}:\n{err}")
+        elif verbose and err.strip():
+            print(err)
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + _quiet(r.stderr))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

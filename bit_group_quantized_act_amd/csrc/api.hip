@@ -1,0 +1,259 @@
+// The C ABI of libw4a8 (declared in include/w4a8.h): host-side validation, the gfx950 device
+// check, and the launches.  No entry point allocates memory or synchronizes.
+#include "../../include/w4a8.h"
+#include "w4a8_kernels.h"
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+w4a8_status fail(w4a8_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+w4a8_status ok() {
+    g_last_error[0] = '\0';
+    return W4A8_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+w4a8_status check_device() {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return fail(W4A8_ERR_DEVICE, "no HIP device is visible");
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(W4A8_ERR_DEVICE, "hipGetDevice failed");
+    }
+    if (dev >= kMaxDevices) return fail(W4A8_ERR_DEVICE, "device index %d is too large", dev);
+    int state = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(W4A8_ERR_DEVICE, "hipGetDeviceProperties(%d) failed", dev);
+        }
+        state = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_ok[dev].store(state, std::memory_order_relaxed);
+        if (state == 2)
+            return fail(W4A8_ERR_DEVICE, "device %d is %s, these kernels are built for gfx950",
+                        dev, prop.gcnArchName);
+    }
+    if (state != 1) return fail(W4A8_ERR_DEVICE, "device %d is not gfx950", dev);
+    return W4A8_OK;
+}
+
+w4a8_status check_layout(const w4a8_layout *L) {
+    if (!L) return fail(W4A8_ERR_ARG, "layout is NULL");
+    w4a8_layout ref;
+    if (w4a8_packed_layout(L->format, L->n, L->k, L->group, &ref) != W4A8_OK)
+        return W4A8_ERR_ARG;   // the message of w4a8_packed_layout stays in place
+    if (memcmp(&ref, L, sizeof ref) != 0)
+        return fail(W4A8_ERR_ARG, "layout was not produced by w4a8_packed_layout");
+    return W4A8_OK;
+}
+
+w4a8::Geom geom_of(const w4a8_layout *L) {
+    w4a8::Geom g;
+    g.fmt = L->format;
+    g.n = L->n;
+    g.k = L->k;
+    g.group = L->group;
+    g.n_pad = L->n_pad;
+    g.meta_bytes = L->meta_bytes;
+    g.off_codes = L->off_codes;
+    g.off_meta = L->off_meta;
+    g.off_codebook = L->off_codebook;
+    return g;
+}
+
+w4a8_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(W4A8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+#define W4A8_REQUIRE_PTR(p)                                                                    \
+    do {                                                                                       \
+        if (!(p)) return fail(W4A8_ERR_ARG, #p " is NULL");                                    \
+        if (!aligned((p), 16)) return fail(W4A8_ERR_ARG, #p " is not 16-byte aligned");        \
+    } while (0)
+
+w4a8_status check_activation_ptrs(const int8_t *xq, const float *xs, const int32_t *xsum) {
+    W4A8_REQUIRE_PTR(xq);
+    W4A8_REQUIRE_PTR(xs);
+    W4A8_REQUIRE_PTR(xsum);
+    return W4A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a8_status w4a8_packed_layout(int32_t format, int32_t n, int32_t k, int32_t group,
+                               w4a8_layout *L) {
+    if (!L) return fail(W4A8_ERR_ARG, "layout is NULL");
+    if (format < W4A8_SYM_I4 || format > W4A8_CODEBOOK_I4)
+        return fail(W4A8_ERR_ARG, "format %d is not a w4a8_format", format);
+    if (group != 64 && group != 128) return fail(W4A8_ERR_ARG, "group %d is not 64 or 128", group);
+    if (n < 1 || n > (1 << 24)) return fail(W4A8_ERR_ARG, "n = %d is outside [1, 2^24]", n);
+    if (k < group || k > (1 << 20) || k % group != 0)
+        return fail(W4A8_ERR_ARG, "k = %d must be a multiple of group %d in [group, 2^20]", k,
+                    group);
+    memset(L, 0, sizeof *L);
+    L->format = format;
+    L->n = n;
+    L->k = k;
+    L->group = group;
+    L->n_pad = static_cast<int32_t>(round_up(n, W4A8_PANEL_ROWS));
+    L->meta_bytes = (format == W4A8_AFFINE_U4) ? 4 : 2;
+    const uint64_t codes = static_cast<uint64_t>(L->n_pad) * k / 2;
+    const uint64_t meta = static_cast<uint64_t>(L->n_pad) * (k / group) * L->meta_bytes;
+    L->off_codes = 0;
+    L->off_meta = round_up(codes, 256);
+    uint64_t end = L->off_meta + round_up(meta, 256);
+    if (format == W4A8_CODEBOOK_I4) {
+        L->off_codebook = end;
+        end += round_up(static_cast<uint64_t>(L->n_pad) * 16, 256);
+    }
+    L->bytes = end;
+    return ok();
+}
+
+w4a8_status w4a8_pack_weights(const w4a8_layout *L, const uint8_t *codes,
+                              const uint16_t *scales_f16, const uint16_t *bias_f16,
+                              const int8_t *codebook, void *packed, void *stream) {
+    w4a8_status s = check_layout(L);
+    if (s != W4A8_OK) return s;
+    W4A8_REQUIRE_PTR(codes);
+    W4A8_REQUIRE_PTR(scales_f16);
+    if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
+    if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
+    if (L->format == W4A8_AFFINE_U4) {
+        W4A8_REQUIRE_PTR(bias_f16);
+    } else if (bias_f16) {
+        return fail(W4A8_ERR_ARG, "bias_f16 is only used by the affine format; pass NULL");
+    }
+    if (L->format == W4A8_CODEBOOK_I4) {
+        W4A8_REQUIRE_PTR(codebook);
+    } else if (codebook) {
+        return fail(W4A8_ERR_ARG, "codebook is only used by the codebook format; pass NULL");
+    }
+    if ((s = check_device()) != W4A8_OK) return s;
+    return launched(w4a8::launch_pack(geom_of(L), codes, scales_f16, bias_f16, codebook,
+                                      static_cast<uint8_t *>(packed),
+                                      static_cast<hipStream_t>(stream)),
+                    "pack launch");
+}
+
+w4a8_status w4a8_prep(const float *x, int32_t m, int32_t k, int32_t group,
+                      int32_t hadamard_block, int8_t *xq, float *xs, int32_t *xsum,
+                      void *stream) {
+    if (m < 0) return fail(W4A8_ERR_ARG, "m = %d is negative", m);
+    if (group != 64 && group != 128) return fail(W4A8_ERR_ARG, "group %d is not 64 or 128", group);
+    if (k < group || k > (1 << 20) || k % group != 0)
+        return fail(W4A8_ERR_ARG, "k = %d must be a multiple of group %d in [group, 2^20]", k,
+                    group);
+    if (hadamard_block != 0 && hadamard_block != 128)
+        return fail(W4A8_ERR_ARG, "hadamard_block %d is not 0 or 128", hadamard_block);
+    if (hadamard_block == 128 && k % 128 != 0)
+        return fail(W4A8_ERR_ARG, "k = %d is not a multiple of the rotation block 128", k);
+    if (static_cast<int64_t>(m) * k > (int64_t{1} << 38))
+        return fail(W4A8_ERR_UNSUPPORTED, "m * k = %lld is above 2^38",
+                    static_cast<long long>(static_cast<int64_t>(m) * k));
+    if (m == 0) return ok();   // nothing to do; the pointers may be NULL
+    W4A8_REQUIRE_PTR(x);
+    w4a8_status s = check_activation_ptrs(xq, xs, xsum);
+    if (s != W4A8_OK) return s;
+    if ((s = check_device()) != W4A8_OK) return s;
+    return launched(w4a8::launch_prep(x, m, k, group, hadamard_block, xq, xs, xsum,
+                                      static_cast<hipStream_t>(stream)),
+                    "prep launch");
+}
+
+w4a8_status w4a8_gemv(const w4a8_layout *L, const void *packed, const int8_t *xq,
+                      const float *xs, const int32_t *xsum, float *y, void *stream) {
+    w4a8_status s = check_layout(L);
+    if (s != W4A8_OK) return s;
+    if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
+    if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
+    if ((s = check_activation_ptrs(xq, xs, xsum)) != W4A8_OK) return s;
+    W4A8_REQUIRE_PTR(y);
+    if ((s = check_device()) != W4A8_OK) return s;
+    return launched(w4a8::launch_gemv(geom_of(L), static_cast<const uint8_t *>(packed), xq, xs,
+                                      xsum, y, nullptr, static_cast<hipStream_t>(stream)),
+                    "gemv launch");
+}
+
+w4a8_status w4a8_gemm(const w4a8_layout *L, const void *packed, int32_t m, const int8_t *xq,
+                      const float *xs, const int32_t *xsum, float *y, void *stream) {
+    w4a8_status s = check_layout(L);
+    if (s != W4A8_OK) return s;
+    if (m < 0) return fail(W4A8_ERR_ARG, "m = %d is negative", m);
+    if (m > (1 << 20)) return fail(W4A8_ERR_UNSUPPORTED, "m = %d is above 2^20", m);
+    if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
+    if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
+    if (m == 0) return ok();   // nothing to do; the activation and output pointers may be NULL
+    if ((s = check_activation_ptrs(xq, xs, xsum)) != W4A8_OK) return s;
+    W4A8_REQUIRE_PTR(y);
+    if ((s = check_device()) != W4A8_OK) return s;
+    return launched(w4a8::launch_gemm(geom_of(L), static_cast<const uint8_t *>(packed), m, xq,
+                                      xs, xsum, y, nullptr, static_cast<hipStream_t>(stream)),
+                    "gemm launch");
+}
+
+w4a8_status w4a8_debug_partials(const w4a8_layout *L, const void *packed, int32_t m,
+                                const int8_t *xq, const int32_t *xsum, int32_t *d,
+                                void *stream) {
+    w4a8_status s = check_layout(L);
+    if (s != W4A8_OK) return s;
+    if (m < 1) return fail(W4A8_ERR_ARG, "m = %d must be at least 1", m);
+    if (m > (1 << 20)) return fail(W4A8_ERR_UNSUPPORTED, "m = %d is above 2^20", m);
+    if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
+    if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
+    W4A8_REQUIRE_PTR(xq);
+    W4A8_REQUIRE_PTR(xsum);
+    W4A8_REQUIRE_PTR(d);
+    if ((s = check_device()) != W4A8_OK) return s;
+    const w4a8::Geom g = geom_of(L);
+    const uint8_t *pk = static_cast<const uint8_t *>(packed);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (m == 1)
+        return launched(w4a8::launch_gemv(g, pk, xq, nullptr, xsum, nullptr, d, st),
+                        "gemv partials launch");
+    return launched(w4a8::launch_gemm(g, pk, m, xq, nullptr, xsum, nullptr, d, st),
+                    "gemm partials launch");
+}
+
+const char *w4a8_status_string(w4a8_status s) {
+    switch (s) {
+    case W4A8_OK: return "ok";
+    case W4A8_ERR_ARG: return "invalid argument";
+    case W4A8_ERR_UNSUPPORTED: return "unsupported";
+    case W4A8_ERR_DEVICE: return "no gfx950 device";
+    case W4A8_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *w4a8_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+"""Python binding of libw4a8 (the C ABI in include/w4a8.h) over torch device tensors.
+
+Argument marshalling only: every step runs in the library's HIP kernels.  torch supplies device
+memory (outputs are allocated with torch unless passed in) and the current HIP stream.  If
+``libw4a8.so`` has not been built, loading raises: there is no other implementation to fall back
+to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a8.so")
+
+SYM, AFFINE, CODEBOOK = 0, 1, 2
+PANEL_ROWS = 64
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "no gfx950 device", 4: "HIP error"}
+
+# Every exported symbol of the C ABI (the header's declarations, in order).
+EXPORTS = ("w4a8_packed_layout", "w4a8_pack_weights", "w4a8_prep", "w4a8_gemv", "w4a8_gemm",
+           "w4a8_debug_partials", "w4a8_status_string", "w4a8_last_error")
+
+
+class Layout(ctypes.Structure):
+    """Mirror of w4a8_layout."""
+    _fields_ = [("format", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("n_pad", ctypes.c_int32),
+                ("meta_bytes", ctypes.c_int32), ("bytes", ctypes.c_uint64),
+                ("off_codes", ctypes.c_uint64), ("off_meta", ctypes.c_uint64),
+                ("off_codebook", ctypes.c_uint64)]
+
+    def __repr__(self):
+        return ("Layout(format=%d, n=%d, k=%d, group=%d, n_pad=%d, bytes=%d)"
+                % (self.format, self.n, self.k, self.group, self.n_pad, self.bytes))
+
+
+class W4A8Error(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libw4a8.so (built in-tree by build.build()); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() or "
+                          "python bit_group_quantized_act_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32 = ctypes.c_void_p, ctypes.c_int32
+    LP = ctypes.POINTER(Layout)
+    lib.w4a8_packed_layout.argtypes = [i32, i32, i32, i32, LP]
+    lib.w4a8_pack_weights.argtypes = [LP, P, P, P, P, P, P]
+    lib.w4a8_prep.argtypes = [P, i32, i32, i32, i32, P, P, P, P]
+    lib.w4a8_gemv.argtypes = [LP, P, P, P, P, P, P]
+    lib.w4a8_gemm.argtypes = [LP, P, i32, P, P, P, P, P]
+    lib.w4a8_debug_partials.argtypes = [LP, P, i32, P, P, P, P]
+    for f in EXPORTS[:6]:
+        getattr(lib, f).restype = ctypes.c_int
+    lib.w4a8_status_string.argtypes = [ctypes.c_int]
+    lib.w4a8_status_string.restype = ctypes.c_char_p
+    lib.w4a8_last_error.argtypes = []
+    lib.w4a8_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise W4A8Error(rc, what, load().w4a8_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def packed_layout(fmt: int, n: int, k: int, group: int) -> Layout:
+    L = Layout()
+    _check(load().w4a8_packed_layout(fmt, n, k, group, ctypes.byref(L)), "w4a8_packed_layout")
+    return L
+
+
+def pack(codes: torch.Tensor, scales: torch.Tensor, fmt: int, group: int, bias=None,
+         codebook=None, out: torch.Tensor | None = None):
+    """Repack canonical device weights.  Returns (layout, packed uint8 tensor of layout.bytes).
+
+    codes uint8 [n, k/2] (low nibble = even k); scales float16 [n, k/group];
+    bias float16 [n, k/group] (affine); codebook int8 [n, 16] (codebook).
+    """
+    n, kh = codes.shape
+    k = 2 * kh
+    L = packed_layout(fmt, n, k, group)
+    _dev(codes, torch.uint8, "codes")
+    _dev(scales, torch.float16, "scales", (n, k // group))
+    if bias is not None:
+        _dev(bias, torch.float16, "bias", (n, k // group))
+    if codebook is not None:
+        _dev(codebook, torch.int8, "codebook", (n, 16))
+    if out is None:
+        out = torch.empty(L.bytes, dtype=torch.uint8, device=codes.device)
+    _dev(out, torch.uint8, "packed", (L.bytes,))
+    _check(load().w4a8_pack_weights(ctypes.byref(L), _ptr(codes), _ptr(scales), _ptr(bias),
+                                    _ptr(codebook), _ptr(out), _stream(codes.device)),
+           "w4a8_pack_weights")
+    return L, out
+
+
+def prep(x: torch.Tensor, group: int, hadamard_block: int = 0, out=None):
+    """Activation prepass on fp32 [m, k] (or [k]).  Returns (xq int8, xs fp32, xsum int32)."""
+    squeeze = x.dim() == 1
+    x2 = x.unsqueeze(0) if squeeze else x
+    _dev(x2, torch.float32, "x")
+    m, k = x2.shape
+    ng = k // group if group else 0
+    if out is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+        xs = torch.empty((m, ng), dtype=torch.float32, device=x.device)
+        xsum = torch.empty((m, ng), dtype=torch.int32, device=x.device)
+    else:
+        xq, xs, xsum = out
+    _check(load().w4a8_prep(_ptr(x2), m, k, group, hadamard_block, _ptr(xq), _ptr(xs),
+                            _ptr(xsum), _stream(x.device)), "w4a8_prep")
+    if squeeze:
+        return xq[0], xs[0], xsum[0]
+    return xq, xs, xsum
+
+
+def gemv(L: Layout, packed: torch.Tensor, xq, xs, xsum, out=None) -> torch.Tensor:
+    """Decode GEMV: one activation row -> fp32 [n]."""
+    y = out if out is not None else torch.empty(L.n, dtype=torch.float32, device=packed.device)
+    _check(load().w4a8_gemv(ctypes.byref(L), _ptr(packed), _ptr(xq), _ptr(xs), _ptr(xsum),
+                            _ptr(y), _stream(packed.device)), "w4a8_gemv")
+    return y
+
+
+def gemm(L: Layout, packed: torch.Tensor, xq, xs, xsum, out=None) -> torch.Tensor:
+    """Prefill GEMM: m activation rows (xq int8 [m, k]) -> fp32 [m, n]."""
+    m = xq.shape[0]
+    y = out if out is not None else torch.empty((m, L.n), dtype=torch.float32,
+                                                device=packed.device)
+    _check(load().w4a8_gemm(ctypes.byref(L), _ptr(packed), m, _ptr(xq), _ptr(xs), _ptr(xsum),
+                            _ptr(y), _stream(packed.device)), "w4a8_gemm")
+    return y
+
+
+def debug_partials(L: Layout, packed: torch.Tensor, xq, xsum) -> torch.Tensor:
+    """Exact int32 partials D [m, n, k/group] from the GEMV (m == 1) or GEMM (m > 1) kernels."""
+    xq2 = xq.unsqueeze(0) if xq.dim() == 1 else xq
+    m = xq2.shape[0]
+    d = torch.empty((m, L.n, L.k // L.group), dtype=torch.int32, device=packed.device)
+    _check(load().w4a8_debug_partials(ctypes.byref(L), _ptr(packed), m, _ptr(xq2), _ptr(xsum),
+                                      _ptr(d), _stream(packed.device)), "w4a8_debug_partials")
+    return d
+
+
+def linear(L: Layout, packed: torch.Tensor, x: torch.Tensor, hadamard_block: int = 0):
+    """prep then GEMV (one row) or GEMM: fp32 activations [m, k] or [k] -> fp32 output."""
+    xq, xs, xsum = prep(x, L.group, hadamard_block)
+    if x.dim() == 1:
+        return gemv(L, packed, xq, xs, xsum)
+    return gemm(L, packed, xq, xs, xsum)

@@ -1,0 +1,187 @@
+/*
+ * w4a8.h -- C ABI of the MI355X (gfx950) W4A8 linear layer: 4-bit group-quantized weights times
+ * int8 group-quantized activations.
+ *
+ * The operation (from the pages this library is written from):
+ *   - "cactus PR #697: SME2 acceleration for CQ4 matmul, prefill attention, and orthogonal
+ *     embeddings", section "Quantized matmul": the M=1 GEMV runs a first phase that applies a
+ *     Hadamard transform to the activations and quantizes them to int8 per group, then streams
+ *     packed 4-bit weight nibbles; the M>1 GEMM produces raw int32 partials that are rescaled in
+ *     a vector epilogue.  The review snippet of the per-group leaf contract in the same page
+ *     defines the partial: for one group and one output channel, the int32 sum over the group
+ *     of activation code times weight value, with activation scale and weight scale applied by
+ *     the caller.
+ *   - "TensorFold PR #3215: simd_qmm on Metal: X's group sums and half operands from a prepass",
+ *     section "What this changes": one prepass per call writes the per-row per-group sums of X
+ *     that the 4-bit affine (scale and bias per 64-group) weights need for their bias term.
+ *   - "geistlib issue #500: native W*A8 int8 GEMM for prefill", sections "Design" and "Scope":
+ *     one shared activation quantization feeding both GEMV and GEMM, and a load-time repack of
+ *     the weights into the kernel's layout.
+ *
+ * Definitions used by every entry point (x is fp32 [m][k]; weight group == activation group G):
+ *   rotation    (optional) normalized Walsh-Hadamard transform of each 128-wide block of a row,
+ *               fp32 butterflies with span 1, 2, ..., 64, then one multiply by fp32(1/sqrt(128))
+ *   xs[r][g]    = amax / 127 (IEEE fp32 divide), amax = max |x| over the group; 0 if amax == 0
+ *   xq[r][k]    = round-half-even(x / xs) (IEEE fp32 divide), in [-127, 127]; 0 if amax == 0
+ *   xsum[r][g]  = sum of the group's xq (int32)
+ *   D[r][n][g]  = sum over k in group g of xq[r][k] * w[n][k]        (exact int32)
+ *                 w = q in [-8, 7] (SYM), u in [0, 15] (AFFINE), codebook[n][j] (CODEBOOK)
+ *   y[r][n]     = sum over g of xs[r][g] * ( sw[n][g] * D[r][n][g] + bw[n][g] * xsum[r][g] )
+ *                 bw = 0 except AFFINE (dequantized weight = sw * u + bw); fp32 result
+ *
+ * Conventions
+ *   - Every data pointer is a DEVICE pointer owned by the caller, except the layout struct,
+ *     which lives in host memory.  No entry point allocates, frees or keeps device memory, and
+ *     none keeps state between calls apart from a per-device architecture check and a
+ *     thread-local error message.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns without synchronizing; faults of enqueued work surface at the
+ *     caller's next synchronization.
+ *   - Arguments are validated on the host before any device work.  On a non-OK status nothing
+ *     was enqueued (except W4A8_ERR_HIP, which reports a failed launch) and w4a8_last_error()
+ *     describes the problem.
+ *   - Device pointers must be 16-byte aligned; `packed` must be 256-byte aligned.
+ *   - There is no fallback path: a request the kernels do not cover returns an error.
+ *   - The current device must be an MI355X-class gfx950 GPU, else W4A8_ERR_DEVICE.
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A8_OK = 0,
+    W4A8_ERR_ARG = 1,          /* an argument is invalid (null, size, alignment, combination) */
+    W4A8_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels implement               */
+    W4A8_ERR_DEVICE = 3,       /* no device, or the current device is not gfx950             */
+    W4A8_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed                 */
+} w4a8_status;
+
+typedef enum {
+    W4A8_SYM_I4 = 0,       /* two's-complement 4-bit q in [-8, 7], fp16 scale per group       */
+    W4A8_AFFINE_U4 = 1,    /* unsigned 4-bit u in [0, 15], fp16 scale and fp16 bias per group */
+    W4A8_CODEBOOK_I4 = 2   /* 4-bit index into a per-output-row 16-entry int8 codebook,
+                              fp16 scale per group (PR #697's CQ4 codebook format)           */
+} w4a8_format;
+
+/* Rows of the packed weight buffer come in panels of this many output channels. */
+#define W4A8_PANEL_ROWS 64
+
+/*
+ * Description of one packed weight buffer (host struct, filled by w4a8_packed_layout).
+ *
+ * Packed buffer (all offsets in bytes from the 256-byte aligned base, each section 256-aligned):
+ *   codes     at off_codes: n_pad/64 panels; each panel is k/32 chunk columns; each chunk column
+ *             is 64 rows x 16 bytes.  The 16 bytes of (row n, chunk c) hold the 32 codes of
+ *             k = 32c .. 32c+31 as four dwords; dword j, byte b holds the code of k = 32c+8j+b in
+ *             its low nibble and of k = 32c+8j+4+b in its high nibble.  SYM stores q's
+ *             two's-complement nibble, AFFINE stores u XOR 8 (= u - 8 as a signed nibble),
+ *             CODEBOOK stores the index.
+ *   meta      at off_meta: per panel, per group g, per panel row: meta_bytes bytes.  SYM and
+ *             CODEBOOK: the fp16 scale.  AFFINE: a dword, fp16 scale in the low half and fp16
+ *             bias in the high half.
+ *   codebook  at off_codebook (CODEBOOK only): int8 [n_pad][16].
+ * Rows n >= n of the padded last panel hold zero codes, zero scales and zero codebooks.
+ */
+typedef struct {
+    int32_t format;       /* w4a8_format                                   */
+    int32_t n;            /* output channels                               */
+    int32_t k;            /* input channels                                */
+    int32_t group;        /* 64 or 128; k % group == 0                     */
+    int32_t n_pad;        /* n rounded up to a multiple of W4A8_PANEL_ROWS */
+    int32_t meta_bytes;   /* 2 (SYM, CODEBOOK) or 4 (AFFINE)               */
+    uint64_t bytes;       /* total size of the packed buffer               */
+    uint64_t off_codes;
+    uint64_t off_meta;
+    uint64_t off_codebook;  /* 0 and unused unless CODEBOOK                */
+} w4a8_layout;
+
+/*
+ * Fill *L for a weight of `n` output channels and `k` input channels.  Host only, no device
+ * call.  Requires format in w4a8_format, group in {64, 128}, 1 <= n <= 2^24, group <= k <= 2^20,
+ * k % group == 0.  Source: "geistlib issue #500", section "Design" (load-time repack into the
+ * inner kernel's layout).
+ */
+w4a8_status w4a8_packed_layout(int32_t format, int32_t n, int32_t k, int32_t group,
+                               w4a8_layout *L);
+
+/*
+ * Repack canonical weights into the layout described by L (a pure permutation of nibbles plus
+ * the AFFINE re-encode u -> u XOR 8; scales, bias and codebook are copied).
+ *   codes      uint8 [n][k/2]: two codes per byte, the low nibble holds the even k
+ *   scales_f16 uint16 [n][k/group] (IEEE binary16 bit patterns)
+ *   bias_f16   uint16 [n][k/group] for AFFINE, else must be NULL
+ *   codebook   int8 [n][16] for CODEBOOK, else must be NULL
+ *   packed     L->bytes of device memory, written completely (padding included)
+ * Source: "cactus PR #697", follow-up commits on the interleaved lm_head and on the single
+ * runtime weight format (one packed format read by every kernel, built once at load).
+ */
+w4a8_status w4a8_pack_weights(const w4a8_layout *L, const uint8_t *codes,
+                              const uint16_t *scales_f16, const uint16_t *bias_f16,
+                              const int8_t *codebook, void *packed, void *stream);
+
+/*
+ * The activation prepass: optional rotation, then per-row per-group int8 quantization and
+ * group sums (definitions above).
+ *   x       fp32 [m][k] row-major (not modified)
+ *   xq      int8 [m][k] row-major
+ *   xs      fp32 [m][k/group]
+ *   xsum    int32 [m][k/group]
+ *   hadamard_block  0 (no rotation) or 128 (requires k % 128 == 0)
+ * m == 0 is a no-op (the pointers may then be NULL).  Bit-exact: the same fp32 operations in the same order for each value as
+ * the definition.  Sources: "cactus PR #697", section "Quantized matmul" (Hadamard + int8
+ * activation quantization as the GEMV's first phase; 128-wide groups of the orthogonal
+ * lm_head); "TensorFold PR #3215", section "What this changes" (group sums from a prepass).
+ */
+w4a8_status w4a8_prep(const float *x, int32_t m, int32_t k, int32_t group,
+                      int32_t hadamard_block, int8_t *xq, float *xs, int32_t *xsum,
+                      void *stream);
+
+/*
+ * Decode GEMV (one activation row): y[n] for n < L->n (definitions above).
+ *   xq int8 [k], xs fp32 [k/group], xsum int32 [k/group] from w4a8_prep with L->group
+ *   y  fp32 [L->n]
+ * Source: "cactus PR #697", section "Quantized matmul" (hybrid fused GEMV, M=1, streaming
+ * packed nibbles).
+ */
+w4a8_status w4a8_gemv(const w4a8_layout *L, const void *packed, const int8_t *xq,
+                      const float *xs, const int32_t *xsum, float *y, void *stream);
+
+/*
+ * Prefill GEMM: y[r][n] for r < m, n < L->n (definitions above).
+ *   xq int8 [m][k], xs fp32 [m][k/group], xsum int32 [m][k/group] from w4a8_prep
+ *   y  fp32 [m][L->n]
+ * m == 0 is a no-op (xq, xs, xsum and y may then be NULL).  Source: "cactus PR #697",
+ * section "Quantized matmul" (fused GEMM, M>1,
+ * raw int32 partials rescaled per tile); "geistlib issue #500" (native int8 GEMM for prefill).
+ */
+w4a8_status w4a8_gemm(const w4a8_layout *L, const void *packed, int32_t m, const int8_t *xq,
+                      const float *xs, const int32_t *xsum, float *y, void *stream);
+
+/*
+ * The exact int32 partials D[r][n][g] (definitions above) written by the same kernel code as
+ * the GEMV (m == 1) or the GEMM (m > 1), with the fp32 epilogue replaced by a store of D.
+ *   xsum  as from w4a8_prep (the AFFINE partial is recovered from the u - 8 codes as
+ *         D_u = D_(u-8) + 8 * xsum)
+ *   d     int32 [m][L->n][k/group]
+ * Source: "cactus PR #697", review snippet of the per-group leaf contract.
+ */
+w4a8_status w4a8_debug_partials(const w4a8_layout *L, const void *packed, int32_t m,
+                                const int8_t *xq, const int32_t *xsum, int32_t *d,
+                                void *stream);
+
+/* A static English name for a status code. */
+const char *w4a8_status_string(w4a8_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char *w4a8_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A8_H */

@@ -1,0 +1,130 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports every function the
+header declares, computes packed layouts, and rejects invalid arguments before any device call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from bit_group_quantized_act_amd import w4a8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a8.h")
+
+ERR_ARG, ERR_UNSUPPORTED, ERR_DEVICE = 1, 2, 3
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return w4a8.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(w4a8_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_binding_exports():
+    assert tuple(_declared_functions()) == w4a8.EXPORTS
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", w4a8.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.w4a8_status_string(s).decode() == w4a8.STATUS[s]
+    assert lib.w4a8_status_string(99).decode() == "unknown status"
+
+
+def test_layout_sizes():
+    L = w4a8.packed_layout(w4a8.SYM, 16384, 2048, 64)
+    assert (L.n_pad, L.meta_bytes) == (16384, 2)
+    assert L.off_codes == 0 and L.off_meta == 16384 * 2048 // 2
+    assert L.bytes == L.off_meta + 16384 * 32 * 2
+    L = w4a8.packed_layout(w4a8.AFFINE, 34816, 5120, 64)
+    assert L.meta_bytes == 4 and L.bytes == 34816 * 2560 + 34816 * 80 * 4
+    L = w4a8.packed_layout(w4a8.CODEBOOK, 1000, 1536, 128)
+    assert L.n_pad == 1024
+    assert L.off_meta == 1024 * 768 and L.off_codebook == L.off_meta + 1024 * 12 * 2
+    assert L.bytes == L.off_codebook + 1024 * 16
+    for off in (L.off_meta, L.off_codebook, L.bytes):
+        assert off % 256 == 0
+
+
+@pytest.mark.parametrize("args", [
+    (3, 64, 64, 64), (-1, 64, 64, 64), (0, 64, 96, 64), (0, 64, 64, 32), (0, 0, 64, 64),
+    (0, 64, 0, 64), (0, 64, 64 * 3, 128), (0, 1 << 25, 64, 64), (0, 64, (1 << 20) + 64, 64),
+])
+def test_layout_rejects(lib, args):
+    L = w4a8.Layout()
+    assert lib.w4a8_packed_layout(*args, ctypes.byref(L)) == ERR_ARG
+    assert lib.w4a8_last_error().decode() != ""
+
+
+def _fake(addr):
+    # host-side validation never dereferences device pointers; these values are never launched
+    return ctypes.c_void_p(addr)
+
+
+def test_invalid_calls_are_rejected_on_the_host(lib):
+    L = w4a8.packed_layout(w4a8.AFFINE, 128, 256, 64)
+    LP = ctypes.byref(L)
+    p, p16, p1 = _fake(1 << 20), _fake((1 << 20) + 16), _fake((1 << 20) + 1)
+    # pack: missing bias (affine), misaligned packed, stray codebook, bad layout
+    assert lib.w4a8_pack_weights(LP, p, p, None, None, p, None) == ERR_ARG
+    assert lib.w4a8_pack_weights(LP, p, p, p, None, p16, None) == ERR_ARG
+    assert lib.w4a8_pack_weights(LP, p, p, p, p, p, None) == ERR_ARG
+    bad = w4a8.Layout.from_buffer_copy(L)
+    bad.bytes += 1
+    assert lib.w4a8_pack_weights(ctypes.byref(bad), p, p, p, None, p, None) == ERR_ARG
+    assert "w4a8_packed_layout" in lib.w4a8_last_error().decode()
+    assert lib.w4a8_pack_weights(None, p, p, p, None, p, None) == ERR_ARG
+    # prep: m < 0, k % group, hadamard block, k % 128 with rotation, null and misaligned
+    assert lib.w4a8_prep(p, -1, 256, 64, 0, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_prep(p, 2, 200, 64, 0, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_prep(p, 2, 256, 64, 64, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_prep(p, 2, 320, 64, 128, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_prep(p, 2, 256, 96, 0, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_prep(None, 2, 256, 64, 0, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_prep(p, 2, 256, 64, 0, p1, p, p, None) == ERR_ARG
+    assert lib.w4a8_prep(p, 1 << 30, 1 << 20, 64, 0, p, p, p, None) == ERR_UNSUPPORTED
+    # m == 0 is a no-op that needs no pointers and no device
+    assert lib.w4a8_prep(None, 0, 256, 64, 0, None, None, None, None) == 0
+    assert lib.w4a8_gemm(LP, p, 0, None, None, None, None, None) == 0
+    # gemv / gemm / partials
+    assert lib.w4a8_gemv(LP, None, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_gemv(LP, p16, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_gemv(LP, p, p, p, p, p1, None) == ERR_ARG
+    assert lib.w4a8_gemm(LP, p, -3, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_gemm(LP, p, 4, p, None, p, p, None) == ERR_ARG
+    assert lib.w4a8_debug_partials(LP, p, 0, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_debug_partials(LP, p, 2, p, p, None, None) == ERR_ARG
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="checks the no-device path; would launch on a GPU")
+def test_valid_calls_without_a_device_report_device_error(lib):
+    L = w4a8.packed_layout(w4a8.SYM, 128, 256, 64)
+    p = _fake(1 << 20)
+    assert lib.w4a8_gemv(ctypes.byref(L), p, p, p, p, p, None) == ERR_DEVICE
+    assert lib.w4a8_prep(p, 2, 256, 64, 0, p, p, p, None) == ERR_DEVICE
+    assert lib.w4a8_last_error().decode() != ""
