@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A8 linear layer on one MI355X; prints one JSON line.
+
+A step is one pass of the per-token hot path over one batch of synthetic input: the activation
+prepass (w4a8_prep) and the linear (w4a8_gemv at one row, w4a8_gemm above).  The default workload
+is the decode GEMV of a gate_up-shaped layer: M=1, K=2048, N=16384, symmetric 4-bit weights in
+64-groups with fp16 scales, X ~ N(0,1) with 8 outlier channels x20.  The weights are packed once
+(load time, not in a step).
+
+Timing.  Weights are replicated into a pool of distinct packed buffers totalling >= 512 MiB (twice
+the 256 MiB last-level cache) and the steps walk through the pool, so every step streams its
+weights from HBM, as a decode does across layers.  The K timed steps are captured once into a HIP
+graph (launch gaps of a Python loop would otherwise dominate microsecond kernels) and replayed
+between stream synchronizations; W warmup steps run first.  The dominant kernel's average
+duration is timed the same way from a graph of linear-only launches over the same pool, bracketed
+by HIP events on the capturing stream.
+
+value      = weight bytes (nibbles + scales [+ bias] [+ codebook]) per step / step time (GB/s)
+roofline   = algorithmic bytes of one linear launch (weights + xq + xs + xsum + y) / its average
+             duration, against the 8 TB/s HBM peak (or int8 ops against the 5.0 POP/s dense MFMA
+             peak for a GEMM whose MFMA floor is above its HBM floor)
+cpu_baseline = the CPU oracle (plain C, OpenMP) on the same workload, repeated for about 10 s
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A8 linear: weight GB/s at M=1 and int8 TOPS at M≥128 (% of roofline)"
+HBM_PEAK_GBPS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+POOL_BYTES = 512 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="C2a",
+                    help="workload (C1, C2a, C2b, C3a, C3b, C4, C5a, C5b); default C2a")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--hot", action="store_true",
+                    help="reuse one weight buffer (measures cache, not HBM; labelled)")
+    return ap.parse_args()
+
+
+def workload_name(cfg):
+    from bit_group_quantized_act_amd import synth
+    kind = "decode GEMV" if cfg.m == 1 else "prefill GEMM"
+    rot = ", 128-block WHT" if cfg.hadamard else ""
+    return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
+            f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights{rot} (prep + linear per step)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (column-parallel "
+              "sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from bit_group_quantized_act_amd import synth, w4a8
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w4a8.load()   # fails loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    layer = synth.make(args.config)
+    cfg = layer["cfg"]
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    lay, packed0 = w4a8.pack(t(layer["codes"]), t(layer["scales"]), cfg.fmt, cfg.group,
+                             bias=t(layer["bias"]), codebook=t(layer["codebook"]))
+    wbytes = synth.weight_bytes(cfg)
+    alg_bytes = synth.algorithmic_bytes(cfg)
+    ops = synth.int_ops(cfg)
+    pool_n = 1 if args.hot else max(2, -(-POOL_BYTES // lay.bytes))
+    pool = [packed0] + [packed0.clone() for _ in range(pool_n - 1)]
+    x = t(layer["x"])
+    ng = cfg.k // cfg.group
+    xq = torch.empty((cfg.m, cfg.k), dtype=torch.int8, device=dev)
+    xs = torch.empty((cfg.m, ng), dtype=torch.float32, device=dev)
+    xsum = torch.empty((cfg.m, ng), dtype=torch.int32, device=dev)
+    y = torch.empty((cfg.m, cfg.n), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def linear(i):
+        pk = pool[i % pool_n]
+        if cfg.m == 1:
+            w4a8.gemv(lay, pk, xq[0], xs[0], xsum[0], out=y[0])
+        else:
+            w4a8.gemm(lay, pk, xq, xs, xsum, out=y)
+
+    def step(i):
+        w4a8.prep(x, cfg.group, cfg.hadamard, out=(xq, xs, xsum))
+        linear(i)
+
+    stream = torch.cuda.Stream()
+
+    def capture(fn, count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            fn(0)                      # one eager call on the capture stream before capturing
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(count):
+                    fn(i)
+        torch.cuda.synchronize()
+        return g
+
+    def timed(g):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    if args.warmup > 0:
+        gw = capture(step, args.warmup)
+        timed(gw)
+    g_steps = capture(step, args.steps)
+    ms_total = timed(g_steps)
+    ms_per_step = ms_total / args.steps
+
+    g_lin = capture(linear, args.steps)
+    timed(g_lin)                                    # warm the graph
+    us_linear = timed(g_lin) * 1000.0 / args.steps
+
+    value = wbytes / (ms_per_step * 1e-3) / 1e9
+    mfma_floor = ops / (INT8_PEAK_TOPS * 1e12)
+    hbm_floor = alg_bytes / (HBM_PEAK_GBPS * 1e9)
+    if cfg.m > 1 and mfma_floor > hbm_floor:
+        achieved = ops / (us_linear * 1e-6) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_PEAK_TOPS,
+                    unit="TFLOP/s", frac=round(achieved / INT8_PEAK_TOPS, 4))
+    else:
+        achieved = alg_bytes / (us_linear * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4))
+    roof.update(traffic=None, kernel="gemv" if cfg.m == 1 else "gemm",
+                kernel_us=round(us_linear, 3), alg_bytes_per_launch=alg_bytes,
+                int_ops_per_launch=ops,
+                tops=round(ops / (us_linear * 1e-6) / 1e12, 2))
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle                      # the CPU baseline leg (test infrastructure)
+        # a bounded sample: all rows, the first `cols` output columns (all of them when the
+        # layer is small), so that one repetition is at most ~2e9 multiply-adds
+        cols = cfg.n if cfg.m * cfg.n * cfg.k <= 2e9 else \
+            max(64, int(2e9 / (cfg.m * cfg.k)) // 64 * 64)
+        sub = lambda a: None if a is None else np.ascontiguousarray(a[:cols])
+        codes, scales, bias, cb = (sub(layer[key]) for key in ("codes", "scales", "bias",
+                                                                "codebook"))
+        sample_wbytes = wbytes * cols / cfg.n
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oq, os_, osum = oracle.prep(layer["x"], cfg.group, cfg.hadamard)
+            oracle.linear(cfg.fmt, codes, scales, oq, os_, osum, cfg.group, bias_f16=bias,
+                          codebook=cb, with_terms=False)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        what = "the whole workload" if cols == cfg.n else f"all {cfg.m} rows x the first {cols} columns"
+        cpu = dict(value=round(sample_wbytes * reps / el / 1e9, 3), unit="GB/s",
+                   cores=oracle.num_threads(), kind="oracle",
+                   sample=f"{what} of {cfg.name} (prep + linear), repeated {reps}x in "
+                          f"{el:.1f} s ({1e3 * el / reps:.2f} ms each)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": workload_name(cfg), "m": cfg.m, "k": cfg.k, "n": cfg.n,
+                   "group": cfg.group, "format": synth.FORMAT_NAMES[cfg.fmt],
+                   "weight_pool_buffers": pool_n, "hot_cache": bool(args.hot),
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

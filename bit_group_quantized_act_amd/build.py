@@ -5,6 +5,8 @@ Every translation unit is compiled in parallel, then linked into
   --offload-arch=gfx950                       MI355X only, no other targets
   -fhip-fp32-correctly-rounded-divide-sqrt    IEEE fp32 division (the prepass is bit-exact)
   -target-feature -packed-fp32-ops            no packed fp32 VALU instructions in device code
+  -amdgpu-mfma-vgpr-form                      MFMA results in VGPRs, where the VALU epilogue reads
+                                              them (no accumulator-register copies)
 """
 from __future__ import annotations
 
@@ -22,6 +24,7 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -6,53 +6,73 @@
 // native int8 GEMM removes the dequantize-to-fp32 intermediate of prefill); "TensorFold PR
 // #3215" (the affine bias term uses the per-row group sums from the prepass).
 //
-// MI355X design.  A workgroup owns one 64-row weight panel and 128 activation rows; each of its 4
-// wavefronts owns 32 activation rows x 64 output channels, i.e. two 32x32 int32 tiles.  For every
-// 64-wide k step the wavefront loads 32 activation bytes per lane straight from global (L2
-// resident: the activations are small and shared by every panel) and one 16-byte weight chunk per
-// lane per tile; the nibbles become int8 in registers (x16 for signed codes, a v_perm lookup for
-// codebooks) and feed two v_mfma_i32_32x32x32_i8 per tile.  Lane l holds activation row l%32 and
-// k half l/32; the packed chunk of lane l is panel row 32t + l%32 at chunk 2q + l/32, so each
-// tile's B fragment is two contiguous 512-byte runs.  The low nibbles of the four chunk dwords
-// pair with activation dwords 0,2,4,6 and the high nibbles with 1,3,5,7 (the same k on both
-// sides, which is all the MFMA needs).
-//
-// Epilogue per group: the coefficient tile xs[row]*sw[col] comes from one fp32 outer-product
-// MFMA (v_mfma_f32_32x32x1_2b, one block per tile), which also puts each coefficient in the same
-// lane/register as its int32 partial; the VALU then does one convert and one FMA per element.
-// The affine bias term sum_g (xs*xsum)[row][g] * (bw + 8 sw)[col][g] is an fp32 matrix product
-// over groups and runs on v_mfma_f32_32x32x2 (two groups per instruction).
+// MI355X design.
+//   Tiles.  A workgroup of 4 wavefronts owns BM activation rows (128 or 64) and BN = 128*64/BM
+//   output channels; each wavefront owns 64 rows x 32 channels as two 32x32 int32 tiles that
+//   share one weight fragment.  Lane l of a tile holds activation row l%32 and k half l/32; the
+//   weight chunk of lane l is panel row l%32 of the wavefront's 32 channels at chunk 2q + l/32,
+//   so a tile's weight fragment is two contiguous 512-byte runs of the packed panel.  The low
+//   nibbles of the chunk are k 0..15 and pair with the lane's first 16 activation bytes, the
+//   high nibbles k 16..31 with the next 16 (the same k on both sides, which is all the MFMA
+//   needs): two v_mfma_i32_32x32x32_i8 per tile per 64-wide k step, operands straight from the
+//   loads.
+//   Loads.  Every operand comes through buffer loads (SGPR descriptor, one fixed VGPR offset per
+//   lane, the k step in the SGPR offset), so the loop does no VALU address arithmetic, and rows
+//   past m read as zeros (the descriptor's range check) instead of being predicated.  Operands
+//   are prefetched in registers (weights 4 k steps ahead, activations 2) to hide latency.
+//   Epilogue per group.  The int32 partials of a group are converted once and accumulated with
+//   one FMA each.  Their coefficients xs[row] * sw[col] come from one fp32 outer-product MFMA
+//   (v_mfma_f32_32x32x1_2b: block t = tile t), which also lands each coefficient in the lane and
+//   register of its partial; the affine bias term xs*xsum[row] * (bw + 8 sw)[col] is a second
+//   outer product accumulated straight into its own fp32 tile on the matrix unit.  So the VALU
+//   does two operations per element and group, the matrix unit the rest.
+//   Signed codes (sym q, affine u-8) enter the MFMA as 16*q (nibble moved to the byte's top);
+//   the 1/16 is folded into sw, and affine's u = (u-8) + 8 is restored through the bias term.
 #include "w4a8_kernels.h"
+
+#include <type_traits>
 
 namespace w4a8 {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 32;
-constexpr int kBlockRows = kWaves * kRowsPerWave;   // activation rows per workgroup
+constexpr int kDepthA = 2;     // k steps of activation operands in flight per wavefront
+constexpr int kDepthB = 4;     // k steps of weight chunks in flight per wavefront
+constexpr uint32_t kRsrcCfg = 0x00020000u;
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint64_t bytes) {
+    const uint32_t n = bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : static_cast<uint32_t>(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, kRsrcCfg);
+}
+
+__device__ __forceinline__ v4i ld128(rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t ld32(rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t ld16(rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
 
 template <int FMT>
-__device__ __forceinline__ void unpack_b(uint4 v, uint4 cb, v4i &lo, v4i &hi) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+__device__ __forceinline__ void unpack_b(v4i v, uint4 cb, v4i &lo, v4i &hi) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+        const uint32_t w = static_cast<uint32_t>(v[j]);
         if (FMT == kFmtCodebook) {
-            lo[j] = static_cast<int>(cb_lo(w[j], cb));
-            hi[j] = static_cast<int>(cb_hi(w[j], cb));
+            lo[j] = static_cast<int>(cb_lo(w, cb));
+            hi[j] = static_cast<int>(cb_hi(w, cb));
         } else {
-            lo[j] = static_cast<int>(lo_x16(w[j]));
-            hi[j] = static_cast<int>(hi_x16(w[j]));
+            lo[j] = static_cast<int>(lo_x16(w));
+            hi[j] = static_cast<int>(hi_x16(w));
         }
     }
 }
 
-__device__ __forceinline__ float meta_scale(const uint8_t *meta, int64_t idx, int mb) {
-    if (mb == 4)
-        return half_bits_to_float(reinterpret_cast<const uint32_t *>(meta)[idx] & 0xFFFFu);
-    return half_bits_to_float(reinterpret_cast<const uint16_t *>(meta)[idx]);
-}
-
-template <int FMT, int G, bool PARTIALS>
+template <int FMT, int G, int BM, bool PARTIALS>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ packed,
                                                    const Geom geom, int m,
                                                    const int8_t *__restrict__ xq,
@@ -60,136 +80,197 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ p
                                                    const int *__restrict__ xsum,
                                                    float *__restrict__ y,
                                                    int *__restrict__ d) {
-    constexpr int kPairsPerGroup = G / 64;   // 64-wide k steps per group
+    constexpr int kWavesM = BM / 64;
+    constexpr int kWavesN = kWaves / kWavesM;
+    constexpr int kBN = 32 * kWavesN;
+    constexpr int kStepsPerGroup = G / 64;
+    static_assert(kDepthB == 4 && kDepthB % kDepthA == 0 && kDepthA % kStepsPerGroup == 0,
+                  "the unrolled loop body assumes 4 weight slots aligned to groups");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int p = blockIdx.x;
-    const int m_base = blockIdx.y * kBlockRows + wave * kRowsPerWave;
-    if (m_base >= m) return;   // whole wavefront past the last row (no barriers below)
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
+    const int r0 = blockIdx.y * BM + wm * 64;            // first activation row of the wavefront
+    const int c0 = blockIdx.x * kBN + wn * 32;           // first output channel of the wavefront
+    if (r0 >= m || c0 >= geom.n_pad) return;             // no barriers below
+    const int p = c0 / kPanelRows;                       // its panel
+    const int prow = (c0 % kPanelRows) + (lane & 31);    // lane's channel row inside the panel
     const int k = geom.k;
     const int kc = k / kChunkK;
     const int ng = k / G;
-    const int half = lane >> 5;          // k half of the MFMA operands
+    const int nsteps = k / 64;
+    const int half = lane >> 5;
     const int r32 = lane & 31;
-    const int a_row = m_base + r32;      // activation row this lane loads
-    const bool a_ok = a_row < m;
+    const int rows = min(m - r0, 64);                    // valid rows of the wavefront
+    constexpr int mb = (FMT == kFmtAffine) ? 4 : 2;       // meta bytes per channel and group
 
-    const uint4 *wpan = reinterpret_cast<const uint4 *>(packed + geom.off_codes) +
-                        (int64_t)p * kc * kPanelRows;
-    const uint8_t *meta = packed + geom.off_meta + (int64_t)p * ng * kPanelRows * geom.meta_bytes;
-    uint4 cb0 = make_uint4(0u, 0u, 0u, 0u), cb1 = cb0;
+    // descriptors rebased at the wavefront's rows / panel: offsets stay far below 2^31 and
+    // anything past the valid range reads as zero
+    const rsrc_t rq = make_rsrc(xq + (int64_t)r0 * k, (uint64_t)rows * k);
+    const rsrc_t rw = make_rsrc(packed + geom.off_codes + (int64_t)p * kc * 1024,
+                                (uint64_t)kc * 1024);
+    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (int64_t)p * ng * kPanelRows * mb,
+                                (uint64_t)ng * kPanelRows * mb);
+    const rsrc_t rs = make_rsrc(xs + (int64_t)r0 * ng, (uint64_t)rows * ng * 4);
+    const rsrc_t rx = make_rsrc(xsum + (int64_t)r0 * ng, (uint64_t)rows * ng * 4);
+
+    // per-lane constant offsets (bytes); the k step goes into the SGPR offset
+    const int a_off0 = r32 * k + 32 * half;                      // tile 0 row, chunk half
+    const int a_off1 = a_off0 + 32 * k;                          // tile 1 row
+    const int w_off = half * 1024 + prow * 16;
+    const int meta_off = prow * mb;
+    const int s_off = lane * ng * 4;                             // row r0 + lane (outer products)
+
+    uint4 cb = make_uint4(0u, 0u, 0u, 0u);
     if (FMT == kFmtCodebook) {
         const uint4 *cbp = reinterpret_cast<const uint4 *>(packed + geom.off_codebook);
-        cb0 = cbp[(int64_t)p * kPanelRows + r32];
-        cb1 = cbp[(int64_t)p * kPanelRows + 32 + r32];
+        cb = cbp[(int64_t)p * kPanelRows + prow];
     }
-    const uint4 *arow = reinterpret_cast<const uint4 *>(xq + (int64_t)(a_ok ? a_row : 0) * k);
 
-    v16f acc0 = {}, acc1 = {};
-    v16f bacc0 = {}, bacc1 = {};
-
-    for (int g = 0; g < ng; ++g) {
-        v16i d0 = {}, d1 = {};
-#pragma unroll
-        for (int q = 0; q < kPairsPerGroup; ++q) {
-            const int c = g * (G / kChunkK) + 2 * q + half;   // this lane's chunk
-            uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0;
-            if (a_ok) {
-                a0 = arow[2 * c];
-                a1 = arow[2 * c + 1];
-            }
-            const uint4 w0 = wpan[(int64_t)c * kPanelRows + r32];
-            const uint4 w1 = wpan[(int64_t)c * kPanelRows + 32 + r32];
-            const v4i alo = {static_cast<int>(a0.x), static_cast<int>(a0.z),
-                             static_cast<int>(a1.x), static_cast<int>(a1.z)};
-            const v4i ahi = {static_cast<int>(a0.y), static_cast<int>(a0.w),
-                             static_cast<int>(a1.y), static_cast<int>(a1.w)};
-            v4i blo0, bhi0, blo1, bhi1;
-            unpack_b<FMT>(w0, cb0, blo0, bhi0);
-            unpack_b<FMT>(w1, cb1, blo1, bhi1);
-            d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo, blo0, d0, 0, 0, 0);
-            d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi, bhi0, d0, 0, 0, 0);
-            d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo, blo1, d1, 0, 0, 0);
-            d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi, bhi1, d1, 0, 0, 0);
+    // Two load rings: activation operands (L2 resident) kDepthA steps ahead, weight chunks and
+    // their metadata (HBM) kDepthB steps ahead.  Loads are unconditional (past the last step the
+    // step index is clamped, re-reading it from cache), so the counted waits stay exact.
+    v4i ra[kDepthA][2][2];      // [slot][tile][16-byte half]: 32 activation bytes per tile
+    float rxs[kDepthA];         // activation scale of row r0 + lane, the step's group
+    int rxsum[kDepthA];         // its group sum (affine)
+    v4i rb[kDepthB];            // 16 weight bytes of the lane's channel
+    uint32_t rmeta[kDepthB];    // fp16 scale (| fp16 bias << 16) of the lane's channel
+    auto load_a = [&](int slot, int step) {
+        step = min(step, nsteps - 1);
+        const int soff = step * 64;
+        ra[slot][0][0] = ld128(rq, a_off0, soff);
+        ra[slot][0][1] = ld128(rq, a_off0 + 16, soff);
+        ra[slot][1][0] = ld128(rq, a_off1, soff);
+        ra[slot][1][1] = ld128(rq, a_off1 + 16, soff);
+        if (!PARTIALS) {
+            const int g = step / kStepsPerGroup;
+            rxs[slot] = __builtin_bit_cast(float, ld32(rs, s_off, g * 4));
+            if (FMT == kFmtAffine) rxsum[slot] = static_cast<int>(ld32(rx, s_off, g * 4));
         }
+    };
+    auto load_b = [&](int slot, int step) {
+        step = min(step, nsteps - 1);
+        rb[slot] = ld128(rw, w_off, step * 2048);
+        if (!PARTIALS) {
+            const int g = step / kStepsPerGroup;
+            rmeta[slot] = (mb == 4) ? ld32(rm, meta_off, g * kPanelRows * 4)
+                                    : ld16(rm, meta_off, g * kPanelRows * 2);
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < kDepthB; ++i) load_b(i, i);
+#pragma unroll
+    for (int i = 0; i < kDepthA; ++i) load_a(i, i);
+
+    v32f acc = {};     // [tile][16]: fp32 output accumulators (bias term included)
+    v16i dt0 = {}, dt1 = {};
+
+    // One 64-wide k step whose operands sit in ring slots I % kDepthA and I % kDepthB; both slots
+    // are refilled right after the MFMAs have taken their operands (the scheduling barriers keep
+    // the compiler from sinking those loads to the end of the loop).
+    auto body = [&](auto I, int s) {
+        constexpr int i = decltype(I)::value;
+        constexpr int sa = i % kDepthA, sb = i % kDepthB;
+        constexpr bool first = (i % kStepsPerGroup) == 0;
+        constexpr bool last = (i % kStepsPerGroup) == kStepsPerGroup - 1;
+        v4i blo, bhi;
+        unpack_b<FMT>(rb[sb], cb, blo, bhi);
+        const v16i z = {};
+        dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ra[sa][0][0], blo, first ? z : dt0, 0, 0, 0);
+        dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ra[sa][1][0], blo, first ? z : dt1, 0, 0, 0);
+        dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ra[sa][0][1], bhi, dt0, 0, 0, 0);
+        dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ra[sa][1][1], bhi, dt1, 0, 0, 0);
+        const uint32_t meta = rmeta[sb];
+        const float xs_l = rxs[sa];
+        const int xsum_l = rxsum[sa];
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(sb, s + kDepthB);
+        load_a(sa, s + kDepthA);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!last) return;
+        const int g = s / kStepsPerGroup;
 
         if (PARTIALS) {
-            // output element i of a tile: row 8*(i/4) + 4*half + i%4, column r32
+            // element e of tile t: row r0 + 32t + 8(e/4) + 4*half + e%4, channel c0 + r32
+            const int col = c0 + r32;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = m_base + 8 * (i / 4) + 4 * half + (i % 4);
-                if (row >= m) continue;
-                int s8 = 0;
-                if (FMT == kFmtAffine) s8 = 8 * xsum[(int64_t)row * ng + g];
-                int v0 = (FMT == kFmtCodebook) ? d0[i] : (d0[i] >> 4);
-                int v1 = (FMT == kFmtCodebook) ? d1[i] : (d1[i] >> 4);
-                const int64_t col0 = (int64_t)p * kPanelRows + r32;
-                if (col0 < geom.n) d[((int64_t)row * geom.n + col0) * ng + g] = v0 + s8;
-                if (col0 + 32 < geom.n) d[((int64_t)row * geom.n + col0 + 32) * ng + g] = v1 + s8;
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = r0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+                    const int raw = t ? dt1[e] : dt0[e];
+                    if (row >= m || col >= geom.n) continue;
+                    int v = (FMT == kFmtCodebook) ? raw : (raw >> 4);
+                    if (FMT == kFmtAffine) v += 8 * xsum[(int64_t)row * ng + g];
+                    d[((int64_t)row * geom.n + col) * ng + g] = v;
+                }
             }
-            continue;
+            return;
         }
 
-        // coefficient tiles: block t of the outer product is xs[rows] x sw16[cols 32t..32t+31];
-        // lane l supplies row l%32 for both blocks and panel column l (= 32t + l%32).
-        const float xs_a = a_ok ? xs[(int64_t)a_row * ng + g] : 0.0f;
-        float sw = meta_scale(meta, (int64_t)g * kPanelRows + lane, geom.meta_bytes);
-        if (FMT != kFmtCodebook) sw *= 0.0625f;   // the signed-code partials are 16x
-        v32f coef = {};
-        coef = __builtin_amdgcn_mfma_f32_32x32x1f32(xs_a, sw, coef, 0, 0, 0);
+        const float sw = half_bits_to_float(meta & 0xFFFFu);
+        const float sw16 = (FMT == kFmtCodebook) ? sw : sw * 0.0625f;
+        const v32f zf = {};
+        const v32f coef = __builtin_amdgcn_mfma_f32_32x32x1f32(xs_l, sw16, zf, 0, 0, 0);
+        if (FMT == kFmtAffine) {
+            // sum_g xs*xsum[row] * (bw + 8 sw)[col]: bias plus the u = (u-8) + 8 correction
+            const float b2 = fmaf(8.0f, sw, half_bits_to_float(meta >> 16));
+            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(xs_l * static_cast<float>(xsum_l), b2, acc,
+                                                       0, 0, 0);
+        }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            acc0[i] = fmaf(static_cast<float>(d0[i]), coef[i], acc0[i]);
-            acc1[i] = fmaf(static_cast<float>(d1[i]), coef[16 + i], acc1[i]);
+        for (int e = 0; e < 16; ++e) {
+            acc[e] = fmaf(static_cast<float>(dt0[e]), coef[e], acc[e]);
+            acc[16 + e] = fmaf(static_cast<float>(dt1[e]), coef[16 + e], acc[16 + e]);
         }
+    };
 
-        if (FMT == kFmtAffine && ((g & 1) || g == ng - 1)) {
-            // bias term for groups (g & ~1) + half: A = xs*xsum [row][group], B = bw + 8*sw
-            // [group][col]; a missing second group contributes zeros.
-            const int gg = (g & ~1) + half;
-            float a2 = 0.0f, b20 = 0.0f, b21 = 0.0f;
-            if (gg <= g) {
-                if (a_ok)
-                    a2 = xs[(int64_t)a_row * ng + gg] *
-                         static_cast<float>(xsum[(int64_t)a_row * ng + gg]);
-                const uint32_t *m4 = reinterpret_cast<const uint32_t *>(meta);
-                const uint32_t e0 = m4[(int64_t)gg * kPanelRows + r32];
-                const uint32_t e1 = m4[(int64_t)gg * kPanelRows + 32 + r32];
-                b20 = fmaf(8.0f, half_bits_to_float(e0 & 0xFFFFu), half_bits_to_float(e0 >> 16));
-                b21 = fmaf(8.0f, half_bits_to_float(e1 & 0xFFFFu), half_bits_to_float(e1 >> 16));
-            }
-            bacc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a2, b20, bacc0, 0, 0, 0);
-            bacc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a2, b21, bacc1, 0, 0, 0);
-        }
+    constexpr int kUnroll = kDepthB;   // a multiple of kDepthA and of the steps per group
+    int s0 = 0;
+    for (; s0 + kUnroll <= nsteps; s0 += kUnroll) {
+        body(std::integral_constant<int, 0>(), s0);
+        body(std::integral_constant<int, 1>(), s0 + 1);
+        body(std::integral_constant<int, 2>(), s0 + 2);
+        body(std::integral_constant<int, 3>(), s0 + 3);
     }
+    // remaining steps (fewer than kUnroll, a whole number of groups) use slots 0, 1, 2
+    if (s0 < nsteps) body(std::integral_constant<int, 0>(), s0);
+    if (s0 + 1 < nsteps) body(std::integral_constant<int, 1>(), s0 + 1);
+    if (s0 + 2 < nsteps) body(std::integral_constant<int, 2>(), s0 + 2);
     if (PARTIALS) return;
 
-    const int64_t col0 = (int64_t)p * kPanelRows + r32;
+    const int col = c0 + r32;
+    if (col >= geom.n) return;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int row = m_base + 8 * (i / 4) + 4 * half + (i % 4);
-        if (row >= m) continue;
-        float v0 = acc0[i], v1 = acc1[i];
-        if (FMT == kFmtAffine) {
-            v0 += bacc0[i];
-            v1 += bacc1[i];
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = r0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+            if (row >= m) continue;
+            y[(int64_t)row * geom.n + col] = acc[16 * t + e];
         }
-        if (col0 < geom.n) y[(int64_t)row * geom.n + col0] = v0;
-        if (col0 + 32 < geom.n) y[(int64_t)row * geom.n + col0 + 32] = v1;
     }
+}
+
+template <int FMT, int G, bool PARTIALS>
+hipError_t launch_bm(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
+                     const float *xs, const int32_t *xsum, float *y, int32_t *d,
+                     hipStream_t stream) {
+    if (m <= 64) {
+        const dim3 grid(static_cast<unsigned>(g.n_pad / 128 + (g.n_pad % 128 ? 1 : 0)), 1);
+        gemm_kernel<FMT, G, 64, PARTIALS><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y, d);
+    } else {
+        const dim3 grid(static_cast<unsigned>(g.n_pad / 64), static_cast<unsigned>((m + 127) / 128));
+        gemm_kernel<FMT, G, 128, PARTIALS><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y, d);
+    }
+    return hipGetLastError();
 }
 
 template <int FMT, bool PARTIALS>
 hipError_t launch_g(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
                     const float *xs, const int32_t *xsum, float *y, int32_t *d,
                     hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(g.n_pad / kPanelRows),
-                    static_cast<unsigned>((m + kBlockRows - 1) / kBlockRows));
-    if (g.group == 64)
-        gemm_kernel<FMT, 64, PARTIALS><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y, d);
-    else
-        gemm_kernel<FMT, 128, PARTIALS><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y, d);
-    return hipGetLastError();
+    if (g.group == 64) return launch_bm<FMT, 64, PARTIALS>(g, packed, m, xq, xs, xsum, y, d, stream);
+    return launch_bm<FMT, 128, PARTIALS>(g, packed, m, xq, xs, xsum, y, d, stream);
 }
 
 template <bool PARTIALS>

@@ -32,8 +32,8 @@ __device__ __forceinline__ int dot_chunk(uint4 v, const int *__restrict__ xc, ui
             lo = lo_x16(w[j]);
             hi = hi_x16(w[j]);
         }
-        acc = __builtin_amdgcn_sdot4(static_cast<int>(lo), xc[2 * j], acc, false);
-        acc = __builtin_amdgcn_sdot4(static_cast<int>(hi), xc[2 * j + 1], acc, false);
+        acc = __builtin_amdgcn_sdot4(static_cast<int>(lo), xc[j], acc, false);
+        acc = __builtin_amdgcn_sdot4(static_cast<int>(hi), xc[4 + j], acc, false);
     }
     return acc;
 }

@@ -6,7 +6,9 @@
 // every kernel, and it should be built once at load.  Here a panel is 64 output rows; its bytes
 // are ordered by 32-wide k chunk, then row, 16 bytes per (row, chunk).  A decode wavefront then
 // reads one contiguous KiB per chunk (one row per lane), and a 32x32x32 int8 MFMA B fragment for
-// 32 rows and a 64-wide k group is two contiguous 512-byte runs.
+// 32 rows and a 64-wide k group is two contiguous 512-byte runs.  Inside a chunk the low nibbles
+// of the four dwords hold k = 0..15 and the high nibbles k = 16..31, so each half of the chunk
+// pairs with one contiguous 16-byte run of activation codes (one MFMA operand, no shuffles).
 #include "w4a8_kernels.h"
 
 namespace w4a8 {
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t *__restri
             for (int i = 0; i < 16; ++i) b[i] = src[i];
             for (int j = 0; j < 4; ++j) {
                 for (int byte = 0; byte < 4; ++byte) {
-                    const int k_lo = 8 * j + byte, k_hi = 8 * j + 4 + byte;
+                    const int k_lo = 4 * j + byte, k_hi = 16 + 4 * j + byte;
                     const uint32_t q_lo = ((b[k_lo / 2] >> (4 * (k_lo & 1))) & 0xFu) ^ flip;
                     const uint32_t q_hi = ((b[k_hi / 2] >> (4 * (k_hi & 1))) & 0xFu) ^ flip;
                     w[j] |= (q_lo | (q_hi << 4)) << (8 * byte);

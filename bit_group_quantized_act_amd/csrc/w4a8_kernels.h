@@ -23,8 +23,8 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
 
-// ---- 4-bit unpack helpers (packed chunk format: dword j, byte b holds the code of k = 8j+b in
-// its low nibble and of k = 8j+4+b in its high nibble).
+// ---- 4-bit unpack helpers (packed chunk format: dword j, byte b holds the code of k = 4j+b in
+// its low nibble and of k = 16+4j+b in its high nibble).
 
 // Signed codes (SYM q, AFFINE u-8) as int8 bytes scaled by 16: the low nibbles moved to the top
 // of each byte, and the high nibbles masked in place.  16*q is exact in int8 for q in [-8, 7].

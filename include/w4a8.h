@@ -77,8 +77,8 @@ typedef enum {
  * Packed buffer (all offsets in bytes from the 256-byte aligned base, each section 256-aligned):
  *   codes     at off_codes: n_pad/64 panels; each panel is k/32 chunk columns; each chunk column
  *             is 64 rows x 16 bytes.  The 16 bytes of (row n, chunk c) hold the 32 codes of
- *             k = 32c .. 32c+31 as four dwords; dword j, byte b holds the code of k = 32c+8j+b in
- *             its low nibble and of k = 32c+8j+4+b in its high nibble.  SYM stores q's
+ *             k = 32c .. 32c+31 as four dwords; dword j, byte b holds the code of k = 32c+4j+b in
+ *             its low nibble and of k = 32c+16+4j+b in its high nibble.  SYM stores q's
  *             two's-complement nibble, AFFINE stores u XOR 8 (= u - 8 as a signed nibble),
  *             CODEBOOK stores the index.
  *   meta      at off_meta: per panel, per group g, per panel row: meta_bytes bytes.  SYM and

@@ -113,7 +113,7 @@ def test_pack_round_trip_and_padding():
             for b in range(4):
                 byte = chunks[:, :, :, 4 * j + b]                      # [panel, chunk, row]
                 lo, hi = byte & 0xF, byte >> 4
-                for kk, val in ((8 * j + b, lo), (8 * j + 4 + b, hi)):
+                for kk, val in ((4 * j + b, lo), (16 + 4 * j + b, hi)):
                     codes.reshape(npad // 64, 64, kc, 32)[:, :, :, kk] = val.transpose(0, 2, 1)
         assert not codes[n:].any()                 # padding rows are zero nibbles
         if cfg.fmt == synth.FMT_AFFINE:
