@@ -92,15 +92,15 @@ def main():
     x = t(layer["x"])
     ng = cfg.k // cfg.group
     xq = torch.empty((cfg.m, cfg.k), dtype=torch.int8, device=dev)
-    xs = torch.empty((cfg.m, ng), dtype=torch.float32, device=dev)
-    xsum = torch.empty((cfg.m, ng), dtype=torch.int32, device=dev)
+    xs = torch.empty((ng, cfg.m), dtype=torch.float32, device=dev)     # group-major
+    xsum = torch.empty((ng, cfg.m), dtype=torch.int32, device=dev)
     y = torch.empty((cfg.m, cfg.n), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def linear(i):
         pk = pool[i % pool_n]
         if cfg.m == 1:
-            w4a8.gemv(lay, pk, xq[0], xs[0], xsum[0], out=y[0])
+            w4a8.gemv(lay, pk, xq[0], xs, xsum, out=y[0])
         else:
             w4a8.gemm(lay, pk, xq, xs, xsum, out=y)
 

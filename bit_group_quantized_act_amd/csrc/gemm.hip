@@ -36,8 +36,10 @@ namespace w4a8 {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kDepthA = 2;     // k steps of activation operands in flight per wavefront
-constexpr int kDepthB = 4;     // k steps of weight chunks in flight per wavefront
+constexpr int kDepthB = 4;       // k steps of weight chunks in flight per wavefront
+constexpr int kStageSteps = 2;   // 64-wide k steps per LDS activation stage
+constexpr int kStageK = 64 * kStageSteps;
+constexpr int kLdsRow = kStageK + 16;   // padded LDS row of one activation stage (bytes)
 constexpr uint32_t kRsrcCfg = 0x00020000u;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -84,69 +86,76 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ p
     constexpr int kWavesN = kWaves / kWavesM;
     constexpr int kBN = 32 * kWavesN;
     constexpr int kStepsPerGroup = G / 64;
-    static_assert(kDepthB == 4 && kDepthB % kDepthA == 0 && kDepthA % kStepsPerGroup == 0,
-                  "the unrolled loop body assumes 4 weight slots aligned to groups");
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int mb = (FMT == kFmtAffine) ? 4 : 2;       // meta bytes per channel and group
+    static_assert(kDepthB == 4 && kStageSteps == 2 && kDepthB % kStepsPerGroup == 0,
+                  "the unrolled loop assumes 4 weight slots and 2-step LDS stages");
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kLdsRow];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / kWavesN, wn = wave % kWavesN;
-    const int r0 = blockIdx.y * BM + wm * 64;            // first activation row of the wavefront
+    const int m0 = blockIdx.y * BM;                      // first activation row of the workgroup
+    const int r0 = m0 + wm * 64;                         // first activation row of the wavefront
     const int c0 = blockIdx.x * kBN + wn * 32;           // first output channel of the wavefront
-    if (r0 >= m || c0 >= geom.n_pad) return;             // no barriers below
-    const int p = c0 / kPanelRows;                       // its panel
+    const bool active = r0 < m && c0 < geom.n_pad;       // wave-uniform
+    const int p = c0 / kPanelRows;                       // the wavefront's panel
     const int prow = (c0 % kPanelRows) + (lane & 31);    // lane's channel row inside the panel
     const int k = geom.k;
     const int kc = k / kChunkK;
     const int ng = k / G;
     const int nsteps = k / 64;
+    const int nstages = (nsteps + kStageSteps - 1) / kStageSteps;
     const int half = lane >> 5;
     const int r32 = lane & 31;
-    const int rows = min(m - r0, 64);                    // valid rows of the wavefront
-    constexpr int mb = (FMT == kFmtAffine) ? 4 : 2;       // meta bytes per channel and group
+    const int rows_wg = min(m - m0, BM);                 // valid rows of the workgroup
 
-    // descriptors rebased at the wavefront's rows / panel: offsets stay far below 2^31 and
-    // anything past the valid range reads as zero
-    const rsrc_t rq = make_rsrc(xq + (int64_t)r0 * k, (uint64_t)rows * k);
-    const rsrc_t rw = make_rsrc(packed + geom.off_codes + (int64_t)p * kc * 1024,
-                                (uint64_t)kc * 1024);
-    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (int64_t)p * ng * kPanelRows * mb,
-                                (uint64_t)ng * kPanelRows * mb);
-    const rsrc_t rs = make_rsrc(xs + (int64_t)r0 * ng, (uint64_t)rows * ng * 4);
-    const rsrc_t rx = make_rsrc(xsum + (int64_t)r0 * ng, (uint64_t)rows * ng * 4);
-
-    // per-lane constant offsets (bytes); the k step goes into the SGPR offset
-    const int a_off0 = r32 * k + 32 * half;                      // tile 0 row, chunk half
-    const int a_off1 = a_off0 + 32 * k;                          // tile 1 row
+    // Descriptors rebased at the workgroup's rows / the wavefront's panel: offsets stay far below
+    // 2^31 and anything past the valid range reads as zero without touching memory.
+    const rsrc_t rq = make_rsrc(xq + (int64_t)m0 * k, (uint64_t)rows_wg * k);
+    const uint8_t *wbase = active ? packed + geom.off_codes + (int64_t)p * kc * 1024 : packed;
+    const rsrc_t rw = make_rsrc(wbase, active ? (uint64_t)kc * 1024 : 0);
+    const uint8_t *mbase =
+        active ? packed + geom.off_meta + (int64_t)p * ng * kPanelRows * mb : packed;
+    const rsrc_t rm = make_rsrc(mbase, active ? (uint64_t)ng * kPanelRows * mb : 0);
     const int w_off = half * 1024 + prow * 16;
     const int meta_off = prow * mb;
-    const int s_off = lane * ng * 4;                             // row r0 + lane (outer products)
 
     uint4 cb = make_uint4(0u, 0u, 0u, 0u);
-    if (FMT == kFmtCodebook) {
+    if (FMT == kFmtCodebook && active) {
         const uint4 *cbp = reinterpret_cast<const uint4 *>(packed + geom.off_codebook);
         cb = cbp[(int64_t)p * kPanelRows + prow];
     }
 
-    // Two load rings: activation operands (L2 resident) kDepthA steps ahead, weight chunks and
-    // their metadata (HBM) kDepthB steps ahead.  Loads are unconditional (past the last step the
-    // step index is clamped, re-reading it from cache), so the counted waits stay exact.
-    v4i ra[kDepthA][2][2];      // [slot][tile][16-byte half]: 32 activation bytes per tile
-    float rxs[kDepthA];         // activation scale of row r0 + lane, the step's group
-    int rxsum[kDepthA];         // its group sum (affine)
+    // ---- activation tiles: global -> registers -> LDS, one 128-wide k stage at a time.  Thread
+    // t moves 16 bytes of row 32j + t/8 per j, eight threads per 128-byte row segment (whole
+    // cache lines); LDS rows are padded to 144 bytes so the MFMA-layout reads below (32 rows at
+    // one k offset per half wavefront) spread over the banks.
+    constexpr int kAJ = BM / 32;
+    v4i stage_regs[kAJ];
+    const int a_row = tid >> 3, a_piece = tid & 7;
+    auto stage_load = [&](int st) {
+        st = min(st, nstages - 1);
+#pragma unroll
+        for (int j = 0; j < kAJ; ++j)
+            stage_regs[j] = ld128(rq, (32 * j + a_row) * k + a_piece * 16, st * kStageK);
+    };
+    auto stage_store = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < kAJ; ++j)
+            *reinterpret_cast<v4i *>(&lds_a[buf][(32 * j + a_row) * kLdsRow + a_piece * 16]) =
+                stage_regs[j];
+    };
+    // LDS offset of this lane's MFMA operands: row wm*64 + 32t + r32, k bytes 32*half + 16*h of
+    // the 64-wide step
+    const int a_lds = (wm * 64 + r32) * kLdsRow + 32 * half;
+
+    // ---- weight chunks and per-group metadata: a ring of kDepthB k steps in registers
     v4i rb[kDepthB];            // 16 weight bytes of the lane's channel
     uint32_t rmeta[kDepthB];    // fp16 scale (| fp16 bias << 16) of the lane's channel
-    auto load_a = [&](int slot, int step) {
-        step = min(step, nsteps - 1);
-        const int soff = step * 64;
-        ra[slot][0][0] = ld128(rq, a_off0, soff);
-        ra[slot][0][1] = ld128(rq, a_off0 + 16, soff);
-        ra[slot][1][0] = ld128(rq, a_off1, soff);
-        ra[slot][1][1] = ld128(rq, a_off1 + 16, soff);
-        if (!PARTIALS) {
-            const int g = step / kStepsPerGroup;
-            rxs[slot] = __builtin_bit_cast(float, ld32(rs, s_off, g * 4));
-            if (FMT == kFmtAffine) rxsum[slot] = static_cast<int>(ld32(rx, s_off, g * 4));
-        }
-    };
+    float rxs[kDepthB];         // activation scale of row r0 + lane, the step's group
+    int rxsum[kDepthB];         // its group sum (affine)
+    const int x_off = (r0 + lane) * 4;                   // row of the outer-product operands
     auto load_b = [&](int slot, int step) {
         step = min(step, nsteps - 1);
         rb[slot] = ld128(rw, w_off, step * 2048);
@@ -154,37 +163,67 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ p
             const int g = step / kStepsPerGroup;
             rmeta[slot] = (mb == 4) ? ld32(rm, meta_off, g * kPanelRows * 4)
                                     : ld16(rm, meta_off, g * kPanelRows * 2);
+            // group-major scales and sums: one descriptor per group column, rows >= m read 0
+            const rsrc_t rs = make_rsrc(xs + (int64_t)g * m, (uint64_t)m * 4);
+            rxs[slot] = __builtin_bit_cast(float, ld32(rs, x_off, 0));
+            if (FMT == kFmtAffine) {
+                const rsrc_t rx = make_rsrc(xsum + (int64_t)g * m, (uint64_t)m * 4);
+                rxsum[slot] = static_cast<int>(ld32(rx, x_off, 0));
+            }
         }
     };
+
+    stage_load(0);
+    stage_store(0);
+    stage_load(1);
 #pragma unroll
     for (int i = 0; i < kDepthB; ++i) load_b(i, i);
-#pragma unroll
-    for (int i = 0; i < kDepthA; ++i) load_a(i, i);
+    __syncthreads();
 
     v32f acc = {};     // [tile][16]: fp32 output accumulators (bias term included)
     v16i dt0 = {}, dt1 = {};
 
-    // One 64-wide k step whose operands sit in ring slots I % kDepthA and I % kDepthB; both slots
-    // are refilled right after the MFMAs have taken their operands (the scheduling barriers keep
-    // the compiler from sinking those loads to the end of the loop).
+    // One 64-wide k step: weights from ring slot I, activations from LDS buffer (I/2)%2, which
+    // holds stage s/2.  The ring slot is refilled right after the MFMAs have taken their operands
+    // (the scheduling barriers keep the compiler from sinking those loads to the loop's end).
     auto body = [&](auto I, int s) {
         constexpr int i = decltype(I)::value;
-        constexpr int sa = i % kDepthA, sb = i % kDepthB;
+        constexpr int buf = (i / kStageSteps) % 2;
+        constexpr int sub = i % kStageSteps;
         constexpr bool first = (i % kStepsPerGroup) == 0;
         constexpr bool last = (i % kStepsPerGroup) == kStepsPerGroup - 1;
+        if (!active) return;
+        const uint8_t *ab = &lds_a[buf][a_lds + sub * 64];
+        const v4i a00 = *reinterpret_cast<const v4i *>(ab);
+        const v4i a01 = *reinterpret_cast<const v4i *>(ab + 16);
+        const v4i a10 = *reinterpret_cast<const v4i *>(ab + 32 * kLdsRow);
+        const v4i a11 = *reinterpret_cast<const v4i *>(ab + 32 * kLdsRow + 16);
         v4i blo, bhi;
-        unpack_b<FMT>(rb[sb], cb, blo, bhi);
+        unpack_b<FMT>(rb[i], cb, blo, bhi);
+        // everything read from ring slot i is consumed before the slot is refilled, so the refill
+        // loads can land in the same registers with no copies (and no early wait)
+        const uint32_t meta = rmeta[i];
+        const float sw = half_bits_to_float(meta & 0xFFFFu);
+        const float sw16 = (FMT == kFmtCodebook) ? sw : sw * 0.0625f;
+        const float xs_l = rxs[i];
+        float b2 = 0.0f, xs_sum = 0.0f;
+        if (FMT == kFmtAffine) {
+            b2 = fmaf(8.0f, sw, half_bits_to_float(meta >> 16));
+            xs_sum = xs_l * static_cast<float>(rxsum[i]);
+        }
         const v16i z = {};
-        dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ra[sa][0][0], blo, first ? z : dt0, 0, 0, 0);
-        dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ra[sa][1][0], blo, first ? z : dt1, 0, 0, 0);
-        dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ra[sa][0][1], bhi, dt0, 0, 0, 0);
-        dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ra[sa][1][1], bhi, dt1, 0, 0, 0);
-        const uint32_t meta = rmeta[sb];
-        const float xs_l = rxs[sa];
-        const int xsum_l = rxsum[sa];
+        dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a00, blo, first ? z : dt0, 0, 0, 0);
+        dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a10, blo, first ? z : dt1, 0, 0, 0);
+        dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a01, bhi, dt0, 0, 0, 0);
+        dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a11, bhi, dt1, 0, 0, 0);
+        // coefficient tiles xs[row] * sw16[col] for the group's epilogue
+        v32f coef = {};
+        if (!PARTIALS && last) {
+            const v32f zf = {};
+            coef = __builtin_amdgcn_mfma_f32_32x32x1f32(xs_l, sw16, zf, 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        load_b(sb, s + kDepthB);
-        load_a(sa, s + kDepthA);
+        load_b(i, s + kDepthB);
         __builtin_amdgcn_sched_barrier(0);
         if (!last) return;
         const int g = s / kStepsPerGroup;
@@ -200,22 +239,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ p
                     const int raw = t ? dt1[e] : dt0[e];
                     if (row >= m || col >= geom.n) continue;
                     int v = (FMT == kFmtCodebook) ? raw : (raw >> 4);
-                    if (FMT == kFmtAffine) v += 8 * xsum[(int64_t)row * ng + g];
+                    if (FMT == kFmtAffine) v += 8 * xsum[(int64_t)g * m + row];
                     d[((int64_t)row * geom.n + col) * ng + g] = v;
                 }
             }
             return;
         }
 
-        const float sw = half_bits_to_float(meta & 0xFFFFu);
-        const float sw16 = (FMT == kFmtCodebook) ? sw : sw * 0.0625f;
-        const v32f zf = {};
-        const v32f coef = __builtin_amdgcn_mfma_f32_32x32x1f32(xs_l, sw16, zf, 0, 0, 0);
         if (FMT == kFmtAffine) {
             // sum_g xs*xsum[row] * (bw + 8 sw)[col]: bias plus the u = (u-8) + 8 correction
-            const float b2 = fmaf(8.0f, sw, half_bits_to_float(meta >> 16));
-            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(xs_l * static_cast<float>(xsum_l), b2, acc,
-                                                       0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(xs_sum, b2, acc, 0, 0, 0);
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -223,20 +256,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ p
             acc[16 + e] = fmaf(static_cast<float>(dt1[e]), coef[16 + e], acc[16 + e]);
         }
     };
+    // After the two steps of stage st: publish stage st+1 (loaded one stage ago) into the buffer
+    // stage st-1 used, fetch stage st+2, and let every wavefront see the new buffer.
+    auto stage_end = [&](int st) {
+        stage_store((st + 1) & 1);
+        stage_load(st + 2);
+        __syncthreads();
+    };
 
-    constexpr int kUnroll = kDepthB;   // a multiple of kDepthA and of the steps per group
-    int s0 = 0;
-    for (; s0 + kUnroll <= nsteps; s0 += kUnroll) {
-        body(std::integral_constant<int, 0>(), s0);
-        body(std::integral_constant<int, 1>(), s0 + 1);
-        body(std::integral_constant<int, 2>(), s0 + 2);
-        body(std::integral_constant<int, 3>(), s0 + 3);
+    int s = 0;
+    for (; s + 4 <= nsteps; s += 4) {
+        body(std::integral_constant<int, 0>(), s);
+        body(std::integral_constant<int, 1>(), s + 1);
+        stage_end(s / 2);
+        body(std::integral_constant<int, 2>(), s + 2);
+        body(std::integral_constant<int, 3>(), s + 3);
+        stage_end(s / 2 + 1);
     }
-    // remaining steps (fewer than kUnroll, a whole number of groups) use slots 0, 1, 2
-    if (s0 < nsteps) body(std::integral_constant<int, 0>(), s0);
-    if (s0 + 1 < nsteps) body(std::integral_constant<int, 1>(), s0 + 1);
-    if (s0 + 2 < nsteps) body(std::integral_constant<int, 2>(), s0 + 2);
-    if (PARTIALS) return;
+    // remaining steps (fewer than 4; a whole number of groups)
+    if (s < nsteps) body(std::integral_constant<int, 0>(), s);
+    if (s + 1 < nsteps) body(std::integral_constant<int, 1>(), s + 1);
+    if (s + 2 < nsteps) {
+        stage_end(s / 2);
+        body(std::integral_constant<int, 2>(), s + 2);
+    }
+    if (PARTIALS || !active) return;
 
     const int col = c0 + r32;
     if (col >= geom.n) return;

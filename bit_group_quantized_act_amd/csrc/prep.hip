@@ -9,9 +9,10 @@
 //
 // Mapping: the [m][k] activations are treated as a flat array of float4 quads.  Thread t owns
 // floats 4t..4t+3; since k is a multiple of the group (64 or 128) and of the rotation block, a
-// group is G/4 consecutive lanes of one wavefront and never straddles rows, so the group index is
-// simply 4t/G and xs/xsum are written flat.  Loads are 16-byte coalesced (1 KiB per wavefront),
-// code stores 4 bytes per lane.
+// group is G/4 consecutive lanes of one wavefront and never straddles rows, so row * (k/G) +
+// group is simply 4t/G.  Loads are 16-byte coalesced (1 KiB per wavefront), code stores 4 bytes
+// per lane.  The scales and sums are stored group-major ([k/G][m]) so that a matmul epilogue reads
+// one group's values for consecutive rows as one contiguous run.
 //
 // Bit-exactness: every value goes through the same fp32 operations as the definition.  The
 // rotation's butterflies are the network with span 1, 2, ..., 64 (spans 1 and 2 inside a lane,
@@ -29,6 +30,7 @@ constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;
 
 template <int G, bool ROT>
 __global__ __launch_bounds__(256) void prep_kernel(const float4 *__restrict__ x, int64_t quads,
+                                                   int64_t m, int ng,
                                                    int *__restrict__ xq4,
                                                    float *__restrict__ xs,
                                                    int *__restrict__ xsum) {
@@ -84,9 +86,10 @@ __global__ __launch_bounds__(256) void prep_kernel(const float4 *__restrict__ x,
         xq4[t] = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) |
                  ((q[3] & 0xFF) << 24);
         if ((lane & (kLanesPerGroup - 1)) == 0) {
-            const int64_t f = t / kLanesPerGroup;
-            xs[f] = scale;
-            xsum[f] = sum;
+            const int64_t f = t / kLanesPerGroup;          // row * ng + group
+            const int64_t o = (f % ng) * m + f / ng;       // group-major: [group][row]
+            xs[o] = scale;
+            xsum[o] = sum;
         }
     }
 }
@@ -100,12 +103,13 @@ hipError_t launch_prep(const float *x, int64_t m, int k, int group, int hadamard
     const unsigned grid = static_cast<unsigned>((quads + 255) / 256);
     const float4 *x4 = reinterpret_cast<const float4 *>(x);
     int *q4 = reinterpret_cast<int *>(xq);
+    const int ng = k / group;
     if (group == 64) {
-        if (hadamard) prep_kernel<64, true><<<grid, 256, 0, stream>>>(x4, quads, q4, xs, xsum);
-        else prep_kernel<64, false><<<grid, 256, 0, stream>>>(x4, quads, q4, xs, xsum);
+        if (hadamard) prep_kernel<64, true><<<grid, 256, 0, stream>>>(x4, quads, m, ng, q4, xs, xsum);
+        else prep_kernel<64, false><<<grid, 256, 0, stream>>>(x4, quads, m, ng, q4, xs, xsum);
     } else {
-        if (hadamard) prep_kernel<128, true><<<grid, 256, 0, stream>>>(x4, quads, q4, xs, xsum);
-        else prep_kernel<128, false><<<grid, 256, 0, stream>>>(x4, quads, q4, xs, xsum);
+        if (hadamard) prep_kernel<128, true><<<grid, 256, 0, stream>>>(x4, quads, m, ng, q4, xs, xsum);
+        else prep_kernel<128, false><<<grid, 256, 0, stream>>>(x4, quads, m, ng, q4, xs, xsum);
     }
     return hipGetLastError();
 }

@@ -130,7 +130,11 @@ def pack(codes: torch.Tensor, scales: torch.Tensor, fmt: int, group: int, bias=N
 
 
 def prep(x: torch.Tensor, group: int, hadamard_block: int = 0, out=None):
-    """Activation prepass on fp32 [m, k] (or [k]).  Returns (xq int8, xs fp32, xsum int32)."""
+    """Activation prepass on fp32 [m, k] (or [k]).
+
+    Returns (xq int8 [m, k], xs fp32 [k/group, m], xsum int32 [k/group, m]); the scales and sums
+    are group-major.  For a 1-D x: (xq [k], xs [k/group], xsum [k/group]).
+    """
     squeeze = x.dim() == 1
     x2 = x.unsqueeze(0) if squeeze else x
     _dev(x2, torch.float32, "x")
@@ -138,14 +142,14 @@ def prep(x: torch.Tensor, group: int, hadamard_block: int = 0, out=None):
     ng = k // group if group else 0
     if out is None:
         xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
-        xs = torch.empty((m, ng), dtype=torch.float32, device=x.device)
-        xsum = torch.empty((m, ng), dtype=torch.int32, device=x.device)
+        xs = torch.empty((ng, m), dtype=torch.float32, device=x.device)
+        xsum = torch.empty((ng, m), dtype=torch.int32, device=x.device)
     else:
         xq, xs, xsum = out
     _check(load().w4a8_prep(_ptr(x2), m, k, group, hadamard_block, _ptr(xq), _ptr(xs),
                             _ptr(xsum), _stream(x.device)), "w4a8_prep")
     if squeeze:
-        return xq[0], xs[0], xsum[0]
+        return xq[0], xs.reshape(ng), xsum.reshape(ng)
     return xq, xs, xsum
 
 
@@ -158,7 +162,7 @@ def gemv(L: Layout, packed: torch.Tensor, xq, xs, xsum, out=None) -> torch.Tenso
 
 
 def gemm(L: Layout, packed: torch.Tensor, xq, xs, xsum, out=None) -> torch.Tensor:
-    """Prefill GEMM: m activation rows (xq int8 [m, k]) -> fp32 [m, n]."""
+    """Prefill GEMM: m activation rows (xq int8 [m, k], xs / xsum [k/group, m]) -> fp32 [m, n]."""
     m = xq.shape[0]
     y = out if out is not None else torch.empty((m, L.n), dtype=torch.float32,
                                                 device=packed.device)

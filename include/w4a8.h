@@ -21,12 +21,13 @@
  * Definitions used by every entry point (x is fp32 [m][k]; weight group == activation group G):
  *   rotation    (optional) normalized Walsh-Hadamard transform of each 128-wide block of a row,
  *               fp32 butterflies with span 1, 2, ..., 64, then one multiply by fp32(1/sqrt(128))
- *   xs[r][g]    = amax / 127 (IEEE fp32 divide), amax = max |x| over the group; 0 if amax == 0
+ *   xs[g][r]    = amax / 127 (IEEE fp32 divide), amax = max |x| over group g of row r; 0 if
+ *                 amax == 0 (stored group-major)
  *   xq[r][k]    = round-half-even(x / xs) (IEEE fp32 divide), in [-127, 127]; 0 if amax == 0
- *   xsum[r][g]  = sum of the group's xq (int32)
+ *   xsum[g][r]  = sum of the group's xq (int32, group-major)
  *   D[r][n][g]  = sum over k in group g of xq[r][k] * w[n][k]        (exact int32)
  *                 w = q in [-8, 7] (SYM), u in [0, 15] (AFFINE), codebook[n][j] (CODEBOOK)
- *   y[r][n]     = sum over g of xs[r][g] * ( sw[n][g] * D[r][n][g] + bw[n][g] * xsum[r][g] )
+ *   y[r][n]     = sum over g of xs[g][r] * ( sw[n][g] * D[r][n][g] + bw[n][g] * xsum[g][r] )
  *                 bw = 0 except AFFINE (dequantized weight = sw * u + bw); fp32 result
  *
  * Conventions
@@ -129,8 +130,8 @@ w4a8_status w4a8_pack_weights(const w4a8_layout *L, const uint8_t *codes,
  * group sums (definitions above).
  *   x       fp32 [m][k] row-major (not modified)
  *   xq      int8 [m][k] row-major
- *   xs      fp32 [m][k/group]
- *   xsum    int32 [m][k/group]
+ *   xs      fp32 [k/group][m] (group-major: one group's scales for all rows are contiguous)
+ *   xsum    int32 [k/group][m] (group-major)
  *   hadamard_block  0 (no rotation) or 128 (requires k % 128 == 0)
  * m == 0 is a no-op (the pointers may then be NULL).  Bit-exact: the same fp32 operations in the same order for each value as
  * the definition.  Sources: "cactus PR #697", section "Quantized matmul" (Hadamard + int8
@@ -153,7 +154,7 @@ w4a8_status w4a8_gemv(const w4a8_layout *L, const void *packed, const int8_t *xq
 
 /*
  * Prefill GEMM: y[r][n] for r < m, n < L->n (definitions above).
- *   xq int8 [m][k], xs fp32 [m][k/group], xsum int32 [m][k/group] from w4a8_prep
+ *   xq int8 [m][k], xs fp32 [k/group][m], xsum int32 [k/group][m] from w4a8_prep
  *   y  fp32 [m][L->n]
  * m == 0 is a no-op (xq, xs, xsum and y may then be NULL).  Source: "cactus PR #697",
  * section "Quantized matmul" (fused GEMM, M>1,

@@ -42,12 +42,13 @@ def _run(L, with_partials=True):
     x = to_dev(L["x"])
     xq, xs, xsum = w.prep(x, cfg.group, cfg.hadamard)
     if cfg.m == 1:
-        y = w.gemv(lay, packed, xq[0], xs[0], xsum[0])
+        y = w.gemv(lay, packed, xq[0], xs, xsum)
     else:
         y = w.gemm(lay, packed, xq, xs, xsum)
     d = w.debug_partials(lay, packed, xq, xsum) if with_partials else None
     torch.cuda.synchronize()
-    out = dict(xq=xq.cpu().numpy(), xs=xs.cpu().numpy(), xsum=xsum.cpu().numpy(),
+    # the library keeps scales and sums group-major [k/group, m]; the oracle row-major [m, k/group]
+    out = dict(xq=xq.cpu().numpy(), xs=xs.cpu().numpy().T.copy(), xsum=xsum.cpu().numpy().T.copy(),
                y=y.cpu().numpy().reshape(cfg.m, cfg.n))
     if d is not None:
         out["d"] = d.cpu().numpy()
@@ -160,8 +161,8 @@ def test_prep_edge_cases():
         torch.cuda.synchronize()
         oq, os_, osum = oracle.prep(x, group, had)
         assert np.array_equal(xq.cpu().numpy(), oq), (group, had)
-        assert np.array_equal(_bits(xs.cpu().numpy()), _bits(os_)), (group, had)
-        assert np.array_equal(xsum.cpu().numpy(), osum), (group, had)
+        assert np.array_equal(_bits(xs.cpu().numpy().T), _bits(os_)), (group, had)
+        assert np.array_equal(xsum.cpu().numpy().T, osum), (group, had)
     # m == 0 is a no-op
     e = torch.empty((0, 256), dtype=torch.float32, device="cuda:0")
     xq, xs, xsum = w.prep(e, 64)
@@ -173,8 +174,8 @@ def test_gemm_m0_is_noop():
     L = synth.make("C3a", full_range=True, m=2, n=64, k=128)
     lay, packed = _pack(L)
     z8 = torch.empty((0, 128), dtype=torch.int8, device="cuda:0")
-    zf = torch.empty((0, 2), dtype=torch.float32, device="cuda:0")
-    zi = torch.empty((0, 2), dtype=torch.int32, device="cuda:0")
+    zf = torch.empty((2, 0), dtype=torch.float32, device="cuda:0")
+    zi = torch.empty((2, 0), dtype=torch.int32, device="cuda:0")
     y = w.gemm(lay, packed, z8, zf, zi)
     torch.cuda.synchronize()
     assert y.shape == (0, 64)
