@@ -38,6 +38,37 @@ HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 POOL_BYTES = 512 << 20
 
+# HBM bytes per launch of the dominant kernel, read from two rocprofv3 --pmc passes (FETCH_SIZE,
+# WRITE_SIZE in KiB per dispatch) and scaled by what the same counters read for a plain 256 MiB
+# device copy (FETCH_SIZE reads half of the copy's bytes on this chip, WRITE_SIZE all of them).
+# Each entry holds the SHA-256 prefix of the kernel's sources when the counters were taken: once
+# the kernel changes, the figure no longer describes it and `traffic` is reported as null.
+KERNEL_SOURCES = {
+    "gemv": ["gemv.hip", "w4a8_kernels.h"],
+    "gemm": ["gemm.hip", "w4a8_kernels.h"],
+}
+TRAFFIC = {
+    "C2a": dict(kernel="gemv", source_sha="1be05b1a921478bf", fetch_kib=8747.29, write_kib=64.0,
+                fetch_factor=1.99979, write_factor=1.0),
+}
+
+
+def kernel_source_sha(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "bit_group_quantized_act_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg_name, kernel):
+    t = TRAFFIC.get(cfg_name)
+    if t is None or t["kernel"] != kernel or t["source_sha"] != kernel_source_sha(kernel):
+        return None
+    return int(round((t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"])
+                     * 1024))
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -50,7 +81,25 @@ def parse():
                     help="time budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--hot", action="store_true",
                     help="reuse one weight buffer (measures cache, not HBM; labelled)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the benchmark, run a plain device copy of this many MiB a "
+                         "few times (the known-size kernel that scales HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy of `mib` MiB, eight times over distinct buffers: a kernel that reads and
+    writes exactly `mib` MiB per launch, for scaling FETCH_SIZE / WRITE_SIZE counter readings."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib << 20
+    srcs = [torch.full((n,), i, dtype=torch.uint8, device=dev) for i in range(2)]
+    dsts = [torch.empty((n,), dtype=torch.uint8, device=dev) for _ in range(2)]
+    torch.cuda.synchronize()
+    for i in range(8):
+        dsts[i % 2].copy_(srcs[(i // 2) % 2])
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 8}), flush=True)
 
 
 def workload_name(cfg):
@@ -75,6 +124,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
+        return
     w4a8.load()   # fails loudly if the HIP library is not built
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -154,7 +206,8 @@ def main():
         achieved = alg_bytes / (us_linear * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4))
-    roof.update(traffic=None, kernel="gemv" if cfg.m == 1 else "gemm",
+    kname = "gemv" if cfg.m == 1 else "gemm"
+    roof.update(traffic=measured_traffic(cfg.name, kname), kernel=kname,
                 kernel_us=round(us_linear, 3), alg_bytes_per_launch=alg_bytes,
                 int_ops_per_launch=ops,
                 tops=round(ops / (us_linear * 1e-6) / 1e12, 2))
