@@ -7,25 +7,33 @@
 // #3215" (the affine bias term uses the per-row group sums from the prepass).
 //
 // MI355X design.
-//   Tiles.  A workgroup of 4 wavefronts owns BM activation rows (128 or 64) and BN = 128*64/BM
-//   output channels; each wavefront owns 64 rows x 32 channels as two 32x32 int32 tiles that
-//   share one weight fragment.  Lane l of a tile holds activation row l%32 and k half l/32; the
-//   weight chunk of lane l is panel row l%32 of the wavefront's 32 channels at chunk 2q + l/32,
-//   so a tile's weight fragment is two contiguous 512-byte runs of the packed panel.  The low
-//   nibbles of the chunk are k 0..15 and pair with the lane's first 16 activation bytes, the
-//   high nibbles k 16..31 with the next 16 (the same k on both sides, which is all the MFMA
-//   needs): two v_mfma_i32_32x32x32_i8 per tile per 64-wide k step, operands straight from the
-//   loads.
+//   Tiles.  A workgroup of 4 wavefronts owns 64 activation rows and 128 output channels; each
+//   wavefront owns all 64 rows x its own 32 channels as two 32x32 int32 tiles that share one
+//   weight fragment, so no two wavefronts load the same weight bytes.  Lane l of a tile holds
+//   activation row l%32 and k half l/32; the weight chunk of lane l is panel row l%32 of the
+//   wavefront's 32 channels at chunk 2q + l/32, so a tile's weight fragment is two contiguous
+//   512-byte runs of the packed panel.  The low nibbles of the chunk are k 0..15 and pair with
+//   the lane's first 16 activation bytes, the high nibbles k 16..31 with the next 16 (the same k
+//   on both sides, which is all the MFMA needs): two v_mfma_i32_32x32x32_i8 per tile per 64-wide
+//   k step.  Workgroups are numbered so that each XCD (one L2) gets a contiguous run of tiles,
+//   with the M tiles of one channel block adjacent: they share its weights in that L2.
 //   Loads.  Every operand comes through buffer loads (SGPR descriptor, one fixed VGPR offset per
-//   lane, the k step in the SGPR offset), so the loop does no VALU address arithmetic, and rows
-//   past m read as zeros (the descriptor's range check) instead of being predicated.  Operands
-//   are prefetched in registers (weights 4 k steps ahead, activations 2) to hide latency.
-//   Epilogue per group.  The int32 partials of a group are converted once and accumulated with
-//   one FMA each.  Their coefficients xs[row] * sw[col] come from one fp32 outer-product MFMA
-//   (v_mfma_f32_32x32x1_2b: block t = tile t), which also lands each coefficient in the lane and
-//   register of its partial; the affine bias term xs*xsum[row] * (bw + 8 sw)[col] is a second
-//   outer product accumulated straight into its own fp32 tile on the matrix unit.  So the VALU
-//   does two operations per element and group, the matrix unit the rest.
+//   lane, the k step in the SGPR offset), so rows past m read as zeros (the descriptor's range
+//   check) instead of being predicated.  Activations are staged through LDS in 128-wide k
+//   stages from three register sets loaded three stages ahead (three LDS buffers, one barrier
+//   per stage); weight chunks and per-group metadata are loaded six k steps ahead.  Loads
+//   complete in issue order, so the two leads are matched (a wait for one load never forces a
+//   much younger one), and no load sits behind a branch (the compiler's waits would otherwise
+//   drain every load in flight): this keeps ~48 KiB of weights in flight per CU.
+//   Software pipeline.  The epilogue of group g-1 runs on the VALU, tile by tile, between the
+//   MFMAs of group g: the int32 partials of a tile are converted and accumulated with one FMA
+//   each, and that tile's MFMAs for group g are issued right after its last read.  The FMA
+//   coefficients xs[row] * sw[col] come from one fp32 outer-product MFMA
+//   (v_mfma_f32_32x32x1_2b: block t = tile t) issued as soon as the previous group's
+//   coefficients are consumed, which also lands each coefficient in the lane and register of
+//   its partial.  The affine bias term xs*xsum[row] * (bw + 8 sw)[col] is a second outer
+//   product accumulated on the matrix unit into its own fp32 tile.  So per element and group the
+//   VALU does two operations and the matrix unit the rest.
 //   Signed codes (sym q, affine u-8) enter the MFMA as 16*q (nibble moved to the byte's top);
 //   the 1/16 is folded into sw, and affine's u = (u-8) + 8 is restored through the bias term.
 #include "w4a8_kernels.h"
@@ -35,11 +43,13 @@
 namespace w4a8 {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kDepthB = 4;       // k steps of weight chunks in flight per wavefront
-constexpr int kStageSteps = 2;   // 64-wide k steps per LDS activation stage
+constexpr int BM = 64;                     // activation rows per workgroup
+constexpr int kBN = 128;                   // output channels per workgroup (4 wavefronts x 32)
+constexpr int kStageSteps = 2;             // 64-wide k steps per LDS activation stage
 constexpr int kStageK = 64 * kStageSteps;
-constexpr int kLdsRow = kStageK + 16;   // padded LDS row of one activation stage (bytes)
+constexpr int kLdsRow = kStageK + 16;      // padded LDS row of one activation stage (bytes)
+constexpr int kSets = 3;                   // activation stages in flight (registers and LDS)
+constexpr int kLead = kSets * kStageSteps; // k steps of weights and metadata loaded ahead
 constexpr uint32_t kRsrcCfg = 0x00020000u;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -74,40 +84,48 @@ __device__ __forceinline__ void unpack_b(v4i v, uint4 cb, v4i &lo, v4i &hi) {
     }
 }
 
-template <int FMT, int G, int BM, bool PARTIALS>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ packed,
-                                                   const Geom geom, int m,
-                                                   const int8_t *__restrict__ xq,
-                                                   const float *__restrict__ xs,
-                                                   const int *__restrict__ xsum,
-                                                   float *__restrict__ y,
-                                                   int *__restrict__ d) {
-    constexpr int kWavesM = BM / 64;
-    constexpr int kWavesN = kWaves / kWavesM;
-    constexpr int kBN = 32 * kWavesN;
-    constexpr int kStepsPerGroup = G / 64;
-    constexpr int mb = (FMT == kFmtAffine) ? 4 : 2;       // meta bytes per channel and group
-    static_assert(kDepthB == 4 && kStageSteps == 2 && kDepthB % kStepsPerGroup == 0,
-                  "the unrolled loop assumes 4 weight slots and 2-step LDS stages");
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kLdsRow];
+template <int FMT, int G, bool PARTIALS>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict__ packed,
+                                                      const Geom geom, int m,
+                                                      const int8_t *__restrict__ xq,
+                                                      const float *__restrict__ xs,
+                                                      const int *__restrict__ xsum,
+                                                      float *__restrict__ y,
+                                                      int *__restrict__ d) {
+    constexpr int SPG = G / 64;                          // 64-wide k steps per group
+    constexpr int kRingG = kLead / SPG;                  // groups of metadata loaded ahead
+    constexpr int kMB = (FMT == kFmtAffine) ? 4 : 2;     // meta bytes per channel and group
+    constexpr int kAJ = BM / 32;                         // 16-byte staging loads per thread
+    static_assert(kLead == 6 && kStageSteps == 2 && kLead % SPG == 0,
+                  "the unrolled loop covers three stages of two k steps");
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kSets][BM * kLdsRow];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / kWavesN, wn = wave % kWavesN;
-    const int m0 = blockIdx.y * BM;                      // first activation row of the workgroup
-    const int r0 = m0 + wm * 64;                         // first activation row of the wavefront
-    const int c0 = blockIdx.x * kBN + wn * 32;           // first output channel of the wavefront
+    const int wn = wave;
+
+    // Tile of this workgroup.  When the tile count is a multiple of the 8 XCDs, workgroup b runs
+    // on XCD b % 8 and takes tile (b % 8) * (T / 8) + b / 8, so each XCD walks a contiguous run.
+    const int tiles_m = (m + BM - 1) / BM;
+    const int tiles_n = (geom.n_pad + kBN - 1) / kBN;
+    const int ntiles = tiles_m * tiles_n;
+    int bid = blockIdx.x;
+    if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+    const int mt = bid % tiles_m, nt = bid / tiles_m;
+
+    const int m0 = mt * BM;                              // first activation row of the workgroup
+    const int r0 = m0;                                   // first activation row of the wavefront
+    const int c0 = nt * kBN + wn * 32;                   // first output channel of the wavefront
     const bool active = r0 < m && c0 < geom.n_pad;       // wave-uniform
     const int p = c0 / kPanelRows;                       // the wavefront's panel
-    const int prow = (c0 % kPanelRows) + (lane & 31);    // lane's channel row inside the panel
+    const int half = lane >> 5;
+    const int r32 = lane & 31;
+    const int prow = (c0 % kPanelRows) + r32;            // lane's channel row inside the panel
     const int k = geom.k;
     const int kc = k / kChunkK;
     const int ng = k / G;
     const int nsteps = k / 64;
-    const int nstages = (nsteps + kStageSteps - 1) / kStageSteps;
-    const int half = lane >> 5;
-    const int r32 = lane & 31;
     const int rows_wg = min(m - m0, BM);                 // valid rows of the workgroup
 
     // Descriptors rebased at the workgroup's rows / the wavefront's panel: offsets stay far below
@@ -116,10 +134,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ p
     const uint8_t *wbase = active ? packed + geom.off_codes + (int64_t)p * kc * 1024 : packed;
     const rsrc_t rw = make_rsrc(wbase, active ? (uint64_t)kc * 1024 : 0);
     const uint8_t *mbase =
-        active ? packed + geom.off_meta + (int64_t)p * ng * kPanelRows * mb : packed;
-    const rsrc_t rm = make_rsrc(mbase, active ? (uint64_t)ng * kPanelRows * mb : 0);
+        active ? packed + geom.off_meta + (int64_t)p * ng * kPanelRows * kMB : packed;
+    const rsrc_t rm = make_rsrc(mbase, active ? (uint64_t)ng * kPanelRows * kMB : 0);
     const int w_off = half * 1024 + prow * 16;
-    const int meta_off = prow * mb;
+    const int meta_off = prow * kMB;
+    const int x_off = (r0 + lane) * 4;                   // row of the outer-product operands
 
     uint4 cb = make_uint4(0u, 0u, 0u, 0u);
     if (FMT == kFmtCodebook && active) {
@@ -127,160 +146,162 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ p
         cb = cbp[(int64_t)p * kPanelRows + prow];
     }
 
-    // ---- activation tiles: global -> registers -> LDS, one 128-wide k stage at a time.  Thread
-    // t moves 16 bytes of row 32j + t/8 per j, eight threads per 128-byte row segment (whole
-    // cache lines); LDS rows are padded to 144 bytes so the MFMA-layout reads below (32 rows at
-    // one k offset per half wavefront) spread over the banks.
-    constexpr int kAJ = BM / 32;
-    v4i stage_regs[kAJ];
+    // ---- activation stages: global -> register set -> LDS.  Thread t moves 16 bytes of row
+    // 32j + t/8 per j, eight threads per 128-byte row segment (whole cache lines).  LDS rows are
+    // padded to 144 bytes so the MFMA-layout reads (32 rows at one k offset per half wavefront)
+    // spread over the banks.
+    v4i stage_regs[kSets][kAJ];
     const int a_row = tid >> 3, a_piece = tid & 7;
-    auto stage_load = [&](int st) {
-        st = min(st, nstages - 1);
+    // Every load in the main loop is issued unconditionally (a stage or step past the end reads
+    // zeros through the range check, or a clamped valid address): the waits the compiler places
+    // for one load then count exactly the loads issued after it, which keeps the deep prefetch
+    // in flight.  A load behind a branch would make those waits drain everything.
+    auto stage_load = [&](auto SET, int st) {
+        constexpr int set = decltype(SET)::value;
 #pragma unroll
         for (int j = 0; j < kAJ; ++j)
-            stage_regs[j] = ld128(rq, (32 * j + a_row) * k + a_piece * 16, st * kStageK);
+            stage_regs[set][j] = ld128(rq, (32 * j + a_row) * k + a_piece * 16, st * kStageK);
     };
-    auto stage_store = [&](int buf) {
+    auto stage_store = [&](auto SET) {
+        constexpr int set = decltype(SET)::value;
 #pragma unroll
         for (int j = 0; j < kAJ; ++j)
-            *reinterpret_cast<v4i *>(&lds_a[buf][(32 * j + a_row) * kLdsRow + a_piece * 16]) =
-                stage_regs[j];
+            *reinterpret_cast<v4i *>(&lds_a[set][(32 * j + a_row) * kLdsRow + a_piece * 16]) =
+                stage_regs[set][j];
     };
-    // LDS offset of this lane's MFMA operands: row wm*64 + 32t + r32, k bytes 32*half + 16*h of
+    // LDS offset of this lane's MFMA operands: row 32t + r32, k bytes 32*half + 16*h of
     // the 64-wide step
-    const int a_lds = (wm * 64 + r32) * kLdsRow + 32 * half;
+    const int a_lds = r32 * kLdsRow + 32 * half;
 
-    // ---- weight chunks and per-group metadata: a ring of kDepthB k steps in registers
-    v4i rb[kDepthB];            // 16 weight bytes of the lane's channel
-    uint32_t rmeta[kDepthB];    // fp16 scale (| fp16 bias << 16) of the lane's channel
-    float rxs[kDepthB];         // activation scale of row r0 + lane, the step's group
-    int rxsum[kDepthB];         // its group sum (affine)
-    const int x_off = (r0 + lane) * 4;                   // row of the outer-product operands
-    auto load_b = [&](int slot, int step) {
-        step = min(step, nsteps - 1);
-        rb[slot] = ld128(rw, w_off, step * 2048);
+    // ---- weight chunks (one k step each) and per-group metadata, loaded kLead steps ahead
+    v4i rb[kLead];              // 16 weight bytes of the lane's channel
+    uint32_t rmeta[kRingG];     // fp16 scale (| fp16 bias << 16) of the lane's channel
+    float rxs[kRingG];          // activation scale of row r0 + lane, the group
+    int rxsum[kRingG];          // its group sum (affine)
+    auto load_b = [&](int slot, int step) { rb[slot] = ld128(rw, w_off, step * 2048); };
+    auto load_meta = [&](int slot, int g) {
+        g = min(g, ng - 1);
         if (!PARTIALS) {
-            const int g = step / kStepsPerGroup;
-            rmeta[slot] = (mb == 4) ? ld32(rm, meta_off, g * kPanelRows * 4)
-                                    : ld16(rm, meta_off, g * kPanelRows * 2);
+            rmeta[slot] = (kMB == 4) ? ld32(rm, meta_off, g * kPanelRows * 4)
+                                     : ld16(rm, meta_off, g * kPanelRows * 2);
             // group-major scales and sums: one descriptor per group column, rows >= m read 0
             const rsrc_t rs = make_rsrc(xs + (int64_t)g * m, (uint64_t)m * 4);
             rxs[slot] = __builtin_bit_cast(float, ld32(rs, x_off, 0));
-            if (FMT == kFmtAffine) {
-                const rsrc_t rx = make_rsrc(xsum + (int64_t)g * m, (uint64_t)m * 4);
-                rxsum[slot] = static_cast<int>(ld32(rx, x_off, 0));
-            }
+        }
+        if (FMT == kFmtAffine && !PARTIALS) {
+            const rsrc_t rx = make_rsrc(xsum + (int64_t)g * m, (uint64_t)m * 4);
+            rxsum[slot] = static_cast<int>(ld32(rx, x_off, 0));
         }
     };
 
-    stage_load(0);
-    stage_store(0);
-    stage_load(1);
+    // prologue: stages 0..2 in flight, then weights and metadata, publish stage 0, start 3
+    stage_load(std::integral_constant<int, 0>(), 0);
+    stage_load(std::integral_constant<int, 1>(), 1);
+    stage_load(std::integral_constant<int, 2>(), 2);
 #pragma unroll
-    for (int i = 0; i < kDepthB; ++i) load_b(i, i);
+    for (int i = 0; i < kLead; ++i) load_b(i, i);
+#pragma unroll
+    for (int i = 0; i < kRingG; ++i) load_meta(i, i);
+    stage_store(std::integral_constant<int, 0>());
     __syncthreads();
+    stage_load(std::integral_constant<int, 0>(), 3);
 
-    v32f acc = {};     // [tile][16]: fp32 output accumulators (bias term included)
-    v16i dt0 = {}, dt1 = {};
+    v16i dt0 = {}, dt1 = {};   // int32 partials of the current group, tiles 0 and 1
+    v32f coef = {};            // [tile][16]: xs[row] * sw16[col] of the group held in dt0/dt1
+    v32f acc = {};             // [tile][16]: fp32 outputs
+    v32f bacc = {};            // [tile][16]: affine bias term
 
-    // One 64-wide k step: weights from ring slot I, activations from LDS buffer (I/2)%2, which
-    // holds stage s/2.  The ring slot is refilled right after the MFMAs have taken their operands
-    // (the scheduling barriers keep the compiler from sinking those loads to the loop's end).
-    auto body = [&](auto I, int s) {
-        constexpr int i = decltype(I)::value;
-        constexpr int buf = (i / kStageSteps) % 2;
-        constexpr int sub = i % kStageSteps;
-        constexpr bool first = (i % kStepsPerGroup) == 0;
-        constexpr bool last = (i % kStepsPerGroup) == kStepsPerGroup - 1;
-        if (!active) return;
-        const uint8_t *ab = &lds_a[buf][a_lds + sub * 64];
-        const v4i a00 = *reinterpret_cast<const v4i *>(ab);
-        const v4i a01 = *reinterpret_cast<const v4i *>(ab + 16);
-        const v4i a10 = *reinterpret_cast<const v4i *>(ab + 32 * kLdsRow);
-        const v4i a11 = *reinterpret_cast<const v4i *>(ab + 32 * kLdsRow + 16);
-        v4i blo, bhi;
-        unpack_b<FMT>(rb[i], cb, blo, bhi);
-        // everything read from ring slot i is consumed before the slot is refilled, so the refill
-        // loads can land in the same registers with no copies (and no early wait)
-        const uint32_t meta = rmeta[i];
-        const float sw = half_bits_to_float(meta & 0xFFFFu);
-        const float sw16 = (FMT == kFmtCodebook) ? sw : sw * 0.0625f;
-        const float xs_l = rxs[i];
-        float b2 = 0.0f, xs_sum = 0.0f;
-        if (FMT == kFmtAffine) {
-            b2 = fmaf(8.0f, sw, half_bits_to_float(meta >> 16));
-            xs_sum = xs_l * static_cast<float>(rxsum[i]);
-        }
-        const v16i z = {};
-        dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a00, blo, first ? z : dt0, 0, 0, 0);
-        dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a10, blo, first ? z : dt1, 0, 0, 0);
-        dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a01, bhi, dt0, 0, 0, 0);
-        dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a11, bhi, dt1, 0, 0, 0);
-        // coefficient tiles xs[row] * sw16[col] for the group's epilogue
-        v32f coef = {};
-        if (!PARTIALS && last) {
-            const v32f zf = {};
-            coef = __builtin_amdgcn_mfma_f32_32x32x1f32(xs_l, sw16, zf, 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        load_b(i, s + kDepthB);
-        __builtin_amdgcn_sched_barrier(0);
-        if (!last) return;
-        const int g = s / kStepsPerGroup;
-
+    // The previous group's epilogue for tile T: convert and accumulate (or store the partials).
+    auto finish_tile = [&](auto TT, int g) {
+        constexpr int t = decltype(TT)::value;
+        const v16i &dt = t ? dt1 : dt0;
         if (PARTIALS) {
             // element e of tile t: row r0 + 32t + 8(e/4) + 4*half + e%4, channel c0 + r32
             const int col = c0 + r32;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int e = 0; e < 16; ++e) {
+                const int row = r0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+                if (row >= m || col >= geom.n) continue;
+                int v = (FMT == kFmtCodebook) ? dt[e] : (dt[e] >> 4);
+                if (FMT == kFmtAffine) v += 8 * xsum[(int64_t)g * m + row];
+                d[((int64_t)row * geom.n + col) * ng + g] = v;
+            }
+        } else {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = r0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
-                    const int raw = t ? dt1[e] : dt0[e];
-                    if (row >= m || col >= geom.n) continue;
-                    int v = (FMT == kFmtCodebook) ? raw : (raw >> 4);
-                    if (FMT == kFmtAffine) v += 8 * xsum[(int64_t)g * m + row];
-                    d[((int64_t)row * geom.n + col) * ng + g] = v;
+            for (int e = 0; e < 16; ++e)
+                acc[16 * t + e] =
+                    fmaf(static_cast<float>(dt[e]), coef[16 * t + e], acc[16 * t + e]);
+        }
+    };
+
+    // Publish stage st + 1 (register set (st+1)%3) into LDS buffer (st+1)%3, which stage st - 2
+    // used; once every wavefront is past the barrier, refill the set with stage st + 4.
+    auto stage_end = [&](auto SET, int st) {
+        stage_store(SET);
+        __syncthreads();
+        stage_load(SET, st + 1 + kSets);
+    };
+
+    // One 64-wide k step s = 6q + I.
+    auto step = [&](auto II, int s) {
+        constexpr int I = decltype(II)::value;
+        constexpr int buf = I / 2;                       // LDS buffer and register set of s / 2
+        constexpr int sub = I % 2;
+        constexpr bool first = (I % SPG) == 0;           // first step of its group
+        constexpr bool last = (I % SPG) == SPG - 1;
+        constexpr int mslot = I / SPG;
+        if (sub == 0 && s > 0) stage_end(std::integral_constant<int, buf>(), s / 2 - 1);
+        const int g = s / SPG;
+        if (s < nsteps && active) {
+            const uint8_t *ab = &lds_a[buf][a_lds + sub * 64];
+            const v4i a00 = *reinterpret_cast<const v4i *>(ab);
+            const v4i a01 = *reinterpret_cast<const v4i *>(ab + 16);
+            const v4i a10 = *reinterpret_cast<const v4i *>(ab + 32 * kLdsRow);
+            const v4i a11 = *reinterpret_cast<const v4i *>(ab + 32 * kLdsRow + 16);
+            v4i blo, bhi;
+            unpack_b<FMT>(rb[I], cb, blo, bhi);
+            const v16i z = {};
+            if (first && g > 0) finish_tile(std::integral_constant<int, 0>(), g - 1);
+            dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a00, blo, first ? z : dt0, 0, 0, 0);
+            dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a01, bhi, dt0, 0, 0, 0);
+            if (first) {
+                if (g > 0) finish_tile(std::integral_constant<int, 1>(), g - 1);
+                if (!PARTIALS) {
+                    // coefficient tiles xs[row] * sw16[col] of group g, after the last read of
+                    // group g-1's coefficients
+                    const float sw = half_bits_to_float(rmeta[mslot] & 0xFFFFu);
+                    const float sw16 = (FMT == kFmtCodebook) ? sw : sw * 0.0625f;
+                    const v32f zf = {};
+                    coef = __builtin_amdgcn_mfma_f32_32x32x1f32(rxs[mslot], sw16, zf, 0, 0, 0);
                 }
             }
-            return;
+            dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a10, blo, first ? z : dt1, 0, 0, 0);
+            dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a11, bhi, dt1, 0, 0, 0);
+            if (last && FMT == kFmtAffine && !PARTIALS) {
+                // sum_g xs*xsum[row] * (bw + 8 sw)[col]: bias plus the u = (u-8) + 8 correction
+                const uint32_t meta = rmeta[mslot];
+                const float b2 = fmaf(8.0f, half_bits_to_float(meta & 0xFFFFu),
+                                      half_bits_to_float(meta >> 16));
+                const float xs_sum = rxs[mslot] * static_cast<float>(rxsum[mslot]);
+                bacc = __builtin_amdgcn_mfma_f32_32x32x1f32(xs_sum, b2, bacc, 0, 0, 0);
+            }
         }
-
-        if (FMT == kFmtAffine) {
-            // sum_g xs*xsum[row] * (bw + 8 sw)[col]: bias plus the u = (u-8) + 8 correction
-            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(xs_sum, b2, acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            acc[e] = fmaf(static_cast<float>(dt0[e]), coef[e], acc[e]);
-            acc[16 + e] = fmaf(static_cast<float>(dt1[e]), coef[16 + e], acc[16 + e]);
-        }
-    };
-    // After the two steps of stage st: publish stage st+1 (loaded one stage ago) into the buffer
-    // stage st-1 used, fetch stage st+2, and let every wavefront see the new buffer.
-    auto stage_end = [&](int st) {
-        stage_store((st + 1) & 1);
-        stage_load(st + 2);
-        __syncthreads();
+        load_b(I, s + kLead);
+        if (last) load_meta(mslot, g + kRingG);
     };
 
-    int s = 0;
-    for (; s + 4 <= nsteps; s += 4) {
-        body(std::integral_constant<int, 0>(), s);
-        body(std::integral_constant<int, 1>(), s + 1);
-        stage_end(s / 2);
-        body(std::integral_constant<int, 2>(), s + 2);
-        body(std::integral_constant<int, 3>(), s + 3);
-        stage_end(s / 2 + 1);
+    for (int s = 0; s < nsteps; s += kLead) {
+        step(std::integral_constant<int, 0>(), s);
+        step(std::integral_constant<int, 1>(), s + 1);
+        step(std::integral_constant<int, 2>(), s + 2);
+        step(std::integral_constant<int, 3>(), s + 3);
+        step(std::integral_constant<int, 4>(), s + 4);
+        step(std::integral_constant<int, 5>(), s + 5);
     }
-    // remaining steps (fewer than 4; a whole number of groups)
-    if (s < nsteps) body(std::integral_constant<int, 0>(), s);
-    if (s + 1 < nsteps) body(std::integral_constant<int, 1>(), s + 1);
-    if (s + 2 < nsteps) {
-        stage_end(s / 2);
-        body(std::integral_constant<int, 2>(), s + 2);
-    }
-    if (PARTIALS || !active) return;
+    if (!active) return;
+    finish_tile(std::integral_constant<int, 0>(), ng - 1);
+    finish_tile(std::integral_constant<int, 1>(), ng - 1);
+    if (PARTIALS) return;
 
     const int col = c0 + r32;
     if (col >= geom.n) return;
@@ -290,7 +311,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ p
         for (int e = 0; e < 16; ++e) {
             const int row = r0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
             if (row >= m) continue;
-            y[(int64_t)row * geom.n + col] = acc[16 * t + e];
+            float v = acc[16 * t + e];
+            if (FMT == kFmtAffine) v += bacc[16 * t + e];
+            y[(int64_t)row * geom.n + col] = v;
         }
     }
 }
@@ -299,13 +322,9 @@ template <int FMT, int G, bool PARTIALS>
 hipError_t launch_bm(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
                      const float *xs, const int32_t *xsum, float *y, int32_t *d,
                      hipStream_t stream) {
-    if (m <= 64) {
-        const dim3 grid(static_cast<unsigned>(g.n_pad / 128 + (g.n_pad % 128 ? 1 : 0)), 1);
-        gemm_kernel<FMT, G, 64, PARTIALS><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y, d);
-    } else {
-        const dim3 grid(static_cast<unsigned>(g.n_pad / 64), static_cast<unsigned>((m + 127) / 128));
-        gemm_kernel<FMT, G, 128, PARTIALS><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y, d);
-    }
+    const unsigned tiles =
+        static_cast<unsigned>(((g.n_pad + kBN - 1) / kBN) * ((m + BM - 1) / BM));
+    gemm_kernel<FMT, G, PARTIALS><<<tiles, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y, d);
     return hipGetLastError();
 }
 
