@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the W4A8 linear layer on one MI355X; prints one JSON line.
 
-A step is one pass of the per-token hot path over one batch of synthetic input: the activation
-prepass (w4a8_prep) and the linear (w4a8_gemv at one row, w4a8_gemm above).  The default workload
+A step is one pass of the per-token hot path over one batch of synthetic input through
+w4a8_linear: the activation prepass and the linear (one fused kernel at one row, where every
+GEMV workgroup quantizes the row itself; the prepass kernel then the GEMM above).  The default workload
 is the decode GEMV of a gate_up-shaped layer: M=1, K=2048, N=16384, symmetric 4-bit weights in
 64-groups with fp16 scales, X ~ N(0,1) with 8 outlier channels x20.  The weights are packed once
 (load time, not in a step).
@@ -12,13 +13,14 @@ the 256 MiB last-level cache) and the steps walk through the pool, so every step
 weights from HBM, as a decode does across layers.  The K timed steps are captured once into a HIP
 graph (launch gaps of a Python loop would otherwise dominate microsecond kernels) and replayed
 between stream synchronizations; W warmup steps run first.  The dominant kernel's average
-duration is timed the same way from a graph of linear-only launches over the same pool, bracketed
-by HIP events on the capturing stream.
+duration is timed the same way from a graph of launches of that kernel alone over the same pool
+(at one row the fused kernel is the whole step), bracketed by HIP events on the capturing stream.
 
 value      = weight bytes (nibbles + scales [+ bias] [+ codebook]) per step / step time (GB/s)
-roofline   = algorithmic bytes of one linear launch (weights + xq + xs + xsum + y) / its average
-             duration, against the 8 TB/s HBM peak (or int8 ops against the 5.0 POP/s dense MFMA
-             peak for a GEMM whose MFMA floor is above its HBM floor)
+roofline   = algorithmic bytes of one launch of the dominant kernel (weights + xq + xs + xsum + y,
+             plus the fp32 row when the prepass is fused in) / its average duration, against
+             the 8 TB/s HBM peak (or int8 ops against the 5.0 POP/s dense MFMA peak for a GEMM
+             whose MFMA floor is above its HBM floor)
 cpu_baseline = the CPU oracle (plain C, OpenMP) on the same workload, repeated for about 10 s
 """
 from __future__ import annotations
@@ -106,8 +108,11 @@ def workload_name(cfg):
     from bit_group_quantized_act_amd import synth
     kind = "decode GEMV" if cfg.m == 1 else "prefill GEMM"
     rot = ", 128-block WHT" if cfg.hadamard else ""
+    fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072
+    how = ("prepass fused into the GEMV" if fused else
+           "prepass + GEMV" if cfg.m == 1 else "prepass + GEMM")
     return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
-            f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights{rot} (prep + linear per step)")
+            f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights{rot} ({how} per step)")
 
 
 def main():
@@ -137,7 +142,8 @@ def main():
     lay, packed0 = w4a8.pack(t(layer["codes"]), t(layer["scales"]), cfg.fmt, cfg.group,
                              bias=t(layer["bias"]), codebook=t(layer["codebook"]))
     wbytes = synth.weight_bytes(cfg)
-    alg_bytes = synth.algorithmic_bytes(cfg)
+    fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072   # w4a8_linear's one-kernel case
+    alg_bytes = synth.algorithmic_bytes(cfg, fused_prep=fused)
     ops = synth.int_ops(cfg)
     pool_n = 1 if args.hot else max(2, -(-POOL_BYTES // lay.bytes))
     pool = [packed0] + [packed0.clone() for _ in range(pool_n - 1)]
@@ -150,15 +156,18 @@ def main():
     torch.cuda.synchronize()
 
     def linear(i):
+        # the dominant kernel alone: the fused prepass + GEMV at one row (the plain GEMV for a
+        # vocabulary-sized row), the GEMM above
         pk = pool[i % pool_n]
-        if cfg.m == 1:
+        if fused:
+            w4a8.linear(lay, pk, x, cfg.hadamard, out=y, prep_out=(xq, xs, xsum))
+        elif cfg.m == 1:
             w4a8.gemv(lay, pk, xq[0], xs, xsum, out=y[0])
         else:
             w4a8.gemm(lay, pk, xq, xs, xsum, out=y)
 
     def step(i):
-        w4a8.prep(x, cfg.group, cfg.hadamard, out=(xq, xs, xsum))
-        linear(i)
+        w4a8.linear(lay, pool[i % pool_n], x, cfg.hadamard, out=y, prep_out=(xq, xs, xsum))
 
     stream = torch.cuda.Stream()
 
@@ -206,7 +215,7 @@ def main():
         achieved = alg_bytes / (us_linear * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4))
-    kname = "gemv" if cfg.m == 1 else "gemm"
+    kname = "gemv" if cfg.m == 1 else "gemm"     # the fused kernel lives in gemv.hip
     roof.update(traffic=measured_traffic(cfg.name, kname), kernel=kname,
                 kernel_us=round(us_linear, 3), alg_bytes_per_launch=alg_bytes,
                 int_ops_per_launch=ops,

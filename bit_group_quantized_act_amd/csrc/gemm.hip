@@ -93,12 +93,17 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                                                       float *__restrict__ y,
                                                       int *__restrict__ d) {
     constexpr int SPG = G / 64;                          // 64-wide k steps per group
-    constexpr int kRingG = kLead / SPG;                  // groups of metadata loaded ahead
+    constexpr int GPSt = kStageSteps / SPG;              // groups per activation stage
+    constexpr int kMD = 16 * (FMT == kFmtAffine ? 4 : 2); // meta dwords per panel and group
     constexpr int kMB = (FMT == kFmtAffine) ? 4 : 2;     // meta bytes per channel and group
     constexpr int kAJ = BM / 32;                         // 16-byte staging loads per thread
     static_assert(kLead == 6 && kStageSteps == 2 && kLead % SPG == 0,
                   "the unrolled loop covers three stages of two k steps");
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[kSets][BM * kLdsRow];
+    // per stage: activation scales and sums of the workgroup's rows ([xs|xsum][group][row]) and
+    // the weight metadata of its two panels ([group][panel][row]), one dword per thread
+    __shared__ uint32_t lds_x[kSets][256];
+    __shared__ uint32_t lds_m[kSets][256];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -133,12 +138,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     const rsrc_t rq = make_rsrc(xq + (int64_t)m0 * k, (uint64_t)rows_wg * k);
     const uint8_t *wbase = active ? packed + geom.off_codes + (int64_t)p * kc * 1024 : packed;
     const rsrc_t rw = make_rsrc(wbase, active ? (uint64_t)kc * 1024 : 0);
-    const uint8_t *mbase =
-        active ? packed + geom.off_meta + (int64_t)p * ng * kPanelRows * kMB : packed;
-    const rsrc_t rm = make_rsrc(mbase, active ? (uint64_t)ng * kPanelRows * kMB : 0);
     const int w_off = half * 1024 + prow * 16;
-    const int meta_off = prow * kMB;
-    const int x_off = (r0 + lane) * 4;                   // row of the outer-product operands
 
     uint4 cb = make_uint4(0u, 0u, 0u, 0u);
     if (FMT == kFmtCodebook && active) {
@@ -151,7 +151,20 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     // padded to 144 bytes so the MFMA-layout reads (32 rows at one k offset per half wavefront)
     // spread over the banks.
     v4i stage_regs[kSets][kAJ];
+    uint32_t stage_x[kSets], stage_m[kSets];
     const int a_row = tid >> 3, a_piece = tid & 7;
+    // Metadata staging: wave w loads xs (w < 2) or xsum (w >= 2) of group w & 1 of the stage for
+    // the 64 rows (one dword per lane), and thread t loads dword t of the stage's weight metadata
+    // block [group][panel][row] of the workgroup's two panels.  Loads that fall outside the data
+    // get an out-of-range offset (zeros, no memory access) instead of a branch.
+    constexpr uint32_t kOOB = 0x7FFFFFF0u;
+    const int x_which = wave >> 1, x_j = wave & 1;
+    const bool x_valid = x_j < GPSt && (x_which == 0 || FMT == kFmtAffine);
+    const int m_j = tid / (2 * kMD), m_pnl = (tid / kMD) & 1, m_d = tid % kMD;
+    const int wg_p0 = nt * (kBN / kPanelRows);           // first panel of the workgroup
+    const int wg_np = min(kBN / kPanelRows, geom.n_pad / kPanelRows - wg_p0);
+    const rsrc_t rmw = make_rsrc(packed + geom.off_meta + (int64_t)wg_p0 * ng * kPanelRows * kMB,
+                                 (uint64_t)wg_np * ng * kPanelRows * kMB);
     // Every load in the main loop is issued unconditionally (a stage or step past the end reads
     // zeros through the range check, or a clamped valid address): the waits the compiler places
     // for one load then count exactly the loads issued after it, which keeps the deep prefetch
@@ -161,6 +174,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
 #pragma unroll
         for (int j = 0; j < kAJ; ++j)
             stage_regs[set][j] = ld128(rq, (32 * j + a_row) * k + a_piece * 16, st * kStageK);
+        const int gb = st * GPSt;                        // first group of the stage
+        const int gv = max(0, min(GPSt, ng - gb));       // its groups that exist
+        const float *xbase = x_which ? reinterpret_cast<const float *>(xsum) : xs;
+        const rsrc_t rx = make_rsrc(xbase + (int64_t)min(gb, ng - 1) * m, (uint64_t)gv * m * 4);
+        stage_x[set] = ld32(rx, x_valid ? (x_j * m + m0 + lane) * 4 : (int)kOOB, 0);
+        const bool mv = m_j < gv;
+        stage_m[set] = ld32(rmw, mv ? ((m_pnl * ng + gb + m_j) * kPanelRows * kMB + m_d * 4)
+                                    : (int)kOOB, 0);
     };
     auto stage_store = [&](auto SET) {
         constexpr int set = decltype(SET)::value;
@@ -168,31 +189,18 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
         for (int j = 0; j < kAJ; ++j)
             *reinterpret_cast<v4i *>(&lds_a[set][(32 * j + a_row) * kLdsRow + a_piece * 16]) =
                 stage_regs[set][j];
+        lds_x[set][tid] = stage_x[set];
+        lds_m[set][tid] = stage_m[set];
     };
     // LDS offset of this lane's MFMA operands: row 32t + r32, k bytes 32*half + 16*h of
     // the 64-wide step
     const int a_lds = r32 * kLdsRow + 32 * half;
 
-    // ---- weight chunks (one k step each) and per-group metadata, loaded kLead steps ahead
-    v4i rb[kLead];              // 16 weight bytes of the lane's channel
-    uint32_t rmeta[kRingG];     // fp16 scale (| fp16 bias << 16) of the lane's channel
-    float rxs[kRingG];          // activation scale of row r0 + lane, the group
-    int rxsum[kRingG];          // its group sum (affine)
+    // ---- weight chunks, one k step each, loaded kLead steps ahead
+    v4i rb[kLead];                 // 16 weight bytes of the lane's channel
+    // the current group's outer-product operands, read from the staged metadata
+    float g_sw16 = 0.0f, g_xs = 0.0f, g_b2 = 0.0f, g_xsum = 0.0f;
     auto load_b = [&](int slot, int step) { rb[slot] = ld128(rw, w_off, step * 2048); };
-    auto load_meta = [&](int slot, int g) {
-        g = min(g, ng - 1);
-        if (!PARTIALS) {
-            rmeta[slot] = (kMB == 4) ? ld32(rm, meta_off, g * kPanelRows * 4)
-                                     : ld16(rm, meta_off, g * kPanelRows * 2);
-            // group-major scales and sums: one descriptor per group column, rows >= m read 0
-            const rsrc_t rs = make_rsrc(xs + (int64_t)g * m, (uint64_t)m * 4);
-            rxs[slot] = __builtin_bit_cast(float, ld32(rs, x_off, 0));
-        }
-        if (FMT == kFmtAffine && !PARTIALS) {
-            const rsrc_t rx = make_rsrc(xsum + (int64_t)g * m, (uint64_t)m * 4);
-            rxsum[slot] = static_cast<int>(ld32(rx, x_off, 0));
-        }
-    };
 
     // prologue: stages 0..2 in flight, then weights and metadata, publish stage 0, start 3
     stage_load(std::integral_constant<int, 0>(), 0);
@@ -200,8 +208,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     stage_load(std::integral_constant<int, 2>(), 2);
 #pragma unroll
     for (int i = 0; i < kLead; ++i) load_b(i, i);
-#pragma unroll
-    for (int i = 0; i < kRingG; ++i) load_meta(i, i);
     stage_store(std::integral_constant<int, 0>());
     __syncthreads();
     stage_load(std::integral_constant<int, 0>(), 3);
@@ -249,17 +255,34 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
         constexpr int sub = I % 2;
         constexpr bool first = (I % SPG) == 0;           // first step of its group
         constexpr bool last = (I % SPG) == SPG - 1;
-        constexpr int mslot = I / SPG;
         if (sub == 0 && s > 0) stage_end(std::integral_constant<int, buf>(), s / 2 - 1);
         const int g = s / SPG;
+        // Consume this step's ring slots first and refill them at once, so the loads for step
+        // s + kLead are in flight while this step computes.
+        v4i blo, bhi;
+        unpack_b<FMT>(rb[I], cb, blo, bhi);
+        load_b(I, s + kLead);
+        if (first && !PARTIALS) {
+            // group j of this stage: the lane's row scale / sum and its channel's metadata
+            constexpr int j = (I % kStageSteps) / SPG;
+            const int pnl = wn >> 1;
+            const uint32_t meta =
+                (kMB == 4) ? lds_m[buf][(j * 2 + pnl) * kPanelRows + prow]
+                           : reinterpret_cast<const uint16_t *>(lds_m[buf])[(j * 2 + pnl) * kPanelRows + prow];
+            const float sw = half_bits_to_float(meta & 0xFFFFu);
+            g_sw16 = (FMT == kFmtCodebook) ? sw : sw * 0.0625f;
+            g_xs = __builtin_bit_cast(float, lds_x[buf][j * 64 + lane]);
+            if (FMT == kFmtAffine) {
+                g_b2 = fmaf(8.0f, sw, half_bits_to_float(meta >> 16));
+                g_xsum = g_xs * static_cast<float>(static_cast<int>(lds_x[buf][128 + j * 64 + lane]));
+            }
+        }
         if (s < nsteps && active) {
             const uint8_t *ab = &lds_a[buf][a_lds + sub * 64];
             const v4i a00 = *reinterpret_cast<const v4i *>(ab);
             const v4i a01 = *reinterpret_cast<const v4i *>(ab + 16);
             const v4i a10 = *reinterpret_cast<const v4i *>(ab + 32 * kLdsRow);
             const v4i a11 = *reinterpret_cast<const v4i *>(ab + 32 * kLdsRow + 16);
-            v4i blo, bhi;
-            unpack_b<FMT>(rb[I], cb, blo, bhi);
             const v16i z = {};
             if (first && g > 0) finish_tile(std::integral_constant<int, 0>(), g - 1);
             dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a00, blo, first ? z : dt0, 0, 0, 0);
@@ -269,25 +292,17 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                 if (!PARTIALS) {
                     // coefficient tiles xs[row] * sw16[col] of group g, after the last read of
                     // group g-1's coefficients
-                    const float sw = half_bits_to_float(rmeta[mslot] & 0xFFFFu);
-                    const float sw16 = (FMT == kFmtCodebook) ? sw : sw * 0.0625f;
                     const v32f zf = {};
-                    coef = __builtin_amdgcn_mfma_f32_32x32x1f32(rxs[mslot], sw16, zf, 0, 0, 0);
+                    coef = __builtin_amdgcn_mfma_f32_32x32x1f32(g_xs, g_sw16, zf, 0, 0, 0);
                 }
             }
             dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a10, blo, first ? z : dt1, 0, 0, 0);
             dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a11, bhi, dt1, 0, 0, 0);
             if (last && FMT == kFmtAffine && !PARTIALS) {
                 // sum_g xs*xsum[row] * (bw + 8 sw)[col]: bias plus the u = (u-8) + 8 correction
-                const uint32_t meta = rmeta[mslot];
-                const float b2 = fmaf(8.0f, half_bits_to_float(meta & 0xFFFFu),
-                                      half_bits_to_float(meta >> 16));
-                const float xs_sum = rxs[mslot] * static_cast<float>(rxsum[mslot]);
-                bacc = __builtin_amdgcn_mfma_f32_32x32x1f32(xs_sum, b2, bacc, 0, 0, 0);
+                bacc = __builtin_amdgcn_mfma_f32_32x32x1f32(g_xsum, g_b2, bacc, 0, 0, 0);
             }
         }
-        load_b(I, s + kLead);
-        if (last) load_meta(mslot, g + kRingG);
     };
 
     for (int s = 0; s < nsteps; s += kLead) {

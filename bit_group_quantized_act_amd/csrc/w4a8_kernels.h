@@ -19,6 +19,7 @@ struct Geom {
 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
@@ -54,6 +55,67 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
+// ---- the activation prepass of one float4 quad
+//
+// Rotation (optional normalized Walsh-Hadamard transform of 128-wide blocks), per-group int8
+// quantization and group sum, as defined in include/w4a8.h.  The calling wavefront holds
+// consecutive quads of a row in consecutive lanes: the G/4 lanes of a group, and the 32 lanes of
+// a 128-wide rotation block, are aligned runs of lanes that are either all active or all
+// inactive (the cross-lane exchanges stay inside them).  Returns the four codes packed into a
+// dword (first element in the low byte); scale and sum come back in every lane of the group.
+// Bit-exactness: each value goes through the same fp32 operations as the definition (butterflies
+// of span 1, 2 inside the lane and 4..64 across lanes 1..16 apart, each output one add or
+// subtract of the same two operands, then one multiply by fp32(1/sqrt(128)); an IEEE-rounded
+// divide by 127 for the scale; an IEEE-rounded divide then round-half-even for each code), with
+// contraction off.
+template <int G, bool ROT>
+__device__ __forceinline__ int prep_quad(float4 v, int lane, float &scale, int &sum) {
+#pragma clang fp contract(off)
+    constexpr int kLanesPerGroup = G / 4;
+    // 1/sqrt(128) = sqrt(2)/16 rounded to the nearest fp32: sqrt(2) rounds to 0x3FB504F3, and the
+    // division by 16 only moves the exponent, giving 0x3DB504F3.
+    constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;
+    float e[4] = {v.x, v.y, v.z, v.w};
+    if (ROT) {
+        float a, b;
+        // span 1: (0,1), (2,3)
+        a = e[0]; b = e[1]; e[0] = a + b; e[1] = a - b;
+        a = e[2]; b = e[3]; e[2] = a + b; e[3] = a - b;
+        // span 2: (0,2), (1,3)
+        a = e[0]; b = e[2]; e[0] = a + b; e[2] = a - b;
+        a = e[1]; b = e[3]; e[1] = a + b; e[3] = a - b;
+        // spans 4..64: partner lane differs in bit s of the lane's position in its 128-block
+#pragma unroll
+        for (int s = 1; s < 32; s <<= 1) {
+            const bool upper = (lane & s) != 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float other = __shfl_xor(e[i], s, 64);
+                e[i] = upper ? (other - e[i]) : (e[i] + other);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = e[i] * kInvSqrt128;
+    }
+    float amax = fmaxf(fmaxf(fabsf(e[0]), fabsf(e[1])), fmaxf(fabsf(e[2]), fabsf(e[3])));
+#pragma unroll
+    for (int s = 1; s < kLanesPerGroup; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 64));
+    scale = amax / 127.0f;
+    int q[4] = {0, 0, 0, 0};
+    if (amax > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float r = rintf(e[i] / scale);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            q[i] = static_cast<int>(r);
+        }
+    }
+    sum = q[0] + q[1] + q[2] + q[3];
+#pragma unroll
+    for (int s = 1; s < kLanesPerGroup; s <<= 1) sum += __shfl_xor(sum, s, 64);
+    return (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | ((q[3] & 0xFF) << 24);
+}
+
 // ---- launchers (each returns the hipGetLastError() of its launch)
 
 hipError_t launch_pack(const Geom &g, const uint8_t *codes, const uint16_t *scales,
@@ -66,6 +128,15 @@ hipError_t launch_prep(const float *x, int64_t m, int k, int group, int hadamard
 // y != nullptr: fp32 output; d != nullptr: int32 partials instead.
 hipError_t launch_gemv(const Geom &g, const uint8_t *packed, const int8_t *xq, const float *xs,
                        const int32_t *xsum, float *y, int32_t *d, hipStream_t stream);
+
+// The decode GEMV with the prepass of its one activation row fused in: every workgroup
+// quantizes x into LDS; workgroup 0 also writes xq, xs, xsum.  k <= kFusedMaxK.  Each workgroup
+// (one 64-row panel) repeats the quantization, so beyond kFusedMaxPanels panels (a vocabulary
+// head) the separate prepass launch costs less than the repeats.
+constexpr int kFusedMaxK = 16384;
+constexpr int kFusedMaxPanels = 2048;
+hipError_t launch_gemv_fused(const Geom &g, const uint8_t *packed, const float *x, int hadamard,
+                             int8_t *xq, float *xs, int32_t *xsum, float *y, hipStream_t stream);
 
 hipError_t launch_gemm(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
                        const float *xs, const int32_t *xsum, float *y, int32_t *d,

@@ -188,10 +188,14 @@ def weight_bytes(cfg: LayerConfig) -> int:
     return b
 
 
-def algorithmic_bytes(cfg: LayerConfig) -> int:
-    """Bytes one linear call must move: weights + xq + xs + xsum + fp32 y."""
+def algorithmic_bytes(cfg: LayerConfig, fused_prep: bool = False) -> int:
+    """Bytes one linear call must move: weights + xq + xs + xsum + fp32 y; with the prepass fused
+    into the same kernel (one activation row), also the fp32 row read."""
     ng = cfg.k // cfg.group
-    return weight_bytes(cfg) + cfg.m * cfg.k + 8 * cfg.m * ng + 4 * cfg.m * cfg.n
+    b = weight_bytes(cfg) + cfg.m * cfg.k + 8 * cfg.m * ng + 4 * cfg.m * cfg.n
+    if fused_prep:
+        b += 4 * cfg.m * cfg.k
+    return b
 
 
 def int_ops(cfg: LayerConfig) -> int:

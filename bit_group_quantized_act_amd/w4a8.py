@@ -21,7 +21,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "no gfx950 device
 
 # Every exported symbol of the C ABI (the header's declarations, in order).
 EXPORTS = ("w4a8_packed_layout", "w4a8_pack_weights", "w4a8_prep", "w4a8_gemv", "w4a8_gemm",
-           "w4a8_debug_partials", "w4a8_status_string", "w4a8_last_error")
+           "w4a8_linear", "w4a8_debug_partials", "w4a8_status_string", "w4a8_last_error")
 
 
 class Layout(ctypes.Structure):
@@ -62,8 +62,9 @@ def load() -> ctypes.CDLL:
     lib.w4a8_prep.argtypes = [P, i32, i32, i32, i32, P, P, P, P]
     lib.w4a8_gemv.argtypes = [LP, P, P, P, P, P, P]
     lib.w4a8_gemm.argtypes = [LP, P, i32, P, P, P, P, P]
+    lib.w4a8_linear.argtypes = [LP, P, i32, P, i32, P, P, P, P, P]
     lib.w4a8_debug_partials.argtypes = [LP, P, i32, P, P, P, P]
-    for f in EXPORTS[:6]:
+    for f in EXPORTS[:7]:
         getattr(lib, f).restype = ctypes.c_int
     lib.w4a8_status_string.argtypes = [ctypes.c_int]
     lib.w4a8_status_string.restype = ctypes.c_char_p
@@ -181,9 +182,30 @@ def debug_partials(L: Layout, packed: torch.Tensor, xq, xsum) -> torch.Tensor:
     return d
 
 
-def linear(L: Layout, packed: torch.Tensor, x: torch.Tensor, hadamard_block: int = 0):
-    """prep then GEMV (one row) or GEMM: fp32 activations [m, k] or [k] -> fp32 output."""
-    xq, xs, xsum = prep(x, L.group, hadamard_block)
-    if x.dim() == 1:
-        return gemv(L, packed, xq, xs, xsum)
-    return gemm(L, packed, xq, xs, xsum)
+def linear(L: Layout, packed: torch.Tensor, x: torch.Tensor, hadamard_block: int = 0, out=None,
+           prep_out=None):
+    """The whole layer (w4a8_linear): fp32 activations [m, k] or [k] -> fp32 output [m, n] or [n].
+
+    One kernel for a single row (the GEMV quantizes the row itself), prepass + GEMM otherwise.
+    prep_out = (xq, xs, xsum) receives the prepass outputs (allocated if None).  Returns y, or
+    (y, (xq, xs, xsum)) when prep_out is given.
+    """
+    squeeze = x.dim() == 1
+    x2 = x.unsqueeze(0) if squeeze else x
+    _dev(x2, torch.float32, "x")
+    m, k = x2.shape
+    if k != L.k:
+        raise ValueError(f"x has k = {k}, the layout {L.k}")
+    ng = k // L.group
+    if prep_out is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+        xs = torch.empty((ng, m), dtype=torch.float32, device=x.device)
+        xsum = torch.empty((ng, m), dtype=torch.int32, device=x.device)
+    else:
+        xq, xs, xsum = prep_out
+    y = out if out is not None else torch.empty((m, L.n), dtype=torch.float32, device=x.device)
+    _check(load().w4a8_linear(ctypes.byref(L), _ptr(packed), m, _ptr(x2), hadamard_block,
+                              _ptr(xq), _ptr(xs), _ptr(xsum), _ptr(y), _stream(x.device)),
+           "w4a8_linear")
+    y = y[0] if (squeeze and out is None) else y
+    return (y, (xq, xs, xsum)) if prep_out is not None else y

@@ -164,6 +164,25 @@ w4a8_status w4a8_gemm(const w4a8_layout *L, const void *packed, int32_t m, const
                       const float *xs, const int32_t *xsum, float *y, void *stream);
 
 /*
+ * The whole hot path of one linear layer: the prepass of x (as w4a8_prep with L->group), then
+ * the GEMV (m == 1) or the GEMM (m > 1).
+ *   x               fp32 [m][L->k] row-major (not modified)
+ *   hadamard_block  0 or 128, as for w4a8_prep
+ *   xq, xs, xsum    the prepass outputs, laid out as for w4a8_prep (written; the GEMM reads them)
+ *   y               fp32 [m][L->n]
+ * m == 1 with L->k <= 16384 and L->n <= 131072 runs one kernel: every workgroup of the GEMV
+ * quantizes the row itself into LDS with the prepass's arithmetic (so xq, xs and xsum are the same
+ * bits as w4a8_prep's), which removes a launch from each decode layer.  Otherwise (including a
+ * vocabulary head, where the repeated quantization would cost more than a launch) the prepass
+ * kernel and then the GEMV or GEMM kernel are enqueued on the stream.  m == 0 is a no-op (the pointers may then be NULL).
+ * Source: "cactus PR #697", section "Quantized matmul" (the fused GEMV's first phase is the
+ * Hadamard rotation and int8 quantization of the activations).
+ */
+w4a8_status w4a8_linear(const w4a8_layout *L, const void *packed, int32_t m, const float *x,
+                        int32_t hadamard_block, int8_t *xq, float *xs, int32_t *xsum, float *y,
+                        void *stream);
+
+/*
  * The exact int32 partials D[r][n][g] (definitions above) written by the same kernel code as
  * the GEMV (m == 1) or the GEMM (m > 1), with the fp32 epilogue replaced by a store of D.
  *   xsum  as from w4a8_prep (the AFFINE partial is recovered from the u - 8 codes as

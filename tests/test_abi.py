@@ -119,6 +119,17 @@ def test_invalid_calls_are_rejected_on_the_host(lib):
     assert lib.w4a8_gemm(LP, p, 4, p, None, p, p, None) == ERR_ARG
     assert lib.w4a8_debug_partials(LP, p, 0, p, p, p, None) == ERR_ARG
     assert lib.w4a8_debug_partials(LP, p, 2, p, p, None, None) == ERR_ARG
+    # linear: m < 0, bad rotation block, k % 128 with rotation, missing x / xq / y, misaligned
+    assert lib.w4a8_linear(LP, p, -1, p, 0, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_linear(LP, p, 1, p, 64, p, p, p, p, None) == ERR_ARG
+    L320 = w4a8.packed_layout(w4a8.SYM, 64, 320, 64)
+    assert lib.w4a8_linear(ctypes.byref(L320), p, 1, p, 128, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_linear(LP, p, 1, None, 0, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_linear(LP, p, 1, p, 0, None, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_linear(LP, p, 3, p, 0, p, p, p, None, None) == ERR_ARG
+    assert lib.w4a8_linear(LP, p16, 1, p, 0, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_linear(LP, p, 1, p1, 0, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_linear(LP, p, 0, None, 0, None, None, None, None, None) == 0
 
 
 @pytest.mark.skipif(_gpu_visible(), reason="checks the no-device path; would launch on a GPU")
@@ -127,4 +138,5 @@ def test_valid_calls_without_a_device_report_device_error(lib):
     p = _fake(1 << 20)
     assert lib.w4a8_gemv(ctypes.byref(L), p, p, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_prep(p, 2, 256, 64, 0, p, p, p, None) == ERR_DEVICE
+    assert lib.w4a8_linear(ctypes.byref(L), p, 1, p, 0, p, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_last_error().decode() != ""

@@ -97,6 +97,57 @@ def test_parity_bitexact_and_tolerance(name, over, full):
     check_y(got["y"], ref["y"], ref["t"], f"{name} {over}")
 
 
+def _run_linear(L):
+    """The whole layer through w4a8_linear (fused prepass + GEMV for one row)."""
+    w = _w4a8()
+    cfg = L["cfg"]
+    lay, packed = _pack(L)
+    x = to_dev(L["x"])
+    ng = cfg.k // cfg.group
+    prep_out = (torch.empty((cfg.m, cfg.k), dtype=torch.int8, device="cuda:0"),
+                torch.empty((ng, cfg.m), dtype=torch.float32, device="cuda:0"),
+                torch.empty((ng, cfg.m), dtype=torch.int32, device="cuda:0"))
+    y, (xq, xs, xsum) = w.linear(lay, packed, x, cfg.hadamard, prep_out=prep_out)
+    torch.cuda.synchronize()
+    return dict(xq=xq.cpu().numpy(), xs=xs.cpu().numpy().T.copy(), xsum=xsum.cpu().numpy().T.copy(),
+                y=y.cpu().numpy().reshape(cfg.m, cfg.n))
+
+
+# one-row cases take the fused kernel (rotation included for C4); the 16448-wide row exceeds the
+# fused kernel's LDS bound and takes prepass + GEMV; multi-row cases take prepass + GEMM
+LINEAR_CASES = [
+    ("C1", dict(), False),
+    ("C1", dict(n=1000), True),
+    ("C2b", dict(n=2049), True),
+    ("C1", dict(group=128, k=1024, n=640), True),
+    ("C3a", dict(m=1, n=1000, k=1024), True),
+    ("C3a", dict(m=1, n=200, k=640), True),
+    ("C4", dict(m=1, n=320, k=768), False),
+    ("C4", dict(m=1, n=130, k=1536), True),
+    ("C1", dict(n=64, k=16448), True),
+    ("C3a", dict(m=65, n=1000, k=1280), True),
+    ("C4", dict(m=200, n=448, k=1536), False),
+]
+
+
+@pytest.mark.parametrize("name,over,full", LINEAR_CASES,
+                         ids=[f"{c}-{'-'.join(f'{k}{v}' for k, v in o.items())}-{'full' if f else 'w'}"
+                              for c, o, f in LINEAR_CASES])
+def test_linear_bitexact_and_tolerance(name, over, full):
+    L = synth.make(name, full_range=full, **over)
+    cfg = L["cfg"]
+    print(f"linear {name} {over} m={cfg.m} n={cfg.n} k={cfg.k} had={cfg.hadamard}", flush=True)
+    got = _run_linear(L)
+    ref = oracle_layer(L)
+    assert np.array_equal(got["xq"], ref["xq"]), "xq differs"
+    assert np.array_equal(_bits(got["xs"]), _bits(ref["xs"])), "xs differs"
+    assert np.array_equal(got["xsum"], ref["xsum"]), "xsum differs"
+    check_y(got["y"], ref["y"], ref["t"], f"linear {name} {over}")
+    # the fused kernel runs the same arithmetic as prepass + GEMV: the same bits
+    split = _run(L, with_partials=False)
+    assert np.array_equal(_bits(got["y"]), _bits(split["y"])), "linear and prep+matmul differ"
+
+
 def test_pack_round_trip_and_padding():
     """Decode the packed buffer on the host from the documented layout and recover the input."""
     for name, over in (("C3a", dict(m=1, n=100, k=640)), ("C4", dict(m=1, n=70, k=256)),
@@ -194,6 +245,10 @@ def test_full_size_sampled(name, ncols, layer_cache):
     cfg = L["cfg"]
     print(f"full {name}: m={cfg.m} n={cfg.n} k={cfg.k}", flush=True)
     got = _run(L, with_partials=False)
+    lin = _run_linear(L)         # the benchmark's path (one fused kernel for a single row)
+    assert np.array_equal(_bits(lin["y"]), _bits(got["y"])), "linear and prep+matmul differ"
+    assert np.array_equal(lin["xq"], got["xq"]) and np.array_equal(lin["xsum"], got["xsum"])
+    assert np.array_equal(_bits(lin["xs"]), _bits(got["xs"]))
     cols = None
     if ncols is not None:
         cols = np.sort(np.random.default_rng(11).choice(cfg.n, ncols, replace=False))
