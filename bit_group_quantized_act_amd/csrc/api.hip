@@ -97,6 +97,21 @@ w4a8_status launched(hipError_t e, const char *what) {
         if (!aligned((p), 16)) return fail(W4A8_ERR_ARG, #p " is not 16-byte aligned");        \
     } while (0)
 
+// Sizes the GEMM addresses with 32-bit offsets: the activation scales and sums of all rows
+// (m * k/group dwords) and the workgroup count.
+w4a8_status check_gemm_size(const w4a8_layout *L, int32_t m) {
+    // (the GEMM's copies run up to 16 groups past the last one)
+    const int64_t scales = static_cast<int64_t>(m) * (L->k / L->group + 16) * 4;
+    if (scales > 0x7FFFFFF0ll)
+        return fail(W4A8_ERR_UNSUPPORTED, "m * k/group = %lld scales exceed 2 GiB",
+                    static_cast<long long>(scales / 4));
+    const int64_t tiles = static_cast<int64_t>((m + 63) / 64) * ((L->n_pad + 127) / 128);
+    if (tiles > 0x7FFFFFFFll)
+        return fail(W4A8_ERR_UNSUPPORTED, "%lld GEMM tiles exceed the grid",
+                    static_cast<long long>(tiles));
+    return W4A8_OK;
+}
+
 w4a8_status check_activation_ptrs(const int8_t *xq, const float *xs, const int32_t *xsum) {
     W4A8_REQUIRE_PTR(xq);
     W4A8_REQUIRE_PTR(xs);
@@ -126,7 +141,8 @@ w4a8_status w4a8_packed_layout(int32_t format, int32_t n, int32_t k, int32_t gro
     L->n_pad = static_cast<int32_t>(round_up(n, W4A8_PANEL_ROWS));
     L->meta_bytes = (format == W4A8_AFFINE_U4) ? 4 : 2;
     const uint64_t codes = static_cast<uint64_t>(L->n_pad) * k / 2;
-    const uint64_t meta = static_cast<uint64_t>(L->n_pad) * (k / group) * L->meta_bytes;
+    // metadata in blocks of 4 groups (the last block zero-padded)
+    const uint64_t meta = static_cast<uint64_t>(L->n_pad) * ((k / group + 3) / 4) * 4 * L->meta_bytes;
     L->off_codes = 0;
     L->off_meta = round_up(codes, 256);
     uint64_t end = L->off_meta + round_up(meta, 256);
@@ -212,6 +228,7 @@ w4a8_status w4a8_gemm(const w4a8_layout *L, const void *packed, int32_t m, const
     if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
     if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
     if (m == 0) return ok();   // nothing to do; the activation and output pointers may be NULL
+    if ((s = check_gemm_size(L, m)) != W4A8_OK) return s;
     if ((s = check_activation_ptrs(xq, xs, xsum)) != W4A8_OK) return s;
     W4A8_REQUIRE_PTR(y);
     if ((s = check_device()) != W4A8_OK) return s;
@@ -234,6 +251,7 @@ w4a8_status w4a8_linear(const w4a8_layout *L, const void *packed, int32_t m, con
     if (hadamard_block == 128 && L->k % 128 != 0)
         return fail(W4A8_ERR_ARG, "k = %d is not a multiple of the rotation block 128", L->k);
     if (m == 0) return ok();
+    if ((s = check_gemm_size(L, m)) != W4A8_OK) return s;
     W4A8_REQUIRE_PTR(x);
     if ((s = check_activation_ptrs(xq, xs, xsum)) != W4A8_OK) return s;
     W4A8_REQUIRE_PTR(y);
@@ -260,6 +278,7 @@ w4a8_status w4a8_debug_partials(const w4a8_layout *L, const void *packed, int32_
     if (m > (1 << 20)) return fail(W4A8_ERR_UNSUPPORTED, "m = %d is above 2^20", m);
     if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
     if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
+    if ((s = check_gemm_size(L, m)) != W4A8_OK) return s;
     W4A8_REQUIRE_PTR(xq);
     W4A8_REQUIRE_PTR(xsum);
     W4A8_REQUIRE_PTR(d);

@@ -11,31 +11,31 @@
 //   wavefront owns all 64 rows x its own 32 channels as two 32x32 int32 tiles that share one
 //   weight fragment, so no two wavefronts load the same weight bytes.  Lane l of a tile holds
 //   activation row l%32 and k half l/32; the weight chunk of lane l is panel row l%32 of the
-//   wavefront's 32 channels at chunk 2q + l/32, so a tile's weight fragment is two contiguous
-//   512-byte runs of the packed panel.  The low nibbles of the chunk are k 0..15 and pair with
-//   the lane's first 16 activation bytes, the high nibbles k 16..31 with the next 16 (the same k
-//   on both sides, which is all the MFMA needs): two v_mfma_i32_32x32x32_i8 per tile per 64-wide
-//   k step.  Workgroups are numbered so that each XCD (one L2) gets a contiguous run of tiles,
-//   with the M tiles of one channel block adjacent: they share its weights in that L2.
-//   Loads.  Every operand comes through buffer loads (SGPR descriptor, one fixed VGPR offset per
-//   lane, the k step in the SGPR offset), so rows past m read as zeros (the descriptor's range
-//   check) instead of being predicated.  Activations are staged through LDS in 128-wide k
-//   stages from three register sets loaded three stages ahead (three LDS buffers, one barrier
-//   per stage); weight chunks and per-group metadata are loaded six k steps ahead.  Loads
-//   complete in issue order, so the two leads are matched (a wait for one load never forces a
-//   much younger one), and no load sits behind a branch (the compiler's waits would otherwise
-//   drain every load in flight): this keeps ~48 KiB of weights in flight per CU.
-//   Software pipeline.  The epilogue of group g-1 runs on the VALU, tile by tile, between the
-//   MFMAs of group g: the int32 partials of a tile are converted and accumulated with one FMA
-//   each, and that tile's MFMAs for group g are issued right after its last read.  The FMA
-//   coefficients xs[row] * sw[col] come from one fp32 outer-product MFMA
-//   (v_mfma_f32_32x32x1_2b: block t = tile t) issued as soon as the previous group's
-//   coefficients are consumed, which also lands each coefficient in the lane and register of
-//   its partial.  The affine bias term xs*xsum[row] * (bw + 8 sw)[col] is a second outer
-//   product accumulated on the matrix unit into its own fp32 tile.  So per element and group the
-//   VALU does two operations and the matrix unit the rest.
-//   Signed codes (sym q, affine u-8) enter the MFMA as 16*q (nibble moved to the byte's top);
-//   the 1/16 is folded into sw, and affine's u = (u-8) + 8 is restored through the bias term.
+//   wavefront's 32 channels at chunk 2s + l/32, so a step's weight fragment is two contiguous
+//   512-byte runs of the packed panel.  The chunk's low nibbles (k 0..15) pair with the lane's
+//   first 16 activation bytes and its high nibbles (k 16..31) with the next 16: two
+//   v_mfma_i32_32x32x32_i8 per tile per 64-wide k step.  Workgroups are numbered so that each
+//   XCD (one L2) gets a contiguous run of tiles, the M tiles of a channel block adjacent.
+//   Stages.  The k range is cut into stages of 256.  A stage's activation rows, the activation
+//   scales (and sums) of its groups and the weight metadata of the workgroup's two panels are
+//   copied from memory straight into one of three LDS stage buffers by buffer loads with an LDS
+//   destination (no registers, no VALU), two stages ahead.  Activation rows sit in LDS as
+//   16-byte units XOR-swizzled by the row, so the MFMA operand reads of 32 rows at one k spread
+//   over all banks.  Each wavefront issues the same six copies per stage, so one fixed wait
+//   count (the loads issued after them) tells it its copies have landed; a barrier then tells
+//   it everybody's have.  Weight chunks go to registers one stage ahead.  A load that may fall
+//   outside its buffer carries its whole offset in the range-checked VGPR operand, and every
+//   load past the data is aimed out of range: it returns zeros and touches no memory.
+//   Epilogue.  The int32 partials of a group are double-buffered by group parity: the MFMAs of
+//   group g+1 are issued before the VALU converts group g's partials and accumulates them with
+//   one FMA each, so the matrix unit and the VALU work side by side.  The FMA coefficients
+//   xs[row] * sw[col] come from one fp32 outer-product MFMA (v_mfma_f32_32x32x1_2b: block t =
+//   tile t), which lands each coefficient in the lane and register of its partial; the affine
+//   bias term xs*xsum[row] * (bw + 8 sw)[col] is a second outer product accumulated on the
+//   matrix unit.  Per element and group the VALU does two operations and the matrix unit the
+//   rest.  Signed codes (sym q, affine u-8) enter the MFMA as 16*q (nibble moved to the byte's
+//   top); the 1/16 is folded into sw, and affine's u = (u-8) + 8 is restored through the bias
+//   term.
 #include "w4a8_kernels.h"
 
 #include <type_traits>
@@ -43,30 +43,35 @@
 namespace w4a8 {
 namespace {
 
-constexpr int BM = 64;                     // activation rows per workgroup
-constexpr int kBN = 128;                   // output channels per workgroup (4 wavefronts x 32)
-constexpr int kStageSteps = 2;             // 64-wide k steps per LDS activation stage
-constexpr int kStageK = 64 * kStageSteps;
-constexpr int kLdsRow = kStageK + 16;      // padded LDS row of one activation stage (bytes)
-constexpr int kSets = 3;                   // activation stages in flight (registers and LDS)
-constexpr int kLead = kSets * kStageSteps; // k steps of weights and metadata loaded ahead
-constexpr uint32_t kRsrcCfg = 0x00020000u;
+constexpr int BM = 64;                      // activation rows per workgroup
+constexpr int kBN = 128;                    // output channels per workgroup (4 wavefronts x 32)
+constexpr int kSK = 256;                    // k per stage
+constexpr int kSteps = kSK / 64;            // 64-wide k steps per stage
+constexpr int kNS = 3;                      // LDS stage buffers
+constexpr int kAStage = BM * kSK;           // activation bytes of a stage (16 KiB)
+constexpr int kXOff = kAStage;              // xs [4 groups][64 rows] fp32, then xsum the same
+constexpr int kMOff = kAStage + 2048;       // weight metadata of the workgroup's two panels
+constexpr int kStageBytes = kAStage + 4096;
+constexpr int kCopiesPerStage = 6;          // LDS copies each wavefront issues per stage
+// Copies are issued two stages ahead, weight chunks three.  Loads a wavefront issues between its
+// copies of stage s and the wait at the top of stage s: the weight chunks of stage s+1, the
+// copies of stage s+1 and the weight chunks of stage s+2.
+constexpr int kVmAfterStage = 2 * kSteps + kCopiesPerStage;
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint64_t bytes) {
-    const uint32_t n = bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : static_cast<uint32_t>(bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, kRsrcCfg);
+// 64 lanes x 16 bytes to LDS byte address lds_addr + 16 * lane.  The destination goes to M0, so it
+// is made a scalar explicitly (otherwise the compiler wraps the copy in a loop over lanes).
+__device__ __forceinline__ void copy16(rsrc_t r, uint32_t lds_addr, int voff) {
+    const uint32_t a = __builtin_amdgcn_readfirstlane(lds_addr);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(uintptr_t)a, 16, voff, 0, 0, 0);
 }
 
-__device__ __forceinline__ v4i ld128(rsrc_t r, int voff, int soff) {
-    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ __forceinline__ uint32_t ld32(rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-}
-__device__ __forceinline__ uint32_t ld16(rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    // s_waitcnt vmcnt(N), expcnt and lgkmcnt left at their maxima
+    static_assert(N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <int FMT>
@@ -92,23 +97,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                                                       const int *__restrict__ xsum,
                                                       float *__restrict__ y,
                                                       int *__restrict__ d) {
-    constexpr int SPG = G / 64;                          // 64-wide k steps per group
-    constexpr int GPSt = kStageSteps / SPG;              // groups per activation stage
-    constexpr int kMD = 16 * (FMT == kFmtAffine ? 4 : 2); // meta dwords per panel and group
-    constexpr int kMB = (FMT == kFmtAffine) ? 4 : 2;     // meta bytes per channel and group
-    constexpr int kAJ = BM / 32;                         // 16-byte staging loads per thread
-    static_assert(kLead == 6 && kStageSteps == 2 && kLead % SPG == 0,
-                  "the unrolled loop covers three stages of two k steps");
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kSets][BM * kLdsRow];
-    // per stage: activation scales and sums of the workgroup's rows ([xs|xsum][group][row]) and
-    // the weight metadata of its two panels ([group][panel][row]), one dword per thread
-    __shared__ uint32_t lds_x[kSets][256];
-    __shared__ uint32_t lds_m[kSets][256];
+    constexpr int SPG = G / 64;                        // k steps per group
+    constexpr int GPS = kSteps / SPG;                  // groups per stage
+    constexpr int kMB = (FMT == kFmtAffine) ? 4 : 2;   // metadata bytes per channel and group
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kNS][kStageBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wn = wave;
 
     // Tile of this workgroup.  When the tile count is a multiple of the 8 XCDs, workgroup b runs
     // on XCD b % 8 and takes tile (b % 8) * (T / 8) + b / 8, so each XCD walks a contiguous run.
@@ -119,204 +115,218 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
     const int mt = bid % tiles_m, nt = bid / tiles_m;
 
-    const int m0 = mt * BM;                              // first activation row of the workgroup
-    const int r0 = m0;                                   // first activation row of the wavefront
-    const int c0 = nt * kBN + wn * 32;                   // first output channel of the wavefront
-    const bool active = r0 < m && c0 < geom.n_pad;       // wave-uniform
-    const int p = c0 / kPanelRows;                       // the wavefront's panel
+    const int k = geom.k;
+    const int ng = k / G;
+    const int nblk = (ng + 3) / 4;                     // metadata blocks of 4 groups
+    const int nsteps = k / 64;
+    const int nstages = (k + kSK - 1) / kSK;
+    const int m0 = mt * BM;
+    const int rows_wg = min(m - m0, BM);
+    const int c0 = nt * kBN + wave * 32;               // first output channel of the wavefront
+    const bool active = c0 < geom.n_pad;               // wave-uniform
     const int half = lane >> 5;
     const int r32 = lane & 31;
-    const int prow = (c0 % kPanelRows) + r32;            // lane's channel row inside the panel
-    const int k = geom.k;
+    const int pnl = wave >> 1;                         // the wavefront's panel in the workgroup
+    const int prow = (wave & 1) * 32 + r32;            // the lane's channel row in that panel
+    const int p = active ? c0 / kPanelRows : 0;        // the wavefront's panel
     const int kc = k / kChunkK;
-    const int ng = k / G;
-    const int nsteps = k / 64;
-    const int rows_wg = min(m - m0, BM);                 // valid rows of the workgroup
+    const int wg_p0 = nt * (kBN / kPanelRows);
+    const int wg_np = max(0, min(kBN / kPanelRows, geom.n_pad / kPanelRows - wg_p0));
 
-    // Descriptors rebased at the workgroup's rows / the wavefront's panel: offsets stay far below
-    // 2^31 and anything past the valid range reads as zero without touching memory.
-    const rsrc_t rq = make_rsrc(xq + (int64_t)m0 * k, (uint64_t)rows_wg * k);
-    const uint8_t *wbase = active ? packed + geom.off_codes + (int64_t)p * kc * 1024 : packed;
-    const rsrc_t rw = make_rsrc(wbase, active ? (uint64_t)kc * 1024 : 0);
-    const int w_off = half * 1024 + prow * 16;
+    // ---- descriptors (offsets rebased per workgroup / panel stay far below 2^31)
+    const rsrc_t ra = make_rsrc(xq + (int64_t)m0 * k, (uint64_t)rows_wg * k);
+    const rsrc_t rw = make_rsrc(packed + geom.off_codes + (int64_t)p * kc * 1024,
+                                active ? (uint64_t)kc * 1024 : 0);
+    const rsrc_t rmeta = make_rsrc(packed + geom.off_meta + (int64_t)wg_p0 * nblk * 64 * 4 * kMB,
+                                   (uint64_t)wg_np * nblk * 64 * 4 * kMB);
+    // copy 5 of a stage: xs (even wavefronts) or xsum (odd wavefronts, affine; else xs again)
+    const bool x_is_sum = (FMT == kFmtAffine || PARTIALS) && (wave & 1);
+    const void *xbase = x_is_sum ? static_cast<const void *>(xsum) : static_cast<const void *>(xs);
+    const rsrc_t rx = make_rsrc(xbase, xbase ? (uint64_t)ng * m * 4 : 0);
 
     uint4 cb = make_uint4(0u, 0u, 0u, 0u);
-    if (FMT == kFmtCodebook && active) {
-        const uint4 *cbp = reinterpret_cast<const uint4 *>(packed + geom.off_codebook);
-        cb = cbp[(int64_t)p * kPanelRows + prow];
+    if (FMT == kFmtCodebook && active)
+        cb = reinterpret_cast<const uint4 *>(packed + geom.off_codebook)[(int64_t)p * 64 + prow];
+
+    // ---- per-lane parts of the stage copies
+    // Activation copy i (0..3) of this wavefront covers rows 16*wave + 4i + lane/16; lane's LDS
+    // unit lane%16 of that row holds the row's k unit (lane%16) ^ (row%16).  Bytes past k need
+    // no care: they meet zero weights (the weight loads past k are out of range).
+    int a_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * wave + 4 * i + (lane >> 4);
+        a_off[i] = row * k + 16 * ((lane & 15) ^ (row & 15));
     }
-
-    // ---- activation stages: global -> register set -> LDS.  Thread t moves 16 bytes of row
-    // 32j + t/8 per j, eight threads per 128-byte row segment (whole cache lines).  LDS rows are
-    // padded to 144 bytes so the MFMA-layout reads (32 rows at one k offset per half wavefront)
-    // spread over the banks.
-    v4i stage_regs[kSets][kAJ];
-    uint32_t stage_x[kSets], stage_m[kSets];
-    const int a_row = tid >> 3, a_piece = tid & 7;
-    // Metadata staging: wave w loads xs (w < 2) or xsum (w >= 2) of group w & 1 of the stage for
-    // the 64 rows (one dword per lane), and thread t loads dword t of the stage's weight metadata
-    // block [group][panel][row] of the workgroup's two panels.  Loads that fall outside the data
-    // get an out-of-range offset (zeros, no memory access) instead of a branch.
-    constexpr uint32_t kOOB = 0x7FFFFFF0u;
-    const int x_which = wave >> 1, x_j = wave & 1;
-    const bool x_valid = x_j < GPSt && (x_which == 0 || FMT == kFmtAffine);
-    const int m_j = tid / (2 * kMD), m_pnl = (tid / kMD) & 1, m_d = tid % kMD;
-    const int wg_p0 = nt * (kBN / kPanelRows);           // first panel of the workgroup
-    const int wg_np = min(kBN / kPanelRows, geom.n_pad / kPanelRows - wg_p0);
-    const rsrc_t rmw = make_rsrc(packed + geom.off_meta + (int64_t)wg_p0 * ng * kPanelRows * kMB,
-                                 (uint64_t)wg_np * ng * kPanelRows * kMB);
-    // Every load in the main loop is issued unconditionally (a stage or step past the end reads
-    // zeros through the range check, or a clamped valid address): the waits the compiler places
-    // for one load then count exactly the loads issued after it, which keeps the deep prefetch
-    // in flight.  A load behind a branch would make those waits drain everything.
-    auto stage_load = [&](auto SET, int st) {
-        constexpr int set = decltype(SET)::value;
+    // scales/sums copy: lane holds group st*GPS + lane/16, rows 4*(lane%16) .. +3; groups past
+    // the last one are out of range of the descriptor (zeros)
+    const int x_off = ((lane >> 4) * m + m0 + 4 * (lane & 15)) * 4;
+    // metadata copy: block (st*GPS)/4 of the workgroup's panels (2-byte entries: both panels in
+    // one copy; 4-byte entries: panel wave & 1)
+    const int vp = (kMB == 2) ? (lane >> 5) : (wave & 1);
+    const int m_off = (kMB == 2) ? (vp * nblk * 512 + (lane & 31) * 16) : (vp * nblk * 1024 + lane * 16);
+    const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (lds_void *)&lds[0][0]));
+    auto issue_stage = [&](int st) __attribute__((always_inline)) {
+        const uint32_t buf = lds_base + (st % kNS) * kStageBytes;
 #pragma unroll
-        for (int j = 0; j < kAJ; ++j)
-            stage_regs[set][j] = ld128(rq, (32 * j + a_row) * k + a_piece * 16, st * kStageK);
-        const int gb = st * GPSt;                        // first group of the stage
-        const int gv = max(0, min(GPSt, ng - gb));       // its groups that exist
-        const float *xbase = x_which ? reinterpret_cast<const float *>(xsum) : xs;
-        const rsrc_t rx = make_rsrc(xbase + (int64_t)min(gb, ng - 1) * m, (uint64_t)gv * m * 4);
-        stage_x[set] = ld32(rx, x_valid ? (x_j * m + m0 + lane) * 4 : (int)kOOB, 0);
-        const bool mv = m_j < gv;
-        stage_m[set] = ld32(rmw, mv ? ((m_pnl * ng + gb + m_j) * kPanelRows * kMB + m_d * 4)
-                                    : (int)kOOB, 0);
-    };
-    auto stage_store = [&](auto SET) {
-        constexpr int set = decltype(SET)::value;
-#pragma unroll
-        for (int j = 0; j < kAJ; ++j)
-            *reinterpret_cast<v4i *>(&lds_a[set][(32 * j + a_row) * kLdsRow + a_piece * 16]) =
-                stage_regs[set][j];
-        lds_x[set][tid] = stage_x[set];
-        lds_m[set][tid] = stage_m[set];
-    };
-    // LDS offset of this lane's MFMA operands: row 32t + r32, k bytes 32*half + 16*h of
-    // the 64-wide step
-    const int a_lds = r32 * kLdsRow + 32 * half;
-
-    // ---- weight chunks, one k step each, loaded kLead steps ahead
-    v4i rb[kLead];                 // 16 weight bytes of the lane's channel
-    // the current group's outer-product operands, read from the staged metadata
-    float g_sw16 = 0.0f, g_xs = 0.0f, g_b2 = 0.0f, g_xsum = 0.0f;
-    auto load_b = [&](int slot, int step) { rb[slot] = ld128(rw, w_off, step * 2048); };
-
-    // prologue: stages 0..2 in flight, then weights and metadata, publish stage 0, start 3
-    stage_load(std::integral_constant<int, 0>(), 0);
-    stage_load(std::integral_constant<int, 1>(), 1);
-    stage_load(std::integral_constant<int, 2>(), 2);
-#pragma unroll
-    for (int i = 0; i < kLead; ++i) load_b(i, i);
-    stage_store(std::integral_constant<int, 0>());
-    __syncthreads();
-    stage_load(std::integral_constant<int, 0>(), 3);
-
-    v16i dt0 = {}, dt1 = {};   // int32 partials of the current group, tiles 0 and 1
-    v32f coef = {};            // [tile][16]: xs[row] * sw16[col] of the group held in dt0/dt1
-    v32f acc = {};             // [tile][16]: fp32 outputs
-    v32f bacc = {};            // [tile][16]: affine bias term
-
-    // The previous group's epilogue for tile T: convert and accumulate (or store the partials).
-    auto finish_tile = [&](auto TT, int g) {
-        constexpr int t = decltype(TT)::value;
-        const v16i &dt = t ? dt1 : dt0;
-        if (PARTIALS) {
-            // element e of tile t: row r0 + 32t + 8(e/4) + 4*half + e%4, channel c0 + r32
-            const int col = c0 + r32;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = r0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
-                if (row >= m || col >= geom.n) continue;
-                int v = (FMT == kFmtCodebook) ? dt[e] : (dt[e] >> 4);
-                if (FMT == kFmtAffine) v += 8 * xsum[(int64_t)g * m + row];
-                d[((int64_t)row * geom.n + col) * ng + g] = v;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[16 * t + e] =
-                    fmaf(static_cast<float>(dt[e]), coef[16 * t + e], acc[16 * t + e]);
-        }
+        for (int i = 0; i < 4; ++i)
+            copy16(ra, buf + (16 * wave + 4 * i) * kSK, a_off[i] + st * kSK);
+        copy16(rx, buf + kXOff + (x_is_sum ? 1024 : 0), x_off + st * GPS * m * 4);
+        const int blk = (st * GPS) / 4;
+        // (a block past the last reads the other panel's metadata or nothing: its groups have
+        // zero scales xs, so nothing from them reaches the output)
+        copy16(rmeta, buf + kMOff + ((kMB == 2) ? 0 : vp * 1024), m_off + blk * ((kMB == 2) ? 512 : 1024));
     };
 
-    // Publish stage st + 1 (register set (st+1)%3) into LDS buffer (st+1)%3, which stage st - 2
-    // used; once every wavefront is past the barrier, refill the set with stage st + 4.
-    auto stage_end = [&](auto SET, int st) {
-        stage_store(SET);
-        __syncthreads();
-        stage_load(SET, st + 1 + kSets);
-    };
+    // ---- weight chunks: register slot s % 12 holds step s (three stages)
+    constexpr int kRingSteps = 3 * kSteps;
+    v4i rb[kRingSteps];
+    const int w_off = (half * 64 + prow) * 16;     // steps past k are past the descriptor's range
+    auto load_b = [&](int slot, int step) { rb[slot] = ld128(rw, w_off + step * 2048); };
 
-    // One 64-wide k step s = 6q + I.
-    auto step = [&](auto II, int s) {
-        constexpr int I = decltype(II)::value;
-        constexpr int buf = I / 2;                       // LDS buffer and register set of s / 2
-        constexpr int sub = I % 2;
-        constexpr bool first = (I % SPG) == 0;           // first step of its group
-        constexpr bool last = (I % SPG) == SPG - 1;
-        if (sub == 0 && s > 0) stage_end(std::integral_constant<int, buf>(), s / 2 - 1);
-        const int g = s / SPG;
-        // Consume this step's ring slots first and refill them at once, so the loads for step
-        // s + kLead are in flight while this step computes.
-        v4i blo, bhi;
-        unpack_b<FMT>(rb[I], cb, blo, bhi);
-        load_b(I, s + kLead);
-        if (first && !PARTIALS) {
-            // group j of this stage: the lane's row scale / sum and its channel's metadata
-            constexpr int j = (I % kStageSteps) / SPG;
-            const int pnl = wn >> 1;
-            const uint32_t meta =
-                (kMB == 4) ? lds_m[buf][(j * 2 + pnl) * kPanelRows + prow]
-                           : reinterpret_cast<const uint16_t *>(lds_m[buf])[(j * 2 + pnl) * kPanelRows + prow];
-            const float sw = half_bits_to_float(meta & 0xFFFFu);
-            g_sw16 = (FMT == kFmtCodebook) ? sw : sw * 0.0625f;
-            g_xs = __builtin_bit_cast(float, lds_x[buf][j * 64 + lane]);
-            if (FMT == kFmtAffine) {
-                g_b2 = fmaf(8.0f, sw, half_bits_to_float(meta >> 16));
-                g_xsum = g_xs * static_cast<float>(static_cast<int>(lds_x[buf][128 + j * 64 + lane]));
-            }
-        }
-        if (s < nsteps && active) {
-            const uint8_t *ab = &lds_a[buf][a_lds + sub * 64];
-            const v4i a00 = *reinterpret_cast<const v4i *>(ab);
-            const v4i a01 = *reinterpret_cast<const v4i *>(ab + 16);
-            const v4i a10 = *reinterpret_cast<const v4i *>(ab + 32 * kLdsRow);
-            const v4i a11 = *reinterpret_cast<const v4i *>(ab + 32 * kLdsRow + 16);
-            const v16i z = {};
-            if (first && g > 0) finish_tile(std::integral_constant<int, 0>(), g - 1);
-            dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a00, blo, first ? z : dt0, 0, 0, 0);
-            dt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a01, bhi, dt0, 0, 0, 0);
-            if (first) {
-                if (g > 0) finish_tile(std::integral_constant<int, 1>(), g - 1);
-                if (!PARTIALS) {
-                    // coefficient tiles xs[row] * sw16[col] of group g, after the last read of
-                    // group g-1's coefficients
-                    const v32f zf = {};
-                    coef = __builtin_amdgcn_mfma_f32_32x32x1f32(g_xs, g_sw16, zf, 0, 0, 0);
+    v16i dt[2][2] = {};       // [group parity][tile] int32 partials
+    v32f coef = {};           // [tile][16]: xs[row] * sw16[col] of the group being finished
+    v32f acc = {};            // [tile][16]: fp32 outputs (the affine bias term accumulates here too)
+    const v32f zf = {};
+
+    // The epilogue of group g, whose partials are in dt[g & 1] and coefficients in coef.
+    // (PARTIALS: the int32 partials go to d instead, with the affine sums from xbuf)
+    auto finish = [&](auto PAR, int g, const uint8_t *xbuf) __attribute__((always_inline)) {
+        constexpr int par = decltype(PAR)::value;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (PARTIALS) {
+                const int col = c0 + r32;
+                const int gi = g % GPS;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int rl = 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+                    const int row = m0 + rl;
+                    if (!active || g >= ng || row >= m || col >= geom.n) continue;
+                    int v = (FMT == kFmtCodebook) ? dt[par][t][e] : (dt[par][t][e] >> 4);
+                    if (FMT == kFmtAffine)
+                        v += 8 * reinterpret_cast<const int *>(xbuf + kXOff + 1024)[gi * 64 + rl];
+                    d[((int64_t)row * geom.n + col) * ng + g] = v;
                 }
-            }
-            dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a10, blo, first ? z : dt1, 0, 0, 0);
-            dt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a11, bhi, dt1, 0, 0, 0);
-            if (last && FMT == kFmtAffine && !PARTIALS) {
-                // sum_g xs*xsum[row] * (bw + 8 sw)[col]: bias plus the u = (u-8) + 8 correction
-                bacc = __builtin_amdgcn_mfma_f32_32x32x1f32(g_xsum, g_b2, bacc, 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[16 * t + e] = fmaf(static_cast<float>(dt[par][t][e]), coef[16 * t + e],
+                                           acc[16 * t + e]);
             }
         }
     };
+    // The outer products of group g from a stage buffer's scales and metadata: its coefficients
+    // (into coef) and, affine, its bias term (into acc).
+    auto group_products = [&](int g, const uint8_t *buf) __attribute__((always_inline)) {
+        const int gi = g % GPS;                        // group inside the stage
+        const int bi = g % 4;                          // group inside the metadata block
+        const float xsv = reinterpret_cast<const float *>(buf + kXOff)[gi * 64 + lane];
+        uint32_t meta;
+        if (kMB == 2)
+            meta = reinterpret_cast<const uint16_t *>(buf + kMOff)[(pnl * 64 + prow) * 4 + bi];
+        else
+            meta = reinterpret_cast<const uint32_t *>(buf + kMOff)[(pnl * 64 + prow) * 4 + bi];
+        const float sw = half_bits_to_float(meta & 0xFFFFu);
+        const float sw16 = (FMT == kFmtCodebook) ? sw : sw * 0.0625f;
+        coef = __builtin_amdgcn_mfma_f32_32x32x1f32(xsv, sw16, zf, 0, 0, 0);
+        if (FMT == kFmtAffine) {
+            const int xsumv = reinterpret_cast<const int *>(buf + kXOff + 1024)[gi * 64 + lane];
+            const float b2 = fmaf(8.0f, sw, half_bits_to_float(meta >> 16));
+            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(xsv * static_cast<float>(xsumv), b2, acc,
+                                                        0, 0, 0);
+        }
+    };
 
-    for (int s = 0; s < nsteps; s += kLead) {
-        step(std::integral_constant<int, 0>(), s);
-        step(std::integral_constant<int, 1>(), s + 1);
-        step(std::integral_constant<int, 2>(), s + 2);
-        step(std::integral_constant<int, 3>(), s + 3);
-        step(std::integral_constant<int, 4>(), s + 4);
-        step(std::integral_constant<int, 5>(), s + 5);
+    // LDS offsets of this lane's activation operands in a stage buffer: step J, MFMA h (units
+    // 4J + 2 half + h of rows r32 (tile 0) and 32 + r32 (tile 1, 32 * kSK bytes on: the swizzle
+    // key row % 16 is the same)).
+    int a_rd[kSteps][2];
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            a_rd[j][h] = r32 * kSK + 16 * ((4 * j + 2 * half + h) ^ (r32 & 15));
+
+    // One 64-wide k step s = kSteps * st + J of stage st, whose LDS buffer and register-ring third
+    // are B = st % 3 (compile-time).  Steps past k run on zero weights.
+    auto step = [&](auto BB, auto JJ, int st) __attribute__((always_inline)) {
+        constexpr int B = decltype(BB)::value;
+        constexpr int J = decltype(JJ)::value;
+        constexpr int sub = J % SPG;                   // step inside its group
+        constexpr bool first = sub == 0;
+        constexpr bool last = sub == SPG - 1;
+        constexpr int par = (J / SPG) & 1;             // g & 1 (GPS is even)
+        const int s = st * kSteps + J;
+        const int g = s / SPG;
+        const uint8_t *buf = lds[B];
+        v4i blo, bhi;
+        unpack_b<FMT>(rb[B * kSteps + J], cb, blo, bhi);
+        load_b(B * kSteps + J, s + kRingSteps);        // the same step three stages on
+        const v4i a00 = *reinterpret_cast<const v4i *>(buf + a_rd[J][0]);
+        const v4i a01 = *reinterpret_cast<const v4i *>(buf + a_rd[J][1]);
+        const v4i a10 = *reinterpret_cast<const v4i *>(buf + a_rd[J][0] + 32 * kSK);
+        const v4i a11 = *reinterpret_cast<const v4i *>(buf + a_rd[J][1] + 32 * kSK);
+        const v16i z = {};
+        v16i &d0 = dt[par][0];
+        v16i &d1 = dt[par][1];
+        d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a00, blo, first ? z : d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a10, blo, first ? z : d1, 0, 0, 0);
+        d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a01, bhi, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a11, bhi, d1, 0, 0, 0);
+        if (PARTIALS) {
+            if (last) finish(std::integral_constant<int, par>(), g, buf);
+        } else {
+            // group g-1 finished on the VALU beside these MFMAs, then group g's products
+            if (first && g > 0) finish(std::integral_constant<int, par ^ 1>(), g - 1, buf);
+            if (last) group_products(g, buf);
+        }
+    };
+
+    // Stage st: this wavefront's copies of it have landed, then everybody's have; every
+    // wavefront is also done with the buffer of stage st - 1, which stage st + 2 refills.
+    auto stage = [&](auto BB, int st) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<kVmAfterStage>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_stage(st + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        step(BB, std::integral_constant<int, 0>(), st);
+        step(BB, std::integral_constant<int, 1>(), st);
+        step(BB, std::integral_constant<int, 2>(), st);
+        step(BB, std::integral_constant<int, 3>(), st);
+    };
+
+    // ---- prologue, in the loop's issue order: chunks of stage 0; copies of 0, chunks of 1;
+    // copies of 1, chunks of 2
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) load_b(j, j);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_stage(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) load_b(kSteps + j, kSteps + j);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_stage(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) load_b(2 * kSteps + j, 2 * kSteps + j);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Stages three at a time: the LDS buffer and the ring third are then compile-time (a runtime
+    // index into registers would make the compiler wait for every load in flight).  Up to two
+    // stages past the end run on zeros.
+    for (int st = 0; st < nstages; st += 3) {
+        stage(std::integral_constant<int, 0>(), st);
+        stage(std::integral_constant<int, 1>(), st + 1);
+        stage(std::integral_constant<int, 2>(), st + 2);
     }
-    if (!active) return;
-    finish_tile(std::integral_constant<int, 0>(), ng - 1);
-    finish_tile(std::integral_constant<int, 1>(), ng - 1);
-    if (PARTIALS) return;
+    __builtin_amdgcn_sched_barrier(0);
+    if (PARTIALS || !active) return;
+    // the last group's epilogue (the group count run is even: parity 1)
+    finish(std::integral_constant<int, 1>(), 0, nullptr);
 
     const int col = c0 + r32;
     if (col >= geom.n) return;
@@ -324,11 +334,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int row = r0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
-            if (row >= m) continue;
-            float v = acc[16 * t + e];
-            if (FMT == kFmtAffine) v += bacc[16 * t + e];
-            y[(int64_t)row * geom.n + col] = v;
+            const int row = m0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+            if (row < m) y[(int64_t)row * geom.n + col] = acc[16 * t + e];
         }
     }
 }

@@ -24,11 +24,11 @@
 namespace w4a8 {
 namespace {
 
-constexpr int kBatchGroups = 4;   // groups whose chunks are loaded before any is consumed
+constexpr int kRing = 4;   // groups whose loads are in flight ahead of the one consumed
 
 template <int FMT>
-__device__ __forceinline__ int dot_chunk(uint4 v, const int *__restrict__ xc, uint4 cb, int acc) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+__device__ __forceinline__ int dot_chunk(v4i v, const int *__restrict__ xc, uint4 cb, int acc) {
+    const uint32_t w[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         uint32_t lo, hi;
@@ -58,87 +58,124 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
                                                       int *__restrict__ d) {
     constexpr int kChunksPerGroup = G / kChunkK;
     constexpr int kLanesPerGroup = G / 4;
-    constexpr int kLdsQuads = FUSED ? kFusedMaxK / 4 : 1;
-    constexpr int kLdsGroups = FUSED ? kFusedMaxK / G : 1;
-    __shared__ __attribute__((aligned(16))) int lds_xq[kLdsQuads];
-    __shared__ float lds_xs[kLdsGroups];
-    __shared__ int lds_xsum[kLdsGroups];
+    // Fused: activation quads (4 values) per lane that a wavefront quantizes, at most (the
+    // launcher checks that the wavefront's groups fit).
+    constexpr int kXQ = FUSED ? kFusedQuadsPerLane : 1;
+    constexpr int kXG = kXQ * 64 / kLanesPerGroup;           // groups per wavefront, at most
+    // wavefront-private codes, scales and sums of its own groups (fused kernel)
+    __shared__ __attribute__((aligned(16))) int lds_xq[FUSED ? W : 1][kXQ * 64];
+    __shared__ float lds_xs[FUSED ? W : 1][kXG];
+    __shared__ int lds_xsum[FUSED ? W : 1][kXG];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int p = blockIdx.x;
     const int kc = geom.k / kChunkK;
     const int ng = geom.k / G;
-    const int g0 = wave * ng / W;
-    const int g1 = (wave + 1) * ng / W;
+    // Wavefront w owns groups [g0, g1), split in whole metadata blocks of 4 groups (which also
+    // keeps each 128-wide rotation block inside one wavefront).
+    const int nblk = (ng + 3) / 4;
+    const int g0 = min(ng, (wave * nblk / W) * 4);
+    const int g1 = min(ng, ((wave + 1) * nblk / W) * 4);
     const int64_t row = (int64_t)p * kPanelRows + lane;
 
-    const uint4 *wp = reinterpret_cast<const uint4 *>(packed + geom.off_codes) +
-                      (int64_t)p * kc * kPanelRows + lane;
-    const uint8_t *meta = packed + geom.off_meta +
-                          ((int64_t)p * ng * kPanelRows + lane) * geom.meta_bytes;
+    constexpr int kMetaBytes = (FMT == kFmtAffine) ? 4 : 2;
+    constexpr int kRowBlk = 4 * kMetaBytes;          // one row's metadata block (4 groups)
+    // the panel's codes and metadata; a load at kOOB returns zeros without a memory access
+    const rsrc_t rw = make_rsrc(packed + geom.off_codes + (int64_t)p * kc * 1024,
+                                (uint64_t)kc * 1024);
+    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (int64_t)p * nblk * kPanelRows * kRowBlk,
+                                (uint64_t)nblk * kPanelRows * kRowBlk);
     uint4 cb = make_uint4(0u, 0u, 0u, 0u);
     if (FMT == kFmtCodebook)
         cb = *reinterpret_cast<const uint4 *>(packed + geom.off_codebook + row * 16);
 
-    uint4 v[kBatchGroups * kChunksPerGroup];
-    // A batch always issues the same loads (slots past the wavefront's groups re-read a valid
-    // chunk of the panel and are never used): with no load behind a branch, the compiler's waits
-    // count exactly the loads issued after the one they wait for.
-    auto load_batch = [&](int gb) {
-        const int glast = max(g1 - 1, 0);
-#pragma unroll
-        for (int i = 0; i < kBatchGroups; ++i) {
-            const int g = min(gb + i, glast);
-#pragma unroll
-            for (int c = 0; c < kChunksPerGroup; ++c)
-                v[i * kChunksPerGroup + c] = wp[(int64_t)(g * kChunksPerGroup + c) * kPanelRows];
-        }
-    };
-    // Fused: the thread's first activation quad is loaded before the weight batch.  Loads complete
-    // in issue order, so the prepass below then waits for x only, with the whole batch still in
-    // flight.  The compiler would sink an ordinary load below the batch (and then drain every
-    // load before the prepass), so this one is issued by hand, ahead of the batch (the memory
-    // clobber keeps the batch behind it), and waited for by hand: vmcnt(batch loads).
-    const float4 *x4 = reinterpret_cast<const float4 *>(x);
-    const int nq = geom.k / 4;
-    v4f xr = {0.f, 0.f, 0.f, 0.f};
-    if (FUSED) {
-        const float4 *xp = x4 + min(static_cast<int>(threadIdx.x), nq - 1);
-        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(xr) : "v"(xp) : "memory");
-    }
-    load_batch(g0);
-    if (FUSED) asm volatile("s_waitcnt vmcnt(%1)" : "+v"(xr) : "n"(kBatchGroups * kChunksPerGroup));
-    const float4 xv0 = make_float4(xr[0], xr[1], xr[2], xr[3]);
-
-    const int *xq4;                 // activation codes, 4 per int
-    const float *xsv;               // per-group scales
-    const int *xsumv;               // per-group sums
-    if (FUSED) {
-        // the prepass of the row, while the first weight batch is in flight
-        for (int t = threadIdx.x; t < nq; t += 64 * W) {
-            float scale;
-            int sum;
-            const float4 xv = (t == static_cast<int>(threadIdx.x)) ? xv0 : x4[t];
-            const int codes = prep_quad<G, ROT>(xv, t & 63, scale, sum);
-            lds_xq[t] = codes;
-            const bool leader = (t & (kLanesPerGroup - 1)) == 0;
-            if (leader) {
-                lds_xs[t / kLanesPerGroup] = scale;
-                lds_xsum[t / kLanesPerGroup] = sum;
+    // Ring of kRing = 4 groups (one metadata block) in flight: slot i holds a group's chunks,
+    // and slot 0's load of a block's first group is preceded by the load of the block's
+    // metadata (8 or 16 bytes per row) into mnext.  Loads complete in issue order, so the wait
+    // for a group's chunks covers its metadata too, and the loads of the groups behind it stay
+    // in flight.  Every load is issued unconditionally (a group past the wavefront's range loads
+    // at kOOB: zeros, no memory traffic, never consumed): with no load behind a branch, the
+    // compiler's waits count exactly the loads issued after the one they wait for.
+    static_assert(kRing == 4, "a ring pass is one metadata block");
+    v4i v[kRing][kChunksPerGroup];
+    v4i mcur = {0, 0, 0, 0}, mnext = {0, 0, 0, 0};  // metadata blocks: this pass, the next
+    auto load_group = [&](int slot, int g) {
+        const bool in = g < g1;
+        if (slot == 0) {
+            const int mo = in ? ((g / 4) * kPanelRows + lane) * kRowBlk : kOOB;
+            if (kRowBlk == 16) {
+                mnext = ld128(rm, mo);
+            } else {
+                const v2i m2 = ld64(rm, mo);
+                mnext = v4i{m2[0], m2[1], 0, 0};
             }
-            if (blockIdx.x == 0) {
-                reinterpret_cast<int *>(xq)[t] = codes;
+        }
+#pragma unroll
+        for (int c = 0; c < kChunksPerGroup; ++c)
+            v[slot][c] = ld128(rw, in ? ((g * kChunksPerGroup + c) * kPanelRows + lane) * 16 : kOOB);
+    };
+    // Issue order is pinned with scheduling barriers (loads complete in issue order, and every
+    // wait above counts on it).  Fused: the lane's activation quads come first (those past the
+    // wavefront's groups at kOOB), so the prepass below waits for x only, with the ring still in
+    // flight behind it.
+    const int qbase = g0 * kLanesPerGroup;            // first quad of the wavefront's groups
+    const int nqw = (g1 - g0) * kLanesPerGroup;       // its quads
+    v4i xr[kXQ];
+    if (FUSED) {
+        const rsrc_t rx = make_rsrc(x, (uint64_t)geom.k * 4);
+#pragma unroll
+        for (int i = 0; i < kXQ; ++i) {
+            const int t = lane + 64 * i;
+            xr[i] = ld128(rx, t < nqw ? (qbase + t) * 16 : kOOB);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+        load_group(i, g0 + i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    mcur = mnext;
+
+    // activation codes (4 per int), scales and sums, indexed by the global quad / group
+    const int *xq4;
+    const float *xsv;
+    const int *xsumv;
+    if (FUSED) {
+        // The prepass of the wavefront's own groups, while the ring is in flight.  A group's
+        // G/4 lanes, and a rotation block's 32 lanes, are aligned runs of the wavefront that are
+        // all active or all inactive.  No other wavefront reads these codes: no barrier.
+#pragma unroll
+        for (int i = 0; i < kXQ; ++i) {
+            const int t = lane + 64 * i;
+            if (t < nqw) {
+                float scale;
+                int sum;
+                // (the whole vector is reinterpreted: clang's bit cast of one vector element
+                // reads element 0 whatever the index)
+                const v4f xf = __builtin_bit_cast(v4f, xr[i]);
+                const float4 xv = make_float4(xf[0], xf[1], xf[2], xf[3]);
+                const int codes = prep_quad<G, ROT>(xv, lane, scale, sum);
+                lds_xq[wave][t] = codes;
+                const bool leader = (t & (kLanesPerGroup - 1)) == 0;
                 if (leader) {
-                    xs[t / kLanesPerGroup] = scale;
-                    xsum[t / kLanesPerGroup] = sum;
+                    lds_xs[wave][t / kLanesPerGroup] = scale;
+                    lds_xsum[wave][t / kLanesPerGroup] = sum;
+                }
+                if (blockIdx.x == 0) {
+                    reinterpret_cast<int *>(xq)[qbase + t] = codes;
+                    if (leader) {
+                        xs[g0 + t / kLanesPerGroup] = scale;
+                        xsum[g0 + t / kLanesPerGroup] = sum;
+                    }
                 }
             }
         }
-        __syncthreads();
-        xq4 = lds_xq;
-        xsv = lds_xs;
-        xsumv = lds_xsum;
+        __builtin_amdgcn_wave_barrier();
+        xq4 = &lds_xq[wave][0] - qbase;
+        xsv = &lds_xs[wave][0] - g0;
+        xsumv = &lds_xsum[wave][0] - g0;
     } else {
         xq4 = reinterpret_cast<const int *>(xq);
         xsv = xs;
@@ -147,19 +184,20 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
 
     float acc = 0.0f;    // sum over groups of xs * sw * (partial as computed, see kOut)
     float bacc = 0.0f;   // AFFINE: sum over groups of xs * xsum * bw
-    for (int gb = g0; gb < g1; gb += kBatchGroups) {
-        if (gb > g0) load_batch(gb);
-        const int nb = min(kBatchGroups, g1 - gb);
+    for (int gb = g0; gb < g1; gb += kRing) {
 #pragma unroll
-        for (int i = 0; i < kBatchGroups; ++i) {
-            if (i < nb) {
-                const int g = gb + i;
+        for (int i = 0; i < kRing; ++i) {
+            const int g = gb + i;
+            // the group's metadata entry: element i of the row's block (2-byte entries pack two
+            // to a dword)
+            const uint32_t mv = (kRowBlk == 16) ? static_cast<uint32_t>(mcur[i])
+                                                : static_cast<uint32_t>(mcur[i / 2]) >> (16 * (i & 1));
+            if (g < g1) {
                 int dot = 0;
 #pragma unroll
                 for (int c = 0; c < kChunksPerGroup; ++c)
-                    dot = dot_chunk<FMT>(v[i * kChunksPerGroup + c],
-                                         xq4 + (g * kChunksPerGroup + c) * (kChunkK / 4), cb,
-                                         dot);
+                    dot = dot_chunk<FMT>(v[i][c], xq4 + (g * kChunksPerGroup + c) * (kChunkK / 4),
+                                         cb, dot);
                 if (PARTIALS) {
                     // sym/affine dot is 16x the signed-code partial; affine adds back 8*xsum.
                     int part = (FMT == kFmtCodebook) ? dot : (dot >> 4);
@@ -167,24 +205,22 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
                     if (row < geom.n) d[row * ng + g] = part;
                 } else {
                     const float a = xsv[g];
+                    const float sw = half_bits_to_float(mv & 0xFFFFu);
                     if (FMT == kFmtAffine) {
-                        const uint32_t mb = *reinterpret_cast<const uint32_t *>(
-                            meta + (int64_t)g * kPanelRows * 4);
-                        const float sw = half_bits_to_float(mb & 0xFFFFu);
-                        const float bw = half_bits_to_float(mb >> 16);
+                        const float bw = half_bits_to_float(mv >> 16);
                         const int s = xsumv[g];
                         // 16*D_u = dot + 128*xsum, exact in int32
                         acc = fmaf(a * sw, static_cast<float>(dot + 128 * s), acc);
                         bacc = fmaf(a * static_cast<float>(s), bw, bacc);
                     } else {
-                        const uint32_t mb = *reinterpret_cast<const uint16_t *>(
-                            meta + (int64_t)g * kPanelRows * 2);
-                        const float sw = half_bits_to_float(mb);
                         acc = fmaf(a * sw, static_cast<float>(dot), acc);
                     }
                 }
             }
+            load_group(i, g + kRing);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        mcur = mnext;
     }
     if (PARTIALS) return;
 
@@ -206,18 +242,28 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
     }
 }
 
+template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT>
+hipError_t launch_wk(const Geom &g, const uint8_t *packed, const float *x, int8_t *xq, float *xs,
+                     int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
+    if (FUSED) {
+        // the wavefront's quads must fit its kFusedQuadsPerLane registers per lane
+        const int nblk = (g.k / G + 3) / 4;
+        const int max_quads = (nblk + W - 1) / W * 4 * (G / 4);
+        if (max_quads > kFusedQuadsPerLane * 64) return hipErrorInvalidValue;
+    }
+    const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
+    gemv_kernel<FMT, G, W, PARTIALS, FUSED, ROT><<<grid, 64 * W, 0, stream>>>(
+        packed, g, x, xq, xs, xsum, y, d);
+    return hipGetLastError();
+}
+
 template <int FMT, int G, bool PARTIALS, bool FUSED, bool ROT>
 hipError_t launch_w(const Geom &g, const uint8_t *packed, const float *x, int8_t *xq, float *xs,
                     int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
-    const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
-    const int ng = g.k / G;
-    if (ng >= 8)
-        gemv_kernel<FMT, G, 8, PARTIALS, FUSED, ROT><<<grid, 512, 0, stream>>>(
-            packed, g, x, xq, xs, xsum, y, d);
-    else
-        gemv_kernel<FMT, G, 4, PARTIALS, FUSED, ROT><<<grid, 256, 0, stream>>>(
-            packed, g, x, xq, xs, xsum, y, d);
-    return hipGetLastError();
+    // W = 8 once there are 6 metadata blocks (some wavefronts may own none), else 4
+    if ((g.k / G + 3) / 4 >= 6)
+        return launch_wk<FMT, G, 8, PARTIALS, FUSED, ROT>(g, packed, x, xq, xs, xsum, y, d, stream);
+    return launch_wk<FMT, G, 4, PARTIALS, FUSED, ROT>(g, packed, x, xq, xs, xsum, y, d, stream);
 }
 
 template <int FMT, bool PARTIALS, bool FUSED, bool ROT>

@@ -4,7 +4,8 @@
 // The pages' lesson ("cactus PR #697", follow-up commits on the interleaved lm_head and on the
 // single runtime weight format): the layout is the largest single lever, one format should feed
 // every kernel, and it should be built once at load.  Here a panel is 64 output rows; its bytes
-// are ordered by 32-wide k chunk, then row, 16 bytes per (row, chunk).  A decode wavefront then
+// are ordered by 32-wide k chunk, then row, 16 bytes per (row, chunk); the per-group metadata is
+// ordered by block of 4 groups, then row, so a row's four entries are one 8- or 16-byte load.  A decode wavefront then
 // reads one contiguous KiB per chunk (one row per lane), and a 32x32x32 int8 MFMA B fragment for
 // 32 rows and a 64-wide k group is two contiguous 512-byte runs.  Inside a chunk the low nibbles
 // of the four dwords hold k = 0..15 and the high nibbles k = 16..31, so each half of the chunk
@@ -45,20 +46,26 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t *__restri
     }
 }
 
+// Metadata in blocks of 4 groups: per panel, per block j, per panel row, the entries of groups
+// 4j .. 4j+3 (zero past the last group), so one 8- or 16-byte load gives a row four groups.
 __global__ __launch_bounds__(256) void pack_meta_kernel(const uint16_t *__restrict__ scales,
                                                         const uint16_t *__restrict__ bias,
                                                         int n, int ng, int64_t total,
                                                         uint8_t *__restrict__ out) {
+    const int nblk = (ng + 3) / 4;
     for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
          t += (int64_t)gridDim.x * blockDim.x) {
-        const int r = static_cast<int>(t % kPanelRows);
-        const int64_t rest = t / kPanelRows;
-        const int g = static_cast<int>(rest % ng);
-        const int64_t p = rest / ng;
+        const int i = static_cast<int>(t & 3);
+        const int r = static_cast<int>((t >> 2) % kPanelRows);
+        const int64_t rest = (t >> 2) / kPanelRows;
+        const int j = static_cast<int>(rest % nblk);
+        const int64_t p = rest / nblk;
         const int64_t row = p * kPanelRows + r;
-        const uint32_t s = row < n ? scales[row * ng + g] : 0u;
+        const int g = 4 * j + i;
+        const bool valid = row < n && g < ng;
+        const uint32_t s = valid ? scales[row * ng + g] : 0u;
         if (bias) {
-            const uint32_t b = row < n ? bias[row * ng + g] : 0u;
+            const uint32_t b = valid ? bias[row * ng + g] : 0u;
             reinterpret_cast<uint32_t *>(out)[t] = s | (b << 16);
         } else {
             reinterpret_cast<uint16_t *>(out)[t] = static_cast<uint16_t>(s);
@@ -90,7 +97,7 @@ hipError_t launch_pack(const Geom &g, const uint8_t *codes, const uint16_t *scal
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int ng = g.k / g.group;
-    const int64_t metas = (int64_t)g.n_pad * ng;
+    const int64_t metas = (int64_t)g.n_pad * ((ng + 3) / 4) * 4;
     pack_meta_kernel<<<grid_for(metas), 256, 0, stream>>>(
         scales, g.fmt == kFmtAffine ? bias : nullptr, g.n, ng, metas, packed + g.off_meta);
     e = hipGetLastError();

@@ -18,11 +18,46 @@ struct Geom {
     uint64_t off_codes, off_meta, off_codebook;
 };
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
+
+// ---- buffer loads
+//
+// A raw buffer descriptor (base, byte range) makes every load whose VGPR offset lies outside the
+// range return zeros without touching memory.  The range check covers the VGPR offset and the
+// instruction offset only, not the SGPR offset, so a load that may fall outside its buffer keeps
+// its whole offset in the VGPR operand.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kRsrcCfg = 0x00020000u;
+constexpr int kOOB = 0x7FFFFFF0;   // a VGPR offset past every range: the load returns zeros
+
+// The descriptor is built from wave-uniform values (read from the first lane), so it lives in
+// SGPRs: a descriptor the compiler places in VGPRs makes it loop over the lanes at every use.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(
+        bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : static_cast<uint32_t>(bytes));
+    void *p = reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, n, kRsrcCfg);
+}
+__device__ __forceinline__ v4i ld128(rsrc_t r, int voff) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+__device__ __forceinline__ v2i ld64(rsrc_t r, int voff) {
+    return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+}
+__device__ __forceinline__ uint32_t ld32(rsrc_t r, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld16(rsrc_t r, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+}
 
 // ---- 4-bit unpack helpers (packed chunk format: dword j, byte b holds the code of k = 4j+b in
 // its low nibble and of k = 16+4j+b in its high nibble).
@@ -135,6 +170,7 @@ hipError_t launch_gemv(const Geom &g, const uint8_t *packed, const int8_t *xq, c
 // head) the separate prepass launch costs less than the repeats.
 constexpr int kFusedMaxK = 16384;
 constexpr int kFusedMaxPanels = 2048;
+constexpr int kFusedQuadsPerLane = 8;   // activation quads one lane of the fused GEMV quantizes
 hipError_t launch_gemv_fused(const Geom &g, const uint8_t *packed, const float *x, int hadamard,
                              int8_t *xq, float *xs, int32_t *xsum, float *y, hipStream_t stream);
 

@@ -82,9 +82,11 @@ typedef enum {
  *             its low nibble and of k = 32c+16+4j+b in its high nibble.  SYM stores q's
  *             two's-complement nibble, AFFINE stores u XOR 8 (= u - 8 as a signed nibble),
  *             CODEBOOK stores the index.
- *   meta      at off_meta: per panel, per group g, per panel row: meta_bytes bytes.  SYM and
- *             CODEBOOK: the fp16 scale.  AFFINE: a dword, fp16 scale in the low half and fp16
- *             bias in the high half.
+ *   meta      at off_meta: per panel, per block j of 4 groups (ceil((k/group)/4) blocks), per
+ *             panel row: the 4 entries of groups 4j .. 4j+3, meta_bytes bytes each (entries
+ *             past the last group are zero).  SYM and CODEBOOK: the fp16 scale.  AFFINE: a
+ *             dword, fp16 scale in the low half and fp16 bias in the high half.  A row's block
+ *             is one 8- or 16-byte load.
  *   codebook  at off_codebook (CODEBOOK only): int8 [n_pad][16].
  * Rows n >= n of the padded last panel hold zero codes, zero scales and zero codebooks.
  */
@@ -156,9 +158,10 @@ w4a8_status w4a8_gemv(const w4a8_layout *L, const void *packed, const int8_t *xq
  * Prefill GEMM: y[r][n] for r < m, n < L->n (definitions above).
  *   xq int8 [m][k], xs fp32 [k/group][m], xsum int32 [k/group][m] from w4a8_prep
  *   y  fp32 [m][L->n]
- * m == 0 is a no-op (xq, xs, xsum and y may then be NULL).  Source: "cactus PR #697",
- * section "Quantized matmul" (fused GEMM, M>1,
- * raw int32 partials rescaled per tile); "geistlib issue #500" (native int8 GEMM for prefill).
+ * m == 0 is a no-op (xq, xs, xsum and y may then be NULL).  W4A8_ERR_UNSUPPORTED when
+ * m * (k/group + 16) * 4 bytes exceed 2^31 - 16.  Source: "cactus PR #697", section
+ * "Quantized matmul" (fused GEMM, M>1, raw int32 partials rescaled per tile); "geistlib issue
+ * #500" (native int8 GEMM for prefill).
  */
 w4a8_status w4a8_gemm(const w4a8_layout *L, const void *packed, int32_t m, const int8_t *xq,
                       const float *xs, const int32_t *xsum, float *y, void *stream);

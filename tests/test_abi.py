@@ -69,6 +69,9 @@ def test_layout_sizes():
     assert L.bytes == L.off_codebook + 1024 * 16
     for off in (L.off_meta, L.off_codebook, L.bytes):
         assert off % 256 == 0
+    # metadata comes in blocks of 4 groups: 5 groups take 2 blocks (the last one padded)
+    L = w4a8.packed_layout(w4a8.SYM, 64, 320, 64)
+    assert L.off_meta == 64 * 160 and L.bytes == L.off_meta + 64 * 2 * 4 * 2
 
 
 @pytest.mark.parametrize("args", [

@@ -172,9 +172,12 @@ def test_pack_round_trip_and_padding():
             codes ^= 8                             # affine stores u XOR 8
         assert np.array_equal(codes[:n], synth.unpack_nibbles(L["codes"])), name
         mb = lay.meta_bytes
-        meta = buf[lay.off_meta:lay.off_meta + npad * ng * mb]
-        meta = meta.view(np.uint32 if mb == 4 else np.uint16).reshape(npad // 64, ng, 64)
-        meta = meta.transpose(0, 2, 1).reshape(npad, ng)
+        nblk = (ng + 3) // 4                       # metadata blocks of 4 groups
+        meta = buf[lay.off_meta:lay.off_meta + npad * nblk * 4 * mb]
+        meta = meta.view(np.uint32 if mb == 4 else np.uint16).reshape(npad // 64, nblk, 64, 4)
+        meta = meta.transpose(0, 2, 1, 3).reshape(npad, nblk * 4)
+        assert not meta[:, ng:].any()              # the padded entries of the last block
+        meta = meta[:, :ng]
         sc = (meta & 0xFFFF).astype(np.uint16)
         assert np.array_equal(sc[:n], L["scales"].view(np.uint16)), name
         assert not sc[n:].any()
