@@ -47,7 +47,8 @@ __device__ __forceinline__ int dot_chunk(v4i v, const int *__restrict__ xc, uint
 
 // FUSED: x is the fp32 activation row; xq/xs/xsum are outputs written by workgroup 0.
 // Otherwise xq/xs/xsum are the prepass outputs (inputs here) and x is unused.
-template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT>
+// XQ (fused only): activation quads per lane, enough for the wavefront's groups.
+template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, int XQ>
 __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict__ packed,
                                                       const Geom geom,
                                                       const float *__restrict__ x,
@@ -59,8 +60,8 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
     constexpr int kChunksPerGroup = G / kChunkK;
     constexpr int kLanesPerGroup = G / 4;
     // Fused: activation quads (4 values) per lane that a wavefront quantizes, at most (the
-    // launcher checks that the wavefront's groups fit).
-    constexpr int kXQ = FUSED ? kFusedQuadsPerLane : 1;
+    // launcher sizes XQ to the wavefront's groups: every one of these loads is issued).
+    constexpr int kXQ = FUSED ? XQ : 1;
     constexpr int kXG = kXQ * 64 / kLanesPerGroup;           // groups per wavefront, at most
     // wavefront-private codes, scales and sums of its own groups (fused kernel)
     __shared__ __attribute__((aligned(16))) int lds_xq[FUSED ? W : 1][kXQ * 64];
@@ -242,19 +243,32 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
     }
 }
 
+template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, int XQ>
+hipError_t launch_k(const Geom &g, const uint8_t *packed, const float *x, int8_t *xq, float *xs,
+                    int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
+    const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
+    gemv_kernel<FMT, G, W, PARTIALS, FUSED, ROT, XQ><<<grid, 64 * W, 0, stream>>>(
+        packed, g, x, xq, xs, xsum, y, d);
+    return hipGetLastError();
+}
+
 template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT>
 hipError_t launch_wk(const Geom &g, const uint8_t *packed, const float *x, int8_t *xq, float *xs,
                      int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
-    if (FUSED) {
-        // the wavefront's quads must fit its kFusedQuadsPerLane registers per lane
-        const int nblk = (g.k / G + 3) / 4;
-        const int max_quads = (nblk + W - 1) / W * 4 * (G / 4);
-        if (max_quads > kFusedQuadsPerLane * 64) return hipErrorInvalidValue;
-    }
-    const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
-    gemv_kernel<FMT, G, W, PARTIALS, FUSED, ROT><<<grid, 64 * W, 0, stream>>>(
-        packed, g, x, xq, xs, xsum, y, d);
-    return hipGetLastError();
+    if (!FUSED) return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 1>(g, packed, x, xq, xs, xsum, y, d, stream);
+    // the quads of the largest wavefront share (whole metadata blocks of 4 groups)
+    const int nblk = (g.k / G + 3) / 4;
+    const int max_quads = (nblk + W - 1) / W * 4 * (G / 4);
+    if (max_quads <= 64)
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 1>(g, packed, x, xq, xs, xsum, y, d, stream);
+    if (max_quads <= 128)
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 2>(g, packed, x, xq, xs, xsum, y, d, stream);
+    if (max_quads <= 256)
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 4>(g, packed, x, xq, xs, xsum, y, d, stream);
+    if (max_quads <= 64 * kFusedQuadsPerLane)
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, kFusedQuadsPerLane>(g, packed, x, xq, xs,
+                                                                            xsum, y, d, stream);
+    return hipErrorInvalidValue;
 }
 
 template <int FMT, int G, bool PARTIALS, bool FUSED, bool ROT>

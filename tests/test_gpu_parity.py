@@ -124,6 +124,9 @@ LINEAR_CASES = [
     ("C3a", dict(m=1, n=200, k=640), True),
     ("C4", dict(m=1, n=320, k=768), False),
     ("C4", dict(m=1, n=130, k=1536), True),
+    ("C2a", dict(n=320, k=4096), True),           # fused, 2 activation quads per lane
+    ("C4", dict(m=1, n=130, k=8192), True),        # fused with rotation, 4 quads per lane
+    ("C1", dict(n=192, k=16384), True),            # fused at its k bound, 8 quads per lane
     ("C1", dict(n=64, k=16448), True),
     ("C3a", dict(m=65, n=1000, k=1280), True),
     ("C4", dict(m=200, n=448, k=1536), False),
