@@ -7,6 +7,8 @@ Every translation unit is compiled in parallel, then linked into
   -target-feature -packed-fp32-ops            no packed fp32 VALU instructions in device code
   -amdgpu-mfma-vgpr-form                      MFMA results in VGPRs, where the VALU epilogue reads
                                               them (no accumulator-register copies)
+The GEMM kernels are also compiled to device assembly, and the build fails if any of them uses
+scratch (see NO_SCRATCH).
 """
 from __future__ import annotations
 
@@ -41,6 +43,30 @@ def _quiet(stderr: str) -> str:
     return "\n".join(l for l in stderr.splitlines() if "packed-fp32-ops" not in l)
 
 
+# The GEMM's stage wait counts the vector memory accesses it issues itself; a register spill
+# would add scratch accesses to that count and make the wait too weak.  Its device assembly is
+# therefore built too and every GEMM kernel must show a zero private segment (no scratch).
+NO_SCRATCH = {"gemm.hip": "gemm_kernel"}
+
+
+def check_no_scratch(asm_path: str, kernel_substr: str) -> None:
+    name = None
+    bad = []
+    with open(asm_path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line.startswith(".amdhsa_kernel "):
+                name = line.split()[1]
+            elif line.startswith(".amdhsa_private_segment_fixed_size") and name \
+                    and kernel_substr in name and int(line.split()[1]) != 0:
+                bad.append((name, int(line.split()[1])))
+            elif line.startswith(".end_amdhsa_kernel"):
+                name = None
+    if bad:
+        raise RuntimeError("kernels use scratch (register spills), which their wait counts do not "
+                           "allow: " + ", ".join(f"{n} ({b} bytes)" for n, b in bad))
+
+
 def build(verbose: bool = False, extra_flags=None) -> str:
     """Compile every HIP source and link libw4a8.so.  Always rebuilds.  Returns the path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -48,6 +74,14 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     flags = HIPCC_FLAGS + list(extra_flags or [])
     procs = []
     objs = []
+    asm_checks = []
+    for src, kernel in NO_SCRATCH.items():
+        asm = os.path.join(BUILD_DIR, src.replace(".hip", ".device.s"))
+        asm_checks.append((asm, kernel))
+        cmd = [cc] + flags + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm]
+        procs.append((src + " (device assembly)",
+                      subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                       text=True)))
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
@@ -66,6 +100,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
             print(err)
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+    for asm, kernel in asm_checks:
+        check_no_scratch(asm, kernel)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)

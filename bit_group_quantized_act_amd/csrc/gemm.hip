@@ -53,6 +53,9 @@ constexpr int kXOff = kAStage;              // xs [4 groups][64 rows] fp32, then
 constexpr int kMOff = kAStage + 2048;       // weight metadata of the workgroup's two panels
 constexpr int kStageBytes = kAStage + 4096;
 constexpr int kCopiesPerStage = 6;          // LDS copies each wavefront issues per stage
+// The count is exact only while the kernel makes no other vector memory access in the loop: a
+// register spill (scratch loads and stores count too) would break it, so the build rejects any
+// GEMM kernel that uses scratch.
 // Copies are issued two stages ahead, weight chunks three.  Loads a wavefront issues between its
 // copies of stage s and the wait at the top of stage s: the weight chunks of stage s+1, the
 // copies of stage s+1 and the weight chunks of stage s+2.
@@ -293,9 +296,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
         __builtin_amdgcn_sched_barrier(0);
         issue_stage(st + 2);
         __builtin_amdgcn_sched_barrier(0);
+        // (a scheduling barrier between steps keeps each group's epilogue in the step after its
+        // MFMAs: hoisted next to them, it would wait for their results instead of overlapping)
         step(BB, std::integral_constant<int, 0>(), st);
+        __builtin_amdgcn_sched_barrier(0);
         step(BB, std::integral_constant<int, 1>(), st);
+        __builtin_amdgcn_sched_barrier(0);
         step(BB, std::integral_constant<int, 2>(), st);
+        __builtin_amdgcn_sched_barrier(0);
         step(BB, std::integral_constant<int, 3>(), st);
     };
 

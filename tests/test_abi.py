@@ -143,3 +143,17 @@ def test_valid_calls_without_a_device_report_device_error(lib):
     assert lib.w4a8_prep(p, 2, 256, 64, 0, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_linear(ctypes.byref(L), p, 1, p, 0, p, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_last_error().decode() != ""
+
+
+def test_build_rejects_gemm_scratch(tmp_path):
+    """The build's guard: a GEMM kernel with a nonzero private segment (a spill) is an error."""
+    from bit_group_quantized_act_amd import build
+    asm = tmp_path / "k.s"
+    asm.write_text(".amdhsa_kernel _ZN4w4a8_gemm_kernelILi0E\n  .amdhsa_private_segment_fixed_size 0\n"
+                   ".end_amdhsa_kernel\n.amdhsa_kernel other_kernel\n"
+                   "  .amdhsa_private_segment_fixed_size 64\n.end_amdhsa_kernel\n")
+    build.check_no_scratch(str(asm), "gemm_kernel")          # only non-GEMM kernels spill: fine
+    asm.write_text(".amdhsa_kernel _ZN4w4a8_gemm_kernelILi1E\n  .amdhsa_private_segment_fixed_size 48\n"
+                   ".end_amdhsa_kernel\n")
+    with pytest.raises(RuntimeError, match="scratch"):
+        build.check_no_scratch(str(asm), "gemm_kernel")
