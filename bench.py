@@ -50,7 +50,7 @@ KERNEL_SOURCES = {
     "gemm": ["gemm.hip", "w4a8_kernels.h"],
 }
 TRAFFIC = {
-    "C2a": dict(kernel="gemv", source_sha="c1a7ad5c75f9777b", fetch_kib=8767.29, write_kib=66.25,
+    "C2a": dict(kernel="gemv", source_sha="20ae573f3297e6ca", fetch_kib=8767.28, write_kib=66.25,
                 fetch_factor=1.99979, write_factor=1.0),
 }
 

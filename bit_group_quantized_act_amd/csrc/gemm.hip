@@ -18,17 +18,22 @@
 //   XCD (one L2) gets a contiguous run of tiles, the M tiles of a channel block adjacent.
 //   Stages.  The k range is cut into stages of 256.  A stage's activation rows, the activation
 //   scales (and sums) of its groups and the weight metadata of the workgroup's two panels are
-//   copied from memory straight into one of three LDS stage buffers by buffer loads with an LDS
-//   destination (no registers, no VALU), two stages ahead.  Activation rows sit in LDS as
+//   copied from memory straight into one of two LDS stage buffers by buffer loads with an LDS
+//   destination (no registers, no VALU), one stage ahead.  Activation rows sit in LDS as
 //   16-byte units XOR-swizzled by the row, so the MFMA operand reads of 32 rows at one k spread
 //   over all banks.  Each wavefront issues the same six copies per stage, so one fixed wait
 //   count (the loads issued after them) tells it its copies have landed; a barrier then tells
 //   it everybody's have.  Weight chunks go to registers one stage ahead.  A load that may fall
 //   outside its buffer carries its whole offset in the range-checked VGPR operand, and every
 //   load past the data is aimed out of range: it returns zeros and touches no memory.
-//   Epilogue.  The int32 partials of a group are double-buffered by group parity: the MFMAs of
-//   group g+1 are issued before the VALU converts group g's partials and accumulates them with
-//   one FMA each, so the matrix unit and the VALU work side by side.  The FMA coefficients
+//   Occupancy.  At most 168 VGPRs and 40 KiB of LDS per workgroup let three workgroups share a
+//   CU (three wavefronts per SIMD).  Measured on MI355X, that beats a register-hungrier layout
+//   at two per SIMD (double-buffered partials, weights three stages ahead, three LDS buffers):
+//   the step is a chain of short dependent phases (unpack, operand reads, MFMAs, epilogue)
+//   that other wavefronts cover better than reordering inside one wavefront does.
+//   Epilogue.  At the last k step of a group the VALU converts the group's int32 partials and
+//   accumulates them with one FMA each (the wait for the MFMA results is covered by the other
+//   wavefronts of the SIMD).  The FMA coefficients
 //   xs[row] * sw[col] come from one fp32 outer-product MFMA (v_mfma_f32_32x32x1_2b: block t =
 //   tile t), which lands each coefficient in the lane and register of its partial; the affine
 //   bias term xs*xsum[row] * (bw + 8 sw)[col] is a second outer product accumulated on the
@@ -47,7 +52,7 @@ constexpr int BM = 64;                      // activation rows per workgroup
 constexpr int kBN = 128;                    // output channels per workgroup (4 wavefronts x 32)
 constexpr int kSK = 256;                    // k per stage
 constexpr int kSteps = kSK / 64;            // 64-wide k steps per stage
-constexpr int kNS = 3;                      // LDS stage buffers
+constexpr int kNS = 2;                      // LDS stage buffers
 constexpr int kAStage = BM * kSK;           // activation bytes of a stage (16 KiB)
 constexpr int kXOff = kAStage;              // xs [4 groups][64 rows] fp32, then xsum the same
 constexpr int kMOff = kAStage + 2048;       // weight metadata of the workgroup's two panels
@@ -56,10 +61,11 @@ constexpr int kCopiesPerStage = 6;          // LDS copies each wavefront issues 
 // The count is exact only while the kernel makes no other vector memory access in the loop: a
 // register spill (scratch loads and stores count too) would break it, so the build rejects any
 // GEMM kernel that uses scratch.
-// Copies are issued two stages ahead, weight chunks three.  Loads a wavefront issues between its
-// copies of stage s and the wait at the top of stage s: the weight chunks of stage s+1, the
-// copies of stage s+1 and the weight chunks of stage s+2.
-constexpr int kVmAfterStage = 2 * kSteps + kCopiesPerStage;
+// Copies and weight chunks are both issued one stage ahead: at the top of stage s a wavefront
+// issues the copies of stage s+1, then its k steps issue the weight chunks of stage s+1.  Loads
+// a wavefront issues between its copies of stage s and the wait at the top of stage s: the
+// weight chunks of stage s.
+constexpr int kVmAfterStage = kSteps;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -93,7 +99,7 @@ __device__ __forceinline__ void unpack_b(v4i v, uint4 cb, v4i &lo, v4i &hi) {
 }
 
 template <int FMT, int G, bool PARTIALS>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict__ packed,
+__global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict__ packed,
                                                       const Geom geom, int m,
                                                       const int8_t *__restrict__ xq,
                                                       const float *__restrict__ xs,
@@ -182,21 +188,20 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
         copy16(rmeta, buf + kMOff + ((kMB == 2) ? 0 : vp * 1024), m_off + blk * ((kMB == 2) ? 512 : 1024));
     };
 
-    // ---- weight chunks: register slot s % 12 holds step s (three stages)
-    constexpr int kRingSteps = 3 * kSteps;
+    // ---- weight chunks: register slot s % 4 holds step s (one stage)
+    constexpr int kRingSteps = kSteps;
     v4i rb[kRingSteps];
     const int w_off = (half * 64 + prow) * 16;     // steps past k are past the descriptor's range
     auto load_b = [&](int slot, int step) { rb[slot] = ld128(rw, w_off + step * 2048); };
 
-    v16i dt[2][2] = {};       // [group parity][tile] int32 partials
-    v32f coef = {};           // [tile][16]: xs[row] * sw16[col] of the group being finished
+    v16i dt[2] = {};          // [tile] int32 partials of the current group
+    v32f coef = {};           // [tile][16]: xs[row] * sw16[col] of the current group
     v32f acc = {};            // [tile][16]: fp32 outputs (the affine bias term accumulates here too)
     const v32f zf = {};
 
-    // The epilogue of group g, whose partials are in dt[g & 1] and coefficients in coef.
+    // The epilogue of group g, whose partials are in dt and coefficients in coef.
     // (PARTIALS: the int32 partials go to d instead, with the affine sums from xbuf)
-    auto finish = [&](auto PAR, int g, const uint8_t *xbuf) __attribute__((always_inline)) {
-        constexpr int par = decltype(PAR)::value;
+    auto finish = [&](int g, const uint8_t *xbuf) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             if (PARTIALS) {
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                     const int rl = 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
                     const int row = m0 + rl;
                     if (!active || g >= ng || row >= m || col >= geom.n) continue;
-                    int v = (FMT == kFmtCodebook) ? dt[par][t][e] : (dt[par][t][e] >> 4);
+                    int v = (FMT == kFmtCodebook) ? dt[t][e] : (dt[t][e] >> 4);
                     if (FMT == kFmtAffine)
                         v += 8 * reinterpret_cast<const int *>(xbuf + kXOff + 1024)[gi * 64 + rl];
                     d[((int64_t)row * geom.n + col) * ng + g] = v;
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
             } else {
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    acc[16 * t + e] = fmaf(static_cast<float>(dt[par][t][e]), coef[16 * t + e],
+                    acc[16 * t + e] = fmaf(static_cast<float>(dt[t][e]), coef[16 * t + e],
                                            acc[16 * t + e]);
             }
         }
@@ -260,44 +265,38 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
         constexpr int sub = J % SPG;                   // step inside its group
         constexpr bool first = sub == 0;
         constexpr bool last = sub == SPG - 1;
-        constexpr int par = (J / SPG) & 1;             // g & 1 (GPS is even)
         const int s = st * kSteps + J;
         const int g = s / SPG;
         const uint8_t *buf = lds[B];
         v4i blo, bhi;
-        unpack_b<FMT>(rb[B * kSteps + J], cb, blo, bhi);
-        load_b(B * kSteps + J, s + kRingSteps);        // the same step three stages on
+        unpack_b<FMT>(rb[J], cb, blo, bhi);
+        load_b(J, s + kRingSteps);                     // the same step one stage on
         const v4i a00 = *reinterpret_cast<const v4i *>(buf + a_rd[J][0]);
         const v4i a01 = *reinterpret_cast<const v4i *>(buf + a_rd[J][1]);
         const v4i a10 = *reinterpret_cast<const v4i *>(buf + a_rd[J][0] + 32 * kSK);
         const v4i a11 = *reinterpret_cast<const v4i *>(buf + a_rd[J][1] + 32 * kSK);
         const v16i z = {};
-        v16i &d0 = dt[par][0];
-        v16i &d1 = dt[par][1];
+        v16i &d0 = dt[0];
+        v16i &d1 = dt[1];
         d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a00, blo, first ? z : d0, 0, 0, 0);
         d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a10, blo, first ? z : d1, 0, 0, 0);
         d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a01, bhi, d0, 0, 0, 0);
         d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a11, bhi, d1, 0, 0, 0);
-        if (PARTIALS) {
-            if (last) finish(std::integral_constant<int, par>(), g, buf);
-        } else {
-            // group g-1 finished on the VALU beside these MFMAs, then group g's products
-            if (first && g > 0) finish(std::integral_constant<int, par ^ 1>(), g - 1, buf);
-            if (last) group_products(g, buf);
+        if (last) {   // group g's products (its coefficients and affine bias), then its epilogue
+            if (!PARTIALS) group_products(g, buf);
+            finish(g, buf);
         }
     };
 
     // Stage st: this wavefront's copies of it have landed, then everybody's have; every
-    // wavefront is also done with the buffer of stage st - 1, which stage st + 2 refills.
+    // wavefront is also done with the buffer of stage st - 1, which stage st + 1 refills.
     auto stage = [&](auto BB, int st) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
         wait_vm<kVmAfterStage>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue_stage(st + 2);
+        issue_stage(st + 1);
         __builtin_amdgcn_sched_barrier(0);
-        // (a scheduling barrier between steps keeps each group's epilogue in the step after its
-        // MFMAs: hoisted next to them, it would wait for their results instead of overlapping)
         step(BB, std::integral_constant<int, 0>(), st);
         __builtin_amdgcn_sched_barrier(0);
         step(BB, std::integral_constant<int, 1>(), st);
@@ -307,34 +306,21 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
         step(BB, std::integral_constant<int, 3>(), st);
     };
 
-    // ---- prologue, in the loop's issue order: chunks of stage 0; copies of 0, chunks of 1;
-    // copies of 1, chunks of 2
-#pragma unroll
-    for (int j = 0; j < kSteps; ++j) load_b(j, j);
-    __builtin_amdgcn_sched_barrier(0);
+    // ---- prologue, in the loop's issue order: copies of stage 0, then its weight chunks
     issue_stage(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < kSteps; ++j) load_b(kSteps + j, kSteps + j);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_stage(1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < kSteps; ++j) load_b(2 * kSteps + j, 2 * kSteps + j);
+    for (int j = 0; j < kSteps; ++j) load_b(j, j);
     __builtin_amdgcn_sched_barrier(0);
 
-    // Stages three at a time: the LDS buffer and the ring third are then compile-time (a runtime
-    // index into registers would make the compiler wait for every load in flight).  Up to two
-    // stages past the end run on zeros.
-    for (int st = 0; st < nstages; st += 3) {
+    // Stages two at a time: the LDS buffer is then compile-time.  A stage past the end runs on
+    // zeros.
+    for (int st = 0; st < nstages; st += 2) {
         stage(std::integral_constant<int, 0>(), st);
         stage(std::integral_constant<int, 1>(), st + 1);
-        stage(std::integral_constant<int, 2>(), st + 2);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (PARTIALS || !active) return;
-    // the last group's epilogue (the group count run is even: parity 1)
-    finish(std::integral_constant<int, 1>(), 0, nullptr);
 
     const int col = c0 + r32;
     if (col >= geom.n) return;

@@ -67,24 +67,22 @@ __device__ __forceinline__ uint32_t ld16(rsrc_t r, int voff) {
 __device__ __forceinline__ uint32_t lo_x16(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t hi_x16(uint32_t w) { return w & 0xF0F0F0F0u; }
 
-// Codebook lookup of four indices (one per byte, each 0..15) in a row's 16 int8 entries held
-// as dwords c0 (entries 0-3) .. c3 (entries 12-15).  v_perm selects bytes 0..7 of a dword
-// pair, so two lookups cover the halves and the index's bit 3 picks between them per byte.
-__device__ __forceinline__ uint32_t cb_lookup(uint32_t idx, uint32_t c0, uint32_t c1,
-                                              uint32_t c2, uint32_t c3) {
-    const uint32_t sel = idx & 0x07070707u;
-    const uint32_t lo = __builtin_amdgcn_perm(c1, c0, sel);
-    const uint32_t hi = __builtin_amdgcn_perm(c3, c2, sel);
-    const uint32_t t = (idx >> 3) & 0x01010101u;
-    const uint32_t mask = (t << 8) - t;               // 0xFF in each byte whose bit 3 is set
-    return (hi & mask) | (lo & ~mask);
+// Codebook lookup of four indices in a row's 16 int8 entries, held as dwords c0 (entries 0-3)
+// .. c3 (entries 12-15).  v_perm picks bytes 0..7 of a dword pair, so one permute per half looks
+// up the index's low three bits in entries 0-7 and in entries 8-15, and a third permute takes
+// byte i of the first result or of the second (selector i or i + 4) by the index's bit 3.  All
+// three are full-rate byte permutes; building a byte mask from bit 3 instead costs a multiply.
+// `w` holds four indices as nibbles at bit offset `S` (0: low nibbles, 4: high nibbles).
+template <int S>
+__device__ __forceinline__ uint32_t cb_lookup(uint32_t w, uint4 cb) {
+    const uint32_t sel = (w >> S) & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(cb.y, cb.x, sel);
+    const uint32_t hi = __builtin_amdgcn_perm(cb.w, cb.z, sel);
+    const uint32_t pick = ((w >> (S + 1)) & 0x04040404u) | 0x03020100u;
+    return __builtin_amdgcn_perm(hi, lo, pick);
 }
-__device__ __forceinline__ uint32_t cb_lo(uint32_t w, uint4 cb) {
-    return cb_lookup(w & 0x0F0F0F0Fu, cb.x, cb.y, cb.z, cb.w);
-}
-__device__ __forceinline__ uint32_t cb_hi(uint32_t w, uint4 cb) {
-    return cb_lookup((w >> 4) & 0x0F0F0F0Fu, cb.x, cb.y, cb.z, cb.w);
-}
+__device__ __forceinline__ uint32_t cb_lo(uint32_t w, uint4 cb) { return cb_lookup<0>(w, cb); }
+__device__ __forceinline__ uint32_t cb_hi(uint32_t w, uint4 cb) { return cb_lookup<4>(w, cb); }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
