@@ -55,8 +55,9 @@ def _load():
     lib.oracle_prep.argtypes = [P, i64, i64, i32, i32, P, P, P]
     lib.oracle_partials.argtypes = [i32, P, P, i64, i64, i32, P, i64, P]
     lib.oracle_linear.argtypes = [i32, P, P, P, P, i64, i64, i32, P, P, P, i64, P, P]
+    lib.oracle_glu.argtypes = [i32, P, P, i64, i64, P, P]
     for f in ("oracle_rotate", "oracle_quantize", "oracle_prep", "oracle_partials",
-              "oracle_linear", "oracle_num_threads"):
+              "oracle_linear", "oracle_glu", "oracle_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -158,3 +159,23 @@ def linear(fmt: int, codes, scales_f16, xq, xs, xsum, group: int, bias_f16=None,
                                  group, _ptr(xq), _ptr(xs), _ptr(xsum), m, _ptr(y), _ptr(t)),
            "linear")
     return (y, t) if with_terms else y
+
+
+ACT_SILU, ACT_GELU_TANH, ACT_GELU_ERF = 0, 1, 2
+
+
+def glu(act: int, y: np.ndarray, t: np.ndarray = None):
+    """Gated output of a [gate; up] linear: z [m, n/2] = act(y[:, :n/2]) * y[:, n/2:] in fp64,
+    and its error-bound magnitude tz when the linear's term magnitudes t are given."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    if y.ndim == 1:
+        y = y[None, :]
+        t = None if t is None else np.ascontiguousarray(t, dtype=np.float64)[None, :]
+    m, n = y.shape
+    z = np.empty((m, n // 2), np.float64)
+    tz = None
+    if t is not None:
+        t = np.ascontiguousarray(t, dtype=np.float64)
+        tz = np.empty((m, n // 2), np.float64)
+    _check(_load().oracle_glu(act, _ptr(y), _ptr(t), m, n, _ptr(z), _ptr(tz)), "glu")
+    return (z, tz) if t is not None else z

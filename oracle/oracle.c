@@ -35,6 +35,17 @@
  *              ("TensorFold PR #3215": 4-bit affine g64 weights, scale and bias per group,
  *              dequantized weight = scale*u + bias).
  *
+ *   glu        "cactus-compute/engine PR #750: Metal Support", the commit list: the fusion-plan
+ *              compiler folds a gelu-gated feed-forward pair into one transform + GEMV and
+ *              sibling quantized GEMVs into one batched GEMV; the kernel commit lists gelu-erf
+ *              and sigmoid activation codes.  "geistlib issue #500", section "Design": paired
+ *              linears share one activation prepass.  Reading taken here: the gate and up
+ *              projections are one packed linear of n = 2F output rows, gate rows first;
+ *              z[r][f] = act(y[r][f]) * y[r][F + f] in fp64, act one of
+ *                silu(v)      = v / (1 + exp(-v))
+ *                gelu_tanh(v) = v/2 * (1 + tanh(sqrt(2/pi) * (v + 0.044715 v^3)))
+ *                gelu_erf(v)  = v/2 * (1 + erf(v / sqrt(2)))
+ *
  * Weight formats (canonical input, one byte holds two 4-bit codes, low nibble = even k):
  *   format 0 (symmetric):  code is a two's-complement q in [-8, 7]; w_int = q
  *   format 1 (affine):     code is an unsigned u in [0, 15];        w_int = u
@@ -283,6 +294,44 @@ int oracle_linear(int32_t format, const uint8_t *codes, const uint16_t *scales_f
         free(w);
     }
     return overflow ? ORACLE_OVERFLOW : ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- gated output -------- */
+#define ORACLE_ACT_SILU 0
+#define ORACLE_ACT_GELU_TANH 1
+#define ORACLE_ACT_GELU_ERF 2
+
+static double oracle_act(int32_t act, double v)
+{
+    const double pi = 3.14159265358979323846;
+    if (act == ORACLE_ACT_SILU)
+        return v / (1.0 + exp(-v));
+    if (act == ORACLE_ACT_GELU_TANH)
+        return 0.5 * v * (1.0 + tanh(sqrt(2.0 / pi) * (v + 0.044715 * v * v * v)));
+    return 0.5 * v * (1.0 + erf(v / sqrt(2.0)));
+}
+
+/*
+ * z[r][f] = act(y[r][f]) * y[r][F + f] for f < F = n / 2 (fp64), from the linear's y [m][n].
+ * tz (may be NULL) bounds how far z moves when the two linear outputs move by at most e times
+ * their term magnitudes t: |dz| <= e * tz with tz = 1.2 * |u| * t_g + |act(g)| * t_u, where 1.2
+ * exceeds the largest slope of every act here (silu about 1.0998, both gelus about 1.1289).
+ */
+int oracle_glu(int32_t act, const double *y, const double *t, int64_t m, int64_t n,
+               double *z, double *tz)
+{
+    if (act < ORACLE_ACT_SILU || act > ORACLE_ACT_GELU_ERF || n % 2 != 0 || m < 0)
+        return ORACLE_BAD_ARGS;
+    int64_t f_n = n / 2;
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t f = 0; f < f_n; ++f) {
+            double g = y[r * n + f], u = y[r * n + f_n + f];
+            double a = oracle_act(act, g);
+            z[r * f_n + f] = a * u;
+            if (tz && t)
+                tz[r * f_n + f] = 1.2 * fabs(u) * t[r * n + f] + fabs(a) * t[r * n + f_n + f];
+        }
+    return ORACLE_OK;
 }
 
 /* Number of OpenMP threads a parallel region here would use (1 without OpenMP). */

@@ -406,3 +406,66 @@ def test_generator_outliers_and_ranges():
     fr = synth.make("C1", full_range=True, n=64)
     assert set(np.unique(synth.unpack_nibbles(fr["codes"]))) == set(range(16))
     assert synth.algorithmic_bytes(synth.config("C1")) == 562304
+
+
+# ----------------------------------------------------------------------------- gated output
+
+def _act_via_glu(act, v):
+    """act(v) from the oracle's gated output with the up half set to 1."""
+    y = np.concatenate([v[None, :], np.ones((1, v.size))], axis=1)
+    return oracle.glu(act, y)[0]
+
+
+GLU_GRID = np.concatenate([np.linspace(-12, 12, 481), [-40.0, -1e-3, 0.0, 1e-3, 40.0]])
+
+
+def test_glu_acts_match_library_routines():
+    torch = pytest.importorskip("torch")
+    from scipy import special
+    v = GLU_GRID
+    t = torch.from_numpy(v)
+    lib = {
+        oracle.ACT_SILU: [torch.nn.functional.silu(t).numpy(), v * special.expit(v)],
+        oracle.ACT_GELU_TANH: [torch.nn.functional.gelu(t, approximate="tanh").numpy()],
+        oracle.ACT_GELU_ERF: [torch.nn.functional.gelu(t).numpy(),
+                              0.5 * v * (1.0 + special.erf(v / np.sqrt(2.0)))],
+    }
+    for act, refs in lib.items():
+        got = _act_via_glu(act, v)
+        for ref in refs:
+            np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("act", [oracle.ACT_SILU, oracle.ACT_GELU_TANH, oracle.ACT_GELU_ERF])
+def test_glu_odd_identity_and_special_values(act):
+    # v * s(v) with s(v) + s(-v) = 1 for all three gates: act(v) - act(-v) = v exactly in math
+    v = GLU_GRID
+    np.testing.assert_allclose(_act_via_glu(act, v) - _act_via_glu(act, -v), v, rtol=1e-13,
+                               atol=1e-13)
+    assert _act_via_glu(act, np.array([0.0]))[0] == 0.0
+    big = _act_via_glu(act, np.array([40.0, -40.0]))
+    assert abs(big[0] - 40.0) < 1e-12 and abs(big[1]) < 1e-12
+
+
+def test_glu_uses_first_half_as_gate_and_control_swap_fails():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    g, u = rng.standard_normal((3, 16)), rng.standard_normal((3, 16))
+    want = torch.nn.functional.silu(torch.from_numpy(g)).numpy() * u
+    np.testing.assert_allclose(oracle.glu(oracle.ACT_SILU, np.concatenate([g, u], 1)), want,
+                               rtol=1e-13, atol=1e-15)
+    # planted mistake: halves swapped -- the library pin above must reject it
+    swapped = oracle.glu(oracle.ACT_SILU, np.concatenate([u, g], 1))
+    assert not np.allclose(swapped, want, rtol=1e-6, atol=1e-9)
+
+
+@pytest.mark.parametrize("act", [oracle.ACT_SILU, oracle.ACT_GELU_TANH, oracle.ACT_GELU_ERF])
+def test_glu_error_bound_covers_perturbed_inputs(act):
+    # moving each linear output by at most e * t moves z by at most e * tz (slope bound 1.2)
+    rng = np.random.default_rng(11)
+    y = rng.standard_normal((4, 512)) * 3.0
+    t = np.abs(y) + rng.uniform(0.5, 2.0, y.shape)
+    z, tz = oracle.glu(act, y, t)
+    for e in (1e-4, 1e-6):
+        yp = y + e * t * rng.choice([-1.0, 1.0], y.shape)
+        assert np.all(np.abs(oracle.glu(act, yp) - z) <= e * tz * (1 + 1e-9) + 1e-300)
