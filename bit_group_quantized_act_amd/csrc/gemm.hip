@@ -41,6 +41,11 @@
 //   rest.  Signed codes (sym q, affine u-8) enter the MFMA as 16*q (nibble moved to the byte's
 //   top); the 1/16 is folded into sw, and affine's u = (u-8) + 8 is restored through the bias
 //   term.
+//   Gated output (GLU).  For a [gate; up] linear (n = 2F, F a multiple of 64) a workgroup owns
+//   64 output channels: wavefronts 0 and 1 compute them from gate panel nt, wavefronts 2 and 3
+//   from the up panel F / 64 panels on (the same tile count as the plain GEMM); after the k loop
+//   the up wavefronts hand their tiles to the gate wavefronts through LDS, which store
+//   act(gate) * up.
 #include "w4a8_kernels.h"
 
 #include <type_traits>
@@ -57,7 +62,6 @@ constexpr int kAStage = BM * kSK;           // activation bytes of a stage (16 K
 constexpr int kXOff = kAStage;              // xs [4 groups][64 rows] fp32, then xsum the same
 constexpr int kMOff = kAStage + 2048;       // weight metadata of the workgroup's two panels
 constexpr int kStageBytes = kAStage + 4096;
-constexpr int kCopiesPerStage = 6;          // LDS copies each wavefront issues per stage
 // The count is exact only while the kernel makes no other vector memory access in the loop: a
 // register spill (scratch loads and stores count too) would break it, so the build rejects any
 // GEMM kernel that uses scratch.
@@ -98,14 +102,15 @@ __device__ __forceinline__ void unpack_b(v4i v, uint4 cb, v4i &lo, v4i &hi) {
     }
 }
 
-template <int FMT, int G, bool PARTIALS>
+template <int FMT, int G, bool PARTIALS, bool GLU>
 __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict__ packed,
                                                       const Geom geom, int m,
                                                       const int8_t *__restrict__ xq,
                                                       const float *__restrict__ xs,
                                                       const int *__restrict__ xsum,
                                                       float *__restrict__ y,
-                                                      int *__restrict__ d) {
+                                                      int *__restrict__ d, int act) {
+    static_assert(!(GLU && PARTIALS), "the gated output has no partials variant");
     constexpr int SPG = G / 64;                        // k steps per group
     constexpr int GPS = kSteps / SPG;                  // groups per stage
     constexpr int kMB = (FMT == kFmtAffine) ? 4 : 2;   // metadata bytes per channel and group
@@ -127,7 +132,6 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     const int k = geom.k;
     const int ng = k / G;
     const int nblk = (ng + 3) / 4;                     // metadata blocks of 4 groups
-    const int nsteps = k / 64;
     const int nstages = (k + kSK - 1) / kSK;
     const int m0 = mt * BM;
     const int rows_wg = min(m - m0, BM);
@@ -137,10 +141,14 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     const int r32 = lane & 31;
     const int pnl = wave >> 1;                         // the wavefront's panel in the workgroup
     const int prow = (wave & 1) * 32 + r32;            // the lane's channel row in that panel
-    const int p = active ? c0 / kPanelRows : 0;        // the wavefront's panel
+    // GLU: gate panel nt (wavefronts 0, 1) and the up panel up_pan panels on (2, 3)
+    const int up_pan = GLU ? geom.n_pad / (2 * kPanelRows) : 0;
+    const int p = GLU ? nt + (pnl ? up_pan : 0) : (active ? c0 / kPanelRows : 0);
     const int kc = k / kChunkK;
-    const int wg_p0 = nt * (kBN / kPanelRows);
-    const int wg_np = max(0, min(kBN / kPanelRows, geom.n_pad / kPanelRows - wg_p0));
+    const int wg_p0 = GLU ? nt : nt * (kBN / kPanelRows);
+    const int pstep = GLU ? up_pan : 1;                // panels between the workgroup's two
+    const int wg_np = GLU ? up_pan + 1
+                          : max(0, min(kBN / kPanelRows, geom.n_pad / kPanelRows - wg_p0));
 
     // ---- descriptors (offsets rebased per workgroup / panel stay far below 2^31)
     const rsrc_t ra = make_rsrc(xq + (int64_t)m0 * k, (uint64_t)rows_wg * k);
@@ -173,7 +181,8 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     // metadata copy: block (st*GPS)/4 of the workgroup's panels (2-byte entries: both panels in
     // one copy; 4-byte entries: panel wave & 1)
     const int vp = (kMB == 2) ? (lane >> 5) : (wave & 1);
-    const int m_off = (kMB == 2) ? (vp * nblk * 512 + (lane & 31) * 16) : (vp * nblk * 1024 + lane * 16);
+    const int m_off = (kMB == 2) ? (vp * pstep * nblk * 512 + (lane & 31) * 16)
+                                 : (vp * pstep * nblk * 1024 + lane * 16);
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
         (lds_void *)&lds[0][0]));
     auto issue_stage = [&](int st) __attribute__((always_inline)) {
@@ -322,6 +331,30 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     __builtin_amdgcn_sched_barrier(0);
     if (PARTIALS || !active) return;
 
+    if (GLU) {
+        // every wavefront is done with the stage buffers; the up wavefronts' tiles go to LDS
+        __syncthreads();
+        float *xch = reinterpret_cast<float *>(&lds[0][0]);   // [2][32][64] fp32, 16 KiB
+        if (pnl) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) xch[((wave & 1) * 32 + i) * 64 + lane] = acc[i];
+        }
+        __syncthreads();
+        if (pnl) return;
+        const int f_n = geom.n / 2;
+        const int colz = nt * kPanelRows + prow;          // output channel, < F
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+                const float u = xch[((wave & 1) * 32 + 16 * t + e) * 64 + lane];
+                if (row < m) y[(int64_t)row * f_n + colz] = act_apply(act, acc[16 * t + e]) * u;
+            }
+        }
+        return;
+    }
+
     const int col = c0 + r32;
     if (col >= geom.n) return;
 #pragma unroll
@@ -334,33 +367,39 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     }
 }
 
-template <int FMT, int G, bool PARTIALS>
-hipError_t launch_bm(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
+// (the gated output has the same tile count: 64 output channels per workgroup from 128 rows)
+template <int FMT, int G, bool PARTIALS, bool GLU>
+hipError_t launch_bm(const Geom &g, int act, const uint8_t *packed, int m, const int8_t *xq,
                      const float *xs, const int32_t *xsum, float *y, int32_t *d,
                      hipStream_t stream) {
     const unsigned tiles =
         static_cast<unsigned>(((g.n_pad + kBN - 1) / kBN) * ((m + BM - 1) / BM));
-    gemm_kernel<FMT, G, PARTIALS><<<tiles, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y, d);
+    gemm_kernel<FMT, G, PARTIALS, GLU><<<tiles, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y,
+                                                                  d, act);
     return hipGetLastError();
 }
 
-template <int FMT, bool PARTIALS>
-hipError_t launch_g(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
+template <int FMT, bool PARTIALS, bool GLU>
+hipError_t launch_g(const Geom &g, int act, const uint8_t *packed, int m, const int8_t *xq,
                     const float *xs, const int32_t *xsum, float *y, int32_t *d,
                     hipStream_t stream) {
-    if (g.group == 64) return launch_bm<FMT, 64, PARTIALS>(g, packed, m, xq, xs, xsum, y, d, stream);
-    return launch_bm<FMT, 128, PARTIALS>(g, packed, m, xq, xs, xsum, y, d, stream);
+    if (g.group == 64)
+        return launch_bm<FMT, 64, PARTIALS, GLU>(g, act, packed, m, xq, xs, xsum, y, d, stream);
+    return launch_bm<FMT, 128, PARTIALS, GLU>(g, act, packed, m, xq, xs, xsum, y, d, stream);
 }
 
-template <bool PARTIALS>
-hipError_t launch_f(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
+template <bool PARTIALS, bool GLU>
+hipError_t launch_f(const Geom &g, int act, const uint8_t *packed, int m, const int8_t *xq,
                     const float *xs, const int32_t *xsum, float *y, int32_t *d,
                     hipStream_t stream) {
     switch (g.fmt) {
-    case kFmtSym: return launch_g<kFmtSym, PARTIALS>(g, packed, m, xq, xs, xsum, y, d, stream);
+    case kFmtSym:
+        return launch_g<kFmtSym, PARTIALS, GLU>(g, act, packed, m, xq, xs, xsum, y, d, stream);
     case kFmtAffine:
-        return launch_g<kFmtAffine, PARTIALS>(g, packed, m, xq, xs, xsum, y, d, stream);
-    default: return launch_g<kFmtCodebook, PARTIALS>(g, packed, m, xq, xs, xsum, y, d, stream);
+        return launch_g<kFmtAffine, PARTIALS, GLU>(g, act, packed, m, xq, xs, xsum, y, d, stream);
+    default:
+        return launch_g<kFmtCodebook, PARTIALS, GLU>(g, act, packed, m, xq, xs, xsum, y, d,
+                                                     stream);
     }
 }
 
@@ -370,8 +409,15 @@ hipError_t launch_gemm(const Geom &g, const uint8_t *packed, int m, const int8_t
                        const float *xs, const int32_t *xsum, float *y, int32_t *d,
                        hipStream_t stream) {
     if (m == 0) return hipSuccess;
-    if (d) return launch_f<true>(g, packed, m, xq, xs, xsum, nullptr, d, stream);
-    return launch_f<false>(g, packed, m, xq, xs, xsum, y, nullptr, stream);
+    if (d) return launch_f<true, false>(g, 0, packed, m, xq, xs, xsum, nullptr, d, stream);
+    return launch_f<false, false>(g, 0, packed, m, xq, xs, xsum, y, nullptr, stream);
+}
+
+hipError_t launch_gemm_glu(const Geom &g, int act, const uint8_t *packed, int m,
+                           const int8_t *xq, const float *xs, const int32_t *xsum, float *y,
+                           hipStream_t stream) {
+    if (m == 0) return hipSuccess;
+    return launch_f<false, true>(g, act, packed, m, xq, xs, xsum, y, nullptr, stream);
 }
 
 }  // namespace w4a8

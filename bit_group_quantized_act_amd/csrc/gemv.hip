@@ -19,6 +19,11 @@
 //   loads, then quantizes the row into LDS with the prepass's arithmetic (prep_quad, so the codes
 //   are the same bits) while the weights are in flight; the dot products then read the codes as
 //   LDS broadcasts.  Workgroup 0 also writes xq, xs and xsum.
+//   Gated output (GLU).  For a [gate; up] linear (n = 2F, F a multiple of 64) workgroup b takes
+//   rows 32 (b & 1) .. +31 of gate panel b / 2 in lanes 0..31 and the same rows of the up panel
+//   F / 64 panels on in lanes 32..63: every load is still two contiguous 512-byte runs, the grid
+//   and the bytes per workgroup are those of the plain GEMV, and after the cross-wavefront sum
+//   lane r < 32 combines its gate value with lane r + 32's up value into act(gate) * up.
 #include "w4a8_kernels.h"
 
 namespace w4a8 {
@@ -48,7 +53,7 @@ __device__ __forceinline__ int dot_chunk(v4i v, const int *__restrict__ xc, uint
 // FUSED: x is the fp32 activation row; xq/xs/xsum are outputs written by workgroup 0.
 // Otherwise xq/xs/xsum are the prepass outputs (inputs here) and x is unused.
 // XQ (fused only): activation quads per lane, enough for the wavefront's groups.
-template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, int XQ>
+template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, int XQ, bool GLU>
 __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict__ packed,
                                                       const Geom geom,
                                                       const float *__restrict__ x,
@@ -56,7 +61,8 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
                                                       float *__restrict__ xs,
                                                       int *__restrict__ xsum,
                                                       float *__restrict__ y,
-                                                      int *__restrict__ d) {
+                                                      int *__restrict__ d, int act) {
+    static_assert(!(GLU && PARTIALS), "the gated output has no partials variant");
     constexpr int kChunksPerGroup = G / kChunkK;
     constexpr int kLanesPerGroup = G / 4;
     // Fused: activation quads (4 values) per lane that a wavefront quantizes, at most (the
@@ -70,7 +76,12 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int p = blockIdx.x;
+    // GLU: the descriptors start at gate panel p and span the up panel up_pan panels on
+    const int up_pan = GLU ? geom.n_pad / (2 * kPanelRows) : 0;
+    const int p = GLU ? static_cast<int>(blockIdx.x >> 1) : static_cast<int>(blockIdx.x);
+    const int lrow = GLU ? static_cast<int>((blockIdx.x & 1) * 32 + (lane & 31)) : lane;
+    const bool up_lane = GLU && lane >= 32;
+    const int npan = GLU ? up_pan + 1 : 1;
     const int kc = geom.k / kChunkK;
     const int ng = geom.k / G;
     // Wavefront w owns groups [g0, g1), split in whole metadata blocks of 4 groups (which also
@@ -78,15 +89,18 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
     const int nblk = (ng + 3) / 4;
     const int g0 = min(ng, (wave * nblk / W) * 4);
     const int g1 = min(ng, ((wave + 1) * nblk / W) * 4);
-    const int64_t row = (int64_t)p * kPanelRows + lane;
+    const int64_t row = (int64_t)(p + (up_lane ? up_pan : 0)) * kPanelRows + lrow;
 
     constexpr int kMetaBytes = (FMT == kFmtAffine) ? 4 : 2;
     constexpr int kRowBlk = 4 * kMetaBytes;          // one row's metadata block (4 groups)
     // the panel's codes and metadata; a load at kOOB returns zeros without a memory access
     const rsrc_t rw = make_rsrc(packed + geom.off_codes + (int64_t)p * kc * 1024,
-                                (uint64_t)kc * 1024);
+                                (uint64_t)npan * kc * 1024);
     const rsrc_t rm = make_rsrc(packed + geom.off_meta + (int64_t)p * nblk * kPanelRows * kRowBlk,
-                                (uint64_t)nblk * kPanelRows * kRowBlk);
+                                (uint64_t)npan * nblk * kPanelRows * kRowBlk);
+    // (GLU: the up lanes' offset to their panel; the host keeps both spans below 2^31)
+    const int wlane = up_lane ? up_pan * kc * 1024 : 0;
+    const int mlane = up_lane ? up_pan * nblk * kPanelRows * kRowBlk : 0;
     uint4 cb = make_uint4(0u, 0u, 0u, 0u);
     if (FMT == kFmtCodebook)
         cb = *reinterpret_cast<const uint4 *>(packed + geom.off_codebook + row * 16);
@@ -104,7 +118,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
     auto load_group = [&](int slot, int g) {
         const bool in = g < g1;
         if (slot == 0) {
-            const int mo = in ? ((g / 4) * kPanelRows + lane) * kRowBlk : kOOB;
+            const int mo = in ? ((g / 4) * kPanelRows + lrow) * kRowBlk + mlane : kOOB;
             if (kRowBlk == 16) {
                 mnext = ld128(rm, mo);
             } else {
@@ -114,7 +128,8 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
         }
 #pragma unroll
         for (int c = 0; c < kChunksPerGroup; ++c)
-            v[slot][c] = ld128(rw, in ? ((g * kChunksPerGroup + c) * kPanelRows + lane) * 16 : kOOB);
+            v[slot][c] = ld128(rw, in ? ((g * kChunksPerGroup + c) * kPanelRows + lrow) * 16 + wlane
+                                      : kOOB);
     };
     // Issue order is pinned with scheduling barriers (loads complete in issue order, and every
     // wait above counts on it).  Fused: the lane's activation quads come first (those past the
@@ -228,78 +243,93 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
     // sym/affine partials were computed x16 (exact power of two, folded in once here)
     constexpr float kOut = (FMT == kFmtCodebook) ? 1.0f : 0.0625f;
     float part = acc * kOut + bacc;
-    if (W == 1) {
-        if (row < geom.n) y[row] = part;
-        return;
-    }
-    __shared__ float red[W][64];
-    red[wave][lane] = part;
-    __syncthreads();
-    if (wave == 0) {
-        float s = red[0][lane];
+    float s = part;
+    if (W > 1) {
+        __shared__ float red[W][64];
+        red[wave][lane] = part;
+        __syncthreads();
+        if (wave != 0) return;
+        s = red[0][lane];
 #pragma unroll
         for (int w = 1; w < W; ++w) s += red[w][lane];
-        if (row < geom.n) y[row] = s;
+    }
+    if (GLU) {
+        const float u = __shfl(s, lane + 32, 64);   // lane r < 32: the up value of its row
+        const int64_t zr = (int64_t)p * kPanelRows + lrow;
+        if (lane < 32 && zr < geom.n / 2) y[zr] = act_apply(act, s) * u;
+    } else if (row < geom.n) {
+        y[row] = s;
     }
 }
 
-template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, int XQ>
-hipError_t launch_k(const Geom &g, const uint8_t *packed, const float *x, int8_t *xq, float *xs,
-                    int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
+// (the gated output keeps the grid: two workgroups per gate panel, one per half of its rows)
+template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, int XQ, bool GLU>
+hipError_t launch_k(const Geom &g, int act, const uint8_t *packed, const float *x, int8_t *xq,
+                    float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
     const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
-    gemv_kernel<FMT, G, W, PARTIALS, FUSED, ROT, XQ><<<grid, 64 * W, 0, stream>>>(
-        packed, g, x, xq, xs, xsum, y, d);
+    gemv_kernel<FMT, G, W, PARTIALS, FUSED, ROT, XQ, GLU><<<grid, 64 * W, 0, stream>>>(
+        packed, g, x, xq, xs, xsum, y, d, act);
     return hipGetLastError();
 }
 
-template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT>
-hipError_t launch_wk(const Geom &g, const uint8_t *packed, const float *x, int8_t *xq, float *xs,
-                     int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
-    if (!FUSED) return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 1>(g, packed, x, xq, xs, xsum, y, d, stream);
+template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, bool GLU>
+hipError_t launch_wk(const Geom &g, int act, const uint8_t *packed, const float *x, int8_t *xq,
+                     float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
+    if (!FUSED)
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 1, GLU>(g, act, packed, x, xq, xs, xsum,
+                                                                 y, d, stream);
     // the quads of the largest wavefront share (whole metadata blocks of 4 groups)
     const int nblk = (g.k / G + 3) / 4;
     const int max_quads = (nblk + W - 1) / W * 4 * (G / 4);
     if (max_quads <= 64)
-        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 1>(g, packed, x, xq, xs, xsum, y, d, stream);
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 1, GLU>(g, act, packed, x, xq, xs,
+                                                                  xsum, y, d, stream);
     if (max_quads <= 128)
-        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 2>(g, packed, x, xq, xs, xsum, y, d, stream);
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 2, GLU>(g, act, packed, x, xq, xs,
+                                                                  xsum, y, d, stream);
     if (max_quads <= 256)
-        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 4>(g, packed, x, xq, xs, xsum, y, d, stream);
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 4, GLU>(g, act, packed, x, xq, xs,
+                                                                  xsum, y, d, stream);
     if (max_quads <= 64 * kFusedQuadsPerLane)
-        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, kFusedQuadsPerLane>(g, packed, x, xq, xs,
-                                                                            xsum, y, d, stream);
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, kFusedQuadsPerLane, GLU>(
+            g, act, packed, x, xq, xs, xsum, y, d, stream);
     return hipErrorInvalidValue;
 }
 
-template <int FMT, int G, bool PARTIALS, bool FUSED, bool ROT>
-hipError_t launch_w(const Geom &g, const uint8_t *packed, const float *x, int8_t *xq, float *xs,
-                    int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
+template <int FMT, int G, bool PARTIALS, bool FUSED, bool ROT, bool GLU>
+hipError_t launch_w(const Geom &g, int act, const uint8_t *packed, const float *x, int8_t *xq,
+                    float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
     // W = 8 once there are 6 metadata blocks (some wavefronts may own none), else 4
     if ((g.k / G + 3) / 4 >= 6)
-        return launch_wk<FMT, G, 8, PARTIALS, FUSED, ROT>(g, packed, x, xq, xs, xsum, y, d, stream);
-    return launch_wk<FMT, G, 4, PARTIALS, FUSED, ROT>(g, packed, x, xq, xs, xsum, y, d, stream);
+        return launch_wk<FMT, G, 8, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y,
+                                                              d, stream);
+    return launch_wk<FMT, G, 4, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y, d,
+                                                          stream);
 }
 
-template <int FMT, bool PARTIALS, bool FUSED, bool ROT>
-hipError_t launch_g(const Geom &g, const uint8_t *packed, const float *x, int8_t *xq, float *xs,
-                    int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
+template <int FMT, bool PARTIALS, bool FUSED, bool ROT, bool GLU>
+hipError_t launch_g(const Geom &g, int act, const uint8_t *packed, const float *x, int8_t *xq,
+                    float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
     if (g.group == 64)
-        return launch_w<FMT, 64, PARTIALS, FUSED, ROT>(g, packed, x, xq, xs, xsum, y, d, stream);
-    return launch_w<FMT, 128, PARTIALS, FUSED, ROT>(g, packed, x, xq, xs, xsum, y, d, stream);
+        return launch_w<FMT, 64, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y, d,
+                                                           stream);
+    return launch_w<FMT, 128, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y, d,
+                                                        stream);
 }
 
-template <bool PARTIALS, bool FUSED, bool ROT>
+template <bool PARTIALS, bool FUSED, bool ROT, bool GLU = false>
 hipError_t launch_f(const Geom &g, const uint8_t *packed, const float *x, int8_t *xq, float *xs,
-                    int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
+                    int32_t *xsum, float *y, int32_t *d, hipStream_t stream, int act = 0) {
     switch (g.fmt) {
     case kFmtSym:
-        return launch_g<kFmtSym, PARTIALS, FUSED, ROT>(g, packed, x, xq, xs, xsum, y, d, stream);
+        return launch_g<kFmtSym, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y, d,
+                                                           stream);
     case kFmtAffine:
-        return launch_g<kFmtAffine, PARTIALS, FUSED, ROT>(g, packed, x, xq, xs, xsum, y, d,
-                                                          stream);
+        return launch_g<kFmtAffine, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y,
+                                                              d, stream);
     default:
-        return launch_g<kFmtCodebook, PARTIALS, FUSED, ROT>(g, packed, x, xq, xs, xsum, y, d,
-                                                            stream);
+        return launch_g<kFmtCodebook, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum,
+                                                                y, d, stream);
     }
 }
 
@@ -319,6 +349,24 @@ hipError_t launch_gemv_fused(const Geom &g, const uint8_t *packed, const float *
                              int8_t *xq, float *xs, int32_t *xsum, float *y, hipStream_t stream) {
     if (hadamard) return launch_f<false, true, true>(g, packed, x, xq, xs, xsum, y, nullptr, stream);
     return launch_f<false, true, false>(g, packed, x, xq, xs, xsum, y, nullptr, stream);
+}
+
+hipError_t launch_gemv_glu(const Geom &g, int act, const uint8_t *packed, const int8_t *xq,
+                           const float *xs, const int32_t *xsum, float *y, hipStream_t stream) {
+    int8_t *q = const_cast<int8_t *>(xq);
+    float *s = const_cast<float *>(xs);
+    int32_t *u = const_cast<int32_t *>(xsum);
+    return launch_f<false, false, false, true>(g, packed, nullptr, q, s, u, y, nullptr, stream,
+                                               act);
+}
+
+hipError_t launch_gemv_glu_fused(const Geom &g, int act, const uint8_t *packed, const float *x,
+                                 int hadamard, int8_t *xq, float *xs, int32_t *xsum, float *y,
+                                 hipStream_t stream) {
+    if (hadamard)
+        return launch_f<false, true, true, true>(g, packed, x, xq, xs, xsum, y, nullptr, stream,
+                                                 act);
+    return launch_f<false, true, false, true>(g, packed, x, xq, xs, xsum, y, nullptr, stream, act);
 }
 
 }  // namespace w4a8

@@ -149,6 +149,20 @@ __device__ __forceinline__ int prep_quad(float4 v, int lane, float &scale, int &
     return (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | ((q[3] & 0xFF) << 24);
 }
 
+// ---- gated output of a [gate; up] linear: act(gate) * up
+//
+// Source: "cactus-compute/engine PR #750: Metal Support", the commit list (a gelu-gated
+// feed-forward pair fused into one GEMV, sibling quantized GEMVs batched into one; gelu-erf and
+// sigmoid activation codes).  The activations, in fp32 through the device math library:
+// silu(v) = v / (1 + e^-v), the tanh approximation of gelu, and gelu with erf.
+constexpr int kActSilu = 0, kActGeluTanh = 1, kActGeluErf = 2;
+__device__ __forceinline__ float act_apply(int act, float v) {
+    if (act == kActSilu) return v / (1.0f + expf(-v));
+    if (act == kActGeluTanh)
+        return 0.5f * v * (1.0f + tanhf(0.7978845608f * (v + 0.044715f * v * v * v)));
+    return 0.5f * v * (1.0f + erff(v * 0.7071067812f));
+}
+
 // ---- launchers (each returns the hipGetLastError() of its launch)
 
 hipError_t launch_pack(const Geom &g, const uint8_t *codes, const uint16_t *scales,
@@ -175,5 +189,16 @@ hipError_t launch_gemv_fused(const Geom &g, const uint8_t *packed, const float *
 hipError_t launch_gemm(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
                        const float *xs, const int32_t *xsum, float *y, int32_t *d,
                        hipStream_t stream);
+
+// Gated variants: g describes the packed [gate; up] linear (g.n = 2F rows, F % 64 == 0, gate
+// rows first); y is [m][F] = act(gate) * up, act one of kActSilu / kActGeluTanh / kActGeluErf.
+hipError_t launch_gemv_glu(const Geom &g, int act, const uint8_t *packed, const int8_t *xq,
+                           const float *xs, const int32_t *xsum, float *y, hipStream_t stream);
+hipError_t launch_gemv_glu_fused(const Geom &g, int act, const uint8_t *packed, const float *x,
+                                 int hadamard, int8_t *xq, float *xs, int32_t *xsum, float *y,
+                                 hipStream_t stream);
+hipError_t launch_gemm_glu(const Geom &g, int act, const uint8_t *packed, int m,
+                           const int8_t *xq, const float *xs, const int32_t *xsum, float *y,
+                           hipStream_t stream);
 
 }  // namespace w4a8

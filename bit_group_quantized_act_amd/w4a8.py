@@ -21,7 +21,9 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "no gfx950 device
 
 # Every exported symbol of the C ABI (the header's declarations, in order).
 EXPORTS = ("w4a8_packed_layout", "w4a8_pack_weights", "w4a8_prep", "w4a8_gemv", "w4a8_gemm",
-           "w4a8_linear", "w4a8_debug_partials", "w4a8_status_string", "w4a8_last_error")
+           "w4a8_linear", "w4a8_linear_glu", "w4a8_debug_partials", "w4a8_status_string",
+           "w4a8_last_error")
+ACT_SILU, ACT_GELU_TANH, ACT_GELU_ERF = 0, 1, 2
 
 
 class Layout(ctypes.Structure):
@@ -63,8 +65,9 @@ def load() -> ctypes.CDLL:
     lib.w4a8_gemv.argtypes = [LP, P, P, P, P, P, P]
     lib.w4a8_gemm.argtypes = [LP, P, i32, P, P, P, P, P]
     lib.w4a8_linear.argtypes = [LP, P, i32, P, i32, P, P, P, P, P]
+    lib.w4a8_linear_glu.argtypes = [LP, P, i32, P, i32, i32, P, P, P, P, P]
     lib.w4a8_debug_partials.argtypes = [LP, P, i32, P, P, P, P]
-    for f in EXPORTS[:7]:
+    for f in EXPORTS[:8]:
         getattr(lib, f).restype = ctypes.c_int
     lib.w4a8_status_string.argtypes = [ctypes.c_int]
     lib.w4a8_status_string.restype = ctypes.c_char_p
@@ -207,5 +210,32 @@ def linear(L: Layout, packed: torch.Tensor, x: torch.Tensor, hadamard_block: int
     _check(load().w4a8_linear(ctypes.byref(L), _ptr(packed), m, _ptr(x2), hadamard_block,
                               _ptr(xq), _ptr(xs), _ptr(xsum), _ptr(y), _stream(x.device)),
            "w4a8_linear")
+    y = y[0] if (squeeze and out is None) else y
+    return (y, (xq, xs, xsum)) if prep_out is not None else y
+
+
+def linear_glu(L: Layout, packed: torch.Tensor, x: torch.Tensor, act: int = ACT_SILU,
+               hadamard_block: int = 0, out=None, prep_out=None):
+    """Gated output of a [gate; up] linear (w4a8_linear_glu): fp32 activations [m, k] or [k]
+    -> act(gate) * up, fp32 [m, n/2] or [n/2].  L.n must be 2F with F a multiple of 64 (gate
+    rows first).  prep_out as for linear."""
+    squeeze = x.dim() == 1
+    x2 = x.unsqueeze(0) if squeeze else x
+    _dev(x2, torch.float32, "x")
+    m, k = x2.shape
+    if k != L.k:
+        raise ValueError(f"x has k = {k}, the layout {L.k}")
+    ng = k // L.group
+    if prep_out is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+        xs = torch.empty((ng, m), dtype=torch.float32, device=x.device)
+        xsum = torch.empty((ng, m), dtype=torch.int32, device=x.device)
+    else:
+        xq, xs, xsum = prep_out
+    y = out if out is not None else torch.empty((m, L.n // 2), dtype=torch.float32,
+                                                device=x.device)
+    _check(load().w4a8_linear_glu(ctypes.byref(L), _ptr(packed), m, _ptr(x2), hadamard_block,
+                                  act, _ptr(xq), _ptr(xs), _ptr(xsum), _ptr(y),
+                                  _stream(x.device)), "w4a8_linear_glu")
     y = y[0] if (squeeze and out is None) else y
     return (y, (xq, xs, xsum)) if prep_out is not None else y

@@ -185,6 +185,37 @@ w4a8_status w4a8_linear(const w4a8_layout *L, const void *packed, int32_t m, con
                         int32_t hadamard_block, int8_t *xq, float *xs, int32_t *xsum, float *y,
                         void *stream);
 
+/* Activation of the gated output (w4a8_linear_glu). */
+typedef enum {
+    W4A8_ACT_SILU = 0,      /* v / (1 + e^-v) */
+    W4A8_ACT_GELU_TANH = 1, /* v/2 * (1 + tanh(sqrt(2/pi) * (v + 0.044715 v^3))) */
+    W4A8_ACT_GELU_ERF = 2   /* v/2 * (1 + erf(v / sqrt(2))) */
+} w4a8_act;
+
+/*
+ * A gated feed-forward input in one call: sibling gate and up projections packed as one weight
+ * matrix of L->n = 2F rows (gate rows 0..F-1, then up rows F..2F-1; F a multiple of 64, so
+ * L->n % 128 == 0), one prepass of x shared by both, and
+ *   y[r][f] = act(gate[r][f]) * up[r][f],  f < F,
+ * written instead of the two halves.  gate and up are the fp32 outputs w4a8_linear computes
+ * for those rows; act and the product are fp32 (device expf, tanhf, erff).
+ *   x, hadamard_block, xq, xs, xsum  as for w4a8_linear (xq, xs and xsum are written)
+ *   act   a w4a8_act
+ *   y     fp32 [m][L->n / 2]
+ * m == 1 with L->k <= 16384 and L->n <= 131072 runs one kernel (the prepass fused, as for
+ * w4a8_linear); otherwise the prepass kernel, then the gated GEMV or GEMM.  m == 0 is a no-op.
+ * W4A8_ERR_ARG: L->n % 128 != 0, or act not a w4a8_act.  W4A8_ERR_UNSUPPORTED: the span from a
+ * gate row to its up row in the packed codes or metadata ((L->n / 2 + 64) rows) exceeds
+ * 2^31 - 16 bytes, or as for w4a8_gemm.
+ * Source: "cactus-compute/engine PR #750: Metal Support", the commit list (a gelu-gated
+ * feed-forward pair fused into one GEMV; sibling quantized GEMVs batched into one; gelu-erf
+ * and sigmoid activation codes); "geistlib issue #500", section "Design" (paired linears share
+ * one activation prepass).
+ */
+w4a8_status w4a8_linear_glu(const w4a8_layout *L, const void *packed, int32_t m, const float *x,
+                            int32_t hadamard_block, int32_t act, int8_t *xq, float *xs,
+                            int32_t *xsum, float *y, void *stream);
+
 /*
  * The exact int32 partials D[r][n][g] (definitions above) written by the same kernel code as
  * the GEMV (m == 1) or the GEMM (m > 1), with the fp32 epilogue replaced by a store of D.

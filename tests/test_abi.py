@@ -133,6 +133,22 @@ def test_invalid_calls_are_rejected_on_the_host(lib):
     assert lib.w4a8_linear(LP, p16, 1, p, 0, p, p, p, p, None) == ERR_ARG
     assert lib.w4a8_linear(LP, p, 1, p1, 0, p, p, p, p, None) == ERR_ARG
     assert lib.w4a8_linear(LP, p, 0, None, 0, None, None, None, None, None) == 0
+    # linear_glu: n not 2F with F % 64 == 0, act out of range, bad rotation block, m < 0,
+    # missing x / y, a gate-to-up span past 2^31 bytes; m == 0 is a no-op
+    silu = w4a8.ACT_SILU
+    L192 = w4a8.packed_layout(w4a8.SYM, 192, 256, 64)
+    assert lib.w4a8_linear_glu(ctypes.byref(L192), p, 1, p, 0, silu, p, p, p, p, None) == ERR_ARG
+    assert "gate" in lib.w4a8_last_error().decode()
+    assert lib.w4a8_linear_glu(LP, p, 1, p, 0, 3, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_linear_glu(LP, p, 1, p, 0, -1, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_linear_glu(LP, p, 1, p, 64, silu, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_linear_glu(LP, p, -1, p, 0, silu, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_linear_glu(LP, p, 2, None, 0, silu, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_linear_glu(LP, p, 2, p, 0, silu, p, p, p, None, None) == ERR_ARG
+    big = w4a8.packed_layout(w4a8.SYM, 262144, 32768, 64)
+    assert lib.w4a8_linear_glu(ctypes.byref(big), p, 1, p, 0, silu, p, p, p, p,
+                               None) == ERR_UNSUPPORTED
+    assert lib.w4a8_linear_glu(LP, p, 0, None, 0, silu, None, None, None, None, None) == 0
 
 
 @pytest.mark.skipif(_gpu_visible(), reason="checks the no-device path; would launch on a GPU")
@@ -142,6 +158,8 @@ def test_valid_calls_without_a_device_report_device_error(lib):
     assert lib.w4a8_gemv(ctypes.byref(L), p, p, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_prep(p, 2, 256, 64, 0, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_linear(ctypes.byref(L), p, 1, p, 0, p, p, p, p, None) == ERR_DEVICE
+    assert lib.w4a8_linear_glu(ctypes.byref(L), p, 2, p, 0, w4a8.ACT_GELU_TANH, p, p, p, p,
+                               None) == ERR_DEVICE
     assert lib.w4a8_last_error().decode() != ""
 
 
