@@ -22,6 +22,9 @@ roofline   = algorithmic bytes of one launch of the dominant kernel (weights + x
              the 8 TB/s HBM peak (or int8 ops against the 5.0 POP/s dense MFMA peak for a GEMM
              whose MFMA floor is above its HBM floor)
 cpu_baseline = the CPU oracle (plain C, OpenMP) on the same workload, repeated for about 10 s
+
+--glu ACT times the gated variant instead (w4a8_linear_glu): the config's weights read as a
+[gate; up] pair (n = 2F), and the output is act(gate) * up, fp32 [m][F].
 """
 from __future__ import annotations
 
@@ -81,6 +84,8 @@ def parse():
                     help="workload (C1, C2a, C2b, C3a, C3b, C4, C5a, C5b); default C2a")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--glu", choices=["silu", "gelu_tanh", "gelu_erf"], default=None,
+                    help="time w4a8_linear_glu (the weights as a [gate; up] pair) instead")
     ap.add_argument("--hot", action="store_true",
                     help="reuse one weight buffer (measures cache, not HBM; labelled)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -104,15 +109,16 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 8}), flush=True)
 
 
-def workload_name(cfg):
+def workload_name(cfg, glu=None):
     from bit_group_quantized_act_amd import synth
     kind = "decode GEMV" if cfg.m == 1 else "prefill GEMM"
     rot = ", 128-block WHT" if cfg.hadamard else ""
     fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072
     how = ("prepass fused into the GEMV" if fused else
            "prepass + GEMV" if cfg.m == 1 else "prepass + GEMM")
+    gated = "" if glu is None else f", gated output {glu}(gate)*up with F={cfg.n // 2}"
     return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
-            f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights{rot} ({how} per step)")
+            f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights{rot}{gated} ({how} per step)")
 
 
 def main():
@@ -144,6 +150,15 @@ def main():
     wbytes = synth.weight_bytes(cfg)
     fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072   # w4a8_linear's one-kernel case
     alg_bytes = synth.algorithmic_bytes(cfg, fused_prep=fused)
+    act = None
+    if args.glu is not None:
+        if cfg.n % 128 != 0:
+            print(f"--glu needs n = 2F with F a multiple of 64 ({cfg.name} has n = {cfg.n})",
+                  file=sys.stderr)
+            sys.exit(2)
+        act = {"silu": w4a8.ACT_SILU, "gelu_tanh": w4a8.ACT_GELU_TANH,
+               "gelu_erf": w4a8.ACT_GELU_ERF}[args.glu]
+        alg_bytes -= 4 * cfg.m * (cfg.n // 2)         # the output is [m][F], not [m][n]
     ops = synth.int_ops(cfg)
     pool_n = 1 if args.hot else max(2, -(-POOL_BYTES // lay.bytes))
     pool = [packed0] + [packed0.clone() for _ in range(pool_n - 1)]
@@ -152,14 +167,20 @@ def main():
     xq = torch.empty((cfg.m, cfg.k), dtype=torch.int8, device=dev)
     xs = torch.empty((ng, cfg.m), dtype=torch.float32, device=dev)     # group-major
     xsum = torch.empty((ng, cfg.m), dtype=torch.int32, device=dev)
-    y = torch.empty((cfg.m, cfg.n), dtype=torch.float32, device=dev)
+    y = torch.empty((cfg.m, cfg.n if act is None else cfg.n // 2), dtype=torch.float32,
+                    device=dev)
     torch.cuda.synchronize()
 
     def linear(i):
         # the dominant kernel alone: the fused prepass + GEMV at one row (the plain GEMV for a
         # vocabulary-sized row), the GEMM above
         pk = pool[i % pool_n]
-        if fused:
+        if act is not None:
+            if fused:
+                w4a8.linear_glu(lay, pk, x, act, cfg.hadamard, out=y, prep_out=(xq, xs, xsum))
+            else:
+                w4a8.gemm_glu(lay, pk, xq, xs, xsum, act, out=y)
+        elif fused:
             w4a8.linear(lay, pk, x, cfg.hadamard, out=y, prep_out=(xq, xs, xsum))
         elif cfg.m == 1:
             w4a8.gemv(lay, pk, xq[0], xs, xsum, out=y[0])
@@ -167,7 +188,11 @@ def main():
             w4a8.gemm(lay, pk, xq, xs, xsum, out=y)
 
     def step(i):
-        w4a8.linear(lay, pool[i % pool_n], x, cfg.hadamard, out=y, prep_out=(xq, xs, xsum))
+        if act is not None:
+            w4a8.linear_glu(lay, pool[i % pool_n], x, act, cfg.hadamard, out=y,
+                            prep_out=(xq, xs, xsum))
+        else:
+            w4a8.linear(lay, pool[i % pool_n], x, cfg.hadamard, out=y, prep_out=(xq, xs, xsum))
 
     stream = torch.cuda.Stream()
 
@@ -216,7 +241,8 @@ def main():
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4))
     kname = "gemv" if cfg.m == 1 else "gemm"     # the fused kernel lives in gemv.hip
-    roof.update(traffic=measured_traffic(cfg.name, kname), kernel=kname,
+    traffic_key = cfg.name if act is None else f"{cfg.name}-glu"   # counters of the plain kernel
+    roof.update(traffic=measured_traffic(traffic_key, kname), kernel=kname,
                 kernel_us=round(us_linear, 3), alg_bytes_per_launch=alg_bytes,
                 int_ops_per_launch=ops,
                 tops=round(ops / (us_linear * 1e-6) / 1e12, 2))
@@ -224,27 +250,35 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         import oracle                      # the CPU baseline leg (test infrastructure)
-        # a bounded sample: all rows, the first `cols` output columns (all of them when the
-        # layer is small), so that one repetition is at most ~2e9 multiply-adds
+        # a bounded sample: all rows, `cols` weight rows (all of them when the layer is small;
+        # matched gate and up rows for the gated output), at most ~2e9 multiply-adds each
         cols = cfg.n if cfg.m * cfg.n * cfg.k <= 2e9 else \
             max(64, int(2e9 / (cfg.m * cfg.k)) // 64 * 64)
-        sub = lambda a: None if a is None else np.ascontiguousarray(a[:cols])
+        rows = np.arange(cols)
+        if act is not None:               # matched gate and up rows: cols / 2 outputs
+            half = max(1, cols // 2)
+            rows = np.concatenate([np.arange(half), cfg.n // 2 + np.arange(half)])
+        sub = lambda a: None if a is None else np.ascontiguousarray(a[rows])
         codes, scales, bias, cb = (sub(layer[key]) for key in ("codes", "scales", "bias",
                                                                 "codebook"))
-        sample_wbytes = wbytes * cols / cfg.n
+        sample_wbytes = wbytes * rows.size / cfg.n
         reps, t0 = 0, time.perf_counter()
         while True:
             oq, os_, osum = oracle.prep(layer["x"], cfg.group, cfg.hadamard)
-            oracle.linear(cfg.fmt, codes, scales, oq, os_, osum, cfg.group, bias_f16=bias,
-                          codebook=cb, with_terms=False)
+            yo = oracle.linear(cfg.fmt, codes, scales, oq, os_, osum, cfg.group, bias_f16=bias,
+                               codebook=cb, with_terms=False)
+            if act is not None:
+                oracle.glu(act, yo)
             reps += 1
             el = time.perf_counter() - t0
             if el >= args.cpu_seconds:
                 break
-        what = "the whole workload" if cols == cfg.n else f"all {cfg.m} rows x the first {cols} columns"
+        what = ("the whole workload" if rows.size == cfg.n else
+                f"all {cfg.m} rows x {rows.size} of the {cfg.n} weight rows")
         cpu = dict(value=round(sample_wbytes * reps / el / 1e9, 3), unit="GB/s",
                    cores=oracle.num_threads(), kind="oracle",
-                   sample=f"{what} of {cfg.name} (prep + linear), repeated {reps}x in "
+                   sample=f"{what} of {cfg.name} (prep + linear"
+                          f"{' + gated output' if act is not None else ''}), repeated {reps}x in "
                           f"{el:.1f} s ({1e3 * el / reps:.2f} ms each)")
 
     out = {
@@ -260,7 +294,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": workload_name(cfg), "m": cfg.m, "k": cfg.k, "n": cfg.n,
+        "config": {"workload": workload_name(cfg, args.glu), "m": cfg.m, "k": cfg.k, "n": cfg.n,
                    "group": cfg.group, "format": synth.FORMAT_NAMES[cfg.fmt],
                    "weight_pool_buffers": pool_n, "hot_cache": bool(args.hot),
                    "parallelism": "single GPU"},

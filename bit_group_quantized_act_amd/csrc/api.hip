@@ -119,6 +119,28 @@ w4a8_status check_activation_ptrs(const int8_t *xq, const float *xs, const int32
     return W4A8_OK;
 }
 
+// Checks shared by the gated entry points (after check_layout): the [gate; up] split, the
+// activation and the gate-to-up span that one descriptor addresses (offsets below 2^31).
+w4a8_status check_glu(const w4a8_layout *L, int32_t m, const void *packed, int32_t act) {
+    if (m < 0) return fail(W4A8_ERR_ARG, "m = %d is negative", m);
+    if (m > (1 << 20)) return fail(W4A8_ERR_UNSUPPORTED, "m = %d is above 2^20", m);
+    if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
+    if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
+    if (L->n % (2 * W4A8_PANEL_ROWS) != 0)
+        return fail(W4A8_ERR_ARG, "n = %d is not 2F with F a multiple of %d (gate, then up rows)",
+                    L->n, W4A8_PANEL_ROWS);
+    if (act < W4A8_ACT_SILU || act > W4A8_ACT_GELU_ERF)
+        return fail(W4A8_ERR_ARG, "act = %d is not a w4a8_act", act);
+    const uint64_t span_rows = static_cast<uint64_t>(L->n / 2 + W4A8_PANEL_ROWS);
+    const uint64_t code_span = span_rows * static_cast<uint64_t>(L->k) / 2;
+    const uint64_t meta_span = span_rows * ((static_cast<uint64_t>(L->k / L->group) + 3) / 4) * 4 *
+                               static_cast<uint64_t>(L->format == W4A8_AFFINE_U4 ? 4 : 2);
+    if (code_span > 0x7FFFFFF0ull || meta_span > 0x7FFFFFF0ull)
+        return fail(W4A8_ERR_UNSUPPORTED, "the gate-to-up span (%llu code bytes) exceeds 2^31 - 16",
+                    static_cast<unsigned long long>(code_span));
+    return W4A8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,32 +291,35 @@ w4a8_status w4a8_linear(const w4a8_layout *L, const void *packed, int32_t m, con
     return launched(w4a8::launch_gemm(g, pk, m, xq, xs, xsum, y, nullptr, st), "gemm launch");
 }
 
+w4a8_status w4a8_gemm_glu(const w4a8_layout *L, const void *packed, int32_t m, const int8_t *xq,
+                          const float *xs, const int32_t *xsum, int32_t act, float *y,
+                          void *stream) {
+    w4a8_status s = check_layout(L);
+    if (s != W4A8_OK) return s;
+    if ((s = check_glu(L, m, packed, act)) != W4A8_OK) return s;
+    if (m == 0) return ok();
+    if ((s = check_gemm_size(L, m)) != W4A8_OK) return s;
+    if ((s = check_activation_ptrs(xq, xs, xsum)) != W4A8_OK) return s;
+    W4A8_REQUIRE_PTR(y);
+    if ((s = check_device()) != W4A8_OK) return s;
+    const w4a8::Geom g = geom_of(L);
+    const uint8_t *pk = static_cast<const uint8_t *>(packed);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (m == 1)
+        return launched(w4a8::launch_gemv_glu(g, act, pk, xq, xs, xsum, y, st), "gated gemv launch");
+    return launched(w4a8::launch_gemm_glu(g, act, pk, m, xq, xs, xsum, y, st), "gated gemm launch");
+}
+
 w4a8_status w4a8_linear_glu(const w4a8_layout *L, const void *packed, int32_t m, const float *x,
                             int32_t hadamard_block, int32_t act, int8_t *xq, float *xs,
                             int32_t *xsum, float *y, void *stream) {
     w4a8_status s = check_layout(L);
     if (s != W4A8_OK) return s;
-    if (m < 0) return fail(W4A8_ERR_ARG, "m = %d is negative", m);
-    if (m > (1 << 20)) return fail(W4A8_ERR_UNSUPPORTED, "m = %d is above 2^20", m);
-    if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
-    if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
-    if (L->n % (2 * W4A8_PANEL_ROWS) != 0)
-        return fail(W4A8_ERR_ARG, "n = %d is not 2F with F a multiple of %d (gate, then up rows)",
-                    L->n, W4A8_PANEL_ROWS);
-    if (act < W4A8_ACT_SILU || act > W4A8_ACT_GELU_ERF)
-        return fail(W4A8_ERR_ARG, "act = %d is not a w4a8_act", act);
+    if ((s = check_glu(L, m, packed, act)) != W4A8_OK) return s;
     if (hadamard_block != 0 && hadamard_block != 128)
         return fail(W4A8_ERR_ARG, "hadamard_block %d is not 0 or 128", hadamard_block);
     if (hadamard_block == 128 && L->k % 128 != 0)
         return fail(W4A8_ERR_ARG, "k = %d is not a multiple of the rotation block 128", L->k);
-    // a gate row and its up row are addressed through one descriptor (offsets below 2^31)
-    const uint64_t span_rows = static_cast<uint64_t>(L->n / 2 + W4A8_PANEL_ROWS);
-    const uint64_t code_span = span_rows * static_cast<uint64_t>(L->k) / 2;
-    const uint64_t meta_span = span_rows * ((static_cast<uint64_t>(L->k / L->group) + 3) / 4) * 4 *
-                               static_cast<uint64_t>(L->format == W4A8_AFFINE_U4 ? 4 : 2);
-    if (code_span > 0x7FFFFFF0ull || meta_span > 0x7FFFFFF0ull)
-        return fail(W4A8_ERR_UNSUPPORTED, "the gate-to-up span (%llu code bytes) exceeds 2^31 - 16",
-                    static_cast<unsigned long long>(code_span));
     if (m == 0) return ok();
     if ((s = check_gemm_size(L, m)) != W4A8_OK) return s;
     W4A8_REQUIRE_PTR(x);

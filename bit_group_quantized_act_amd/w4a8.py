@@ -21,8 +21,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "no gfx950 device
 
 # Every exported symbol of the C ABI (the header's declarations, in order).
 EXPORTS = ("w4a8_packed_layout", "w4a8_pack_weights", "w4a8_prep", "w4a8_gemv", "w4a8_gemm",
-           "w4a8_linear", "w4a8_linear_glu", "w4a8_debug_partials", "w4a8_status_string",
-           "w4a8_last_error")
+           "w4a8_linear", "w4a8_linear_glu", "w4a8_gemm_glu", "w4a8_debug_partials",
+           "w4a8_status_string", "w4a8_last_error")
 ACT_SILU, ACT_GELU_TANH, ACT_GELU_ERF = 0, 1, 2
 
 
@@ -66,8 +66,9 @@ def load() -> ctypes.CDLL:
     lib.w4a8_gemm.argtypes = [LP, P, i32, P, P, P, P, P]
     lib.w4a8_linear.argtypes = [LP, P, i32, P, i32, P, P, P, P, P]
     lib.w4a8_linear_glu.argtypes = [LP, P, i32, P, i32, i32, P, P, P, P, P]
+    lib.w4a8_gemm_glu.argtypes = [LP, P, i32, P, P, P, i32, P, P]
     lib.w4a8_debug_partials.argtypes = [LP, P, i32, P, P, P, P]
-    for f in EXPORTS[:8]:
+    for f in EXPORTS[:9]:
         getattr(lib, f).restype = ctypes.c_int
     lib.w4a8_status_string.argtypes = [ctypes.c_int]
     lib.w4a8_status_string.restype = ctypes.c_char_p
@@ -239,3 +240,17 @@ def linear_glu(L: Layout, packed: torch.Tensor, x: torch.Tensor, act: int = ACT_
                                   _stream(x.device)), "w4a8_linear_glu")
     y = y[0] if (squeeze and out is None) else y
     return (y, (xq, xs, xsum)) if prep_out is not None else y
+
+
+def gemm_glu(L: Layout, packed: torch.Tensor, xq: torch.Tensor, xs: torch.Tensor,
+             xsum: torch.Tensor, act: int = ACT_SILU, out=None):
+    """Gated output from prepared activations (w4a8_gemm_glu): xq [m, k] (or [k]), xs and xsum
+    [k/group, m] -> act(gate) * up, fp32 [m, n/2] (or [n/2])."""
+    squeeze = xq.dim() == 1
+    q2 = xq.unsqueeze(0) if squeeze else xq
+    m = q2.shape[0]
+    y = out if out is not None else torch.empty((m, L.n // 2), dtype=torch.float32,
+                                                device=xq.device)
+    _check(load().w4a8_gemm_glu(ctypes.byref(L), _ptr(packed), m, _ptr(q2), _ptr(xs),
+                                _ptr(xsum), act, _ptr(y), _stream(xq.device)), "w4a8_gemm_glu")
+    return y[0] if (squeeze and out is None) else y

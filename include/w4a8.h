@@ -217,6 +217,18 @@ w4a8_status w4a8_linear_glu(const w4a8_layout *L, const void *packed, int32_t m,
                             int32_t *xsum, float *y, void *stream);
 
 /*
+ * The gated output from prepared activations (the second half of w4a8_linear_glu):
+ *   xq int8 [m][k], xs fp32 [k/group][m], xsum int32 [k/group][m] from w4a8_prep
+ *   act   a w4a8_act
+ *   y     fp32 [m][L->n / 2] = act(gate) * up, as for w4a8_linear_glu
+ * m == 1 runs the gated GEMV, m > 1 the gated GEMM; m == 0 is a no-op.  Errors as for
+ * w4a8_linear_glu.  Source: as for w4a8_linear_glu.
+ */
+w4a8_status w4a8_gemm_glu(const w4a8_layout *L, const void *packed, int32_t m, const int8_t *xq,
+                          const float *xs, const int32_t *xsum, int32_t act, float *y,
+                          void *stream);
+
+/*
  * The exact int32 partials D[r][n][g] (definitions above) written by the same kernel code as
  * the GEMV (m == 1) or the GEMM (m > 1), with the fp32 epilogue replaced by a store of D.
  *   xsum  as from w4a8_prep (the AFFINE partial is recovered from the u - 8 codes as

@@ -149,6 +149,14 @@ def test_invalid_calls_are_rejected_on_the_host(lib):
     assert lib.w4a8_linear_glu(ctypes.byref(big), p, 1, p, 0, silu, p, p, p, p,
                                None) == ERR_UNSUPPORTED
     assert lib.w4a8_linear_glu(LP, p, 0, None, 0, silu, None, None, None, None, None) == 0
+    # gemm_glu: the same split / act / span checks, missing activations, m == 0 a no-op
+    assert lib.w4a8_gemm_glu(ctypes.byref(L192), p, 2, p, p, p, silu, p, None) == ERR_ARG
+    assert lib.w4a8_gemm_glu(LP, p, 2, p, p, p, 7, p, None) == ERR_ARG
+    assert lib.w4a8_gemm_glu(LP, p, 2, None, p, p, silu, p, None) == ERR_ARG
+    assert lib.w4a8_gemm_glu(LP, p, 2, p, p, p, silu, None, None) == ERR_ARG
+    assert lib.w4a8_gemm_glu(LP, p16, 2, p, p, p, silu, p, None) == ERR_ARG
+    assert lib.w4a8_gemm_glu(ctypes.byref(big), p, 2, p, p, p, silu, p, None) == ERR_UNSUPPORTED
+    assert lib.w4a8_gemm_glu(LP, p, 0, None, None, None, silu, None, None) == 0
 
 
 @pytest.mark.skipif(_gpu_visible(), reason="checks the no-device path; would launch on a GPU")

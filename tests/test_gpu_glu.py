@@ -101,6 +101,30 @@ def test_glu_parity(name, over, act):
     check_z(got["z"], ref["z"], ref["tz"], f"glu {name} {over}")
 
 
+@pytest.mark.parametrize("name,over,act", [("C2a", dict(n=640, k=4096), S),
+                                            ("C4", dict(m=1, n=384, k=1536), GE),
+                                            ("C3a", dict(m=65, n=1280, k=1280), GT)],
+                         ids=["gemv-fused", "gemv-rot", "gemm"])
+def test_glu_from_prepared_activations_same_bits(name, over, act):
+    # w4a8_gemm_glu on w4a8_linear_glu's own prepass outputs: the same kernel arithmetic, so the
+    # same bits (the decode row compares the fused kernel with prepass + gated GEMV)
+    w = _w4a8()
+    L = synth.make(name, full_range=True, **over)
+    cfg = L["cfg"]
+    lay, packed = w.pack(to_dev(L["codes"]), to_dev(L["scales"]), cfg.fmt, cfg.group,
+                         bias=to_dev(L["bias"]), codebook=to_dev(L["codebook"]))
+    z1, (xq, xs, xsum) = w.linear_glu(lay, packed, to_dev(L["x"]), act, cfg.hadamard,
+                                      prep_out=tuple(torch.empty(s, dtype=d, device="cuda:0")
+                                                     for s, d in (((cfg.m, cfg.k), torch.int8),
+                                                                  ((cfg.k // cfg.group, cfg.m),
+                                                                   torch.float32),
+                                                                  ((cfg.k // cfg.group, cfg.m),
+                                                                   torch.int32))))
+    z2 = w.gemm_glu(lay, packed, xq, xs, xsum, act)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(z1.cpu().numpy().reshape(z2.shape)), _bits(z2.cpu().numpy()))
+
+
 def test_glu_output_differs_from_the_other_activation():
     # the act argument reaches the kernel: silu and gelu outputs of one layer differ
     L = synth.make("C1", n=256, full_range=True)
