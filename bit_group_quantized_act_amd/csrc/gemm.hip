@@ -44,8 +44,8 @@
 //   Gated output (GLU).  For a [gate; up] linear (n = 2F, F a multiple of 64) a workgroup owns
 //   64 output channels: wavefronts 0 and 1 compute them from gate panel nt, wavefronts 2 and 3
 //   from the up panel F / 64 panels on (the same tile count as the plain GEMM); after the k loop
-//   the up wavefronts hand their tiles to the gate wavefronts through LDS, which store
-//   act(gate) * up.
+//   each gate/up pair swaps half its tiles through LDS and each of the two stores one row tile
+//   of act(gate) * up.
 #include "w4a8_kernels.h"
 
 #include <type_traits>
@@ -332,25 +332,27 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     if (PARTIALS || !active) return;
 
     if (GLU) {
-        // every wavefront is done with the stage buffers; the up wavefronts' tiles go to LDS
+        // Gate wavefront q and up wavefront q + 2 hold the same outputs' gate and up tiles.  Every
+        // wavefront is done with the stage buffers; each pair swaps half its tiles through LDS
+        // (the up tile 0 to the gate wavefront, the gate tile 1 to the up wavefront), and each
+        // wavefront finishes one row tile: the activations split evenly.
         __syncthreads();
-        float *xch = reinterpret_cast<float *>(&lds[0][0]);   // [2][32][64] fp32, 16 KiB
-        if (pnl) {
+        float *xch = reinterpret_cast<float *>(&lds[0][0]);   // [pnl][pair][16][64] fp32, 16 KiB
+        const int q = wave & 1;
+        const int give = pnl ? 0 : 16;                         // the tile this wavefront hands over
 #pragma unroll
-            for (int i = 0; i < 32; ++i) xch[((wave & 1) * 32 + i) * 64 + lane] = acc[i];
-        }
+        for (int e = 0; e < 16; ++e) xch[((pnl * 2 + q) * 16 + e) * 64 + lane] = acc[give + e];
         __syncthreads();
-        if (pnl) return;
         const int f_n = geom.n / 2;
-        const int colz = nt * kPanelRows + prow;          // output channel, < F
+        const int colz = nt * kPanelRows + prow;               // output channel, < F
+        const int t = pnl;                                     // the row tile this wavefront stores
+        const int other = ((pnl ^ 1) * 2 + q) * 16;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = m0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
-                const float u = xch[((wave & 1) * 32 + 16 * t + e) * 64 + lane];
-                if (row < m) y[(int64_t)row * f_n + colz] = act_apply(act, acc[16 * t + e]) * u;
-            }
+        for (int e = 0; e < 16; ++e) {
+            const int row = m0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+            const float mine = acc[16 * t + e], theirs = xch[(other + e) * 64 + lane];
+            const float g = pnl ? theirs : mine, u = pnl ? mine : theirs;
+            if (row < m) y[(int64_t)row * f_n + colz] = act_apply(act, g) * u;
         }
         return;
     }
