@@ -56,8 +56,9 @@ def _load():
     lib.oracle_partials.argtypes = [i32, P, P, i64, i64, i32, P, i64, P]
     lib.oracle_linear.argtypes = [i32, P, P, P, P, i64, i64, i32, P, P, P, i64, P, P]
     lib.oracle_glu.argtypes = [i32, P, P, i64, i64, P, P]
+    lib.oracle_softcap_argmax.argtypes = [P, i64, i64, ctypes.c_double, P, P, P]
     for f in ("oracle_rotate", "oracle_quantize", "oracle_prep", "oracle_partials",
-              "oracle_linear", "oracle_glu", "oracle_num_threads"):
+              "oracle_linear", "oracle_glu", "oracle_softcap_argmax", "oracle_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -179,3 +180,20 @@ def glu(act: int, y: np.ndarray, t: np.ndarray = None):
         tz = np.empty((m, n // 2), np.float64)
     _check(_load().oracle_glu(act, _ptr(y), _ptr(t), m, n, _ptr(z), _ptr(tz)), "glu")
     return (z, tz) if t is not None else z
+
+
+def softcap_argmax(y: np.ndarray, cap: float = 0.0):
+    """Greedy tail of a vocabulary head: (logits, token, value) per row of y [m, n] (or [n]);
+    logits = cap * tanh(y / cap) for cap > 0 (y for cap == 0), token = the smallest index of
+    the largest logit, all in fp64."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    one = y.ndim == 1
+    if one:
+        y = y[None, :]
+    m, n = y.shape
+    logits = np.empty_like(y)
+    token = np.empty(m, np.int64)
+    value = np.empty(m, np.float64)
+    _check(_load().oracle_softcap_argmax(_ptr(y), m, n, float(cap), _ptr(logits), _ptr(token),
+                                         _ptr(value)), "softcap_argmax")
+    return (logits[0], int(token[0]), float(value[0])) if one else (logits, token, value)

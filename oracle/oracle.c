@@ -45,6 +45,13 @@
  *                silu(v)      = v / (1 + exp(-v))
  *                gelu_tanh(v) = v/2 * (1 + tanh(sqrt(2/pi) * (v + 0.044715 v^3)))
  *                gelu_erf(v)  = v/2 * (1 + erf(v / sqrt(2)))
+ *   lm_head    "cactus-compute/engine PR #750: Metal Support", the commit list (the orthogonal
+ *              lm_head with its softcap fused into a GPU argmax / sampling tail) and the file
+ *              table (GPU-side sampling and argmax helpers); "cactus PR #697", the lm_head commit
+ *              (one scale per weight row viewed as K/128 virtual 128-wide groups, exactly).
+ *              Reading: logits = c * tanh(y / c) for a cap c > 0, logits = y for c == 0; the
+ *              greedy token is the smallest index of the largest logit.  The row-scale view is
+ *              the output formula with every group scale of a row equal to the row's scale.
  *
  * Weight formats (canonical input, one byte holds two 4-bit codes, low nibble = even k):
  *   format 0 (symmetric):  code is a two's-complement q in [-8, 7]; w_int = q
@@ -331,6 +338,32 @@ int oracle_glu(int32_t act, const double *y, const double *t, int64_t m, int64_t
             if (tz && t)
                 tz[r * f_n + f] = 1.2 * fabs(u) * t[r * n + f] + fabs(a) * t[r * n + f_n + f];
         }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- greedy tail ---------- */
+/*
+ * Per row r of y [m][n]: logits = cap * tanh(y / cap) (cap > 0) or y (cap == 0), in fp64, and
+ * token[r] = the smallest index of the largest logit, value[r] = that logit.
+ */
+int oracle_softcap_argmax(const double *y, int64_t m, int64_t n, double cap, double *logits,
+                          int64_t *token, double *value)
+{
+    if (n <= 0 || m < 0 || cap < 0.0)
+        return ORACLE_BAD_ARGS;
+    for (int64_t r = 0; r < m; ++r) {
+        int64_t best = 0;
+        for (int64_t c = 0; c < n; ++c) {
+            double v = y[r * n + c];
+            if (cap > 0.0)
+                v = cap * tanh(v / cap);
+            logits[r * n + c] = v;
+            if (v > logits[r * n + best])
+                best = c;
+        }
+        token[r] = best;
+        value[r] = logits[r * n + best];
+    }
     return ORACLE_OK;
 }
 

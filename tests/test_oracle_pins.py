@@ -469,3 +469,47 @@ def test_glu_error_bound_covers_perturbed_inputs(act):
     for e in (1e-4, 1e-6):
         yp = y + e * t * rng.choice([-1.0, 1.0], y.shape)
         assert np.all(np.abs(oracle.glu(act, yp) - z) <= e * tz * (1 + 1e-9) + 1e-300)
+
+
+# ----------------------------------------------------------------------------- greedy tail
+
+def test_softcap_matches_library_tanh_and_bounds():
+    rng = np.random.default_rng(5)
+    y = rng.standard_normal((3, 1000)) * 60.0
+    for cap in (30.0, 5.0):
+        logits, tok, val = oracle.softcap_argmax(y, cap)
+        np.testing.assert_allclose(logits, cap * np.tanh(y / cap), rtol=1e-15, atol=1e-13)
+        assert np.all(np.abs(logits) <= cap)   # tanh rounds to exactly 1 far out
+    logits, tok, val = oracle.softcap_argmax(y, 0.0)
+    assert np.array_equal(logits, y)
+
+
+def test_argmax_first_index_on_ties_and_softcap_keeps_the_order():
+    rng = np.random.default_rng(6)
+    y = rng.standard_normal((5, 300))
+    y[:, [17, 42, 299]] = 9.0            # three equal maxima: the smallest index wins
+    _, tok, val = oracle.softcap_argmax(y, 0.0)
+    assert np.all(tok == 17) and np.all(val == 9.0)
+    # softcap is strictly increasing: the same token as numpy's first-occurrence argmax of y
+    z = rng.standard_normal((4, 500)) * 20.0
+    _, tok_c, _ = oracle.softcap_argmax(z, 30.0)
+    assert np.array_equal(tok_c, np.argmax(z, axis=1))
+    # control: a planted "last index on ties" reading picks 299, not 17
+    assert int(np.flatnonzero(y[0] == y[0].max())[-1]) != int(tok[0])
+
+
+def test_row_scale_view_equals_one_scale_per_row():
+    # one scale per weight row replicated over K/128 groups gives y = s_row * sum_g xs_g * D_g
+    # exactly in fp64 (a power-of-two row scale keeps every product exact)
+    rng = np.random.default_rng(9)
+    n, k, g = 8, 512, 128
+    codes = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    s_row = (2.0 ** rng.integers(-12, -6, size=n)).astype(np.float16)
+    scales = np.repeat(s_row[:, None], k // g, axis=1)
+    x = rng.standard_normal((2, k)).astype(np.float32)
+    xq, xs, xsum = oracle.prep(x, g, 128)
+    y = oracle.linear(oracle.FORMAT_SYM, codes, scales, xq, xs, xsum, g, with_terms=False)
+    d = oracle.partials(oracle.FORMAT_SYM, codes, xq, g)            # [m][n][ng]
+    want = s_row.astype(np.float64)[None, :] * np.einsum("mng,mg->mn", d.astype(np.float64),
+                                                            xs.astype(np.float64))
+    np.testing.assert_allclose(y, want, rtol=1e-15, atol=0)
