@@ -25,6 +25,12 @@ cpu_baseline = the CPU oracle (plain C, OpenMP) on the same workload, repeated f
 
 --glu ACT times the gated variant instead (w4a8_linear_glu): the config's weights read as a
 [gate; up] pair (n = 2F), and the output is act(gate) * up, fp32 [m][F].
+
+--argmax CAP times the greedy tail of a vocabulary head instead (one row; w4a8_lm_head_argmax:
+the prepass, the GEMV that also soft-caps the logits with CAP (0: no cap) and stores each
+64-row panel's largest key, and a one-workgroup reduction of those keys into the token).  The
+timed "kernel" is w4a8_gemv_argmax on prepared activations: the GEMV and the reduction
+together, with the plain GEMV's algorithmic bytes plus the keys (written and read) and the token.
 """
 from __future__ import annotations
 
@@ -86,6 +92,9 @@ def parse():
                     help="time budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--glu", choices=["silu", "gelu_tanh", "gelu_erf"], default=None,
                     help="time w4a8_linear_glu (the weights as a [gate; up] pair) instead")
+    ap.add_argument("--argmax", type=float, default=None, metavar="CAP",
+                    help="time w4a8_lm_head_argmax (soft cap CAP, 0 for none) on a one-row "
+                         "workload instead")
     ap.add_argument("--hot", action="store_true",
                     help="reuse one weight buffer (measures cache, not HBM; labelled)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -109,16 +118,19 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 8}), flush=True)
 
 
-def workload_name(cfg, glu=None):
+def workload_name(cfg, glu=None, cap=None):
     from bit_group_quantized_act_amd import synth
     kind = "decode GEMV" if cfg.m == 1 else "prefill GEMM"
     rot = ", 128-block WHT" if cfg.hadamard else ""
     fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072
-    how = ("prepass fused into the GEMV" if fused else
+    how = ("prepass fused into the GEMV" if fused and cap is None else
            "prepass + GEMV" if cfg.m == 1 else "prepass + GEMM")
     gated = "" if glu is None else f", gated output {glu}(gate)*up with F={cfg.n // 2}"
+    tail = "" if cap is None else (f", greedy tail: logits soft-capped at {cap:g} and their "
+                                   f"first maximum" if cap > 0 else
+                                   ", greedy tail: the first maximum of the logits")
     return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
-            f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights{rot}{gated} ({how} per step)")
+            f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights{rot}{gated}{tail} ({how} per step)")
 
 
 def main():
@@ -149,7 +161,15 @@ def main():
                              bias=t(layer["bias"]), codebook=t(layer["codebook"]))
     wbytes = synth.weight_bytes(cfg)
     fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072   # w4a8_linear's one-kernel case
+    cap = args.argmax
+    if cap is not None:
+        if cfg.m != 1 or args.glu is not None or not cap >= 0:
+            print("--argmax needs a one-row workload, no --glu and a cap >= 0", file=sys.stderr)
+            sys.exit(2)
+        fused = False                                  # the tail runs in the two-kernel path
     alg_bytes = synth.algorithmic_bytes(cfg, fused_prep=fused)
+    if cap is not None:                                # keys written and read, token, logit
+        alg_bytes += 2 * w4a8.argmax_work_bytes(cfg.n) + 8
     act = None
     if args.glu is not None:
         if cfg.n % 128 != 0:
@@ -169,13 +189,18 @@ def main():
     xsum = torch.empty((ng, cfg.m), dtype=torch.int32, device=dev)
     y = torch.empty((cfg.m, cfg.n if act is None else cfg.n // 2), dtype=torch.float32,
                     device=dev)
+    token = torch.empty(1, dtype=torch.int32, device=dev)
+    tval = torch.empty(1, dtype=torch.float32, device=dev)
+    work = w4a8.argmax_work(lay, dev)
     torch.cuda.synchronize()
 
     def linear(i):
         # the dominant kernel alone: the fused prepass + GEMV at one row (the plain GEMV for a
         # vocabulary-sized row), the GEMM above
         pk = pool[i % pool_n]
-        if act is not None:
+        if cap is not None:
+            w4a8.gemv_argmax(lay, pk, xq, xs, xsum, cap, out=(y[0], token, tval), work=work)
+        elif act is not None:
             if fused:
                 w4a8.linear_glu(lay, pk, x, act, cfg.hadamard, out=y, prep_out=(xq, xs, xsum))
             else:
@@ -188,7 +213,10 @@ def main():
             w4a8.gemm(lay, pk, xq, xs, xsum, out=y)
 
     def step(i):
-        if act is not None:
+        if cap is not None:
+            w4a8.lm_head_argmax(lay, pool[i % pool_n], x, cap, cfg.hadamard,
+                                out=(y[0], token, tval), work=work, prep_out=(xq, xs, xsum))
+        elif act is not None:
             w4a8.linear_glu(lay, pool[i % pool_n], x, act, cfg.hadamard, out=y,
                             prep_out=(xq, xs, xsum))
         else:
@@ -241,8 +269,10 @@ def main():
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4))
     kname = "gemv" if cfg.m == 1 else "gemm"     # the fused kernel lives in gemv.hip
-    traffic_key = cfg.name if act is None else f"{cfg.name}-glu"   # counters of the plain kernel
-    roof.update(traffic=measured_traffic(traffic_key, kname), kernel=kname,
+    traffic_key = (cfg.name if act is None and cap is None else   # counters of the plain kernel
+                   f"{cfg.name}-{'glu' if act is not None else 'argmax'}")
+    shown = kname if cap is None else "gemv_argmax (GEMV with the tail + key reduction)"
+    roof.update(traffic=measured_traffic(traffic_key, kname), kernel=shown,
                 kernel_us=round(us_linear, 3), alg_bytes_per_launch=alg_bytes,
                 int_ops_per_launch=ops,
                 tops=round(ops / (us_linear * 1e-6) / 1e12, 2))
@@ -269,6 +299,8 @@ def main():
                                codebook=cb, with_terms=False)
             if act is not None:
                 oracle.glu(act, yo)
+            if cap is not None:
+                oracle.softcap_argmax(yo, cap)
             reps += 1
             el = time.perf_counter() - t0
             if el >= args.cpu_seconds:
@@ -278,7 +310,9 @@ def main():
         cpu = dict(value=round(sample_wbytes * reps / el / 1e9, 3), unit="GB/s",
                    cores=oracle.num_threads(), kind="oracle",
                    sample=f"{what} of {cfg.name} (prep + linear"
-                          f"{' + gated output' if act is not None else ''}), repeated {reps}x in "
+                          f"{' + gated output' if act is not None else ''}"
+                          f"{' + soft cap and argmax' if cap is not None else ''}), repeated "
+                          f"{reps}x in "
                           f"{el:.1f} s ({1e3 * el / reps:.2f} ms each)")
 
     out = {
@@ -294,7 +328,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": workload_name(cfg, args.glu), "m": cfg.m, "k": cfg.k, "n": cfg.n,
+        "config": {"workload": workload_name(cfg, args.glu, cap), "m": cfg.m, "k": cfg.k, "n": cfg.n,
                    "group": cfg.group, "format": synth.FORMAT_NAMES[cfg.fmt],
                    "weight_pool_buffers": pool_n, "hot_cache": bool(args.hot),
                    "parallelism": "single GPU"},

@@ -3,6 +3,8 @@
 #include "../../include/w4a8.h"
 #include "w4a8_kernels.h"
 
+#include <cmath>
+
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -116,6 +118,24 @@ w4a8_status check_activation_ptrs(const int8_t *xq, const float *xs, const int32
     W4A8_REQUIRE_PTR(xq);
     W4A8_REQUIRE_PTR(xs);
     W4A8_REQUIRE_PTR(xsum);
+    return W4A8_OK;
+}
+
+// Checks shared by the greedy-tail entry points: the cap and the three tail buffers.
+w4a8_status check_tail(const w4a8_layout *L, float softcap, const int32_t *token,
+                       const float *value, const void *work, uint64_t work_bytes) {
+    if (!(softcap >= 0.0f) || !std::isfinite(softcap))
+        return fail(W4A8_ERR_ARG, "softcap %g is negative or not finite", softcap);
+    if (!token) return fail(W4A8_ERR_ARG, "token is NULL");
+    if (!value) return fail(W4A8_ERR_ARG, "value is NULL");
+    if (!aligned(token, 4) || !aligned(value, 4))
+        return fail(W4A8_ERR_ARG, "token / value are not 4-byte aligned");
+    if (!work) return fail(W4A8_ERR_ARG, "work is NULL");
+    if (!aligned(work, 8)) return fail(W4A8_ERR_ARG, "work is not 8-byte aligned");
+    if (work_bytes < W4A8_ARGMAX_WORK_BYTES(L->n))
+        return fail(W4A8_ERR_ARG, "work has %llu bytes, n = %d needs %llu",
+                    static_cast<unsigned long long>(work_bytes), L->n,
+                    static_cast<unsigned long long>(W4A8_ARGMAX_WORK_BYTES(L->n)));
     return W4A8_OK;
 }
 
@@ -338,6 +358,51 @@ w4a8_status w4a8_linear_glu(const w4a8_layout *L, const void *packed, int32_t m,
     if (m == 1)
         return launched(w4a8::launch_gemv_glu(g, act, pk, xq, xs, xsum, y, st), "gated gemv launch");
     return launched(w4a8::launch_gemm_glu(g, act, pk, m, xq, xs, xsum, y, st), "gated gemm launch");
+}
+
+w4a8_status w4a8_lm_head_argmax(const w4a8_layout *L, const void *packed, const float *x,
+                                int32_t hadamard_block, float softcap, int8_t *xq, float *xs,
+                                int32_t *xsum, float *logits, int32_t *token, float *value,
+                                void *work, uint64_t work_bytes, void *stream) {
+    w4a8_status s = check_layout(L);
+    if (s != W4A8_OK) return s;
+    if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
+    if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
+    if ((s = check_tail(L, softcap, token, value, work, work_bytes)) != W4A8_OK) return s;
+    if (hadamard_block != 0 && hadamard_block != 128)
+        return fail(W4A8_ERR_ARG, "hadamard_block %d is not 0 or 128", hadamard_block);
+    if (hadamard_block == 128 && L->k % 128 != 0)
+        return fail(W4A8_ERR_ARG, "k = %d is not a multiple of the rotation block 128", L->k);
+    W4A8_REQUIRE_PTR(x);
+    if ((s = check_activation_ptrs(xq, xs, xsum)) != W4A8_OK) return s;
+    W4A8_REQUIRE_PTR(logits);
+    if ((s = check_device()) != W4A8_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = w4a8::launch_prep(x, 1, L->k, L->group, hadamard_block, xq, xs, xsum, st);
+    if (e != hipSuccess) return launched(e, "prep launch");
+    const w4a8::Tail tail{softcap, static_cast<unsigned long long *>(work), token, value};
+    return launched(w4a8::launch_gemv_argmax(geom_of(L), static_cast<const uint8_t *>(packed), xq,
+                                             xs, xsum, logits, tail, st),
+                    "greedy tail gemv launch");
+}
+
+w4a8_status w4a8_gemv_argmax(const w4a8_layout *L, const void *packed, const int8_t *xq,
+                             const float *xs, const int32_t *xsum, float softcap, float *logits,
+                             int32_t *token, float *value, void *work, uint64_t work_bytes,
+                             void *stream) {
+    w4a8_status s = check_layout(L);
+    if (s != W4A8_OK) return s;
+    if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
+    if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
+    if ((s = check_tail(L, softcap, token, value, work, work_bytes)) != W4A8_OK) return s;
+    if ((s = check_activation_ptrs(xq, xs, xsum)) != W4A8_OK) return s;
+    W4A8_REQUIRE_PTR(logits);
+    if ((s = check_device()) != W4A8_OK) return s;
+    const w4a8::Tail tail{softcap, static_cast<unsigned long long *>(work), token, value};
+    return launched(w4a8::launch_gemv_argmax(geom_of(L), static_cast<const uint8_t *>(packed), xq,
+                                             xs, xsum, logits, tail,
+                                             static_cast<hipStream_t>(stream)),
+                    "greedy tail gemv launch");
 }
 
 w4a8_status w4a8_debug_partials(const w4a8_layout *L, const void *packed, int32_t m,

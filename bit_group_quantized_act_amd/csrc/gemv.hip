@@ -24,6 +24,11 @@
 //   F / 64 panels on in lanes 32..63: every load is still two contiguous 512-byte runs, the grid
 //   and the bytes per workgroup are those of the plain GEMV, and after the cross-wavefront sum
 //   lane r < 32 combines its gate value with lane r + 32's up value into act(gate) * up.
+//   Greedy tail (ARGMAX).  Wavefront 0 caps each logit, stores it, and turns it into a 64-bit key
+//   (an order-preserving image of the value above, the inverted row below: the largest key is
+//   the largest logit at its smallest row); a butterfly gives the workgroup's largest key, one
+//   atomic max merges it into the buffer the prepass cleared, and the workgroup that counts
+//   last decodes the token and its logit.  Nothing waits on another workgroup.
 #include "w4a8_kernels.h"
 
 namespace w4a8 {
@@ -50,10 +55,25 @@ __device__ __forceinline__ int dot_chunk(v4i v, const int *__restrict__ xc, uint
     return acc;
 }
 
+// The greedy tail's key of a logit v at row r: the logit's order in the high half (sign bit
+// flipped for v >= 0, all bits for v < 0: unsigned order = float order), ~r in the low half (on
+// equal logits the smaller row wins).  The largest key over a wavefront's lanes:
+__device__ inline unsigned long long wave_max_key(unsigned long long key) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), o, 64);
+        const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key >> 32), o, 64);
+        const unsigned long long other = (static_cast<unsigned long long>(hi) << 32) | lo;
+        key = other > key ? other : key;
+    }
+    return key;
+}
+
 // FUSED: x is the fp32 activation row; xq/xs/xsum are outputs written by workgroup 0.
 // Otherwise xq/xs/xsum are the prepass outputs (inputs here) and x is unused.
 // XQ (fused only): activation quads per lane, enough for the wavefront's groups.
-template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, int XQ, bool GLU>
+template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, int XQ, bool GLU,
+          bool ARGMAX>
 __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict__ packed,
                                                       const Geom geom,
                                                       const float *__restrict__ x,
@@ -61,8 +81,9 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
                                                       float *__restrict__ xs,
                                                       int *__restrict__ xsum,
                                                       float *__restrict__ y,
-                                                      int *__restrict__ d, int act) {
+                                                      int *__restrict__ d, int act, Tail tail) {
     static_assert(!(GLU && PARTIALS), "the gated output has no partials variant");
+    static_assert(!(ARGMAX && (GLU || PARTIALS || FUSED)), "the greedy tail is a plain GEMV's");
     constexpr int kChunksPerGroup = G / kChunkK;
     constexpr int kLanesPerGroup = G / 4;
     // Fused: activation quads (4 values) per lane that a wavefront quantizes, at most (the
@@ -257,18 +278,34 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
         const float u = __shfl(s, lane + 32, 64);   // lane r < 32: the up value of its row
         const int64_t zr = (int64_t)p * kPanelRows + lrow;
         if (lane < 32 && zr < geom.n / 2) y[zr] = act_apply(act, s) * u;
+    } else if (ARGMAX) {
+        float v = s;
+        if (tail.cap > 0.0f) v = tail.cap * tanhf(v / tail.cap);
+        v = v + 0.0f;                               // -0 becomes +0: equal logits, equal keys
+        unsigned long long key = 0ull;              // below every logit's key
+        if (row < geom.n) {
+            y[row] = v;
+            const uint32_t b = __float_as_uint(v);
+            const uint32_t u = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+            key = (static_cast<unsigned long long>(u) << 32) |
+                  (0xFFFFFFFFu - static_cast<uint32_t>(row));
+        }
+        key = wave_max_key(key);
+        if (lane == 0) tail.keys[blockIdx.x] = key;
     } else if (row < geom.n) {
         y[row] = s;
     }
 }
 
 // (the gated output keeps the grid: two workgroups per gate panel, one per half of its rows)
-template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, int XQ, bool GLU>
+template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, int XQ, bool GLU,
+          bool ARGMAX = false>
 hipError_t launch_k(const Geom &g, int act, const uint8_t *packed, const float *x, int8_t *xq,
-                    float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
+                    float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream,
+                    const Tail &tail = Tail{}) {
     const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
-    gemv_kernel<FMT, G, W, PARTIALS, FUSED, ROT, XQ, GLU><<<grid, 64 * W, 0, stream>>>(
-        packed, g, x, xq, xs, xsum, y, d, act);
+    gemv_kernel<FMT, G, W, PARTIALS, FUSED, ROT, XQ, GLU, ARGMAX><<<grid, 64 * W, 0, stream>>>(
+        packed, g, x, xq, xs, xsum, y, d, act, tail);
     return hipGetLastError();
 }
 
@@ -349,6 +386,69 @@ hipError_t launch_gemv_fused(const Geom &g, const uint8_t *packed, const float *
                              int8_t *xq, float *xs, int32_t *xsum, float *y, hipStream_t stream) {
     if (hadamard) return launch_f<false, true, true>(g, packed, x, xq, xs, xsum, y, nullptr, stream);
     return launch_f<false, true, false>(g, packed, x, xq, xs, xsum, y, nullptr, stream);
+}
+
+namespace {
+template <int FMT, int G>
+hipError_t launch_argmax_w(const Geom &g, const uint8_t *packed, const int8_t *xq,
+                           const float *xs, const int32_t *xsum, float *y, const Tail &tail,
+                           hipStream_t stream) {
+    int8_t *q = const_cast<int8_t *>(xq);
+    float *s = const_cast<float *>(xs);
+    int32_t *u = const_cast<int32_t *>(xsum);
+    if ((g.k / G + 3) / 4 >= 6)
+        return launch_k<FMT, G, 8, false, false, false, 1, false, true>(g, 0, packed, nullptr, q,
+                                                                        s, u, y, nullptr, stream,
+                                                                        tail);
+    return launch_k<FMT, G, 4, false, false, false, 1, false, true>(g, 0, packed, nullptr, q, s,
+                                                                    u, y, nullptr, stream, tail);
+}
+
+// The last step of the greedy tail: the largest of the GEMV workgroups' keys (1024 lanes, each
+// over a strided slice; then wavefronts, then the 16 wavefront results in one lane), decoded into
+// the token (its row) and the value (its logit).
+constexpr int kKeyThreads = 1024;
+__global__ __launch_bounds__(kKeyThreads) void argmax_keys_kernel(
+        const unsigned long long *__restrict__ keys, int nkeys, int32_t *__restrict__ token,
+        float *__restrict__ value) {
+    __shared__ unsigned long long wave_key[kKeyThreads / 64];
+    unsigned long long key = 0ull;
+    for (int i = threadIdx.x; i < nkeys; i += kKeyThreads) key = keys[i] > key ? keys[i] : key;
+    key = wave_max_key(key);
+    if ((threadIdx.x & 63) == 0) wave_key[threadIdx.x >> 6] = key;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kKeyThreads / 64; ++w) key = wave_key[w] > key ? wave_key[w] : key;
+        const uint32_t u = static_cast<uint32_t>(key >> 32);
+        *token = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+        *value = __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+    }
+}
+
+template <int FMT>
+hipError_t launch_argmax_g(const Geom &g, const uint8_t *packed, const int8_t *xq,
+                           const float *xs, const int32_t *xsum, float *y, const Tail &tail,
+                           hipStream_t stream) {
+    if (g.group == 64) return launch_argmax_w<FMT, 64>(g, packed, xq, xs, xsum, y, tail, stream);
+    return launch_argmax_w<FMT, 128>(g, packed, xq, xs, xsum, y, tail, stream);
+}
+}  // namespace
+
+hipError_t launch_gemv_argmax(const Geom &g, const uint8_t *packed, const int8_t *xq,
+                              const float *xs, const int32_t *xsum, float *y, const Tail &tail,
+                              hipStream_t stream) {
+    hipError_t e;
+    switch (g.fmt) {
+    case kFmtSym: e = launch_argmax_g<kFmtSym>(g, packed, xq, xs, xsum, y, tail, stream); break;
+    case kFmtAffine:
+        e = launch_argmax_g<kFmtAffine>(g, packed, xq, xs, xsum, y, tail, stream);
+        break;
+    default: e = launch_argmax_g<kFmtCodebook>(g, packed, xq, xs, xsum, y, tail, stream); break;
+    }
+    if (e != hipSuccess) return e;
+    argmax_keys_kernel<<<1, kKeyThreads, 0, stream>>>(tail.keys, g.n_pad / kPanelRows, tail.token,
+                                                      tail.value);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv_glu(const Geom &g, int act, const uint8_t *packed, const int8_t *xq,

@@ -197,6 +197,20 @@ hipError_t launch_gemv_glu(const Geom &g, int act, const uint8_t *packed, const 
 hipError_t launch_gemv_glu_fused(const Geom &g, int act, const uint8_t *packed, const float *x,
                                  int hadamard, int8_t *xq, float *xs, int32_t *xsum, float *y,
                                  hipStream_t stream);
+// The greedy tail of one activation row: logits = cap * tanh(y / cap) (cap > 0) or y, stored to
+// y; token / value = the smallest index of the largest logit and that logit.  Each GEMV
+// workgroup stores the largest key (logit order, then smaller index) of its 64 rows to
+// keys[panel]; a one-workgroup kernel after it on the stream reduces the n_pad / 64 keys.
+struct Tail {
+    float cap;
+    unsigned long long *keys;
+    int32_t *token;
+    float *value;
+};
+hipError_t launch_gemv_argmax(const Geom &g, const uint8_t *packed, const int8_t *xq,
+                              const float *xs, const int32_t *xsum, float *y, const Tail &tail,
+                              hipStream_t stream);
+
 hipError_t launch_gemm_glu(const Geom &g, int act, const uint8_t *packed, int m,
                            const int8_t *xq, const float *xs, const int32_t *xsum, float *y,
                            hipStream_t stream);

@@ -21,8 +21,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "no gfx950 device
 
 # Every exported symbol of the C ABI (the header's declarations, in order).
 EXPORTS = ("w4a8_packed_layout", "w4a8_pack_weights", "w4a8_prep", "w4a8_gemv", "w4a8_gemm",
-           "w4a8_linear", "w4a8_linear_glu", "w4a8_gemm_glu", "w4a8_debug_partials",
-           "w4a8_status_string", "w4a8_last_error")
+           "w4a8_linear", "w4a8_linear_glu", "w4a8_gemm_glu", "w4a8_lm_head_argmax",
+           "w4a8_gemv_argmax", "w4a8_debug_partials", "w4a8_status_string", "w4a8_last_error")
 ACT_SILU, ACT_GELU_TANH, ACT_GELU_ERF = 0, 1, 2
 
 
@@ -67,8 +67,12 @@ def load() -> ctypes.CDLL:
     lib.w4a8_linear.argtypes = [LP, P, i32, P, i32, P, P, P, P, P]
     lib.w4a8_linear_glu.argtypes = [LP, P, i32, P, i32, i32, P, P, P, P, P]
     lib.w4a8_gemm_glu.argtypes = [LP, P, i32, P, P, P, i32, P, P]
+    u64 = ctypes.c_uint64
+    lib.w4a8_lm_head_argmax.argtypes = [LP, P, P, i32, ctypes.c_float, P, P, P, P, P, P, P, u64,
+                                        P]
+    lib.w4a8_gemv_argmax.argtypes = [LP, P, P, P, P, ctypes.c_float, P, P, P, P, u64, P]
     lib.w4a8_debug_partials.argtypes = [LP, P, i32, P, P, P, P]
-    for f in EXPORTS[:9]:
+    for f in EXPORTS[:11]:
         getattr(lib, f).restype = ctypes.c_int
     lib.w4a8_status_string.argtypes = [ctypes.c_int]
     lib.w4a8_status_string.restype = ctypes.c_char_p
@@ -254,3 +258,66 @@ def gemm_glu(L: Layout, packed: torch.Tensor, xq: torch.Tensor, xs: torch.Tensor
     _check(load().w4a8_gemm_glu(ctypes.byref(L), _ptr(packed), m, _ptr(q2), _ptr(xs),
                                 _ptr(xsum), act, _ptr(y), _stream(xq.device)), "w4a8_gemm_glu")
     return y[0] if (squeeze and out is None) else y
+
+
+def argmax_work_bytes(n: int) -> int:
+    """Bytes of the greedy tail's work buffer for an n-row head: one 64-bit key per 64 rows."""
+    return (n + 63) // 64 * 8
+
+
+def argmax_work(L: Layout, device) -> torch.Tensor:
+    """A work buffer for lm_head_argmax / gemv_argmax on layout L (contents need no setting)."""
+    return torch.empty(argmax_work_bytes(L.n) // 8, dtype=torch.int64, device=device)
+
+
+def _work_bytes(work: torch.Tensor) -> int:
+    return work.numel() * work.element_size()
+
+
+def lm_head_argmax(L: Layout, packed: torch.Tensor, x: torch.Tensor, softcap: float = 0.0,
+                   hadamard_block: int = 0, out=None, work=None, prep_out=None):
+    """Greedy tail of a vocabulary head (w4a8_lm_head_argmax) for one row x [k]: returns
+    (logits [n], token int32 [1], value fp32 [1]) as device tensors.  out = (logits, token,
+    value) and work (argmax_work) may be given to avoid allocations."""
+    x1 = x.reshape(-1)
+    _dev(x1, torch.float32, "x")
+    if x1.numel() != L.k:
+        raise ValueError(f"x has {x1.numel()} values, the layout k = {L.k}")
+    ng = L.k // L.group
+    if prep_out is None:
+        xq = torch.empty((1, L.k), dtype=torch.int8, device=x.device)
+        xs = torch.empty((ng, 1), dtype=torch.float32, device=x.device)
+        xsum = torch.empty((ng, 1), dtype=torch.int32, device=x.device)
+    else:
+        xq, xs, xsum = prep_out
+    if out is None:
+        out = (torch.empty(L.n, dtype=torch.float32, device=x.device),
+               torch.empty(1, dtype=torch.int32, device=x.device),
+               torch.empty(1, dtype=torch.float32, device=x.device))
+    logits, token, value = out
+    if work is None:
+        work = argmax_work(L, x.device)
+    _check(load().w4a8_lm_head_argmax(ctypes.byref(L), _ptr(packed), _ptr(x1), hadamard_block,
+                                      float(softcap), _ptr(xq), _ptr(xs), _ptr(xsum),
+                                      _ptr(logits), _ptr(token), _ptr(value), _ptr(work),
+                                      _work_bytes(work), _stream(x.device)),
+           "w4a8_lm_head_argmax")
+    return logits, token, value
+
+
+def gemv_argmax(L: Layout, packed: torch.Tensor, xq, xs, xsum, softcap: float = 0.0, out=None,
+                work=None):
+    """The GEMV + greedy tail of lm_head_argmax on prepared activations (w4a8_gemv_argmax).
+    Returns (logits [n], token [1], value [1])."""
+    if out is None:
+        out = (torch.empty(L.n, dtype=torch.float32, device=packed.device),
+               torch.empty(1, dtype=torch.int32, device=packed.device),
+               torch.empty(1, dtype=torch.float32, device=packed.device))
+    logits, token, value = out
+    if work is None:
+        work = argmax_work(L, packed.device)
+    _check(load().w4a8_gemv_argmax(ctypes.byref(L), _ptr(packed), _ptr(xq), _ptr(xs),
+                                   _ptr(xsum), float(softcap), _ptr(logits), _ptr(token),
+                                   _ptr(value), _ptr(work), _work_bytes(work),
+                                   _stream(packed.device)), "w4a8_gemv_argmax")
+    return logits, token, value

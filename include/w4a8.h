@@ -229,6 +229,47 @@ w4a8_status w4a8_gemm_glu(const w4a8_layout *L, const void *packed, int32_t m, c
                           void *stream);
 
 /*
+ * The greedy tail of a vocabulary head for one activation row: its logits, optionally
+ * soft-capped, and the index of their maximum, with the maximum found on the GPU.
+ *   x        fp32 [L->k] (one row, not modified)
+ *   hadamard_block, xq, xs, xsum  as for w4a8_linear with m = 1 (xq, xs, xsum are written)
+ *   softcap  c > 0: logits = c * tanh(y / c); c == 0: logits = y (y as w4a8_gemv computes it)
+ *   logits   fp32 [L->n] (written)
+ *   token    int32 [1]: the smallest index of the largest logit (written)
+ *   value    fp32 [1]: that logit (written)
+ *   work, work_bytes  device scratch of at least W4A8_ARGMAX_WORK_BYTES(L->n) bytes, 8-byte
+ *            aligned: one 64-bit key per 64-row panel (no initial contents are needed; calls
+ *            that overlap on one work buffer race)
+ * Three kernels on the stream: the prepass; the GEMV, which also caps and stores the logits and
+ * stores each panel's largest (logit, smaller index) key to work; a one-workgroup kernel that
+ * reduces the keys into token and value.  A one-scale-per-row head (the orthogonal lm_head) is
+ * packed with that scale repeated over its 128-wide groups (group = 128): the same formula.
+ * W4A8_ERR_ARG: softcap negative or not finite, token / value / work NULL or misaligned,
+ * work_bytes too small.
+ * Source: "cactus-compute/engine PR #750: Metal Support", the commit list (the orthogonal lm_head
+ * with its softcap fused into the GPU argmax / sampling tail) and its file table (GPU-side
+ * sampling and argmax helpers); "cactus PR #697", the lm_head commit (the virtual 128-wide group
+ * view of one scale per row).
+ */
+#define W4A8_ARGMAX_WORK_BYTES(n) ((((uint64_t)(n) + 63u) / 64u) * 8u)
+
+w4a8_status w4a8_lm_head_argmax(const w4a8_layout *L, const void *packed, const float *x,
+                                int32_t hadamard_block, float softcap, int8_t *xq, float *xs,
+                                int32_t *xsum, float *logits, int32_t *token, float *value,
+                                void *work, uint64_t work_bytes, void *stream);
+
+/*
+ * The GEMV and greedy tail of w4a8_lm_head_argmax on activations already quantized by w4a8_prep
+ * (m = 1): the same two kernels, so the same logits, token and value.
+ * Errors as w4a8_gemv and w4a8_lm_head_argmax.
+ * Source: as w4a8_lm_head_argmax.
+ */
+w4a8_status w4a8_gemv_argmax(const w4a8_layout *L, const void *packed, const int8_t *xq,
+                             const float *xs, const int32_t *xsum, float softcap, float *logits,
+                             int32_t *token, float *value, void *work, uint64_t work_bytes,
+                             void *stream);
+
+/*
  * The exact int32 partials D[r][n][g] (definitions above) written by the same kernel code as
  * the GEMV (m == 1) or the GEMM (m > 1), with the fp32 epilogue replaced by a store of D.
  *   xsum  as from w4a8_prep (the AFFINE partial is recovered from the u - 8 codes as

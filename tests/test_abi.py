@@ -157,7 +157,35 @@ def test_invalid_calls_are_rejected_on_the_host(lib):
     assert lib.w4a8_gemm_glu(LP, p16, 2, p, p, p, silu, p, None) == ERR_ARG
     assert lib.w4a8_gemm_glu(ctypes.byref(big), p, 2, p, p, p, silu, p, None) == ERR_UNSUPPORTED
     assert lib.w4a8_gemm_glu(LP, p, 0, None, None, None, silu, None, None) == 0
-
+    # lm_head_argmax: softcap negative / not finite, missing token / value / work, misaligned
+    # or too small work (n = 128: two 64-row panels, 16 bytes), bad rotation block
+    f = ctypes.c_float
+    wb = w4a8.argmax_work_bytes(L.n)
+    assert wb == 16
+    assert lib.w4a8_lm_head_argmax(LP, p, p, 0, f(-1.0), p, p, p, p, p, p, p, wb, None) == ERR_ARG
+    assert lib.w4a8_lm_head_argmax(LP, p, p, 0, f(float("inf")), p, p, p, p, p, p, p, wb,
+                                   None) == ERR_ARG
+    assert lib.w4a8_lm_head_argmax(LP, p, p, 0, f(0.0), p, p, p, p, None, p, p, wb,
+                                   None) == ERR_ARG
+    assert lib.w4a8_lm_head_argmax(LP, p, p, 0, f(0.0), p, p, p, p, p, None, p, wb,
+                                   None) == ERR_ARG
+    assert lib.w4a8_lm_head_argmax(LP, p, p, 0, f(0.0), p, p, p, p, p, p, None, wb,
+                                   None) == ERR_ARG
+    assert lib.w4a8_lm_head_argmax(LP, p, p, 0, f(0.0), p, p, p, p, p, p, _fake((1 << 20) + 4),
+                                   wb, None) == ERR_ARG
+    assert lib.w4a8_lm_head_argmax(LP, p, p, 0, f(0.0), p, p, p, p, p, p, p, wb - 8,
+                                   None) == ERR_ARG
+    assert "work has 8 bytes" in lib.w4a8_last_error().decode()
+    assert lib.w4a8_lm_head_argmax(LP, p, p, 64, f(0.0), p, p, p, p, p, p, p, wb, None) == ERR_ARG
+    assert lib.w4a8_lm_head_argmax(LP, p, None, 0, f(30.0), p, p, p, p, p, p, p, wb,
+                                   None) == ERR_ARG
+    assert lib.w4a8_gemv_argmax(LP, p, p, p, p, f(-0.5), p, p, p, p, wb, None) == ERR_ARG
+    assert lib.w4a8_gemv_argmax(LP, p, p, p, p, f(float("nan")), p, p, p, p, wb, None) == ERR_ARG
+    assert lib.w4a8_gemv_argmax(LP, p, p, p, p, f(0.0), p, p, p, None, wb, None) == ERR_ARG
+    assert lib.w4a8_gemv_argmax(LP, p, p, p, p, f(0.0), p, p, p, p, 0, None) == ERR_ARG
+    assert lib.w4a8_gemv_argmax(LP, p, None, p, p, f(0.0), p, p, p, p, wb, None) == ERR_ARG
+    assert lib.w4a8_gemv_argmax(LP, p, p, p, p, f(0.0), None, p, p, p, wb, None) == ERR_ARG
+    assert lib.w4a8_gemv_argmax(LP, p1, p, p, p, f(0.0), p, p, p, p, wb, None) == ERR_ARG
 
 @pytest.mark.skipif(_gpu_visible(), reason="checks the no-device path; would launch on a GPU")
 def test_valid_calls_without_a_device_report_device_error(lib):
@@ -168,6 +196,10 @@ def test_valid_calls_without_a_device_report_device_error(lib):
     assert lib.w4a8_linear(ctypes.byref(L), p, 1, p, 0, p, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_linear_glu(ctypes.byref(L), p, 2, p, 0, w4a8.ACT_GELU_TANH, p, p, p, p,
                                None) == ERR_DEVICE
+    assert lib.w4a8_lm_head_argmax(ctypes.byref(L), p, p, 0, ctypes.c_float(30.0), p, p, p, p,
+                                   p, p, p, 16, None) == ERR_DEVICE
+    assert lib.w4a8_gemv_argmax(ctypes.byref(L), p, p, p, p, ctypes.c_float(0.0), p, p, p, p,
+                                16, None) == ERR_DEVICE
     assert lib.w4a8_last_error().decode() != ""
 
 
