@@ -59,7 +59,7 @@ KERNEL_SOURCES = {
     "gemm": ["gemm.hip", "w4a8_kernels.h"],
 }
 TRAFFIC = {
-    "C2a": dict(kernel="gemv", source_sha="20ae573f3297e6ca", fetch_kib=8767.28, write_kib=66.25,
+    "C2a": dict(kernel="gemv", source_sha="390ee810759e881f", fetch_kib=8767.26, write_kib=66.25,
                 fetch_factor=1.99979, write_factor=1.0),
 }
 
@@ -87,7 +87,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="C2a",
-                    help="workload (C1, C2a, C2b, C3a, C3b, C4, C5a, C5b); default C2a")
+                    help="workload (C1, C2a, C2b, C3a, C3b, C4, C5a, C5b, C5o); default C2a")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--glu", choices=["silu", "gelu_tanh", "gelu_erf"], default=None,
@@ -122,6 +122,8 @@ def workload_name(cfg, glu=None, cap=None):
     from bit_group_quantized_act_amd import synth
     kind = "decode GEMV" if cfg.m == 1 else "prefill GEMM"
     rot = ", 128-block WHT" if cfg.hadamard else ""
+    if cfg.extra.get("row_scale"):
+        rot += f", one scale per row seen as K/{cfg.group} groups"
     fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072
     how = ("prepass fused into the GEMV" if fused and cap is None else
            "prepass + GEMV" if cfg.m == 1 else "prepass + GEMM")
@@ -157,8 +159,13 @@ def main():
     layer = synth.make(args.config)
     cfg = layer["cfg"]
     t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    lay, packed0 = w4a8.pack(t(layer["codes"]), t(layer["scales"]), cfg.fmt, cfg.group,
-                             bias=t(layer["bias"]), codebook=t(layer["codebook"]))
+    if "row_scales" in layer:      # one scale per row, packed through the row-scale view
+        lay, packed0 = w4a8.pack_row_scale(t(layer["codes"]), t(layer["row_scales"]), cfg.fmt,
+                                           cfg.group, row_bias=t(layer["row_bias"]),
+                                           codebook=t(layer["codebook"]))
+    else:
+        lay, packed0 = w4a8.pack(t(layer["codes"]), t(layer["scales"]), cfg.fmt, cfg.group,
+                                 bias=t(layer["bias"]), codebook=t(layer["codebook"]))
     wbytes = synth.weight_bytes(cfg)
     fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072   # w4a8_linear's one-kernel case
     cap = args.argmax

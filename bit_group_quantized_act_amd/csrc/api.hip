@@ -196,9 +196,10 @@ w4a8_status w4a8_packed_layout(int32_t format, int32_t n, int32_t k, int32_t gro
     return ok();
 }
 
-w4a8_status w4a8_pack_weights(const w4a8_layout *L, const uint8_t *codes,
-                              const uint16_t *scales_f16, const uint16_t *bias_f16,
-                              const int8_t *codebook, void *packed, void *stream) {
+namespace {
+w4a8_status pack_checked(const w4a8_layout *L, const uint8_t *codes, const uint16_t *scales_f16,
+                         const uint16_t *bias_f16, const int8_t *codebook, void *packed,
+                         void *stream, bool row_scale) {
     w4a8_status s = check_layout(L);
     if (s != W4A8_OK) return s;
     W4A8_REQUIRE_PTR(codes);
@@ -218,8 +219,22 @@ w4a8_status w4a8_pack_weights(const w4a8_layout *L, const uint8_t *codes,
     if ((s = check_device()) != W4A8_OK) return s;
     return launched(w4a8::launch_pack(geom_of(L), codes, scales_f16, bias_f16, codebook,
                                       static_cast<uint8_t *>(packed),
-                                      static_cast<hipStream_t>(stream)),
+                                      static_cast<hipStream_t>(stream), row_scale),
                     "pack launch");
+}
+}  // namespace
+
+w4a8_status w4a8_pack_weights(const w4a8_layout *L, const uint8_t *codes,
+                              const uint16_t *scales_f16, const uint16_t *bias_f16,
+                              const int8_t *codebook, void *packed, void *stream) {
+    return pack_checked(L, codes, scales_f16, bias_f16, codebook, packed, stream, false);
+}
+
+w4a8_status w4a8_pack_weights_row_scale(const w4a8_layout *L, const uint8_t *codes,
+                                        const uint16_t *row_scales_f16,
+                                        const uint16_t *row_bias_f16, const int8_t *codebook,
+                                        void *packed, void *stream) {
+    return pack_checked(L, codes, row_scales_f16, row_bias_f16, codebook, packed, stream, true);
 }
 
 w4a8_status w4a8_prep(const float *x, int32_t m, int32_t k, int32_t group,

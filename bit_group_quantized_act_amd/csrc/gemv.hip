@@ -55,20 +55,6 @@ __device__ __forceinline__ int dot_chunk(v4i v, const int *__restrict__ xc, uint
     return acc;
 }
 
-// The greedy tail's key of a logit v at row r: the logit's order in the high half (sign bit
-// flipped for v >= 0, all bits for v < 0: unsigned order = float order), ~r in the low half (on
-// equal logits the smaller row wins).  The largest key over a wavefront's lanes:
-__device__ inline unsigned long long wave_max_key(unsigned long long key) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), o, 64);
-        const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key >> 32), o, 64);
-        const unsigned long long other = (static_cast<unsigned long long>(hi) << 32) | lo;
-        key = other > key ? other : key;
-    }
-    return key;
-}
-
 // FUSED: x is the fp32 activation row; xq/xs/xsum are outputs written by workgroup 0.
 // Otherwise xq/xs/xsum are the prepass outputs (inputs here) and x is unused.
 // XQ (fused only): activation quads per lane, enough for the wavefront's groups.
@@ -404,27 +390,6 @@ hipError_t launch_argmax_w(const Geom &g, const uint8_t *packed, const int8_t *x
                                                                     u, y, nullptr, stream, tail);
 }
 
-// The last step of the greedy tail: the largest of the GEMV workgroups' keys (1024 lanes, each
-// over a strided slice; then wavefronts, then the 16 wavefront results in one lane), decoded into
-// the token (its row) and the value (its logit).
-constexpr int kKeyThreads = 1024;
-__global__ __launch_bounds__(kKeyThreads) void argmax_keys_kernel(
-        const unsigned long long *__restrict__ keys, int nkeys, int32_t *__restrict__ token,
-        float *__restrict__ value) {
-    __shared__ unsigned long long wave_key[kKeyThreads / 64];
-    unsigned long long key = 0ull;
-    for (int i = threadIdx.x; i < nkeys; i += kKeyThreads) key = keys[i] > key ? keys[i] : key;
-    key = wave_max_key(key);
-    if ((threadIdx.x & 63) == 0) wave_key[threadIdx.x >> 6] = key;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int w = 1; w < kKeyThreads / 64; ++w) key = wave_key[w] > key ? wave_key[w] : key;
-        const uint32_t u = static_cast<uint32_t>(key >> 32);
-        *token = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
-        *value = __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-    }
-}
-
 template <int FMT>
 hipError_t launch_argmax_g(const Geom &g, const uint8_t *packed, const int8_t *xq,
                            const float *xs, const int32_t *xsum, float *y, const Tail &tail,
@@ -446,9 +411,7 @@ hipError_t launch_gemv_argmax(const Geom &g, const uint8_t *packed, const int8_t
     default: e = launch_argmax_g<kFmtCodebook>(g, packed, xq, xs, xsum, y, tail, stream); break;
     }
     if (e != hipSuccess) return e;
-    argmax_keys_kernel<<<1, kKeyThreads, 0, stream>>>(tail.keys, g.n_pad / kPanelRows, tail.token,
-                                                      tail.value);
-    return hipGetLastError();
+    return launch_argmax_keys(tail.keys, g.n_pad / kPanelRows, tail.token, tail.value, stream);
 }
 
 hipError_t launch_gemv_glu(const Geom &g, int act, const uint8_t *packed, const int8_t *xq,

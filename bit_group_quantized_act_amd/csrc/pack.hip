@@ -48,9 +48,12 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t *__restri
 
 // Metadata in blocks of 4 groups: per panel, per block j, per panel row, the entries of groups
 // 4j .. 4j+3 (zero past the last group), so one 8- or 16-byte load gives a row four groups.
+// The scale (and bias) of (row, group g) is scales[row * row_stride + g * group_stride]: (ng, 1)
+// for one value per group, (1, 0) for one value per row seen as every group's.
 __global__ __launch_bounds__(256) void pack_meta_kernel(const uint16_t *__restrict__ scales,
                                                         const uint16_t *__restrict__ bias,
-                                                        int n, int ng, int64_t total,
+                                                        int n, int ng, int row_stride,
+                                                        int group_stride, int64_t total,
                                                         uint8_t *__restrict__ out) {
     const int nblk = (ng + 3) / 4;
     for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
@@ -63,9 +66,10 @@ __global__ __launch_bounds__(256) void pack_meta_kernel(const uint16_t *__restri
         const int64_t row = p * kPanelRows + r;
         const int g = 4 * j + i;
         const bool valid = row < n && g < ng;
-        const uint32_t s = valid ? scales[row * ng + g] : 0u;
+        const int64_t src = row * row_stride + static_cast<int64_t>(g) * group_stride;
+        const uint32_t s = valid ? scales[src] : 0u;
         if (bias) {
-            const uint32_t b = valid ? bias[row * ng + g] : 0u;
+            const uint32_t b = valid ? bias[src] : 0u;
             reinterpret_cast<uint32_t *>(out)[t] = s | (b << 16);
         } else {
             reinterpret_cast<uint16_t *>(out)[t] = static_cast<uint16_t>(s);
@@ -90,7 +94,7 @@ unsigned grid_for(int64_t total) {
 
 hipError_t launch_pack(const Geom &g, const uint8_t *codes, const uint16_t *scales,
                        const uint16_t *bias, const int8_t *codebook, uint8_t *packed,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool row_scale) {
     const int64_t chunks = (int64_t)g.n_pad * (g.k / kChunkK);
     pack_codes_kernel<<<grid_for(chunks), 256, 0, stream>>>(
         codes, g.n, g.k, g.fmt, chunks, reinterpret_cast<uint4 *>(packed + g.off_codes));
@@ -99,7 +103,8 @@ hipError_t launch_pack(const Geom &g, const uint8_t *codes, const uint16_t *scal
     const int ng = g.k / g.group;
     const int64_t metas = (int64_t)g.n_pad * ((ng + 3) / 4) * 4;
     pack_meta_kernel<<<grid_for(metas), 256, 0, stream>>>(
-        scales, g.fmt == kFmtAffine ? bias : nullptr, g.n, ng, metas, packed + g.off_meta);
+        scales, g.fmt == kFmtAffine ? bias : nullptr, g.n, ng, row_scale ? 1 : ng,
+        row_scale ? 0 : 1, metas, packed + g.off_meta);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (g.fmt == kFmtCodebook) {

@@ -167,7 +167,7 @@ __device__ __forceinline__ float act_apply(int act, float v) {
 
 hipError_t launch_pack(const Geom &g, const uint8_t *codes, const uint16_t *scales,
                        const uint16_t *bias, const int8_t *codebook, uint8_t *packed,
-                       hipStream_t stream);
+                       hipStream_t stream, bool row_scale = false);
 
 hipError_t launch_prep(const float *x, int64_t m, int k, int group, int hadamard,
                        int8_t *xq, float *xs, int32_t *xsum, hipStream_t stream);
@@ -210,6 +210,23 @@ struct Tail {
 hipError_t launch_gemv_argmax(const Geom &g, const uint8_t *packed, const int8_t *xq,
                               const float *xs, const int32_t *xsum, float *y, const Tail &tail,
                               hipStream_t stream);
+// The reduction of nkeys panel keys into token and value (one workgroup).
+hipError_t launch_argmax_keys(const unsigned long long *keys, int nkeys, int32_t *token,
+                              float *value, hipStream_t stream);
+
+// The greedy tail's key of a logit v at row r: the logit's order in the high half (sign bit
+// flipped for v >= 0, all bits for v < 0: unsigned order = float order), ~r in the low half (on
+// equal logits the smaller row wins).  The largest key over a wavefront's lanes:
+__device__ inline unsigned long long wave_max_key(unsigned long long key) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), o, 64);
+        const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key >> 32), o, 64);
+        const unsigned long long other = (static_cast<unsigned long long>(hi) << 32) | lo;
+        key = other > key ? other : key;
+    }
+    return key;
+}
 
 hipError_t launch_gemm_glu(const Geom &g, int act, const uint8_t *packed, int m,
                            const int8_t *xq, const float *xs, const int32_t *xsum, float *y,

@@ -71,6 +71,9 @@ CONFIGS = {
                        "vocabulary head, decode GEMV"),
     "C5b": LayerConfig("C5b", 64, 1536, 262144, 64, FMT_SYM, 0, 15, 15.0, 0.02, 5, 1, 0,
                        "vocabulary head, chunked prefill"),
+    "C5o": LayerConfig("C5o", 1, 1536, 262144, 128, FMT_CODEBOOK, 128, 15, 15.0, 0.0, 6, 0, 0,
+                       "orthogonal vocabulary head: rotated codebook weights, one scale per "
+                       "row seen as K/128 groups", extra={"row_scale": True}),
 }
 
 
@@ -143,9 +146,10 @@ def make_weights(cfg: LayerConfig, full_range: bool = False):
         cb = np.clip(np.rint(40.0 * rng(cfg.cfg_id, cfg.w_variant, 3).standard_normal((n, 16))),
                      -127, 127).astype(np.int8)
         idx = rng(cfg.cfg_id, cfg.w_variant, 4).integers(0, 16, size=(n, k), dtype=np.uint8)
-        sc = (rng(cfg.cfg_id, cfg.w_variant, 5).uniform(0.5, 1.5, size=(n, ng))
+        cols = 1 if cfg.extra.get("row_scale") else ng
+        sc = (rng(cfg.cfg_id, cfg.w_variant, 5).uniform(0.5, 1.5, size=(n, cols))
               * 5e-4).astype(np.float16)
-        return pack_nibbles(idx), sc, None, cb
+        return pack_nibbles(idx), np.repeat(sc, ng // cols, axis=1), None, cb
     r = rng(cfg.cfg_id, cfg.w_variant, 2)
     if full_range:
         c = r.integers(0, 16, size=(n, k), dtype=np.uint8)
@@ -175,14 +179,20 @@ def make(name_or_cfg, full_range: bool = False, **overrides):
     cfg = name_or_cfg if isinstance(name_or_cfg, LayerConfig) else config(name_or_cfg,
                                                                           **overrides)
     codes, scales, bias, cb = make_weights(cfg, full_range=full_range)
-    return dict(cfg=cfg, x=make_x(cfg), codes=codes, scales=scales, bias=bias, codebook=cb)
+    out = dict(cfg=cfg, x=make_x(cfg), codes=codes, scales=scales, bias=bias, codebook=cb)
+    if cfg.extra.get("row_scale"):      # the per-row values (every group of a row holds them)
+        out["row_scales"] = np.ascontiguousarray(scales[:, 0])
+        out["row_bias"] = None if bias is None else np.ascontiguousarray(bias[:, 0])
+    return out
 
 
 def weight_bytes(cfg: LayerConfig) -> int:
-    """Algorithmic weight bytes: nibbles + fp16 scales (+ fp16 bias) (+ int8 codebook)."""
-    b = cfg.n * cfg.k // 2 + 2 * cfg.n * (cfg.k // cfg.group)
+    """Algorithmic weight bytes: nibbles + fp16 scales (+ fp16 bias) (+ int8 codebook); one
+    scale (and bias) per row for a row-scaled head."""
+    per_row = 1 if cfg.extra.get("row_scale") else cfg.k // cfg.group
+    b = cfg.n * cfg.k // 2 + 2 * cfg.n * per_row
     if cfg.fmt == FMT_AFFINE:
-        b += 2 * cfg.n * (cfg.k // cfg.group)
+        b += 2 * cfg.n * per_row
     if cfg.fmt == FMT_CODEBOOK:
         b += 16 * cfg.n
     return b

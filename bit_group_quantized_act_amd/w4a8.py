@@ -20,7 +20,8 @@ PANEL_ROWS = 64
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "no gfx950 device", 4: "HIP error"}
 
 # Every exported symbol of the C ABI (the header's declarations, in order).
-EXPORTS = ("w4a8_packed_layout", "w4a8_pack_weights", "w4a8_prep", "w4a8_gemv", "w4a8_gemm",
+EXPORTS = ("w4a8_packed_layout", "w4a8_pack_weights", "w4a8_pack_weights_row_scale",
+           "w4a8_prep", "w4a8_gemv", "w4a8_gemm",
            "w4a8_linear", "w4a8_linear_glu", "w4a8_gemm_glu", "w4a8_lm_head_argmax",
            "w4a8_gemv_argmax", "w4a8_debug_partials", "w4a8_status_string", "w4a8_last_error")
 ACT_SILU, ACT_GELU_TANH, ACT_GELU_ERF = 0, 1, 2
@@ -61,6 +62,7 @@ def load() -> ctypes.CDLL:
     LP = ctypes.POINTER(Layout)
     lib.w4a8_packed_layout.argtypes = [i32, i32, i32, i32, LP]
     lib.w4a8_pack_weights.argtypes = [LP, P, P, P, P, P, P]
+    lib.w4a8_pack_weights_row_scale.argtypes = [LP, P, P, P, P, P, P]
     lib.w4a8_prep.argtypes = [P, i32, i32, i32, i32, P, P, P, P]
     lib.w4a8_gemv.argtypes = [LP, P, P, P, P, P, P]
     lib.w4a8_gemm.argtypes = [LP, P, i32, P, P, P, P, P]
@@ -72,7 +74,7 @@ def load() -> ctypes.CDLL:
                                         P]
     lib.w4a8_gemv_argmax.argtypes = [LP, P, P, P, P, ctypes.c_float, P, P, P, P, u64, P]
     lib.w4a8_debug_partials.argtypes = [LP, P, i32, P, P, P, P]
-    for f in EXPORTS[:11]:
+    for f in EXPORTS[:12]:
         getattr(lib, f).restype = ctypes.c_int
     lib.w4a8_status_string.argtypes = [ctypes.c_int]
     lib.w4a8_status_string.restype = ctypes.c_char_p
@@ -135,6 +137,28 @@ def pack(codes: torch.Tensor, scales: torch.Tensor, fmt: int, group: int, bias=N
     _check(load().w4a8_pack_weights(ctypes.byref(L), _ptr(codes), _ptr(scales), _ptr(bias),
                                     _ptr(codebook), _ptr(out), _stream(codes.device)),
            "w4a8_pack_weights")
+    return L, out
+
+
+def pack_row_scale(codes: torch.Tensor, row_scales: torch.Tensor, fmt: int, group: int,
+                   row_bias=None, codebook=None, out: torch.Tensor | None = None):
+    """Repack weights with one scale (affine: and one bias) per output row, float16 [n], seen as
+    the scale of each of the row's k/group groups (w4a8_pack_weights_row_scale)."""
+    n, kh = codes.shape
+    L = packed_layout(fmt, n, 2 * kh, group)
+    _dev(codes, torch.uint8, "codes")
+    _dev(row_scales, torch.float16, "row_scales", (n,))
+    if row_bias is not None:
+        _dev(row_bias, torch.float16, "row_bias", (n,))
+    if codebook is not None:
+        _dev(codebook, torch.int8, "codebook", (n, 16))
+    if out is None:
+        out = torch.empty(L.bytes, dtype=torch.uint8, device=codes.device)
+    _dev(out, torch.uint8, "packed", (L.bytes,))
+    _check(load().w4a8_pack_weights_row_scale(ctypes.byref(L), _ptr(codes), _ptr(row_scales),
+                                              _ptr(row_bias), _ptr(codebook), _ptr(out),
+                                              _stream(codes.device)),
+           "w4a8_pack_weights_row_scale")
     return L, out
 
 

@@ -128,6 +128,23 @@ w4a8_status w4a8_pack_weights(const w4a8_layout *L, const uint8_t *codes,
                               const int8_t *codebook, void *packed, void *stream);
 
 /*
+ * w4a8_pack_weights for weights with one scale (and, AFFINE, one bias) per output row: the row's
+ * value is seen as the scale of each of its K / L->group groups, so every kernel computes
+ *   y[r][n] = s[n] * sum_g xs[r][g] * D[r][n][g]   (+ b[n] * sum_g xs[r][g] * xsum[r][g], AFFINE)
+ * and the packed buffer is the one w4a8_pack_weights writes from scales repeated over the groups.
+ *   row_scales_f16  uint16 [n] (IEEE binary16 bit patterns)
+ *   row_bias_f16    uint16 [n] for AFFINE, else must be NULL
+ *   codes, codebook, packed, errors: as w4a8_pack_weights
+ * Source: "cactus PR #697", the lm_head commit (the orthogonal lm_head keeps one scale per row and
+ * views it as K/128 groups of 128, which is exact because a group's partial is an integer and its
+ * weight scale a constant of the row).
+ */
+w4a8_status w4a8_pack_weights_row_scale(const w4a8_layout *L, const uint8_t *codes,
+                                        const uint16_t *row_scales_f16,
+                                        const uint16_t *row_bias_f16, const int8_t *codebook,
+                                        void *packed, void *stream);
+
+/*
  * The activation prepass: optional rotation, then per-row per-group int8 quantization and
  * group sums (definitions above).
  *   x       fp32 [m][k] row-major (not modified)

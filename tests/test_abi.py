@@ -102,6 +102,12 @@ def test_invalid_calls_are_rejected_on_the_host(lib):
     assert lib.w4a8_pack_weights(ctypes.byref(bad), p, p, p, None, p, None) == ERR_ARG
     assert "w4a8_packed_layout" in lib.w4a8_last_error().decode()
     assert lib.w4a8_pack_weights(None, p, p, p, None, p, None) == ERR_ARG
+    # the row-scale view: the same checks
+    assert lib.w4a8_pack_weights_row_scale(LP, p, p, None, None, p, None) == ERR_ARG
+    assert lib.w4a8_pack_weights_row_scale(LP, p, p, p, None, p16, None) == ERR_ARG
+    assert lib.w4a8_pack_weights_row_scale(LP, p, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_pack_weights_row_scale(LP, p, None, p, None, p, None) == ERR_ARG
+    assert lib.w4a8_pack_weights_row_scale(None, p, p, p, None, p, None) == ERR_ARG
     # prep: m < 0, k % group, hadamard block, k % 128 with rotation, null and misaligned
     assert lib.w4a8_prep(p, -1, 256, 64, 0, p, p, p, None) == ERR_ARG
     assert lib.w4a8_prep(p, 2, 200, 64, 0, p, p, p, None) == ERR_ARG
@@ -192,6 +198,8 @@ def test_valid_calls_without_a_device_report_device_error(lib):
     L = w4a8.packed_layout(w4a8.SYM, 128, 256, 64)
     p = _fake(1 << 20)
     assert lib.w4a8_gemv(ctypes.byref(L), p, p, p, p, p, None) == ERR_DEVICE
+    assert lib.w4a8_pack_weights_row_scale(ctypes.byref(L), p, p, None, None, p,
+                                           None) == ERR_DEVICE
     assert lib.w4a8_prep(p, 2, 256, 64, 0, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_linear(ctypes.byref(L), p, 1, p, 0, p, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_linear_glu(ctypes.byref(L), p, 2, p, 0, w4a8.ACT_GELU_TANH, p, p, p, p,

@@ -269,3 +269,77 @@ def test_gemv_argmax_on_prepared_activations_same_bits():
         assert np.array_equal(_bits(lg.cpu().numpy()), _bits(lg_ref)), f"call {i}: logits"
         assert int(tk.cpu()[0]) == tk_ref, f"call {i}: token"
         assert _bits(vl.cpu().numpy()[0]) == _bits(vl_ref), f"call {i}: value"
+
+
+def _row_scaled(L):
+    """L with one scale (and bias) per row: the first group's, written into every group."""
+    ng = L["scales"].shape[1]
+    L = dict(L)
+    L["row_scales"] = np.ascontiguousarray(L["scales"][:, 0])
+    L["scales"] = np.repeat(L["row_scales"][:, None], ng, axis=1)
+    L["row_bias"] = None
+    if L["bias"] is not None:
+        L["row_bias"] = np.ascontiguousarray(L["bias"][:, 0])
+        L["bias"] = np.repeat(L["row_bias"][:, None], ng, axis=1)
+    return L
+
+
+@pytest.mark.parametrize("name,over", [("C5o", dict(n=640)), ("C5a", dict(n=1000)),
+                                       ("C3a", dict(m=1, n=320, k=640))],
+                         ids=["codebook-g128", "sym-g64-ragged", "affine-g64"])
+def test_row_scale_packing_is_the_replicated_layout(name, over):
+    # the row-scale view writes the same packed bytes as w4a8_pack_weights given the row's value
+    # in every group (so every kernel computes the view's formula)
+    w = _w4a8()
+    L = synth.make(name, full_range=True, **over)
+    if "row_scales" not in L:
+        L = _row_scaled(L)
+    cfg = L["cfg"]
+    _, ref = _pack(L)
+    _, got = w.pack_row_scale(to_dev(L["codes"]), to_dev(L["row_scales"]), cfg.fmt, cfg.group,
+                              row_bias=to_dev(L["row_bias"]), codebook=to_dev(L["codebook"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref.cpu().numpy())
+
+
+def _run_row_scaled(L, cap):
+    w = _w4a8()
+    cfg = L["cfg"]
+    lay, packed = w.pack_row_scale(to_dev(L["codes"]), to_dev(L["row_scales"]), cfg.fmt,
+                                   cfg.group, row_bias=to_dev(L["row_bias"]),
+                                   codebook=to_dev(L["codebook"]))
+    logits, token, value = w.lm_head_argmax(lay, packed, to_dev(L["x"].reshape(-1)), cap,
+                                            cfg.hadamard)
+    torch.cuda.synchronize()
+    return dict(logits=logits.cpu().numpy(), token=int(token.cpu().numpy()[0]),
+                value=value.cpu().numpy()[0])
+
+
+@pytest.mark.parametrize("n,cap", [(4000, 30.0), (4096, 0.0)], ids=["ragged-cap30", "cap0"])
+def test_orthogonal_head_greedy_tail(n, cap):
+    # the orthogonal head: rotated activations, codebook weights, one scale per row seen as
+    # K/128 groups, packed by the row-scale view; the oracle takes the scale in every group
+    L = synth.make("C5o", n=n, full_range=True)
+    got = _run_row_scaled(L, cap)
+    ref = _oracle(L, cap)
+    check_logits(got["logits"], ref, f"orthogonal n {n}")
+    check_token(got, ref, f"orthogonal n {n}")
+
+
+def test_orthogonal_head_full_vocabulary(layer_cache):
+    """The 262144-entry orthogonal head (k 1536, rotation, codebook, one scale per row): the token
+    against all the GPU's logits, the logits against the oracle on a sample and the top 64."""
+    if "C5o" not in layer_cache:
+        layer_cache["C5o"] = synth.make("C5o")
+    L = layer_cache["C5o"]
+    cfg = L["cfg"]
+    print(f"orthogonal head full: n={cfg.n} k={cfg.k}", flush=True)
+    got = _run_row_scaled(L, 30.0)
+    lg = got["logits"]
+    t = got["token"]
+    assert t == int(np.argmax(lg)) and _bits(got["value"]) == _bits(lg[t])
+    top = np.argsort(-lg.astype(np.float64), kind="stable")[:64]
+    rows = np.unique(np.concatenate([np.random.default_rng(19).choice(cfg.n, 2048,
+                                                                      replace=False), top,
+                                     [cfg.n - 1]]))
+    check_logits(lg[rows], _oracle(L, 30.0, rows=rows), "orthogonal full vocabulary")
