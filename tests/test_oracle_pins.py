@@ -484,6 +484,28 @@ def test_softcap_matches_library_tanh_and_bounds():
     assert np.array_equal(logits, y)
 
 
+def test_softcap_closed_forms_symmetry_and_small_argument_limit():
+    # y = c * atanh(t) = (c/2) ln((1+t)/(1-t)) gives c * t exactly (tanh of a logarithm is a
+    # rational function: (e^2u - 1)/(e^2u + 1) = t), independent of any tanh routine
+    t = np.array([0.0, 0.1, 0.25, 0.5, 0.6, 0.75, 0.9, 0.99, -0.5, -0.9])
+    for cap in (30.0, 2.5):
+        y = (cap / 2.0) * np.log((1.0 + t) / (1.0 - t))
+        logits, _, _ = oracle.softcap_argmax(y[None, :], cap)
+        np.testing.assert_allclose(logits[0], cap * t, rtol=1e-14, atol=1e-14)
+        # odd: capping -y gives -logits
+        yy = np.random.default_rng(7).standard_normal(200) * 3 * cap
+        a, _, _ = oracle.softcap_argmax(yy, cap)
+        b, _, _ = oracle.softcap_argmax(-yy, cap)
+        assert np.array_equal(a, -b)
+        # small arguments: c tanh(y/c) = y - y^3 / (3 c^2) + O(y^5 / c^4)
+        ys = np.array([1e-3, -2e-3, 5e-3]) * cap
+        ls, _, _ = oracle.softcap_argmax(ys, cap)
+        np.testing.assert_allclose(ls, ys - ys ** 3 / (3 * cap ** 2), rtol=1e-9)
+    # controls: readings that misplace the cap fail the closed form
+    y = 15.0 * np.log(3.0)                          # c = 30, t = 0.5 -> logit 15
+    assert abs(np.tanh(y) - 15.0) > 1 and abs(30.0 * np.tanh(y) - 15.0) > 1
+
+
 def test_argmax_first_index_on_ties_and_softcap_keeps_the_order():
     rng = np.random.default_rng(6)
     y = rng.standard_normal((5, 300))
