@@ -57,8 +57,13 @@ def _load():
     lib.oracle_linear.argtypes = [i32, P, P, P, P, i64, i64, i32, P, P, P, i64, P, P]
     lib.oracle_glu.argtypes = [i32, P, P, i64, i64, P, P]
     lib.oracle_softcap_argmax.argtypes = [P, i64, i64, ctypes.c_double, P, P, P]
+    lib.oracle_float_to_half.argtypes = [ctypes.c_float]
+    lib.oracle_float_to_half.restype = ctypes.c_uint16
+    lib.oracle_prep_a16.argtypes = [P, i64, i64, P, P]
+    lib.oracle_linear_a16.argtypes = [i32, P, P, P, P, i64, i64, i32, P, P, i64, P, P]
     for f in ("oracle_rotate", "oracle_quantize", "oracle_prep", "oracle_partials",
-              "oracle_linear", "oracle_glu", "oracle_softcap_argmax", "oracle_num_threads"):
+              "oracle_linear", "oracle_glu", "oracle_softcap_argmax", "oracle_prep_a16",
+              "oracle_linear_a16", "oracle_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -197,3 +202,46 @@ def softcap_argmax(y: np.ndarray, cap: float = 0.0):
     _check(_load().oracle_softcap_argmax(_ptr(y), m, n, float(cap), _ptr(logits), _ptr(token),
                                          _ptr(value)), "softcap_argmax")
     return (logits[0], int(token[0]), float(value[0])) if one else (logits, token, value)
+
+
+def float_to_half(x) -> np.ndarray:
+    """binary16 bit patterns (uint16) nearest to each fp32 value, ties to even (one call per
+    value: meant for pins and small cases)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    f = _load().oracle_float_to_half
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint16).reshape(x.shape)
+
+
+def prep_a16(x):
+    """fp16-activation prepass of x float32 [m, k] (k % 64 == 0): (xh uint16 binary16 bits
+    [m, k] in natural order, S float32 [m, k/64] group sums by the fixed tree)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    m, k = x.shape
+    xh = np.empty((m, k), np.uint16)
+    xsf = np.empty((m, k // 64), np.float32)
+    _check(_load().oracle_prep_a16(_ptr(x), m, k, _ptr(xh), _ptr(xsf)), "prep_a16")
+    return xh, xsf
+
+
+def linear_a16(fmt: int, codes, scales_f16, xh, xsf, group: int = 64, bias_f16=None,
+               codebook=None, with_terms: bool = True):
+    """fp64 output y [m, n] of the fp16-activation linear (and its term magnitude T)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales_f16, dtype=np.float16).view(np.uint16)
+    bias = None if bias_f16 is None else \
+        np.ascontiguousarray(bias_f16, dtype=np.float16).view(np.uint16)
+    cb = None if codebook is None else np.ascontiguousarray(codebook, dtype=np.int8)
+    xh = np.ascontiguousarray(xh, dtype=np.uint16)
+    xsf = np.ascontiguousarray(xsf, dtype=np.float32)
+    if xh.ndim == 1:
+        xh, xsf = xh[None, :], xsf[None, :]
+    n = codes.shape[0]
+    m, k = xh.shape
+    y = np.empty((m, n), np.float64)
+    t = np.empty((m, n), np.float64) if with_terms else None
+    _check(_load().oracle_linear_a16(fmt, _ptr(codes), _ptr(scales), _ptr(bias), _ptr(cb), n, k,
+                                     group, _ptr(xh), _ptr(xsf), m, _ptr(y), _ptr(t)),
+           "linear_a16")
+    return (y, t) if with_terms else y

@@ -45,6 +45,15 @@
  *                silu(v)      = v / (1 + exp(-v))
  *                gelu_tanh(v) = v/2 * (1 + tanh(sqrt(2/pi) * (v + 0.044715 v^3)))
  *                gelu_erf(v)  = v/2 * (1 + erf(v / sqrt(2)))
+ *   fp16 path  "TensorFold PR #3215, simd_qmm on Metal: X's group sums and half operands from a
+ *              prepass", section "What this changes": the prompt tiles multiply 4-bit g64
+ *              weights (dequantized w = scale * u + bias) with X, either in fp32 or as half; a
+ *              prepass writes X as half and each row's 64-wide group sums for the bias term,
+ *              summed by the tiles' fixed tree ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)), each c a
+ *              left-to-right sum of 8 consecutive inputs.  Reading taken here: xh = x rounded to
+ *              the nearest binary16 (ties to even); S[r][g] = that tree over x in fp32 (fma with
+ *              a unit factor is an add); y[r][n] = sum over g of ( sw * sum_k w_int * xh
+ *              + bw * S ) in fp64, w_int the format's integer weight (affine: unsigned u).
  *   lm_head    "cactus-compute/engine PR #750: Metal Support", the commit list (the orthogonal
  *              lm_head with its softcap fused into a GPU argmax / sampling tail) and the file
  *              table (GPU-side sampling and argmax helpers); "cactus PR #697", the lm_head commit
@@ -363,6 +372,126 @@ int oracle_softcap_argmax(const double *y, int64_t m, int64_t n, double cap, dou
         }
         token[r] = best;
         value[r] = logits[r * n + best];
+    }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- fp16 activations ----- */
+
+/* Round a non-negative double q to the nearest integer, ties to the even one. */
+static double oracle_round_half_even(double q)
+{
+    double fl = floor(q);
+    double diff = q - fl;                           /* exact for the q used here */
+    if (diff > 0.5)
+        return fl + 1.0;
+    if (diff < 0.5)
+        return fl;
+    return fmod(fl, 2.0) == 0.0 ? fl : fl + 1.0;
+}
+
+/*
+ * IEEE binary16 bit pattern nearest to f, ties to even (round-to-nearest-even conversion):
+ * binary16 has 10 stored fraction bits, exponents -14..15, subnormals down to 2^-24, and every
+ * magnitude from 65520 (half-way between 65504 and 2^16) up rounds to infinity.
+ */
+uint16_t oracle_float_to_half(float f)
+{
+    uint32_t bits;
+    memcpy(&bits, &f, 4);
+    uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+    if (((bits >> 23) & 0xffu) == 0xffu)            /* infinity or NaN */
+        return sign | 0x7c00u | ((bits & 0x7fffffu) ? 0x200u : 0u);
+    double v = fabs((double)f);                     /* exact */
+    if (v >= 65520.0)
+        return sign | 0x7c00u;
+    if (v < ldexp(1.0, -14)) {                      /* subnormal range: units of 2^-24 */
+        double q = oracle_round_half_even(v * ldexp(1.0, 24));
+        return sign | (uint16_t)q;                  /* q == 1024 is the smallest normal */
+    }
+    int ex;
+    frexp(v, &ex);                                  /* v in [2^(ex-1), 2^ex) */
+    int e = ex - 1;
+    double q = oracle_round_half_even(ldexp(v, 10 - e));   /* in [1024, 2048] */
+    if (q == 2048.0) {
+        q = 1024.0;
+        e += 1;
+    }
+    if (e + 15 >= 31)
+        return sign | 0x7c00u;
+    return sign | (uint16_t)(((e + 15) << 10) | ((int)q - 1024));
+}
+
+/*
+ * The fp16-activation prepass: xh[r][k] = binary16(x[r][k]) (natural order) and, per row and
+ * 64-wide group, S[r][g] = ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)) in fp32 with
+ * c_o = (((x[8o] + x[8o+1]) + x[8o+2]) + ... ) + x[8o+7] over the group's inputs.
+ * Output layouts xh[m][k], xsf[m][k/64].
+ */
+int oracle_prep_a16(const float *x, int64_t m, int64_t k, uint16_t *xh, float *xsf)
+{
+    if (m < 0 || k <= 0 || k % 64 != 0)
+        return ORACLE_BAD_ARGS;
+    int64_t ng = k / 64;
+    for (int64_t i = 0; i < m * k; ++i)
+        xh[i] = oracle_float_to_half(x[i]);
+    for (int64_t r = 0; r < m; ++r) {
+        for (int64_t g = 0; g < ng; ++g) {
+            const float *v = x + r * k + g * 64;
+            float c[8];
+            for (int o = 0; o < 8; ++o) {
+                float acc = v[8 * o];
+                for (int i = 1; i < 8; ++i)
+                    acc = acc + v[8 * o + i];
+                c[o] = acc;
+            }
+            xsf[r * ng + g] = ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * y[r][n] = sum_g ( sw[n][g] * sum_{k in g} w_int[n][k] * xh[r][k] + bw[n][g] * S[r][g] )
+ * t[r][n] = sum_g ( sum_{k in g} |sw * w_int * xh| + |bw * S| )          (fp64, g and k ascending)
+ * xh holds binary16 bit patterns [m][k], xsf the fp32 group sums [m][k/group]; bias_f16 is used
+ * only for format 1.  t may be NULL.
+ */
+int oracle_linear_a16(int32_t format, const uint8_t *codes, const uint16_t *scales_f16,
+                      const uint16_t *bias_f16, const int8_t *codebook, int64_t n, int64_t k,
+                      int32_t group, const uint16_t *xh, const float *xsf, int64_t m,
+                      double *y, double *t)
+{
+    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 2)
+        return ORACLE_BAD_ARGS;
+    if ((format == 1 && bias_f16 == NULL) || (format == 2 && codebook == NULL))
+        return ORACLE_BAD_ARGS;
+    int64_t ng = k / group;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t c = 0; c < n; ++c) {
+        double *w = (double *)malloc((size_t)k * sizeof(double));
+        for (int64_t kk = 0; kk < k; ++kk)
+            w[kk] = (double)oracle_weight_int(format, codes, codebook, k, c, kk);
+        for (int64_t r = 0; r < m; ++r) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t g = 0; g < ng; ++g) {
+                double sw = oracle_half_to_double(scales_f16[c * ng + g]);
+                double bw = (format == 1) ? oracle_half_to_double(bias_f16[c * ng + g]) : 0.0;
+                double dot = 0.0, dmag = 0.0;
+                for (int64_t kk = g * group; kk < (g + 1) * group; ++kk) {
+                    double p = w[kk] * oracle_half_to_double(xh[r * k + kk]);
+                    dot += p;
+                    dmag += fabs(p);
+                }
+                double bias_term = bw * (double)xsf[r * ng + g];
+                acc += sw * dot + bias_term;
+                mag += fabs(sw) * dmag + fabs(bias_term);
+            }
+            y[r * n + c] = acc;
+            if (t)
+                t[r * n + c] = mag;
+        }
+        free(w);
     }
     return ORACLE_OK;
 }

@@ -535,3 +535,129 @@ def test_row_scale_view_equals_one_scale_per_row():
     want = s_row.astype(np.float64)[None, :] * np.einsum("mng,mg->mn", d.astype(np.float64),
                                                             xs.astype(np.float64))
     np.testing.assert_allclose(y, want, rtol=1e-15, atol=0)
+
+
+# ---- the fp16-activation path (TensorFold PR #3215's half tiles)
+
+def test_float_to_half_matches_numpy_round_to_nearest_even():
+    # numpy's float16 conversion is an independent round-to-nearest-even implementation
+    rng = np.random.default_rng(21)
+    vals = [rng.standard_normal(3000) * 10.0 ** rng.integers(-9, 6, size=3000)]
+    # exact ties between binary16 neighbours (normal and subnormal), the largest finite, the
+    # overflow threshold 65520, signed zeros and the subnormal/normal boundary
+    ulp1 = 2.0 ** -10
+    ties = [1 + ulp1 / 2, 1 + 3 * ulp1 / 2, 2049 / 2048 * 2, 2.0 ** -25, 3 * 2.0 ** -25,
+            2.0 ** -14 - 2.0 ** -25, 65504.0, 65519.99, 65520.0, 70000.0, 0.0, -0.0,
+            2.0 ** -14, 2.0 ** -24, 2.0 ** -26, 1e-8]
+    vals.append(np.array(ties + [-v for v in ties]))
+    x = np.concatenate(vals).astype(np.float32)
+    got = oracle.float_to_half(x)
+    with np.errstate(over="ignore"):                    # the overflow cases are intended
+        want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want), x[got != want][:5]
+    assert oracle.float_to_half(np.float32([np.inf]))[0] == 0x7C00
+
+
+def _load_tree_golden():
+    cases, cur = [], None
+    for line in open(os.path.join(GOLDEN, "a16_group_sum_tree.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        f = line.split()
+        if f[0] == "case":
+            cur = dict(name=f[1], want=float(f[2]), x=np.zeros(64, np.float32))
+            cases.append(cur)
+        else:
+            cur["x"][int(f[0])] = np.float32(float(f[1]))
+    for c in cases:
+        if c["name"] == "exact":
+            c["x"] = np.arange(1, 65, dtype=np.float32)
+    return cases
+
+
+def test_a16_group_sum_tree_golden():
+    cases = _load_tree_golden()
+    assert [c["name"] for c in cases] == ["order", "tree", "exact"]
+    for c in cases:
+        x = np.concatenate([c["x"], np.ones(64, np.float32)])[None, :]   # two groups
+        _, s = oracle.prep_a16(x)
+        assert s[0, 0] == np.float32(c["want"]), (c["name"], s[0, 0])
+        assert s[0, 1] == np.float32(64.0)
+    # controls: a plain left-to-right sum and numpy's pairwise sum miss the tree case
+    tree = cases[1]["x"]
+    left = np.float32(0)
+    for v in tree:
+        left = np.float32(left + v)
+    assert left != np.float32(cases[1]["want"])
+    assert np.float32(tree.astype(np.float64).sum()) != np.float32(cases[1]["want"])
+
+
+def test_a16_prep_halves_are_the_conversion():
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal((3, 256)) * 4).astype(np.float32)
+    xh, _ = oracle.prep_a16(x)
+    assert np.array_equal(xh, x.astype(np.float16).view(np.uint16))
+
+
+def _dequant(fmt, codes, scales, bias, cb, group):
+    """Independent numpy dequantization of the canonical weights: W [n, k] in fp64."""
+    from bit_group_quantized_act_amd import synth
+    c = synth.unpack_nibbles(codes).astype(np.int64)
+    if fmt == oracle.FORMAT_SYM:
+        wi = np.where(c >= 8, c - 16, c)
+    elif fmt == oracle.FORMAT_AFFINE:
+        wi = c
+    else:
+        wi = np.take_along_axis(cb.astype(np.int64), c, axis=1)
+    sw = np.repeat(scales.astype(np.float64), group, axis=1)
+    w = sw * wi
+    if bias is not None:
+        w = w + np.repeat(bias.astype(np.float64), group, axis=1)
+    return w, wi, sw
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_a16_linear_brute_force(fmt):
+    # y = xh @ (sw * w_int)^T + sum_g bw * S in numpy fp64 (matmul on dequantized weights)
+    rng = np.random.default_rng(30 + fmt)
+    n, k, g, m = 24, 256, 64, 3
+    codes = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scales = (rng.uniform(0.5, 1.5, size=(n, k // g)) * 0.01).astype(np.float16)
+    bias = (rng.standard_normal((n, k // g)) * 0.05).astype(np.float16) if fmt == 1 else None
+    cb = rng.integers(-127, 128, size=(n, 16), dtype=np.int8) if fmt == 2 else None
+    x = (rng.standard_normal((m, k)) * 3).astype(np.float32)
+    xh, xsf = oracle.prep_a16(x)
+    y, t = oracle.linear_a16(fmt, codes, scales, xh, xsf, g, bias_f16=bias, codebook=cb)
+    _, wi, sw = _dequant(fmt, codes, scales, None, cb, g)
+    xf = xh.view(np.float16).astype(np.float64)
+    want = xf @ (sw * wi).T
+    if bias is not None:
+        want = want + xsf.astype(np.float64) @ bias.astype(np.float64).T
+    np.testing.assert_allclose(y, want, rtol=0, atol=1e-12 * t.max())
+    assert np.all(t >= np.abs(y) * (1 - 1e-12))
+    # a planted mistake (affine read as signed codes) moves the output beyond the tolerance
+    if fmt == 1:
+        wrong = xf @ (sw * np.where(wi >= 8, wi - 16, wi)).T + xsf.astype(np.float64) @ \
+            bias.astype(np.float64).T
+        assert np.abs(wrong - y).max() > 1e-3
+
+
+def test_a16_linear_equals_the_int8_path_on_exactly_quantized_inputs():
+    # inputs that both prepasses represent exactly (multiples of 1/16 with a group maximum of
+    # 127/16: xs = 1/16, the codes are 16x, the halves exact, the tree sums exact) give the same
+    # output from the two independent oracle definitions
+    rng = np.random.default_rng(31)
+    n, k, g, m = 16, 256, 64, 2
+    q = rng.integers(-127, 128, size=(m, k)).astype(np.float32)
+    q[:, ::g] = 127.0
+    x = q / np.float32(16.0)
+    codes = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scales = (rng.uniform(0.5, 1.5, size=(n, k // g)) * 0.01).astype(np.float16)
+    bias = (rng.standard_normal((n, k // g)) * 0.05).astype(np.float16)
+    xq, xs, xsum = oracle.prep(x, g, 0)
+    assert np.all(xs == np.float32(1 / 16))
+    y8, t8 = oracle.linear(oracle.FORMAT_AFFINE, codes, scales, xq, xs, xsum, g, bias_f16=bias)
+    xh, xsf = oracle.prep_a16(x)
+    y16, _ = oracle.linear_a16(oracle.FORMAT_AFFINE, codes, scales, xh, xsf, g, bias_f16=bias)
+    np.testing.assert_allclose(y16, y8, rtol=0, atol=1e-12 * t8.max())
