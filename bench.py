@@ -26,6 +26,11 @@ cpu_baseline = the CPU oracle (plain C, OpenMP) on the same workload, repeated f
 --glu ACT times the gated variant instead (w4a8_linear_glu): the config's weights read as a
 [gate; up] pair (n = 2F), and the output is act(gate) * up, fp32 [m][F].
 
+--a16 times the fp16-activation path instead (w4a8_linear_a16: the prepass writing X as half
+and its fp32 group sums, then the GEMV / GEMM with f16 MFMA); its dominant kernel is the GEMV /
+GEMM alone (w4a8_gemm_a16), priced against the 2.5 PFLOP/s dense fp16 MFMA peak when that floor
+is above the HBM floor.
+
 --argmax CAP times the greedy tail of a vocabulary head instead (one row; w4a8_lm_head_argmax:
 the prepass, the GEMV that also soft-caps the logits with CAP (0: no cap) and stores each
 64-row panel's largest key, and a one-workgroup reduction of those keys into the token).  The
@@ -47,6 +52,7 @@ if ROOT not in sys.path:
 METRIC = "W4A8 linear: weight GB/s at M=1 and int8 TOPS at M≥128 (% of roofline)"
 HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0
+F16_PEAK_TFLOPS = 2500.0
 POOL_BYTES = 512 << 20
 
 # HBM bytes per launch of the dominant kernel, read from two rocprofv3 --pmc passes (FETCH_SIZE,
@@ -95,6 +101,8 @@ def parse():
     ap.add_argument("--argmax", type=float, default=None, metavar="CAP",
                     help="time w4a8_lm_head_argmax (soft cap CAP, 0 for none) on a one-row "
                          "workload instead")
+    ap.add_argument("--a16", action="store_true",
+                    help="time the fp16-activation path (w4a8_linear_a16) instead")
     ap.add_argument("--hot", action="store_true",
                     help="reuse one weight buffer (measures cache, not HBM; labelled)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -118,13 +126,17 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 8}), flush=True)
 
 
-def workload_name(cfg, glu=None, cap=None):
+def workload_name(cfg, glu=None, cap=None, a16=False):
     from bit_group_quantized_act_amd import synth
     kind = "decode GEMV" if cfg.m == 1 else "prefill GEMM"
     rot = ", 128-block WHT" if cfg.hadamard else ""
     if cfg.extra.get("row_scale"):
         rot += f", one scale per row seen as K/{cfg.group} groups"
     fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072
+    if a16:
+        return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
+                f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights x fp16 activations (prepass writing "
+                f"X as half and its fp32 group sums + {'GEMV' if cfg.m == 1 else 'GEMM'} per step)")
     how = ("prepass fused into the GEMV" if fused and cap is None else
            "prepass + GEMV" if cfg.m == 1 else "prepass + GEMM")
     gated = "" if glu is None else f", gated output {glu}(gate)*up with F={cfg.n // 2}"
@@ -169,12 +181,21 @@ def main():
     wbytes = synth.weight_bytes(cfg)
     fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072   # w4a8_linear's one-kernel case
     cap = args.argmax
+    a16 = args.a16
+    if a16 and (cap is not None or args.glu is not None or cfg.group != 64 or
+                cfg.fmt == synth.FMT_CODEBOOK):
+        print("--a16 needs a symmetric or affine 64-group workload and no --glu / --argmax",
+              file=sys.stderr)
+        sys.exit(2)
     if cap is not None:
         if cfg.m != 1 or args.glu is not None or not cap >= 0:
             print("--argmax needs a one-row workload, no --glu and a cap >= 0", file=sys.stderr)
             sys.exit(2)
         fused = False                                  # the tail runs in the two-kernel path
     alg_bytes = synth.algorithmic_bytes(cfg, fused_prep=fused)
+    if a16:          # weights + xh (2 bytes per input) + fp32 group sums + y, no xq / xs / xsum
+        alg_bytes = synth.weight_bytes(cfg) + 2 * cfg.m * cfg.k + 4 * cfg.m * (cfg.k // 64) + \
+            4 * cfg.m * cfg.n
     if cap is not None:                                # keys written and read, token, logit
         alg_bytes += 2 * w4a8.argmax_work_bytes(cfg.n) + 8
     act = None
@@ -199,13 +220,16 @@ def main():
     token = torch.empty(1, dtype=torch.int32, device=dev)
     tval = torch.empty(1, dtype=torch.float32, device=dev)
     work = w4a8.argmax_work(lay, dev)
+    xh16, xsf16 = w4a8.a16_buffers(cfg.m, cfg.k, dev) if a16 else (None, None)
     torch.cuda.synchronize()
 
     def linear(i):
         # the dominant kernel alone: the fused prepass + GEMV at one row (the plain GEMV for a
         # vocabulary-sized row), the GEMM above
         pk = pool[i % pool_n]
-        if cap is not None:
+        if a16:
+            w4a8.gemm_a16(lay, pk, xh16, xsf16, out=y)
+        elif cap is not None:
             w4a8.gemv_argmax(lay, pk, xq, xs, xsum, cap, out=(y[0], token, tval), work=work)
         elif act is not None:
             if fused:
@@ -220,7 +244,9 @@ def main():
             w4a8.gemm(lay, pk, xq, xs, xsum, out=y)
 
     def step(i):
-        if cap is not None:
+        if a16:
+            w4a8.linear_a16(lay, pool[i % pool_n], x, out=y, prep_out=(xh16, xsf16))
+        elif cap is not None:
             w4a8.lm_head_argmax(lay, pool[i % pool_n], x, cap, cfg.hadamard,
                                 out=(y[0], token, tval), work=work, prep_out=(xq, xs, xsum))
         elif act is not None:
@@ -265,20 +291,22 @@ def main():
     us_linear = timed(g_lin) * 1000.0 / args.steps
 
     value = wbytes / (ms_per_step * 1e-3) / 1e9
-    mfma_floor = ops / (INT8_PEAK_TOPS * 1e12)
     hbm_floor = alg_bytes / (HBM_PEAK_GBPS * 1e9)
+    peak_mfma = F16_PEAK_TFLOPS if a16 else INT8_PEAK_TOPS
+    mfma_floor = ops / (peak_mfma * 1e12)
     if cfg.m > 1 and mfma_floor > hbm_floor:
         achieved = ops / (us_linear * 1e-6) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_PEAK_TOPS,
-                    unit="TFLOP/s", frac=round(achieved / INT8_PEAK_TOPS, 4))
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak_mfma,
+                    unit="TFLOP/s", frac=round(achieved / peak_mfma, 4))
     else:
         achieved = alg_bytes / (us_linear * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4))
     kname = "gemv" if cfg.m == 1 else "gemm"     # the fused kernel lives in gemv.hip
-    traffic_key = (cfg.name if act is None and cap is None else   # counters of the plain kernel
-                   f"{cfg.name}-{'glu' if act is not None else 'argmax'}")
-    shown = kname if cap is None else "gemv_argmax (GEMV with the tail + key reduction)"
+    traffic_key = (cfg.name if act is None and cap is None and not a16 else
+                   f"{cfg.name}-{'glu' if act is not None else 'argmax' if cap is not None else 'a16'}")
+    shown = ("gemv_argmax (GEMV with the tail + key reduction)" if cap is not None else
+             f"{kname}_a16" if a16 else kname)
     roof.update(traffic=measured_traffic(traffic_key, kname), kernel=shown,
                 kernel_us=round(us_linear, 3), alg_bytes_per_launch=alg_bytes,
                 int_ops_per_launch=ops,
@@ -301,9 +329,14 @@ def main():
         sample_wbytes = wbytes * rows.size / cfg.n
         reps, t0 = 0, time.perf_counter()
         while True:
-            oq, os_, osum = oracle.prep(layer["x"], cfg.group, cfg.hadamard)
-            yo = oracle.linear(cfg.fmt, codes, scales, oq, os_, osum, cfg.group, bias_f16=bias,
-                               codebook=cb, with_terms=False)
+            if a16:
+                oh, osf = oracle.prep_a16(layer["x"])
+                yo = oracle.linear_a16(cfg.fmt, codes, scales, oh, osf, cfg.group, bias_f16=bias,
+                                       with_terms=False)
+            else:
+                oq, os_, osum = oracle.prep(layer["x"], cfg.group, cfg.hadamard)
+                yo = oracle.linear(cfg.fmt, codes, scales, oq, os_, osum, cfg.group,
+                                   bias_f16=bias, codebook=cb, with_terms=False)
             if act is not None:
                 oracle.glu(act, yo)
             if cap is not None:
@@ -316,7 +349,7 @@ def main():
                 f"all {cfg.m} rows x {rows.size} of the {cfg.n} weight rows")
         cpu = dict(value=round(sample_wbytes * reps / el / 1e9, 3), unit="GB/s",
                    cores=oracle.num_threads(), kind="oracle",
-                   sample=f"{what} of {cfg.name} (prep + linear"
+                   sample=f"{what} of {cfg.name} ({'fp16-activation ' if a16 else ''}prep + linear"
                           f"{' + gated output' if act is not None else ''}"
                           f"{' + soft cap and argmax' if cap is not None else ''}), repeated "
                           f"{reps}x in "
@@ -333,9 +366,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "f16" if a16 else "int8",
         "data": "synthetic",
-        "config": {"workload": workload_name(cfg, args.glu, cap), "m": cfg.m, "k": cfg.k, "n": cfg.n,
+        "config": {"workload": workload_name(cfg, args.glu, cap, a16), "m": cfg.m, "k": cfg.k, "n": cfg.n,
                    "group": cfg.group, "format": synth.FORMAT_NAMES[cfg.fmt],
                    "weight_pool_buffers": pool_n, "hot_cache": bool(args.hot),
                    "parallelism": "single GPU"},

@@ -1,0 +1,373 @@
+// The fp16-activation path (W4A16): 4-bit weights in the packed format times activations
+// rounded to binary16, with fp32 group sums for the affine bias term.
+//
+// Source: "TensorFold PR #3215, simd_qmm on Metal: X's group sums and half operands from a
+// prepass", section "What this changes": the prompt tiles multiply 4-bit g64 weights
+// (w = scale * u + bias) with X as half; a prepass writes X as half and each row's 64-wide group
+// sums for the bias term, added by the tiles' fixed tree ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)),
+// each c a left-to-right sum of 8 consecutive inputs.  Output:
+//   y[r][n] = sum_g ( sw[n][g] * sum_{k in g} w_int[n][k] * xh[r][k] + bw[n][g] * S[r][g] )
+// with w_int = q (symmetric, -8..7) or u (affine, 0..15): the affine code enters unsigned, so the
+// bias term takes the fp32 sums of X itself, not of its halves.
+//
+// Interleaved halves.  Within every 32-wide block of a row, the prepass stores xh so that the
+// 4-byte word 4j + e holds the two inputs that nibble pair e of the weight chunk's dword j meets
+// (see the packed chunk format: byte b of dword j holds k = 4j + b low and 16 + 4j + b high):
+//   word 4j+0: k 4j, 4j+2     word 4j+1: k 16+4j, 18+4j
+//   word 4j+2: k 4j+1, 4j+3   word 4j+3: k 17+4j, 19+4j
+// so a dword of codes becomes four half pairs with one shift, one and-or and one packed add each
+// (the magic-number conversion: 0x6400 | v is the binary16 value 1024 + v), and meets four
+// consecutive words of xh: one v_dot2_f32_f16 each in the GEMV, one 16-byte operand in the GEMM.
+//
+// MI355X design.
+//   Prepass: one lane per 8 consecutive inputs (two 16-byte loads); the octet's left-to-right
+//   sum, then the tree as three cross-lane adds (lanes 8 apart form a group); the halves go
+//   through LDS to be written interleaved, 16 bytes per lane.
+//   GEMV (one row): a workgroup per 64-row panel, 8 wavefronts taking every 8th group, lane r
+//   on panel row r (each chunk load is one contiguous KiB per wavefront); four groups in flight
+//   per wavefront; the row's halves and sums are wave-uniform and come through scalar loads.
+//   GEMM: a workgroup owns 64 rows x 128 channels, each wavefront 64 rows x its 32 channels as
+//   two 32x32 tiles sharing one weight fragment (v_mfma_f32_32x32x16_f16, four per tile and
+//   group: weight dword j against the 16-byte word run 4j..4j+3).  The rows' halves are staged
+//   through two LDS buffers of 128 k (XOR-swizzled 16-byte units, so the 32 rows one operand
+//   read touches spread over the banks), loaded one stage ahead together with the weight
+//   chunks, scales and sums.  Each group ends with acc += sw * P (one FMA per element; the
+//   lane's column is fixed, so sw is one register) and the affine bias as a rank-1 update
+//   S x bw on the matrix unit (v_mfma_f32_32x32x2_f32).
+#include "w4a8_kernels.h"
+
+namespace w4a8 {
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
+
+constexpr int kGroupA16 = 64;
+
+// The half pair e of code dword w (already XORed with 0x88888888, so each nibble holds
+// v = code + 8 for the symmetric format and u for the affine one) as binary16 w_int values.
+template <int FMT>
+__device__ __forceinline__ uint32_t half_pair(uint32_t w, int e) {
+    const uint32_t h = ((w >> (4 * e)) & 0x000F000Fu) | 0x64006400u;    // 1024 + v
+    const _Float16 off = static_cast<_Float16>(FMT == kFmtAffine ? -1024.0f : -1032.0f);
+    const h2_t r = __builtin_bit_cast(h2_t, h) + h2_t{off, off};        // exact: |w_int| <= 15
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---- prepass
+
+__global__ __launch_bounds__(256) void prep_a16_kernel(const float4 *__restrict__ x,
+                                                       int64_t octets, int64_t m, int k,
+                                                       uint4 *__restrict__ xh,
+                                                       float *__restrict__ xsf) {
+#pragma clang fp contract(off)
+    __shared__ _Float16 tile[256 * 8];                 // the block's octets as halves, in order
+    const int64_t t = blockIdx.x * (int64_t)256 + threadIdx.x;
+    const bool live = t < octets;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (live) {
+        const float4 a = x[2 * t], b = x[2 * t + 1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    float c = v[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) c = c + v[i];
+    // ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)): lanes 8 apart hold the group's octets in order; an
+    // IEEE add is commutative, so every lane of the group ends with the same bits
+    c = c + __shfl_xor(c, 1, 64);
+    c = c + __shfl_xor(c, 2, 64);
+    c = c + __shfl_xor(c, 4, 64);
+    const int64_t per_row = k / 8;
+    if (live && (t & 7) == 0) {
+        const int64_t row = t / per_row;
+        const int64_t g = (t % per_row) / 8;
+        xsf[g * m + row] = c;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[threadIdx.x * 8 + i] = static_cast<_Float16>(v[i]);
+    __syncthreads();
+    if (!live) return;
+    // this lane writes word run 4j..4j+3 of its 32-wide block (4 lanes per block, aligned)
+    const int base = (threadIdx.x & ~3) * 8;
+    const int j = threadIdx.x & 3;
+    const int src[8] = {4 * j, 4 * j + 2, 16 + 4 * j, 18 + 4 * j,
+                        4 * j + 1, 4 * j + 3, 17 + 4 * j, 19 + 4 * j};
+    uint32_t wd[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, tile[base + src[2 * e]]);
+        const uint32_t hi = __builtin_bit_cast(uint16_t, tile[base + src[2 * e + 1]]);
+        wd[e] = lo | (hi << 16);
+    }
+    xh[t] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+}
+
+// ---- GEMV (one activation row)
+
+constexpr int kA16Waves = 8;
+constexpr int kA16Ring = 4;                            // groups in flight per wavefront
+
+template <int FMT>
+__global__ __launch_bounds__(64 * kA16Waves) void gemv_a16_kernel(const uint8_t *__restrict__ packed,
+                                                                  const Geom geom,
+                                                                  const uint32_t *__restrict__ xw,
+                                                                  const float *__restrict__ xsf,
+                                                                  float *__restrict__ y) {
+    constexpr int MB = (FMT == kFmtAffine) ? 4 : 2;
+    __shared__ float red[kA16Waves][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int p = blockIdx.x;
+    const int kc = geom.k / kChunkK;
+    const int ng = geom.k / kGroupA16;
+    const int nblk = (ng + 3) / 4;
+    const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)p * kc * 1024,
+                                (uint64_t)kc * 1024);
+    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)p * nblk * 256 * MB,
+                                (uint64_t)nblk * 256 * MB);
+    auto code_off = [&](int g, int h) {
+        return g < ng ? ((2 * g + h) * 64 + lane) * 16 : kOOB;
+    };
+    auto meta_off = [&](int g) {
+        return g < ng ? (((g >> 2) * 64 + lane) * 4 + (g & 3)) * MB : kOOB;
+    };
+    v4i ring[kA16Ring][2];
+    uint32_t meta[kA16Ring];
+#pragma unroll
+    for (int s = 0; s < kA16Ring; ++s) {
+        const int g = wave + s * kA16Waves;
+        ring[s][0] = ld128(rc, code_off(g, 0));
+        ring[s][1] = ld128(rc, code_off(g, 1));
+        meta[s] = (MB == 4) ? ld32(rm, meta_off(g)) : ld16(rm, meta_off(g));
+    }
+    float acc = 0.0f;
+    for (int g0 = wave; g0 < ng; g0 += kA16Ring * kA16Waves) {
+#pragma unroll
+        for (int s = 0; s < kA16Ring; ++s) {
+            const int g = g0 + s * kA16Waves;
+            if (g < ng) {
+                const uint32_t *xg = xw + 32 * g;        // the group's 64 halves: wave-uniform
+                float dot = 0.0f;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t w = static_cast<uint32_t>(ring[s][h][j]) ^ 0x88888888u;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t wp = half_pair<FMT>(w, e);
+                            dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, wp),
+                                                         __builtin_bit_cast(h2_t, xg[16 * h + 4 * j + e]),
+                                                         dot, false);
+                        }
+                    }
+                }
+                const float sw = half_bits_to_float(meta[s] & 0xFFFFu);
+                acc = fmaf(sw, dot, acc);
+                if (FMT == kFmtAffine) acc = fmaf(half_bits_to_float(meta[s] >> 16), xsf[g], acc);
+            }
+            const int gn = g + kA16Ring * kA16Waves;
+            ring[s][0] = ld128(rc, code_off(gn, 0));
+            ring[s][1] = ld128(rc, code_off(gn, 1));
+            meta[s] = (MB == 4) ? ld32(rm, meta_off(gn)) : ld16(rm, meta_off(gn));
+        }
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    float s = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < kA16Waves; ++w) s += red[w][lane];
+    const int row = p * kPanelRows + lane;
+    if (row < geom.n) y[row] = s;
+}
+
+// ---- GEMM (several activation rows)
+
+constexpr int kA16BN = 128;                        // channels per workgroup (4 wavefronts x 32)
+constexpr int kA16SK = 128;                        // k per LDS stage (two groups)
+
+template <int FMT>
+__global__ __launch_bounds__(256, 2) void gemm_a16_kernel(const uint8_t *__restrict__ packed,
+                                                          const Geom geom, int m,
+                                                          const uint16_t *__restrict__ xh,
+                                                          const float *__restrict__ xsf,
+                                                          float *__restrict__ y) {
+    constexpr int MB = (FMT == kFmtAffine) ? 4 : 2;
+    __shared__ __attribute__((aligned(16))) v4i lds[2][64 * 16];   // [buf][row][16-byte unit]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+    const int r32 = lane & 31;
+
+    const int mtiles = (m + 63) / 64;
+    int bid = blockIdx.x;
+    const int nb = gridDim.x;
+    if (nb % 8 == 0) bid = (bid % 8) * (nb / 8) + bid / 8;   // consecutive tiles on one XCD
+    const int mt = bid % mtiles, nt = bid / mtiles;
+    const int m0 = mt * 64;
+    const int c0 = nt * kA16BN + wave * 32;                 // this wavefront's first channel
+    const bool wact = c0 < geom.n_pad;                      // panels are whole: all or none
+    const int col = c0 + r32;
+    const int p = col / kPanelRows, prow = col % kPanelRows;
+    const int k = geom.k;
+    const int kc = k / kChunkK;
+    const int ng = k / kGroupA16;
+    const int nblk = (ng + 3) / 4;
+    const int nstage = (k + kA16SK - 1) / kA16SK;
+
+    const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)(wact ? p : 0) * kc * 1024,
+                                wact ? (uint64_t)kc * 1024 : 0);
+    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)(wact ? p : 0) * nblk * 256 * MB,
+                                wact ? (uint64_t)nblk * 256 * MB : 0);
+    const rsrc_t rx = make_rsrc(xh, (uint64_t)m * k * 2);
+    const rsrc_t rs = make_rsrc(xsf, (uint64_t)ng * m * 4);
+
+    // stage loads: activation units (4 per thread), the lane's two weight chunks, the two
+    // groups' scale (and bias) of the lane's channel, the two groups' sums of the tiles' rows
+    auto load_a = [&](int s, v4i (&a)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = i * 16 + (tid >> 4), u = tid & 15;
+            const int kk = s * kA16SK + 8 * u;
+            const bool ok = (m0 + rr < m) && (kk < k);
+            a[i] = ld128(rx, ok ? ((m0 + rr) * k + kk) * 2 : kOOB);
+        }
+    };
+    auto load_b = [&](int s, v4i (&b)[2], uint32_t (&mt2)[2], float (&sv)[2][2]) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int g = 2 * s + st;
+            const int c = 2 * g + half;
+            b[st] = ld128(rc, g < ng ? (c * 64 + prow) * 16 : kOOB);
+            const int mo = g < ng ? (((g >> 2) * 64 + prow) * 4 + (g & 3)) * MB : kOOB;
+            mt2[st] = (MB == 4) ? ld32(rm, mo) : ld16(rm, mo);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int row = m0 + 32 * t + r32;
+                const bool ok = FMT == kFmtAffine && g < ng && half == 0 && row < m;
+                sv[st][t] = __builtin_bit_cast(float, ld32(rs, ok ? (g * m + row) * 4 : kOOB));
+            }
+        }
+    };
+    auto store_a = [&](int buf, const v4i (&a)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = i * 16 + (tid >> 4), u = tid & 15;
+            lds[buf][rr * 16 + (u ^ (rr & 7))] = a[i];
+        }
+    };
+
+    v16f acc[2], part[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { acc[t][e] = 0.0f; part[t][e] = 0.0f; }
+    }
+    v4i a_nx[4], b_cur[2], b_nx[2];
+    uint32_t m_cur[2], m_nx[2];
+    float s_cur[2][2], s_nx[2][2];
+    load_a(0, a_nx);
+    load_b(0, b_cur, m_cur, s_cur);
+    store_a(0, a_nx);
+    __syncthreads();
+
+    for (int s = 0; s < nstage; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nstage) {
+            load_a(s + 1, a_nx);
+            load_b(s + 1, b_nx, m_nx, s_nx);
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int g = 2 * s + st;
+            if (g >= ng) break;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t w = static_cast<uint32_t>(b_cur[st][j]) ^ 0x88888888u;
+                const v4i bw4 = {static_cast<int>(half_pair<FMT>(w, 0)),
+                                 static_cast<int>(half_pair<FMT>(w, 1)),
+                                 static_cast<int>(half_pair<FMT>(w, 2)),
+                                 static_cast<int>(half_pair<FMT>(w, 3))};
+                const v8h_t bop = __builtin_bit_cast(v8h_t, bw4);
+                const int unit = (2 * st + half) * 4 + j;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int rr = 32 * t + r32;
+                    const v8h_t aop = __builtin_bit_cast(v8h_t, lds[buf][rr * 16 + (unit ^ (rr & 7))]);
+                    part[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop, part[t], 0, 0, 0);
+                }
+            }
+            const float sw = half_bits_to_float(m_cur[st] & 0xFFFFu);
+            const float bw = (FMT == kFmtAffine && half == 0) ? half_bits_to_float(m_cur[st] >> 16)
+                                                               : 0.0f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    acc[t][e] = fmaf(sw, part[t][e], acc[t][e]);
+                    part[t][e] = 0.0f;
+                }
+                if (FMT == kFmtAffine)
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(s_cur[st][t], bw, acc[t], 0, 0, 0);
+            }
+        }
+        if (s + 1 < nstage) {
+            store_a(buf ^ 1, a_nx);
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                b_cur[st] = b_nx[st];
+                m_cur[st] = m_nx[st];
+                s_cur[st][0] = s_nx[st][0];
+                s_cur[st][1] = s_nx[st][1];
+            }
+        }
+        __syncthreads();
+    }
+
+    if (!wact || col >= geom.n) return;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = m0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+            if (row < m) y[(int64_t)row * geom.n + col] = acc[t][e];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prep_a16(const float *x, int64_t m, int k, uint16_t *xh, float *xsf,
+                           hipStream_t stream) {
+    const int64_t octets = m * (int64_t)k / 8;
+    if (octets == 0) return hipSuccess;
+    const unsigned grid = static_cast<unsigned>((octets + 255) / 256);
+    prep_a16_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<const float4 *>(x), octets, m, k,
+                                              reinterpret_cast<uint4 *>(xh), xsf);
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_a16(const Geom &g, const uint8_t *packed, int m, const uint16_t *xh,
+                             const float *xsf, float *y, hipStream_t stream) {
+    if (m == 0) return hipSuccess;
+    if (m == 1) {
+        const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
+        const uint32_t *xw = reinterpret_cast<const uint32_t *>(xh);
+        if (g.fmt == kFmtAffine)
+            gemv_a16_kernel<kFmtAffine><<<grid, 64 * kA16Waves, 0, stream>>>(packed, g, xw, xsf, y);
+        else
+            gemv_a16_kernel<kFmtSym><<<grid, 64 * kA16Waves, 0, stream>>>(packed, g, xw, xsf, y);
+        return hipGetLastError();
+    }
+    const unsigned grid = static_cast<unsigned>(((m + 63) / 64) * ((g.n_pad + kA16BN - 1) / kA16BN));
+    if (g.fmt == kFmtAffine)
+        gemm_a16_kernel<kFmtAffine><<<grid, 256, 0, stream>>>(packed, g, m, xh, xsf, y);
+    else
+        gemm_a16_kernel<kFmtSym><<<grid, 256, 0, stream>>>(packed, g, m, xh, xsf, y);
+    return hipGetLastError();
+}
+
+}  // namespace w4a8

@@ -420,6 +420,82 @@ w4a8_status w4a8_gemv_argmax(const w4a8_layout *L, const void *packed, const int
                     "greedy tail gemv launch");
 }
 
+namespace {
+// Arguments of the fp16-activation prepass (shared by the entry points that run it).
+w4a8_status check_prep_a16(const float *x, int32_t m, int32_t k, int32_t group, uint16_t *xh,
+                           float *xsf) {
+    if (m < 0) return fail(W4A8_ERR_ARG, "m = %d is negative", m);
+    if (group != 64)
+        return fail(W4A8_ERR_ARG, "group %d: the fp16-activation path sums 64-wide groups",
+                    group);
+    if (k < 64 || k > (1 << 20) || k % 64 != 0)
+        return fail(W4A8_ERR_ARG, "k = %d must be a multiple of 64 in [64, 2^20]", k);
+    if (static_cast<int64_t>(m) * k * 2 > 0x7FFFFFF0ll)
+        return fail(W4A8_ERR_UNSUPPORTED, "m * k = %lld halves exceed 2^31 - 16 bytes",
+                    static_cast<long long>(static_cast<int64_t>(m) * k));
+    if (m == 0) return W4A8_OK;
+    W4A8_REQUIRE_PTR(x);
+    W4A8_REQUIRE_PTR(xh);
+    W4A8_REQUIRE_PTR(xsf);
+    return W4A8_OK;
+}
+
+// The layout and output arguments of the fp16-activation linear.
+w4a8_status check_linear_a16(const w4a8_layout *L, const void *packed, int32_t m, float *y) {
+    w4a8_status s = check_layout(L);
+    if (s != W4A8_OK) return s;
+    if (L->format == W4A8_CODEBOOK_I4)
+        return fail(W4A8_ERR_UNSUPPORTED, "the fp16-activation path takes SYM or AFFINE weights");
+    if (L->group != 64)
+        return fail(W4A8_ERR_ARG, "group %d: the fp16-activation path sums 64-wide groups",
+                    L->group);
+    if (m < 0) return fail(W4A8_ERR_ARG, "m = %d is negative", m);
+    if (m == 0) return W4A8_OK;
+    if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
+    if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
+    W4A8_REQUIRE_PTR(y);
+    return W4A8_OK;
+}
+}  // namespace
+
+w4a8_status w4a8_prep_a16(const float *x, int32_t m, int32_t k, int32_t group, uint16_t *xh,
+                          float *xsf, void *stream) {
+    w4a8_status s = check_prep_a16(x, m, k, group, xh, xsf);
+    if (s != W4A8_OK || m == 0) return s;
+    if ((s = check_device()) != W4A8_OK) return s;
+    return launched(w4a8::launch_prep_a16(x, m, k, xh, xsf, static_cast<hipStream_t>(stream)),
+                    "fp16-activation prep launch");
+}
+
+w4a8_status w4a8_gemm_a16(const w4a8_layout *L, const void *packed, int32_t m,
+                          const uint16_t *xh, const float *xsf, float *y, void *stream) {
+    w4a8_status s = check_linear_a16(L, packed, m, y);
+    if (s != W4A8_OK || m == 0) return s;
+    if (static_cast<int64_t>(m) * L->k * 2 > 0x7FFFFFF0ll)
+        return fail(W4A8_ERR_UNSUPPORTED, "m * k = %lld halves exceed 2^31 - 16 bytes",
+                    static_cast<long long>(static_cast<int64_t>(m) * L->k));
+    W4A8_REQUIRE_PTR(xh);
+    W4A8_REQUIRE_PTR(xsf);
+    if ((s = check_device()) != W4A8_OK) return s;
+    return launched(w4a8::launch_linear_a16(geom_of(L), static_cast<const uint8_t *>(packed), m,
+                                            xh, xsf, y, static_cast<hipStream_t>(stream)),
+                    "fp16-activation linear launch");
+}
+
+w4a8_status w4a8_linear_a16(const w4a8_layout *L, const void *packed, int32_t m, const float *x,
+                            uint16_t *xh, float *xsf, float *y, void *stream) {
+    w4a8_status s = check_linear_a16(L, packed, m, y);
+    if (s != W4A8_OK) return s;
+    if ((s = check_prep_a16(x, m, L->k, L->group, xh, xsf)) != W4A8_OK || m == 0) return s;
+    if ((s = check_device()) != W4A8_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = w4a8::launch_prep_a16(x, m, L->k, xh, xsf, st);
+    if (e != hipSuccess) return launched(e, "fp16-activation prep launch");
+    return launched(w4a8::launch_linear_a16(geom_of(L), static_cast<const uint8_t *>(packed), m,
+                                            xh, xsf, y, st),
+                    "fp16-activation linear launch");
+}
+
 w4a8_status w4a8_debug_partials(const w4a8_layout *L, const void *packed, int32_t m,
                                 const int8_t *xq, const int32_t *xsum, int32_t *d,
                                 void *stream) {

@@ -210,6 +210,14 @@ struct Tail {
 hipError_t launch_gemv_argmax(const Geom &g, const uint8_t *packed, const int8_t *xq,
                               const float *xs, const int32_t *xsum, float *y, const Tail &tail,
                               hipStream_t stream);
+// The fp16-activation path: the prepass (x fp32 [m][k] -> interleaved halves xh [m][k] and the
+// fp32 group sums xsf [k/64][m]) and the linear on them (GEMV for m == 1, GEMM above), for the
+// symmetric and affine formats with 64-wide groups.
+hipError_t launch_prep_a16(const float *x, int64_t m, int k, uint16_t *xh, float *xsf,
+                           hipStream_t stream);
+hipError_t launch_linear_a16(const Geom &g, const uint8_t *packed, int m, const uint16_t *xh,
+                             const float *xsf, float *y, hipStream_t stream);
+
 // The reduction of nkeys panel keys into token and value (one workgroup).
 hipError_t launch_argmax_keys(const unsigned long long *keys, int nkeys, int32_t *token,
                               float *value, hipStream_t stream);

@@ -23,7 +23,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "no gfx950 device
 EXPORTS = ("w4a8_packed_layout", "w4a8_pack_weights", "w4a8_pack_weights_row_scale",
            "w4a8_prep", "w4a8_gemv", "w4a8_gemm",
            "w4a8_linear", "w4a8_linear_glu", "w4a8_gemm_glu", "w4a8_lm_head_argmax",
-           "w4a8_gemv_argmax", "w4a8_debug_partials", "w4a8_status_string", "w4a8_last_error")
+           "w4a8_gemv_argmax", "w4a8_prep_a16", "w4a8_linear_a16", "w4a8_gemm_a16",
+           "w4a8_debug_partials", "w4a8_status_string", "w4a8_last_error")
 ACT_SILU, ACT_GELU_TANH, ACT_GELU_ERF = 0, 1, 2
 
 
@@ -73,8 +74,11 @@ def load() -> ctypes.CDLL:
     lib.w4a8_lm_head_argmax.argtypes = [LP, P, P, i32, ctypes.c_float, P, P, P, P, P, P, P, u64,
                                         P]
     lib.w4a8_gemv_argmax.argtypes = [LP, P, P, P, P, ctypes.c_float, P, P, P, P, u64, P]
+    lib.w4a8_prep_a16.argtypes = [P, i32, i32, i32, P, P, P]
+    lib.w4a8_linear_a16.argtypes = [LP, P, i32, P, P, P, P, P]
+    lib.w4a8_gemm_a16.argtypes = [LP, P, i32, P, P, P, P]
     lib.w4a8_debug_partials.argtypes = [LP, P, i32, P, P, P, P]
-    for f in EXPORTS[:12]:
+    for f in EXPORTS[:15]:
         getattr(lib, f).restype = ctypes.c_int
     lib.w4a8_status_string.argtypes = [ctypes.c_int]
     lib.w4a8_status_string.restype = ctypes.c_char_p
@@ -345,3 +349,43 @@ def gemv_argmax(L: Layout, packed: torch.Tensor, xq, xs, xsum, softcap: float = 
                                    _ptr(value), _ptr(work), _work_bytes(work),
                                    _stream(packed.device)), "w4a8_gemv_argmax")
     return logits, token, value
+
+
+def a16_buffers(m: int, k: int, device):
+    """The fp16-activation prepass outputs: xh binary16 [m, k] (interleaved), xsf fp32 [k/64, m]."""
+    return (torch.empty((m, k), dtype=torch.float16, device=device),
+            torch.empty((k // 64, m), dtype=torch.float32, device=device))
+
+
+def prep_a16(x: torch.Tensor, out=None):
+    """fp16-activation prepass (w4a8_prep_a16) of x fp32 [m, k]: returns (xh, xsf)."""
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    _dev(x2, torch.float32, "x")
+    m, k = x2.shape
+    xh, xsf = out if out is not None else a16_buffers(m, k, x.device)
+    _check(load().w4a8_prep_a16(_ptr(x2), m, k, 64, _ptr(xh), _ptr(xsf), _stream(x.device)),
+           "w4a8_prep_a16")
+    return xh, xsf
+
+
+def linear_a16(L: Layout, packed: torch.Tensor, x: torch.Tensor, out=None, prep_out=None):
+    """fp16-activation linear (w4a8_linear_a16): x fp32 [m, k] -> y fp32 [m, n]; with
+    prep_out = (xh, xsf) also returns them."""
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    _dev(x2, torch.float32, "x")
+    m = x2.shape[0]
+    xh, xsf = prep_out if prep_out is not None else a16_buffers(m, L.k, x.device)
+    y = out if out is not None else torch.empty((m, L.n), dtype=torch.float32, device=x.device)
+    _check(load().w4a8_linear_a16(ctypes.byref(L), _ptr(packed), m, _ptr(x2), _ptr(xh),
+                                  _ptr(xsf), _ptr(y), _stream(x.device)), "w4a8_linear_a16")
+    return (y, (xh, xsf)) if prep_out is not None else y
+
+
+def gemm_a16(L: Layout, packed: torch.Tensor, xh: torch.Tensor, xsf: torch.Tensor, out=None):
+    """The fp16-activation GEMV / GEMM alone on prepared (xh, xsf) (w4a8_gemm_a16)."""
+    m = xh.shape[0]
+    y = out if out is not None else torch.empty((m, L.n), dtype=torch.float32,
+                                                device=packed.device)
+    _check(load().w4a8_gemm_a16(ctypes.byref(L), _ptr(packed), m, _ptr(xh), _ptr(xsf), _ptr(y),
+                                _stream(packed.device)), "w4a8_gemm_a16")
+    return y

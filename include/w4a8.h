@@ -287,6 +287,38 @@ w4a8_status w4a8_gemv_argmax(const w4a8_layout *L, const void *packed, const int
                              void *stream);
 
 /*
+ * The fp16-activation path (W4A16): the same packed 4-bit weights times activations rounded to
+ * binary16, with the affine bias term on fp32 group sums of the activations:
+ *   y[r][n] = sum_g ( sw[n][g] * sum_{k in g} w_int[n][k] * xh[r][k] + bw[n][g] * S[r][g] )
+ * where w_int is q (SYM) or the unsigned u (AFFINE), xh = binary16(x) rounded to nearest even,
+ * and S[r][g] = ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)) in fp32, c_o the left-to-right fp32 sum of
+ * the group's inputs 8o .. 8o+7.  Groups are 64 wide (L->group == 64).
+ *
+ * w4a8_prep_a16: the prepass.
+ *   x     fp32 [m][k] row-major, 16-byte aligned (not modified); k % 64 == 0
+ *   xh    binary16 [m][k], 16-byte aligned (written) in an interleaved order: within every
+ *         32-wide block of a row, element 8j + h holds input k = {4j, 4j+2, 16+4j, 18+4j, 4j+1,
+ *         4j+3, 17+4j, 19+4j}[h] of the block (j = 0..3)
+ *   xsf   fp32 [k/64][m] group-major (written)
+ *   W4A8_ERR_ARG: m < 0, group != 64, k not a positive multiple of 64 up to 2^20, NULL or
+ *   misaligned pointers.  W4A8_ERR_UNSUPPORTED: m * k * 2 above 2^31 - 16.
+ * w4a8_linear_a16: the prepass, then the GEMV (m == 1) or the GEMM (m > 1) on its outputs.
+ *   packed, L  SYM or AFFINE with group 64 (CODEBOOK: W4A8_ERR_UNSUPPORTED)
+ *   x, xh, xsf as for w4a8_prep_a16 (xh and xsf are written); y fp32 [m][L->n] (written)
+ * w4a8_gemm_a16: the GEMV / GEMM alone on xh and xsf from w4a8_prep_a16.
+ * Source: "TensorFold PR #3215, simd_qmm on Metal: X's group sums and half operands from a
+ * prepass", section "What this changes" (the half tiles, the prepass writing X as half and the
+ * group sums, the sums' fixed tree) and the "Perf" section (4-bit affine g64 weights, 128-row
+ * prompt tiles).
+ */
+w4a8_status w4a8_prep_a16(const float *x, int32_t m, int32_t k, int32_t group, uint16_t *xh,
+                          float *xsf, void *stream);
+w4a8_status w4a8_linear_a16(const w4a8_layout *L, const void *packed, int32_t m, const float *x,
+                            uint16_t *xh, float *xsf, float *y, void *stream);
+w4a8_status w4a8_gemm_a16(const w4a8_layout *L, const void *packed, int32_t m,
+                          const uint16_t *xh, const float *xsf, float *y, void *stream);
+
+/*
  * The exact int32 partials D[r][n][g] (definitions above) written by the same kernel code as
  * the GEMV (m == 1) or the GEMM (m > 1), with the fp32 epilogue replaced by a store of D.
  *   xsum  as from w4a8_prep (the AFFINE partial is recovered from the u - 8 codes as

@@ -192,6 +192,23 @@ def test_invalid_calls_are_rejected_on_the_host(lib):
     assert lib.w4a8_gemv_argmax(LP, p, None, p, p, f(0.0), p, p, p, p, wb, None) == ERR_ARG
     assert lib.w4a8_gemv_argmax(LP, p, p, p, p, f(0.0), None, p, p, p, wb, None) == ERR_ARG
     assert lib.w4a8_gemv_argmax(LP, p1, p, p, p, f(0.0), p, p, p, p, wb, None) == ERR_ARG
+    # fp16-activation path: group must be 64, k a multiple of 64, SYM / AFFINE only, sizes
+    assert lib.w4a8_prep_a16(p, 2, 256, 128, p, p, None) == ERR_ARG
+    assert lib.w4a8_prep_a16(p, 2, 200, 64, p, p, None) == ERR_ARG
+    assert lib.w4a8_prep_a16(p, -1, 256, 64, p, p, None) == ERR_ARG
+    assert lib.w4a8_prep_a16(None, 2, 256, 64, p, p, None) == ERR_ARG
+    assert lib.w4a8_prep_a16(p, 2, 256, 64, p1, p, None) == ERR_ARG
+    assert lib.w4a8_prep_a16(p, 1 << 20, 1 << 20, 64, p, p, None) == ERR_UNSUPPORTED
+    assert lib.w4a8_prep_a16(None, 0, 256, 64, None, None, None) == 0
+    assert lib.w4a8_linear_a16(LP, p, 2, p, p, p, None, None) == ERR_ARG          # y NULL
+    assert lib.w4a8_linear_a16(LP, p16, 2, p, p, p, p, None) == ERR_ARG           # packed
+    assert lib.w4a8_gemm_a16(LP, p, 2, None, p, p, None) == ERR_ARG
+    assert lib.w4a8_gemm_a16(LP, p, -2, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_gemm_a16(LP, p, 0, None, None, None, None) == 0
+    cbl = w4a8.packed_layout(w4a8.CODEBOOK, 128, 256, 64)
+    assert lib.w4a8_linear_a16(ctypes.byref(cbl), p, 2, p, p, p, p, None) == ERR_UNSUPPORTED
+    g128 = w4a8.packed_layout(w4a8.SYM, 128, 256, 128)
+    assert lib.w4a8_gemm_a16(ctypes.byref(g128), p, 2, p, p, p, None) == ERR_ARG
 
 @pytest.mark.skipif(_gpu_visible(), reason="checks the no-device path; would launch on a GPU")
 def test_valid_calls_without_a_device_report_device_error(lib):
@@ -208,6 +225,8 @@ def test_valid_calls_without_a_device_report_device_error(lib):
                                    p, p, p, 16, None) == ERR_DEVICE
     assert lib.w4a8_gemv_argmax(ctypes.byref(L), p, p, p, p, ctypes.c_float(0.0), p, p, p, p,
                                 16, None) == ERR_DEVICE
+    assert lib.w4a8_prep_a16(p, 2, 256, 64, p, p, None) == ERR_DEVICE
+    assert lib.w4a8_linear_a16(ctypes.byref(L), p, 2, p, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_last_error().decode() != ""
 
 
