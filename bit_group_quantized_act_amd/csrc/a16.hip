@@ -30,11 +30,15 @@
 //   two 32x32 tiles sharing one weight fragment (v_mfma_f32_32x32x16_f16, four per tile and
 //   group: weight dword j against the 16-byte word run 4j..4j+3).  The rows' halves are staged
 //   through two LDS buffers of 128 k (XOR-swizzled 16-byte units, so the 32 rows one operand
-//   read touches spread over the banks), loaded one stage ahead together with the weight
-//   chunks, scales and sums.  Each group ends with acc += sw * P (one FMA per element; the
-//   lane's column is fixed, so sw is one register) and the affine bias as a rank-1 update
-//   S x bw on the matrix unit (v_mfma_f32_32x32x2_f32).
+//   read touches spread over the banks); a stage's halves, weight chunks, scales and sums are
+//   loaded two stages ahead into a register ring (one stage of work does not cover the latency
+//   of a load under full load).  Each group ends with acc += sw * P (one FMA per element; the
+//   lane's column is fixed, so sw is one register); the affine bias of a stage's two groups is
+//   one update on the matrix unit (v_mfma_f32_32x32x2_f32, k slot h = group 2s + h: rows' sums
+//   times the channel's bias).
 #include "w4a8_kernels.h"
+
+#include <type_traits>
 
 namespace w4a8 {
 namespace {
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(64 * kA16Waves) void gemv_a16_kernel(const uint8_t 
             const int g = g0 + s * kA16Waves;
             if (g < ng) {
                 const uint32_t *xg = xw + 32 * g;        // the group's 64 halves: wave-uniform
-                float dot = 0.0f;
+                float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // one chain per code dword
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -157,12 +161,13 @@ __global__ __launch_bounds__(64 * kA16Waves) void gemv_a16_kernel(const uint8_t 
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const uint32_t wp = half_pair<FMT>(w, e);
-                            dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, wp),
-                                                         __builtin_bit_cast(h2_t, xg[16 * h + 4 * j + e]),
-                                                         dot, false);
+                            d4[j] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, wp),
+                                                           __builtin_bit_cast(h2_t, xg[16 * h + 4 * j + e]),
+                                                           d4[j], false);
                         }
                     }
                 }
+                const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
                 const float sw = half_bits_to_float(meta[s] & 0xFFFFu);
                 acc = fmaf(sw, dot, acc);
                 if (FMT == kFmtAffine) acc = fmaf(half_bits_to_float(meta[s] >> 16), xsf[g], acc);
@@ -187,6 +192,17 @@ __global__ __launch_bounds__(64 * kA16Waves) void gemv_a16_kernel(const uint8_t 
 
 constexpr int kA16BN = 128;                        // channels per workgroup (4 wavefronts x 32)
 constexpr int kA16SK = 128;                        // k per LDS stage (two groups)
+
+// Everything one LDS stage needs from memory, loaded two stages ahead: the rows' halves (four
+// 16-byte units per thread), the lane's weight chunk of each of the stage's two groups, those
+// groups' scale (and bias) of the lane's channel, and each tile's row sums of the lane's group
+// (group 2s for lanes 0-31, 2s+1 for lanes 32-63: the two k slots of the bias update).
+struct StageRegs {
+    v4i a[4];
+    v4i b[2];
+    uint32_t meta[2];
+    float sum[2];
+};
 
 template <int FMT>
 __global__ __launch_bounds__(256, 2) void gemm_a16_kernel(const uint8_t *__restrict__ packed,
@@ -225,68 +241,67 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_kernel(const uint8_t *__restr
     const rsrc_t rx = make_rsrc(xh, (uint64_t)m * k * 2);
     const rsrc_t rs = make_rsrc(xsf, (uint64_t)ng * m * 4);
 
-    // stage loads: activation units (4 per thread), the lane's two weight chunks, the two
-    // groups' scale (and bias) of the lane's channel, the two groups' sums of the tiles' rows
-    auto load_a = [&](int s, v4i (&a)[4]) {
+    auto load_stage = [&](int s, StageRegs &r) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rr = i * 16 + (tid >> 4), u = tid & 15;
             const int kk = s * kA16SK + 8 * u;
             const bool ok = (m0 + rr < m) && (kk < k);
-            a[i] = ld128(rx, ok ? ((m0 + rr) * k + kk) * 2 : kOOB);
+            r.a[i] = ld128(rx, ok ? ((m0 + rr) * k + kk) * 2 : kOOB);
         }
-    };
-    auto load_b = [&](int s, v4i (&b)[2], uint32_t (&mt2)[2], float (&sv)[2][2]) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const int g = 2 * s + st;
-            const int c = 2 * g + half;
-            b[st] = ld128(rc, g < ng ? (c * 64 + prow) * 16 : kOOB);
+            r.b[st] = ld128(rc, g < ng ? ((2 * g + half) * 64 + prow) * 16 : kOOB);
             const int mo = g < ng ? (((g >> 2) * 64 + prow) * 4 + (g & 3)) * MB : kOOB;
-            mt2[st] = (MB == 4) ? ld32(rm, mo) : ld16(rm, mo);
+            r.meta[st] = (MB == 4) ? ld32(rm, mo) : ld16(rm, mo);
+        }
+        const int gs = 2 * s + half;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int row = m0 + 32 * t + r32;
-                const bool ok = FMT == kFmtAffine && g < ng && half == 0 && row < m;
-                sv[st][t] = __builtin_bit_cast(float, ld32(rs, ok ? (g * m + row) * 4 : kOOB));
-            }
+        for (int t = 0; t < 2; ++t) {
+            const int row = m0 + 32 * t + r32;
+            const bool ok = FMT == kFmtAffine && gs < ng && row < m;
+            r.sum[t] = __builtin_bit_cast(float, ld32(rs, ok ? (gs * m + row) * 4 : kOOB));
         }
     };
-    auto store_a = [&](int buf, const v4i (&a)[4]) {
+    auto store_a = [&](int buf, const StageRegs &r) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rr = i * 16 + (tid >> 4), u = tid & 15;
-            lds[buf][rr * 16 + (u ^ (rr & 7))] = a[i];
+            lds[buf][rr * 16 + (u ^ (rr & 7))] = r.a[i];
         }
     };
 
-    v16f acc[2], part[2];
+    v16f acc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { acc[t][e] = 0.0f; part[t][e] = 0.0f; }
+        for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
     }
-    v4i a_nx[4], b_cur[2], b_nx[2];
-    uint32_t m_cur[2], m_nx[2];
-    float s_cur[2][2], s_nx[2][2];
-    load_a(0, a_nx);
-    load_b(0, b_cur, m_cur, s_cur);
-    store_a(0, a_nx);
+    const v16f zero16 = acc[0];
+
+    // stage s reads LDS buffer s & 1 and its loads sit in ring slot s & 1; at stage s the slot
+    // is refilled with stage s + 2, and at its end stage s + 1's halves go to the other buffer
+    StageRegs ring[2];
+    load_stage(0, ring[0]);
+    if (nstage > 1) load_stage(1, ring[1]);
+    store_a(0, ring[0]);
     __syncthreads();
 
-    for (int s = 0; s < nstage; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nstage) {
-            load_a(s + 1, a_nx);
-            load_b(s + 1, b_nx, m_nx, s_nx);
-        }
+    auto stage = [&](auto slot_c, int s) {
+        constexpr int slot = decltype(slot_c)::value;
+        const v4i b[2] = {ring[slot].b[0], ring[slot].b[1]};
+        const uint32_t meta[2] = {ring[slot].meta[0], ring[slot].meta[1]};
+        const float sum[2] = {ring[slot].sum[0], ring[slot].sum[1]};
+        if (s + 2 < nstage) load_stage(s + 2, ring[slot]);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const int g = 2 * s + st;
             if (g >= ng) break;
+            v16f part[2] = {zero16, zero16};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t w = static_cast<uint32_t>(b_cur[st][j]) ^ 0x88888888u;
+                const uint32_t w = static_cast<uint32_t>(b[st][j]) ^ 0x88888888u;
                 const v4i bw4 = {static_cast<int>(half_pair<FMT>(w, 0)),
                                  static_cast<int>(half_pair<FMT>(w, 1)),
                                  static_cast<int>(half_pair<FMT>(w, 2)),
@@ -296,35 +311,31 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_kernel(const uint8_t *__restr
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int rr = 32 * t + r32;
-                    const v8h_t aop = __builtin_bit_cast(v8h_t, lds[buf][rr * 16 + (unit ^ (rr & 7))]);
+                    const v8h_t aop =
+                        __builtin_bit_cast(v8h_t, lds[slot][rr * 16 + (unit ^ (rr & 7))]);
                     part[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop, part[t], 0, 0, 0);
                 }
             }
-            const float sw = half_bits_to_float(m_cur[st] & 0xFFFFu);
-            const float bw = (FMT == kFmtAffine && half == 0) ? half_bits_to_float(m_cur[st] >> 16)
-                                                               : 0.0f;
+            const float sw = half_bits_to_float(meta[st] & 0xFFFFu);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    acc[t][e] = fmaf(sw, part[t][e], acc[t][e]);
-                    part[t][e] = 0.0f;
-                }
-                if (FMT == kFmtAffine)
-                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(s_cur[st][t], bw, acc[t], 0, 0, 0);
+                for (int e = 0; e < 16; ++e) acc[t][e] = fmaf(sw, part[t][e], acc[t][e]);
             }
         }
-        if (s + 1 < nstage) {
-            store_a(buf ^ 1, a_nx);
+        if (FMT == kFmtAffine) {
+            // both groups' bias at once: k slot h of the update is group 2s + h
+            const float bw = half_bits_to_float(meta[half] >> 16);
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                b_cur[st] = b_nx[st];
-                m_cur[st] = m_nx[st];
-                s_cur[st][0] = s_nx[st][0];
-                s_cur[st][1] = s_nx[st][1];
-            }
+            for (int t = 0; t < 2; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(sum[t], bw, acc[t], 0, 0, 0);
         }
+        if (s + 1 < nstage) store_a(slot ^ 1, ring[slot ^ 1]);
         __syncthreads();
+    };
+    for (int s = 0; s < nstage; s += 2) {
+        stage(std::integral_constant<int, 0>{}, s);
+        if (s + 1 < nstage) stage(std::integral_constant<int, 1>{}, s + 1);
     }
 
     if (!wact || col >= geom.n) return;
