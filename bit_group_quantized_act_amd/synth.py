@@ -210,3 +210,68 @@ def algorithmic_bytes(cfg: LayerConfig, fused_prep: bool = False) -> int:
 
 def int_ops(cfg: LayerConfig) -> int:
     return 2 * cfg.m * cfg.n * cfg.k
+
+
+# ---- prefill attention over a cached int8 segment
+#
+# Gemma-style heads: head_dim 256, 8 query heads sharing 2 key/value heads, a 256-query prefill
+# chunk against a 1024-slot cache (the pages' 1068-token prompt), scores scaled by 1/sqrt(256).
+# The cache holds int8 keys and values with one fp32 scale per 32 of the head dimension (the
+# cache writer's quantization, done here as input preparation: scale = max|v| / 127, codes
+# rounded to nearest even).  A sliding-window layer keeps `sink` positions and a rolled ring of
+# the most recent ones.  Streams: 0 = Q, 1 = K, 2 = V, 3 = ring rotation.
+
+@dataclass(frozen=True)
+class AttnConfig:
+    name: str
+    nh: int
+    nkvh: int
+    nq: int
+    nkv: int
+    d: int
+    window: int          # 0: global layer
+    sink: int            # slots exempt from the window
+    rolled: bool         # the cache is a ring (slot order is not position order)
+    cfg_id: int
+    pos0: int = -1       # first query's position (-1: right after the cache)
+
+
+ATTN_CONFIGS = {
+    "A1": AttnConfig("A1", 8, 2, 256, 1024, 256, 0, 0, False, 11),
+    "A2": AttnConfig("A2", 8, 2, 256, 1024, 256, 512, 4, True, 12, pos0=1500),
+}
+
+
+def attn_config(name: str, **overrides) -> AttnConfig:
+    return replace(ATTN_CONFIGS[name], **overrides)
+
+
+def _quantize_groups(v: np.ndarray, group: int):
+    vg = v.reshape(*v.shape[:-1], v.shape[-1] // group, group)
+    s = (np.abs(vg).max(axis=-1) / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s[..., None] > 0, np.rint(vg / np.where(s[..., None] > 0, s[..., None], 1)),
+                     0)
+    return np.clip(q, -127, 127).astype(np.int8).reshape(v.shape), s
+
+
+def make_attn(name_or_cfg, **overrides):
+    """Inputs of one attention call: dict(cfg, q fp32 [nh, nq, d], k8/v8 int8 [nkvh, nkv, d],
+    ks/vs fp32 [nkvh, nkv, d/32], kvpos int32 [nkv], pos0, scale)."""
+    cfg = name_or_cfg if isinstance(name_or_cfg, AttnConfig) else attn_config(name_or_cfg,
+                                                                              **overrides)
+    q = rng(cfg.cfg_id, 0, 0).standard_normal((cfg.nh, cfg.nq, cfg.d), dtype=np.float32)
+    kf = rng(cfg.cfg_id, 0, 1).standard_normal((cfg.nkvh, cfg.nkv, cfg.d), dtype=np.float32)
+    vf = rng(cfg.cfg_id, 0, 2).standard_normal((cfg.nkvh, cfg.nkv, cfg.d), dtype=np.float32)
+    k8, ks = _quantize_groups(kf, 32)
+    v8, vs = _quantize_groups(vf, 32)
+    pos0 = cfg.pos0 if cfg.pos0 >= 0 else cfg.nkv
+    if cfg.rolled:
+        ring = cfg.nkv - cfg.sink
+        recent = np.arange(pos0 - ring, pos0, dtype=np.int64)
+        shift = int(rng(cfg.cfg_id, 0, 3).integers(0, ring))
+        kvpos = np.concatenate([np.arange(cfg.sink), np.roll(recent, shift)]).astype(np.int32)
+    else:
+        kvpos = np.arange(cfg.nkv, dtype=np.int32)
+    return dict(cfg=cfg, q=q, k8=k8, ks=ks, v8=v8, vs=vs, kvpos=kvpos, pos0=pos0,
+                scale=1.0 / np.sqrt(cfg.d))

@@ -61,9 +61,15 @@ def _load():
     lib.oracle_float_to_half.restype = ctypes.c_uint16
     lib.oracle_prep_a16.argtypes = [P, i64, i64, P, P]
     lib.oracle_linear_a16.argtypes = [i32, P, P, P, P, i64, i64, i32, P, P, i64, P, P]
+    lib.oracle_attn_requant_k.argtypes = [P, P, i64, i64, i32, P, P]
+    lib.oracle_attn_int8.argtypes = [P, P, i64, i64, P, P, P, P, P, i64, i64, i64, i32, i64, i32,
+                                     i32, ctypes.c_double, P, P, P]
+    lib.oracle_attn_exact.argtypes = [P, i64, i64, P, P, P, P, P, i64, i64, i64, i32, i32, i64,
+                                      i32, i32, ctypes.c_double, P]
     for f in ("oracle_rotate", "oracle_quantize", "oracle_prep", "oracle_partials",
               "oracle_linear", "oracle_glu", "oracle_softcap_argmax", "oracle_prep_a16",
-              "oracle_linear_a16", "oracle_num_threads"):
+              "oracle_linear_a16", "oracle_attn_requant_k", "oracle_attn_int8",
+              "oracle_attn_exact", "oracle_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -245,3 +251,65 @@ def linear_a16(fmt: int, codes, scales_f16, xh, xsf, group: int = 64, bias_f16=N
                                      group, _ptr(xh), _ptr(xsf), m, _ptr(y), _ptr(t)),
            "linear_a16")
     return (y, t) if with_terms else y
+
+
+# ---- prefill attention over the cached int8 segment
+
+ATTN_GROUP = 32          # width of the cache's key and value scale groups (head_dim / 32 each)
+
+
+def attn_requant_k(k8, ks, gk: int = ATTN_GROUP):
+    """Keys to one flat scale per vector: (kq int8 [.., n, d], sk float32 [.., n])."""
+    k8 = np.ascontiguousarray(k8, dtype=np.int8)
+    ks = np.ascontiguousarray(ks, dtype=np.float32)
+    d = k8.shape[-1]
+    n = k8.size // d
+    kq = np.empty_like(k8)
+    sk = np.empty(k8.shape[:-1], np.float32)
+    _check(_load().oracle_attn_requant_k(_ptr(k8), _ptr(ks), n, d, gk, _ptr(kq), _ptr(sk)),
+           "attn_requant_k")
+    return kq, sk
+
+
+def attn_quant_q(q):
+    """Queries to int8 with one flat scale per row: (q8 [.., d], sq [..])."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    d = q.shape[-1]
+    q8, sq, _ = prep(q.reshape(-1, d), d, 0)
+    return q8.reshape(q.shape), sq.reshape(q.shape[:-1])
+
+
+def attn_int8(q8, sq, kq, sk, v8, vs, kvpos, pos0: int, window: int = 0, sink: int = 0,
+              scale: float = 1.0, gv: int = ATTN_GROUP):
+    """The int8 method: (o [nh, nq, d] unnormalized, m [nh, nq], l [nh, nq]) in fp64."""
+    q8 = np.ascontiguousarray(q8, dtype=np.int8)
+    nh, nq, d = q8.shape
+    kq = np.ascontiguousarray(kq, dtype=np.int8)
+    nkvh, nkv, _ = kq.shape
+    args = [np.ascontiguousarray(a, dtype=t) for a, t in ((sq, np.float32), (sk, np.float32),
+                                                           (v8, np.int8), (vs, np.float32),
+                                                           (kvpos, np.int32))]
+    o = np.empty((nh, nq, d), np.float64)
+    m = np.empty((nh, nq), np.float64)
+    l = np.empty((nh, nq), np.float64)
+    _check(_load().oracle_attn_int8(_ptr(q8), _ptr(args[0]), nh, nq, _ptr(kq), _ptr(args[1]),
+                                    _ptr(args[2]), _ptr(args[3]), _ptr(args[4]), nkvh, nkv, d,
+                                    gv, pos0, window, sink, float(scale), _ptr(o), _ptr(m),
+                                    _ptr(l)), "attn_int8")
+    return o, m, l
+
+
+def attn_exact(q, k8, ks, v8, vs, kvpos, pos0: int, window: int = 0, sink: int = 0,
+               scale: float = 1.0, gk: int = ATTN_GROUP, gv: int = ATTN_GROUP):
+    """Plain fp64 attention on unquantized q and the dequantized cache: out [nh, nq, d]."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    nh, nq, d = q.shape
+    k8 = np.ascontiguousarray(k8, dtype=np.int8)
+    nkvh, nkv, _ = k8.shape
+    ks, v8, vs, kvpos = (np.ascontiguousarray(a, dtype=t) for a, t in (
+        (ks, np.float32), (v8, np.int8), (vs, np.float32), (kvpos, np.int32)))
+    out = np.empty((nh, nq, d), np.float64)
+    _check(_load().oracle_attn_exact(_ptr(q), nh, nq, _ptr(k8), _ptr(ks), _ptr(v8), _ptr(vs),
+                                     _ptr(kvpos), nkvh, nkv, d, gk, gv, pos0, window, sink,
+                                     float(scale), _ptr(out)), "attn_exact")
+    return out

@@ -54,6 +54,20 @@
  *              the nearest binary16 (ties to even); S[r][g] = that tree over x in fp32 (fma with
  *              a unit factor is an add); y[r][n] = sum over g of ( sw * sum_k w_int * xh
  *              + bw * S ) in fp64, w_int the format's integer weight (affine: unsigned u).
+ *   attention  "cactus PR #697", section "Prefill attention": the cached-int8 KV segment of a
+ *              prefill chunk (fully visible by causality) with int8 QK products under one flat
+ *              scale per query row and per key vector (the keys' group-scale ratios requantized
+ *              into their int8 values), a masked softmax over 64-key blocks carried online, and
+ *              an unsigned 8-bit P quantized per (row, value group, block) with the value group's
+ *              scale folded into it; sliding window with attention-sink exemption; the new-token
+ *              segment continues from the running statistics.  Readings taken here: Q codes as
+ *              the activation quantization with one group per row; sk = max of the key's group
+ *              scales and kq = round-half-even(k8 * fp32(ks_g / sk)) in fp32; logits
+ *              scale * sq * sk * sum q8*kq; per block m' = max(m, block max), alpha = e^(m-m'),
+ *              P = e^(S-m'), l = alpha*l + sum P; per value group g, P'_j = P_j * vs[j][g],
+ *              sp = max P' / 255, u_j = round-half-even(P'_j / sp), O_g = alpha*O_g +
+ *              sp * sum_j u_j * v8[j]; a slot at position p is seen by the query at t when
+ *              p >= 0 and (no window, or p < sink, or t - p < window).
  *   lm_head    "cactus-compute/engine PR #750: Metal Support", the commit list (the orthogonal
  *              lm_head with its softcap fused into a GPU argmax / sampling tail) and the file
  *              table (GPU-side sampling and argmax helpers); "cactus PR #697", the lm_head commit
@@ -492,6 +506,181 @@ int oracle_linear_a16(int32_t format, const uint8_t *codes, const uint16_t *scal
                 t[r * n + c] = mag;
         }
         free(w);
+    }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- prefill attention ---- */
+
+/*
+ * Keys to one flat scale per vector: sk[j] = max_g ks[j][g]; kq[j][i] = round-half-even of
+ * k8[j][i] * fp32(ks[j][g] / sk[j]) in fp32 (0 when sk == 0).  Layouts k8, kq [n][d],
+ * ks [n][d/gk], sk [n].
+ */
+int oracle_attn_requant_k(const int8_t *k8, const float *ks, int64_t n, int64_t d, int32_t gk,
+                          int8_t *kq, float *sk)
+{
+    if (gk <= 0 || d % gk != 0 || n < 0)
+        return ORACLE_BAD_ARGS;
+    int64_t ng = d / gk;
+    for (int64_t j = 0; j < n; ++j) {
+        float mx = 0.0f;
+        for (int64_t g = 0; g < ng; ++g)
+            if (ks[j * ng + g] > mx)
+                mx = ks[j * ng + g];
+        sk[j] = mx;
+        for (int64_t i = 0; i < d; ++i) {
+            float v = 0.0f;
+            if (mx > 0.0f) {
+                float ratio = ks[j * ng + i / gk] / mx;
+                v = rintf((float)k8[j * d + i] * ratio);
+            }
+            kq[j * d + i] = (int8_t)v;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Is the cache slot at position p visible to the query at position t? */
+static int oracle_attn_visible(int64_t t, int64_t p, int32_t window, int32_t sink)
+{
+    if (p < 0 || p > t)
+        return 0;
+    if (window <= 0 || p < sink)
+        return 1;
+    return t - p < window;
+}
+
+/*
+ * The int8 method in fp64, blocks of 64 slots in slot order.  Inputs: q8 [nh][nq][d], sq
+ * [nh][nq]; kq [nkvh][nkv][d], sk [nkvh][nkv]; v8 [nkvh][nkv][d], vs [nkvh][nkv][d/gv];
+ * kvpos [nkv]; query i sits at position pos0 + i; query head h reads key/value head
+ * h / (nh / nkvh).  Outputs: the running state o [nh][nq][d] (unnormalized), m, l [nh][nq]
+ * (m = -inf and l = 0 where no slot is visible).
+ */
+int oracle_attn_int8(const int8_t *q8, const float *sq, int64_t nh, int64_t nq,
+                     const int8_t *kq, const float *sk, const int8_t *v8, const float *vs,
+                     const int32_t *kvpos, int64_t nkvh, int64_t nkv, int64_t d, int32_t gv,
+                     int64_t pos0, int32_t window, int32_t sink, double scale,
+                     double *o, double *m, double *l)
+{
+    if (nh <= 0 || nkvh <= 0 || nh % nkvh != 0 || gv <= 0 || d % gv != 0)
+        return ORACLE_BAD_ARGS;
+    int64_t ng = d / gv, per = nh / nkvh;
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+    for (int64_t h = 0; h < nh; ++h) {
+        for (int64_t i = 0; i < nq; ++i) {
+            int64_t kh = h / per, t = pos0 + i;
+            const int8_t *qr = q8 + (h * nq + i) * d;
+            double *orow = o + (h * nq + i) * d;
+            double mrun = -INFINITY, lrun = 0.0;
+            double sv[64], pv[64], pg[64];
+            int vis[64];
+            for (int64_t c = 0; c < d; ++c)
+                orow[c] = 0.0;
+            for (int64_t j0 = 0; j0 < nkv; j0 += 64) {
+                int64_t nb = (nkv - j0 < 64) ? nkv - j0 : 64;
+                double mb = -INFINITY;
+                for (int64_t jj = 0; jj < nb; ++jj) {
+                    int64_t j = j0 + jj;
+                    vis[jj] = oracle_attn_visible(t, kvpos[j], window, sink);
+                    if (!vis[jj])
+                        continue;
+                    const int8_t *kr = kq + (kh * nkv + j) * d;
+                    int64_t dot = 0;
+                    for (int64_t c = 0; c < d; ++c)
+                        dot += (int64_t)qr[c] * (int64_t)kr[c];
+                    sv[jj] = scale * (double)sq[h * nq + i] * (double)sk[kh * nkv + j] * (double)dot;
+                    if (sv[jj] > mb)
+                        mb = sv[jj];
+                }
+                if (mb == -INFINITY)
+                    continue;                                   /* nothing visible here */
+                double mnew = mrun > mb ? mrun : mb;
+                double alpha = exp(mrun - mnew);                /* 0 while mrun = -inf */
+                double psum = 0.0;
+                for (int64_t jj = 0; jj < nb; ++jj) {
+                    pv[jj] = vis[jj] ? exp(sv[jj] - mnew) : 0.0;
+                    psum += pv[jj];
+                }
+                lrun = lrun * alpha + psum;
+                for (int64_t g = 0; g < ng; ++g) {
+                    double mx = 0.0;
+                    for (int64_t jj = 0; jj < nb; ++jj) {
+                        pg[jj] = pv[jj] * (double)vs[(kh * nkv + j0 + jj) * ng + g];
+                        if (pg[jj] > mx)
+                            mx = pg[jj];
+                    }
+                    double sp = mx / 255.0;
+                    for (int64_t c = g * gv; c < (g + 1) * gv; ++c) {
+                        double acc = 0.0;
+                        for (int64_t jj = 0; jj < nb; ++jj) {
+                            double u = mx > 0.0 ? oracle_round_half_even(pg[jj] / sp) : 0.0;
+                            acc += u * (double)v8[(kh * nkv + j0 + jj) * d + c];
+                        }
+                        orow[c] = orow[c] * alpha + sp * acc;
+                    }
+                }
+                mrun = mnew;
+            }
+            m[h * nq + i] = mrun;
+            l[h * nq + i] = lrun;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Plain attention in fp64 on the unquantized queries and the dequantized cache (k8 * ks_g,
+ * v8 * vs_g): out[h][i] = sum_j softmax_j(scale * q . k_j) v_j over the visible slots (0 when
+ * none is visible).  The reference the int8 method is measured against.
+ */
+int oracle_attn_exact(const float *q, int64_t nh, int64_t nq, const int8_t *k8, const float *ks,
+                      const int8_t *v8, const float *vs, const int32_t *kvpos, int64_t nkvh,
+                      int64_t nkv, int64_t d, int32_t gk, int32_t gv, int64_t pos0,
+                      int32_t window, int32_t sink, double scale, double *out)
+{
+    if (nh <= 0 || nkvh <= 0 || nh % nkvh != 0 || gk <= 0 || gv <= 0 || d % gk || d % gv)
+        return ORACLE_BAD_ARGS;
+    int64_t per = nh / nkvh, ngk = d / gk, ngv = d / gv;
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+    for (int64_t h = 0; h < nh; ++h) {
+        for (int64_t i = 0; i < nq; ++i) {
+            int64_t kh = h / per, t = pos0 + i;
+            const float *qr = q + (h * nq + i) * d;
+            double *orow = out + (h * nq + i) * d;
+            double *sc = (double *)malloc((size_t)(nkv > 0 ? nkv : 1) * sizeof(double));
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < nkv; ++j) {
+                sc[j] = -INFINITY;
+                if (!oracle_attn_visible(t, kvpos[j], window, sink))
+                    continue;
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    dot += (double)qr[c] * (double)k8[(kh * nkv + j) * d + c] *
+                           (double)ks[(kh * nkv + j) * ngk + c / gk];
+                sc[j] = scale * dot;
+                if (sc[j] > mx)
+                    mx = sc[j];
+            }
+            for (int64_t c = 0; c < d; ++c)
+                orow[c] = 0.0;
+            if (mx != -INFINITY) {
+                double den = 0.0;
+                for (int64_t j = 0; j < nkv; ++j) {
+                    if (sc[j] == -INFINITY)
+                        continue;
+                    double p = exp(sc[j] - mx);
+                    den += p;
+                    for (int64_t c = 0; c < d; ++c)
+                        orow[c] += p * (double)v8[(kh * nkv + j) * d + c] *
+                                   (double)vs[(kh * nkv + j) * ngv + c / gv];
+                }
+                for (int64_t c = 0; c < d; ++c)
+                    orow[c] /= den;
+            }
+            free(sc);
+        }
     }
     return ORACLE_OK;
 }

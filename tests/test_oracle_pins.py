@@ -661,3 +661,127 @@ def test_a16_linear_equals_the_int8_path_on_exactly_quantized_inputs():
     xh, xsf = oracle.prep_a16(x)
     y16, _ = oracle.linear_a16(oracle.FORMAT_AFFINE, codes, scales, xh, xsf, g, bias_f16=bias)
     np.testing.assert_allclose(y16, y8, rtol=0, atol=1e-12 * t8.max())
+
+
+# ---- prefill attention over the cached int8 segment (PR #697's hybrid attention)
+
+def _np_attention(q, k, v, kvpos, pos0, window, sink, scale):
+    """Independent numpy attention with the window / sink mask written out per pair."""
+    nh, nq, d = q.shape
+    nkvh, nkv, _ = k.shape
+    out = np.zeros((nh, nq, d))
+    for h in range(nh):
+        kh = h // (nh // nkvh)
+        s = scale * (q[h].astype(np.float64) @ k[kh].T)
+        t = pos0 + np.arange(nq)[:, None]
+        p = kvpos[None, :].astype(np.int64)
+        vis = (p >= 0) & (p <= t)
+        if window > 0:
+            vis &= (p < sink) | (t - p < window)
+        s = np.where(vis, s, -np.inf)
+        mx = s.max(axis=1, keepdims=True)
+        e = np.where(vis, np.exp(s - np.where(np.isfinite(mx), mx, 0)), 0.0)
+        den = e.sum(axis=1, keepdims=True)
+        out[h] = np.where(den > 0, (e @ v[kh]) / np.where(den > 0, den, 1), 0.0)
+    return out
+
+
+def _deq(c8, sc, g=32):
+    return c8.astype(np.float64) * np.repeat(sc.astype(np.float64), g, axis=-1)
+
+
+@pytest.mark.parametrize("name,over", [("A1", dict(nq=40, nkv=150, d=64)),
+                                       ("A2", dict(nq=40, nkv=150, d=64, window=70, sink=3,
+                                                   pos0=400))])
+def test_attn_exact_matches_numpy_attention(name, over):
+    from bit_group_quantized_act_amd import synth
+    A = synth.make_attn(name, nh=4, **over)
+    c = A["cfg"]
+    got = oracle.attn_exact(A["q"], A["k8"], A["ks"], A["v8"], A["vs"], A["kvpos"], A["pos0"],
+                            c.window, c.sink, A["scale"])
+    want = _np_attention(A["q"], _deq(A["k8"], A["ks"]), _deq(A["v8"], A["vs"]), A["kvpos"],
+                         A["pos0"], c.window, c.sink, A["scale"])
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
+    if c.window:
+        # control: a window read one position wider changes the output
+        wide = _np_attention(A["q"], _deq(A["k8"], A["ks"]), _deq(A["v8"], A["vs"]),
+                             A["kvpos"], A["pos0"], c.window + 1, c.sink, A["scale"])
+        assert np.abs(wide - got).max() > 1e-6
+
+
+def test_attn_requant_k_golden():
+    # hand-derived: group 1 has half the flat scale, so its codes are halved, ties to even
+    k8 = np.zeros((1, 64), np.int8)
+    vals = [3, 5, -3, -5, 127, 1, 7, -127]
+    k8[0, 32:40] = vals
+    k8[0, 0:4] = [9, -9, 127, -128 + 1]
+    ks = np.array([[1.0, 0.5]], np.float32)
+    kq, sk = oracle.attn_requant_k(k8, ks)
+    assert sk[0] == np.float32(1.0)
+    assert list(kq[0, 32:40]) == [2, 2, -2, -2, 64, 0, 4, -64]       # 1.5->2, 2.5->2, 63.5->64
+    assert list(kq[0, 0:4]) == [9, -9, 127, -127]                   # ratio 1: unchanged
+    kq2, sk2 = oracle.attn_requant_k(np.full((1, 32), 5, np.int8), np.zeros((1, 1), np.float32))
+    assert sk2[0] == 0 and not kq2.any()
+
+
+def _method(A, window=None, sink=None):
+    c = A["cfg"]
+    q8, sq = oracle.attn_quant_q(A["q"])
+    kq, sk = oracle.attn_requant_k(A["k8"], A["ks"])
+    return oracle.attn_int8(q8, sq, kq, sk, A["v8"], A["vs"], A["kvpos"], A["pos0"],
+                            c.window if window is None else window,
+                            c.sink if sink is None else sink, A["scale"])
+
+
+@pytest.mark.parametrize("name,over", [("A1", dict(nq=40, nkv=300, d=128)),
+                                       ("A2", dict(nq=40, nkv=300, d=128, window=170, sink=4,
+                                                   pos0=700))])
+def test_attn_int8_method_close_to_exact_attention(name, over):
+    # int8 queries and keys with one flat scale per row / vector move Gaussian scores enough
+    # for about 1% relative error per output row (mean); wrong scales, masks or block merges
+    # give errors of tens of percent
+    from bit_group_quantized_act_amd import synth
+    A = synth.make_attn(name, nh=4, **over)
+    c = A["cfg"]
+    o, m, l = _method(A)
+    got = o / l[..., None]
+    want = oracle.attn_exact(A["q"], A["k8"], A["ks"], A["v8"], A["vs"], A["kvpos"], A["pos0"],
+                             c.window, c.sink, A["scale"])
+    rel = np.linalg.norm(got - want, axis=-1) / np.linalg.norm(want, axis=-1)
+    assert rel.max() < 3e-2 and rel.mean() < 1.5e-2, (rel.max(), rel.mean())
+
+
+def test_attn_int8_uniform_attention_within_the_pages_bound():
+    # adversarial uniform attention (every score equal): only the quantization of P acts; the
+    # pages bound the method's worst-case relative error near 0.6-0.7%
+    from bit_group_quantized_act_amd import synth
+    A = synth.make_attn("A1", nh=2, nq=4, nkv=500, d=128)
+    A = dict(A, q=np.zeros_like(A["q"]))
+    o, m, l = _method(A)
+    want = oracle.attn_exact(A["q"], A["k8"], A["ks"], A["v8"], A["vs"], A["kvpos"], A["pos0"],
+                             0, 0, A["scale"])
+    got = o / l[..., None]
+    rel = np.linalg.norm(got - want, axis=-1) / np.linalg.norm(want, axis=-1)
+    assert rel.max() < 7e-3, rel.max()
+
+
+def test_attn_int8_closed_forms():
+    from bit_group_quantized_act_amd import synth
+    A = synth.make_attn("A1", nh=2, nq=8, nkv=130, d=64)
+    # one visible slot: P = 1, its code 255, so the output is that slot's dequantized value row
+    one = A["kvpos"].copy()
+    one[:] = -1
+    one[77] = 5
+    B = dict(A, kvpos=one, pos0=10)
+    o, m, l = _method(B)
+    v77 = _deq(A["v8"][:, 77], A["vs"][:, 77])                  # [nkvh, d]
+    np.testing.assert_allclose(o / l[..., None], np.repeat(v77[:, None, :], 8, axis=1)
+                               .repeat(1, axis=0)[[0, 1]], rtol=1e-12, atol=1e-15)
+    # uniform attention (zero queries) with one value scale: every code is 255, so the output
+    # is the mean of the visible value rows exactly
+    C = dict(A, q=np.zeros_like(A["q"]), vs=np.full_like(A["vs"], 0.01))
+    o, m, l = _method(C)
+    mean = (A["v8"].astype(np.float64) * np.float64(np.float32(0.01))).mean(axis=1)
+    np.testing.assert_allclose(o / l[..., None], mean[:, None, :].repeat(8, axis=1),
+                               rtol=1e-12, atol=1e-15)
+    assert np.all(l == 130.0) and np.all(m == 0.0)
