@@ -496,6 +496,109 @@ w4a8_status w4a8_linear_a16(const w4a8_layout *L, const void *packed, int32_t m,
                     "fp16-activation linear launch");
 }
 
+namespace {
+w4a8_status check_attn_layout(const w4a8_attn_layout *AL) {
+    if (!AL) return fail(W4A8_ERR_ARG, "attention layout is NULL");
+    w4a8_attn_layout ref;
+    if (w4a8_attn_layout_init(AL->nkvh, AL->nkv, AL->d, &ref) != W4A8_OK ||
+        std::memcmp(&ref, AL, sizeof(ref)) != 0)
+        return fail(W4A8_ERR_ARG, "attention layout was not filled by w4a8_attn_layout_init");
+    return W4A8_OK;
+}
+
+w4a8::AttnGeom attn_geom_of(const w4a8_attn_layout *AL) {
+    return w4a8::AttnGeom{AL->nkvh, AL->nkv, AL->d, AL->nblk, AL->off_kq, AL->off_sk,
+                          AL->off_pos, AL->off_vt, AL->off_sv, AL->off_vsum};
+}
+}  // namespace
+
+w4a8_status w4a8_attn_layout_init(int32_t nkvh, int32_t nkv, int32_t d, w4a8_attn_layout *AL) {
+    if (!AL) return fail(W4A8_ERR_ARG, "AL is NULL");
+    if (d != 64 && d != 128 && d != 256)
+        return fail(W4A8_ERR_ARG, "head dimension %d is not 64, 128 or 256", d);
+    if (nkvh < 1 || nkvh > 1024) return fail(W4A8_ERR_ARG, "nkvh = %d is outside [1, 1024]", nkvh);
+    if (nkv < 1 || nkv > (1 << 24)) return fail(W4A8_ERR_ARG, "nkv = %d is outside [1, 2^24]", nkv);
+    std::memset(AL, 0, sizeof(*AL));
+    AL->nkvh = nkvh;
+    AL->nkv = nkv;
+    AL->d = d;
+    AL->nblk = (nkv + 63) / 64;
+    const uint64_t slots = static_cast<uint64_t>(nkvh) * AL->nblk * 64;
+    uint64_t off = 0;
+    AL->off_kq = off;   off = round_up(off + slots * d, 256);
+    AL->off_sk = off;   off = round_up(off + slots * 4, 256);
+    AL->off_pos = off;  off = round_up(off + slots * 4, 256);
+    AL->off_vt = off;   off = round_up(off + slots * d, 256);
+    AL->off_sv = off;   off = round_up(off + slots * (d / 32) * 4, 256);
+    AL->off_vsum = off; off = round_up(off + static_cast<uint64_t>(nkvh) * AL->nblk * d * 4, 256);
+    AL->bytes = off;
+    return W4A8_OK;
+}
+
+w4a8_status w4a8_attn_pack_kv(const w4a8_attn_layout *AL, const int8_t *k8, const float *ks,
+                              const int8_t *v8, const float *vs, const int32_t *kvpos,
+                              void *packed, void *stream) {
+    w4a8_status s = check_attn_layout(AL);
+    if (s != W4A8_OK) return s;
+    W4A8_REQUIRE_PTR(k8);
+    W4A8_REQUIRE_PTR(ks);
+    W4A8_REQUIRE_PTR(v8);
+    W4A8_REQUIRE_PTR(vs);
+    W4A8_REQUIRE_PTR(kvpos);
+    if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
+    if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
+    if ((s = check_device()) != W4A8_OK) return s;
+    return launched(w4a8::launch_attn_pack(attn_geom_of(AL), k8, ks, v8, vs, kvpos,
+                                           static_cast<uint8_t *>(packed),
+                                           static_cast<hipStream_t>(stream)),
+                    "attention cache pack launch");
+}
+
+uint64_t w4a8_attn_work_bytes(const w4a8_attn_layout *AL, int32_t nh, int32_t nq) {
+    if (!AL || nh < 1 || nq < 1) return 0;
+    const int splits = w4a8::attn_splits(nh, nq, AL->nblk);
+    if (splits <= 1) return 0;
+    return static_cast<uint64_t>(splits) * nh * nq * (AL->d + 2) * 4;
+}
+
+w4a8_status w4a8_attn_prefill(const w4a8_attn_layout *AL, const void *packed, const float *q,
+                              int32_t nh, int32_t nq, int32_t pos0, int32_t window, int32_t sink,
+                              float scale, int8_t *q8, float *sq, float *o, float *m, float *l,
+                              void *work, uint64_t work_bytes, void *stream) {
+    w4a8_status s = check_attn_layout(AL);
+    if (s != W4A8_OK) return s;
+    if (nh < 1 || nh % AL->nkvh != 0)
+        return fail(W4A8_ERR_ARG, "nh = %d is not a positive multiple of nkvh = %d", nh, AL->nkvh);
+    if (nq < 0 || pos0 < 0 || window < 0 || sink < 0)
+        return fail(W4A8_ERR_ARG, "nq, pos0, window and sink must not be negative");
+    if (!(scale > 0.0f) || !std::isfinite(scale))
+        return fail(W4A8_ERR_ARG, "scale %g is not positive and finite", scale);
+    if (static_cast<int64_t>(nh) * nq * AL->d > (int64_t{1} << 34))
+        return fail(W4A8_ERR_UNSUPPORTED, "nh * nq * d is above 2^34");
+    if (nq == 0) return W4A8_OK;
+    if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
+    if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
+    W4A8_REQUIRE_PTR(q);
+    W4A8_REQUIRE_PTR(q8);
+    W4A8_REQUIRE_PTR(sq);
+    W4A8_REQUIRE_PTR(o);
+    W4A8_REQUIRE_PTR(m);
+    W4A8_REQUIRE_PTR(l);
+    const uint64_t need = w4a8_attn_work_bytes(AL, nh, nq);
+    if (need > 0) {
+        if (work_bytes < need)
+            return fail(W4A8_ERR_ARG, "work has %llu bytes, %llu are needed",
+                        static_cast<unsigned long long>(work_bytes),
+                        static_cast<unsigned long long>(need));
+        W4A8_REQUIRE_PTR(work);
+    }
+    if ((s = check_device()) != W4A8_OK) return s;
+    return launched(w4a8::launch_attn(attn_geom_of(AL), static_cast<const uint8_t *>(packed), q,
+                                      nh, nq, pos0, window, sink, scale, q8, sq, o, m, l,
+                                      static_cast<float *>(work), static_cast<hipStream_t>(stream)),
+                    "attention launch");
+}
+
 w4a8_status w4a8_debug_partials(const w4a8_layout *L, const void *packed, int32_t m,
                                 const int8_t *xq, const int32_t *xsum, int32_t *d,
                                 void *stream) {

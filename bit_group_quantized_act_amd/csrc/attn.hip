@@ -1,0 +1,397 @@
+// Prefill attention over the cached int8 key/value segment.
+//
+// Source: "cactus PR #697", section "Prefill attention": for the cached-int8 part of a prefill
+// chunk (fully visible by causality), int8 QK products under one flat scale per query row and
+// per key vector (the keys' group-scale ratios requantized into their int8 values), a masked
+// softmax over 64-key blocks carried online, and an unsigned 8-bit P quantized per (row, value
+// group, block) with the value group's scale folded in; sliding window with attention-sink
+// exemption; the new-token segment continues from the running statistics (m, l) and the
+// unnormalized output.
+//
+// MI355X design.
+//   Packing (once per cache write): keys requantized to their flat scale; each 64-slot block's
+//   values stored transposed ([d][slot]) with the slots in the order the MFMA output holds
+//   them, so that P never moves between lanes: the QK product is computed transposed (slots as
+//   rows, queries as columns, v_mfma_i32_32x32x32_i8 with the keys as A), lane (q, h) then holds
+//   slots 32t + 8(e/4) + 4h + e%4 (e = 0..15) of its query, which are exactly the 16 k slots it
+//   supplies as the B operand of the AV product (values^T as A).  Slot scales, positions and
+//   value-group scales are stored in the same order; per block and d, the column sum of the
+//   value codes.
+//   AV with unsigned P on a signed MFMA: u - 128 enters the i8 product and 128 * (the block's
+//   column sum) is added back in int32, exactly.
+//   Kernel: a workgroup of 4 wavefronts per (query head, 32-query tile, slot range); each
+//   wavefront takes every 4th block of the range, keeps its own (O, m, l) in registers and skips
+//   blocks no query of the tile sees; the wavefronts merge through LDS, and ranges split over
+//   several workgroups (to fill the chip) merge in a second kernel, both in a fixed order.
+#include "w4a8_kernels.h"
+
+namespace w4a8 {
+namespace {
+
+constexpr int kSlots = 64;      // slots per block
+constexpr int kQT = 32;         // queries per tile
+constexpr int kAW = 4;          // wavefronts per workgroup
+constexpr float kNegInf = -__builtin_inff();
+
+// Position of slot jj (0..63) of a block in the MFMA order: subtile t = jj / 32, row r = jj % 32
+// sits in lane half h = (r / 4) % 2 at element e = 4 (r / 8) + r % 4.
+__device__ __forceinline__ int mfma_order(int jj) {
+    const int t = jj >> 5, r = jj & 31;
+    return t * 32 + ((r >> 2) & 1) * 16 + 4 * (r >> 3) + (r & 3);
+}
+
+// ---- packing
+
+__global__ __launch_bounds__(256) void attn_pack_slots(const AttnGeom ag, const int8_t *__restrict__ k8,
+                                                       const float *__restrict__ ks,
+                                                       const int8_t *__restrict__ v8,
+                                                       const float *__restrict__ vs,
+                                                       const int32_t *__restrict__ kvpos,
+                                                       uint8_t *__restrict__ out) {
+#pragma clang fp contract(off)
+    const int64_t t = blockIdx.x * (int64_t)256 + threadIdx.x;
+    const int64_t npad = (int64_t)ag.nblk * kSlots;
+    if (t >= (int64_t)ag.nkvh * npad) return;
+    const int kh = static_cast<int>(t / npad);
+    const int j = static_cast<int>(t % npad);
+    const int d = ag.d, ng = d / 32;
+    const int b = j / kSlots, idx = mfma_order(j % kSlots);
+    const bool live = j < ag.nkv;
+    const int64_t src = (int64_t)kh * ag.nkv + j;
+    int8_t *kq = reinterpret_cast<int8_t *>(out + ag.off_kq) + ((int64_t)kh * npad + j) * d;
+    float sk = 0.0f;
+    if (live)
+        for (int g = 0; g < ng; ++g) sk = fmaxf(sk, ks[src * ng + g]);
+    for (int i = 0; i < d; ++i) {
+        float v = 0.0f;
+        if (live && sk > 0.0f) v = rintf(static_cast<float>(k8[src * d + i]) * (ks[src * ng + i / 32] / sk));
+        kq[i] = static_cast<int8_t>(v);
+    }
+    const int64_t bo = ((int64_t)kh * ag.nblk + b) * kSlots + idx;
+    reinterpret_cast<float *>(out + ag.off_sk)[bo] = sk;
+    reinterpret_cast<int32_t *>(out + ag.off_pos)[bo] = live ? kvpos[j] : -1;
+    int8_t *vt = reinterpret_cast<int8_t *>(out + ag.off_vt) + ((int64_t)kh * ag.nblk + b) * d * kSlots;
+    for (int i = 0; i < d; ++i) vt[i * kSlots + idx] = live ? v8[src * d + i] : 0;
+    float *sv = reinterpret_cast<float *>(out + ag.off_sv) + ((int64_t)kh * ag.nblk + b) * ng * kSlots;
+    for (int g = 0; g < ng; ++g) sv[g * kSlots + idx] = live ? vs[src * ng + g] : 0.0f;
+}
+
+// column sums of a block's value codes, stored per (group, lane half, element) in the order the
+// AV output tile holds the d rows: d = 32g + 8(e/4) + 4h + e%4
+__global__ __launch_bounds__(256) void attn_pack_vsum(const AttnGeom ag, const int8_t *__restrict__ v8,
+                                                      uint8_t *__restrict__ out) {
+    const int64_t t = blockIdx.x * (int64_t)256 + threadIdx.x;
+    const int d = ag.d;
+    if (t >= (int64_t)ag.nkvh * ag.nblk * d) return;
+    const int i = static_cast<int>(t % d);
+    const int64_t kb = t / d;                                   // kh * nblk + b
+    const int kh = static_cast<int>(kb / ag.nblk), b = static_cast<int>(kb % ag.nblk);
+    int32_t s = 0;
+    for (int jj = 0; jj < kSlots; ++jj) {
+        const int j = b * kSlots + jj;
+        if (j < ag.nkv) s += v8[((int64_t)kh * ag.nkv + j) * d + i];
+    }
+    const int g = i / 32, r = i % 32;
+    const int h = (r >> 2) & 1, e = 4 * (r >> 3) + (r & 3);
+    reinterpret_cast<int32_t *>(out + ag.off_vsum)[kb * d + g * 32 + h * 16 + e] = s;
+}
+
+// ---- attention
+
+struct AttnArgs {
+    const float *q;            // [nh][nq][d]
+    int nh, nq, pos0, window, sink, nsplit, bps;   // bps: blocks per split
+    float scale;
+    int8_t *q8;                // [nh][nq][d]
+    float *sq;                 // [nh][nq]
+    float *o, *m, *l;          // final [nh][nq][d], [nh][nq] (nsplit == 1) ...
+    float *work;               // ... or partial states [nsplit][nh][nq][d + 2]
+};
+
+__device__ __forceinline__ float wave_max32(float v) {          // max with the other lane half
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
+                                                        const uint8_t *__restrict__ packed,
+                                                        const AttnArgs a) {
+#pragma clang fp contract(off)
+    constexpr int NG = D / 32;
+    __shared__ float xm[kAW][kQT];
+    __shared__ float xo[kAW - 1][64][16];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = lane >> 5, col = lane & 31;
+    const int qtiles = (a.nq + kQT - 1) / kQT;
+    const int split = blockIdx.x % a.nsplit;
+    const int hq = blockIdx.x / a.nsplit;                     // head * qtiles + tile
+    const int head = hq / qtiles, q0 = (hq % qtiles) * kQT;
+    const int kh = head / (a.nh / ag.nkvh);
+    const int qi = q0 + col;                                  // this lane's query
+    const bool qlive = qi < a.nq;
+    const int64_t qpos = (int64_t)a.pos0 + qi;
+
+    // the query row's int8 codes (one flat scale per row), as the B operands of the QK product:
+    // lane (q, h) holds d = 32i + 16h .. +15 of each 32-wide chunk i
+    v4i qb[NG];
+    float sq;
+    {
+        float x[NG][16];
+        float amax = 0.0f;
+        const float *qr = a.q + ((int64_t)head * a.nq + (qlive ? qi : 0)) * D;
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+#pragma unroll
+            for (int c = 0; c < 16; c += 4) {
+                const float4 v = qlive ? *reinterpret_cast<const float4 *>(qr + 32 * i + 16 * half + c)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+                x[i][c] = v.x; x[i][c + 1] = v.y; x[i][c + 2] = v.z; x[i][c + 3] = v.w;
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
+        }
+        amax = wave_max32(amax);
+        sq = amax / 127.0f;
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            uint32_t w4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                int cq = 0;
+                if (amax > 0.0f) cq = static_cast<int>(fminf(fmaxf(rintf(x[i][c] / sq), -127.0f), 127.0f));
+                w4[c >> 2] |= (static_cast<uint32_t>(cq) & 0xFFu) << (8 * (c & 3));
+            }
+            qb[i] = v4i{static_cast<int>(w4[0]), static_cast<int>(w4[1]), static_cast<int>(w4[2]),
+                        static_cast<int>(w4[3])};
+        }
+        if (wave == 0 && split == 0 && qlive) {
+            int8_t *q8r = a.q8 + ((int64_t)head * a.nq + qi) * D;
+#pragma unroll
+            for (int i = 0; i < NG; ++i)
+                *reinterpret_cast<v4i *>(q8r + 32 * i + 16 * half) = qb[i];
+            if (half == 0) a.sq[(int64_t)head * a.nq + qi] = sq;
+        }
+    }
+    const float qscale = sq * a.scale;
+
+    const int8_t *kqb = reinterpret_cast<const int8_t *>(packed + ag.off_kq) + (int64_t)kh * ag.nblk * kSlots * D;
+    const float *skb = reinterpret_cast<const float *>(packed + ag.off_sk) + (int64_t)kh * ag.nblk * kSlots;
+    const int32_t *posb = reinterpret_cast<const int32_t *>(packed + ag.off_pos) + (int64_t)kh * ag.nblk * kSlots;
+    const int8_t *vtb = reinterpret_cast<const int8_t *>(packed + ag.off_vt) + (int64_t)kh * ag.nblk * D * kSlots;
+    const float *svb = reinterpret_cast<const float *>(packed + ag.off_sv) + (int64_t)kh * ag.nblk * NG * kSlots;
+    const int32_t *vsb = reinterpret_cast<const int32_t *>(packed + ag.off_vsum) + (int64_t)kh * ag.nblk * D;
+
+    float mrun = kNegInf, lrun = 0.0f;
+    v16f o[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[g][e] = 0.0f;
+
+    const int b_lo = split * a.bps;
+    const int b_hi = min(ag.nblk, b_lo + a.bps);
+    for (int b = b_lo + wave; b < b_hi; b += kAW) {
+        // positions and visibility of the lane's 32 slots (two subtiles of 16)
+        float s[2][16];
+        bool any = false;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int base = b * kSlots + t * 32 + half * 16;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t p = posb[base + e];
+                const bool vis = qlive && p >= 0 && p <= qpos &&
+                                 (a.window <= 0 || p < a.sink || qpos - p < a.window);
+                s[t][e] = vis ? 0.0f : kNegInf;
+                any |= vis;
+            }
+        }
+        if (__builtin_amdgcn_ballot_w64(any) == 0) continue;          // no query sees the block
+        // S^T = K Q^T for the block's two 32-slot subtiles
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            v16i acc = {};
+            const int8_t *kr = kqb + ((int64_t)b * kSlots + t * 32 + col) * D + 16 * half;
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                const v4i ka = *reinterpret_cast<const v4i *>(kr + 32 * i);
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qb[i], acc, 0, 0, 0);
+            }
+            const int base = b * kSlots + t * 32 + half * 16;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (s[t][e] == 0.0f) s[t][e] = static_cast<float>(acc[e]) * qscale * skb[base + e];
+        }
+        float mb = kNegInf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mb = fmaxf(mb, s[t][e]);
+        mb = wave_max32(mb);
+        const float mnew = fmaxf(mrun, mb);
+        const float alpha = (mrun == kNegInf) ? 0.0f : expf(mrun - mnew);
+        float p[2][16];
+        float psum = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                p[t][e] = (s[t][e] == kNegInf) ? 0.0f : expf(s[t][e] - mnew);
+                psum += p[t][e];
+            }
+        lrun = lrun * alpha + psum;
+        mrun = (mb == kNegInf) ? mrun : mnew;
+        const float keep = (mb == kNegInf) ? 1.0f : alpha;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            // P folded with the value group's scale, quantized to u8 per (row, group, block)
+            float pg[2][16];
+            float mx = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const float *svr = svb + ((int64_t)b * NG + g) * kSlots + t * 32 + half * 16;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    pg[t][e] = p[t][e] * svr[e];
+                    mx = fmaxf(mx, pg[t][e]);
+                }
+            }
+            mx = wave_max32(mx);
+            const float sp = mx / 255.0f;
+            v16i iacc = {};
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                uint32_t w4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int u = (mx > 0.0f) ? static_cast<int>(fminf(rintf(pg[t][e] / sp), 255.0f)) : 0;
+                    w4[e >> 2] |= static_cast<uint32_t>((u - 128) & 0xFF) << (8 * (e & 3));
+                }
+                const v4i pb = {static_cast<int>(w4[0]), static_cast<int>(w4[1]),
+                                static_cast<int>(w4[2]), static_cast<int>(w4[3])};
+                const v4i va = *reinterpret_cast<const v4i *>(
+                    vtb + ((int64_t)b * D + 32 * g + col) * kSlots + t * 32 + half * 16);
+                iacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, pb, iacc, 0, 0, 0);
+            }
+            const int32_t *vsr = vsb + (int64_t)b * D + g * 32 + half * 16;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float av = static_cast<float>(iacc[e] + 128 * vsr[e]);
+                o[g][e] = o[g][e] * keep + ((mx > 0.0f) ? sp * av : 0.0f);
+            }
+        }
+    }
+
+    // merge the wavefronts' states (fixed order): M = max m_w, each scaled by e^(m_w - M)
+    const float lw = lrun + __shfl_xor(lrun, 32, 64);
+    if (half == 0) xm[wave][col] = mrun;
+    __syncthreads();
+    float mall = xm[0][col];
+#pragma unroll
+    for (int w = 1; w < kAW; ++w) mall = fmaxf(mall, xm[w][col]);
+    const float mine = (mrun == kNegInf) ? 0.0f : expf(mrun - mall);
+    __syncthreads();
+    if (half == 0) xm[wave][col] = lw * mine;
+    __syncthreads();
+    float lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kAW; ++w) lsum += xm[w][col];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        if (wave != 0)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) xo[wave - 1][lane][e] = o[g][e] * mine;
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float v = o[g][e] * mine;
+#pragma unroll
+                for (int w = 1; w < kAW; ++w) v += xo[w - 1][lane][e];
+                o[g][e] = v;
+            }
+        }
+        __syncthreads();
+    }
+    if (wave != 0 || !qlive) return;
+    const int64_t row = (int64_t)head * a.nq + qi;
+    float *orow;
+    if (a.nsplit == 1) {
+        orow = a.o + row * D;
+        if (half == 0) { a.m[row] = mall; a.l[row] = lsum; }
+    } else {
+        float *ws = a.work + ((int64_t)split * a.nh * a.nq + row) * (D + 2);
+        orow = ws;
+        if (half == 0) { ws[D] = mall; ws[D + 1] = lsum; }
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            orow[32 * g + 8 * (e >> 2) + 4 * half + (e & 3)] = o[g][e];
+}
+
+// the split states of each (head, query) merged in split order
+__global__ __launch_bounds__(256) void attn_merge(int nsplit, int64_t rows, int d,
+                                                  const float *__restrict__ work,
+                                                  float *__restrict__ o, float *__restrict__ m,
+                                                  float *__restrict__ l) {
+    const int64_t t = blockIdx.x * (int64_t)256 + threadIdx.x;
+    if (t >= rows * d) return;
+    const int64_t row = t / d;
+    const int c = static_cast<int>(t % d);
+    float mall = kNegInf;
+    for (int s = 0; s < nsplit; ++s) mall = fmaxf(mall, work[(s * rows + row) * (d + 2) + d]);
+    float acc = 0.0f, lsum = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+        const float *ws = work + (s * rows + row) * (d + 2);
+        const float f = (ws[d] == kNegInf) ? 0.0f : expf(ws[d] - mall);
+        acc += ws[c] * f;
+        lsum += ws[d + 1] * f;
+    }
+    o[t] = acc;
+    if (c == 0) { m[row] = mall; l[row] = lsum; }
+}
+
+}  // namespace
+
+int attn_splits(int nh, int nq, int nblk) {
+    const int tiles = nh * ((nq + kQT - 1) / kQT);
+    int s = (512 + tiles - 1) / tiles;                 // aim at two workgroups per CU
+    s = max(1, min(s, (nblk + kAW - 1) / kAW));        // at least one block per wavefront
+    return s;
+}
+
+hipError_t launch_attn_pack(const AttnGeom &ag, const int8_t *k8, const float *ks,
+                            const int8_t *v8, const float *vs, const int32_t *kvpos,
+                            uint8_t *packed, hipStream_t stream) {
+    const int64_t slots = (int64_t)ag.nkvh * ag.nblk * kSlots;
+    attn_pack_slots<<<static_cast<unsigned>((slots + 255) / 256), 256, 0, stream>>>(ag, k8, ks, v8, vs,
+                                                                                  kvpos, packed);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t cols = (int64_t)ag.nkvh * ag.nblk * ag.d;
+    attn_pack_vsum<<<static_cast<unsigned>((cols + 255) / 256), 256, 0, stream>>>(ag, v8, packed);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnGeom &ag, const uint8_t *packed, const float *q, int nh, int nq,
+                       int pos0, int window, int sink, float scale, int8_t *q8, float *sq,
+                       float *o, float *m, float *l, float *work, hipStream_t stream) {
+    if (nq == 0) return hipSuccess;
+    AttnArgs a{q, nh, nq, pos0, window, sink, attn_splits(nh, nq, ag.nblk), 0, scale, q8, sq, o, m,
+               l, work};
+    a.bps = (ag.nblk + a.nsplit - 1) / a.nsplit;
+    const unsigned grid = static_cast<unsigned>(nh * ((nq + kQT - 1) / kQT) * a.nsplit);
+    if (ag.d == 64) attn_kernel<64><<<grid, 64 * kAW, 0, stream>>>(ag, packed, a);
+    else if (ag.d == 128) attn_kernel<128><<<grid, 64 * kAW, 0, stream>>>(ag, packed, a);
+    else attn_kernel<256><<<grid, 64 * kAW, 0, stream>>>(ag, packed, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    const int64_t n = (int64_t)nh * nq * ag.d;
+    attn_merge<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(
+        a.nsplit, (int64_t)nh * nq, ag.d, work, o, m, l);
+    return hipGetLastError();
+}
+
+}  // namespace w4a8

@@ -218,6 +218,20 @@ hipError_t launch_prep_a16(const float *x, int64_t m, int k, uint16_t *xh, float
 hipError_t launch_linear_a16(const Geom &g, const uint8_t *packed, int m, const uint16_t *xh,
                              const float *xsf, float *y, hipStream_t stream);
 
+// Prefill attention over a packed int8 key/value cache (the packed layout is described in
+// include/w4a8.h; offsets in bytes from the packed buffer).
+struct AttnGeom {
+    int nkvh, nkv, d, nblk;
+    uint64_t off_kq, off_sk, off_pos, off_vt, off_sv, off_vsum;
+};
+int attn_splits(int nh, int nq, int nblk);
+hipError_t launch_attn_pack(const AttnGeom &ag, const int8_t *k8, const float *ks,
+                            const int8_t *v8, const float *vs, const int32_t *kvpos,
+                            uint8_t *packed, hipStream_t stream);
+hipError_t launch_attn(const AttnGeom &ag, const uint8_t *packed, const float *q, int nh, int nq,
+                       int pos0, int window, int sink, float scale, int8_t *q8, float *sq,
+                       float *o, float *m, float *l, float *work, hipStream_t stream);
+
 // The reduction of nkeys panel keys into token and value (one workgroup).
 hipError_t launch_argmax_keys(const unsigned long long *keys, int nkeys, int32_t *token,
                               float *value, hipStream_t stream);

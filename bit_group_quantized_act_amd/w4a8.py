@@ -24,7 +24,9 @@ EXPORTS = ("w4a8_packed_layout", "w4a8_pack_weights", "w4a8_pack_weights_row_sca
            "w4a8_prep", "w4a8_gemv", "w4a8_gemm",
            "w4a8_linear", "w4a8_linear_glu", "w4a8_gemm_glu", "w4a8_lm_head_argmax",
            "w4a8_gemv_argmax", "w4a8_prep_a16", "w4a8_linear_a16", "w4a8_gemm_a16",
-           "w4a8_debug_partials", "w4a8_status_string", "w4a8_last_error")
+           "w4a8_attn_layout_init", "w4a8_attn_pack_kv", "w4a8_attn_work_bytes",
+           "w4a8_attn_prefill", "w4a8_debug_partials", "w4a8_status_string", "w4a8_last_error")
+_NOT_STATUS = ("w4a8_attn_work_bytes", "w4a8_status_string", "w4a8_last_error")
 ACT_SILU, ACT_GELU_TANH, ACT_GELU_ERF = 0, 1, 2
 
 
@@ -77,9 +79,17 @@ def load() -> ctypes.CDLL:
     lib.w4a8_prep_a16.argtypes = [P, i32, i32, i32, P, P, P]
     lib.w4a8_linear_a16.argtypes = [LP, P, i32, P, P, P, P, P]
     lib.w4a8_gemm_a16.argtypes = [LP, P, i32, P, P, P, P]
+    AP = ctypes.POINTER(AttnLayout)
+    lib.w4a8_attn_layout_init.argtypes = [i32, i32, i32, AP]
+    lib.w4a8_attn_pack_kv.argtypes = [AP, P, P, P, P, P, P, P]
+    lib.w4a8_attn_prefill.argtypes = [AP, P, P, i32, i32, i32, i32, i32, ctypes.c_float, P, P, P,
+                                      P, P, P, u64, P]
+    lib.w4a8_attn_work_bytes.argtypes = [AP, i32, i32]
+    lib.w4a8_attn_work_bytes.restype = u64
     lib.w4a8_debug_partials.argtypes = [LP, P, i32, P, P, P, P]
-    for f in EXPORTS[:15]:
-        getattr(lib, f).restype = ctypes.c_int
+    for f in EXPORTS:
+        if f not in _NOT_STATUS:
+            getattr(lib, f).restype = ctypes.c_int
     lib.w4a8_status_string.argtypes = [ctypes.c_int]
     lib.w4a8_status_string.restype = ctypes.c_char_p
     lib.w4a8_last_error.argtypes = []
@@ -389,3 +399,56 @@ def gemm_a16(L: Layout, packed: torch.Tensor, xh: torch.Tensor, xsf: torch.Tenso
     _check(load().w4a8_gemm_a16(ctypes.byref(L), _ptr(packed), m, _ptr(xh), _ptr(xsf), _ptr(y),
                                 _stream(packed.device)), "w4a8_gemm_a16")
     return y
+
+
+
+class AttnLayout(ctypes.Structure):
+    """w4a8_attn_layout: the packed int8 key/value cache of one attention layer."""
+    _fields_ = [("nkvh", ctypes.c_int32), ("nkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("nblk", ctypes.c_int32), ("bytes", ctypes.c_uint64), ("off_kq", ctypes.c_uint64),
+                ("off_sk", ctypes.c_uint64), ("off_pos", ctypes.c_uint64),
+                ("off_vt", ctypes.c_uint64), ("off_sv", ctypes.c_uint64),
+                ("off_vsum", ctypes.c_uint64)]
+
+
+def attn_pack_kv(k8, ks, v8, vs, kvpos, out=None):
+    """Pack a canonical int8 cache (k8 / v8 int8 [nkvh, nkv, d], ks / vs fp32 [nkvh, nkv, d/32],
+    kvpos int32 [nkv], device tensors): returns (layout, packed uint8 tensor)."""
+    nkvh, nkv, d = k8.shape
+    AL = AttnLayout()
+    _check(load().w4a8_attn_layout_init(nkvh, nkv, d, ctypes.byref(AL)), "w4a8_attn_layout_init")
+    _dev(k8, torch.int8, "k8")
+    _dev(v8, torch.int8, "v8", tuple(k8.shape))
+    _dev(ks, torch.float32, "ks", (nkvh, nkv, d // 32))
+    _dev(vs, torch.float32, "vs", (nkvh, nkv, d // 32))
+    _dev(kvpos, torch.int32, "kvpos", (nkv,))
+    if out is None:
+        out = torch.empty(AL.bytes, dtype=torch.uint8, device=k8.device)
+    _check(load().w4a8_attn_pack_kv(ctypes.byref(AL), _ptr(k8), _ptr(ks), _ptr(v8), _ptr(vs),
+                                    _ptr(kvpos), _ptr(out), _stream(k8.device)),
+           "w4a8_attn_pack_kv")
+    return AL, out
+
+
+def attn_prefill(AL: AttnLayout, packed, q, pos0: int, window: int = 0, sink: int = 0,
+                 scale: float = 1.0, out=None, work=None):
+    """Prefill attention of q fp32 [nh, nq, d] over the packed cache: returns (o unnormalized
+    [nh, nq, d], m [nh, nq], l [nh, nq], q8 [nh, nq, d], sq [nh, nq])."""
+    nh, nq, d = q.shape
+    _dev(q, torch.float32, "q")
+    dev = q.device
+    if out is None:
+        out = (torch.empty((nh, nq, d), dtype=torch.float32, device=dev),
+               torch.empty((nh, nq), dtype=torch.float32, device=dev),
+               torch.empty((nh, nq), dtype=torch.float32, device=dev),
+               torch.empty((nh, nq, d), dtype=torch.int8, device=dev),
+               torch.empty((nh, nq), dtype=torch.float32, device=dev))
+    o, m, l, q8, sq = out
+    need = load().w4a8_attn_work_bytes(ctypes.byref(AL), nh, nq)
+    if work is None and need > 0:
+        work = torch.empty(need // 4, dtype=torch.float32, device=dev)
+    wb = 0 if work is None else work.numel() * work.element_size()
+    _check(load().w4a8_attn_prefill(ctypes.byref(AL), _ptr(packed), _ptr(q), nh, nq, pos0, window,
+                                    sink, float(scale), _ptr(q8), _ptr(sq), _ptr(o), _ptr(m),
+                                    _ptr(l), _ptr(work), wb, _stream(dev)), "w4a8_attn_prefill")
+    return o, m, l, q8, sq

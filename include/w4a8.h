@@ -319,6 +319,61 @@ w4a8_status w4a8_gemm_a16(const w4a8_layout *L, const void *packed, int32_t m,
                           const uint16_t *xh, const float *xsf, float *y, void *stream);
 
 /*
+ * Prefill attention over the cached int8 key/value segment of a prefill chunk.
+ *
+ * Cache (canonical input): for nkvh key/value heads and nkv slots of head dimension d (64, 128
+ * or 256): k8, v8 int8 [nkvh][nkv][d]; ks, vs fp32 [nkvh][nkv][d/32] (one scale per 32 of the
+ * head dimension); kvpos int32 [nkv], the position held by each slot (-1: empty; slots need not
+ * be in position order, as in a rolled sliding-window ring).
+ * Queries: q fp32 [nh][nq][d], nh a multiple of nkvh (query head h reads cache head
+ * h / (nh / nkvh)); query i sits at position pos0 + i.
+ * A slot at position p is seen by the query at t when p >= 0, p <= t, and window == 0 (a global
+ * layer) or p < sink (attention sinks) or t - p < window.
+ * Method: q8 = round-half-even(q / sq), sq = max|q row| / 127 (one scale per query row); keys to
+ * one flat scale per vector, sk = max_g ks[g], kq = round-half-even(k8 * fp32(ks[g] / sk));
+ * logits S = scale * sq * sk * (q8 . kq); over blocks of 64 slots in slot order, an online
+ * softmax m' = max(m, block max), alpha = e^(m - m'), P = e^(S - m'), l = alpha * l + sum P;
+ * per value group g of 32 dims, P'_j = P_j * vs[j][g] quantized to u = round(P'_j / sp) in
+ * 0..255 with sp = max_j P' / 255 per (query, group, block), and O_g = alpha * O_g +
+ * sp * sum_j u_j * v8[j].  Results: the unnormalized O [nh][nq][d], m, l [nh][nq] (m = -inf,
+ * l = 0, O = 0 for a query that sees no slot): the state a following new-token segment
+ * continues from; O / l is the attention output over the cached segment.
+ *
+ * w4a8_attn_layout_init: host only; d in {64, 128, 256}, 1 <= nkvh, 1 <= nkv <= 2^24.
+ * w4a8_attn_pack_kv: repack the canonical cache into AL->bytes of device memory (256-byte
+ *   aligned): keys requantized to their flat scales ([nkvh][nblk*64][d], slot order); per block
+ *   of 64 slots the values transposed ([d][64]), the slots' scales, positions (-1 past nkv) and
+ *   value-group scales ([d/32][64]), all with slot jj of the block at index 32t + 16h + 4(r/8) +
+ *   r%4 (t = jj/32, r = jj%32, h = (r/4)%2: the order the matrix-core output holds them), and
+ *   each column's sum of the block's value codes.
+ * w4a8_attn_work_bytes: the bytes of device scratch w4a8_attn_prefill needs for (nh, nq)
+ *   (0 when the slot range is not split).
+ * w4a8_attn_prefill: q8 int8 [nh][nq][d] and sq fp32 [nh][nq] (the query codes, written), o, m,
+ *   l (written), work (w4a8_attn_work_bytes of scratch, 16-byte aligned, contents irrelevant;
+ *   may be NULL when that is 0).  W4A8_ERR_ARG: nh not a positive multiple of AL->nkvh, nq < 0,
+ *   pos0 / window / sink negative, scale not positive and finite, NULL or misaligned pointers,
+ *   work_bytes too small.
+ * Source: "cactus PR #697", section "Prefill attention" (and its test list: the attention
+ * differential against a double-precision oracle, global and sliding-window layers, a rolled
+ * cache with the sink exemption live, partial query tiles and key blocks).
+ */
+typedef struct w4a8_attn_layout {
+    int32_t nkvh, nkv, d, nblk;   /* nblk = ceil(nkv / 64) */
+    uint64_t bytes;               /* total size of the packed cache */
+    uint64_t off_kq, off_sk, off_pos, off_vt, off_sv, off_vsum;
+} w4a8_attn_layout;
+
+w4a8_status w4a8_attn_layout_init(int32_t nkvh, int32_t nkv, int32_t d, w4a8_attn_layout *AL);
+w4a8_status w4a8_attn_pack_kv(const w4a8_attn_layout *AL, const int8_t *k8, const float *ks,
+                              const int8_t *v8, const float *vs, const int32_t *kvpos,
+                              void *packed, void *stream);
+uint64_t w4a8_attn_work_bytes(const w4a8_attn_layout *AL, int32_t nh, int32_t nq);
+w4a8_status w4a8_attn_prefill(const w4a8_attn_layout *AL, const void *packed, const float *q,
+                              int32_t nh, int32_t nq, int32_t pos0, int32_t window, int32_t sink,
+                              float scale, int8_t *q8, float *sq, float *o, float *m, float *l,
+                              void *work, uint64_t work_bytes, void *stream);
+
+/*
  * The exact int32 partials D[r][n][g] (definitions above) written by the same kernel code as
  * the GEMV (m == 1) or the GEMM (m > 1), with the fp32 epilogue replaced by a store of D.
  *   xsum  as from w4a8_prep (the AFFINE partial is recovered from the u - 8 codes as

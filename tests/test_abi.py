@@ -209,6 +209,35 @@ def test_invalid_calls_are_rejected_on_the_host(lib):
     assert lib.w4a8_linear_a16(ctypes.byref(cbl), p, 2, p, p, p, p, None) == ERR_UNSUPPORTED
     g128 = w4a8.packed_layout(w4a8.SYM, 128, 256, 128)
     assert lib.w4a8_gemm_a16(ctypes.byref(g128), p, 2, p, p, p, None) == ERR_ARG
+    # attention: layout limits, a forged layout, heads, negative arguments, scale, work size
+    AL = w4a8.AttnLayout()
+    assert lib.w4a8_attn_layout_init(2, 100, 96, ctypes.byref(AL)) == ERR_ARG
+    assert lib.w4a8_attn_layout_init(0, 100, 64, ctypes.byref(AL)) == ERR_ARG
+    assert lib.w4a8_attn_layout_init(2, 0, 64, ctypes.byref(AL)) == ERR_ARG
+    assert lib.w4a8_attn_layout_init(2, 1000, 256, ctypes.byref(AL)) == 0
+    assert AL.nblk == 16 and AL.bytes % 256 == 0 and AL.off_vsum > AL.off_sv > AL.off_vt
+    ALP = ctypes.byref(AL)
+    forged = w4a8.AttnLayout.from_buffer_copy(AL)
+    forged.off_vt += 256
+    assert lib.w4a8_attn_pack_kv(ctypes.byref(forged), p, p, p, p, p, p, None) == ERR_ARG
+    assert lib.w4a8_attn_pack_kv(ALP, p, p, p, p, None, p, None) == ERR_ARG
+    assert lib.w4a8_attn_pack_kv(ALP, p, p, p, p, p, p16, None) == ERR_ARG
+    f = ctypes.c_float
+    wb = lib.w4a8_attn_work_bytes(ALP, 8, 256)
+    assert wb > 0 and lib.w4a8_attn_work_bytes(ALP, 8, 0) == 0
+    args = lambda **kw: [kw.get(k, v) for k, v in (
+        ("AL", ALP), ("packed", p), ("q", p), ("nh", 8), ("nq", 256), ("pos0", 1000),
+        ("window", 0), ("sink", 0), ("scale", f(0.0625)), ("q8", p), ("sq", p), ("o", p),
+        ("m", p), ("l", p), ("work", p), ("wb", wb), ("stream", None))]
+    assert lib.w4a8_attn_prefill(*args(nh=7)) == ERR_ARG                 # not a multiple of 2
+    assert lib.w4a8_attn_prefill(*args(nq=-1)) == ERR_ARG
+    assert lib.w4a8_attn_prefill(*args(window=-5)) == ERR_ARG
+    assert lib.w4a8_attn_prefill(*args(scale=f(0.0))) == ERR_ARG
+    assert lib.w4a8_attn_prefill(*args(scale=f(float("nan")))) == ERR_ARG
+    assert lib.w4a8_attn_prefill(*args(wb=wb - 4)) == ERR_ARG
+    assert lib.w4a8_attn_prefill(*args(o=None)) == ERR_ARG
+    assert lib.w4a8_attn_prefill(*args(q=p1)) == ERR_ARG
+    assert lib.w4a8_attn_prefill(*args(nq=0, q=None, o=None)) == 0
 
 @pytest.mark.skipif(_gpu_visible(), reason="checks the no-device path; would launch on a GPU")
 def test_valid_calls_without_a_device_report_device_error(lib):
@@ -226,6 +255,9 @@ def test_valid_calls_without_a_device_report_device_error(lib):
     assert lib.w4a8_gemv_argmax(ctypes.byref(L), p, p, p, p, ctypes.c_float(0.0), p, p, p, p,
                                 16, None) == ERR_DEVICE
     assert lib.w4a8_prep_a16(p, 2, 256, 64, p, p, None) == ERR_DEVICE
+    AL = w4a8.AttnLayout()
+    assert lib.w4a8_attn_layout_init(1, 64, 64, ctypes.byref(AL)) == 0
+    assert lib.w4a8_attn_pack_kv(ctypes.byref(AL), p, p, p, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_linear_a16(ctypes.byref(L), p, 2, p, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_last_error().decode() != ""
 

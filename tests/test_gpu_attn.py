@@ -1,0 +1,129 @@
+"""GPU parity of the int8 prefill attention over a cached segment (w4a8_attn_pack_kv,
+w4a8_attn_prefill) against the oracle's int8 method.
+
+Bit-exact: the query codes and scales, and the requantized keys.  The running state: m within
+2e-5 (1 + |m|) (fp32 logits against fp64), l within 1e-4 relative (fp32 exponentials summed),
+and the normalized output O / l with relative L2 error <= 1e-4 over each case and <= 1e-3 per
+query row.  Row bound: a code of the 8-bit P can differ from the oracle's only where P' / sp
+lies within fp32 rounding of a half-integer, and one such difference moves a row's output by at
+most 1/255 of one value row's share of it, well under 1e-3."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_group_quantized_act_amd import synth
+from _util import to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _w4a8():
+    from bit_group_quantized_act_amd import w4a8
+    w4a8.load()
+    return w4a8
+
+
+def _run(A):
+    w = _w4a8()
+    c = A["cfg"]
+    AL, packed = w.attn_pack_kv(to_dev(A["k8"]), to_dev(A["ks"]), to_dev(A["v8"]),
+                                to_dev(A["vs"]), to_dev(A["kvpos"]))
+    o, m, l, q8, sq = w.attn_prefill(AL, packed, to_dev(A["q"]), A["pos0"], c.window, c.sink,
+                                     A["scale"])
+    torch.cuda.synchronize()
+    pk = packed.cpu().numpy()
+    npad = AL.nblk * 64
+    kq = pk[AL.off_kq:AL.off_kq + c.nkvh * npad * c.d].view(np.int8).reshape(c.nkvh, npad, c.d)
+    return dict(o=o.cpu().numpy(), m=m.cpu().numpy(), l=l.cpu().numpy(), q8=q8.cpu().numpy(),
+                sq=sq.cpu().numpy(), kq=kq[:, :c.nkv])
+
+
+def _oracle(A):
+    c = A["cfg"]
+    q8, sq = oracle.attn_quant_q(A["q"])
+    kq, sk = oracle.attn_requant_k(A["k8"], A["ks"])
+    o, m, l = oracle.attn_int8(q8, sq, kq, sk, A["v8"], A["vs"], A["kvpos"], A["pos0"],
+                               c.window, c.sink, A["scale"])
+    return dict(o=o, m=m, l=l, q8=q8, sq=sq, kq=kq)
+
+
+def check_attn(got, ref, what):
+    assert np.array_equal(got["q8"], ref["q8"]), f"{what}: query codes differ"
+    assert np.array_equal(got["sq"].view(np.uint32), ref["sq"].view(np.uint32)), \
+        f"{what}: query scales differ"
+    assert np.array_equal(got["kq"], ref["kq"]), f"{what}: requantized keys differ"
+    seen = np.isfinite(ref["m"])
+    assert np.array_equal(np.isfinite(got["m"]), seen), f"{what}: visibility differs"
+    assert np.all(got["l"][~seen] == 0) and not got["o"][~seen].any()
+    assert np.all(np.abs(got["m"][seen] - ref["m"][seen]) <= 2e-5 * (1 + np.abs(ref["m"][seen])))
+    np.testing.assert_allclose(got["l"][seen], ref["l"][seen], rtol=1e-4)
+    if not seen.any():
+        return 0.0, 0.0
+    on = got["o"][seen] / got["l"][seen][:, None]
+    rn = ref["o"][seen] / ref["l"][seen][:, None]
+    row = np.linalg.norm(on - rn, axis=1) / np.maximum(np.linalg.norm(rn, axis=1), 1e-30)
+    tot = np.linalg.norm(on - rn) / np.linalg.norm(rn)
+    assert tot <= 1e-4, f"{what}: relative L2 error {tot:.3e}"
+    assert row.max() <= 1e-3, f"{what}: worst row {row.max():.3e}"
+    return tot, row.max()
+
+
+# partial query tiles (nq % 32) and partial blocks (nkv % 64), every head dimension, key/value
+# heads shared by several query heads, a rolled window ring with sinks, a window that hides the
+# oldest blocks entirely (skipped), and queries that see no slot at all
+CASES = [
+    ("A1", dict(nh=2, nkvh=1, nq=40, nkv=150, d=64)),
+    ("A2", dict(nh=4, nkvh=2, nq=33, nkv=200, d=128, window=70, sink=3, pos0=400)),
+    ("A2", dict(nh=4, nkvh=1, nq=64, nkv=300, d=256, window=100, sink=0, rolled=False,
+                pos0=300)),
+    ("A1", dict(nh=3, nkvh=3, nq=7, nkv=64, d=256)),
+    ("A2", dict(nh=2, nkvh=1, nq=20, nkv=90, d=64, window=5, sink=0, rolled=False, pos0=400)),
+]
+
+
+@pytest.mark.parametrize("name,over", CASES,
+                         ids=[f"{n}-{'-'.join(f'{k}{v}' for k, v in o.items())}"
+                              for n, o in CASES])
+def test_attn_parity(name, over):
+    A = synth.make_attn(name, **over)
+    c = A["cfg"]
+    print(f"attn {name} {over}", flush=True)
+    got = _run(A)
+    ref = _oracle(A)
+    if c.window == 5:
+        assert not np.isfinite(ref["m"]).any()      # every query is past the cache's window
+    check_attn(got, ref, f"attn {name} {over}")
+
+
+def test_attn_empty_slots_and_rerun_same_bits():
+    # slots holding no position are never seen; a second call gives the same bits
+    A = synth.make_attn("A1", nh=2, nkvh=1, nq=32, nkv=128, d=128)
+    pos = A["kvpos"].copy()
+    pos[::3] = -1
+    A = dict(A, kvpos=pos)
+    got = _run(A)
+    check_attn(got, _oracle(A), "empty slots")
+    again = _run(A)
+    assert np.array_equal(got["o"].view(np.uint32), again["o"].view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["A1", "A2"])
+def test_attn_full_size(name):
+    """The Gemma-style layer: 8 query heads on 2 key/value heads, head_dim 256, 256 queries
+    against 1024 cached slots (A2: a 512-wide window over a rolled ring with 4 sinks)."""
+    A = synth.make_attn(name)
+    print(f"attn full {name}", flush=True)
+    got = _run(A)
+    ref = _oracle(A)
+    check_attn(got, ref, f"attn full {name}")
+    # and the method's distance to plain attention on the dequantized cache stays at the
+    # oracle's own level
+    c = A["cfg"]
+    exact = oracle.attn_exact(A["q"], A["k8"], A["ks"], A["v8"], A["vs"], A["kvpos"], A["pos0"],
+                              c.window, c.sink, A["scale"])
+    on = got["o"] / got["l"][..., None]
+    rel = np.linalg.norm(on - exact, axis=-1) / np.linalg.norm(exact, axis=-1)
+    assert rel.mean() < 1.5e-2 and rel.max() < 4e-2, (rel.mean(), rel.max())
