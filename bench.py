@@ -31,6 +31,12 @@ and its fp32 group sums, then the GEMV / GEMM with f16 MFMA); its dominant kerne
 GEMM alone (w4a8_gemm_a16), priced against the 2.5 PFLOP/s dense fp16 MFMA peak when that floor
 is above the HBM floor.
 
+--attn A1|A2 times the int8 prefill attention over a cached segment instead (w4a8_attn_prefill
+on a cache packed once by w4a8_attn_pack_kv): A1 a global layer, A2 a 512-wide sliding window
+over a rolled ring with 4 sinks; 8 query heads on 2 key/value heads, head_dim 256, 256 queries
+against 1024 cached slots.  value = int8 operations of the two products over the visible
+(query, slot) pairs per second, against the 5.0 POP/s dense int8 MFMA peak.
+
 --argmax CAP times the greedy tail of a vocabulary head instead (one row; w4a8_lm_head_argmax:
 the prepass, the GEMV that also soft-caps the logits with CAP (0: no cap) and stores each
 64-row panel's largest key, and a one-workgroup reduction of those keys into the token).  The
@@ -103,6 +109,8 @@ def parse():
                          "workload instead")
     ap.add_argument("--a16", action="store_true",
                     help="time the fp16-activation path (w4a8_linear_a16) instead")
+    ap.add_argument("--attn", choices=["A1", "A2"], default=None,
+                    help="time the int8 prefill attention over a cached segment instead")
     ap.add_argument("--hot", action="store_true",
                     help="reuse one weight buffer (measures cache, not HBM; labelled)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -124,6 +132,104 @@ def copy_calibration(mib):
         dsts[i % 2].copy_(srcs[(i // 2) % 2])
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 8}), flush=True)
+
+
+def attention_bench(args):
+    """The int8 prefill attention: one JSON line in the same format."""
+    import numpy as np
+    import torch
+    from bit_group_quantized_act_amd import synth, w4a8
+    w4a8.load()
+    dev = torch.device("cuda:0")
+    A = synth.make_attn(args.attn)
+    c = A["cfg"]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    AL, packed = w4a8.attn_pack_kv(t(A["k8"]), t(A["ks"]), t(A["v8"]), t(A["vs"]), t(A["kvpos"]))
+    q = t(A["q"])
+    nh, nq, d = c.nh, c.nq, c.d
+    out = (torch.empty((nh, nq, d), dtype=torch.float32, device=dev),
+           torch.empty((nh, nq), dtype=torch.float32, device=dev),
+           torch.empty((nh, nq), dtype=torch.float32, device=dev),
+           torch.empty((nh, nq, d), dtype=torch.int8, device=dev),
+           torch.empty((nh, nq), dtype=torch.float32, device=dev))
+    need = w4a8.load().w4a8_attn_work_bytes(__import__("ctypes").byref(AL), nh, nq)
+    work = torch.empty(max(1, need // 4), dtype=torch.float32, device=dev)
+    # visible (query, slot) pairs, from the positions (the same rule the kernel applies)
+    tq = A["pos0"] + np.arange(nq)[:, None]
+    p = A["kvpos"][None, :].astype(np.int64)
+    vis = (p >= 0) & (p <= tq)
+    if c.window > 0:
+        vis &= (p < c.sink) | (tq - p < c.window)
+    ops = 4 * nh * d * int(vis.sum())            # QK and AV: 2 ops per multiply-add each
+    stream = torch.cuda.Stream()
+
+    def call():
+        w4a8.attn_prefill(AL, packed, q, A["pos0"], c.window, c.sink, A["scale"], out=out,
+                          work=work)
+
+    def graph(count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            call()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(count):
+                    call()
+        torch.cuda.synchronize()
+        return g
+
+    def timed(g):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    if args.warmup > 0:
+        timed(graph(args.warmup))
+    g = graph(args.steps)
+    timed(g)
+    ms = timed(g) / args.steps
+    tops = ops / (ms * 1e-3) / 1e12
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle                      # the CPU baseline leg (test infrastructure)
+        hq = c.nh // c.nkvh                # one key/value head and its query heads
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            q8, sq = oracle.attn_quant_q(A["q"][:hq])
+            kq, sk = oracle.attn_requant_k(A["k8"][:1], A["ks"][:1])
+            oracle.attn_int8(q8, sq, kq, sk, A["v8"][:1], A["vs"][:1], A["kvpos"], A["pos0"],
+                             c.window, c.sink, A["scale"])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        cpu = dict(value=round(ops * hq / nh * reps / el / 1e12, 5), unit="TOPS",
+                   cores=oracle.num_threads(), kind="oracle",
+                   sample=f"{hq} of the {nh} query heads (one key/value head) of {c.name}, "
+                          f"repeated {reps}x in {el:.1f} s")
+    line = {
+        "metric": "int8 prefill attention over a cached segment: int8 TOPS of QK and AV",
+        "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"{c.name}: {nh} query heads on {c.nkvh} key/value heads, "
+                               f"head_dim {d}, {nq} queries against {c.nkv} cached int8 slots"
+                               + (f", window {c.window} with {c.sink} sinks over a rolled ring"
+                                  if c.window else ", global layer"),
+                   "visible_pairs_per_head": int(vis.sum()), "parallelism": "single GPU"},
+        "roofline": dict(bound="mfma", achieved=round(tops, 3), peak=INT8_PEAK_TOPS,
+                         unit="TOPS", frac=round(tops / INT8_PEAK_TOPS, 5), traffic=None,
+                         kernel="attn_kernel (+ attn_merge)", kernel_us=round(ms * 1000, 3),
+                         int_ops_per_launch=ops),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def workload_name(cfg, glu=None, cap=None, a16=False):
@@ -163,6 +269,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration_mib > 0:
         copy_calibration(args.copy_calibration_mib)
+        return
+    if args.attn is not None:
+        attention_bench(args)
         return
     w4a8.load()   # fails loudly if the HIP library is not built
     dev = torch.device("cuda:0")

@@ -20,9 +20,12 @@
 //   AV with unsigned P on a signed MFMA: u - 128 enters the i8 product and 128 * (the block's
 //   column sum) is added back in int32, exactly.
 //   Kernel: a workgroup of 4 wavefronts per (query head, 32-query tile, slot range); each
-//   wavefront takes every 4th block of the range, keeps its own (O, m, l) in registers and skips
+//   wavefront takes every 4th block of the range (head_dim 256: every 2nd block and half of the
+//   value groups, to keep its output state in registers), keeps its own (O, m, l) and skips
 //   blocks no query of the tile sees; the wavefronts merge through LDS, and ranges split over
-//   several workgroups (to fill the chip) merge in a second kernel, both in a fixed order.
+//   several workgroups (to fill the chip) merge in a second kernel, both in a fixed order.  The
+//   next value group's scales, codes and column sums load while the current one is quantized;
+//   the codes are P' * (255 / max P'), one reciprocal per (row, group, block).
 #include "w4a8_kernels.h"
 
 namespace w4a8 {
@@ -112,16 +115,22 @@ __device__ __forceinline__ float wave_max32(float v) {          // max with the 
     return fmaxf(v, __shfl_xor(v, 32, 64));
 }
 
-template <int D>
+// DS = 2 (head_dim 256) splits the value groups over wavefront pairs: wavefront w takes groups
+// (w / 2) * NG/2 .. +NG/2-1 of every second block (w % 2), so its output state is half as large
+// (both of a pair compute the block's QK product and softmax, identically).
+template <int D, int DS>
 __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
                                                         const uint8_t *__restrict__ packed,
                                                         const AttnArgs a) {
 #pragma clang fp contract(off)
-    constexpr int NG = D / 32;
+    constexpr int NG = D / 32;           // value groups of the head
+    constexpr int NGW = NG / DS;         // value groups of this wavefront
+    constexpr int BL = kAW / DS;         // wavefronts sharing a group set (one block each)
     __shared__ float xm[kAW][kQT];
     __shared__ float xo[kAW - 1][64][16];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int dpart = wave / BL, blane = wave % BL;
     const int half = lane >> 5, col = lane & 31;
     const int qtiles = (a.nq + kQT - 1) / kQT;
     const int split = blockIdx.x % a.nsplit;
@@ -182,24 +191,35 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     const int32_t *vsb = reinterpret_cast<const int32_t *>(packed + ag.off_vsum) + (int64_t)kh * ag.nblk * D;
 
     float mrun = kNegInf, lrun = 0.0f;
-    v16f o[NG];
+    v16f o[NGW];
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+    for (int g = 0; g < NGW; ++g)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[g][e] = 0.0f;
 
     const int b_lo = split * a.bps;
     const int b_hi = min(ag.nblk, b_lo + a.bps);
-    for (int b = b_lo + wave; b < b_hi; b += kAW) {
+    for (int b = b_lo + blane; b < b_hi; b += BL) {
         // positions and visibility of the lane's 32 slots (two subtiles of 16)
         float s[2][16];
+        float skv[2][16];
         bool any = false;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int base = b * kSlots + t * 32 + half * 16;
+            int pos16[16];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int4 pv = reinterpret_cast<const int4 *>(posb + base)[c];
+                const float4 kv = reinterpret_cast<const float4 *>(skb + base)[c];
+                pos16[4 * c] = pv.x; pos16[4 * c + 1] = pv.y; pos16[4 * c + 2] = pv.z;
+                pos16[4 * c + 3] = pv.w;
+                skv[t][4 * c] = kv.x; skv[t][4 * c + 1] = kv.y; skv[t][4 * c + 2] = kv.z;
+                skv[t][4 * c + 3] = kv.w;
+            }
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t p = posb[base + e];
+                const int64_t p = pos16[e];
                 const bool vis = qlive && p >= 0 && p <= qpos &&
                                  (a.window <= 0 || p < a.sink || qpos - p < a.window);
                 s[t][e] = vis ? 0.0f : kNegInf;
@@ -217,10 +237,9 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
                 const v4i ka = *reinterpret_cast<const v4i *>(kr + 32 * i);
                 acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qb[i], acc, 0, 0, 0);
             }
-            const int base = b * kSlots + t * 32 + half * 16;
 #pragma unroll
             for (int e = 0; e < 16; ++e)
-                if (s[t][e] == 0.0f) s[t][e] = static_cast<float>(acc[e]) * qscale * skb[base + e];
+                if (s[t][e] == 0.0f) s[t][e] = static_cast<float>(acc[e]) * qscale * skv[t][e];
         }
         float mb = kNegInf;
 #pragma unroll
@@ -242,93 +261,126 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
         lrun = lrun * alpha + psum;
         mrun = (mb == kNegInf) ? mrun : mnew;
         const float keep = (mb == kNegInf) ? 1.0f : alpha;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            // P folded with the value group's scale, quantized to u8 per (row, group, block)
-            float pg[2][16];
-            float mx = 0.0f;
+        // the value side of group g: its scales for the lane's 32 slots, the transposed value
+        // codes (A operands) and the column sums; loaded one group ahead of their use
+        struct VGroup {
+            float4 sv[2][4];
+            v4i va[2];
+            int4 vsum[4];
+        };
+        auto load_group = [&](int g, VGroup &v) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const float *svr = svb + ((int64_t)b * NG + g) * kSlots + t * 32 + half * 16;
+                const float4 *svr = reinterpret_cast<const float4 *>(
+                    svb + ((int64_t)b * NG + g) * kSlots + t * 32 + half * 16);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    pg[t][e] = p[t][e] * svr[e];
-                    mx = fmaxf(mx, pg[t][e]);
-                }
+                for (int c = 0; c < 4; ++c) v.sv[t][c] = svr[c];
+                v.va[t] = *reinterpret_cast<const v4i *>(
+                    vtb + ((int64_t)b * D + 32 * g + col) * kSlots + t * 32 + half * 16);
             }
+            const int4 *vsr = reinterpret_cast<const int4 *>(vsb + (int64_t)b * D + g * 32 + half * 16);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v.vsum[c] = vsr[c];
+        };
+        VGroup vg[2];
+        load_group(dpart * NGW, vg[0]);
+#pragma unroll
+        for (int g = 0; g < NGW; ++g) {
+            VGroup &cur = vg[g & 1];
+            if (g + 1 < NGW) load_group(dpart * NGW + g + 1, vg[(g + 1) & 1]);
+            // P folded with the value group's scale, quantized to u8 per (row, group, block)
+            float mx = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float4 sv = cur.sv[t][c];
+                    mx = fmaxf(mx, fmaxf(fmaxf(p[t][4 * c] * sv.x, p[t][4 * c + 1] * sv.y),
+                                         fmaxf(p[t][4 * c + 2] * sv.z, p[t][4 * c + 3] * sv.w)));
+                }
             mx = wave_max32(mx);
             const float sp = mx / 255.0f;
+            const float rsp = 255.0f / mx;        // one reciprocal per (row, group, block)
             v16i iacc = {};
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 uint32_t w4[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int u = (mx > 0.0f) ? static_cast<int>(fminf(rintf(pg[t][e] / sp), 255.0f)) : 0;
-                    w4[e >> 2] |= static_cast<uint32_t>((u - 128) & 0xFF) << (8 * (e & 3));
+                for (int c = 0; c < 4; ++c) {
+                    const float sv4[4] = {cur.sv[t][c].x, cur.sv[t][c].y, cur.sv[t][c].z,
+                                          cur.sv[t][c].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float pg = p[t][4 * c + i] * sv4[i];
+                        const int u = (mx > 0.0f) ? static_cast<int>(fminf(rintf(pg * rsp), 255.0f)) : 0;
+                        w4[c] |= static_cast<uint32_t>((u - 128) & 0xFF) << (8 * i);
+                    }
                 }
                 const v4i pb = {static_cast<int>(w4[0]), static_cast<int>(w4[1]),
                                 static_cast<int>(w4[2]), static_cast<int>(w4[3])};
-                const v4i va = *reinterpret_cast<const v4i *>(
-                    vtb + ((int64_t)b * D + 32 * g + col) * kSlots + t * 32 + half * 16);
-                iacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, pb, iacc, 0, 0, 0);
+                iacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.va[t], pb, iacc, 0, 0, 0);
             }
-            const int32_t *vsr = vsb + (int64_t)b * D + g * 32 + half * 16;
+            const int vs16[16] = {cur.vsum[0].x, cur.vsum[0].y, cur.vsum[0].z, cur.vsum[0].w,
+                                  cur.vsum[1].x, cur.vsum[1].y, cur.vsum[1].z, cur.vsum[1].w,
+                                  cur.vsum[2].x, cur.vsum[2].y, cur.vsum[2].z, cur.vsum[2].w,
+                                  cur.vsum[3].x, cur.vsum[3].y, cur.vsum[3].z, cur.vsum[3].w};
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float av = static_cast<float>(iacc[e] + 128 * vsr[e]);
+                const float av = static_cast<float>(iacc[e] + 128 * vs16[e]);
                 o[g][e] = o[g][e] * keep + ((mx > 0.0f) ? sp * av : 0.0f);
             }
         }
     }
 
-    // merge the wavefronts' states (fixed order): M = max m_w, each scaled by e^(m_w - M)
+    // merge the states of the BL wavefronts of each group set (fixed order): M = max m_w, each
+    // scaled by e^(m_w - M); the two group sets of DS = 2 hold the same (m, l)
     const float lw = lrun + __shfl_xor(lrun, 32, 64);
     if (half == 0) xm[wave][col] = mrun;
     __syncthreads();
-    float mall = xm[0][col];
+    float mall = xm[dpart * BL][col];
 #pragma unroll
-    for (int w = 1; w < kAW; ++w) mall = fmaxf(mall, xm[w][col]);
+    for (int w = 1; w < BL; ++w) mall = fmaxf(mall, xm[dpart * BL + w][col]);
     const float mine = (mrun == kNegInf) ? 0.0f : expf(mrun - mall);
     __syncthreads();
     if (half == 0) xm[wave][col] = lw * mine;
     __syncthreads();
     float lsum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kAW; ++w) lsum += xm[w][col];
+    for (int w = 0; w < BL; ++w) lsum += xm[dpart * BL + w][col];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        if (wave != 0)
+    for (int g = 0; g < NGW; ++g) {
+        if (blane != 0)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) xo[wave - 1][lane][e] = o[g][e] * mine;
+            for (int e = 0; e < 16; ++e) xo[dpart * (BL - 1) + blane - 1][lane][e] = o[g][e] * mine;
         __syncthreads();
-        if (wave == 0) {
+        if (blane == 0) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 float v = o[g][e] * mine;
 #pragma unroll
-                for (int w = 1; w < kAW; ++w) v += xo[w - 1][lane][e];
+                for (int w = 1; w < BL; ++w) v += xo[dpart * (BL - 1) + w - 1][lane][e];
                 o[g][e] = v;
             }
         }
         __syncthreads();
     }
-    if (wave != 0 || !qlive) return;
+    if (blane != 0 || !qlive) return;
     const int64_t row = (int64_t)head * a.nq + qi;
     float *orow;
+    const bool stats = dpart == 0 && half == 0;
     if (a.nsplit == 1) {
         orow = a.o + row * D;
-        if (half == 0) { a.m[row] = mall; a.l[row] = lsum; }
+        if (stats) { a.m[row] = mall; a.l[row] = lsum; }
     } else {
         float *ws = a.work + ((int64_t)split * a.nh * a.nq + row) * (D + 2);
         orow = ws;
-        if (half == 0) { ws[D] = mall; ws[D + 1] = lsum; }
+        if (stats) { ws[D] = mall; ws[D + 1] = lsum; }
     }
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+    for (int g = 0; g < NGW; ++g)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-            orow[32 * g + 8 * (e >> 2) + 4 * half + (e & 3)] = o[g][e];
+            orow[32 * (dpart * NGW + g) + 8 * (e >> 2) + 4 * half + (e & 3)] = o[g][e];
 }
 
 // the split states of each (head, query) merged in split order
@@ -358,7 +410,7 @@ __global__ __launch_bounds__(256) void attn_merge(int nsplit, int64_t rows, int 
 int attn_splits(int nh, int nq, int nblk) {
     const int tiles = nh * ((nq + kQT - 1) / kQT);
     int s = (512 + tiles - 1) / tiles;                 // aim at two workgroups per CU
-    s = max(1, min(s, (nblk + kAW - 1) / kAW));        // at least one block per wavefront
+    s = max(1, min(s, (nblk + kAW - 1) / kAW));        // about one block per wavefront
     return s;
 }
 
@@ -383,9 +435,9 @@ hipError_t launch_attn(const AttnGeom &ag, const uint8_t *packed, const float *q
                l, work};
     a.bps = (ag.nblk + a.nsplit - 1) / a.nsplit;
     const unsigned grid = static_cast<unsigned>(nh * ((nq + kQT - 1) / kQT) * a.nsplit);
-    if (ag.d == 64) attn_kernel<64><<<grid, 64 * kAW, 0, stream>>>(ag, packed, a);
-    else if (ag.d == 128) attn_kernel<128><<<grid, 64 * kAW, 0, stream>>>(ag, packed, a);
-    else attn_kernel<256><<<grid, 64 * kAW, 0, stream>>>(ag, packed, a);
+    if (ag.d == 64) attn_kernel<64, 1><<<grid, 64 * kAW, 0, stream>>>(ag, packed, a);
+    else if (ag.d == 128) attn_kernel<128, 1><<<grid, 64 * kAW, 0, stream>>>(ag, packed, a);
+    else attn_kernel<256, 2><<<grid, 64 * kAW, 0, stream>>>(ag, packed, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     const int64_t n = (int64_t)nh * nq * ag.d;
