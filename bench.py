@@ -71,7 +71,7 @@ KERNEL_SOURCES = {
     "gemm": ["gemm.hip", "w4a8_kernels.h"],
 }
 TRAFFIC = {
-    "C2a": dict(kernel="gemv", source_sha="390ee810759e881f", fetch_kib=8767.26, write_kib=66.25,
+    "C2a": dict(kernel="gemv", source_sha="b3fb8338e57ea99c", fetch_kib=8767.25, write_kib=66.25,
                 fetch_factor=1.99979, write_factor=1.0),
 }
 
