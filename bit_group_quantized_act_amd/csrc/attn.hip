@@ -19,12 +19,13 @@
 //   value codes.
 //   AV with unsigned P on a signed MFMA: u - 128 enters the i8 product and 128 * (the block's
 //   column sum) is added back in int32, exactly.
+//   Queries: a prepass writes the int8 codes and row scales once; the attention kernel loads them.
 //   Kernel: a workgroup of 4 wavefronts per (query head, 32-query tile, slot range); each
 //   wavefront takes every 4th block of the range (head_dim 256: every 2nd block and half of the
 //   value groups, to keep its output state in registers), keeps its own (O, m, l) and skips
 //   blocks no query of the tile sees; the wavefronts merge through LDS, and ranges split over
 //   several workgroups (to fill the chip) merge in a second kernel, both in a fixed order.  The
-//   next value group's scales, codes and column sums load while the current one is quantized;
+//   next value group's scales, codes and column sums load as soon as the current group's are used;
 //   the codes are P' * (255 / max P'), one reciprocal per (row, group, block).
 #include "w4a8_kernels.h"
 
@@ -141,46 +142,15 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     const bool qlive = qi < a.nq;
     const int64_t qpos = (int64_t)a.pos0 + qi;
 
-    // the query row's int8 codes (one flat scale per row), as the B operands of the QK product:
+    // the query row's int8 codes (from the query prepass), as the B operands of the QK product:
     // lane (q, h) holds d = 32i + 16h .. +15 of each 32-wide chunk i
     v4i qb[NG];
-    float sq;
-    {
-        float x[NG][16];
-        float amax = 0.0f;
-        const float *qr = a.q + ((int64_t)head * a.nq + (qlive ? qi : 0)) * D;
+    const int64_t qrow = (int64_t)head * a.nq + (qlive ? qi : 0);
 #pragma unroll
-        for (int i = 0; i < NG; ++i) {
-#pragma unroll
-            for (int c = 0; c < 16; c += 4) {
-                const float4 v = qlive ? *reinterpret_cast<const float4 *>(qr + 32 * i + 16 * half + c)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-                x[i][c] = v.x; x[i][c + 1] = v.y; x[i][c + 2] = v.z; x[i][c + 3] = v.w;
-                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-            }
-        }
-        amax = wave_max32(amax);
-        sq = amax / 127.0f;
-#pragma unroll
-        for (int i = 0; i < NG; ++i) {
-            uint32_t w4[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                int cq = 0;
-                if (amax > 0.0f) cq = static_cast<int>(fminf(fmaxf(rintf(x[i][c] / sq), -127.0f), 127.0f));
-                w4[c >> 2] |= (static_cast<uint32_t>(cq) & 0xFFu) << (8 * (c & 3));
-            }
-            qb[i] = v4i{static_cast<int>(w4[0]), static_cast<int>(w4[1]), static_cast<int>(w4[2]),
-                        static_cast<int>(w4[3])};
-        }
-        if (wave == 0 && split == 0 && qlive) {
-            int8_t *q8r = a.q8 + ((int64_t)head * a.nq + qi) * D;
-#pragma unroll
-            for (int i = 0; i < NG; ++i)
-                *reinterpret_cast<v4i *>(q8r + 32 * i + 16 * half) = qb[i];
-            if (half == 0) a.sq[(int64_t)head * a.nq + qi] = sq;
-        }
-    }
+    for (int i = 0; i < NG; ++i)
+        qb[i] = qlive ? *reinterpret_cast<const v4i *>(a.q8 + qrow * D + 32 * i + 16 * half)
+                      : v4i{0, 0, 0, 0};
+    const float sq = qlive ? a.sq[qrow] : 0.0f;
     const float qscale = sq * a.scale;
 
     const int8_t *kqb = reinterpret_cast<const int8_t *>(packed + ag.off_kq) + (int64_t)kh * ag.nblk * kSlots * D;
@@ -202,7 +172,6 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     for (int b = b_lo + blane; b < b_hi; b += BL) {
         // positions and visibility of the lane's 32 slots (two subtiles of 16)
         float s[2][16];
-        float skv[2][16];
         bool any = false;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -211,11 +180,8 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int4 pv = reinterpret_cast<const int4 *>(posb + base)[c];
-                const float4 kv = reinterpret_cast<const float4 *>(skb + base)[c];
                 pos16[4 * c] = pv.x; pos16[4 * c + 1] = pv.y; pos16[4 * c + 2] = pv.z;
                 pos16[4 * c + 3] = pv.w;
-                skv[t][4 * c] = kv.x; skv[t][4 * c + 1] = kv.y; skv[t][4 * c + 2] = kv.z;
-                skv[t][4 * c + 3] = kv.w;
             }
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -237,9 +203,16 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
                 const v4i ka = *reinterpret_cast<const v4i *>(kr + 32 * i);
                 acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qb[i], acc, 0, 0, 0);
             }
+            const float4 *skr = reinterpret_cast<const float4 *>(skb + b * kSlots + t * 32 + half * 16);
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (s[t][e] == 0.0f) s[t][e] = static_cast<float>(acc[e]) * qscale * skv[t][e];
+            for (int c = 0; c < 4; ++c) {
+                const float4 kv = skr[c];
+                const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (s[t][4 * c + i] == 0.0f)
+                        s[t][4 * c + i] = static_cast<float>(acc[4 * c + i]) * qscale * k4[i];
+            }
         }
         float mb = kNegInf;
 #pragma unroll
@@ -282,12 +255,12 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
 #pragma unroll
             for (int c = 0; c < 4; ++c) v.vsum[c] = vsr[c];
         };
-        VGroup vg[2];
-        load_group(dpart * NGW, vg[0]);
+        // one group's operands in flight: the next group's scales and codes load as soon as the
+        // current group's are consumed, overlapping its matrix product and epilogue
+        VGroup cur;
+        load_group(dpart * NGW, cur);
 #pragma unroll
         for (int g = 0; g < NGW; ++g) {
-            VGroup &cur = vg[g & 1];
-            if (g + 1 < NGW) load_group(dpart * NGW + g + 1, vg[(g + 1) & 1]);
             // P folded with the value group's scale, quantized to u8 per (row, group, block)
             float mx = 0.0f;
 #pragma unroll
@@ -324,6 +297,7 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
                                   cur.vsum[1].x, cur.vsum[1].y, cur.vsum[1].z, cur.vsum[1].w,
                                   cur.vsum[2].x, cur.vsum[2].y, cur.vsum[2].z, cur.vsum[2].w,
                                   cur.vsum[3].x, cur.vsum[3].y, cur.vsum[3].z, cur.vsum[3].w};
+            if (g + 1 < NGW) load_group(dpart * NGW + g + 1, cur);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const float av = static_cast<float>(iacc[e] + 128 * vs16[e]);
@@ -383,6 +357,31 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
             orow[32 * (dpart * NGW + g) + 8 * (e >> 2) + 4 * half + (e & 3)] = o[g][e];
 }
 
+// The query prepass: one lane per 4 inputs of a row (a row is D/4 lanes of one wavefront),
+// sq = max|row| / 127 and q8 = round-half-even(q / sq) in fp32, as the activation quantization.
+__global__ __launch_bounds__(256) void attn_quant_q(const float4 *__restrict__ q, int64_t quads,
+                                                    int lanes_per_row, int *__restrict__ q8,
+                                                    float *__restrict__ sq) {
+#pragma clang fp contract(off)
+    const int64_t t = blockIdx.x * (int64_t)256 + threadIdx.x;
+    const bool live = t < quads;
+    const float4 v = live ? q[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    for (int o = 1; o < lanes_per_row; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float scale = amax / 127.0f;
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t w = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int c = 0;
+        if (amax > 0.0f) c = static_cast<int>(fminf(fmaxf(rintf(e[i] / scale), -127.0f), 127.0f));
+        w |= (static_cast<uint32_t>(c) & 0xFFu) << (8 * i);
+    }
+    if (!live) return;
+    q8[t] = static_cast<int>(w);
+    if (t % lanes_per_row == 0) sq[t / lanes_per_row] = scale;
+}
+
 // the split states of each (head, query) merged in split order
 __global__ __launch_bounds__(256) void attn_merge(int nsplit, int64_t rows, int d,
                                                   const float *__restrict__ work,
@@ -431,6 +430,11 @@ hipError_t launch_attn(const AttnGeom &ag, const uint8_t *packed, const float *q
                        int pos0, int window, int sink, float scale, int8_t *q8, float *sq,
                        float *o, float *m, float *l, float *work, hipStream_t stream) {
     if (nq == 0) return hipSuccess;
+    const int64_t quads = (int64_t)nh * nq * ag.d / 4;
+    attn_quant_q<<<static_cast<unsigned>((quads + 255) / 256), 256, 0, stream>>>(
+        reinterpret_cast<const float4 *>(q), quads, ag.d / 4, reinterpret_cast<int *>(q8), sq);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
     AttnArgs a{q, nh, nq, pos0, window, sink, attn_splits(nh, nq, ag.nblk), 0, scale, q8, sq, o, m,
                l, work};
     a.bps = (ag.nblk + a.nsplit - 1) / a.nsplit;
