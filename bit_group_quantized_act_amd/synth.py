@@ -16,6 +16,7 @@ Canonical formats (consumed by both the HIP library and the oracle):
   scales     float16 [n, k/group]
   bias       float16 [n, k/group]            affine only
   codebook   int8    [n, 16]                 codebook only
+  (int8 weights: codes int8 [n, k], one signed byte per weight, with the same fp16 scales)
 
 Shapes and distributions follow the workloads the pages measure: Gemma-style decode GEMVs
 (K=2048, gate_up N=16384, o_proj N=2048), a 128-row prefill chunk of a 5120-wide model's fused
@@ -29,8 +30,8 @@ from __future__ import annotations
 from dataclasses import dataclass, field, replace
 import numpy as np
 
-FMT_SYM, FMT_AFFINE, FMT_CODEBOOK = 0, 1, 2
-FORMAT_NAMES = {FMT_SYM: "sym", FMT_AFFINE: "affine", FMT_CODEBOOK: "codebook"}
+FMT_SYM, FMT_AFFINE, FMT_CODEBOOK, FMT_INT8 = 0, 1, 2, 3
+FORMAT_NAMES = {FMT_SYM: "sym", FMT_AFFINE: "affine", FMT_CODEBOOK: "codebook", FMT_INT8: "int8"}
 
 _W_CHUNK_ROWS = 8192  # W is drawn in fixed row chunks so large heads stay within memory
 
@@ -151,6 +152,24 @@ def make_weights(cfg: LayerConfig, full_range: bool = False):
               * 5e-4).astype(np.float16)
         return pack_nibbles(idx), np.repeat(sc, ng // cols, axis=1), None, cb
     r = rng(cfg.cfg_id, cfg.w_variant, 2)
+    if cfg.fmt == FMT_INT8:
+        if full_range:
+            c = r.integers(-127, 128, size=(n, k), dtype=np.int8)
+            sc = (r.uniform(0.5, 1.5, size=(n, ng)) * cfg.w_sigma / 40.0).astype(np.float16)
+            return c, sc, None, None
+        codes = np.empty((n, k), np.int8)
+        scales = np.empty((n, ng), np.float16)
+        for r0 in range(0, n, _W_CHUNK_ROWS):
+            rows = min(_W_CHUNK_ROWS, n - r0)
+            w = r.standard_normal((rows, k), dtype=np.float32) * np.float32(cfg.w_sigma)
+            wg = w.reshape(rows, ng, g)
+            s16 = (np.abs(wg).max(axis=2) / np.float32(127.0)).astype(np.float16)
+            s32 = s16.astype(np.float32)[:, :, None]
+            with np.errstate(divide="ignore", invalid="ignore"):
+                q = np.where(s32 > 0, np.rint(wg / np.where(s32 > 0, s32, 1)), 0)
+            codes[r0:r0 + rows] = np.clip(q, -127, 127).astype(np.int8).reshape(rows, k)
+            scales[r0:r0 + rows] = s16
+        return codes, scales, None, None
     if full_range:
         c = r.integers(0, 16, size=(n, k), dtype=np.uint8)
         sc = (r.uniform(0.5, 1.5, size=(n, ng)) * cfg.w_sigma / 3.0).astype(np.float16)
@@ -190,7 +209,7 @@ def weight_bytes(cfg: LayerConfig) -> int:
     """Algorithmic weight bytes: nibbles + fp16 scales (+ fp16 bias) (+ int8 codebook); one
     scale (and bias) per row for a row-scaled head."""
     per_row = 1 if cfg.extra.get("row_scale") else cfg.k // cfg.group
-    b = cfg.n * cfg.k // 2 + 2 * cfg.n * per_row
+    b = cfg.n * cfg.k // (1 if cfg.fmt == FMT_INT8 else 2) + 2 * cfg.n * per_row
     if cfg.fmt == FMT_AFFINE:
         b += 2 * cfg.n * per_row
     if cfg.fmt == FMT_CODEBOOK:

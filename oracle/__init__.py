@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-FORMAT_SYM, FORMAT_AFFINE, FORMAT_CODEBOOK = 0, 1, 2
+FORMAT_SYM, FORMAT_AFFINE, FORMAT_CODEBOOK, FORMAT_INT8 = 0, 1, 2, 3
 
 _lib = None
 
@@ -136,13 +136,13 @@ def prep(x: np.ndarray, group: int, hadamard_block: int = 0):
 
 def partials(fmt: int, codes: np.ndarray, xq: np.ndarray, group: int, codebook=None):
     """Integer per-group partials D [m, n, k/group] (int32)."""
-    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    codes = np.ascontiguousarray(codes).view(np.uint8)      # int8 codes (format 3) as bytes
     xq = np.ascontiguousarray(xq, dtype=np.int8)
     if xq.ndim == 1:
         xq = xq[None, :]
     n = codes.shape[0]
     m, k = xq.shape
-    assert codes.shape[1] * 2 == k
+    assert codes.shape[1] * (1 if fmt == FORMAT_INT8 else 2) == k
     cb = None if codebook is None else np.ascontiguousarray(codebook, dtype=np.int8)
     d = np.empty((m, n, k // group), np.int32)
     _check(_load().oracle_partials(fmt, _ptr(codes), _ptr(cb), n, k, group, _ptr(xq), m,
@@ -153,7 +153,7 @@ def partials(fmt: int, codes: np.ndarray, xq: np.ndarray, group: int, codebook=N
 def linear(fmt: int, codes, scales_f16, xq, xs, xsum, group: int, bias_f16=None,
            codebook=None, with_terms: bool = True):
     """fp64 output y [m, n] (and the term magnitude T [m, n] if with_terms)."""
-    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    codes = np.ascontiguousarray(codes).view(np.uint8)      # int8 codes (format 3) as bytes
     scales = np.ascontiguousarray(scales_f16, dtype=np.float16).view(np.uint16)
     bias = None if bias_f16 is None else \
         np.ascontiguousarray(bias_f16, dtype=np.float16).view(np.uint16)
@@ -234,7 +234,7 @@ def prep_a16(x):
 def linear_a16(fmt: int, codes, scales_f16, xh, xsf, group: int = 64, bias_f16=None,
                codebook=None, with_terms: bool = True):
     """fp64 output y [m, n] of the fp16-activation linear (and its term magnitude T)."""
-    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    codes = np.ascontiguousarray(codes).view(np.uint8)      # int8 codes (format 3) as bytes
     scales = np.ascontiguousarray(scales_f16, dtype=np.float16).view(np.uint16)
     bias = None if bias_f16 is None else \
         np.ascontiguousarray(bias_f16, dtype=np.float16).view(np.uint16)

@@ -81,6 +81,10 @@
  *   format 1 (affine):     code is an unsigned u in [0, 15];        w_int = u
  *   format 2 (codebook):   code is an index j in [0, 15];           w_int = codebook[n][j]
  *                          (PR #697's CQ4: 4-bit codebook indices expanded to int8 by lookup)
+ *   format 3 (int8):       codes are int8 [n][k], one byte per weight; w_int = the byte
+ *                          ("geistlib issue #500", sections "Scope" and "Design sketch": the
+ *                          W8A8 inner kernel beside the W4A8 one, sharing the activation side;
+ *                          symmetric, one fp16 scale per group)
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared (no fast-math), so that every fp32
  * operation is a single IEEE-rounded operation in program order.
@@ -234,6 +238,8 @@ static int oracle_code(const uint8_t *codes, int64_t k_total, int64_t n, int64_t
 static int32_t oracle_weight_int(int format, const uint8_t *codes, const int8_t *codebook,
                                  int64_t k_total, int64_t n, int64_t k)
 {
+    if (format == 3)
+        return (int32_t)((const int8_t *)codes)[n * k_total + k];   /* one byte per weight */
     int c = oracle_code(codes, k_total, n, k);
     if (format == 0)
         return c >= 8 ? c - 16 : c;                 /* two's-complement nibble */
@@ -252,7 +258,7 @@ int oracle_partials(int32_t format, const uint8_t *codes, const int8_t *codebook
                     int64_t n, int64_t k, int32_t group, const int8_t *xq, int64_t m,
                     int32_t *d)
 {
-    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 2)
+    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 3)
         return ORACLE_BAD_ARGS;
     if (format == 2 && codebook == NULL)
         return ORACLE_BAD_ARGS;
@@ -290,7 +296,7 @@ int oracle_linear(int32_t format, const uint8_t *codes, const uint16_t *scales_f
                   const int8_t *xq, const float *xs, const int32_t *xsum, int64_t m,
                   double *y, double *t)
 {
-    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 2)
+    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 3)
         return ORACLE_BAD_ARGS;
     if ((format == 1 && bias_f16 == NULL) || (format == 2 && codebook == NULL))
         return ORACLE_BAD_ARGS;
@@ -476,7 +482,7 @@ int oracle_linear_a16(int32_t format, const uint8_t *codes, const uint16_t *scal
                       int32_t group, const uint16_t *xh, const float *xsf, int64_t m,
                       double *y, double *t)
 {
-    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 2)
+    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 3)
         return ORACLE_BAD_ARGS;
     if ((format == 1 && bias_f16 == NULL) || (format == 2 && codebook == NULL))
         return ORACLE_BAD_ARGS;

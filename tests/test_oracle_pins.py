@@ -785,3 +785,39 @@ def test_attn_int8_closed_forms():
     np.testing.assert_allclose(o / l[..., None], mean[:, None, :].repeat(8, axis=1),
                                rtol=1e-12, atol=1e-15)
     assert np.all(l == 130.0) and np.all(m == 0.0)
+
+
+
+# ---- int8 weights (W8A8, geistlib issue #500's W8A8 inner kernel beside the W4A8 one)
+
+def test_int8_weights_brute_force_and_partials():
+    rng = np.random.default_rng(41)
+    n, k, g, m = 12, 256, 64, 3
+    w8 = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    w8[0, :] = -127
+    w8[1, :] = 127
+    sc = (rng.uniform(0.5, 1.5, size=(n, k // g)) * 1e-3).astype(np.float16)
+    x = (rng.standard_normal((m, k)) * 2).astype(np.float32)
+    xq, xs, xsum = oracle.prep(x, g, 0)
+    d = oracle.partials(oracle.FORMAT_INT8, w8, xq, g)
+    want_d = np.einsum("mgk,ngk->mng", xq.astype(np.int64).reshape(m, k // g, g),
+                       w8.astype(np.int64).reshape(n, k // g, g))
+    assert np.array_equal(d, want_d)
+    y, t = oracle.linear(oracle.FORMAT_INT8, w8, sc, xq, xs, xsum, g)
+    want = np.einsum("mng,mg,ng->mn", want_d.astype(np.float64), xs.astype(np.float64),
+                     sc.astype(np.float64))
+    np.testing.assert_allclose(y, want, rtol=0, atol=1e-13 * t.max())
+
+
+def test_int8_weights_within_4_bits_equal_the_symmetric_format():
+    # codes in [-8, 7] as bytes or as two's-complement nibbles: the same layer
+    from bit_group_quantized_act_amd import synth
+    rng = np.random.default_rng(42)
+    n, k, g, m = 10, 256, 64, 2
+    q = rng.integers(-8, 8, size=(n, k)).astype(np.int8)
+    sc = (rng.uniform(0.5, 1.5, size=(n, k // g)) * 1e-3).astype(np.float16)
+    xq, xs, xsum = oracle.prep((rng.standard_normal((m, k)) * 3).astype(np.float32), g, 0)
+    y8 = oracle.linear(oracle.FORMAT_INT8, q, sc, xq, xs, xsum, g, with_terms=False)
+    y4 = oracle.linear(oracle.FORMAT_SYM, synth.pack_nibbles(q.astype(np.uint8) & 0xF), sc, xq,
+                       xs, xsum, g, with_terms=False)
+    assert np.array_equal(y8, y4)
