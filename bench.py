@@ -107,6 +107,8 @@ def parse():
     ap.add_argument("--argmax", type=float, default=None, metavar="CAP",
                     help="time w4a8_lm_head_argmax (soft cap CAP, 0 for none) on a one-row "
                          "workload instead")
+    ap.add_argument("--w8", action="store_true",
+                    help="the config's shape with int8 weights (format 3, W8A8) instead")
     ap.add_argument("--a16", action="store_true",
                     help="time the fp16-activation path (w4a8_linear_a16) instead")
     ap.add_argument("--attn", choices=["A1", "A2"], default=None,
@@ -238,7 +240,7 @@ def workload_name(cfg, glu=None, cap=None, a16=False):
     rot = ", 128-block WHT" if cfg.hadamard else ""
     if cfg.extra.get("row_scale"):
         rot += f", one scale per row seen as K/{cfg.group} groups"
-    fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072
+    fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072 and cfg.fmt != synth.FMT_INT8
     if a16:
         return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
                 f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights x fp16 activations (prepass writing "
@@ -277,7 +279,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    layer = synth.make(args.config)
+    layer = synth.make(args.config, **({"fmt": synth.FMT_INT8} if args.w8 else {}))
     cfg = layer["cfg"]
     t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     if "row_scales" in layer:      # one scale per row, packed through the row-scale view
@@ -288,9 +290,13 @@ def main():
         lay, packed0 = w4a8.pack(t(layer["codes"]), t(layer["scales"]), cfg.fmt, cfg.group,
                                  bias=t(layer["bias"]), codebook=t(layer["codebook"]))
     wbytes = synth.weight_bytes(cfg)
-    fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072   # w4a8_linear's one-kernel case
+    fused = (cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072     # w4a8_linear's one-kernel
+             and cfg.fmt != synth.FMT_INT8)                          # case (4-bit formats)
     cap = args.argmax
     a16 = args.a16
+    if (a16 or cap is not None or args.glu is not None) and cfg.fmt == synth.FMT_INT8:
+        print("--w8 times the plain linear only", file=sys.stderr)
+        sys.exit(2)
     if a16 and (cap is not None or args.glu is not None or cfg.group != 64 or
                 cfg.fmt == synth.FMT_CODEBOOK):
         print("--a16 needs a symmetric or affine 64-group workload and no --glu / --argmax",
@@ -412,10 +418,10 @@ def main():
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4))
     kname = "gemv" if cfg.m == 1 else "gemm"     # the fused kernel lives in gemv.hip
-    traffic_key = (cfg.name if act is None and cap is None and not a16 else
+    traffic_key = (cfg.name if act is None and cap is None and not a16 and cfg.fmt != synth.FMT_INT8 else
                    f"{cfg.name}-{'glu' if act is not None else 'argmax' if cap is not None else 'a16'}")
     shown = ("gemv_argmax (GEMV with the tail + key reduction)" if cap is not None else
-             f"{kname}_a16" if a16 else kname)
+             f"{kname}_a16" if a16 else f"{kname}_w8" if cfg.fmt == synth.FMT_INT8 else kname)
     roof.update(traffic=measured_traffic(traffic_key, kname), kernel=shown,
                 kernel_us=round(us_linear, 3), alg_bytes_per_launch=alg_bytes,
                 int_ops_per_launch=ops,

@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libw4a8.so")
 SOURCES = ["api.hip", "pack.hip", "prep.hip", "gemv.hip", "gemm.hip", "tail.hip", "a16.hip",
-           "attn.hip"]
+           "attn.hip", "w8.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -95,10 +95,15 @@ unsigned grid_for(int64_t total) {
 hipError_t launch_pack(const Geom &g, const uint8_t *codes, const uint16_t *scales,
                        const uint16_t *bias, const int8_t *codebook, uint8_t *packed,
                        hipStream_t stream, bool row_scale) {
-    const int64_t chunks = (int64_t)g.n_pad * (g.k / kChunkK);
-    pack_codes_kernel<<<grid_for(chunks), 256, 0, stream>>>(
-        codes, g.n, g.k, g.fmt, chunks, reinterpret_cast<uint4 *>(packed + g.off_codes));
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (g.fmt == kFmtInt8) {
+        e = launch_pack_codes_w8(g, reinterpret_cast<const int8_t *>(codes), packed, stream);
+    } else {
+        const int64_t chunks = (int64_t)g.n_pad * (g.k / kChunkK);
+        pack_codes_kernel<<<grid_for(chunks), 256, 0, stream>>>(
+            codes, g.n, g.k, g.fmt, chunks, reinterpret_cast<uint4 *>(packed + g.off_codes));
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     const int ng = g.k / g.group;
     const int64_t metas = (int64_t)g.n_pad * ((ng + 3) / 4) * 4;

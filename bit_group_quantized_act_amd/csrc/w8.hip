@@ -1,0 +1,300 @@
+// Int8 weights (W8A8): one signed byte per weight with one fp16 scale per group, against the
+// same int8 activations, scales and group sums as the 4-bit formats.
+//
+// Source: "geistlib issue #500: native W*A8 int8 GEMM for prefill", sections "Scope" and
+// "Design sketch": a W8A8 inner kernel beside the W4A8 one, both behind a load-time repack,
+// sharing the activation quantization; w8a8 GEMV and GEMM entry points.
+//   y[r][n] = sum_g xs[r][g] * sw[n][g] * D[r][n][g],  D = sum_{k in g} xq[r][k] * w8[n][k]
+//
+// Packed layout: the format's codes section holds, per 64-row panel and per 16-wide k chunk,
+// 64 rows x 16 bytes (chunk c of row r is w8[r][16c .. 16c+15]); the scales use the symmetric
+// format's blocked metadata.
+//
+// MI355X design.
+//   GEMV (one row): a workgroup per panel, 8 wavefronts over the groups, lane r on panel row r
+//   (a chunk load is one contiguous KiB per wavefront); v_dot4_i32_i8 of the weight bytes
+//   against the row's codes, which are wave-uniform and come through scalar loads; a ring of
+//   256 k of groups in flight per wavefront.
+//   GEMM: 64 rows x 128 channels per workgroup; each wavefront two 32x32 int32 tiles
+//   (v_mfma_i32_32x32x32_i8) sharing its weight bytes, which enter the matrix unit unchanged
+//   (lane (c, h) reads chunk 2j + h of its channel: k slots 16h .. 16h+15 of 32-wide block j);
+//   activation codes staged through two LDS buffers of 128 k (XOR-swizzled 16-byte units), a
+//   stage's codes, weight chunks, scales and activation scales loaded two stages ahead into a
+//   register ring.  Each group ends with coef = xs (x) sw as one outer product on the matrix
+//   unit (v_mfma_f32_32x32x2_f32) and acc += coef * float(D): a convert and an FMA per element.
+#include "w4a8_kernels.h"
+
+#include <type_traits>
+
+namespace w4a8 {
+namespace {
+
+constexpr int kW8Chunk = 16;        // k per 16-byte chunk
+constexpr int kW8Waves = 8;
+
+// ---- packing
+
+__global__ __launch_bounds__(256) void pack_codes_w8_kernel(const int8_t *__restrict__ w8, int n,
+                                                            int k, int64_t total,
+                                                            uint4 *__restrict__ out) {
+    const int kc = k / kW8Chunk;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int r = static_cast<int>(t % kPanelRows);
+        const int64_t rest = t / kPanelRows;
+        const int c = static_cast<int>(rest % kc);
+        const int64_t row = (rest / kc) * kPanelRows + r;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (row < n) v = *reinterpret_cast<const uint4 *>(w8 + row * (int64_t)k + (int64_t)c * kW8Chunk);
+        out[t] = v;
+    }
+}
+
+// ---- GEMV
+
+template <int G>
+__global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *__restrict__ packed,
+                                                                const Geom geom,
+                                                                const int *__restrict__ xq4,
+                                                                const float *__restrict__ xs,
+                                                                float *__restrict__ y) {
+    constexpr int CPG = G / kW8Chunk;                 // chunks per group
+    constexpr int RING = 256 / G;                     // groups in flight per wavefront
+    __shared__ float red[kW8Waves][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int p = blockIdx.x;
+    const int kc = geom.k / kW8Chunk;
+    const int ng = geom.k / G;
+    const int nblk = (ng + 3) / 4;
+    const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)p * kc * 1024,
+                                (uint64_t)kc * 1024);
+    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)p * nblk * 512,
+                                (uint64_t)nblk * 512);
+    v4i ring[RING][CPG];
+    uint32_t meta[RING];
+    auto load = [&](int s, int g) {
+#pragma unroll
+        for (int c = 0; c < CPG; ++c)
+            ring[s][c] = ld128(rc, g < ng ? ((g * CPG + c) * 64 + lane) * 16 : kOOB);
+        meta[s] = ld16(rm, g < ng ? (((g >> 2) * 64 + lane) * 4 + (g & 3)) * 2 : kOOB);
+    };
+#pragma unroll
+    for (int s = 0; s < RING; ++s) load(s, wave + s * kW8Waves);
+    float acc = 0.0f;
+    for (int g0 = wave; g0 < ng; g0 += RING * kW8Waves) {
+#pragma unroll
+        for (int s = 0; s < RING; ++s) {
+            const int g = g0 + s * kW8Waves;
+            if (g < ng) {
+                const int *xg = xq4 + g * (G / 4);       // the group's codes: wave-uniform
+                int d4[4] = {0, 0, 0, 0};
+#pragma unroll
+                for (int c = 0; c < CPG; ++c)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        d4[e] = __builtin_amdgcn_sdot4(ring[s][c][e], xg[4 * c + e], d4[e], false);
+                const int dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+                const float coef = xs[g] * half_bits_to_float(meta[s] & 0xFFFFu);
+                acc = fmaf(coef, static_cast<float>(dot), acc);
+            }
+            load(s, g + RING * kW8Waves);
+        }
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    float s = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < kW8Waves; ++w) s += red[w][lane];
+    const int row = p * kPanelRows + lane;
+    if (row < geom.n) y[row] = s;
+}
+
+// ---- GEMM
+
+constexpr int kW8BN = 128;          // channels per workgroup (4 wavefronts x 32)
+constexpr int kW8SK = 128;          // k per LDS stage: four 32-wide MFMA blocks
+
+template <int G>
+struct W8Stage {
+    static constexpr int GPS = kW8SK / G;             // groups per stage (2 or 1)
+    v4i a[2];                                         // two 16-byte activation units per thread
+    v4i b[4];                                         // the lane's chunk of each MFMA block
+    uint32_t meta[GPS];
+    float xs[GPS][2];                                 // per group and tile: the row's scale
+};
+
+template <int G>
+__global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restrict__ packed,
+                                                         const Geom geom, int m,
+                                                         const int8_t *__restrict__ xq,
+                                                         const float *__restrict__ xs,
+                                                         float *__restrict__ y) {
+    constexpr int GPS = kW8SK / G;
+    constexpr int BPG = G / 32;                       // MFMA blocks per group
+    __shared__ __attribute__((aligned(16))) v4i lds[2][64 * 8];   // [buf][row][16-byte unit]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+    const int r32 = lane & 31;
+
+    const int mtiles = (m + 63) / 64;
+    int bid = blockIdx.x;
+    const int nb = gridDim.x;
+    if (nb % 8 == 0) bid = (bid % 8) * (nb / 8) + bid / 8;   // consecutive tiles on one XCD
+    const int mt = bid % mtiles, nt = bid / mtiles;
+    const int m0 = mt * 64;
+    const int c0 = nt * kW8BN + wave * 32;
+    const bool wact = c0 < geom.n_pad;
+    const int col = c0 + r32;
+    const int p = col / kPanelRows, prow = col % kPanelRows;
+    const int k = geom.k;
+    const int kc = k / kW8Chunk;
+    const int ng = k / G;
+    const int nblk = (ng + 3) / 4;
+    const int nstage = (k + kW8SK - 1) / kW8SK;
+
+    const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)(wact ? p : 0) * kc * 1024,
+                                wact ? (uint64_t)kc * 1024 : 0);
+    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)(wact ? p : 0) * nblk * 512,
+                                wact ? (uint64_t)nblk * 512 : 0);
+    const rsrc_t rx = make_rsrc(xq, (uint64_t)m * k);
+    const rsrc_t rs = make_rsrc(xs, (uint64_t)ng * m * 4);
+
+    auto load_stage = [&](int s, W8Stage<G> &r) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int rr = i * 32 + (tid >> 3), u = tid & 7;
+            const int kk = s * kW8SK + 16 * u;
+            const bool ok = (m0 + rr < m) && (kk < k);
+            r.a[i] = ld128(rx, ok ? (m0 + rr) * k + kk : kOOB);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = s * (kW8SK / kW8Chunk) + 2 * j + half;
+            r.b[j] = ld128(rc, c < kc ? (c * 64 + prow) * 16 : kOOB);
+        }
+#pragma unroll
+        for (int q = 0; q < GPS; ++q) {
+            const int g = s * GPS + q;
+            r.meta[q] = ld16(rm, g < ng ? (((g >> 2) * 64 + prow) * 4 + (g & 3)) * 2 : kOOB);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int row = m0 + 32 * t + r32;
+                const bool ok = g < ng && half == 0 && row < m;
+                r.xs[q][t] = __builtin_bit_cast(float, ld32(rs, ok ? (g * m + row) * 4 : kOOB));
+            }
+        }
+    };
+    auto store_a = [&](int buf, const W8Stage<G> &r) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int rr = i * 32 + (tid >> 3), u = tid & 7;
+            lds[buf][rr * 8 + (u ^ (rr & 7))] = r.a[i];
+        }
+    };
+
+    v16f acc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+    const v16f zero16 = acc[0];
+    v16i part[2] = {};
+
+    W8Stage<G> ring[2];
+    load_stage(0, ring[0]);
+    if (nstage > 1) load_stage(1, ring[1]);
+    store_a(0, ring[0]);
+    __syncthreads();
+
+    auto stage = [&](auto slot_c, int s) {
+        constexpr int slot = decltype(slot_c)::value;
+        v4i b[4];
+        uint32_t meta[GPS];
+        float xsv[GPS][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = ring[slot].b[j];
+#pragma unroll
+        for (int q = 0; q < GPS; ++q) {
+            meta[q] = ring[slot].meta[q];
+            xsv[q][0] = ring[slot].xs[q][0];
+            xsv[q][1] = ring[slot].xs[q][1];
+        }
+        if (s + 2 < nstage) load_stage(s + 2, ring[slot]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int g = s * GPS + j / BPG;
+            if (g >= ng) break;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int rr = 32 * t + r32;
+                const v4i aop = lds[slot][rr * 8 + ((2 * j + half) ^ (rr & 7))];
+                part[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, b[j], part[t], 0, 0, 0);
+            }
+            if (j % BPG == BPG - 1) {                 // the group's last block: rescale
+                const int q = j / BPG;
+                const float sw = (half == 0) ? half_bits_to_float(meta[q] & 0xFFFFu) : 0.0f;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const v16f coef = __builtin_amdgcn_mfma_f32_32x32x2f32(xsv[q][t], sw, zero16,
+                                                                          0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        acc[t][e] = fmaf(coef[e], static_cast<float>(part[t][e]), acc[t][e]);
+                        part[t][e] = 0;
+                    }
+                }
+            }
+        }
+        if (s + 1 < nstage) store_a(slot ^ 1, ring[slot ^ 1]);
+        __syncthreads();
+    };
+    for (int s = 0; s < nstage; s += 2) {
+        stage(std::integral_constant<int, 0>{}, s);
+        if (s + 1 < nstage) stage(std::integral_constant<int, 1>{}, s + 1);
+    }
+
+    if (!wact || col >= geom.n) return;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = m0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+            if (row < m) y[(int64_t)row * geom.n + col] = acc[t][e];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pack_codes_w8(const Geom &g, const int8_t *w8, uint8_t *packed,
+                                hipStream_t stream) {
+    const int64_t chunks = (int64_t)g.n_pad * (g.k / kW8Chunk);
+    const int64_t blocks = (chunks + 255) / 256;
+    pack_codes_w8_kernel<<<static_cast<unsigned>(blocks < 65536 ? blocks : 65536), 256, 0, stream>>>(
+        w8, g.n, g.k, chunks, reinterpret_cast<uint4 *>(packed + g.off_codes));
+    return hipGetLastError();
+}
+
+hipError_t launch_w8(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
+                     const float *xs, float *y, hipStream_t stream) {
+    if (m == 0) return hipSuccess;
+    if (m == 1) {
+        const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
+        const int *x4 = reinterpret_cast<const int *>(xq);
+        if (g.group == 64)
+            gemv_w8_kernel<64><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+        else
+            gemv_w8_kernel<128><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+        return hipGetLastError();
+    }
+    const unsigned grid = static_cast<unsigned>(((m + 63) / 64) * ((g.n_pad + kW8BN - 1) / kW8BN));
+    if (g.group == 64) gemm_w8_kernel<64><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y);
+    else gemm_w8_kernel<128><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y);
+    return hipGetLastError();
+}
+
+}  // namespace w4a8

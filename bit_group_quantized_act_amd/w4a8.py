@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a8.so")
 
-SYM, AFFINE, CODEBOOK = 0, 1, 2
+SYM, AFFINE, CODEBOOK, INT8 = 0, 1, 2, 3
 PANEL_ROWS = 64
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "no gfx950 device", 4: "HIP error"}
 
@@ -133,13 +133,13 @@ def pack(codes: torch.Tensor, scales: torch.Tensor, fmt: int, group: int, bias=N
          codebook=None, out: torch.Tensor | None = None):
     """Repack canonical device weights.  Returns (layout, packed uint8 tensor of layout.bytes).
 
-    codes uint8 [n, k/2] (low nibble = even k); scales float16 [n, k/group];
-    bias float16 [n, k/group] (affine); codebook int8 [n, 16] (codebook).
+    codes uint8 [n, k/2] (low nibble = even k), or int8 [n, k] for INT8; scales float16
+    [n, k/group]; bias float16 [n, k/group] (affine); codebook int8 [n, 16] (codebook).
     """
     n, kh = codes.shape
-    k = 2 * kh
+    k = kh if fmt == INT8 else 2 * kh
     L = packed_layout(fmt, n, k, group)
-    _dev(codes, torch.uint8, "codes")
+    _dev(codes, torch.int8 if fmt == INT8 else torch.uint8, "codes")
     _dev(scales, torch.float16, "scales", (n, k // group))
     if bias is not None:
         _dev(bias, torch.float16, "bias", (n, k // group))

@@ -75,7 +75,7 @@ def test_layout_sizes():
 
 
 @pytest.mark.parametrize("args", [
-    (3, 64, 64, 64), (-1, 64, 64, 64), (0, 64, 96, 64), (0, 64, 64, 32), (0, 0, 64, 64),
+    (4, 64, 64, 64), (-1, 64, 64, 64), (0, 64, 96, 64), (0, 64, 64, 32), (0, 0, 64, 64),
     (0, 64, 0, 64), (0, 64, 64 * 3, 128), (0, 1 << 25, 64, 64), (0, 64, (1 << 20) + 64, 64),
 ])
 def test_layout_rejects(lib, args):
@@ -209,6 +209,18 @@ def test_invalid_calls_are_rejected_on_the_host(lib):
     assert lib.w4a8_linear_a16(ctypes.byref(cbl), p, 2, p, p, p, p, None) == ERR_UNSUPPORTED
     g128 = w4a8.packed_layout(w4a8.SYM, 128, 256, 128)
     assert lib.w4a8_gemm_a16(ctypes.byref(g128), p, 2, p, p, p, None) == ERR_ARG
+    # int8 weights: one byte per weight in the layout; the 4-bit-only entry points refuse them
+    L8 = w4a8.packed_layout(w4a8.INT8, 100, 256, 64)
+    L4 = w4a8.packed_layout(w4a8.SYM, 100, 256, 64)
+    assert L8.off_meta == 128 * 256 and L4.off_meta == 128 * 128 and L8.meta_bytes == 2
+    L8P = ctypes.byref(L8)
+    assert lib.w4a8_gemm_glu(ctypes.byref(w4a8.packed_layout(w4a8.INT8, 128, 256, 64)), p, 2, p,
+                             p, p, silu, p, None) == ERR_UNSUPPORTED
+    assert lib.w4a8_gemv_argmax(L8P, p, p, p, p, f(0.0), p, p, p, p, 16, None) == ERR_UNSUPPORTED
+    assert lib.w4a8_debug_partials(L8P, p, 2, p, p, p, None) == ERR_UNSUPPORTED
+    assert lib.w4a8_gemm_a16(L8P, p, 2, p, p, p, None) == ERR_UNSUPPORTED
+    assert lib.w4a8_gemm(ctypes.byref(w4a8.packed_layout(w4a8.INT8, 64, 1 << 20, 64)), p, 4096,
+                         p, p, p, p, None) == ERR_UNSUPPORTED                # m * k above 2^31
     # attention: layout limits, a forged layout, heads, negative arguments, scale, work size
     AL = w4a8.AttnLayout()
     assert lib.w4a8_attn_layout_init(2, 100, 96, ctypes.byref(AL)) == ERR_ARG
