@@ -20,8 +20,9 @@
 //   (lane (c, h) reads chunk 2j + h of its channel: k slots 16h .. 16h+15 of 32-wide block j);
 //   activation codes staged through two LDS buffers of 128 k (XOR-swizzled 16-byte units), a
 //   stage's codes, weight chunks, scales and activation scales loaded two stages ahead into a
-//   register ring.  Each group ends with coef = xs (x) sw as one outer product on the matrix
-//   unit (v_mfma_f32_32x32x2_f32) and acc += coef * float(D): a convert and an FMA per element.
+//   register ring.  Each group ends with coef = xs (x) sw for both tiles as one two-block outer
+//   product on the matrix unit (v_mfma_f32_32x32x1_2b_f32: block t = tile t) and
+//   acc += coef * float(D): a convert and an FMA per element.
 #include "w4a8_kernels.h"
 
 #include <type_traits>
@@ -122,8 +123,8 @@ struct W8Stage {
     v4i a[2];                                         // two 16-byte activation units per thread
     v4i b[4];                                         // the lane's chunk of each MFMA block
     uint32_t meta[GPS];
-    float xs[GPS][2];                                 // per group and tile: the row's scale
-};
+    float xs[GPS];                                    // per group: the scale of the lane's row
+};                                                    // (row r32 of tile `half`)
 
 template <int G>
 __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restrict__ packed,
@@ -180,12 +181,9 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
         for (int q = 0; q < GPS; ++q) {
             const int g = s * GPS + q;
             r.meta[q] = ld16(rm, g < ng ? (((g >> 2) * 64 + prow) * 4 + (g & 3)) * 2 : kOOB);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int row = m0 + 32 * t + r32;
-                const bool ok = g < ng && half == 0 && row < m;
-                r.xs[q][t] = __builtin_bit_cast(float, ld32(rs, ok ? (g * m + row) * 4 : kOOB));
-            }
+            const int row = m0 + 32 * half + r32;
+            const bool ok = g < ng && row < m;
+            r.xs[q] = __builtin_bit_cast(float, ld32(rs, ok ? (g * m + row) * 4 : kOOB));
         }
     };
     auto store_a = [&](int buf, const W8Stage<G> &r) {
@@ -201,7 +199,10 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
-    const v16f zero16 = acc[0];
+    v32f zero32;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) zero32[e] = 0.0f;
+    const v16i izero = {};
     v16i part[2] = {};
 
     W8Stage<G> ring[2];
@@ -214,14 +215,13 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
         constexpr int slot = decltype(slot_c)::value;
         v4i b[4];
         uint32_t meta[GPS];
-        float xsv[GPS][2];
+        float xsv[GPS];
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[j] = ring[slot].b[j];
 #pragma unroll
         for (int q = 0; q < GPS; ++q) {
             meta[q] = ring[slot].meta[q];
-            xsv[q][0] = ring[slot].xs[q][0];
-            xsv[q][1] = ring[slot].xs[q][1];
+            xsv[q] = ring[slot].xs[q];
         }
         if (s + 2 < nstage) load_stage(s + 2, ring[slot]);
 #pragma unroll
@@ -232,21 +232,22 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
             for (int t = 0; t < 2; ++t) {
                 const int rr = 32 * t + r32;
                 const v4i aop = lds[slot][rr * 8 + ((2 * j + half) ^ (rr & 7))];
-                part[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, b[j], part[t], 0, 0, 0);
+                // the group's first block starts from zero (no separate clear)
+                part[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, b[j],
+                                                                (j % BPG == 0) ? izero : part[t],
+                                                                0, 0, 0);
             }
             if (j % BPG == BPG - 1) {                 // the group's last block: rescale
                 const int q = j / BPG;
-                const float sw = (half == 0) ? half_bits_to_float(meta[q] & 0xFFFFu) : 0.0f;
+                const float sw = half_bits_to_float(meta[q] & 0xFFFFu);
+                // both tiles' coefficients in one two-block outer product: block t = tile t
+                const v32f coef = __builtin_amdgcn_mfma_f32_32x32x1f32(xsv[q], sw, zero32, 0, 0, 0);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const v16f coef = __builtin_amdgcn_mfma_f32_32x32x2f32(xsv[q][t], sw, zero16,
-                                                                          0, 0, 0);
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        acc[t][e] = fmaf(coef[e], static_cast<float>(part[t][e]), acc[t][e]);
-                        part[t][e] = 0;
-                    }
-                }
+                    for (int e = 0; e < 16; ++e)
+                        acc[t][e] = fmaf(coef[16 * t + e], static_cast<float>(part[t][e]),
+                                         acc[t][e]);
             }
         }
         if (s + 1 < nstage) store_a(slot ^ 1, ring[slot ^ 1]);
