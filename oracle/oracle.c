@@ -85,6 +85,11 @@
  *                          ("geistlib issue #500", sections "Scope" and "Design sketch": the
  *                          W8A8 inner kernel beside the W4A8 one, sharing the activation side;
  *                          symmetric, one fp16 scale per group)
+ *   format 4 (2-bit codebook): codes uint8 [n][k/4], byte b holding the indices of k = 4b .. 4b+3
+ *                          in bits 0-1, 2-3, 4-5, 6-7; w_int = codebook[n][index], a 4-entry
+ *                          int8 codebook per row ("cactus PR #697": the CQ1-CQ4 codebook family,
+ *                          of which this is CQ2; "geistlib issue #500", "Acceptance criteria":
+ *                          W2A8 models), one fp16 scale per group
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared (no fast-math), so that every fp32
  * operation is a single IEEE-rounded operation in program order.
@@ -240,6 +245,10 @@ static int32_t oracle_weight_int(int format, const uint8_t *codes, const int8_t 
 {
     if (format == 3)
         return (int32_t)((const int8_t *)codes)[n * k_total + k];   /* one byte per weight */
+    if (format == 4) {                                             /* four indices per byte */
+        int idx = (codes[n * (k_total / 4) + k / 4] >> (2 * (k % 4))) & 3;
+        return (int32_t)codebook[n * 4 + idx];
+    }
     int c = oracle_code(codes, k_total, n, k);
     if (format == 0)
         return c >= 8 ? c - 16 : c;                 /* two's-complement nibble */
@@ -258,9 +267,9 @@ int oracle_partials(int32_t format, const uint8_t *codes, const int8_t *codebook
                     int64_t n, int64_t k, int32_t group, const int8_t *xq, int64_t m,
                     int32_t *d)
 {
-    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 3)
+    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 4)
         return ORACLE_BAD_ARGS;
-    if (format == 2 && codebook == NULL)
+    if ((format == 2 || format == 4) && codebook == NULL)
         return ORACLE_BAD_ARGS;
     int64_t ng = k / group;
     int overflow = 0;
@@ -296,9 +305,9 @@ int oracle_linear(int32_t format, const uint8_t *codes, const uint16_t *scales_f
                   const int8_t *xq, const float *xs, const int32_t *xsum, int64_t m,
                   double *y, double *t)
 {
-    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 3)
+    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 4)
         return ORACLE_BAD_ARGS;
-    if ((format == 1 && bias_f16 == NULL) || (format == 2 && codebook == NULL))
+    if ((format == 1 && bias_f16 == NULL) || ((format == 2 || format == 4) && codebook == NULL))
         return ORACLE_BAD_ARGS;
     int64_t ng = k / group;
     int overflow = 0;
@@ -482,7 +491,7 @@ int oracle_linear_a16(int32_t format, const uint8_t *codes, const uint16_t *scal
                       int32_t group, const uint16_t *xh, const float *xsf, int64_t m,
                       double *y, double *t)
 {
-    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 3)
+    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 4)
         return ORACLE_BAD_ARGS;
     if ((format == 1 && bias_f16 == NULL) || (format == 2 && codebook == NULL))
         return ORACLE_BAD_ARGS;
