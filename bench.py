@@ -109,6 +109,8 @@ def parse():
                          "workload instead")
     ap.add_argument("--w8", action="store_true",
                     help="the config's shape with int8 weights (format 3, W8A8) instead")
+    ap.add_argument("--cq2", action="store_true",
+                    help="the config's shape with 2-bit codebook weights (format 4, CQ2) instead")
     ap.add_argument("--a16", action="store_true",
                     help="time the fp16-activation path (w4a8_linear_a16) instead")
     ap.add_argument("--attn", choices=["A1", "A2"], default=None,
@@ -240,7 +242,8 @@ def workload_name(cfg, glu=None, cap=None, a16=False):
     rot = ", 128-block WHT" if cfg.hadamard else ""
     if cfg.extra.get("row_scale"):
         rot += f", one scale per row seen as K/{cfg.group} groups"
-    fused = cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072 and cfg.fmt != synth.FMT_INT8
+    fused = (cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072 and
+             cfg.fmt not in (synth.FMT_INT8, synth.FMT_CQ2))
     if a16:
         return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
                 f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights x fp16 activations (prepass writing "
@@ -279,7 +282,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    layer = synth.make(args.config, **({"fmt": synth.FMT_INT8} if args.w8 else {}))
+    over = {"fmt": synth.FMT_INT8} if args.w8 else {"fmt": synth.FMT_CQ2} if args.cq2 else {}
+    layer = synth.make(args.config, **over)
+    byte_decoded = layer["cfg"].fmt in (synth.FMT_INT8, synth.FMT_CQ2)
     cfg = layer["cfg"]
     t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     if "row_scales" in layer:      # one scale per row, packed through the row-scale view
@@ -291,11 +296,11 @@ def main():
                                  bias=t(layer["bias"]), codebook=t(layer["codebook"]))
     wbytes = synth.weight_bytes(cfg)
     fused = (cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072     # w4a8_linear's one-kernel
-             and cfg.fmt != synth.FMT_INT8)                          # case (4-bit formats)
+             and not byte_decoded)                                   # case (4-bit formats)
     cap = args.argmax
     a16 = args.a16
-    if (a16 or cap is not None or args.glu is not None) and cfg.fmt == synth.FMT_INT8:
-        print("--w8 times the plain linear only", file=sys.stderr)
+    if (a16 or cap is not None or args.glu is not None) and byte_decoded:
+        print("--w8 / --cq2 time the plain linear only", file=sys.stderr)
         sys.exit(2)
     if a16 and (cap is not None or args.glu is not None or cfg.group != 64 or
                 cfg.fmt == synth.FMT_CODEBOOK):
@@ -418,10 +423,10 @@ def main():
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4))
     kname = "gemv" if cfg.m == 1 else "gemm"     # the fused kernel lives in gemv.hip
-    traffic_key = (cfg.name if act is None and cap is None and not a16 and cfg.fmt != synth.FMT_INT8 else
+    traffic_key = (cfg.name if act is None and cap is None and not a16 and not byte_decoded else
                    f"{cfg.name}-{'glu' if act is not None else 'argmax' if cap is not None else 'a16'}")
     shown = ("gemv_argmax (GEMV with the tail + key reduction)" if cap is not None else
-             f"{kname}_a16" if a16 else f"{kname}_w8" if cfg.fmt == synth.FMT_INT8 else kname)
+             f"{kname}_a16" if a16 else f"{kname}_w8" if byte_decoded else kname)
     roof.update(traffic=measured_traffic(traffic_key, kname), kernel=shown,
                 kernel_us=round(us_linear, 3), alg_bytes_per_launch=alg_bytes,
                 int_ops_per_launch=ops,

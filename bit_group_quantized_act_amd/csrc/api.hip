@@ -101,26 +101,32 @@ w4a8_status launched(hipError_t e, const char *what) {
 
 // Sizes the GEMM addresses with 32-bit offsets: the activation scales and sums of all rows
 // (m * k/group dwords) and the workgroup count.
+// Int8 and 2-bit codebook weights run through their own GEMV / GEMM.
+bool byte_decoded(const w4a8_layout *L) {
+    return L->format == W4A8_INT8 || L->format == W4A8_CQ2;
+}
+
+// Entry points whose kernels read only the 4-bit formats.
+w4a8_status reject_int8(const w4a8_layout *L, const char *what) {
+    if (byte_decoded(L))
+        return fail(W4A8_ERR_UNSUPPORTED, "%s takes the 4-bit formats, not format %d", what,
+                    L->format);
+    return W4A8_OK;
+}
+
 w4a8_status check_gemm_size(const w4a8_layout *L, int32_t m) {
     // (the GEMM's copies run up to 16 groups past the last one)
     const int64_t scales = static_cast<int64_t>(m) * (L->k / L->group + 16) * 4;
     if (scales > 0x7FFFFFF0ll)
         return fail(W4A8_ERR_UNSUPPORTED, "m * k/group = %lld scales exceed 2 GiB",
                     static_cast<long long>(scales / 4));
-    if (L->format == W4A8_INT8 && static_cast<int64_t>(m) * L->k > 0x7FFFFFF0ll)
+    if (byte_decoded(L) && static_cast<int64_t>(m) * L->k > 0x7FFFFFF0ll)
         return fail(W4A8_ERR_UNSUPPORTED, "m * k = %lld activation codes exceed 2^31 - 16",
                     static_cast<long long>(static_cast<int64_t>(m) * L->k));
     const int64_t tiles = static_cast<int64_t>((m + 63) / 64) * ((L->n_pad + 127) / 128);
     if (tiles > 0x7FFFFFFFll)
         return fail(W4A8_ERR_UNSUPPORTED, "%lld GEMM tiles exceed the grid",
                     static_cast<long long>(tiles));
-    return W4A8_OK;
-}
-
-// Entry points whose kernels read only the 4-bit formats.
-w4a8_status reject_int8(const w4a8_layout *L, const char *what) {
-    if (L->format == W4A8_INT8)
-        return fail(W4A8_ERR_UNSUPPORTED, "%s takes the 4-bit formats, not int8 weights", what);
     return W4A8_OK;
 }
 
@@ -179,7 +185,7 @@ extern "C" {
 w4a8_status w4a8_packed_layout(int32_t format, int32_t n, int32_t k, int32_t group,
                                w4a8_layout *L) {
     if (!L) return fail(W4A8_ERR_ARG, "layout is NULL");
-    if (format < W4A8_SYM_I4 || format > W4A8_INT8)
+    if (format < W4A8_SYM_I4 || format > W4A8_CQ2)
         return fail(W4A8_ERR_ARG, "format %d is not a w4a8_format", format);
     if (group != 64 && group != 128) return fail(W4A8_ERR_ARG, "group %d is not 64 or 128", group);
     if (n < 1 || n > (1 << 24)) return fail(W4A8_ERR_ARG, "n = %d is outside [1, 2^24]", n);
@@ -193,15 +199,16 @@ w4a8_status w4a8_packed_layout(int32_t format, int32_t n, int32_t k, int32_t gro
     L->group = group;
     L->n_pad = static_cast<int32_t>(round_up(n, W4A8_PANEL_ROWS));
     L->meta_bytes = (format == W4A8_AFFINE_U4) ? 4 : 2;
-    const uint64_t codes = static_cast<uint64_t>(L->n_pad) * k / (format == W4A8_INT8 ? 1 : 2);
+    const uint64_t codes = static_cast<uint64_t>(L->n_pad) * k /
+                           (format == W4A8_INT8 ? 1 : format == W4A8_CQ2 ? 4 : 2);
     // metadata in blocks of 4 groups (the last block zero-padded)
     const uint64_t meta = static_cast<uint64_t>(L->n_pad) * ((k / group + 3) / 4) * 4 * L->meta_bytes;
     L->off_codes = 0;
     L->off_meta = round_up(codes, 256);
     uint64_t end = L->off_meta + round_up(meta, 256);
-    if (format == W4A8_CODEBOOK_I4) {
+    if (format == W4A8_CODEBOOK_I4 || format == W4A8_CQ2) {
         L->off_codebook = end;
-        end += round_up(static_cast<uint64_t>(L->n_pad) * 16, 256);
+        end += round_up(static_cast<uint64_t>(L->n_pad) * (format == W4A8_CQ2 ? 4 : 16), 256);
     }
     L->bytes = end;
     return ok();
@@ -222,7 +229,7 @@ w4a8_status pack_checked(const w4a8_layout *L, const uint8_t *codes, const uint1
     } else if (bias_f16) {
         return fail(W4A8_ERR_ARG, "bias_f16 is only used by the affine format; pass NULL");
     }
-    if (L->format == W4A8_CODEBOOK_I4) {
+    if (L->format == W4A8_CODEBOOK_I4 || L->format == W4A8_CQ2) {
         W4A8_REQUIRE_PTR(codebook);
     } else if (codebook) {
         return fail(W4A8_ERR_ARG, "codebook is only used by the codebook format; pass NULL");
@@ -282,7 +289,7 @@ w4a8_status w4a8_gemv(const w4a8_layout *L, const void *packed, const int8_t *xq
     if ((s = check_activation_ptrs(xq, xs, xsum)) != W4A8_OK) return s;
     W4A8_REQUIRE_PTR(y);
     if ((s = check_device()) != W4A8_OK) return s;
-    if (L->format == W4A8_INT8)
+    if (byte_decoded(L))
         return launched(w4a8::launch_w8(geom_of(L), static_cast<const uint8_t *>(packed), 1, xq,
                                         xs, y, static_cast<hipStream_t>(stream)),
                         "int8-weight gemv launch");
@@ -304,7 +311,7 @@ w4a8_status w4a8_gemm(const w4a8_layout *L, const void *packed, int32_t m, const
     if ((s = check_activation_ptrs(xq, xs, xsum)) != W4A8_OK) return s;
     W4A8_REQUIRE_PTR(y);
     if ((s = check_device()) != W4A8_OK) return s;
-    if (L->format == W4A8_INT8)
+    if (byte_decoded(L))
         return launched(w4a8::launch_w8(geom_of(L), static_cast<const uint8_t *>(packed), m, xq,
                                         xs, y, static_cast<hipStream_t>(stream)),
                         "int8-weight gemm launch");
@@ -335,13 +342,13 @@ w4a8_status w4a8_linear(const w4a8_layout *L, const void *packed, int32_t m, con
     const w4a8::Geom g = geom_of(L);
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (L->format != W4A8_INT8 && m == 1 && L->k <= w4a8::kFusedMaxK &&
+    if (!byte_decoded(L) && m == 1 && L->k <= w4a8::kFusedMaxK &&
         L->n_pad / W4A8_PANEL_ROWS <= w4a8::kFusedMaxPanels)
         return launched(w4a8::launch_gemv_fused(g, pk, x, hadamard_block, xq, xs, xsum, y, st),
                         "fused gemv launch");
     hipError_t e = w4a8::launch_prep(x, m, L->k, L->group, hadamard_block, xq, xs, xsum, st);
     if (e != hipSuccess) return launched(e, "prep launch");
-    if (L->format == W4A8_INT8)
+    if (byte_decoded(L))
         return launched(w4a8::launch_w8(g, pk, m, xq, xs, y, st), "int8-weight linear launch");
     if (m == 1)
         return launched(w4a8::launch_gemv(g, pk, xq, xs, xsum, y, nullptr, st), "gemv launch");
@@ -468,7 +475,7 @@ w4a8_status check_prep_a16(const float *x, int32_t m, int32_t k, int32_t group, 
 w4a8_status check_linear_a16(const w4a8_layout *L, const void *packed, int32_t m, float *y) {
     w4a8_status s = check_layout(L);
     if (s != W4A8_OK) return s;
-    if (L->format == W4A8_CODEBOOK_I4 || L->format == W4A8_INT8)
+    if (L->format != W4A8_SYM_I4 && L->format != W4A8_AFFINE_U4)
         return fail(W4A8_ERR_UNSUPPORTED, "the fp16-activation path takes SYM or AFFINE weights");
     if (L->group != 64)
         return fail(W4A8_ERR_ARG, "group %d: the fp16-activation path sums 64-wide groups",

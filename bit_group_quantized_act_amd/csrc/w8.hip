@@ -1,14 +1,22 @@
-// Int8 weights (W8A8): one signed byte per weight with one fp16 scale per group, against the
-// same int8 activations, scales and group sums as the 4-bit formats.
+// Int8 weights (W8A8) and 2-bit codebook weights (CQ2 / W2A8), against the same int8 activations,
+// scales and group sums as the 4-bit formats; both decode to int8 weights in registers.
 //
 // Source: "geistlib issue #500: native W*A8 int8 GEMM for prefill", sections "Scope" and
 // "Design sketch": a W8A8 inner kernel beside the W4A8 one, both behind a load-time repack,
 // sharing the activation quantization; w8a8 GEMV and GEMM entry points.
 //   y[r][n] = sum_g xs[r][g] * sw[n][g] * D[r][n][g],  D = sum_{k in g} xq[r][k] * w8[n][k]
 //
-// Packed layout: the format's codes section holds, per 64-row panel and per 16-wide k chunk,
-// 64 rows x 16 bytes (chunk c of row r is w8[r][16c .. 16c+15]); the scales use the symmetric
-// format's blocked metadata.
+// 2-bit codebook: "cactus PR #697", the CQ1-CQ4 codebook family (this is CQ2: a 2-bit index per
+// weight into a per-row table of 4 int8 entries, one fp16 scale per group); "geistlib issue
+// #500", "Acceptance criteria" (W2A8 models).
+//
+// Packed layouts: per 64-row panel and per k chunk, 64 rows x 16 bytes.  Int8: chunk c of row r
+// is w8[r][16c .. 16c+15].  CQ2: a chunk holds 64 k as four 32-bit words in the k order
+// 0-15, 32-47, 16-31, 48-63, and in a word covering k = b .. b+15 the index of k = b + 4s + j sits
+// at bits 8j + 2s, so (w >> 2s) & 0x03030303 selects four consecutive weights and one v_perm
+// against the row's codebook dword turns them into int8; the words' order lets a GEMM lane half
+// read its two MFMA blocks of a chunk as one 8-byte run.  Scales: the symmetric format's blocked
+// metadata; CQ2's codebooks: one dword per row.
 //
 // MI355X design.
 //   GEMV (one row): a workgroup per panel, 8 wavefronts over the groups, lane r on panel row r
@@ -51,27 +59,71 @@ __global__ __launch_bounds__(256) void pack_codes_w8_kernel(const int8_t *__rest
     }
 }
 
+__global__ __launch_bounds__(256) void pack_codes_cq2_kernel(const uint8_t *__restrict__ codes,
+                                                             const int8_t *__restrict__ cb, int n,
+                                                             int k, int64_t total,
+                                                             uint4 *__restrict__ out,
+                                                             uint32_t *__restrict__ cb_out) {
+    const int kc = k / 64;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int r = static_cast<int>(t % kPanelRows);
+        const int64_t rest = t / kPanelRows;
+        const int c = static_cast<int>(rest % kc);
+        const int64_t row = (rest / kc) * kPanelRows + r;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if (row < n) {
+            const uint8_t *src = codes + row * (int64_t)(k / 4) + (int64_t)c * 16;   // 64 k
+            const int kq[4] = {0, 32, 16, 48};            // k offset of word position q
+            for (int q = 0; q < 4; ++q)
+                for (int s4 = 0; s4 < 4; ++s4)
+                    for (int j = 0; j < 4; ++j) {
+                        const int kk = kq[q] + 4 * s4 + j;                     // k within chunk
+                        const uint32_t idx = (src[kk / 4] >> (2 * (kk % 4))) & 3u;
+                        w[q] |= idx << (8 * j + 2 * s4);
+                    }
+        }
+        out[t] = make_uint4(w[0], w[1], w[2], w[3]);
+        if (c == 0) {
+            uint32_t v = 0u;
+            if (row < n)
+                for (int e = 0; e < 4; ++e)
+                    v |= static_cast<uint32_t>(static_cast<uint8_t>(cb[row * 4 + e])) << (8 * e);
+            cb_out[row] = v;
+        }
+    }
+}
+
+// Four int8 weights of k = b + 4s .. b + 4s + 3 from a CQ2 word (the layout above).
+__device__ __forceinline__ int cq2_dword(uint32_t w, int s, uint32_t cb) {
+    return static_cast<int>(__builtin_amdgcn_perm(cb, cb, (w >> (2 * s)) & 0x03030303u));
+}
+
 // ---- GEMV
 
-template <int G>
+template <int FMT, int G>
 __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *__restrict__ packed,
                                                                 const Geom geom,
                                                                 const int *__restrict__ xq4,
                                                                 const float *__restrict__ xs,
                                                                 float *__restrict__ y) {
-    constexpr int CPG = G / kW8Chunk;                 // chunks per group
-    constexpr int RING = 256 / G;                     // groups in flight per wavefront
+    constexpr int CK = (FMT == kFmtCQ2) ? 64 : kW8Chunk;   // k per chunk
+    constexpr int CPG = G / CK;                       // chunks per group
+    constexpr int RING = (FMT == kFmtCQ2) ? 4 : 256 / G;   // groups in flight per wavefront
     __shared__ float red[kW8Waves][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int p = blockIdx.x;
-    const int kc = geom.k / kW8Chunk;
+    const int kc = geom.k / CK;
     const int ng = geom.k / G;
     const int nblk = (ng + 3) / 4;
     const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)p * kc * 1024,
                                 (uint64_t)kc * 1024);
     const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)p * nblk * 512,
                                 (uint64_t)nblk * 512);
+    uint32_t cb = 0u;
+    if (FMT == kFmtCQ2)
+        cb = reinterpret_cast<const uint32_t *>(packed + geom.off_codebook)[p * kPanelRows + lane];
     v4i ring[RING][CPG];
     uint32_t meta[RING];
     auto load = [&](int s, int g) {
@@ -90,11 +142,24 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *_
             if (g < ng) {
                 const int *xg = xq4 + g * (G / 4);       // the group's codes: wave-uniform
                 int d4[4] = {0, 0, 0, 0};
+                if (FMT == kFmtCQ2) {
+                    constexpr int kq[4] = {0, 32, 16, 48};  // k offset of word position q
 #pragma unroll
-                for (int c = 0; c < CPG; ++c)
+                    for (int c = 0; c < CPG; ++c)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        d4[e] = __builtin_amdgcn_sdot4(ring[s][c][e], xg[4 * c + e], d4[e], false);
+                        for (int q = 0; q < 4; ++q)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                d4[e] = __builtin_amdgcn_sdot4(
+                                    cq2_dword(static_cast<uint32_t>(ring[s][c][q]), e, cb),
+                                    xg[(64 * c + kq[q]) / 4 + e], d4[e], false);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CPG; ++c)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            d4[e] = __builtin_amdgcn_sdot4(ring[s][c][e], xg[4 * c + e], d4[e], false);
+                }
                 const int dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
                 const float coef = xs[g] * half_bits_to_float(meta[s] & 0xFFFFu);
                 acc = fmaf(coef, static_cast<float>(dot), acc);
@@ -117,16 +182,17 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *_
 constexpr int kW8BN = 128;          // channels per workgroup (4 wavefronts x 32)
 constexpr int kW8SK = 128;          // k per LDS stage: four 32-wide MFMA blocks
 
-template <int G>
+template <int FMT, int G>
 struct W8Stage {
     static constexpr int GPS = kW8SK / G;             // groups per stage (2 or 1)
     v4i a[2];                                         // two 16-byte activation units per thread
-    v4i b[4];                                         // the lane's chunk of each MFMA block
+    v4i b[4];                                         // int8: the lane's chunk of each MFMA block
+    v2i w2[2];                                        // CQ2: the lane's 8 bytes of each chunk
     uint32_t meta[GPS];
     float xs[GPS];                                    // per group: the scale of the lane's row
 };                                                    // (row r32 of tile `half`)
 
-template <int G>
+template <int FMT, int G>
 __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restrict__ packed,
                                                          const Geom geom, int m,
                                                          const int8_t *__restrict__ xq,
@@ -152,10 +218,13 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
     const int col = c0 + r32;
     const int p = col / kPanelRows, prow = col % kPanelRows;
     const int k = geom.k;
-    const int kc = k / kW8Chunk;
+    const int kc = k / ((FMT == kFmtCQ2) ? 64 : kW8Chunk);
     const int ng = k / G;
     const int nblk = (ng + 3) / 4;
     const int nstage = (k + kW8SK - 1) / kW8SK;
+    uint32_t cb = 0u;
+    if (FMT == kFmtCQ2 && wact)
+        cb = reinterpret_cast<const uint32_t *>(packed + geom.off_codebook)[col];
 
     const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)(wact ? p : 0) * kc * 1024,
                                 wact ? (uint64_t)kc * 1024 : 0);
@@ -164,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
     const rsrc_t rx = make_rsrc(xq, (uint64_t)m * k);
     const rsrc_t rs = make_rsrc(xs, (uint64_t)ng * m * 4);
 
-    auto load_stage = [&](int s, W8Stage<G> &r) {
+    auto load_stage = [&](int s, W8Stage<FMT, G> &r) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int rr = i * 32 + (tid >> 3), u = tid & 7;
@@ -172,10 +241,18 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
             const bool ok = (m0 + rr < m) && (kk < k);
             r.a[i] = ld128(rx, ok ? (m0 + rr) * k + kk : kOOB);
         }
+        if (FMT == kFmtCQ2) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = s * (kW8SK / kW8Chunk) + 2 * j + half;
-            r.b[j] = ld128(rc, c < kc ? (c * 64 + prow) * 16 : kOOB);
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const int c = 2 * s + c2;
+                r.w2[c2] = ld64(rc, c < kc ? (c * 64 + prow) * 16 + 8 * half : kOOB);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = s * (kW8SK / kW8Chunk) + 2 * j + half;
+                r.b[j] = ld128(rc, c < kc ? (c * 64 + prow) * 16 : kOOB);
+            }
         }
 #pragma unroll
         for (int q = 0; q < GPS; ++q) {
@@ -186,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
             r.xs[q] = __builtin_bit_cast(float, ld32(rs, ok ? (g * m + row) * 4 : kOOB));
         }
     };
-    auto store_a = [&](int buf, const W8Stage<G> &r) {
+    auto store_a = [&](int buf, const W8Stage<FMT, G> &r) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int rr = i * 32 + (tid >> 3), u = tid & 7;
@@ -205,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
     const v16i izero = {};
     v16i part[2] = {};
 
-    W8Stage<G> ring[2];
+    W8Stage<FMT, G> ring[2];
     load_stage(0, ring[0]);
     if (nstage > 1) load_stage(1, ring[1]);
     store_a(0, ring[0]);
@@ -216,8 +293,18 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
         v4i b[4];
         uint32_t meta[GPS];
         float xsv[GPS];
+        if (FMT == kFmtCQ2) {
+            // block j: word (j % 2) of the lane's 8 bytes of chunk j / 2, decoded to 16 bytes
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = ring[slot].b[j];
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t w = static_cast<uint32_t>(ring[slot].w2[j >> 1][j & 1]);
+                b[j] = v4i{cq2_dword(w, 0, cb), cq2_dword(w, 1, cb), cq2_dword(w, 2, cb),
+                           cq2_dword(w, 3, cb)};
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = ring[slot].b[j];
+        }
 #pragma unroll
         for (int q = 0; q < GPS; ++q) {
             meta[q] = ring[slot].meta[q];
@@ -280,21 +367,40 @@ hipError_t launch_pack_codes_w8(const Geom &g, const int8_t *w8, uint8_t *packed
     return hipGetLastError();
 }
 
-hipError_t launch_w8(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
-                     const float *xs, float *y, hipStream_t stream) {
-    if (m == 0) return hipSuccess;
+namespace {
+template <int FMT>
+hipError_t launch_w8_fmt(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
+                         const float *xs, float *y, hipStream_t stream) {
     if (m == 1) {
         const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
         const int *x4 = reinterpret_cast<const int *>(xq);
         if (g.group == 64)
-            gemv_w8_kernel<64><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+            gemv_w8_kernel<FMT, 64><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
         else
-            gemv_w8_kernel<128><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+            gemv_w8_kernel<FMT, 128><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
         return hipGetLastError();
     }
     const unsigned grid = static_cast<unsigned>(((m + 63) / 64) * ((g.n_pad + kW8BN - 1) / kW8BN));
-    if (g.group == 64) gemm_w8_kernel<64><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y);
-    else gemm_w8_kernel<128><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y);
+    if (g.group == 64) gemm_w8_kernel<FMT, 64><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y);
+    else gemm_w8_kernel<FMT, 128><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_w8(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
+                     const float *xs, float *y, hipStream_t stream) {
+    if (m == 0) return hipSuccess;
+    if (g.fmt == kFmtCQ2) return launch_w8_fmt<kFmtCQ2>(g, packed, m, xq, xs, y, stream);
+    return launch_w8_fmt<kFmtInt8>(g, packed, m, xq, xs, y, stream);
+}
+
+hipError_t launch_pack_cq2(const Geom &g, const uint8_t *codes, const int8_t *codebook,
+                           uint8_t *packed, hipStream_t stream) {
+    const int64_t chunks = (int64_t)g.n_pad * (g.k / 64);
+    const int64_t blocks = (chunks + 255) / 256;
+    pack_codes_cq2_kernel<<<static_cast<unsigned>(blocks < 65536 ? blocks : 65536), 256, 0, stream>>>(
+        codes, codebook, g.n, g.k, chunks, reinterpret_cast<uint4 *>(packed + g.off_codes),
+        reinterpret_cast<uint32_t *>(packed + g.off_codebook));
     return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a8.so")
 
-SYM, AFFINE, CODEBOOK, INT8 = 0, 1, 2, 3
+SYM, AFFINE, CODEBOOK, INT8, CQ2 = 0, 1, 2, 3, 4
 PANEL_ROWS = 64
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "no gfx950 device", 4: "HIP error"}
 
@@ -133,18 +133,19 @@ def pack(codes: torch.Tensor, scales: torch.Tensor, fmt: int, group: int, bias=N
          codebook=None, out: torch.Tensor | None = None):
     """Repack canonical device weights.  Returns (layout, packed uint8 tensor of layout.bytes).
 
-    codes uint8 [n, k/2] (low nibble = even k), or int8 [n, k] for INT8; scales float16
-    [n, k/group]; bias float16 [n, k/group] (affine); codebook int8 [n, 16] (codebook).
+    codes uint8 [n, k/2] (low nibble = even k), int8 [n, k] for INT8, uint8 [n, k/4] for CQ2;
+    scales float16 [n, k/group]; bias float16 [n, k/group] (affine); codebook int8 [n, 16]
+    (codebook) or [n, 4] (CQ2).
     """
     n, kh = codes.shape
-    k = kh if fmt == INT8 else 2 * kh
+    k = kh * {INT8: 1, CQ2: 4}.get(fmt, 2)
     L = packed_layout(fmt, n, k, group)
     _dev(codes, torch.int8 if fmt == INT8 else torch.uint8, "codes")
     _dev(scales, torch.float16, "scales", (n, k // group))
     if bias is not None:
         _dev(bias, torch.float16, "bias", (n, k // group))
     if codebook is not None:
-        _dev(codebook, torch.int8, "codebook", (n, 16))
+        _dev(codebook, torch.int8, "codebook", (n, 4 if fmt == CQ2 else 16))
     if out is None:
         out = torch.empty(L.bytes, dtype=torch.uint8, device=codes.device)
     _dev(out, torch.uint8, "packed", (L.bytes,))
@@ -165,7 +166,7 @@ def pack_row_scale(codes: torch.Tensor, row_scales: torch.Tensor, fmt: int, grou
     if row_bias is not None:
         _dev(row_bias, torch.float16, "row_bias", (n,))
     if codebook is not None:
-        _dev(codebook, torch.int8, "codebook", (n, 16))
+        _dev(codebook, torch.int8, "codebook", (n, 4 if fmt == CQ2 else 16))
     if out is None:
         out = torch.empty(L.bytes, dtype=torch.uint8, device=codes.device)
     _dev(out, torch.uint8, "packed", (L.bytes,))

@@ -67,11 +67,16 @@ typedef enum {
     W4A8_AFFINE_U4 = 1,    /* unsigned 4-bit u in [0, 15], fp16 scale and fp16 bias per group */
     W4A8_CODEBOOK_I4 = 2,  /* 4-bit index into a per-output-row 16-entry int8 codebook,
                               fp16 scale per group (PR #697's CQ4 codebook format)           */
-    W4A8_INT8 = 3          /* signed int8 weight, fp16 scale per group (W8A8: "geistlib issue
+    W4A8_INT8 = 3,         /* signed int8 weight, fp16 scale per group (W8A8: "geistlib issue
                               #500", sections "Scope" and "Design sketch"); codes are int8
-                              [n][k], one byte per weight.  w4a8_gemv / w4a8_gemm / w4a8_linear
-                              take it (no fused one-row kernel); the gated, greedy-tail, partials
-                              and fp16-activation entry points return W4A8_ERR_UNSUPPORTED   */
+                              [n][k], one byte per weight                                    */
+    W4A8_CQ2 = 4           /* 2-bit index into a per-output-row 4-entry int8 codebook, fp16
+                              scale per group (CQ2 of PR #697's CQ1-CQ4 family; W2A8); codes
+                              are uint8 [n][k/4], the index of k = 4b + i in bits 2i, 2i+1 of
+                              byte b; codebook int8 [n][4]                                   */
+    /* W4A8_INT8 and W4A8_CQ2 run through w4a8_gemv / w4a8_gemm / w4a8_linear (no fused one-row
+       kernel); the gated, greedy-tail, partials and fp16-activation entry points return
+       W4A8_ERR_UNSUPPORTED for them. */
 } w4a8_format;
 
 /* Rows of the packed weight buffer come in panels of this many output channels. */

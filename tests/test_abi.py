@@ -75,7 +75,7 @@ def test_layout_sizes():
 
 
 @pytest.mark.parametrize("args", [
-    (4, 64, 64, 64), (-1, 64, 64, 64), (0, 64, 96, 64), (0, 64, 64, 32), (0, 0, 64, 64),
+    (5, 64, 64, 64), (-1, 64, 64, 64), (0, 64, 96, 64), (0, 64, 64, 32), (0, 0, 64, 64),
     (0, 64, 0, 64), (0, 64, 64 * 3, 128), (0, 1 << 25, 64, 64), (0, 64, (1 << 20) + 64, 64),
 ])
 def test_layout_rejects(lib, args):
@@ -213,6 +213,10 @@ def test_invalid_calls_are_rejected_on_the_host(lib):
     L8 = w4a8.packed_layout(w4a8.INT8, 100, 256, 64)
     L4 = w4a8.packed_layout(w4a8.SYM, 100, 256, 64)
     assert L8.off_meta == 128 * 256 and L4.off_meta == 128 * 128 and L8.meta_bytes == 2
+    L2 = w4a8.packed_layout(w4a8.CQ2, 100, 256, 64)
+    assert L2.off_meta == 128 * 64 and L2.off_codebook > L2.off_meta and L2.bytes % 256 == 0
+    assert lib.w4a8_pack_weights(ctypes.byref(L2), p, p, None, None, p, None) == ERR_ARG   # codebook
+    assert lib.w4a8_debug_partials(ctypes.byref(L2), p, 2, p, p, p, None) == ERR_UNSUPPORTED
     L8P = ctypes.byref(L8)
     assert lib.w4a8_gemm_glu(ctypes.byref(w4a8.packed_layout(w4a8.INT8, 128, 256, 64)), p, 2, p,
                              p, p, silu, p, None) == ERR_UNSUPPORTED

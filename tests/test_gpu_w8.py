@@ -1,6 +1,6 @@
-"""GPU parity of int8 weights (format 3, W8A8) through w4a8_linear / w4a8_gemv / w4a8_gemm
-against the oracle: the prepass outputs bit-exact, y within the linear's bar (relative L2 error
-<= 1e-5, |err| <= 1e-4 T per element)."""
+"""GPU parity of int8 weights (format 3, W8A8) and 2-bit codebook weights (format 4, CQ2) through
+w4a8_linear / w4a8_gemv / w4a8_gemm against the oracle: the prepass outputs bit-exact, y within
+the linear's bar (relative L2 error <= 1e-5, |err| <= 1e-4 T per element)."""
 from __future__ import annotations
 
 import numpy as np
@@ -23,7 +23,8 @@ def _w4a8():
 def _run(L):
     w = _w4a8()
     cfg = L["cfg"]
-    lay, packed = w.pack(to_dev(L["codes"]), to_dev(L["scales"]), cfg.fmt, cfg.group)
+    lay, packed = w.pack(to_dev(L["codes"]), to_dev(L["scales"]), cfg.fmt, cfg.group,
+                         codebook=to_dev(L["codebook"]))
     ng = cfg.k // cfg.group
     po = (torch.empty((cfg.m, cfg.k), dtype=torch.int8, device="cuda:0"),
           torch.empty((ng, cfg.m), dtype=torch.float32, device="cuda:0"),
@@ -49,13 +50,18 @@ CASES = [
 ]
 
 
+FORMATS = [synth.FMT_INT8, synth.FMT_CQ2]
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=["int8", "cq2"])
 @pytest.mark.parametrize("name,over", CASES,
                          ids=[f"{c}-{'-'.join(f'{k}{v}' for k, v in o.items())}"
                               for c, o in CASES])
-def test_w8_parity(name, over):
-    L = synth.make(name, full_range=True, fmt=synth.FMT_INT8, **over)
+def test_w8_parity(name, over, fmt):
+    L = synth.make(name, full_range=True, fmt=fmt, **over)
     cfg = L["cfg"]
-    print(f"w8 {name} {over} m={cfg.m} n={cfg.n} k={cfg.k} g={cfg.group} had={cfg.hadamard}",
+    print(f"fmt {fmt} {name} {over} m={cfg.m} n={cfg.n} k={cfg.k} g={cfg.group} "
+          f"had={cfg.hadamard}",
           flush=True)
     got = _run(L)
     ref = oracle_layer(L)
@@ -64,11 +70,12 @@ def test_w8_parity(name, over):
     check_y(got["y"], ref["y"], ref["t"], f"w8 {name} {over}")
 
 
-def test_w8_gemv_gemm_entry_points_same_bits():
+@pytest.mark.parametrize("fmt", FORMATS, ids=["int8", "cq2"])
+def test_w8_gemv_gemm_entry_points_same_bits(fmt):
     # w4a8_gemv / w4a8_gemm on w4a8_linear's own prepass outputs run the same kernels
     w = _w4a8()
     for name, over in (("C2a", dict(n=1000, k=2048)), ("C3a", dict(m=65, n=1000, k=640))):
-        L = synth.make(name, full_range=True, fmt=synth.FMT_INT8, **over)
+        L = synth.make(name, full_range=True, fmt=fmt, **over)
         got = _run(L)
         xq, xs, xsum = got["dev"]
         if L["cfg"].m == 1:
@@ -79,12 +86,14 @@ def test_w8_gemv_gemm_entry_points_same_bits():
         assert np.array_equal(got["y"].view(np.uint32), y2.view(np.uint32))
 
 
-def test_w8_full_size_prompt_tile(layer_cache):
-    """C3a's 128 x 5120 x 34816 shape with int8 weights (Gaussian draws quantized per group),
-    on a seeded sample of output channels."""
-    if "C3a-w8" not in layer_cache:
-        layer_cache["C3a-w8"] = synth.make("C3a", fmt=synth.FMT_INT8)
-    L = layer_cache["C3a-w8"]
+@pytest.mark.parametrize("fmt", FORMATS, ids=["int8", "cq2"])
+def test_w8_full_size_prompt_tile(layer_cache, fmt):
+    """C3a's 128 x 5120 x 34816 shape with int8 weights (Gaussian draws quantized per group) or
+    2-bit codebook weights, on a seeded sample of output channels."""
+    key = f"C3a-fmt{fmt}"
+    if key not in layer_cache:
+        layer_cache[key] = synth.make("C3a", fmt=fmt)
+    L = layer_cache[key]
     cfg = L["cfg"]
     print(f"w8 full C3a: m={cfg.m} n={cfg.n} k={cfg.k}", flush=True)
     got = _run(L)
