@@ -18,7 +18,8 @@ Canonical formats (consumed by both the HIP library and the oracle):
   codebook   int8    [n, 16]                 codebook only
   (int8 weights: codes int8 [n, k], one signed byte per weight, with the same fp16 scales)
   (2-bit codebook: codes uint8 [n, k/4], four indices per byte, low bits = first k; codebook
-  int8 [n, 4])
+  int8 [n, 4]; 1-bit: codes uint8 [n, k/8], bit i of byte b = index of k = 8b + i, codebook
+  [n, 2]; 3-bit: codes uint8 [n, k], one index 0..7 per byte, codebook [n, 8])
 
 Shapes and distributions follow the workloads the pages measure: Gemma-style decode GEMVs
 (K=2048, gate_up N=16384, o_proj N=2048), a 128-row prefill chunk of a 5120-wide model's fused
@@ -32,9 +33,10 @@ from __future__ import annotations
 from dataclasses import dataclass, field, replace
 import numpy as np
 
-FMT_SYM, FMT_AFFINE, FMT_CODEBOOK, FMT_INT8, FMT_CQ2 = 0, 1, 2, 3, 4
+FMT_SYM, FMT_AFFINE, FMT_CODEBOOK, FMT_INT8, FMT_CQ2, FMT_CQ1, FMT_CQ3 = 0, 1, 2, 3, 4, 5, 6
 FORMAT_NAMES = {FMT_SYM: "sym", FMT_AFFINE: "affine", FMT_CODEBOOK: "codebook", FMT_INT8: "int8",
-                FMT_CQ2: "cq2"}
+                FMT_CQ2: "cq2", FMT_CQ1: "cq1", FMT_CQ3: "cq3"}
+CQ_BITS = {FMT_CQ1: 1, FMT_CQ2: 2, FMT_CQ3: 3}
 
 _W_CHUNK_ROWS = 8192  # W is drawn in fixed row chunks so large heads stay within memory
 
@@ -152,13 +154,16 @@ def make_weights(cfg: LayerConfig, full_range: bool = False):
     """Canonical (codes [n,k/2] u8, scales [n,k/g] f16, bias f16|None, codebook i8|None)."""
     n, k, g = cfg.n, cfg.k, cfg.group
     ng = k // g
-    if cfg.fmt == FMT_CQ2:
-        cb = np.clip(np.rint(40.0 * rng(cfg.cfg_id, cfg.w_variant, 3).standard_normal((n, 4))),
+    if cfg.fmt in CQ_BITS:
+        ne = 1 << CQ_BITS[cfg.fmt]
+        cb = np.clip(np.rint(40.0 * rng(cfg.cfg_id, cfg.w_variant, 3).standard_normal((n, ne))),
                      -127, 127).astype(np.int8)
-        idx = rng(cfg.cfg_id, cfg.w_variant, 4).integers(0, 4, size=(n, k), dtype=np.uint8)
+        idx = rng(cfg.cfg_id, cfg.w_variant, 4).integers(0, ne, size=(n, k), dtype=np.uint8)
         sc = (rng(cfg.cfg_id, cfg.w_variant, 5).uniform(0.5, 1.5, size=(n, ng))
               * 5e-4).astype(np.float16)
-        return pack_crumbs(idx), sc, None, cb
+        codes = (pack_crumbs(idx) if cfg.fmt == FMT_CQ2 else
+                 np.packbits(idx, axis=1, bitorder="little") if cfg.fmt == FMT_CQ1 else idx)
+        return codes, sc, None, cb
     if cfg.fmt == FMT_CODEBOOK:
         cb = np.clip(np.rint(40.0 * rng(cfg.cfg_id, cfg.w_variant, 3).standard_normal((n, 16))),
                      -127, 127).astype(np.int8)
@@ -225,13 +230,14 @@ def weight_bytes(cfg: LayerConfig) -> int:
     """Algorithmic weight bytes: nibbles + fp16 scales (+ fp16 bias) (+ int8 codebook); one
     scale (and bias) per row for a row-scaled head."""
     per_row = 1 if cfg.extra.get("row_scale") else cfg.k // cfg.group
-    b = cfg.n * cfg.k // {FMT_INT8: 1, FMT_CQ2: 4}.get(cfg.fmt, 2) + 2 * cfg.n * per_row
+    b = (cfg.n * cfg.k * CQ_BITS[cfg.fmt] // 8 if cfg.fmt in CQ_BITS else
+         cfg.n * cfg.k // (1 if cfg.fmt == FMT_INT8 else 2)) + 2 * cfg.n * per_row
     if cfg.fmt == FMT_AFFINE:
         b += 2 * cfg.n * per_row
     if cfg.fmt == FMT_CODEBOOK:
         b += 16 * cfg.n
-    if cfg.fmt == FMT_CQ2:
-        b += 4 * cfg.n
+    if cfg.fmt in CQ_BITS:
+        b += (1 << CQ_BITS[cfg.fmt]) * cfg.n
     return b
 
 

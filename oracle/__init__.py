@@ -20,7 +20,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-FORMAT_SYM, FORMAT_AFFINE, FORMAT_CODEBOOK, FORMAT_INT8, FORMAT_CQ2 = 0, 1, 2, 3, 4
+FORMAT_SYM, FORMAT_AFFINE, FORMAT_CODEBOOK, FORMAT_INT8, FORMAT_CQ2, FORMAT_CQ1, FORMAT_CQ3 = \
+    0, 1, 2, 3, 4, 5, 6
 
 _lib = None
 
@@ -142,7 +143,7 @@ def partials(fmt: int, codes: np.ndarray, xq: np.ndarray, group: int, codebook=N
         xq = xq[None, :]
     n = codes.shape[0]
     m, k = xq.shape
-    assert codes.shape[1] * {FORMAT_INT8: 1, FORMAT_CQ2: 4}.get(fmt, 2) == k
+    assert codes.shape[1] * {FORMAT_INT8: 1, FORMAT_CQ2: 4, FORMAT_CQ1: 8, FORMAT_CQ3: 1}.get(fmt, 2) == k
     cb = None if codebook is None else np.ascontiguousarray(codebook, dtype=np.int8)
     d = np.empty((m, n, k // group), np.int32)
     _check(_load().oracle_partials(fmt, _ptr(codes), _ptr(cb), n, k, group, _ptr(xq), m,

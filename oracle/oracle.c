@@ -90,6 +90,10 @@
  *                          int8 codebook per row ("cactus PR #697": the CQ1-CQ4 codebook family,
  *                          of which this is CQ2; "geistlib issue #500", "Acceptance criteria":
  *                          W2A8 models), one fp16 scale per group
+ *   format 5 (1-bit codebook, CQ1): codes uint8 [n][k/8], bit i of byte b is the index of
+ *                          k = 8b + i; w_int = codebook[n][index], 2 entries per row
+ *   format 6 (3-bit codebook, CQ3): codes uint8 [n][k], one index 0..7 per byte (low 3 bits);
+ *                          w_int = codebook[n][index], 8 entries per row
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared (no fast-math), so that every fp32
  * operation is a single IEEE-rounded operation in program order.
@@ -249,6 +253,12 @@ static int32_t oracle_weight_int(int format, const uint8_t *codes, const int8_t 
         int idx = (codes[n * (k_total / 4) + k / 4] >> (2 * (k % 4))) & 3;
         return (int32_t)codebook[n * 4 + idx];
     }
+    if (format == 5) {                                             /* eight indices per byte */
+        int idx = (codes[n * (k_total / 8) + k / 8] >> (k % 8)) & 1;
+        return (int32_t)codebook[n * 2 + idx];
+    }
+    if (format == 6)                                               /* one index per byte */
+        return (int32_t)codebook[n * 8 + (codes[n * k_total + k] & 7)];
     int c = oracle_code(codes, k_total, n, k);
     if (format == 0)
         return c >= 8 ? c - 16 : c;                 /* two's-complement nibble */
@@ -267,9 +277,9 @@ int oracle_partials(int32_t format, const uint8_t *codes, const int8_t *codebook
                     int64_t n, int64_t k, int32_t group, const int8_t *xq, int64_t m,
                     int32_t *d)
 {
-    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 4)
+    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 6)
         return ORACLE_BAD_ARGS;
-    if ((format == 2 || format == 4) && codebook == NULL)
+    if ((format == 2 || format >= 4) && codebook == NULL)
         return ORACLE_BAD_ARGS;
     int64_t ng = k / group;
     int overflow = 0;
@@ -305,9 +315,9 @@ int oracle_linear(int32_t format, const uint8_t *codes, const uint16_t *scales_f
                   const int8_t *xq, const float *xs, const int32_t *xsum, int64_t m,
                   double *y, double *t)
 {
-    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 4)
+    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 6)
         return ORACLE_BAD_ARGS;
-    if ((format == 1 && bias_f16 == NULL) || ((format == 2 || format == 4) && codebook == NULL))
+    if ((format == 1 && bias_f16 == NULL) || ((format == 2 || format >= 4) && codebook == NULL))
         return ORACLE_BAD_ARGS;
     int64_t ng = k / group;
     int overflow = 0;
@@ -491,7 +501,7 @@ int oracle_linear_a16(int32_t format, const uint8_t *codes, const uint16_t *scal
                       int32_t group, const uint16_t *xh, const float *xsf, int64_t m,
                       double *y, double *t)
 {
-    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 4)
+    if (group <= 0 || k % group != 0 || k % 2 != 0 || format < 0 || format > 6)
         return ORACLE_BAD_ARGS;
     if ((format == 1 && bias_f16 == NULL) || (format == 2 && codebook == NULL))
         return ORACLE_BAD_ARGS;

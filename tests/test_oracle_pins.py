@@ -860,3 +860,33 @@ def test_cq2_brute_force_and_equal_forms():
     # control: the two index pairs of each nibble swapped change the partials
     wrong = ((codes >> 2) & 0x33) | ((codes << 2) & 0xCC)
     assert not np.array_equal(oracle.partials(oracle.FORMAT_CQ2, wrong, xq, g, codebook=cb), d)
+
+
+
+@pytest.mark.parametrize("fmt,bits", [(5, 1), (6, 3)], ids=["cq1", "cq3"])
+def test_cq1_cq3_brute_force_and_the_4_bit_codebook(fmt, bits):
+    # 1- and 3-bit codebooks: numpy brute force of the partials, and the 4-bit codebook format
+    # with the same entries first gives the same output
+    from bit_group_quantized_act_amd import synth
+    rng = np.random.default_rng(44 + bits)
+    n, k, g, m = 9, 256, 64, 3
+    ne = 1 << bits
+    idx = rng.integers(0, ne, size=(n, k), dtype=np.uint8)
+    cb = rng.integers(-127, 128, size=(n, ne), dtype=np.int8)
+    codes = np.packbits(idx, axis=1, bitorder="little") if bits == 1 else idx.copy()
+    sc = (rng.uniform(0.5, 1.5, size=(n, k // g)) * 1e-3).astype(np.float16)
+    xq, xs, xsum = oracle.prep((rng.standard_normal((m, k)) * 3).astype(np.float32), g, 0)
+    w = np.take_along_axis(cb.astype(np.int64), idx.astype(np.int64), axis=1)
+    d = oracle.partials(fmt, codes, xq, g, codebook=cb)
+    want = np.einsum("mgk,ngk->mng", xq.astype(np.int64).reshape(m, k // g, g),
+                     w.reshape(n, k // g, g))
+    assert np.array_equal(d, want)
+    cb16 = np.zeros((n, 16), np.int8)
+    cb16[:, :ne] = cb
+    y = oracle.linear(fmt, codes, sc, xq, xs, xsum, g, codebook=cb, with_terms=False)
+    y4 = oracle.linear(oracle.FORMAT_CODEBOOK, synth.pack_nibbles(idx), sc, xq, xs, xsum, g,
+                       codebook=cb16, with_terms=False)
+    assert np.array_equal(y, y4)
+    if bits == 1:      # control: bit order read from the top of each byte fails
+        wrong = np.packbits(idx, axis=1, bitorder="big")
+        assert not np.array_equal(oracle.partials(fmt, wrong, xq, g, codebook=cb), d)
