@@ -57,6 +57,8 @@ if ROOT not in sys.path:
 
 METRIC = "W4A8 linear: weight GB/s at M=1 and int8 TOPS at M≥128 (% of roofline)"
 HBM_PEAK_GBPS = 8000.0
+# weight formats 3-6 (int8, and the 2-, 1- and 3-bit codebooks) have their own GEMV / GEMM
+BYTE_DECODED = (3, 4, 5, 6)
 INT8_PEAK_TOPS = 5000.0
 F16_PEAK_TFLOPS = 2500.0
 POOL_BYTES = 512 << 20
@@ -111,6 +113,10 @@ def parse():
                     help="the config's shape with int8 weights (format 3, W8A8) instead")
     ap.add_argument("--cq2", action="store_true",
                     help="the config's shape with 2-bit codebook weights (format 4, CQ2) instead")
+    ap.add_argument("--cq1", action="store_true",
+                    help="the config's shape with 1-bit codebook weights (format 5, CQ1) instead")
+    ap.add_argument("--cq3", action="store_true",
+                    help="the config's shape with 3-bit codebook weights (format 6, CQ3) instead")
     ap.add_argument("--a16", action="store_true",
                     help="time the fp16-activation path (w4a8_linear_a16) instead")
     ap.add_argument("--attn", choices=["A1", "A2"], default=None,
@@ -243,7 +249,7 @@ def workload_name(cfg, glu=None, cap=None, a16=False):
     if cfg.extra.get("row_scale"):
         rot += f", one scale per row seen as K/{cfg.group} groups"
     fused = (cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072 and
-             cfg.fmt not in (synth.FMT_INT8, synth.FMT_CQ2))
+             cfg.fmt not in BYTE_DECODED)
     if a16:
         return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
                 f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights x fp16 activations (prepass writing "
@@ -254,8 +260,11 @@ def workload_name(cfg, glu=None, cap=None, a16=False):
     tail = "" if cap is None else (f", greedy tail: logits soft-capped at {cap:g} and their "
                                    f"first maximum" if cap > 0 else
                                    ", greedy tail: the first maximum of the logits")
+    wdesc = {synth.FMT_INT8: "int8", synth.FMT_CQ2: "2-bit codebook (CQ2)",
+             synth.FMT_CQ1: "1-bit codebook (CQ1)", synth.FMT_CQ3: "3-bit codebook (CQ3)"}.get(
+        cfg.fmt, f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit")
     return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
-            f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights{rot}{gated}{tail} ({how} per step)")
+            f"{wdesc} weights{rot}{gated}{tail} ({how} per step)")
 
 
 def main():
@@ -282,9 +291,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    over = {"fmt": synth.FMT_INT8} if args.w8 else {"fmt": synth.FMT_CQ2} if args.cq2 else {}
+    chosen = [f for f, on in ((synth.FMT_INT8, args.w8), (synth.FMT_CQ2, args.cq2),
+                              (synth.FMT_CQ1, args.cq1), (synth.FMT_CQ3, args.cq3)) if on]
+    if len(chosen) > 1:
+        print("give at most one of --w8 / --cq2 / --cq1 / --cq3", file=sys.stderr)
+        sys.exit(2)
+    over = {"fmt": chosen[0]} if chosen else {}
     layer = synth.make(args.config, **over)
-    byte_decoded = layer["cfg"].fmt in (synth.FMT_INT8, synth.FMT_CQ2)
+    byte_decoded = layer["cfg"].fmt in BYTE_DECODED
     cfg = layer["cfg"]
     t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     if "row_scales" in layer:      # one scale per row, packed through the row-scale view
@@ -300,7 +314,7 @@ def main():
     cap = args.argmax
     a16 = args.a16
     if (a16 or cap is not None or args.glu is not None) and byte_decoded:
-        print("--w8 / --cq2 time the plain linear only", file=sys.stderr)
+        print("--w8 / --cq1 / --cq2 / --cq3 time the plain linear only", file=sys.stderr)
         sys.exit(2)
     if a16 and (cap is not None or args.glu is not None or cfg.group != 64 or
                 cfg.fmt == synth.FMT_CODEBOOK):

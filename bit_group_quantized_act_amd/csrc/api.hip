@@ -103,7 +103,12 @@ w4a8_status launched(hipError_t e, const char *what) {
 // (m * k/group dwords) and the workgroup count.
 // Int8 and 2-bit codebook weights run through their own GEMV / GEMM.
 bool byte_decoded(const w4a8_layout *L) {
-    return L->format == W4A8_INT8 || L->format == W4A8_CQ2;
+    return L->format >= W4A8_INT8 && L->format <= W4A8_CQ3;
+}
+
+bool has_codebook(int32_t format) {
+    return format == W4A8_CODEBOOK_I4 || format == W4A8_CQ2 || format == W4A8_CQ1 ||
+           format == W4A8_CQ3;
 }
 
 // Entry points whose kernels read only the 4-bit formats.
@@ -185,7 +190,7 @@ extern "C" {
 w4a8_status w4a8_packed_layout(int32_t format, int32_t n, int32_t k, int32_t group,
                                w4a8_layout *L) {
     if (!L) return fail(W4A8_ERR_ARG, "layout is NULL");
-    if (format < W4A8_SYM_I4 || format > W4A8_CQ2)
+    if (format < W4A8_SYM_I4 || format > W4A8_CQ3)
         return fail(W4A8_ERR_ARG, "format %d is not a w4a8_format", format);
     if (group != 64 && group != 128) return fail(W4A8_ERR_ARG, "group %d is not 64 or 128", group);
     if (n < 1 || n > (1 << 24)) return fail(W4A8_ERR_ARG, "n = %d is outside [1, 2^24]", n);
@@ -199,16 +204,23 @@ w4a8_status w4a8_packed_layout(int32_t format, int32_t n, int32_t k, int32_t gro
     L->group = group;
     L->n_pad = static_cast<int32_t>(round_up(n, W4A8_PANEL_ROWS));
     L->meta_bytes = (format == W4A8_AFFINE_U4) ? 4 : 2;
-    const uint64_t codes = static_cast<uint64_t>(L->n_pad) * k /
-                           (format == W4A8_INT8 ? 1 : format == W4A8_CQ2 ? 4 : 2);
+    // bytes per 128 k of a row: 128 (int8), 64 (4-bit), 32 (CQ2), 16 (CQ1), 48 (CQ3; CQ1 and
+    // CQ3 pad k up to a multiple of 128)
+    const uint64_t chunks128 = static_cast<uint64_t>(k + 127) / 128;
+    const uint64_t codes =
+        format == W4A8_CQ1 ? L->n_pad * chunks128 * 16
+        : format == W4A8_CQ3 ? L->n_pad * chunks128 * 48
+        : static_cast<uint64_t>(L->n_pad) * k /
+              (format == W4A8_INT8 ? 1 : format == W4A8_CQ2 ? 4 : 2);
     // metadata in blocks of 4 groups (the last block zero-padded)
     const uint64_t meta = static_cast<uint64_t>(L->n_pad) * ((k / group + 3) / 4) * 4 * L->meta_bytes;
     L->off_codes = 0;
     L->off_meta = round_up(codes, 256);
     uint64_t end = L->off_meta + round_up(meta, 256);
-    if (format == W4A8_CODEBOOK_I4 || format == W4A8_CQ2) {
+    if (has_codebook(format)) {
         L->off_codebook = end;
-        end += round_up(static_cast<uint64_t>(L->n_pad) * (format == W4A8_CQ2 ? 4 : 16), 256);
+        const int per_row = format == W4A8_CODEBOOK_I4 ? 16 : format == W4A8_CQ3 ? 8 : 4;
+        end += round_up(static_cast<uint64_t>(L->n_pad) * per_row, 256);
     }
     L->bytes = end;
     return ok();
@@ -229,7 +241,7 @@ w4a8_status pack_checked(const w4a8_layout *L, const uint8_t *codes, const uint1
     } else if (bias_f16) {
         return fail(W4A8_ERR_ARG, "bias_f16 is only used by the affine format; pass NULL");
     }
-    if (L->format == W4A8_CODEBOOK_I4 || L->format == W4A8_CQ2) {
+    if (has_codebook(L->format)) {
         W4A8_REQUIRE_PTR(codebook);
     } else if (codebook) {
         return fail(W4A8_ERR_ARG, "codebook is only used by the codebook format; pass NULL");

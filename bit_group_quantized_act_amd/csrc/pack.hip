@@ -100,6 +100,8 @@ hipError_t launch_pack(const Geom &g, const uint8_t *codes, const uint16_t *scal
         e = launch_pack_codes_w8(g, reinterpret_cast<const int8_t *>(codes), packed, stream);
     } else if (g.fmt == kFmtCQ2) {
         e = launch_pack_cq2(g, codes, codebook, packed, stream);     // codes and codebooks
+    } else if (g.fmt == kFmtCQ1 || g.fmt == kFmtCQ3) {
+        e = launch_pack_bits(g, codes, codebook, packed, stream);    // codes and codebooks
     } else {
         const int64_t chunks = (int64_t)g.n_pad * (g.k / kChunkK);
         pack_codes_kernel<<<grid_for(chunks), 256, 0, stream>>>(

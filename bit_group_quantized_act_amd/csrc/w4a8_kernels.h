@@ -10,7 +10,8 @@ namespace w4a8 {
 
 constexpr int kPanelRows = 64;   // output channels per packed panel
 constexpr int kChunkK = 32;      // k values per 16-byte chunk of one row
-constexpr int kFmtSym = 0, kFmtAffine = 1, kFmtCodebook = 2, kFmtInt8 = 3, kFmtCQ2 = 4;
+constexpr int kFmtSym = 0, kFmtAffine = 1, kFmtCodebook = 2, kFmtInt8 = 3, kFmtCQ2 = 4,
+              kFmtCQ1 = 5, kFmtCQ3 = 6;
 
 // What the kernels need from a w4a8_layout (plain values, passed by value to kernels).
 struct Geom {
@@ -232,12 +233,14 @@ hipError_t launch_attn(const AttnGeom &ag, const uint8_t *packed, const float *q
                        int pos0, int window, int sink, float scale, int8_t *q8, float *sq,
                        float *o, float *m, float *l, float *work, hipStream_t stream);
 
-// Int8 weights (format 3) and 2-bit codebook weights (format 4): the codes (and the CQ2
-// codebooks) of the packed layout, and the GEMV (m == 1) / GEMM of both.
+// Int8 weights (format 3) and 2-, 1- and 3-bit codebook weights (formats 4, 5, 6): the codes
+// (and the codebooks) of the packed layout, and the GEMV (m == 1) / GEMM of each.
 hipError_t launch_pack_codes_w8(const Geom &g, const int8_t *w8, uint8_t *packed,
                                 hipStream_t stream);
 hipError_t launch_pack_cq2(const Geom &g, const uint8_t *codes, const int8_t *codebook,
                            uint8_t *packed, hipStream_t stream);
+hipError_t launch_pack_bits(const Geom &g, const uint8_t *codes, const int8_t *codebook,
+                            uint8_t *packed, hipStream_t stream);
 hipError_t launch_w8(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
                      const float *xs, float *y, hipStream_t stream);
 

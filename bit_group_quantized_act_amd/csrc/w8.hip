@@ -1,22 +1,32 @@
-// Int8 weights (W8A8) and 2-bit codebook weights (CQ2 / W2A8), against the same int8 activations,
-// scales and group sums as the 4-bit formats; both decode to int8 weights in registers.
+// Int8 weights (W8A8) and 1-, 2- and 3-bit codebook weights (CQ1, CQ2 / W2A8, CQ3), against the
+// same int8 activations, scales and group sums as the 4-bit formats; all decode to int8 weights
+// in registers.
 //
 // Source: "geistlib issue #500: native W*A8 int8 GEMM for prefill", sections "Scope" and
 // "Design sketch": a W8A8 inner kernel beside the W4A8 one, both behind a load-time repack,
 // sharing the activation quantization; w8a8 GEMV and GEMM entry points.
 //   y[r][n] = sum_g xs[r][g] * sw[n][g] * D[r][n][g],  D = sum_{k in g} xq[r][k] * w8[n][k]
 //
-// 2-bit codebook: "cactus PR #697", the CQ1-CQ4 codebook family (this is CQ2: a 2-bit index per
-// weight into a per-row table of 4 int8 entries, one fp16 scale per group); "geistlib issue
-// #500", "Acceptance criteria" (W2A8 models).
+// Codebooks: "cactus PR #697", the CQ1-CQ4 codebook family (a b-bit index per weight into a
+// per-row table of 2^b int8 entries, one fp16 scale per group; CQ4 is the 4-bit codebook
+// format); "geistlib issue #500", "Acceptance criteria" (W2A8 models).
 //
 // Packed layouts: per 64-row panel and per k chunk, 64 rows x 16 bytes.  Int8: chunk c of row r
 // is w8[r][16c .. 16c+15].  CQ2: a chunk holds 64 k as four 32-bit words in the k order
 // 0-15, 32-47, 16-31, 48-63, and in a word covering k = b .. b+15 the index of k = b + 4s + j sits
 // at bits 8j + 2s, so (w >> 2s) & 0x03030303 selects four consecutive weights and one v_perm
 // against the row's codebook dword turns them into int8; the words' order lets a GEMM lane half
-// read its two MFMA blocks of a chunk as one 8-byte run.  Scales: the symmetric format's blocked
-// metadata; CQ2's codebooks: one dword per row.
+// read its two MFMA blocks of a chunk as one 8-byte run.
+// CQ1 and CQ3 (bit-plane formats): a chunk covers 128 k in P planes of 64 rows x 16 bytes
+// (P = 1 for CQ1, 3 for CQ3), plane-major inside the chunk so that every load of a wavefront is
+// one contiguous KiB.  The bit plane: word 2h + q covers k = 64q + 16h + 4s + j at bit
+// 8j + s and k = 64q + 32 + 16h + 4s + j at bit 8j + 4 + s (the halves h of MFMA blocks 2q and
+// 2q + 1), so (w >> (4P + s)) & 0x01010101 is one bit of four consecutive weights and a GEMM
+// lane half again reads 8 bytes.  CQ1 stores the index there; CQ3 stores index >> 2 there and
+// index & 3 in planes 0 and 1 (CQ2's layout for k = 0..63 and 64..127), and one v_perm over the
+// two codebook dwords (entries 0-3 in the second source, 4-7 in the first) decodes the 3-bit
+// selectors.  Scales: the symmetric format's blocked metadata; codebooks: one dword per row
+// (CQ1: entries in bytes 0 and 1, CQ2), two dwords per row (CQ3).
 //
 // MI355X design.
 //   GEMV (one row): a workgroup per panel, 8 wavefronts over the groups, lane r on panel row r
@@ -40,6 +50,12 @@ namespace {
 
 constexpr int kW8Chunk = 16;        // k per 16-byte chunk
 constexpr int kW8Waves = 8;
+constexpr int kBitChunk = 128;      // k per chunk of the bit-plane formats
+
+template <int FMT>
+constexpr bool bit_plane = FMT == kFmtCQ1 || FMT == kFmtCQ3;
+template <int FMT>
+constexpr int planes = FMT == kFmtCQ3 ? 3 : 1;     // 16-byte planes per row per chunk
 
 // ---- packing
 
@@ -94,9 +110,78 @@ __global__ __launch_bounds__(256) void pack_codes_cq2_kernel(const uint8_t *__re
     }
 }
 
+template <int FMT>
+__global__ __launch_bounds__(256) void pack_codes_bits_kernel(const uint8_t *__restrict__ codes,
+                                                              const int8_t *__restrict__ cb,
+                                                              int n, int k, int64_t total,
+                                                              uint4 *__restrict__ out,
+                                                              uint32_t *__restrict__ cb_out) {
+    constexpr int P = planes<FMT>;
+    constexpr int NE = FMT == kFmtCQ3 ? 8 : 2;         // codebook entries
+    const int kc = (k + kBitChunk - 1) / kBitChunk;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int r = static_cast<int>(t % kPanelRows);
+        const int64_t rest = t / kPanelRows;         // panel * kc + chunk
+        const int c = static_cast<int>(rest % kc);
+        const int64_t row = (rest / kc) * kPanelRows + r;
+        // the index of k = 128c + kk (zero past the weight)
+        auto index = [&](int kk) -> uint32_t {
+            const int ka = c * kBitChunk + kk;
+            if (row >= n || ka >= k) return 0u;
+            if (FMT == kFmtCQ1) return (codes[row * (int64_t)(k / 8) + ka / 8] >> (ka % 8)) & 1u;
+            return codes[row * (int64_t)k + ka] & 7u;
+        };
+        uint32_t bits[4] = {0u, 0u, 0u, 0u};
+        for (int h = 0; h < 2; ++h)
+            for (int q = 0; q < 2; ++q)
+                for (int pb = 0; pb < 2; ++pb)                 // block 2q + pb
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t idx = index(64 * q + 32 * pb + 16 * h + 4 * s4 + j);
+                            bits[2 * h + q] |= (FMT == kFmtCQ3 ? idx >> 2 : idx)
+                                               << (8 * j + 4 * pb + s4);
+                        }
+        uint4 *dst = out + rest * P * kPanelRows + r;
+        if (FMT == kFmtCQ3) {
+            const int kq[4] = {0, 32, 16, 48};            // k offset of word position q
+            for (int u = 0; u < 2; ++u) {
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+                for (int q = 0; q < 4; ++q)
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        for (int j = 0; j < 4; ++j)
+                            w[q] |= (index(64 * u + kq[q] + 4 * s4 + j) & 3u) << (8 * j + 2 * s4);
+                dst[u * kPanelRows] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        dst[(P - 1) * kPanelRows] = make_uint4(bits[0], bits[1], bits[2], bits[3]);
+        if (c == 0) {
+            constexpr int CBW = NE == 8 ? 2 : 1;          // codebook dwords per row
+            uint32_t v[2] = {0u, 0u};
+            if (row < n)
+                for (int e = 0; e < NE; ++e)
+                    v[e / 4] |= static_cast<uint32_t>(static_cast<uint8_t>(cb[row * NE + e]))
+                                << (8 * (e % 4));
+            for (int w = 0; w < CBW; ++w) cb_out[row * CBW + w] = v[w];
+        }
+    }
+}
+
 // Four int8 weights of k = b + 4s .. b + 4s + 3 from a CQ2 word (the layout above).
 __device__ __forceinline__ int cq2_dword(uint32_t w, int s, uint32_t cb) {
     return static_cast<int>(__builtin_amdgcn_perm(cb, cb, (w >> (2 * s)) & 0x03030303u));
+}
+
+// The bit-plane formats: four int8 weights whose one-bit selectors sit at bits 8j + sh of the
+// bit word bw (CQ1), or whose low two bits sit at 8j + 2s of the crumb word w and high bit at
+// 8j + sh of bw (CQ3; cb0 holds entries 0-3, cb1 entries 4-7).
+__device__ __forceinline__ int cq1_dword(uint32_t bw, int sh, uint32_t cb) {
+    return static_cast<int>(__builtin_amdgcn_perm(cb, cb, (bw >> sh) & 0x01010101u));
+}
+__device__ __forceinline__ int cq3_dword(uint32_t w, int s, uint32_t bw, int sh, uint32_t cb0,
+                                         uint32_t cb1) {
+    const uint32_t sel = ((w >> (2 * s)) & 0x03030303u) | (((bw >> sh) & 0x01010101u) << 2);
+    return static_cast<int>(__builtin_amdgcn_perm(cb1, cb0, sel));
 }
 
 // ---- GEMV
@@ -177,6 +262,105 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *_
     if (row < geom.n) y[row] = s;
 }
 
+// One row against the bit-plane formats: a workgroup per panel, 8 wavefronts over the 128-k
+// chunks, lane r on panel row r; a chunk is P 16-byte loads per lane and holds 128 / G groups.
+template <int FMT, int G>
+__global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t *__restrict__ packed,
+                                                                  const Geom geom,
+                                                                  const int *__restrict__ xq4,
+                                                                  const float *__restrict__ xs,
+                                                                  float *__restrict__ y) {
+    constexpr int P = planes<FMT>;
+    constexpr int GPC = kBitChunk / G;                // groups per chunk (2 or 1)
+    constexpr int RING = FMT == kFmtCQ3 ? 2 : 4;      // chunks in flight per wavefront
+    __shared__ float red[kW8Waves][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int p = blockIdx.x;
+    const int kc = (geom.k + kBitChunk - 1) / kBitChunk;
+    const int ng = geom.k / G;
+    const int nblk = (ng + 3) / 4;
+    const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)p * kc * P * 1024,
+                                (uint64_t)kc * P * 1024);
+    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)p * nblk * 512,
+                                (uint64_t)nblk * 512);
+    const int row = p * kPanelRows + lane;
+    uint32_t cb0, cb1 = 0u;
+    if (FMT == kFmtCQ3) {
+        const uint2 v = reinterpret_cast<const uint2 *>(packed + geom.off_codebook)[row];
+        cb0 = v.x;
+        cb1 = v.y;
+    } else {
+        cb0 = reinterpret_cast<const uint32_t *>(packed + geom.off_codebook)[row];
+    }
+    v4i ring[RING][P];
+    uint32_t meta[RING];
+    auto load = [&](int s, int c) {
+#pragma unroll
+        for (int u = 0; u < P; ++u)
+            ring[s][u] = ld128(rc, c < kc ? ((c * P + u) * 64 + lane) * 16 : kOOB);
+        // the chunk's groups share one block of 4 (GPC * c is even when GPC = 2)
+        const int g = c * GPC;
+        if (GPC == 2) meta[s] = ld32(rm, c < kc ? (((g >> 2) * 64 + lane) * 4 + (g & 3)) * 2 : kOOB);
+        else meta[s] = ld16(rm, c < kc ? (((g >> 2) * 64 + lane) * 4 + (g & 3)) * 2 : kOOB);
+    };
+#pragma unroll
+    for (int s = 0; s < RING; ++s) load(s, wave + s * kW8Waves);
+    float acc = 0.0f;
+    for (int c0 = wave; c0 < kc; c0 += RING * kW8Waves) {
+#pragma unroll
+        for (int s = 0; s < RING; ++s) {
+            const int c = c0 + s * kW8Waves;
+            if (c < kc) {
+                int dot = 0;
+#pragma unroll
+                for (int gi = 0; gi < 2; ++gi) {             // the chunk's two 64-k halves
+                    const int g = (c * kBitChunk + 64 * gi) / G;
+                    if (g >= ng) break;                      // (a ragged last chunk)
+                    const int *xg = xq4 + c * (kBitChunk / 4) + 16 * gi;   // wave-uniform
+                    int d4[4] = {0, 0, 0, 0};
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                // k = 128c + 64gi + 32pb + 16h + 4e .. + 3
+                                const uint32_t bw = static_cast<uint32_t>(ring[s][P - 1][2 * h + gi]);
+                                int wv;
+                                if (FMT == kFmtCQ3)
+                                    wv = cq3_dword(static_cast<uint32_t>(ring[s][gi][pb + 2 * h]), e,
+                                                   bw, 4 * pb + e, cb0, cb1);
+                                else
+                                    wv = cq1_dword(bw, 4 * pb + e, cb0);
+                                d4[e] = __builtin_amdgcn_sdot4(wv, xg[8 * pb + 4 * h + e], d4[e],
+                                                               false);
+                            }
+                    const int dgi = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+                    if (GPC == 2) {
+                        const float coef = xs[g] * half_bits_to_float((meta[s] >> (16 * gi)) & 0xFFFFu);
+                        acc = fmaf(coef, static_cast<float>(dgi), acc);
+                    } else {
+                        dot += dgi;
+                    }
+                }
+                if (GPC == 1) {
+                    const float coef = xs[c] * half_bits_to_float(meta[s] & 0xFFFFu);
+                    acc = fmaf(coef, static_cast<float>(dot), acc);
+                }
+            }
+            load(s, c + RING * kW8Waves);
+        }
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    float t = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < kW8Waves; ++w) t += red[w][lane];
+    if (row < geom.n) y[row] = t;
+}
+
 // ---- GEMM
 
 constexpr int kW8BN = 128;          // channels per workgroup (4 wavefronts x 32)
@@ -187,7 +371,9 @@ struct W8Stage {
     static constexpr int GPS = kW8SK / G;             // groups per stage (2 or 1)
     v4i a[2];                                         // two 16-byte activation units per thread
     v4i b[4];                                         // int8: the lane's chunk of each MFMA block
-    v2i w2[2];                                        // CQ2: the lane's 8 bytes of each chunk
+    v2i w2[2];                                        // CQ2 / CQ3: the lane's 8 bytes of each
+                                                      // chunk / crumb plane
+    v2i bp;                                           // CQ1 / CQ3: the lane's 8 bytes of bits
     uint32_t meta[GPS];
     float xs[GPS];                                    // per group: the scale of the lane's row
 };                                                    // (row r32 of tile `half`)
@@ -218,16 +404,23 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
     const int col = c0 + r32;
     const int p = col / kPanelRows, prow = col % kPanelRows;
     const int k = geom.k;
-    const int kc = k / ((FMT == kFmtCQ2) ? 64 : kW8Chunk);
+    constexpr int P = planes<FMT>;
+    const int kc = bit_plane<FMT> ? (k + kBitChunk - 1) / kBitChunk
+                                  : k / ((FMT == kFmtCQ2) ? 64 : kW8Chunk);
     const int ng = k / G;
     const int nblk = (ng + 3) / 4;
     const int nstage = (k + kW8SK - 1) / kW8SK;
-    uint32_t cb = 0u;
-    if (FMT == kFmtCQ2 && wact)
+    uint32_t cb = 0u, cb1 = 0u;
+    if ((FMT == kFmtCQ2 || FMT == kFmtCQ1) && wact)
         cb = reinterpret_cast<const uint32_t *>(packed + geom.off_codebook)[col];
+    if (FMT == kFmtCQ3 && wact) {
+        const uint2 v = reinterpret_cast<const uint2 *>(packed + geom.off_codebook)[col];
+        cb = v.x;
+        cb1 = v.y;
+    }
 
-    const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)(wact ? p : 0) * kc * 1024,
-                                wact ? (uint64_t)kc * 1024 : 0);
+    const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)(wact ? p : 0) * kc * P * 1024,
+                                wact ? (uint64_t)kc * P * 1024 : 0);
     const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)(wact ? p : 0) * nblk * 512,
                                 wact ? (uint64_t)nblk * 512 : 0);
     const rsrc_t rx = make_rsrc(xq, (uint64_t)m * k);
@@ -241,7 +434,14 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
             const bool ok = (m0 + rr < m) && (kk < k);
             r.a[i] = ld128(rx, ok ? (m0 + rr) * k + kk : kOOB);
         }
-        if (FMT == kFmtCQ2) {
+        if (bit_plane<FMT>) {                         // one chunk per stage
+            const bool okc = s < kc;
+            if (FMT == kFmtCQ3)
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    r.w2[u] = ld64(rc, okc ? ((s * P + u) * 64 + prow) * 16 + 8 * half : kOOB);
+            r.bp = ld64(rc, okc ? ((s * P + P - 1) * 64 + prow) * 16 + 8 * half : kOOB);
+        } else if (FMT == kFmtCQ2) {
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const int c = 2 * s + c2;
@@ -300,6 +500,20 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
                 const uint32_t w = static_cast<uint32_t>(ring[slot].w2[j >> 1][j & 1]);
                 b[j] = v4i{cq2_dword(w, 0, cb), cq2_dword(w, 1, cb), cq2_dword(w, 2, cb),
                            cq2_dword(w, 3, cb)};
+            }
+        } else if (bit_plane<FMT>) {
+            // block j = 2q + pb: bit word q of the lane's 8 bytes at shift 4pb; CQ3's crumbs as CQ2
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t bw = static_cast<uint32_t>(ring[slot].bp[j >> 1]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (FMT == kFmtCQ3)
+                        b[j][e] = cq3_dword(static_cast<uint32_t>(ring[slot].w2[j >> 1][j & 1]), e,
+                                            bw, 4 * (j & 1) + e, cb, cb1);
+                    else
+                        b[j][e] = cq1_dword(bw, 4 * (j & 1) + e, cb);
+                }
             }
         } else {
 #pragma unroll
@@ -374,10 +588,17 @@ hipError_t launch_w8_fmt(const Geom &g, const uint8_t *packed, int m, const int8
     if (m == 1) {
         const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
         const int *x4 = reinterpret_cast<const int *>(xq);
-        if (g.group == 64)
-            gemv_w8_kernel<FMT, 64><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
-        else
-            gemv_w8_kernel<FMT, 128><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+        if constexpr (bit_plane<FMT>) {
+            if (g.group == 64)
+                gemv_bits_kernel<FMT, 64><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+            else
+                gemv_bits_kernel<FMT, 128><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+        } else {
+            if (g.group == 64)
+                gemv_w8_kernel<FMT, 64><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+            else
+                gemv_w8_kernel<FMT, 128><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+        }
         return hipGetLastError();
     }
     const unsigned grid = static_cast<unsigned>(((m + 63) / 64) * ((g.n_pad + kW8BN - 1) / kW8BN));
@@ -391,6 +612,8 @@ hipError_t launch_w8(const Geom &g, const uint8_t *packed, int m, const int8_t *
                      const float *xs, float *y, hipStream_t stream) {
     if (m == 0) return hipSuccess;
     if (g.fmt == kFmtCQ2) return launch_w8_fmt<kFmtCQ2>(g, packed, m, xq, xs, y, stream);
+    if (g.fmt == kFmtCQ1) return launch_w8_fmt<kFmtCQ1>(g, packed, m, xq, xs, y, stream);
+    if (g.fmt == kFmtCQ3) return launch_w8_fmt<kFmtCQ3>(g, packed, m, xq, xs, y, stream);
     return launch_w8_fmt<kFmtInt8>(g, packed, m, xq, xs, y, stream);
 }
 
@@ -401,6 +624,22 @@ hipError_t launch_pack_cq2(const Geom &g, const uint8_t *codes, const int8_t *co
     pack_codes_cq2_kernel<<<static_cast<unsigned>(blocks < 65536 ? blocks : 65536), 256, 0, stream>>>(
         codes, codebook, g.n, g.k, chunks, reinterpret_cast<uint4 *>(packed + g.off_codes),
         reinterpret_cast<uint32_t *>(packed + g.off_codebook));
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_bits(const Geom &g, const uint8_t *codes, const int8_t *codebook,
+                            uint8_t *packed, hipStream_t stream) {
+    const int64_t chunks = (int64_t)g.n_pad * ((g.k + kBitChunk - 1) / kBitChunk);
+    const int64_t blocks = (chunks + 255) / 256;
+    const unsigned grid = static_cast<unsigned>(blocks < 65536 ? blocks : 65536);
+    uint4 *out = reinterpret_cast<uint4 *>(packed + g.off_codes);
+    uint32_t *cb_out = reinterpret_cast<uint32_t *>(packed + g.off_codebook);
+    if (g.fmt == kFmtCQ3)
+        pack_codes_bits_kernel<kFmtCQ3><<<grid, 256, 0, stream>>>(codes, codebook, g.n, g.k,
+                                                                  chunks, out, cb_out);
+    else
+        pack_codes_bits_kernel<kFmtCQ1><<<grid, 256, 0, stream>>>(codes, codebook, g.n, g.k,
+                                                                  chunks, out, cb_out);
     return hipGetLastError();
 }
 

@@ -15,7 +15,10 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a8.so")
 
-SYM, AFFINE, CODEBOOK, INT8, CQ2 = 0, 1, 2, 3, 4
+SYM, AFFINE, CODEBOOK, INT8, CQ2, CQ1, CQ3 = 0, 1, 2, 3, 4, 5, 6
+# k per byte of canonical codes, and codebook entries per row
+_K_PER_BYTE = {INT8: 1, CQ2: 4, CQ1: 8, CQ3: 1}
+_CB_ENTRIES = {CODEBOOK: 16, CQ2: 4, CQ1: 2, CQ3: 8}
 PANEL_ROWS = 64
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "no gfx950 device", 4: "HIP error"}
 
@@ -133,19 +136,20 @@ def pack(codes: torch.Tensor, scales: torch.Tensor, fmt: int, group: int, bias=N
          codebook=None, out: torch.Tensor | None = None):
     """Repack canonical device weights.  Returns (layout, packed uint8 tensor of layout.bytes).
 
-    codes uint8 [n, k/2] (low nibble = even k), int8 [n, k] for INT8, uint8 [n, k/4] for CQ2;
+    codes uint8 [n, k/2] (low nibble = even k), int8 [n, k] for INT8, uint8 [n, k/4] for CQ2,
+    [n, k/8] for CQ1 (bit i of byte b = index of k = 8b + i), [n, k] for CQ3 (low 3 bits);
     scales float16 [n, k/group]; bias float16 [n, k/group] (affine); codebook int8 [n, 16]
-    (codebook) or [n, 4] (CQ2).
+    (codebook), [n, 4] (CQ2), [n, 2] (CQ1) or [n, 8] (CQ3).
     """
     n, kh = codes.shape
-    k = kh * {INT8: 1, CQ2: 4}.get(fmt, 2)
+    k = kh * _K_PER_BYTE.get(fmt, 2)
     L = packed_layout(fmt, n, k, group)
     _dev(codes, torch.int8 if fmt == INT8 else torch.uint8, "codes")
     _dev(scales, torch.float16, "scales", (n, k // group))
     if bias is not None:
         _dev(bias, torch.float16, "bias", (n, k // group))
     if codebook is not None:
-        _dev(codebook, torch.int8, "codebook", (n, 4 if fmt == CQ2 else 16))
+        _dev(codebook, torch.int8, "codebook", (n, _CB_ENTRIES.get(fmt, 16)))
     if out is None:
         out = torch.empty(L.bytes, dtype=torch.uint8, device=codes.device)
     _dev(out, torch.uint8, "packed", (L.bytes,))
@@ -160,13 +164,13 @@ def pack_row_scale(codes: torch.Tensor, row_scales: torch.Tensor, fmt: int, grou
     """Repack weights with one scale (affine: and one bias) per output row, float16 [n], seen as
     the scale of each of the row's k/group groups (w4a8_pack_weights_row_scale)."""
     n, kh = codes.shape
-    L = packed_layout(fmt, n, 2 * kh, group)
-    _dev(codes, torch.uint8, "codes")
+    L = packed_layout(fmt, n, kh * _K_PER_BYTE.get(fmt, 2), group)
+    _dev(codes, torch.int8 if fmt == INT8 else torch.uint8, "codes")
     _dev(row_scales, torch.float16, "row_scales", (n,))
     if row_bias is not None:
         _dev(row_bias, torch.float16, "row_bias", (n,))
     if codebook is not None:
-        _dev(codebook, torch.int8, "codebook", (n, 4 if fmt == CQ2 else 16))
+        _dev(codebook, torch.int8, "codebook", (n, _CB_ENTRIES.get(fmt, 16)))
     if out is None:
         out = torch.empty(L.bytes, dtype=torch.uint8, device=codes.device)
     _dev(out, torch.uint8, "packed", (L.bytes,))

@@ -70,13 +70,20 @@ typedef enum {
     W4A8_INT8 = 3,         /* signed int8 weight, fp16 scale per group (W8A8: "geistlib issue
                               #500", sections "Scope" and "Design sketch"); codes are int8
                               [n][k], one byte per weight                                    */
-    W4A8_CQ2 = 4           /* 2-bit index into a per-output-row 4-entry int8 codebook, fp16
+    W4A8_CQ2 = 4,          /* 2-bit index into a per-output-row 4-entry int8 codebook, fp16
                               scale per group (CQ2 of PR #697's CQ1-CQ4 family; W2A8); codes
                               are uint8 [n][k/4], the index of k = 4b + i in bits 2i, 2i+1 of
                               byte b; codebook int8 [n][4]                                   */
-    /* W4A8_INT8 and W4A8_CQ2 run through w4a8_gemv / w4a8_gemm / w4a8_linear (no fused one-row
-       kernel); the gated, greedy-tail, partials and fp16-activation entry points return
-       W4A8_ERR_UNSUPPORTED for them. */
+    W4A8_CQ1 = 5,          /* 1-bit index into a per-output-row 2-entry int8 codebook, fp16
+                              scale per group (CQ1); codes are uint8 [n][k/8], the index of
+                              k = 8b + i in bit i of byte b; codebook int8 [n][2]            */
+    W4A8_CQ3 = 6           /* 3-bit index into a per-output-row 8-entry int8 codebook, fp16
+                              scale per group (CQ3); codes are uint8 [n][k], one index per
+                              byte in its low 3 bits (the high bits are ignored); codebook
+                              int8 [n][8]                                                    */
+    /* W4A8_INT8 and the CQ1-CQ3 formats run through w4a8_gemv / w4a8_gemm / w4a8_linear (no
+       fused one-row kernel); the gated, greedy-tail, partials and fp16-activation entry points
+       return W4A8_ERR_UNSUPPORTED for them. */
 } w4a8_format;
 
 /* Rows of the packed weight buffer come in panels of this many output channels. */
@@ -98,6 +105,11 @@ typedef enum {
  *             dword, fp16 scale in the low half and fp16 bias in the high half.  A row's block
  *             is one 8- or 16-byte load.
  *   codebook  at off_codebook (CODEBOOK only): int8 [n_pad][16].
+ * INT8, CQ2, CQ1 and CQ3 keep the panels and the meta section (SYM's) and change the codes:
+ *   INT8: chunk column c holds w[n][16c .. 16c+15];  CQ2: chunk column c holds 64 k;
+ *   CQ1 / CQ3: each 128 k (k padded to a multiple of 128) is 1 / 3 chunk columns in a row.
+ *   Their codebooks at off_codebook: CQ2 and CQ1 one dword per row (entries in its bytes), CQ3
+ *   two.  The exact bit order inside a chunk is the kernels' own (the packer writes it).
  * Rows n >= n of the padded last panel hold zero codes, zero scales and zero codebooks.
  */
 typedef struct {
@@ -110,7 +122,7 @@ typedef struct {
     uint64_t bytes;       /* total size of the packed buffer               */
     uint64_t off_codes;
     uint64_t off_meta;
-    uint64_t off_codebook;  /* 0 and unused unless CODEBOOK                */
+    uint64_t off_codebook;  /* 0 and unused unless a codebook format       */
 } w4a8_layout;
 
 /*
@@ -125,10 +137,11 @@ w4a8_status w4a8_packed_layout(int32_t format, int32_t n, int32_t k, int32_t gro
 /*
  * Repack canonical weights into the layout described by L (a pure permutation of nibbles plus
  * the AFFINE re-encode u -> u XOR 8; scales, bias and codebook are copied).
- *   codes      uint8 [n][k/2]: two codes per byte, the low nibble holds the even k
+ *   codes      uint8 [n][k/2]: two codes per byte, the low nibble holds the even k (4-bit
+ *              formats); the w4a8_format comments give INT8's and the CQ formats' shapes
  *   scales_f16 uint16 [n][k/group] (IEEE binary16 bit patterns)
  *   bias_f16   uint16 [n][k/group] for AFFINE, else must be NULL
- *   codebook   int8 [n][16] for CODEBOOK, else must be NULL
+ *   codebook   int8 [n][16] for CODEBOOK, [n][4] CQ2, [n][2] CQ1, [n][8] CQ3, else NULL
  *   packed     L->bytes of device memory, written completely (padding included)
  * Source: "cactus PR #697", follow-up commits on the interleaved lm_head and on the single
  * runtime weight format (one packed format read by every kernel, built once at load).

@@ -75,7 +75,7 @@ def test_layout_sizes():
 
 
 @pytest.mark.parametrize("args", [
-    (5, 64, 64, 64), (-1, 64, 64, 64), (0, 64, 96, 64), (0, 64, 64, 32), (0, 0, 64, 64),
+    (7, 64, 64, 64), (-1, 64, 64, 64), (0, 64, 96, 64), (0, 64, 64, 32), (0, 0, 64, 64),
     (0, 64, 0, 64), (0, 64, 64 * 3, 128), (0, 1 << 25, 64, 64), (0, 64, (1 << 20) + 64, 64),
 ])
 def test_layout_rejects(lib, args):
@@ -217,6 +217,15 @@ def test_invalid_calls_are_rejected_on_the_host(lib):
     assert L2.off_meta == 128 * 64 and L2.off_codebook > L2.off_meta and L2.bytes % 256 == 0
     assert lib.w4a8_pack_weights(ctypes.byref(L2), p, p, None, None, p, None) == ERR_ARG   # codebook
     assert lib.w4a8_debug_partials(ctypes.byref(L2), p, 2, p, p, p, None) == ERR_UNSUPPORTED
+    # 1- and 3-bit codebooks: 16 / 48 bytes per 128 k of a row, k padded to a multiple of 128
+    L1 = w4a8.packed_layout(w4a8.CQ1, 100, 192, 64)
+    L3 = w4a8.packed_layout(w4a8.CQ3, 100, 192, 64)
+    assert L1.off_meta == 128 * 2 * 16 and L3.off_meta == 128 * 2 * 48
+    assert L1.bytes - L1.off_codebook == 512 and L3.bytes - L3.off_codebook == 1024
+    assert lib.w4a8_pack_weights(ctypes.byref(L3), p, p, None, None, p, None) == ERR_ARG
+    assert lib.w4a8_gemv_argmax(ctypes.byref(L1), p, p, p, p, f(0.0), p, p, p, p, 16,
+                                None) == ERR_UNSUPPORTED
+    assert lib.w4a8_packed_layout(7, 100, 256, 64, ctypes.byref(L1)) == ERR_ARG
     L8P = ctypes.byref(L8)
     assert lib.w4a8_gemm_glu(ctypes.byref(w4a8.packed_layout(w4a8.INT8, 128, 256, 64)), p, 2, p,
                              p, p, silu, p, None) == ERR_UNSUPPORTED

@@ -1,5 +1,5 @@
-"""GPU parity of int8 weights (format 3, W8A8) and 2-bit codebook weights (format 4, CQ2) through
-w4a8_linear / w4a8_gemv / w4a8_gemm against the oracle: the prepass outputs bit-exact, y within
+"""GPU parity of int8 weights (format 3, W8A8) and 2-, 1- and 3-bit codebook weights (formats 4, 5,
+6: CQ2, CQ1, CQ3) through w4a8_linear / w4a8_gemv / w4a8_gemm against the oracle: the prepass outputs bit-exact, y within
 the linear's bar (relative L2 error <= 1e-5, |err| <= 1e-4 T per element)."""
 from __future__ import annotations
 
@@ -37,9 +37,11 @@ def _run(L):
 
 
 # one row (GEMV) with both group widths and a rotated prepass; several rows (GEMM): ragged m and
-# n (a half-empty 128-channel tile), an odd group count (a one-group last stage), one group
+# n (a half-empty 128-channel tile), an odd group count (a one-group last stage), one group; k
+# an odd multiple of 64 (half of the bit-plane formats' last 128-k chunk is padding)
 CASES = [
     ("C2a", dict(n=1000, k=2048)),
+    ("C2a", dict(n=200, k=320)),
     ("C4", dict(m=1, n=320, k=1536)),
     ("C1", dict(n=64, k=64)),
     ("C3a", dict(m=65, n=1000, k=640)),
@@ -50,10 +52,11 @@ CASES = [
 ]
 
 
-FORMATS = [synth.FMT_INT8, synth.FMT_CQ2]
+FORMATS = [synth.FMT_INT8, synth.FMT_CQ2, synth.FMT_CQ1, synth.FMT_CQ3]
+FMT_IDS = ["int8", "cq2", "cq1", "cq3"]
 
 
-@pytest.mark.parametrize("fmt", FORMATS, ids=["int8", "cq2"])
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
 @pytest.mark.parametrize("name,over", CASES,
                          ids=[f"{c}-{'-'.join(f'{k}{v}' for k, v in o.items())}"
                               for c, o in CASES])
@@ -70,7 +73,7 @@ def test_w8_parity(name, over, fmt):
     check_y(got["y"], ref["y"], ref["t"], f"w8 {name} {over}")
 
 
-@pytest.mark.parametrize("fmt", FORMATS, ids=["int8", "cq2"])
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
 def test_w8_gemv_gemm_entry_points_same_bits(fmt):
     # w4a8_gemv / w4a8_gemm on w4a8_linear's own prepass outputs run the same kernels
     w = _w4a8()
@@ -86,10 +89,10 @@ def test_w8_gemv_gemm_entry_points_same_bits(fmt):
         assert np.array_equal(got["y"].view(np.uint32), y2.view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt", FORMATS, ids=["int8", "cq2"])
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
 def test_w8_full_size_prompt_tile(layer_cache, fmt):
     """C3a's 128 x 5120 x 34816 shape with int8 weights (Gaussian draws quantized per group) or
-    2-bit codebook weights, on a seeded sample of output channels."""
+    1-, 2- or 3-bit codebook weights, on a seeded sample of output channels."""
     key = f"C3a-fmt{fmt}"
     if key not in layer_cache:
         layer_cache[key] = synth.make("C3a", fmt=fmt)
@@ -101,3 +104,15 @@ def test_w8_full_size_prompt_tile(layer_cache, fmt):
     cols[-1] = cfg.n - 1
     ref = oracle_layer(L, cols)
     check_y(got["y"][:, cols], ref["y"], ref["t"], "w8 full C3a")
+
+
+def test_cq3_ignores_the_high_bits_of_its_codes():
+    # the canonical 3-bit codes keep one index per byte; bits 3-7 are not part of it
+    base = synth.make("C3a", full_range=True, fmt=synth.FMT_CQ3, m=3, n=200, k=320)
+    noisy = dict(base)
+    extra = np.random.default_rng(31).integers(0, 32, size=base["codes"].shape, dtype=np.uint8)
+    noisy["codes"] = base["codes"] | (extra << 3)
+    a, b = _run(base), _run(noisy)
+    assert np.array_equal(a["y"].view(np.uint32), b["y"].view(np.uint32))
+    ref = oracle_layer(noisy)
+    check_y(b["y"], ref["y"], ref["t"], "cq3 high bits")
