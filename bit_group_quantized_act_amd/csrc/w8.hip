@@ -51,6 +51,8 @@ namespace {
 constexpr int kW8Chunk = 16;        // k per 16-byte chunk
 constexpr int kW8Waves = 8;
 constexpr int kBitChunk = 128;      // k per chunk of the bit-plane formats
+constexpr int kMinUnits = 4;        // GEMV: groups (chunks) per wavefront before panels share
+constexpr int kMinGrid = 1024;      // GEMV: fewest workgroups once panels share one
 
 template <int FMT>
 constexpr bool bit_plane = FMT == kFmtCQ1 || FMT == kFmtCQ3;
@@ -186,28 +188,32 @@ __device__ __forceinline__ int cq3_dword(uint32_t w, int s, uint32_t bw, int sh,
 
 // ---- GEMV
 
+// wpp: wavefronts per panel (1, 2, 4 or 8); a workgroup takes 8 / wpp consecutive panels, so a
+// short row still gives each wavefront several groups (or chunks) and each workgroup more bytes.
 template <int FMT, int G>
 __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *__restrict__ packed,
                                                                 const Geom geom,
                                                                 const int *__restrict__ xq4,
                                                                 const float *__restrict__ xs,
-                                                                float *__restrict__ y) {
+                                                                float *__restrict__ y, int wpp) {
     constexpr int CK = (FMT == kFmtCQ2) ? 64 : kW8Chunk;   // k per chunk
     constexpr int CPG = G / CK;                       // chunks per group
     constexpr int RING = (FMT == kFmtCQ2) ? 4 : 256 / G;   // groups in flight per wavefront
     __shared__ float red[kW8Waves][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int p = blockIdx.x;
+    const int wsub = wave & (wpp - 1);
+    const int p = blockIdx.x * (kW8Waves / wpp) + wave / wpp;
+    const bool live = p < geom.n_pad / kPanelRows;    // (the last workgroup may be partial)
     const int kc = geom.k / CK;
-    const int ng = geom.k / G;
-    const int nblk = (ng + 3) / 4;
-    const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)p * kc * 1024,
-                                (uint64_t)kc * 1024);
-    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)p * nblk * 512,
-                                (uint64_t)nblk * 512);
+    const int ng = live ? geom.k / G : 0;
+    const int nblk = (geom.k / G + 3) / 4;
+    const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)(live ? p : 0) * kc * 1024,
+                                live ? (uint64_t)kc * 1024 : 0);
+    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)(live ? p : 0) * nblk * 512,
+                                live ? (uint64_t)nblk * 512 : 0);
     uint32_t cb = 0u;
-    if (FMT == kFmtCQ2)
+    if (FMT == kFmtCQ2 && live)
         cb = reinterpret_cast<const uint32_t *>(packed + geom.off_codebook)[p * kPanelRows + lane];
     v4i ring[RING][CPG];
     uint32_t meta[RING];
@@ -218,12 +224,12 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *_
         meta[s] = ld16(rm, g < ng ? (((g >> 2) * 64 + lane) * 4 + (g & 3)) * 2 : kOOB);
     };
 #pragma unroll
-    for (int s = 0; s < RING; ++s) load(s, wave + s * kW8Waves);
+    for (int s = 0; s < RING; ++s) load(s, wsub + s * wpp);
     float acc = 0.0f;
-    for (int g0 = wave; g0 < ng; g0 += RING * kW8Waves) {
+    for (int g0 = wsub; g0 < ng; g0 += RING * wpp) {
 #pragma unroll
         for (int s = 0; s < RING; ++s) {
-            const int g = g0 + s * kW8Waves;
+            const int g = g0 + s * wpp;
             if (g < ng) {
                 const int *xg = xq4 + g * (G / 4);       // the group's codes: wave-uniform
                 int d4[4] = {0, 0, 0, 0};
@@ -249,15 +255,14 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *_
                 const float coef = xs[g] * half_bits_to_float(meta[s] & 0xFFFFu);
                 acc = fmaf(coef, static_cast<float>(dot), acc);
             }
-            load(s, g + RING * kW8Waves);
+            load(s, g + RING * wpp);
         }
     }
     red[wave][lane] = acc;
     __syncthreads();
-    if (wave != 0) return;
-    float s = red[0][lane];
-#pragma unroll
-    for (int w = 1; w < kW8Waves; ++w) s += red[w][lane];
+    if (wsub != 0 || !live) return;
+    float s = red[wave][lane];
+    for (int w = 1; w < wpp; ++w) s += red[wave + w][lane];
     const int row = p * kPanelRows + lane;
     if (row < geom.n) y[row] = s;
 }
@@ -269,28 +274,30 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
                                                                   const Geom geom,
                                                                   const int *__restrict__ xq4,
                                                                   const float *__restrict__ xs,
-                                                                  float *__restrict__ y) {
+                                                                  float *__restrict__ y, int wpp) {
     constexpr int P = planes<FMT>;
     constexpr int GPC = kBitChunk / G;                // groups per chunk (2 or 1)
     constexpr int RING = FMT == kFmtCQ3 ? 2 : 4;      // chunks in flight per wavefront
     __shared__ float red[kW8Waves][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int p = blockIdx.x;
-    const int kc = (geom.k + kBitChunk - 1) / kBitChunk;
+    const int wsub = wave & (wpp - 1);
+    const int p = blockIdx.x * (kW8Waves / wpp) + wave / wpp;
+    const bool live = p < geom.n_pad / kPanelRows;    // (the last workgroup may be partial)
+    const int kc = live ? (geom.k + kBitChunk - 1) / kBitChunk : 0;
     const int ng = geom.k / G;
     const int nblk = (ng + 3) / 4;
-    const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)p * kc * P * 1024,
+    const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)(live ? p : 0) * kc * P * 1024,
                                 (uint64_t)kc * P * 1024);
-    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)p * nblk * 512,
-                                (uint64_t)nblk * 512);
+    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)(live ? p : 0) * nblk * 512,
+                                live ? (uint64_t)nblk * 512 : 0);
     const int row = p * kPanelRows + lane;
-    uint32_t cb0, cb1 = 0u;
-    if (FMT == kFmtCQ3) {
+    uint32_t cb0 = 0u, cb1 = 0u;
+    if (FMT == kFmtCQ3 && live) {
         const uint2 v = reinterpret_cast<const uint2 *>(packed + geom.off_codebook)[row];
         cb0 = v.x;
         cb1 = v.y;
-    } else {
+    } else if (live) {
         cb0 = reinterpret_cast<const uint32_t *>(packed + geom.off_codebook)[row];
     }
     v4i ring[RING][P];
@@ -305,12 +312,12 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
         else meta[s] = ld16(rm, c < kc ? (((g >> 2) * 64 + lane) * 4 + (g & 3)) * 2 : kOOB);
     };
 #pragma unroll
-    for (int s = 0; s < RING; ++s) load(s, wave + s * kW8Waves);
+    for (int s = 0; s < RING; ++s) load(s, wsub + s * wpp);
     float acc = 0.0f;
-    for (int c0 = wave; c0 < kc; c0 += RING * kW8Waves) {
+    for (int c0 = wsub; c0 < kc; c0 += RING * wpp) {
 #pragma unroll
         for (int s = 0; s < RING; ++s) {
-            const int c = c0 + s * kW8Waves;
+            const int c = c0 + s * wpp;
             if (c < kc) {
                 int dot = 0;
 #pragma unroll
@@ -349,15 +356,14 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
                     acc = fmaf(coef, static_cast<float>(dot), acc);
                 }
             }
-            load(s, c + RING * kW8Waves);
+            load(s, c + RING * wpp);
         }
     }
     red[wave][lane] = acc;
     __syncthreads();
-    if (wave != 0) return;
-    float t = red[0][lane];
-#pragma unroll
-    for (int w = 1; w < kW8Waves; ++w) t += red[w][lane];
+    if (wsub != 0 || !live) return;
+    float t = red[wave][lane];
+    for (int w = 1; w < wpp; ++w) t += red[wave + w][lane];
     if (row < geom.n) y[row] = t;
 }
 
@@ -586,18 +592,29 @@ template <int FMT>
 hipError_t launch_w8_fmt(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
                          const float *xs, float *y, hipStream_t stream) {
     if (m == 1) {
-        const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
+        // waves per panel: halved while a wavefront would get fewer than kMinUnits groups
+        // (chunks) and the grid keeps at least kMinGrid workgroups (4 per CU)
+        const int units = bit_plane<FMT> ? (g.k + kBitChunk - 1) / kBitChunk : g.k / g.group;
+        const int panels = g.n_pad / kPanelRows;
+        int wpp = kW8Waves;
+        while (wpp > 1 && units < kMinUnits * wpp) {
+            const int ppw_next = kW8Waves / (wpp / 2);
+            if ((panels + ppw_next - 1) / ppw_next < kMinGrid) break;
+            wpp /= 2;
+        }
+        const int ppw = kW8Waves / wpp;
+        const unsigned grid = static_cast<unsigned>((panels + ppw - 1) / ppw);
         const int *x4 = reinterpret_cast<const int *>(xq);
         if constexpr (bit_plane<FMT>) {
             if (g.group == 64)
-                gemv_bits_kernel<FMT, 64><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+                gemv_bits_kernel<FMT, 64><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y, wpp);
             else
-                gemv_bits_kernel<FMT, 128><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+                gemv_bits_kernel<FMT, 128><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y, wpp);
         } else {
             if (g.group == 64)
-                gemv_w8_kernel<FMT, 64><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+                gemv_w8_kernel<FMT, 64><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y, wpp);
             else
-                gemv_w8_kernel<FMT, 128><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y);
+                gemv_w8_kernel<FMT, 128><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y, wpp);
         }
         return hipGetLastError();
     }

@@ -116,3 +116,26 @@ def test_cq3_ignores_the_high_bits_of_its_codes():
     assert np.array_equal(a["y"].view(np.uint32), b["y"].view(np.uint32))
     ref = oracle_layer(noisy)
     check_y(b["y"], ref["y"], ref["t"], "cq3 high bits")
+
+
+FULL_ROW = [(synth.FMT_INT8, 262144), (synth.FMT_CQ2, 262144), (synth.FMT_CQ1, 262080),
+            (synth.FMT_CQ3, 262080)]
+
+
+@pytest.mark.parametrize("fmt,n", FULL_ROW, ids=[f"{i}-n{n}" for i, (_, n) in
+                                                  zip(FMT_IDS, FULL_ROW)])
+def test_w8_full_size_decode_row(layer_cache, fmt, n):
+    """C5a's one-row vocabulary shape (K = 1536): at this width several panels share a GEMV
+    workgroup; n = 262080 (4095 panels) leaves the last workgroup partly empty.  A seeded sample
+    of output channels and the last one."""
+    key = f"C5a-fmt{fmt}-n{n}"
+    if key not in layer_cache:
+        layer_cache[key] = synth.make("C5a", full_range=True, fmt=fmt, n=n)
+    L = layer_cache[key]
+    cfg = L["cfg"]
+    print(f"w8 full C5a: fmt={fmt} n={cfg.n} k={cfg.k}", flush=True)
+    got = _run(L)
+    cols = np.sort(np.random.default_rng(37).choice(cfg.n, 512, replace=False))
+    cols[-1] = cfg.n - 1
+    ref = oracle_layer(L, cols)
+    check_y(got["y"][:, cols], ref["y"], ref["t"], "w8 full C5a")
