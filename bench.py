@@ -73,7 +73,9 @@ KERNEL_SOURCES = {
     "gemm": ["gemm.hip", "w4a8_kernels.h"],
 }
 TRAFFIC = {
-    "C2a": dict(kernel="gemv", source_sha="b3fb8338e57ea99c", fetch_kib=8767.25, write_kib=66.25,
+    "C2a": dict(kernel="gemv", source_sha="f594f3a2a1de214d", fetch_kib=8767.26, write_kib=66.25,
+                fetch_factor=1.99979, write_factor=1.0),
+    "C3a": dict(kernel="gemm", source_sha="b8c12df0a1d95bfa", fetch_kib=53302.25, write_kib=17408.0,
                 fetch_factor=1.99979, write_factor=1.0),
 }
 
@@ -437,8 +439,9 @@ def main():
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4))
     kname = "gemv" if cfg.m == 1 else "gemm"     # the fused kernel lives in gemv.hip
-    traffic_key = (cfg.name if act is None and cap is None and not a16 and not byte_decoded else
-                   f"{cfg.name}-{'glu' if act is not None else 'argmax' if cap is not None else 'a16'}")
+    variant = ("glu" if act is not None else "argmax" if cap is not None else "a16" if a16 else
+               synth.FORMAT_NAMES[cfg.fmt] if byte_decoded else None)
+    traffic_key = cfg.name if variant is None else f"{cfg.name}-{variant}"   # counters per kernel
     shown = ("gemv_argmax (GEMV with the tail + key reduction)" if cap is not None else
              f"{kname}_a16" if a16 else f"{kname}_w8" if byte_decoded else kname)
     roof.update(traffic=measured_traffic(traffic_key, kname), kernel=shown,
