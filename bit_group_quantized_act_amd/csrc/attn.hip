@@ -26,7 +26,9 @@
 //   blocks no query of the tile sees; the wavefronts merge through LDS, and ranges split over
 //   several workgroups (to fill the chip) merge in a second kernel, both in a fixed order.  The
 //   next value group's scales, codes and column sums load as soon as the current group's are used;
-//   the codes are P' * (255 / max P'), one reciprocal per (row, group, block).
+//   the codes are P' * (255 / max P'), one reciprocal per (row, group, block).  At one wavefront
+//   per SIMD the waits are the cost: a block's positions and key scales load during the
+//   wavefront's previous block, and its first value group right behind its key codes.
 #include "w4a8_kernels.h"
 
 namespace w4a8 {
@@ -109,7 +111,8 @@ struct AttnArgs {
     int8_t *q8;                // [nh][nq][d]
     float *sq;                 // [nh][nq]
     float *o, *m, *l;          // final [nh][nq][d], [nh][nq] (nsplit == 1) ...
-    float *work;               // ... or partial states [nsplit][nh][nq][d + 2]
+    float *work;               // ... or partial states: o [nsplit][nh][nq][d], then (m, l)
+                               // [nsplit][nh][nq][2]
 };
 
 __device__ __forceinline__ float wave_max32(float v) {          // max with the other lane half
@@ -140,7 +143,10 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     const int kh = head / (a.nh / ag.nkvh);
     const int qi = q0 + col;                                  // this lane's query
     const bool qlive = qi < a.nq;
-    const int64_t qpos = (int64_t)a.pos0 + qi;
+    // positions compare as unsigned 32-bit: pos0 + qi < 2^32, and a slot's p is checked >= 0
+    // (then p <= qpos makes qpos - p exact)
+    const uint32_t qpos = static_cast<uint32_t>(a.pos0) + static_cast<uint32_t>(qi);
+    const uint32_t window = static_cast<uint32_t>(a.window), sink = static_cast<uint32_t>(a.sink);
 
     // the query row's int8 codes (from the query prepass), as the B operands of the QK product:
     // lane (q, h) holds d = 32i + 16h .. +15 of each 32-wide chunk i
@@ -169,44 +175,89 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
 
     const int b_lo = split * a.bps;
     const int b_hi = min(ag.nblk, b_lo + a.bps);
-    for (int b = b_lo + blane; b < b_hi; b += BL) {
-        // positions and visibility of the lane's 32 slots (two subtiles of 16)
+    // a block's slot positions and key scales for the lane's 32 slots: loaded while the
+    // wavefront's previous block is processed, so visibility needs no wait at a block's start
+    struct KBlock {
+        int4 pos[2][4];
+        float4 sk[2][4];
+    };
+    auto load_kblock = [&](int b, KBlock &k) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int base = b * kSlots + t * 32 + half * 16;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) k.pos[t][c] = reinterpret_cast<const int4 *>(posb + base)[c];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) k.sk[t][c] = reinterpret_cast<const float4 *>(skb + base)[c];
+        }
+    };
+    // block b with its positions and key scales in kc; the wavefront's next block's load into kn
+    auto block = [&](int b, const KBlock &kc, KBlock &kn) {
+        if (b + BL < b_hi) load_kblock(b + BL, kn);
+        // visibility of the lane's 32 slots (two subtiles of 16)
         float s[2][16];
         bool any = false;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int base = b * kSlots + t * 32 + half * 16;
             int pos16[16];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int4 pv = reinterpret_cast<const int4 *>(posb + base)[c];
+                const int4 pv = kc.pos[t][c];
                 pos16[4 * c] = pv.x; pos16[4 * c + 1] = pv.y; pos16[4 * c + 2] = pv.z;
                 pos16[4 * c + 3] = pv.w;
             }
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t p = pos16[e];
-                const bool vis = qlive && p >= 0 && p <= qpos &&
-                                 (a.window <= 0 || p < a.sink || qpos - p < a.window);
+                const uint32_t p = static_cast<uint32_t>(pos16[e]);
+                const bool vis = qlive && pos16[e] >= 0 && p <= qpos &&
+                                 (window == 0u || p < sink || qpos - p < window);
                 s[t][e] = vis ? 0.0f : kNegInf;
                 any |= vis;
             }
         }
-        if (__builtin_amdgcn_ballot_w64(any) == 0) continue;          // no query sees the block
+        if (__builtin_amdgcn_ballot_w64(any) == 0) return;            // no query sees the block
+        // the value side of group g: its scales for the lane's 32 slots, the transposed value
+        // codes (A operands) and the column sums
+        struct VGroup {
+            float4 sv[2][4];
+            v4i va[2];
+            int4 vsum[4];
+        };
+        auto load_group = [&](int g, VGroup &v) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const float4 *svr = reinterpret_cast<const float4 *>(
+                    svb + ((int64_t)b * NG + g) * kSlots + t * 32 + half * 16);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v.sv[t][c] = svr[c];
+                v.va[t] = *reinterpret_cast<const v4i *>(
+                    vtb + ((int64_t)b * D + 32 * g + col) * kSlots + t * 32 + half * 16);
+            }
+            const int4 *vsr = reinterpret_cast<const int4 *>(vsb + (int64_t)b * D + g * 32 + half * 16);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v.vsum[c] = vsr[c];
+        };
+        // the key codes of both subtiles, then the first value group: its loads complete while
+        // the QK product and the softmax run
+        v4i ka[2][NG];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int8_t *kr = kqb + ((int64_t)b * kSlots + t * 32 + col) * D + 16 * half;
+#pragma unroll
+            for (int i = 0; i < NG; ++i) ka[t][i] = *reinterpret_cast<const v4i *>(kr + 32 * i);
+        }
+        VGroup cur;
+        load_group(dpart * NGW, cur);
         // S^T = K Q^T for the block's two 32-slot subtiles
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             v16i acc = {};
-            const int8_t *kr = kqb + ((int64_t)b * kSlots + t * 32 + col) * D + 16 * half;
 #pragma unroll
-            for (int i = 0; i < NG; ++i) {
-                const v4i ka = *reinterpret_cast<const v4i *>(kr + 32 * i);
-                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qb[i], acc, 0, 0, 0);
-            }
-            const float4 *skr = reinterpret_cast<const float4 *>(skb + b * kSlots + t * 32 + half * 16);
+            for (int i = 0; i < NG; ++i)
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[t][i], qb[i], acc, 0, 0, 0);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float4 kv = skr[c];
+                const float4 kv = kc.sk[t][c];
                 const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -234,31 +285,8 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
         lrun = lrun * alpha + psum;
         mrun = (mb == kNegInf) ? mrun : mnew;
         const float keep = (mb == kNegInf) ? 1.0f : alpha;
-        // the value side of group g: its scales for the lane's 32 slots, the transposed value
-        // codes (A operands) and the column sums; loaded one group ahead of their use
-        struct VGroup {
-            float4 sv[2][4];
-            v4i va[2];
-            int4 vsum[4];
-        };
-        auto load_group = [&](int g, VGroup &v) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const float4 *svr = reinterpret_cast<const float4 *>(
-                    svb + ((int64_t)b * NG + g) * kSlots + t * 32 + half * 16);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) v.sv[t][c] = svr[c];
-                v.va[t] = *reinterpret_cast<const v4i *>(
-                    vtb + ((int64_t)b * D + 32 * g + col) * kSlots + t * 32 + half * 16);
-            }
-            const int4 *vsr = reinterpret_cast<const int4 *>(vsb + (int64_t)b * D + g * 32 + half * 16);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) v.vsum[c] = vsr[c];
-        };
         // one group's operands in flight: the next group's scales and codes load as soon as the
         // current group's are consumed, overlapping its matrix product and epilogue
-        VGroup cur;
-        load_group(dpart * NGW, cur);
 #pragma unroll
         for (int g = 0; g < NGW; ++g) {
             // P folded with the value group's scale, quantized to u8 per (row, group, block)
@@ -272,22 +300,28 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
                                          fmaxf(p[t][4 * c + 2] * sv.z, p[t][4 * c + 3] * sv.w)));
                 }
             mx = wave_max32(mx);
-            const float sp = mx / 255.0f;
-            const float rsp = 255.0f / mx;        // one reciprocal per (row, group, block)
+            const float sp = mx / 255.0f;         // 0 when nothing of the row is visible
+            // one reciprocal per (row, group, block); u = rint(pg * rsp) lies in 0..255 since
+            // pg <= mx, and every pg is 0 when mx is
+            const float rsp = (mx > 0.0f) ? 255.0f / mx : 0.0f;
             v16i iacc = {};
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                uint32_t w4[4] = {0u, 0u, 0u, 0u};
+                uint32_t w4[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const float sv4[4] = {cur.sv[t][c].x, cur.sv[t][c].y, cur.sv[t][c].z,
                                           cur.sv[t][c].w};
+                    // x + (2^23 + 2^22 + 128) rounds x to the nearest integer (ties to even) in
+                    // the sum's low bits, already offset by 128: the low byte is u - 128 as int8
+                    uint32_t bq[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float pg = p[t][4 * c + i] * sv4[i];
-                        const int u = (mx > 0.0f) ? static_cast<int>(fminf(rintf(pg * rsp), 255.0f)) : 0;
-                        w4[c] |= static_cast<uint32_t>((u - 128) & 0xFF) << (8 * i);
+                        bq[i] = __float_as_uint(pg * rsp + 12583040.0f);
                     }
+                    w4[c] = __builtin_amdgcn_perm(bq[1], bq[0], 0x0C0C0400u) |
+                            __builtin_amdgcn_perm(bq[3], bq[2], 0x04000C0Cu);
                 }
                 const v4i pb = {static_cast<int>(w4[0]), static_cast<int>(w4[1]),
                                 static_cast<int>(w4[2]), static_cast<int>(w4[3])};
@@ -301,9 +335,16 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const float av = static_cast<float>(iacc[e] + 128 * vs16[e]);
-                o[g][e] = o[g][e] * keep + ((mx > 0.0f) ? sp * av : 0.0f);
+                o[g][e] = fmaf(o[g][e], keep, sp * av);
             }
         }
+    };
+    // the wavefront's blocks b_lo + blane, + BL, ..., two per turn with the key sides ping-ponged
+    KBlock k0, k1;
+    if (b_lo + blane < b_hi) load_kblock(b_lo + blane, k0);
+    for (int b = b_lo + blane; b < b_hi; b += 2 * BL) {
+        block(b, k0, k1);
+        if (b + BL < b_hi) block(b + BL, k1, k0);
     }
 
     // merge the states of the BL wavefronts of each group set (fixed order): M = max m_w, each
@@ -346,9 +387,13 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
         orow = a.o + row * D;
         if (stats) { a.m[row] = mall; a.l[row] = lsum; }
     } else {
-        float *ws = a.work + ((int64_t)split * a.nh * a.nq + row) * (D + 2);
-        orow = ws;
-        if (stats) { ws[D] = mall; ws[D + 1] = lsum; }
+        const int64_t rows = (int64_t)a.nh * a.nq, srow = (int64_t)split * rows + row;
+        orow = a.work + srow * D;
+        if (stats) {
+            float *ml = a.work + a.nsplit * rows * D + 2 * srow;
+            ml[0] = mall;
+            ml[1] = lsum;
+        }
     }
 #pragma unroll
     for (int g = 0; g < NGW; ++g)
@@ -382,26 +427,33 @@ __global__ __launch_bounds__(256) void attn_quant_q(const float4 *__restrict__ q
     if (t % lanes_per_row == 0) sq[t / lanes_per_row] = scale;
 }
 
-// the split states of each (head, query) merged in split order
+// the split states of each (head, query) merged in split order; a thread per 4 columns of a row
 __global__ __launch_bounds__(256) void attn_merge(int nsplit, int64_t rows, int d,
                                                   const float *__restrict__ work,
                                                   float *__restrict__ o, float *__restrict__ m,
                                                   float *__restrict__ l) {
     const int64_t t = blockIdx.x * (int64_t)256 + threadIdx.x;
-    if (t >= rows * d) return;
-    const int64_t row = t / d;
-    const int c = static_cast<int>(t % d);
+    const int q4 = d / 4;
+    if (t >= rows * q4) return;
+    const int64_t row = t / q4;
+    const int c4 = static_cast<int>(t % q4);
+    const float2 *ml = reinterpret_cast<const float2 *>(work + nsplit * rows * d);
     float mall = kNegInf;
-    for (int s = 0; s < nsplit; ++s) mall = fmaxf(mall, work[(s * rows + row) * (d + 2) + d]);
-    float acc = 0.0f, lsum = 0.0f;
+    for (int s = 0; s < nsplit; ++s) mall = fmaxf(mall, ml[s * rows + row].x);
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float lsum = 0.0f;
     for (int s = 0; s < nsplit; ++s) {
-        const float *ws = work + (s * rows + row) * (d + 2);
-        const float f = (ws[d] == kNegInf) ? 0.0f : expf(ws[d] - mall);
-        acc += ws[c] * f;
-        lsum += ws[d + 1] * f;
+        const float2 st = ml[s * rows + row];
+        const float f = (st.x == kNegInf) ? 0.0f : expf(st.x - mall);
+        const float4 v = reinterpret_cast<const float4 *>(work + (s * rows + row) * d)[c4];
+        acc.x += v.x * f;
+        acc.y += v.y * f;
+        acc.z += v.z * f;
+        acc.w += v.w * f;
+        lsum += st.y * f;
     }
-    o[t] = acc;
-    if (c == 0) { m[row] = mall; l[row] = lsum; }
+    reinterpret_cast<float4 *>(o)[t] = acc;
+    if (c4 == 0) { m[row] = mall; l[row] = lsum; }
 }
 
 }  // namespace
@@ -444,7 +496,7 @@ hipError_t launch_attn(const AttnGeom &ag, const uint8_t *packed, const float *q
     else attn_kernel<256, 2><<<grid, 64 * kAW, 0, stream>>>(ag, packed, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    const int64_t n = (int64_t)nh * nq * ag.d;
+    const int64_t n = (int64_t)nh * nq * ag.d / 4;
     attn_merge<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(
         a.nsplit, (int64_t)nh * nq, ag.d, work, o, m, l);
     return hipGetLastError();
