@@ -376,7 +376,6 @@ template <int FMT, int G>
 struct W8Stage {
     static constexpr int GPS = kW8SK / G;             // groups per stage (2 or 1)
     v4i a[2];                                         // two 16-byte activation units per thread
-    v4i b[4];                                         // int8: the lane's chunk of each MFMA block
     v2i w2[2];                                        // CQ2 / CQ3: the lane's 8 bytes of each
                                                       // chunk / crumb plane
     v2i bp;                                           // CQ1 / CQ3: the lane's 8 bytes of bits
@@ -384,8 +383,10 @@ struct W8Stage {
     float xs[GPS];                                    // per group: the scale of the lane's row
 };                                                    // (row r32 of tile `half`)
 
+// Three workgroups per CU (12 wavefronts) where the registers allow it: the int8 variant keeps
+// its 16-byte weight operands one stage ahead instead of two for that.
 template <int FMT, int G>
-__global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restrict__ packed,
+__global__ __launch_bounds__(256, 3) void gemm_w8_kernel(const uint8_t *__restrict__ packed,
                                                          const Geom geom, int m,
                                                          const int8_t *__restrict__ xq,
                                                          const float *__restrict__ xs,
@@ -453,12 +454,6 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
                 const int c = 2 * s + c2;
                 r.w2[c2] = ld64(rc, c < kc ? (c * 64 + prow) * 16 + 8 * half : kOOB);
             }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = s * (kW8SK / kW8Chunk) + 2 * j + half;
-                r.b[j] = ld128(rc, c < kc ? (c * 64 + prow) * 16 : kOOB);
-            }
         }
 #pragma unroll
         for (int q = 0; q < GPS; ++q) {
@@ -488,6 +483,16 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
     const v16i izero = {};
     v16i part[2] = {};
 
+    // int8: the lane's weight chunks of the next stage (loaded one stage ahead)
+    v4i wnext[4];
+    auto load_w = [&](int s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = s * (kW8SK / kW8Chunk) + 2 * j + half;
+            wnext[j] = ld128(rc, c < kc ? (c * 64 + prow) * 16 : kOOB);
+        }
+    };
+    if (FMT == kFmtInt8) load_w(0);
     W8Stage<FMT, G> ring[2];
     load_stage(0, ring[0]);
     if (nstage > 1) load_stage(1, ring[1]);
@@ -523,7 +528,8 @@ __global__ __launch_bounds__(256, 2) void gemm_w8_kernel(const uint8_t *__restri
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = ring[slot].b[j];
+            for (int j = 0; j < 4; ++j) b[j] = wnext[j];
+            if (s + 1 < nstage) load_w(s + 1);
         }
 #pragma unroll
         for (int q = 0; q < GPS; ++q) {
