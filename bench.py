@@ -75,7 +75,7 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     "C2a": dict(kernel="gemv", source_sha="f594f3a2a1de214d", fetch_kib=8767.26, write_kib=66.25,
                 fetch_factor=1.99979, write_factor=1.0),
-    "C3a": dict(kernel="gemm", source_sha="b8c12df0a1d95bfa", fetch_kib=53302.25, write_kib=17408.0,
+    "C3a": dict(kernel="gemm", source_sha="b8c12df0a1d95bfa", fetch_kib=53322.23, write_kib=17408.0,
                 fetch_factor=1.99979, write_factor=1.0),
 }
 
