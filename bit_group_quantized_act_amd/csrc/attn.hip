@@ -38,6 +38,7 @@ constexpr int kSlots = 64;      // slots per block
 constexpr int kQT = 32;         // queries per tile
 constexpr int kAW = 4;          // wavefronts per workgroup
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kMergeRegs = 8;  // split states the merge holds in registers at once
 
 // Position of slot jj (0..63) of a block in the MFMA order: subtile t = jj / 32, row r = jj % 32
 // sits in lane half h = (r / 4) % 2 at element e = 4 (r / 8) + r % 4.
@@ -438,19 +439,37 @@ __global__ __launch_bounds__(256) void attn_merge(int nsplit, int64_t rows, int 
     const int64_t row = t / q4;
     const int c4 = static_cast<int>(t % q4);
     const float2 *ml = reinterpret_cast<const float2 *>(work + nsplit * rows * d);
-    float mall = kNegInf;
-    for (int s = 0; s < nsplit; ++s) mall = fmaxf(mall, ml[s * rows + row].x);
+    auto part = [&](int s) { return reinterpret_cast<const float4 *>(work + (s * rows + row) * d)[c4]; };
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float lsum = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float2 st = ml[s * rows + row];
+    float mall = kNegInf, lsum = 0.0f;
+    auto add = [&](float2 st, float4 v) {
         const float f = (st.x == kNegInf) ? 0.0f : expf(st.x - mall);
-        const float4 v = reinterpret_cast<const float4 *>(work + (s * rows + row) * d)[c4];
         acc.x += v.x * f;
         acc.y += v.y * f;
         acc.z += v.z * f;
         acc.w += v.w * f;
         lsum += st.y * f;
+    };
+    if (nsplit <= kMergeRegs) {
+        // every split's state loaded at once (one memory round trip), then the same arithmetic
+        float2 st[kMergeRegs];
+        float4 v[kMergeRegs];
+#pragma unroll
+        for (int s = 0; s < kMergeRegs; ++s) {
+            if (s < nsplit) {
+                st[s] = ml[s * rows + row];
+                v[s] = part(s);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < kMergeRegs; ++s)
+            if (s < nsplit) mall = fmaxf(mall, st[s].x);
+#pragma unroll
+        for (int s = 0; s < kMergeRegs; ++s)
+            if (s < nsplit) add(st[s], v[s]);
+    } else {
+        for (int s = 0; s < nsplit; ++s) mall = fmaxf(mall, ml[s * rows + row].x);
+        for (int s = 0; s < nsplit; ++s) add(ml[s * rows + row], part(s));
     }
     reinterpret_cast<float4 *>(o)[t] = acc;
     if (c4 == 0) { m[row] = mall; l[row] = lsum; }
