@@ -80,6 +80,18 @@ TRAFFIC = {
 }
 
 
+def w8_gemv_workgroups(cfg):
+    """Workgroups of the one-row GEMV of the int8 and CQ1-CQ3 formats, as the library picks them:
+    8 wavefronts per 64-row panel, halved while a wavefront would get fewer than 4 groups (128-k
+    chunks for CQ1 / CQ3) and the grid keeps at least 1024 workgroups."""
+    units = -(-cfg.k // 128) if cfg.fmt in (5, 6) else cfg.k // cfg.group
+    panels = -(-cfg.n // 64)
+    wpp = 8
+    while wpp > 1 and units < 4 * wpp and -(-panels // (8 // (wpp // 2))) >= 1024:
+        wpp //= 2
+    return -(-panels // (8 // wpp))
+
+
 def kernel_source_sha(kernel):
     import hashlib
     h = hashlib.sha256()
@@ -250,8 +262,8 @@ def workload_name(cfg, glu=None, cap=None, a16=False):
     rot = ", 128-block WHT" if cfg.hadamard else ""
     if cfg.extra.get("row_scale"):
         rot += f", one scale per row seen as K/{cfg.group} groups"
-    fused = (cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072 and
-             cfg.fmt not in BYTE_DECODED)
+    fused = (cfg.m == 1 and cfg.k <= 16384 and
+             (w8_gemv_workgroups(cfg) <= 1024 if cfg.fmt in BYTE_DECODED else cfg.n <= 131072))
     if a16:
         return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
                 f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights x fp16 activations (prepass writing "
@@ -311,8 +323,8 @@ def main():
         lay, packed0 = w4a8.pack(t(layer["codes"]), t(layer["scales"]), cfg.fmt, cfg.group,
                                  bias=t(layer["bias"]), codebook=t(layer["codebook"]))
     wbytes = synth.weight_bytes(cfg)
-    fused = (cfg.m == 1 and cfg.k <= 16384 and cfg.n <= 131072     # w4a8_linear's one-kernel
-             and not byte_decoded)                                   # case (4-bit formats)
+    fused = (cfg.m == 1 and cfg.k <= 16384 and                    # w4a8_linear's one-kernel
+             (w8_gemv_workgroups(cfg) <= 1024 if byte_decoded else cfg.n <= 131072))   # case
     cap = args.argmax
     a16 = args.a16
     if (a16 or cap is not None or args.glu is not None) and byte_decoded:

@@ -358,6 +358,10 @@ w4a8_status w4a8_linear(const w4a8_layout *L, const void *packed, int32_t m, con
         L->n_pad / W4A8_PANEL_ROWS <= w4a8::kFusedMaxPanels)
         return launched(w4a8::launch_gemv_fused(g, pk, x, hadamard_block, xq, xs, xsum, y, st),
                         "fused gemv launch");
+    if (byte_decoded(L) && m == 1 && L->k <= w4a8::kFusedMaxK &&
+        w4a8::w8_gemv_workgroups(g) <= w4a8::kFusedMaxW8Workgroups)
+        return launched(w4a8::launch_w8_fused(g, pk, x, hadamard_block, xq, xs, xsum, y, st),
+                        "fused int8-weight gemv launch");
     hipError_t e = w4a8::launch_prep(x, m, L->k, L->group, hadamard_block, xq, xs, xsum, st);
     if (e != hipSuccess) return launched(e, "prep launch");
     if (byte_decoded(L))

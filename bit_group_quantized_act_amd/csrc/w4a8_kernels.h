@@ -243,6 +243,20 @@ hipError_t launch_pack_bits(const Geom &g, const uint8_t *codes, const int8_t *c
                             uint8_t *packed, hipStream_t stream);
 hipError_t launch_w8(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
                      const float *xs, float *y, hipStream_t stream);
+// Their one-row GEMV with the prepass fused in (k <= kFusedMaxK): every workgroup quantizes x
+// into LDS, workgroup 0 also writes xq, xs and xsum.  w8_gemv_workgroups is its grid size; past
+// kFusedMaxW8Workgroups the separate prepass costs less than the repeats (at 2048 workgroups of
+// a 262144-row head the fused int8 and 2-bit GEMVs measured 1-7% slower than prepass + GEMV).
+struct FusedIO {
+    const float *x;
+    int8_t *xq;
+    float *xs;
+    int32_t *xsum;
+};
+constexpr int kFusedMaxW8Workgroups = 1024;
+int w8_gemv_workgroups(const Geom &g);
+hipError_t launch_w8_fused(const Geom &g, const uint8_t *packed, const float *x, int hadamard,
+                           int8_t *xq, float *xs, int32_t *xsum, float *y, hipStream_t stream);
 
 // The reduction of nkeys panel keys into token and value (one workgroup).
 hipError_t launch_argmax_keys(const unsigned long long *keys, int nkeys, int32_t *token,

@@ -53,6 +53,50 @@ constexpr int kW8Waves = 8;
 constexpr int kBitChunk = 128;      // k per chunk of the bit-plane formats
 constexpr int kMinUnits = 4;        // GEMV: groups (chunks) per wavefront before panels share
 constexpr int kMinGrid = 1024;      // GEMV: fewest workgroups once panels share one
+constexpr int kFusedQuads = kFusedMaxK / 4 / (64 * kW8Waves);   // fused prepass: quads per thread
+
+// The prepass fused into a one-row GEMV: every workgroup quantizes the whole row into LDS
+// (workgroup 0 also writes xq, xs and xsum).  issue() loads the thread's quads and goes before
+// the kernel's weight loads, so run() waits for x only (loads complete in issue order).
+template <int G, bool ROT>
+struct FusedPrep {
+    v4i xr[kFusedQuads];
+    __device__ __forceinline__ void issue(const FusedIO &io, int k) {
+        const rsrc_t rx = make_rsrc(io.x, (uint64_t)k * 4);
+#pragma unroll
+        for (int i = 0; i < kFusedQuads; ++i) {
+            const int q = threadIdx.x + 64 * kW8Waves * i;
+            xr[i] = ld128(rx, q < k / 4 ? q * 16 : kOOB);
+        }
+    }
+    // A wavefront's quads are 64 consecutive ones, so a group's G/4 lanes and a rotation block's
+    // 32 are aligned runs that are all active or all inactive (k is a multiple of G and of 128).
+    __device__ __forceinline__ void run(const FusedIO &io, int k, int *lxq, float *lxs) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < kFusedQuads; ++i) {
+            const int q = threadIdx.x + 64 * kW8Waves * i;
+            if (q < k / 4) {
+                float scale;
+                int sum;
+                const v4f xf = __builtin_bit_cast(v4f, xr[i]);
+                const int codes = prep_quad<G, ROT>(make_float4(xf[0], xf[1], xf[2], xf[3]), lane,
+                                                    scale, sum);
+                lxq[q] = codes;
+                const bool leader = (q & (G / 4 - 1)) == 0;
+                if (leader) lxs[q / (G / 4)] = scale;
+                if (blockIdx.x == 0) {
+                    reinterpret_cast<int *>(io.xq)[q] = codes;
+                    if (leader) {
+                        io.xs[q / (G / 4)] = scale;
+                        io.xsum[q / (G / 4)] = sum;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+};
 
 template <int FMT>
 constexpr bool bit_plane = FMT == kFmtCQ1 || FMT == kFmtCQ3;
@@ -190,16 +234,23 @@ __device__ __forceinline__ int cq3_dword(uint32_t w, int s, uint32_t bw, int sh,
 
 // wpp: wavefronts per panel (1, 2, 4 or 8); a workgroup takes 8 / wpp consecutive panels, so a
 // short row still gives each wavefront several groups (or chunks) and each workgroup more bytes.
-template <int FMT, int G>
+// FUSED: the prepass runs in the kernel (x in io) and xq4 / xs are not read.
+template <int FMT, int G, bool FUSED, bool ROT>
 __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *__restrict__ packed,
                                                                 const Geom geom,
                                                                 const int *__restrict__ xq4,
                                                                 const float *__restrict__ xs,
-                                                                float *__restrict__ y, int wpp) {
+                                                                float *__restrict__ y, int wpp,
+                                                                const FusedIO io) {
     constexpr int CK = (FMT == kFmtCQ2) ? 64 : kW8Chunk;   // k per chunk
     constexpr int CPG = G / CK;                       // chunks per group
     constexpr int RING = (FMT == kFmtCQ2) ? 4 : 256 / G;   // groups in flight per wavefront
     __shared__ float red[kW8Waves][64];
+    __shared__ __attribute__((aligned(16))) int lxq[FUSED ? kFusedMaxK / 4 : 1];
+    __shared__ float lxs[FUSED ? kFusedMaxK / 64 : 1];
+    FusedPrep<G, ROT> fp;
+    if constexpr (FUSED) fp.issue(io, geom.k);
+    __builtin_amdgcn_sched_barrier(0);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wsub = wave & (wpp - 1);
@@ -225,13 +276,23 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *_
     };
 #pragma unroll
     for (int s = 0; s < RING; ++s) load(s, wsub + s * wpp);
+    const int *xsrc;                                  // the row's codes and scales: LDS when fused
+    const float *xssrc;
+    if constexpr (FUSED) {
+        fp.run(io, geom.k, lxq, lxs);
+        xsrc = lxq;
+        xssrc = lxs;
+    } else {
+        xsrc = xq4;
+        xssrc = xs;
+    }
     float acc = 0.0f;
     for (int g0 = wsub; g0 < ng; g0 += RING * wpp) {
 #pragma unroll
         for (int s = 0; s < RING; ++s) {
             const int g = g0 + s * wpp;
             if (g < ng) {
-                const int *xg = xq4 + g * (G / 4);       // the group's codes: wave-uniform
+                const int *xg = xsrc + g * (G / 4);      // the group's codes: wave-uniform
                 int d4[4] = {0, 0, 0, 0};
                 if (FMT == kFmtCQ2) {
                     constexpr int kq[4] = {0, 32, 16, 48};  // k offset of word position q
@@ -252,7 +313,7 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *_
                             d4[e] = __builtin_amdgcn_sdot4(ring[s][c][e], xg[4 * c + e], d4[e], false);
                 }
                 const int dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-                const float coef = xs[g] * half_bits_to_float(meta[s] & 0xFFFFu);
+                const float coef = xssrc[g] * half_bits_to_float(meta[s] & 0xFFFFu);
                 acc = fmaf(coef, static_cast<float>(dot), acc);
             }
             load(s, g + RING * wpp);
@@ -269,16 +330,22 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *_
 
 // One row against the bit-plane formats: a workgroup per panel, 8 wavefronts over the 128-k
 // chunks, lane r on panel row r; a chunk is P 16-byte loads per lane and holds 128 / G groups.
-template <int FMT, int G>
+template <int FMT, int G, bool FUSED, bool ROT>
 __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t *__restrict__ packed,
                                                                   const Geom geom,
                                                                   const int *__restrict__ xq4,
                                                                   const float *__restrict__ xs,
-                                                                  float *__restrict__ y, int wpp) {
+                                                                  float *__restrict__ y, int wpp,
+                                                                  const FusedIO io) {
     constexpr int P = planes<FMT>;
     constexpr int GPC = kBitChunk / G;                // groups per chunk (2 or 1)
     constexpr int RING = FMT == kFmtCQ3 ? 2 : 4;      // chunks in flight per wavefront
     __shared__ float red[kW8Waves][64];
+    __shared__ __attribute__((aligned(16))) int lxq[FUSED ? kFusedMaxK / 4 : 1];
+    __shared__ float lxs[FUSED ? kFusedMaxK / 64 : 1];
+    FusedPrep<G, ROT> fp;
+    if constexpr (FUSED) fp.issue(io, geom.k);
+    __builtin_amdgcn_sched_barrier(0);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wsub = wave & (wpp - 1);
@@ -313,6 +380,16 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
     };
 #pragma unroll
     for (int s = 0; s < RING; ++s) load(s, wsub + s * wpp);
+    const int *xsrc;                                  // the row's codes and scales: LDS when fused
+    const float *xssrc;
+    if constexpr (FUSED) {
+        fp.run(io, geom.k, lxq, lxs);
+        xsrc = lxq;
+        xssrc = lxs;
+    } else {
+        xsrc = xq4;
+        xssrc = xs;
+    }
     float acc = 0.0f;
     for (int c0 = wsub; c0 < kc; c0 += RING * wpp) {
 #pragma unroll
@@ -324,7 +401,7 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
                 for (int gi = 0; gi < 2; ++gi) {             // the chunk's two 64-k halves
                     const int g = (c * kBitChunk + 64 * gi) / G;
                     if (g >= ng) break;                      // (a ragged last chunk)
-                    const int *xg = xq4 + c * (kBitChunk / 4) + 16 * gi;   // wave-uniform
+                    const int *xg = xsrc + c * (kBitChunk / 4) + 16 * gi;  // wave-uniform
                     int d4[4] = {0, 0, 0, 0};
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
@@ -345,14 +422,14 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
                             }
                     const int dgi = (d4[0] + d4[1]) + (d4[2] + d4[3]);
                     if (GPC == 2) {
-                        const float coef = xs[g] * half_bits_to_float((meta[s] >> (16 * gi)) & 0xFFFFu);
+                        const float coef = xssrc[g] * half_bits_to_float((meta[s] >> (16 * gi)) & 0xFFFFu);
                         acc = fmaf(coef, static_cast<float>(dgi), acc);
                     } else {
                         dot += dgi;
                     }
                 }
                 if (GPC == 1) {
-                    const float coef = xs[c] * half_bits_to_float(meta[s] & 0xFFFFu);
+                    const float coef = xssrc[c] * half_bits_to_float(meta[s] & 0xFFFFu);
                     acc = fmaf(coef, static_cast<float>(dot), acc);
                 }
             }
@@ -594,34 +671,58 @@ hipError_t launch_pack_codes_w8(const Geom &g, const int8_t *w8, uint8_t *packed
 }
 
 namespace {
+// One-row GEMV shape: waves per panel, halved while a wavefront would get fewer than kMinUnits
+// groups (chunks) and the grid keeps at least kMinGrid workgroups (4 per CU).
+int gemv_wpp(const Geom &g, int *grid) {
+    const bool bits = g.fmt == kFmtCQ1 || g.fmt == kFmtCQ3;
+    const int units = bits ? (g.k + kBitChunk - 1) / kBitChunk : g.k / g.group;
+    const int panels = g.n_pad / kPanelRows;
+    int wpp = kW8Waves;
+    while (wpp > 1 && units < kMinUnits * wpp) {
+        const int ppw_next = kW8Waves / (wpp / 2);
+        if ((panels + ppw_next - 1) / ppw_next < kMinGrid) break;
+        wpp /= 2;
+    }
+    const int ppw = kW8Waves / wpp;
+    *grid = (panels + ppw - 1) / ppw;
+    return wpp;
+}
+
+template <int FMT, int G, bool FUSED, bool ROT>
+void gemv_go(const Geom &g, unsigned grid, int wpp, const uint8_t *packed, const int *x4,
+             const float *xs, float *y, const FusedIO &io, hipStream_t stream) {
+    if constexpr (bit_plane<FMT>)
+        gemv_bits_kernel<FMT, G, FUSED, ROT><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs,
+                                                                                y, wpp, io);
+    else
+        gemv_w8_kernel<FMT, G, FUSED, ROT><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y,
+                                                                              wpp, io);
+}
+
+template <int FMT, bool FUSED, bool ROT>
+void gemv_fmt(const Geom &g, const uint8_t *packed, const int *x4, const float *xs, float *y,
+              const FusedIO &io, hipStream_t stream) {
+    int grid;
+    const int wpp = gemv_wpp(g, &grid);
+    if (g.group == 64)
+        gemv_go<FMT, 64, FUSED, ROT>(g, static_cast<unsigned>(grid), wpp, packed, x4, xs, y, io, stream);
+    else
+        gemv_go<FMT, 128, FUSED, ROT>(g, static_cast<unsigned>(grid), wpp, packed, x4, xs, y, io, stream);
+}
+
+template <int FMT>
+void gemv_fused_fmt(const Geom &g, const uint8_t *packed, int hadamard, const FusedIO &io,
+                    float *y, hipStream_t stream) {
+    if (hadamard == 128) gemv_fmt<FMT, true, true>(g, packed, nullptr, nullptr, y, io, stream);
+    else gemv_fmt<FMT, true, false>(g, packed, nullptr, nullptr, y, io, stream);
+}
+
 template <int FMT>
 hipError_t launch_w8_fmt(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
                          const float *xs, float *y, hipStream_t stream) {
     if (m == 1) {
-        // waves per panel: halved while a wavefront would get fewer than kMinUnits groups
-        // (chunks) and the grid keeps at least kMinGrid workgroups (4 per CU)
-        const int units = bit_plane<FMT> ? (g.k + kBitChunk - 1) / kBitChunk : g.k / g.group;
-        const int panels = g.n_pad / kPanelRows;
-        int wpp = kW8Waves;
-        while (wpp > 1 && units < kMinUnits * wpp) {
-            const int ppw_next = kW8Waves / (wpp / 2);
-            if ((panels + ppw_next - 1) / ppw_next < kMinGrid) break;
-            wpp /= 2;
-        }
-        const int ppw = kW8Waves / wpp;
-        const unsigned grid = static_cast<unsigned>((panels + ppw - 1) / ppw);
-        const int *x4 = reinterpret_cast<const int *>(xq);
-        if constexpr (bit_plane<FMT>) {
-            if (g.group == 64)
-                gemv_bits_kernel<FMT, 64><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y, wpp);
-            else
-                gemv_bits_kernel<FMT, 128><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y, wpp);
-        } else {
-            if (g.group == 64)
-                gemv_w8_kernel<FMT, 64><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y, wpp);
-            else
-                gemv_w8_kernel<FMT, 128><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y, wpp);
-        }
+        gemv_fmt<FMT, false, false>(g, packed, reinterpret_cast<const int *>(xq), xs, y,
+                                    FusedIO{}, stream);
         return hipGetLastError();
     }
     const unsigned grid = static_cast<unsigned>(((m + 63) / 64) * ((g.n_pad + kW8BN - 1) / kW8BN));
@@ -638,6 +739,23 @@ hipError_t launch_w8(const Geom &g, const uint8_t *packed, int m, const int8_t *
     if (g.fmt == kFmtCQ1) return launch_w8_fmt<kFmtCQ1>(g, packed, m, xq, xs, y, stream);
     if (g.fmt == kFmtCQ3) return launch_w8_fmt<kFmtCQ3>(g, packed, m, xq, xs, y, stream);
     return launch_w8_fmt<kFmtInt8>(g, packed, m, xq, xs, y, stream);
+}
+
+int w8_gemv_workgroups(const Geom &g) {
+    int grid;
+    gemv_wpp(g, &grid);
+    return grid;
+}
+
+hipError_t launch_w8_fused(const Geom &g, const uint8_t *packed, const float *x, int hadamard,
+                           int8_t *xq, float *xs, int32_t *xsum, float *y, hipStream_t stream) {
+    if (g.k > kFusedMaxK) return hipErrorInvalidValue;
+    const FusedIO io{x, xq, xs, xsum};
+    if (g.fmt == kFmtCQ2) gemv_fused_fmt<kFmtCQ2>(g, packed, hadamard, io, y, stream);
+    else if (g.fmt == kFmtCQ1) gemv_fused_fmt<kFmtCQ1>(g, packed, hadamard, io, y, stream);
+    else if (g.fmt == kFmtCQ3) gemv_fused_fmt<kFmtCQ3>(g, packed, hadamard, io, y, stream);
+    else gemv_fused_fmt<kFmtInt8>(g, packed, hadamard, io, y, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack_cq2(const Geom &g, const uint8_t *codes, const int8_t *codebook,
