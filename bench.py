@@ -265,9 +265,12 @@ def workload_name(cfg, glu=None, cap=None, a16=False):
     fused = (cfg.m == 1 and cfg.k <= 16384 and
              (w8_gemv_workgroups(cfg) <= 1024 if cfg.fmt in BYTE_DECODED else cfg.n <= 131072))
     if a16:
+        one = cfg.m == 1 and cfg.k <= 16384 and -(-cfg.n // 64) <= 2048
         return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
-                f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights x fp16 activations (prepass writing "
-                f"X as half and its fp32 group sums + {'GEMV' if cfg.m == 1 else 'GEMM'} per step)")
+                f"{synth.FORMAT_NAMES[cfg.fmt]} 4-bit weights x fp16 activations ("
+                + ("prepass (X as half, fp32 group sums) fused into the GEMV" if one else
+                   f"prepass writing X as half and its fp32 group sums + "
+                   f"{'GEMV' if cfg.m == 1 else 'GEMM'}") + " per step)")
     how = ("prepass fused into the GEMV" if fused and cap is None else
            "prepass + GEMV" if cfg.m == 1 else "prepass + GEMM")
     gated = "" if glu is None else f", gated output {glu}(gate)*up with F={cfg.n // 2}"
@@ -341,9 +344,14 @@ def main():
             sys.exit(2)
         fused = False                                  # the tail runs in the two-kernel path
     alg_bytes = synth.algorithmic_bytes(cfg, fused_prep=fused)
+    # fp16 activations at one row (k <= 16384, at most 2048 panels): w4a8_linear_a16 is one
+    # kernel with the prepass fused in
+    fused_a16 = a16 and cfg.m == 1 and cfg.k <= 16384 and -(-cfg.n // 64) <= 2048
     if a16:          # weights + xh (2 bytes per input) + fp32 group sums + y, no xq / xs / xsum
         alg_bytes = synth.weight_bytes(cfg) + 2 * cfg.m * cfg.k + 4 * cfg.m * (cfg.k // 64) + \
             4 * cfg.m * cfg.n
+        if fused_a16:                                  # + the fp32 row read
+            alg_bytes += 4 * cfg.k
     if cap is not None:                                # keys written and read, token, logit
         alg_bytes += 2 * w4a8.argmax_work_bytes(cfg.n) + 8
     act = None
@@ -375,7 +383,9 @@ def main():
         # the dominant kernel alone: the fused prepass + GEMV at one row (the plain GEMV for a
         # vocabulary-sized row), the GEMM above
         pk = pool[i % pool_n]
-        if a16:
+        if fused_a16:
+            w4a8.linear_a16(lay, pk, x, out=y, prep_out=(xh16, xsf16))
+        elif a16:
             w4a8.gemm_a16(lay, pk, xh16, xsf16, out=y)
         elif cap is not None:
             w4a8.gemv_argmax(lay, pk, xq, xs, xsum, cap, out=(y[0], token, tval), work=work)

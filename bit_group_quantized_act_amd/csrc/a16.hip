@@ -111,15 +111,39 @@ __global__ __launch_bounds__(256) void prep_a16_kernel(const float4 *__restrict_
 
 constexpr int kA16Waves = 8;
 constexpr int kA16Ring = 4;                            // groups in flight per wavefront
+constexpr int kA16FusedIters = kFusedMaxK / 8 / (64 * kA16Waves);   // fused: octets per thread
 
-template <int FMT>
+// FUSED: the prepass runs in every workgroup (x is the fp32 row; xw / xsf are not read): the
+// row's halves in the interleaved order and its group sums go to LDS with the prepass's own
+// arithmetic, and workgroup 0 also writes them to xh_out / xsf_out.  The row's loads are issued
+// before the weight loads, so the prepass waits for x only (loads complete in issue order).
+template <int FMT, bool FUSED>
 __global__ __launch_bounds__(64 * kA16Waves) void gemv_a16_kernel(const uint8_t *__restrict__ packed,
                                                                   const Geom geom,
                                                                   const uint32_t *__restrict__ xw,
                                                                   const float *__restrict__ xsf,
-                                                                  float *__restrict__ y) {
+                                                                  float *__restrict__ y,
+                                                                  const float *__restrict__ x,
+                                                                  uint4 *__restrict__ xh_out,
+                                                                  float *__restrict__ xsf_out) {
+#pragma clang fp contract(off)
     constexpr int MB = (FMT == kFmtAffine) ? 4 : 2;
     __shared__ float red[kA16Waves][64];
+    __shared__ __attribute__((aligned(16))) uint32_t lxw[FUSED ? kFusedMaxK / 2 : 1];
+    __shared__ float lxsf[FUSED ? kFusedMaxK / kGroupA16 : 1];
+    __shared__ _Float16 tile[FUSED ? 64 * kA16Waves * 8 : 1];
+    const int noct = geom.k / 8;
+    float4 xr[FUSED ? 2 * kA16FusedIters : 1];
+    if constexpr (FUSED) {
+        const rsrc_t rx = make_rsrc(x, (uint64_t)geom.k * 4);
+#pragma unroll
+        for (int i = 0; i < kA16FusedIters; ++i) {
+            const int o = threadIdx.x + 64 * kA16Waves * i;
+            xr[2 * i] = __builtin_bit_cast(float4, ld128(rx, o < noct ? o * 32 : kOOB));
+            xr[2 * i + 1] = __builtin_bit_cast(float4, ld128(rx, o < noct ? o * 32 + 16 : kOOB));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int p = blockIdx.x;
@@ -145,13 +169,63 @@ __global__ __launch_bounds__(64 * kA16Waves) void gemv_a16_kernel(const uint8_t 
         ring[s][1] = ld128(rc, code_off(g, 1));
         meta[s] = (MB == 4) ? ld32(rm, meta_off(g)) : ld16(rm, meta_off(g));
     }
+    const uint32_t *xsrc;                             // the row's halves and sums: LDS when fused
+    const float *xsfsrc;
+    if constexpr (FUSED) {
+        // per octet as the prepass kernel: the left-to-right sum of 8, the tree over a group's 8
+        // octets (8 aligned lanes, all active or all inactive), the halves through a staging tile
+        // into the interleaved word order (a 32-wide block is 4 aligned lanes)
+#pragma unroll
+        for (int i = 0; i < kA16FusedIters; ++i) {
+            const int o = threadIdx.x + 64 * kA16Waves * i;
+            if (64 * kA16Waves * i >= noct) break;    // (uniform across the workgroup)
+            const bool live = o < noct;
+            const float4 a = xr[2 * i], b = xr[2 * i + 1];
+            const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            float c = v[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) c = c + v[e];
+            c = c + __shfl_xor(c, 1, 64);
+            c = c + __shfl_xor(c, 2, 64);
+            c = c + __shfl_xor(c, 4, 64);
+            if (live && (o & 7) == 0) {
+                lxsf[o / 8] = c;
+                if (blockIdx.x == 0) xsf_out[o / 8] = c;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tile[threadIdx.x * 8 + e] = static_cast<_Float16>(v[e]);
+            __syncthreads();
+            if (live) {
+                const int base = (threadIdx.x & ~3) * 8;
+                const int j = threadIdx.x & 3;
+                const int src[8] = {4 * j, 4 * j + 2, 16 + 4 * j, 18 + 4 * j,
+                                    4 * j + 1, 4 * j + 3, 17 + 4 * j, 19 + 4 * j};
+                uint32_t wd[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = __builtin_bit_cast(uint16_t, tile[base + src[2 * e]]);
+                    const uint32_t hi = __builtin_bit_cast(uint16_t, tile[base + src[2 * e + 1]]);
+                    wd[e] = lo | (hi << 16);
+                }
+                const uint4 q = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                reinterpret_cast<uint4 *>(lxw)[o] = q;
+                if (blockIdx.x == 0) xh_out[o] = q;
+            }
+            __syncthreads();
+        }
+        xsrc = lxw;
+        xsfsrc = lxsf;
+    } else {
+        xsrc = xw;
+        xsfsrc = xsf;
+    }
     float acc = 0.0f;
     for (int g0 = wave; g0 < ng; g0 += kA16Ring * kA16Waves) {
 #pragma unroll
         for (int s = 0; s < kA16Ring; ++s) {
             const int g = g0 + s * kA16Waves;
             if (g < ng) {
-                const uint32_t *xg = xw + 32 * g;        // the group's 64 halves: wave-uniform
+                const uint32_t *xg = xsrc + 32 * g;      // the group's 64 halves: wave-uniform
                 float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // one chain per code dword
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -170,7 +244,7 @@ __global__ __launch_bounds__(64 * kA16Waves) void gemv_a16_kernel(const uint8_t 
                 const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
                 const float sw = half_bits_to_float(meta[s] & 0xFFFFu);
                 acc = fmaf(sw, dot, acc);
-                if (FMT == kFmtAffine) acc = fmaf(half_bits_to_float(meta[s] >> 16), xsf[g], acc);
+                if (FMT == kFmtAffine) acc = fmaf(half_bits_to_float(meta[s] >> 16), xsfsrc[g], acc);
             }
             const int gn = g + kA16Ring * kA16Waves;
             ring[s][0] = ld128(rc, code_off(gn, 0));
@@ -368,9 +442,11 @@ hipError_t launch_linear_a16(const Geom &g, const uint8_t *packed, int m, const 
         const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
         const uint32_t *xw = reinterpret_cast<const uint32_t *>(xh);
         if (g.fmt == kFmtAffine)
-            gemv_a16_kernel<kFmtAffine><<<grid, 64 * kA16Waves, 0, stream>>>(packed, g, xw, xsf, y);
+            gemv_a16_kernel<kFmtAffine, false><<<grid, 64 * kA16Waves, 0, stream>>>(
+                packed, g, xw, xsf, y, nullptr, nullptr, nullptr);
         else
-            gemv_a16_kernel<kFmtSym><<<grid, 64 * kA16Waves, 0, stream>>>(packed, g, xw, xsf, y);
+            gemv_a16_kernel<kFmtSym, false><<<grid, 64 * kA16Waves, 0, stream>>>(
+                packed, g, xw, xsf, y, nullptr, nullptr, nullptr);
         return hipGetLastError();
     }
     const unsigned grid = static_cast<unsigned>(((m + 63) / 64) * ((g.n_pad + kA16BN - 1) / kA16BN));
@@ -378,6 +454,20 @@ hipError_t launch_linear_a16(const Geom &g, const uint8_t *packed, int m, const 
         gemm_a16_kernel<kFmtAffine><<<grid, 256, 0, stream>>>(packed, g, m, xh, xsf, y);
     else
         gemm_a16_kernel<kFmtSym><<<grid, 256, 0, stream>>>(packed, g, m, xh, xsf, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_a16_fused(const Geom &g, const uint8_t *packed, const float *x,
+                                   uint16_t *xh, float *xsf, float *y, hipStream_t stream) {
+    if (g.k > kFusedMaxK) return hipErrorInvalidValue;
+    const unsigned grid = static_cast<unsigned>(g.n_pad / kPanelRows);
+    uint4 *xh4 = reinterpret_cast<uint4 *>(xh);
+    if (g.fmt == kFmtAffine)
+        gemv_a16_kernel<kFmtAffine, true><<<grid, 64 * kA16Waves, 0, stream>>>(
+            packed, g, nullptr, nullptr, y, x, xh4, xsf);
+    else
+        gemv_a16_kernel<kFmtSym, true><<<grid, 64 * kA16Waves, 0, stream>>>(
+            packed, g, nullptr, nullptr, y, x, xh4, xsf);
     return hipGetLastError();
 }
 

@@ -536,6 +536,10 @@ w4a8_status w4a8_linear_a16(const w4a8_layout *L, const void *packed, int32_t m,
     if ((s = check_prep_a16(x, m, L->k, L->group, xh, xsf)) != W4A8_OK || m == 0) return s;
     if ((s = check_device()) != W4A8_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (m == 1 && L->k <= w4a8::kFusedMaxK && L->n_pad / W4A8_PANEL_ROWS <= w4a8::kFusedMaxPanels)
+        return launched(w4a8::launch_linear_a16_fused(geom_of(L), static_cast<const uint8_t *>(packed),
+                                                      x, xh, xsf, y, st),
+                        "fused fp16-activation gemv launch");
     hipError_t e = w4a8::launch_prep_a16(x, m, L->k, xh, xsf, st);
     if (e != hipSuccess) return launched(e, "fp16-activation prep launch");
     return launched(w4a8::launch_linear_a16(geom_of(L), static_cast<const uint8_t *>(packed), m,

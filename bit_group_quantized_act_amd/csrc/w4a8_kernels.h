@@ -218,6 +218,10 @@ hipError_t launch_prep_a16(const float *x, int64_t m, int k, uint16_t *xh, float
                            hipStream_t stream);
 hipError_t launch_linear_a16(const Geom &g, const uint8_t *packed, int m, const uint16_t *xh,
                              const float *xsf, float *y, hipStream_t stream);
+// The one-row fp16-activation linear with its prepass fused in (k <= kFusedMaxK): every
+// workgroup builds the row's halves and group sums in LDS, workgroup 0 also writes xh and xsf.
+hipError_t launch_linear_a16_fused(const Geom &g, const uint8_t *packed, const float *x,
+                                   uint16_t *xh, float *xsf, float *y, hipStream_t stream);
 
 // Prefill attention over a packed int8 key/value cache (the packed layout is described in
 // include/w4a8.h; offsets in bytes from the packed buffer).
