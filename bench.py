@@ -73,9 +73,9 @@ KERNEL_SOURCES = {
     "gemm": ["gemm.hip", "w4a8_kernels.h"],
 }
 TRAFFIC = {
-    "C2a": dict(kernel="gemv", source_sha="0e29fed115686f50", fetch_kib=8767.26, write_kib=66.25,
+    "C2a": dict(kernel="gemv", source_sha="b229ce4a0f0aee72", fetch_kib=8767.26, write_kib=66.25,
                 fetch_factor=1.99979, write_factor=1.0),
-    "C3a": dict(kernel="gemm", source_sha="e20826acd36f6dba", fetch_kib=53305.85, write_kib=17408.0,
+    "C3a": dict(kernel="gemm", source_sha="0b572a365962d46b", fetch_kib=53311.44, write_kib=17408.0,
                 fetch_factor=1.99979, write_factor=1.0),
 }
 
