@@ -75,7 +75,7 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     "C2a": dict(kernel="gemv", source_sha="b229ce4a0f0aee72", fetch_kib=8767.26, write_kib=66.25,
                 fetch_factor=1.99979, write_factor=1.0),
-    "C3a": dict(kernel="gemm", source_sha="0b572a365962d46b", fetch_kib=53311.44, write_kib=17408.0,
+    "C3a": dict(kernel="gemm", source_sha="0b572a365962d46b", fetch_kib=53337.35, write_kib=17408.0,
                 fetch_factor=1.99979, write_factor=1.0),
 }
 
