@@ -70,6 +70,7 @@ def test_w8_parity(name, over, fmt):
     ref = oracle_layer(L)
     assert np.array_equal(got["xq"], ref["xq"])
     assert np.array_equal(got["xs"].view(np.uint32), ref["xs"].view(np.uint32))
+    assert np.array_equal(got["xsum"], ref["xsum"])     # (written by the fused one-row kernel too)
     check_y(got["y"], ref["y"], ref["t"], f"w8 {name} {over}")
 
 
