@@ -65,6 +65,8 @@ def _oracle(L, cols=None):
 CASES = [
     ("C2a", dict(n=1000, k=2048)),
     ("C3a", dict(m=1, n=640, k=640)),
+    ("C2a", dict(n=128, k=16384)),          # the fused prepass's largest row: 4 passes
+    ("C3a", dict(m=1, n=100, k=8256)),      # 3 passes, the last one partly empty
     ("C1", dict(n=64, k=64)),
     ("C1", dict(n=320, k=1024, x_outliers=4)),
     ("C3a", dict(m=2, n=320, k=640)),

@@ -42,6 +42,8 @@ def _run(L):
 CASES = [
     ("C2a", dict(n=1000, k=2048)),
     ("C2a", dict(n=200, k=320)),
+    ("C2a", dict(n=200, k=16384)),          # the fused prepass's largest row: 8 passes
+    ("C4", dict(m=1, n=130, k=8320)),       # rotated, 5 passes, the last one partly empty
     ("C4", dict(m=1, n=320, k=1536)),
     ("C1", dict(n=64, k=64)),
     ("C3a", dict(m=65, n=1000, k=640)),
