@@ -420,7 +420,7 @@ __global__ __launch_bounds__(256) void attn_quant_q(const float4 *__restrict__ q
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         int c = 0;
-        if (amax > 0.0f) c = static_cast<int>(fminf(fmaxf(rintf(e[i] / scale), -127.0f), 127.0f));
+        if (scale > 0.0f) c = static_cast<int>(fminf(fmaxf(rintf(e[i] / scale), -127.0f), 127.0f));
         w |= (static_cast<uint32_t>(c) & 0xFFu) << (8 * i);
     }
     if (!live) return;

@@ -136,7 +136,9 @@ __device__ __forceinline__ int prep_quad(float4 v, int lane, float &scale, int &
     for (int s = 1; s < kLanesPerGroup; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 64));
     scale = amax / 127.0f;
     int q[4] = {0, 0, 0, 0};
-    if (amax > 0.0f) {
+    // Codes only where the scale is nonzero: amax / 127 also rounds to 0 for a group of tiny
+    // subnormals (amax <= 63 * 2^-149), and then every code is 0, as for amax == 0.
+    if (scale > 0.0f) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float r = rintf(e[i] / scale);

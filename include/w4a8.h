@@ -21,9 +21,12 @@
  * Definitions used by every entry point (x is fp32 [m][k]; weight group == activation group G):
  *   rotation    (optional) normalized Walsh-Hadamard transform of each 128-wide block of a row,
  *               fp32 butterflies with span 1, 2, ..., 64, then one multiply by fp32(1/sqrt(128))
- *   xs[g][r]    = amax / 127 (IEEE fp32 divide), amax = max |x| over group g of row r; 0 if
- *                 amax == 0 (stored group-major)
- *   xq[r][k]    = round-half-even(x / xs) (IEEE fp32 divide), in [-127, 127]; 0 if amax == 0
+ *   xs[g][r]    = amax / 127 (IEEE fp32 divide), amax = max |x| over group g of row r (stored
+ *                 group-major); it is 0 when amax == 0 and also when amax / 127 underflows to 0
+ *                 (a group of subnormals with amax <= 63 * 2^-149)
+ *   xq[r][k]    = round-half-even(x / xs) (IEEE fp32 divide) clamped to [-127, 127]; every code
+ *                 of a group is 0 when its xs == 0 (a subnormal xs has few significant bits, so
+ *                 x / xs can pass 127 and the clamp applies)
  *   xsum[g][r]  = sum of the group's xq (int32, group-major)
  *   D[r][n][g]  = sum over k in group g of xq[r][k] * w[n][k]        (exact int32)
  *                 w = q in [-8, 7] (SYM), u in [0, 15] (AFFINE), codebook[n][j] (CODEBOOK)
@@ -352,7 +355,8 @@ w4a8_status w4a8_gemm_a16(const w4a8_layout *L, const void *packed, int32_t m,
  * h / (nh / nkvh)); query i sits at position pos0 + i.
  * A slot at position p is seen by the query at t when p >= 0, p <= t, and window == 0 (a global
  * layer) or p < sink (attention sinks) or t - p < window.
- * Method: q8 = round-half-even(q / sq), sq = max|q row| / 127 (one scale per query row); keys to
+ * Method: q8 = round-half-even(q / sq) clamped to [-127, 127], sq = max|q row| / 127 (one scale
+ * per query row; q8 = 0 when sq == 0, as in the activation quantization); keys to
  * one flat scale per vector, sk = max_g ks[g], kq = round-half-even(k8 * fp32(ks[g] / sk));
  * logits S = scale * sq * sk * (q8 . kq); over blocks of 64 slots in slot order, an online
  * softmax m' = max(m, block max), alpha = e^(m - m'), P = e^(S - m'), l = alpha * l + sum P;

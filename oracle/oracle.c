@@ -19,8 +19,9 @@
  *              the per-group SMOPA leaf contract (per-group int8 activations, one activation
  *              scale per group).  Reading: per row and group, amax = max|x| (exact),
  *              xs = amax / 127 as an IEEE fp32 divide, xq = round-half-even(x / xs) as an IEEE
- *              fp32 divide then rint, so codes lie in [-127, 127]; amax == 0 gives xs = 0 and
- *              xq = 0.
+ *              fp32 divide then rint, clamped to [-127, 127]; a group whose scale is 0 (amax == 0,
+ *              or amax / 127 underflows to 0 for a group of tiny subnormals) has xs = 0 and
+ *              every code 0.
  *   group sums "TensorFold PR #3215, simd_qmm on Metal: X's group sums and half operands from a
  *              prepass", section "What this changes": the prepass writes each row's per-group
  *              sums once, for the affine bias term.  Reading: the int32 sum of the int8 codes of
@@ -176,7 +177,10 @@ int oracle_rotate(float *x, int64_t m, int64_t k, int32_t block)
 /*
  * Per row r and group g of `group` consecutive k:
  *   amax = max |x|;  xs = amax / 127 (fp32 divide);  xq = rint(x / xs) (fp32 divide, ties to even)
- *   xsum = sum of the group's codes (int32).
+ *   clamped to [-127, 127];  xsum = sum of the group's codes (int32).
+ *   The codes are taken only where xs > 0: when amax / 127 rounds to 0 (amax == 0, or amax at
+ *   most 63 * 2^-149) the group is all zero codes with xs = 0.  When xs is itself subnormal it
+ *   carries fewer significant bits, x / xs can exceed 127 and the clamp does apply.
  */
 int oracle_quantize(const float *x, int64_t m, int64_t k, int32_t group,
                     int8_t *xq, float *xs, int32_t *xsum)
@@ -198,10 +202,10 @@ int oracle_quantize(const float *x, int64_t m, int64_t k, int32_t group,
             int32_t sum = 0;
             for (int i = 0; i < group; ++i) {
                 int32_t q = 0;
-                if (amax > 0.0f) {
+                if (scale > 0.0f) {
                     float t = xg[i] / scale;
                     float rq = rintf(t);          /* round to nearest, ties to even */
-                    if (rq > 127.0f) rq = 127.0f;   /* unreachable: |x| <= amax          */
+                    if (rq > 127.0f) rq = 127.0f;   /* reached only with a subnormal scale */
                     if (rq < -127.0f) rq = -127.0f;
                     q = (int32_t)rq;
                 }

@@ -110,6 +110,53 @@ def test_attn_empty_slots_and_rerun_same_bits():
     assert np.array_equal(got["o"].view(np.uint32), again["o"].view(np.uint32))
 
 
+def test_attn_p_value_scale_fold_golden_on_gpu():
+    """The hand-derived case of tests/golden/attn_p_value_scale_fold.txt through the kernel:
+    the value group's scale folded into P before its 8-bit quantization."""
+    import os
+    want = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden",
+                           "attn_p_value_scale_fold.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                key, val = line.split()
+                want[key] = float(val)
+    w = _w4a8()
+    k8 = np.zeros((1, 2, 64), np.int8)
+    ks = np.ones((1, 2, 2), np.float32)
+    v8 = np.empty((1, 2, 64), np.int8)
+    v8[0, 0], v8[0, 1] = 51, -102
+    vs = np.array([[[1.0, 0.25], [0.25, 1.0]]], np.float32)
+    AL, packed = w.attn_pack_kv(to_dev(k8), to_dev(ks), to_dev(v8), to_dev(vs),
+                                to_dev(np.array([0, 1], np.int32)))
+    o, m, l, q8, sq = w.attn_prefill(AL, packed, to_dev(np.zeros((1, 1, 64), np.float32)), 5,
+                                     0, 0, 0.125)
+    torch.cuda.synchronize()
+    o, m, l = o.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()
+    assert m[0, 0] == want["m"] and l[0, 0] == want["l"]
+    np.testing.assert_allclose(o[0, 0, :32], want["o_group0"], rtol=1e-6)
+    np.testing.assert_allclose(o[0, 0, 32:], want["o_group1"], rtol=1e-6)
+
+
+def test_attn_subnormal_query_rows():
+    """Query rows of subnormals: a scale that underflows to 0 (all codes 0: uniform attention
+    over the visible slots) and a subnormal scale 2^-149 whose largest code clamps at 127."""
+    A = synth.make_attn("A1", nh=2, nkvh=1, nq=32, nkv=128, d=128)
+    q = A["q"].copy()
+    tiny = np.float32(2.0 ** -149)
+    q[0, 3, :] = 0.0
+    q[0, 3, :4] = [np.float32(j) * tiny for j in (5, -3, 2, 1)]        # scale -> 0
+    q[1, 7, :] = 0.0
+    q[1, 7, :3] = [np.float32(j) * tiny for j in (190, -95, 1)]        # scale 2^-149, clamp
+    A = dict(A, q=q)
+    got = _run(A)
+    ref = _oracle(A)
+    assert ref["sq"][0, 3] == 0 and not ref["q8"][0, 3].any()
+    assert ref["sq"][1, 7].view(np.uint32) == 1 and ref["q8"][1, 7, 0] == 127
+    check_attn(got, ref, "subnormal query rows")
+
+
 @pytest.mark.parametrize("name", ["A1", "A2"])
 def test_attn_full_size(name):
     """The Gemma-style layer: 8 query heads on 2 key/value heads, head_dim 256, 256 queries

@@ -202,6 +202,43 @@ def test_flipped_nibble_moves_one_column():
     assert diff.tolist() == [77]
 
 
+def _subnormal_groups(rows, k):
+    """Rows whose 64-wide groups hold the subnormal golden cases (multiples j of 2^-149 whose
+    scale rounds to 0, to 2^-149 with a clamped code, or to 3 * 2^-149), cycled over the
+    groups; the rest of each group is zero."""
+    cases = [[5, -3], [63, -63, 1], [64, -1, 6], [190, -95, 1], [381, -7, 3, 1, 2, -5]]
+    x = np.zeros((rows, k), np.float32)
+    tiny = np.float32(2.0 ** -149)
+    for r in range(rows):
+        for g in range(k // 64):
+            vals = cases[(r * (k // 64) + g) % len(cases)]
+            x[r, 64 * g:64 * g + len(vals)] = [np.float32(j) * tiny for j in vals]
+    return x
+
+
+def test_subnormal_groups_through_the_fused_gemv():
+    """One decode row whose groups are subnormal golden cases, through the fused prepass + GEMV
+    (with and without rotation) and through prepass + GEMV: codes, scales and sums bit-exact."""
+    for name, over in (("C1", dict(n=192, k=640)), ("C4", dict(m=1, n=130, k=768))):
+        L = synth.make(name, full_range=True, **over)
+        cfg = L["cfg"]
+        x = L["x"].copy()
+        x[:, :320] = _subnormal_groups(1, 320)        # five subnormal groups, the rest normal
+        L = dict(L, x=x)
+        print(f"subnormal linear {name} {over} had={cfg.hadamard}", flush=True)
+        got = _run_linear(L)
+        ref = oracle_layer(L)
+        if cfg.hadamard == 0:
+            assert (ref["xs"][0, :5] == 0).sum() == 2 and (ref["xs"][0, :5] > 0).sum() == 3
+            assert np.abs(ref["xq"][0, :320]).max() == 127
+        assert np.array_equal(got["xq"], ref["xq"]), "xq differs"
+        assert np.array_equal(_bits(got["xs"]), _bits(ref["xs"])), "xs differs"
+        assert np.array_equal(got["xsum"], ref["xsum"]), "xsum differs"
+        check_y(got["y"], ref["y"], ref["t"], f"subnormal linear {name}")
+        split = _run(L, with_partials=False)
+        assert np.array_equal(_bits(got["y"]), _bits(split["y"])), "linear and prep+matmul differ"
+
+
 def test_prep_edge_cases():
     w = _w4a8()
     rng = np.random.default_rng(7)
@@ -213,6 +250,9 @@ def test_prep_edge_cases():
     x[2, 65:70] = [0.5, 1.5, 2.5, -0.5, -2.5]          # ties round to even
     x[3, :] = rng.standard_normal(256).astype(np.float32) * np.float32(1e-30)   # tiny values
     x[4, :] = rng.standard_normal(256).astype(np.float32) * np.float32(1e30)    # huge values
+    # subnormal groups: scales that underflow to 0 (codes 0) and subnormal scales whose codes
+    # clamp at 127 (the golden cases of the oracle's pins, one per 64-wide group)
+    x = np.concatenate([x, _subnormal_groups(2, 256)])
     for group, had in ((64, 0), (128, 0), (64, 128), (128, 128)):
         xq, xs, xsum = w.prep(to_dev(x), group, had)
         torch.cuda.synchronize()

@@ -152,6 +152,60 @@ def test_quant_zero_groups():
     assert np.abs(xq[1, 64:128]).max() == 127
 
 
+def _load_subnormal_golden():
+    cases = []
+    with open(os.path.join(GOLDEN, "quant_subnormal_scale.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            fields = line.split()
+            assert fields[0] == "case"
+            pairs = [tuple(int(v) for v in p.split(":")) for p in fields[4:]]
+            cases.append((int(fields[2], 16), int(fields[3]), pairs))
+    return cases
+
+
+def _subnormal_rows(cases):
+    """One 64-wide group per golden case: the listed multiples of 2^-149, then zeros."""
+    x = np.zeros((len(cases), 64), np.float32)
+    for r, (_, _, pairs) in enumerate(cases):
+        x[r, :len(pairs)] = [np.float32(j) * np.float32(2.0 ** -149) for j, _ in pairs]
+    return x
+
+
+def test_quant_subnormal_scale_golden():
+    """Scales that underflow to zero give all-zero codes; subnormal scales clamp at 127."""
+    cases = _load_subnormal_golden()
+    x = _subnormal_rows(cases)
+    # the inputs really are the listed subnormal multiples
+    assert np.array_equal((x.astype(np.float64) * 2.0 ** 149)[:, :6].round(),
+                          (x.astype(np.float64) * 2.0 ** 149)[:, :6])
+    xq, xs, xsum = oracle.quantize(x, 64)
+    for r, (bits, total, pairs) in enumerate(cases):
+        assert int(xs[r, 0].view(np.uint32)) == bits, r
+        assert list(xq[r, :len(pairs)]) == [c for _, c in pairs], r
+        assert np.all(xq[r, len(pairs):] == 0), r
+        assert xsum[r, 0] == total, r
+
+
+def test_control_amax_test_breaks_subnormal_golden():
+    """The reading that takes codes whenever amax > 0 divides by a zero scale on the first two
+    cases; with the usual NaN-ignoring clamp (fmax then fmin) the zeros become -127 and the
+    golden fails."""
+    cases = _load_subnormal_golden()
+    x = _subnormal_rows(cases)
+    amax = np.abs(x).max(axis=1, keepdims=True)
+    scale = correctly_rounded_div(amax, np.float32(127))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint(x / scale)
+    planted = np.fmin(np.fmax(q, np.float32(-127)), np.float32(127))
+    planted = np.where(amax > 0, planted, 0).astype(np.int64)
+    xq, _, _ = oracle.quantize(x, 64)
+    assert not np.array_equal(planted, xq.astype(np.int64))
+    assert not np.array_equal(planted[:2], np.zeros_like(planted[:2]))
+
+
 def _adversarial_rows(seed=4):
     """Rows with outliers and values placed so that x/xs lands within an ulp of k + 0.5."""
     r = np.random.default_rng(seed)
@@ -722,6 +776,53 @@ def test_attn_requant_k_golden():
     assert list(kq[0, 0:4]) == [9, -9, 127, -127]                   # ratio 1: unchanged
     kq2, sk2 = oracle.attn_requant_k(np.full((1, 32), 5, np.int8), np.zeros((1, 1), np.float32))
     assert sk2[0] == 0 and not kq2.any()
+
+
+def _p_fold_golden_inputs():
+    k8 = np.zeros((1, 2, 64), np.int8)
+    ks = np.ones((1, 2, 2), np.float32)
+    v8 = np.empty((1, 2, 64), np.int8)
+    v8[0, 0], v8[0, 1] = 51, -102
+    vs = np.array([[[1.0, 0.25], [0.25, 1.0]]], np.float32)
+    return np.zeros((1, 1, 64), np.float32), k8, ks, v8, vs, np.array([0, 1], np.int32)
+
+
+def _load_p_fold_golden():
+    want = {}
+    with open(os.path.join(GOLDEN, "attn_p_value_scale_fold.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                key, val = line.split()
+                want[key] = float(val)
+    return want
+
+
+def test_attn_p_value_scale_fold_golden():
+    """The value group's scale enters P before its 8-bit quantization (hand-derived values)."""
+    want = _load_p_fold_golden()
+    q, k8, ks, v8, vs, kvpos = _p_fold_golden_inputs()
+    q8, sq = oracle.attn_quant_q(q)
+    assert sq[0, 0] == 0 and not q8.any()
+    kq, sk = oracle.attn_requant_k(k8, ks)
+    o, m, l = oracle.attn_int8(q8, sq, kq, sk, v8, vs, kvpos, 5, 0, 0, 0.125)
+    assert m[0, 0] == want["m"] and l[0, 0] == want["l"]
+    np.testing.assert_allclose(o[0, 0, :32], want["o_group0"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o[0, 0, 32:], want["o_group1"], rtol=0, atol=1e-12)
+
+
+def test_control_p_quantized_before_value_scales_breaks_fold_golden():
+    """Planted reading: P quantized once per block (sp = max P / 255) and the value scales
+    applied to the product afterwards.  It misses the golden values."""
+    want = _load_p_fold_golden()
+    _, _, _, v8, vs, _ = _p_fold_golden_inputs()
+    p = np.ones(2)                                   # zero logits
+    sp = p.max() / 255.0
+    u = np.rint(p / sp)
+    planted = [sp * sum(u[j] * vs[0, j, g] * float(v8[0, j, 0]) for j in range(2))
+               for g in range(2)]
+    assert abs(planted[0] - want["o_group0"]) > 0.05
+    assert abs(planted[1] - want["o_group1"]) > 0.02
 
 
 def _method(A, window=None, sink=None):
