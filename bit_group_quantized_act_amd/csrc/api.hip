@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 namespace {
 
@@ -420,12 +421,16 @@ w4a8_status w4a8_linear_glu(const w4a8_layout *L, const void *packed, int32_t m,
     return launched(w4a8::launch_gemm_glu(g, act, pk, m, xq, xs, xsum, y, st), "gated gemm launch");
 }
 
-w4a8_status w4a8_lm_head_argmax(const w4a8_layout *L, const void *packed, const float *x,
-                                int32_t hadamard_block, float softcap, int8_t *xq, float *xs,
-                                int32_t *xsum, float *logits, int32_t *token, float *value,
-                                void *work, uint64_t work_bytes, void *stream) {
-    w4a8_status s = check_layout(L);
-    if (s != W4A8_OK) return s;
+}  // extern "C"
+
+namespace {
+// Validation and launches of the one-row greedy tail on a given key buffer (the caller's work
+// buffer, or the library's own static one for w4a8_lm_head_argmax_noalloc).
+w4a8_status lm_head_argmax_checked(const w4a8_layout *L, const void *packed, const float *x,
+                                   int32_t hadamard_block, float softcap, int8_t *xq, float *xs,
+                                   int32_t *xsum, float *logits, int32_t *token, float *value,
+                                   void *work, uint64_t work_bytes, void *stream) {
+    w4a8_status s;
     if ((s = reject_int8(L, "the greedy tail")) != W4A8_OK) return s;
     if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
     if (!aligned(packed, 256)) return fail(W4A8_ERR_ARG, "packed is not 256-byte aligned");
@@ -445,6 +450,71 @@ w4a8_status w4a8_lm_head_argmax(const w4a8_layout *L, const void *packed, const 
     return launched(w4a8::launch_gemv_argmax(geom_of(L), static_cast<const uint8_t *>(packed), xq,
                                              xs, xsum, logits, tail, st),
                     "greedy tail gemv launch");
+}
+
+// ---- the key buffer of w4a8_lm_head_argmax_noalloc
+//
+// One 64-bit key per 64-row panel of the largest head the entry point takes.  Every GPU the
+// library runs on holds its own copy until the process ends.  Host code never uses the array's
+// name as an address (on the host it is only a stand-in for the symbol): the device address is
+// looked up once per device with hipGetSymbolAddress, with that device current, and kept.
+constexpr uint64_t kNoAllocKeyBytes = W4A8_ARGMAX_WORK_BYTES(W4A8_NOALLOC_MAX_N);
+static __device__ __align__(256) unsigned long long scratch[kNoAllocKeyBytes / 8];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device (nullptr: not yet)
+
+w4a8_status scratch_of_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(W4A8_ERR_DEVICE, "hipGetDevice failed");
+    }
+    if (dev >= kMaxDevices) return fail(W4A8_ERR_DEVICE, "device index %d is too large", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return fail(W4A8_ERR_HIP, "hipGetSymbolAddress of the key buffer on device %d: %s",
+                        dev, hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return W4A8_OK;
+}
+}  // namespace
+
+extern "C" {
+
+w4a8_status w4a8_lm_head_argmax(const w4a8_layout *L, const void *packed, const float *x,
+                                int32_t hadamard_block, float softcap, int8_t *xq, float *xs,
+                                int32_t *xsum, float *logits, int32_t *token, float *value,
+                                void *work, uint64_t work_bytes, void *stream) {
+    w4a8_status s = check_layout(L);
+    if (s != W4A8_OK) return s;
+    return lm_head_argmax_checked(L, packed, x, hadamard_block, softcap, xq, xs, xsum, logits,
+                                  token, value, work, work_bytes, stream);
+}
+
+w4a8_status w4a8_lm_head_argmax_noalloc(const w4a8_layout *L, const void *packed,
+                                        const float *x, int32_t hadamard_block, float softcap,
+                                        int8_t *xq, float *xs, int32_t *xsum, float *logits,
+                                        int32_t *token, float *value, void *stream) {
+    w4a8_status s = check_layout(L);
+    if (s != W4A8_OK) return s;
+    if (L->n > W4A8_NOALLOC_MAX_N)
+        return fail(W4A8_ERR_UNSUPPORTED,
+                    "n = %d is above W4A8_NOALLOC_MAX_N = %d, the size of the library's own key "
+                    "buffer (w4a8_lm_head_argmax takes a work buffer of any size)",
+                    L->n, W4A8_NOALLOC_MAX_N);
+    if ((s = check_device()) != W4A8_OK) return s;
+    void *keys = nullptr;
+    if ((s = scratch_of_current_device(&keys)) != W4A8_OK) return s;
+    return lm_head_argmax_checked(L, packed, x, hadamard_block, softcap, xq, xs, xsum, logits,
+                                  token, value, keys, kNoAllocKeyBytes, stream);
 }
 
 w4a8_status w4a8_gemv_argmax(const w4a8_layout *L, const void *packed, const int8_t *xq,

@@ -26,6 +26,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "no gfx950 device
 EXPORTS = ("w4a8_packed_layout", "w4a8_pack_weights", "w4a8_pack_weights_row_scale",
            "w4a8_prep", "w4a8_gemv", "w4a8_gemm",
            "w4a8_linear", "w4a8_linear_glu", "w4a8_gemm_glu", "w4a8_lm_head_argmax",
+           "w4a8_lm_head_argmax_noalloc",
            "w4a8_gemv_argmax", "w4a8_prep_a16", "w4a8_linear_a16", "w4a8_gemm_a16",
            "w4a8_attn_layout_init", "w4a8_attn_pack_kv", "w4a8_attn_work_bytes",
            "w4a8_attn_prefill", "w4a8_debug_partials", "w4a8_status_string", "w4a8_last_error")
@@ -78,6 +79,8 @@ def load() -> ctypes.CDLL:
     u64 = ctypes.c_uint64
     lib.w4a8_lm_head_argmax.argtypes = [LP, P, P, i32, ctypes.c_float, P, P, P, P, P, P, P, u64,
                                         P]
+    lib.w4a8_lm_head_argmax_noalloc.argtypes = [LP, P, P, i32, ctypes.c_float, P, P, P, P, P,
+                                                P, P]
     lib.w4a8_gemv_argmax.argtypes = [LP, P, P, P, P, ctypes.c_float, P, P, P, P, u64, P]
     lib.w4a8_prep_a16.argtypes = [P, i32, i32, i32, P, P, P]
     lib.w4a8_linear_a16.argtypes = [LP, P, i32, P, P, P, P, P]
@@ -315,6 +318,29 @@ def argmax_work(L: Layout, device) -> torch.Tensor:
 
 def _work_bytes(work: torch.Tensor) -> int:
     return work.numel() * work.element_size()
+
+
+NOALLOC_MAX_N = 1 << 20     # W4A8_NOALLOC_MAX_N
+
+
+def lm_head_argmax_noalloc(L: Layout, packed: torch.Tensor, x: torch.Tensor, out,
+                           prep_out, softcap: float = 0.0, hadamard_block: int = 0):
+    """w4a8_lm_head_argmax_noalloc: the greedy tail with the library's own key buffer.  Every
+    buffer is the caller's: out = (logits [n], token int32 [1], value fp32 [1]), prep_out =
+    (xq [1, k], xs [k/group, 1], xsum [k/group, 1]); nothing is allocated here or in the
+    library.  Returns out."""
+    x1 = x.reshape(-1)
+    _dev(x1, torch.float32, "x")
+    if x1.numel() != L.k:
+        raise ValueError(f"x has {x1.numel()} values, the layout k = {L.k}")
+    xq, xs, xsum = prep_out
+    logits, token, value = out
+    _check(load().w4a8_lm_head_argmax_noalloc(ctypes.byref(L), _ptr(packed), _ptr(x1),
+                                              hadamard_block, float(softcap), _ptr(xq), _ptr(xs),
+                                              _ptr(xsum), _ptr(logits), _ptr(token), _ptr(value),
+                                              _stream(x.device)),
+           "w4a8_lm_head_argmax_noalloc")
+    return out
 
 
 def lm_head_argmax(L: Layout, packed: torch.Tensor, x: torch.Tensor, softcap: float = 0.0,

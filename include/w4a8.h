@@ -302,6 +302,26 @@ w4a8_status w4a8_lm_head_argmax(const w4a8_layout *L, const void *packed, const 
                                 void *work, uint64_t work_bytes, void *stream);
 
 /*
+ * w4a8_lm_head_argmax for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same validation, the same
+ * three kernels and the same results, with the panel keys in a buffer the library holds on each
+ * GPU it runs on (W4A8_ARGMAX_WORK_BYTES(W4A8_NOALLOC_MAX_N) = 128 KiB, kept until the process
+ * ends) instead of a caller's work buffer.  Nothing is allocated or freed: the buffer is a static
+ * device array whose address is looked up once per device, on the first call there.
+ *   every argument  as for w4a8_lm_head_argmax (there is no work buffer)
+ * The keys need no initial contents.  Every call on one GPU shares that GPU's key buffer: calls
+ * that overlap on one GPU (concurrent streams, or threads) race and may return a wrong token.
+ * W4A8_ERR_UNSUPPORTED: L->n > W4A8_NOALLOC_MAX_N.  W4A8_ERR_HIP: the buffer's address lookup
+ * failed.  Other errors as w4a8_lm_head_argmax.
+ */
+#define W4A8_NOALLOC_MAX_N (1 << 20)
+
+w4a8_status w4a8_lm_head_argmax_noalloc(const w4a8_layout *L, const void *packed,
+                                        const float *x, int32_t hadamard_block, float softcap,
+                                        int8_t *xq, float *xs, int32_t *xsum, float *logits,
+                                        int32_t *token, float *value, void *stream);
+
+/*
  * The GEMV and greedy tail of w4a8_lm_head_argmax on activations already quantized by w4a8_prep
  * (m = 1): the same two kernels, so the same logits, token and value.
  * Errors as w4a8_gemv and w4a8_lm_head_argmax.
