@@ -2,11 +2,15 @@
 """Benchmark of the W4A8 linear layer on one MI355X; prints one JSON line.
 
 A step is one pass of the per-token hot path over one batch of synthetic input through
-w4a8_linear: the activation prepass and the linear (one fused kernel at one row, where every
-GEMV workgroup quantizes the row itself; the prepass kernel then the GEMM above).  The default workload
-is the decode GEMV of a gate_up-shaped layer: M=1, K=2048, N=16384, symmetric 4-bit weights in
-64-groups with fp16 scales, X ~ N(0,1) with 8 outlier channels x20.  The weights are packed once
-(load time, not in a step).
+w4a8_linear: the activation prepass and the linear (one fused kernel at one row when the head is
+small enough, where every GEMV workgroup quantizes the row itself; the prepass kernel then the
+GEMV or GEMM otherwise).  The default workload is the largest one-row configuration, the decode
+GEMV of a vocabulary head: M=1, K=1536, N=262144, symmetric 4-bit weights in 64-groups with fp16
+scales (215 MB per step), X ~ N(0,1) with 15 outlier channels x15.  The same line carries a
+`secondary` record for the prefill GEMM half of the metric, timed in the same process: by
+default the 128-row gate|up prompt tile M=128, K=5120, N=34816 with affine 4-bit weights, priced
+in int8 TOPS against the dense int8 MFMA peak.  The weights are packed once (load time, not in a
+step).
 
 Timing.  Weights are replicated into a pool of distinct packed buffers totalling >= 512 MiB (twice
 the 256 MiB last-level cache) and the steps walk through the pool, so every step streams its
@@ -20,8 +24,19 @@ value      = weight bytes (nibbles + scales [+ bias] [+ codebook]) per step / st
 roofline   = algorithmic bytes of one launch of the dominant kernel (weights + xq + xs + xsum + y,
              plus the fp32 row when the prepass is fused in) / its average duration, against
              the 8 TB/s HBM peak (or int8 ops against the 5.0 POP/s dense MFMA peak for a GEMM
-             whose MFMA floor is above its HBM floor)
-cpu_baseline = the CPU oracle (plain C, OpenMP) on the same workload, repeated for about 10 s
+             whose MFMA floor is above its HBM floor).  The duration is the median over
+             --batches batches (default 7) that alternate between the line's kernels (and the
+             HBM read probe), each batch a graph of --steps launches between two HIP events on
+             the launching stream; the best batch is reported beside it.
+             pct_hbm_probe (one-row workloads): the kernel's byte rate over that of a plain read
+             of the same packed buffers (libw4a8_probe.so, 16-byte loads), the achievable rate.
+             pct_valu_ceiling (GEMMs): the time the VALU needs for the epilogue alone (an int32
+             convert and one FMA per output element and group, 2*M*N*K/G lane operations at
+             39.3 T lane-ops/s: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz) over the kernel's time.
+             pct_roofline (GEMMs): achieved TOPS over min(peak, arithmetic intensity x 8 TB/s).
+sclk_mhz   = the shader clock the driver reports during the run, where it can be read
+cpu_baseline = the CPU oracle (plain C, OpenMP) on the primary workload (a column sample of it
+             when large), repeated for about 10 s
 
 --glu ACT times the gated variant instead (w4a8_linear_glu): the config's weights read as a
 [gate; up] pair (n = 2F), and the output is act(gate) * up, fp32 [m][F].
@@ -60,6 +75,7 @@ HBM_PEAK_GBPS = 8000.0
 # weight formats 3-6 (int8, and the 2-, 1- and 3-bit codebooks) have their own GEMV / GEMM
 BYTE_DECODED = (3, 4, 5, 6)
 INT8_PEAK_TOPS = 5000.0
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9          # fp32 lane operations per second, no packed math
 F16_PEAK_TFLOPS = 2500.0
 POOL_BYTES = 512 << 20
 
@@ -73,10 +89,10 @@ KERNEL_SOURCES = {
     "gemm": ["gemm.hip", "w4a8_kernels.h"],
 }
 TRAFFIC = {
-    "C2a": dict(kernel="gemv", source_sha="b229ce4a0f0aee72", fetch_kib=8767.26, write_kib=66.25,
-                fetch_factor=1.99979, write_factor=1.0),
-    "C3a": dict(kernel="gemm", source_sha="0b572a365962d46b", fetch_kib=53337.35, write_kib=17408.0,
-                fetch_factor=1.99979, write_factor=1.0),
+    "C5a": dict(kernel="gemv", source_sha="315e736737d82dec", fetch_kib=104488.40,
+                write_kib=1024.0, fetch_factor=1.99980, write_factor=1.0),
+    "C3a": dict(kernel="gemm", source_sha="1ac63d195dcdf5db", fetch_kib=53370.26,
+                write_kib=17408.0, fetch_factor=1.99980, write_factor=1.0),
 }
 
 
@@ -114,8 +130,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="C2a",
-                    help="workload (C1, C2a, C2b, C3a, C3b, C4, C5a, C5b, C5o); default C2a")
+    ap.add_argument("--config", default="C5a",
+                    help="workload (C1, C2a, C2b, C3a, C3b, C4, C5a, C5b, C5o); default C5a")
+    ap.add_argument("--secondary", default="C3a",
+                    help="a second workload timed in the same process and reported as the line's "
+                         "`secondary` record (its plain linear); 'none' disables it; default C3a")
+    ap.add_argument("--batches", type=int, default=7,
+                    help="alternating timing batches of the line's kernels (median and best)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--glu", choices=["silu", "gelu_tanh", "gelu_erf"], default=None,
@@ -284,6 +305,270 @@ def workload_name(cfg, glu=None, cap=None, a16=False):
             f"{wdesc} weights{rot}{gated}{tail} ({how} per step)")
 
 
+def read_sclk_mhz():
+    """The current shader clock from the driver's sysfs table (the entry marked '*'), else from
+    rocm-smi; None if neither can be read."""
+    import glob
+    import re
+    import subprocess
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as fh:
+                for line in fh:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                        if m:
+                            return int(m.group(1))
+        except OSError:
+            continue
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                           timeout=20)
+        m = re.search(r"sclk.*?\((\d+)\s*Mhz\)", r.stdout, re.I)
+        if m:
+            return int(m.group(1))
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return None
+
+
+class LayerBench:
+    """One workload's buffers, its step (w4a8_linear or the chosen variant) and its dominant
+    kernel alone, over a pool of weight copies that defeats the last-level cache."""
+
+    def __init__(self, args, name, variants=True):
+        import numpy as np
+        import torch
+        from bit_group_quantized_act_amd import synth, w4a8
+        self.w4a8, self.synth = w4a8, synth
+        dev = self.dev = torch.device("cuda:0")
+        chosen = [f for f, on in ((synth.FMT_INT8, args.w8), (synth.FMT_CQ2, args.cq2),
+                                  (synth.FMT_CQ1, args.cq1), (synth.FMT_CQ3, args.cq3))
+                  if on and variants]
+        over = {"fmt": chosen[0]} if chosen else {}
+        layer = self.layer = synth.make(name, **over)
+        cfg = self.cfg = layer["cfg"]
+        self.byte_decoded = cfg.fmt in BYTE_DECODED
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        if "row_scales" in layer:      # one scale per row, packed through the row-scale view
+            lay, packed0 = w4a8.pack_row_scale(t(layer["codes"]), t(layer["row_scales"]),
+                                               cfg.fmt, cfg.group, row_bias=t(layer["row_bias"]),
+                                               codebook=t(layer["codebook"]))
+        else:
+            lay, packed0 = w4a8.pack(t(layer["codes"]), t(layer["scales"]), cfg.fmt, cfg.group,
+                                     bias=t(layer["bias"]), codebook=t(layer["codebook"]))
+        self.lay = lay
+        self.wbytes = synth.weight_bytes(cfg)
+        fused = (cfg.m == 1 and cfg.k <= 16384 and                # w4a8_linear's one-kernel
+                 (w8_gemv_workgroups(cfg) <= 1024 if self.byte_decoded else cfg.n <= 131072))
+        self.cap = cap = args.argmax if variants else None
+        self.a16 = a16 = args.a16 and variants
+        self.glu = args.glu if variants else None
+        if cap is not None:
+            fused = False                                  # the tail runs in the two-kernel path
+        alg_bytes = synth.algorithmic_bytes(cfg, fused_prep=fused)
+        # fp16 activations at one row (k <= 16384, at most 2048 panels): w4a8_linear_a16 is one
+        # kernel with the prepass fused in
+        self.fused_a16 = fused_a16 = a16 and cfg.m == 1 and cfg.k <= 16384 and \
+            -(-cfg.n // 64) <= 2048
+        if a16:      # weights + xh (2 bytes per input) + fp32 group sums + y, no xq / xs / xsum
+            alg_bytes = synth.weight_bytes(cfg) + 2 * cfg.m * cfg.k + 4 * cfg.m * (cfg.k // 64) \
+                + 4 * cfg.m * cfg.n
+            if fused_a16:                                  # + the fp32 row read
+                alg_bytes += 4 * cfg.k
+        if cap is not None:                                # keys written and read, token, logit
+            alg_bytes += 2 * w4a8.argmax_work_bytes(cfg.n) + 8
+        act = None
+        if self.glu is not None:
+            act = {"silu": w4a8.ACT_SILU, "gelu_tanh": w4a8.ACT_GELU_TANH,
+                   "gelu_erf": w4a8.ACT_GELU_ERF}[self.glu]
+            alg_bytes -= 4 * cfg.m * (cfg.n // 2)         # the output is [m][F], not [m][n]
+        self.act, self.fused, self.alg_bytes = act, fused, alg_bytes
+        self.ops = synth.int_ops(cfg)
+        pool_n = self.pool_n = 1 if args.hot else max(2, -(-POOL_BYTES // lay.bytes))
+        self.pool = [packed0] + [packed0.clone() for _ in range(pool_n - 1)]
+        self.x = t(layer["x"])
+        ng = cfg.k // cfg.group
+        self.xq = torch.empty((cfg.m, cfg.k), dtype=torch.int8, device=dev)
+        self.xs = torch.empty((ng, cfg.m), dtype=torch.float32, device=dev)     # group-major
+        self.xsum = torch.empty((ng, cfg.m), dtype=torch.int32, device=dev)
+        self.y = torch.empty((cfg.m, cfg.n if act is None else cfg.n // 2), dtype=torch.float32,
+                             device=dev)
+        self.token = torch.empty(1, dtype=torch.int32, device=dev)
+        self.tval = torch.empty(1, dtype=torch.float32, device=dev)
+        self.work = w4a8.argmax_work(lay, dev)
+        self.xh16, self.xsf16 = w4a8.a16_buffers(cfg.m, cfg.k, dev) if a16 else (None, None)
+        torch.cuda.synchronize()
+
+    def kernel(self, i):
+        """The dominant kernel alone: the fused prepass + GEMV at one row (the plain GEMV for a
+        vocabulary-sized row), the GEMM above."""
+        w, lay, pk = self.w4a8, self.lay, self.pool[i % self.pool_n]
+        x, y, xq, xs, xsum = self.x, self.y, self.xq, self.xs, self.xsum
+        if self.fused_a16:
+            w.linear_a16(lay, pk, x, out=y, prep_out=(self.xh16, self.xsf16))
+        elif self.a16:
+            w.gemm_a16(lay, pk, self.xh16, self.xsf16, out=y)
+        elif self.cap is not None:
+            w.gemv_argmax(lay, pk, xq, xs, xsum, self.cap, out=(y[0], self.token, self.tval),
+                          work=self.work)
+        elif self.act is not None:
+            if self.fused:
+                w.linear_glu(lay, pk, x, self.act, self.cfg.hadamard, out=y,
+                             prep_out=(xq, xs, xsum))
+            else:
+                w.gemm_glu(lay, pk, xq, xs, xsum, self.act, out=y)
+        elif self.fused:
+            w.linear(lay, pk, x, self.cfg.hadamard, out=y, prep_out=(xq, xs, xsum))
+        elif self.cfg.m == 1:
+            w.gemv(lay, pk, xq[0], xs, xsum, out=y[0])
+        else:
+            w.gemm(lay, pk, xq, xs, xsum, out=y)
+
+    def step(self, i):
+        """One pass of the hot path: the prepass and the linear (or the chosen variant)."""
+        w, lay, pk = self.w4a8, self.lay, self.pool[i % self.pool_n]
+        x, y, prep = self.x, self.y, (self.xq, self.xs, self.xsum)
+        if self.a16:
+            w.linear_a16(lay, pk, x, out=y, prep_out=(self.xh16, self.xsf16))
+        elif self.cap is not None:
+            w.lm_head_argmax(lay, pk, x, self.cap, self.cfg.hadamard,
+                             out=(y[0], self.token, self.tval), work=self.work, prep_out=prep)
+        elif self.act is not None:
+            w.linear_glu(lay, pk, x, self.act, self.cfg.hadamard, out=y, prep_out=prep)
+        else:
+            w.linear(lay, pk, x, self.cfg.hadamard, out=y, prep_out=prep)
+
+    def kernel_name(self):
+        kname = "gemv" if self.cfg.m == 1 else "gemm"  # the fused kernel lives in gemv.hip
+        return ("gemv_argmax (GEMV with the tail + key reduction)" if self.cap is not None else
+                f"{kname}_a16" if self.a16 else f"{kname}_w8" if self.byte_decoded else kname)
+
+    def traffic(self):
+        kname = "gemv" if self.cfg.m == 1 else "gemm"
+        variant = ("glu" if self.act is not None else "argmax" if self.cap is not None else
+                   "a16" if self.a16 else
+                   self.synth.FORMAT_NAMES[self.cfg.fmt] if self.byte_decoded else None)
+        key = self.cfg.name if variant is None else f"{self.cfg.name}-{variant}"
+        return measured_traffic(key, kname)
+
+    def roofline(self, us_median, us_best, probe_gbps=None):
+        """The dominant kernel against its bound: HBM bytes, or int8 / fp16 MFMA operations for
+        a GEMM whose MFMA floor is above its HBM floor."""
+        cfg = self.cfg
+        hbm_floor = self.alg_bytes / (HBM_PEAK_GBPS * 1e9)
+        peak_mfma = F16_PEAK_TFLOPS if self.a16 else INT8_PEAK_TOPS
+        mfma_floor = self.ops / (peak_mfma * 1e12)
+        tops = self.ops / (us_median * 1e-6) / 1e12
+        if cfg.m > 1 and mfma_floor > hbm_floor:
+            roof = dict(bound="mfma", achieved=round(tops, 2), peak=peak_mfma,
+                        unit="TFLOP/s", frac=round(tops / peak_mfma, 4))
+        else:
+            achieved = self.alg_bytes / (us_median * 1e-6) / 1e9
+            roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS,
+                        unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4))
+        roof.update(traffic=self.traffic(), kernel=self.kernel_name(),
+                    kernel_us=round(us_median, 3), kernel_us_best=round(us_best, 3),
+                    alg_bytes_per_launch=self.alg_bytes, int_ops_per_launch=self.ops,
+                    tops=round(tops, 2))
+        if probe_gbps is not None:
+            roof["probe_GBps"] = round(probe_gbps, 1)
+            roof["pct_hbm_probe"] = round(self.alg_bytes / (us_median * 1e-6) / 1e9 /
+                                          probe_gbps, 4)
+        if cfg.m > 1:
+            roof["pct_mfma_peak"] = round(tops / peak_mfma, 4)
+            roof["pct_hbm_peak"] = round(self.alg_bytes / (us_median * 1e-6) / 1e9 /
+                                         HBM_PEAK_GBPS, 4)
+            valu_us = 2.0 * cfg.m * cfg.n * (cfg.k // cfg.group) / VALU_LANE_OPS * 1e6
+            roof["valu_epilogue_floor_us"] = round(valu_us, 3)
+            roof["pct_valu_ceiling"] = round(valu_us / us_median, 4)
+            ceiling = min(peak_mfma, self.ops / self.alg_bytes * HBM_PEAK_GBPS / 1000.0)
+            roof["pct_roofline"] = round(tops / ceiling, 4)
+        return roof
+
+
+class StreamProbe:
+    """A plain read of the packed weight buffers of a workload (its pool, so every launch
+    streams from HBM), in one of a few launch shapes: the achievable read rate for that byte
+    count is the best shape's."""
+
+    SHAPES = [(wg, u) for wg in (1024, 2048, 4096, 8192) for u in (4, 8)]
+
+    def __init__(self, lb):
+        import ctypes
+        import torch
+        path = os.path.join(ROOT, "bit_group_quantized_act_amd", "libw4a8_probe.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built: run __graft_entry__.build()")
+        self.lib = ctypes.CDLL(path)
+        self.lib.stream_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+        self.lib.stream_probe_read.restype = ctypes.c_int
+        self.lb = lb
+        self.bytes = lb.lay.bytes // 16 * 16
+        self.sink = torch.empty(max(wg for wg, _ in self.SHAPES), dtype=torch.int32,
+                                device=lb.dev)
+
+    def kernel(self, shape):
+        import ctypes
+        import torch
+        wg, unroll = shape
+
+        def call(i):
+            pk = self.lb.pool[i % self.lb.pool_n]
+            rc = self.lib.stream_probe_read(
+                ctypes.c_void_p(pk.data_ptr()), self.bytes, ctypes.c_void_p(self.sink.data_ptr()),
+                wg, unroll, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"stream_probe_read failed: hipError {rc}")
+        return call
+
+
+def cpu_baseline(lb, seconds):
+    """The CPU oracle (test infrastructure) on a bounded sample of the workload: all rows,
+    `cols` weight rows (all of them when the layer is small; matched gate and up rows for the
+    gated output), at most ~2e9 multiply-adds per repetition, repeated for `seconds`."""
+    import numpy as np
+    import oracle
+    cfg, layer, act, cap, a16 = lb.cfg, lb.layer, lb.act, lb.cap, lb.a16
+    cols = cfg.n if cfg.m * cfg.n * cfg.k <= 2e9 else \
+        max(64, int(2e9 / (cfg.m * cfg.k)) // 64 * 64)
+    rows = np.arange(cols)
+    if act is not None:               # matched gate and up rows: cols / 2 outputs
+        half = max(1, cols // 2)
+        rows = np.concatenate([np.arange(half), cfg.n // 2 + np.arange(half)])
+    sub = lambda a: None if a is None else np.ascontiguousarray(a[rows])
+    codes, scales, bias, cb = (sub(layer[key]) for key in ("codes", "scales", "bias",
+                                                            "codebook"))
+    sample_wbytes = lb.wbytes * rows.size / cfg.n
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        if a16:
+            oh, osf = oracle.prep_a16(layer["x"])
+            yo = oracle.linear_a16(cfg.fmt, codes, scales, oh, osf, cfg.group, bias_f16=bias,
+                                   with_terms=False)
+        else:
+            oq, os_, osum = oracle.prep(layer["x"], cfg.group, cfg.hadamard)
+            yo = oracle.linear(cfg.fmt, codes, scales, oq, os_, osum, cfg.group,
+                               bias_f16=bias, codebook=cb, with_terms=False)
+        if act is not None:
+            oracle.glu(act, yo)
+        if cap is not None:
+            oracle.softcap_argmax(yo, cap)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    what = ("the whole workload" if rows.size == cfg.n else
+            f"all {cfg.m} rows x {rows.size} of the {cfg.n} weight rows")
+    return dict(value=round(sample_wbytes * reps / el / 1e9, 3), unit="GB/s",
+                cores=oracle.num_threads(), kind="oracle",
+                sample=f"{what} of {cfg.name} ({'fp16-activation ' if a16 else ''}prep + linear"
+                       f"{' + gated output' if act is not None else ''}"
+                       f"{' + soft cap and argmax' if cap is not None else ''}), repeated "
+                       f"{reps}x in {el:.1f} s ({1e3 * el / reps:.2f} ms each)")
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -291,7 +576,6 @@ def main():
               "sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from bit_group_quantized_act_amd import synth, w4a8
 
@@ -305,114 +589,36 @@ def main():
         attention_bench(args)
         return
     w4a8.load()   # fails loudly if the HIP library is not built
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    torch.cuda.set_device(torch.device("cuda:0"))
 
-    chosen = [f for f, on in ((synth.FMT_INT8, args.w8), (synth.FMT_CQ2, args.cq2),
-                              (synth.FMT_CQ1, args.cq1), (synth.FMT_CQ3, args.cq3)) if on]
-    if len(chosen) > 1:
+    if sum(bool(v) for v in (args.w8, args.cq2, args.cq1, args.cq3)) > 1:
         print("give at most one of --w8 / --cq2 / --cq1 / --cq3", file=sys.stderr)
         sys.exit(2)
-    over = {"fmt": chosen[0]} if chosen else {}
-    layer = synth.make(args.config, **over)
-    byte_decoded = layer["cfg"].fmt in BYTE_DECODED
-    cfg = layer["cfg"]
-    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    if "row_scales" in layer:      # one scale per row, packed through the row-scale view
-        lay, packed0 = w4a8.pack_row_scale(t(layer["codes"]), t(layer["row_scales"]), cfg.fmt,
-                                           cfg.group, row_bias=t(layer["row_bias"]),
-                                           codebook=t(layer["codebook"]))
-    else:
-        lay, packed0 = w4a8.pack(t(layer["codes"]), t(layer["scales"]), cfg.fmt, cfg.group,
-                                 bias=t(layer["bias"]), codebook=t(layer["codebook"]))
-    wbytes = synth.weight_bytes(cfg)
-    fused = (cfg.m == 1 and cfg.k <= 16384 and                    # w4a8_linear's one-kernel
-             (w8_gemv_workgroups(cfg) <= 1024 if byte_decoded else cfg.n <= 131072))   # case
-    cap = args.argmax
-    a16 = args.a16
-    if (a16 or cap is not None or args.glu is not None) and byte_decoded:
+    cfg0 = synth.config(args.config)
+    variant = args.a16 or args.argmax is not None or args.glu is not None
+    if variant and (args.w8 or args.cq2 or args.cq1 or args.cq3):
         print("--w8 / --cq1 / --cq2 / --cq3 time the plain linear only", file=sys.stderr)
         sys.exit(2)
-    if a16 and (cap is not None or args.glu is not None or cfg.group != 64 or
-                cfg.fmt == synth.FMT_CODEBOOK):
+    if args.a16 and (args.argmax is not None or args.glu is not None or cfg0.group != 64 or
+                     cfg0.fmt == synth.FMT_CODEBOOK):
         print("--a16 needs a symmetric or affine 64-group workload and no --glu / --argmax",
               file=sys.stderr)
         sys.exit(2)
-    if cap is not None:
-        if cfg.m != 1 or args.glu is not None or not cap >= 0:
-            print("--argmax needs a one-row workload, no --glu and a cap >= 0", file=sys.stderr)
-            sys.exit(2)
-        fused = False                                  # the tail runs in the two-kernel path
-    alg_bytes = synth.algorithmic_bytes(cfg, fused_prep=fused)
-    # fp16 activations at one row (k <= 16384, at most 2048 panels): w4a8_linear_a16 is one
-    # kernel with the prepass fused in
-    fused_a16 = a16 and cfg.m == 1 and cfg.k <= 16384 and -(-cfg.n // 64) <= 2048
-    if a16:          # weights + xh (2 bytes per input) + fp32 group sums + y, no xq / xs / xsum
-        alg_bytes = synth.weight_bytes(cfg) + 2 * cfg.m * cfg.k + 4 * cfg.m * (cfg.k // 64) + \
-            4 * cfg.m * cfg.n
-        if fused_a16:                                  # + the fp32 row read
-            alg_bytes += 4 * cfg.k
-    if cap is not None:                                # keys written and read, token, logit
-        alg_bytes += 2 * w4a8.argmax_work_bytes(cfg.n) + 8
-    act = None
-    if args.glu is not None:
-        if cfg.n % 128 != 0:
-            print(f"--glu needs n = 2F with F a multiple of 64 ({cfg.name} has n = {cfg.n})",
-                  file=sys.stderr)
-            sys.exit(2)
-        act = {"silu": w4a8.ACT_SILU, "gelu_tanh": w4a8.ACT_GELU_TANH,
-               "gelu_erf": w4a8.ACT_GELU_ERF}[args.glu]
-        alg_bytes -= 4 * cfg.m * (cfg.n // 2)         # the output is [m][F], not [m][n]
-    ops = synth.int_ops(cfg)
-    pool_n = 1 if args.hot else max(2, -(-POOL_BYTES // lay.bytes))
-    pool = [packed0] + [packed0.clone() for _ in range(pool_n - 1)]
-    x = t(layer["x"])
-    ng = cfg.k // cfg.group
-    xq = torch.empty((cfg.m, cfg.k), dtype=torch.int8, device=dev)
-    xs = torch.empty((ng, cfg.m), dtype=torch.float32, device=dev)     # group-major
-    xsum = torch.empty((ng, cfg.m), dtype=torch.int32, device=dev)
-    y = torch.empty((cfg.m, cfg.n if act is None else cfg.n // 2), dtype=torch.float32,
-                    device=dev)
-    token = torch.empty(1, dtype=torch.int32, device=dev)
-    tval = torch.empty(1, dtype=torch.float32, device=dev)
-    work = w4a8.argmax_work(lay, dev)
-    xh16, xsf16 = w4a8.a16_buffers(cfg.m, cfg.k, dev) if a16 else (None, None)
-    torch.cuda.synchronize()
+    if args.argmax is not None and (cfg0.m != 1 or args.glu is not None or
+                                    not args.argmax >= 0):
+        print("--argmax needs a one-row workload, no --glu and a cap >= 0", file=sys.stderr)
+        sys.exit(2)
+    if args.glu is not None and cfg0.n % 128 != 0:
+        print(f"--glu needs n = 2F with F a multiple of 64 ({cfg0.name} has n = {cfg0.n})",
+              file=sys.stderr)
+        sys.exit(2)
 
-    def linear(i):
-        # the dominant kernel alone: the fused prepass + GEMV at one row (the plain GEMV for a
-        # vocabulary-sized row), the GEMM above
-        pk = pool[i % pool_n]
-        if fused_a16:
-            w4a8.linear_a16(lay, pk, x, out=y, prep_out=(xh16, xsf16))
-        elif a16:
-            w4a8.gemm_a16(lay, pk, xh16, xsf16, out=y)
-        elif cap is not None:
-            w4a8.gemv_argmax(lay, pk, xq, xs, xsum, cap, out=(y[0], token, tval), work=work)
-        elif act is not None:
-            if fused:
-                w4a8.linear_glu(lay, pk, x, act, cfg.hadamard, out=y, prep_out=(xq, xs, xsum))
-            else:
-                w4a8.gemm_glu(lay, pk, xq, xs, xsum, act, out=y)
-        elif fused:
-            w4a8.linear(lay, pk, x, cfg.hadamard, out=y, prep_out=(xq, xs, xsum))
-        elif cfg.m == 1:
-            w4a8.gemv(lay, pk, xq[0], xs, xsum, out=y[0])
-        else:
-            w4a8.gemm(lay, pk, xq, xs, xsum, out=y)
-
-    def step(i):
-        if a16:
-            w4a8.linear_a16(lay, pool[i % pool_n], x, out=y, prep_out=(xh16, xsf16))
-        elif cap is not None:
-            w4a8.lm_head_argmax(lay, pool[i % pool_n], x, cap, cfg.hadamard,
-                                out=(y[0], token, tval), work=work, prep_out=(xq, xs, xsum))
-        elif act is not None:
-            w4a8.linear_glu(lay, pool[i % pool_n], x, act, cfg.hadamard, out=y,
-                            prep_out=(xq, xs, xsum))
-        else:
-            w4a8.linear(lay, pool[i % pool_n], x, cfg.hadamard, out=y, prep_out=(xq, xs, xsum))
-
+    primary = LayerBench(args, args.config)
+    cfg = primary.cfg
+    secondary = None
+    if args.secondary.lower() != "none" and args.secondary != args.config:
+        secondary = LayerBench(args, args.secondary, variants=False)
+    probe = StreamProbe(primary) if cfg.m == 1 else None
     stream = torch.cuda.Stream()
 
     def capture(fn, count):
@@ -427,6 +633,7 @@ def main():
         return g
 
     def timed(g):
+        # HIP events recorded on the stream the graph's kernels run on
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -437,82 +644,57 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
+    # the steps: warmup, then exactly `steps` steps of the primary workload in one graph
     if args.warmup > 0:
-        gw = capture(step, args.warmup)
-        timed(gw)
-    g_steps = capture(step, args.steps)
-    ms_total = timed(g_steps)
-    ms_per_step = ms_total / args.steps
+        timed(capture(primary.step, args.warmup))
+    g_steps = capture(primary.step, args.steps)
+    ms_per_step = timed(g_steps) / args.steps
+    sec_ms_per_step = None
+    if secondary is not None:
+        g_sec_steps = capture(secondary.step, args.steps)
+        timed(g_sec_steps)
+        sec_ms_per_step = timed(g_sec_steps) / args.steps
 
-    g_lin = capture(linear, args.steps)
-    timed(g_lin)                                    # warm the graph
-    us_linear = timed(g_lin) * 1000.0 / args.steps
+    # the dominant kernels alone, in alternating batches
+    graphs = [("primary", capture(primary.kernel, args.steps))]
+    if secondary is not None:
+        graphs.append(("secondary", capture(secondary.kernel, args.steps)))
+    if probe is not None:
+        for shape in probe.SHAPES:
+            graphs.append((("probe",) + shape, capture(probe.kernel(shape), args.steps)))
+    for _, g in graphs:
+        timed(g)                                    # warm each graph
+    us = {name: [] for name, _ in graphs}
+    for _ in range(max(1, args.batches)):
+        for name, g in graphs:
+            us[name].append(timed(g) * 1000.0 / args.steps)
+    med = {k: float(sorted(v)[len(v) // 2]) for k, v in us.items()}
+    best = {k: float(min(v)) for k, v in us.items()}
+    sclk = read_sclk_mhz()
 
-    value = wbytes / (ms_per_step * 1e-3) / 1e9
-    hbm_floor = alg_bytes / (HBM_PEAK_GBPS * 1e9)
-    peak_mfma = F16_PEAK_TFLOPS if a16 else INT8_PEAK_TOPS
-    mfma_floor = ops / (peak_mfma * 1e12)
-    if cfg.m > 1 and mfma_floor > hbm_floor:
-        achieved = ops / (us_linear * 1e-6) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak_mfma,
-                    unit="TFLOP/s", frac=round(achieved / peak_mfma, 4))
-    else:
-        achieved = alg_bytes / (us_linear * 1e-6) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBPS, 4))
-    kname = "gemv" if cfg.m == 1 else "gemm"     # the fused kernel lives in gemv.hip
-    variant = ("glu" if act is not None else "argmax" if cap is not None else "a16" if a16 else
-               synth.FORMAT_NAMES[cfg.fmt] if byte_decoded else None)
-    traffic_key = cfg.name if variant is None else f"{cfg.name}-{variant}"   # counters per kernel
-    shown = ("gemv_argmax (GEMV with the tail + key reduction)" if cap is not None else
-             f"{kname}_a16" if a16 else f"{kname}_w8" if byte_decoded else kname)
-    roof.update(traffic=measured_traffic(traffic_key, kname), kernel=shown,
-                kernel_us=round(us_linear, 3), alg_bytes_per_launch=alg_bytes,
-                int_ops_per_launch=ops,
-                tops=round(ops / (us_linear * 1e-6) / 1e12, 2))
+    probe_gbps = None
+    if probe is not None:
+        pkey = min((k for k in med if k[0] == "probe"), key=lambda k: med[k])
+        probe_gbps = probe.bytes / (med[pkey] * 1e-6) / 1e9
+    roof = primary.roofline(med["primary"], best["primary"], probe_gbps)
+    if probe is not None:
+        roof["probe_us"] = round(med[pkey], 3)
+        roof["probe_shape"] = f"{pkey[1]} workgroups x 256 lanes, {pkey[2]} loads in flight"
+    value = primary.wbytes / (ms_per_step * 1e-3) / 1e9
 
-    cpu = None
-    if args.cpu_seconds > 0:
-        import oracle                      # the CPU baseline leg (test infrastructure)
-        # a bounded sample: all rows, `cols` weight rows (all of them when the layer is small;
-        # matched gate and up rows for the gated output), at most ~2e9 multiply-adds each
-        cols = cfg.n if cfg.m * cfg.n * cfg.k <= 2e9 else \
-            max(64, int(2e9 / (cfg.m * cfg.k)) // 64 * 64)
-        rows = np.arange(cols)
-        if act is not None:               # matched gate and up rows: cols / 2 outputs
-            half = max(1, cols // 2)
-            rows = np.concatenate([np.arange(half), cfg.n // 2 + np.arange(half)])
-        sub = lambda a: None if a is None else np.ascontiguousarray(a[rows])
-        codes, scales, bias, cb = (sub(layer[key]) for key in ("codes", "scales", "bias",
-                                                                "codebook"))
-        sample_wbytes = wbytes * rows.size / cfg.n
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            if a16:
-                oh, osf = oracle.prep_a16(layer["x"])
-                yo = oracle.linear_a16(cfg.fmt, codes, scales, oh, osf, cfg.group, bias_f16=bias,
-                                       with_terms=False)
-            else:
-                oq, os_, osum = oracle.prep(layer["x"], cfg.group, cfg.hadamard)
-                yo = oracle.linear(cfg.fmt, codes, scales, oq, os_, osum, cfg.group,
-                                   bias_f16=bias, codebook=cb, with_terms=False)
-            if act is not None:
-                oracle.glu(act, yo)
-            if cap is not None:
-                oracle.softcap_argmax(yo, cap)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
-        what = ("the whole workload" if rows.size == cfg.n else
-                f"all {cfg.m} rows x {rows.size} of the {cfg.n} weight rows")
-        cpu = dict(value=round(sample_wbytes * reps / el / 1e9, 3), unit="GB/s",
-                   cores=oracle.num_threads(), kind="oracle",
-                   sample=f"{what} of {cfg.name} ({'fp16-activation ' if a16 else ''}prep + linear"
-                          f"{' + gated output' if act is not None else ''}"
-                          f"{' + soft cap and argmax' if cap is not None else ''}), repeated "
-                          f"{reps}x in "
-                          f"{el:.1f} s ({1e3 * el / reps:.2f} ms each)")
+    sec = None
+    if secondary is not None:
+        sc = secondary.cfg
+        sec = {"workload": workload_name(sc), "m": sc.m, "k": sc.k, "n": sc.n,
+               "group": sc.group, "format": synth.FORMAT_NAMES[sc.fmt],
+               "weight_pool_buffers": secondary.pool_n,
+               "metric": "int8 TOPS (2*M*N*K per second)" if sc.m > 1 else "weight GB/s",
+               "ms_per_step": round(sec_ms_per_step, 6),
+               "step_value": round(secondary.ops / (sec_ms_per_step * 1e-3) / 1e12, 2)
+               if sc.m > 1 else round(secondary.wbytes / (sec_ms_per_step * 1e-3) / 1e9, 2),
+               "roofline": secondary.roofline(med["secondary"], best["secondary"])}
+
+    cpu = cpu_baseline(primary, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
     out = {
         "metric": METRIC,
@@ -525,13 +707,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if a16 else "int8",
+        "dtype": "f16" if primary.a16 else "int8",
         "data": "synthetic",
-        "config": {"workload": workload_name(cfg, args.glu, cap, a16), "m": cfg.m, "k": cfg.k, "n": cfg.n,
-                   "group": cfg.group, "format": synth.FORMAT_NAMES[cfg.fmt],
-                   "weight_pool_buffers": pool_n, "hot_cache": bool(args.hot),
-                   "parallelism": "single GPU"},
+        "config": {"workload": workload_name(cfg, primary.glu, primary.cap, primary.a16),
+                   "m": cfg.m, "k": cfg.k, "n": cfg.n, "group": cfg.group,
+                   "format": synth.FORMAT_NAMES[cfg.fmt], "weight_pool_buffers": primary.pool_n,
+                   "hot_cache": bool(args.hot), "parallelism": "single GPU",
+                   "batches": max(1, args.batches)},
         "roofline": roof,
+        "secondary": sec,
+        "sclk_mhz": sclk,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -1,7 +1,9 @@
 """Build libw4a8.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc.
 
 Every translation unit is compiled in parallel, then linked into
-``bit_group_quantized_act_amd/libw4a8.so`` (replaced atomically).  Flags:
+``bit_group_quantized_act_amd/libw4a8.so`` (replaced atomically).  The benchmark's HBM read probe
+(csrc/stream_probe.hip) is built into its own ``libw4a8_probe.so``, outside the layer's C ABI.
+Flags:
   --offload-arch=gfx950                       MI355X only, no other targets
   -fhip-fp32-correctly-rounded-divide-sqrt    IEEE fp32 division (the prepass is bit-exact)
   -target-feature -packed-fp32-ops            no packed fp32 VALU instructions in device code
@@ -20,6 +22,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libw4a8.so")
+PROBE_LIB = os.path.join(HERE, "libw4a8_probe.so")
+PROBE_SOURCE = "stream_probe.hip"
 SOURCES = ["api.hip", "pack.hip", "prep.hip", "gemv.hip", "gemm.hip", "tail.hip", "a16.hip",
            "attn.hip", "w8.hip"]
 
@@ -83,6 +87,10 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         procs.append((src + " (device assembly)",
                       subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
                                        text=True)))
+    probe_tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    procs.append((PROBE_SOURCE, subprocess.Popen(
+        [cc] + flags + ["-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", probe_tmp],
+        stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
@@ -109,6 +117,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + _quiet(r.stderr))
     os.replace(tmp, LIB)
+    os.replace(probe_tmp, PROBE_LIB)
     return LIB
 
 
