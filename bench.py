@@ -284,7 +284,7 @@ def workload_name(cfg, glu=None, cap=None, a16=False):
     if cfg.extra.get("row_scale"):
         rot += f", one scale per row seen as K/{cfg.group} groups"
     fused = (cfg.m == 1 and cfg.k <= 16384 and
-             (w8_gemv_workgroups(cfg) <= 1024 if cfg.fmt in BYTE_DECODED else cfg.n <= 131072))
+             (w8_gemv_workgroups(cfg) <= 1024 if cfg.fmt in BYTE_DECODED else cfg.n <= 262144))
     if a16:
         one = cfg.m == 1 and cfg.k <= 16384 and -(-cfg.n // 64) <= 2048
         return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
@@ -360,7 +360,7 @@ class LayerBench:
         self.lay = lay
         self.wbytes = synth.weight_bytes(cfg)
         fused = (cfg.m == 1 and cfg.k <= 16384 and                # w4a8_linear's one-kernel
-                 (w8_gemv_workgroups(cfg) <= 1024 if self.byte_decoded else cfg.n <= 131072))
+                 (w8_gemv_workgroups(cfg) <= 1024 if self.byte_decoded else cfg.n <= 262144))
         self.cap = cap = args.argmax if variants else None
         self.a16 = a16 = args.a16 and variants
         self.glu = args.glu if variants else None

@@ -181,10 +181,11 @@ hipError_t launch_gemv(const Geom &g, const uint8_t *packed, const int8_t *xq, c
 
 // The decode GEMV with the prepass of its one activation row fused in: every workgroup
 // quantizes x into LDS; workgroup 0 also writes xq, xs, xsum.  k <= kFusedMaxK.  Each workgroup
-// (one 64-row panel) repeats the quantization, so beyond kFusedMaxPanels panels (a vocabulary
-// head) the separate prepass launch costs less than the repeats.
+// (one 64-row panel) repeats the quantization of its wavefronts' groups from L2, which costs less
+// than a second launch up to a 262144-row vocabulary head (4096 panels, measured at k 1536: one
+// kernel 35.9 us, prepass + GEMV 37.6 us); beyond kFusedMaxPanels the prepass runs on its own.
 constexpr int kFusedMaxK = 16384;
-constexpr int kFusedMaxPanels = 2048;
+constexpr int kFusedMaxPanels = 4096;
 constexpr int kFusedQuadsPerLane = 8;   // activation quads one lane of the fused GEMV quantizes
 hipError_t launch_gemv_fused(const Geom &g, const uint8_t *packed, const float *x, int hadamard,
                              int8_t *xq, float *xs, int32_t *xsum, float *y, hipStream_t stream);

@@ -75,6 +75,13 @@ CASES = [
     ("C4", dict(m=200, n=448, k=1536), False),
     ("C4", dict(m=3, n=2049, k=512), False),
     ("C5b", dict(m=64, n=1000, k=1536), False),
+    # taller activation blocks with 128-wide groups: several row tiles with a 1-row or a
+    # 44-row last tile, ragged n, and 1024 rows in the sign-folded and affine formats
+    ("C4", dict(m=256, n=96, k=384), False),
+    ("C4", dict(m=300, n=1000, k=768), True),
+    ("C1", dict(m=257, n=200, k=1024, group=128), True),
+    ("C3a", dict(m=513, n=130, k=768, group=128), True),
+    ("C3a", dict(m=1024, n=384, k=256, group=128), True),
 ]
 
 
@@ -114,7 +121,8 @@ def _run_linear(L):
 
 
 # one-row cases take the fused kernel (rotation included for C4); the 16448-wide row exceeds the
-# fused kernel's LDS bound and takes prepass + GEMV; multi-row cases take prepass + GEMM
+# fused kernel's LDS bound, and 262145 outputs its panel bound, and take prepass + GEMV;
+# multi-row cases take prepass + GEMM
 LINEAR_CASES = [
     ("C1", dict(), False),
     ("C1", dict(n=1000), True),
@@ -128,6 +136,8 @@ LINEAR_CASES = [
     ("C4", dict(m=1, n=130, k=8192), True),        # fused with rotation, 4 quads per lane
     ("C1", dict(n=192, k=16384), True),            # fused at its k bound, 8 quads per lane
     ("C1", dict(n=64, k=16448), True),
+    ("C1", dict(n=262144, k=128), False),          # fused at its row bound, 4096 panels
+    ("C1", dict(n=262145, k=128), False),          # one row past it: prepass + GEMV
     ("C3a", dict(m=65, n=1000, k=1280), True),
     ("C4", dict(m=200, n=448, k=1536), False),
 ]
