@@ -725,7 +725,6 @@ w4a8_status w4a8_debug_partials(const w4a8_layout *L, const void *packed, int32_
                                 void *stream) {
     w4a8_status s = check_layout(L);
     if (s != W4A8_OK) return s;
-    if ((s = reject_int8(L, "w4a8_debug_partials")) != W4A8_OK) return s;
     if (m < 1) return fail(W4A8_ERR_ARG, "m = %d must be at least 1", m);
     if (m > (1 << 20)) return fail(W4A8_ERR_UNSUPPORTED, "m = %d is above 2^20", m);
     if (!packed) return fail(W4A8_ERR_ARG, "packed is NULL");
@@ -738,6 +737,9 @@ w4a8_status w4a8_debug_partials(const w4a8_layout *L, const void *packed, int32_
     const w4a8::Geom g = geom_of(L);
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (byte_decoded(L))
+        return launched(w4a8::launch_w8_partials(g, pk, m, xq, d, st),
+                        "int8-weight partials launch");
     if (m == 1)
         return launched(w4a8::launch_gemv(g, pk, xq, nullptr, xsum, nullptr, d, st),
                         "gemv partials launch");

@@ -234,14 +234,17 @@ __device__ __forceinline__ int cq3_dword(uint32_t w, int s, uint32_t bw, int sh,
 
 // wpp: wavefronts per panel (1, 2, 4 or 8); a workgroup takes 8 / wpp consecutive panels, so a
 // short row still gives each wavefront several groups (or chunks) and each workgroup more bytes.
-// FUSED: the prepass runs in the kernel (x in io) and xq4 / xs are not read.
-template <int FMT, int G, bool FUSED, bool ROT>
+// FUSED: the prepass runs in the kernel (x in io) and xq4 / xs are not read.  PARTIALS: each
+// group's int32 dot product is stored to d[row][g] in place of the fp32 epilogue.
+template <int FMT, int G, bool FUSED, bool ROT, bool PARTIALS = false>
 __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *__restrict__ packed,
                                                                 const Geom geom,
                                                                 const int *__restrict__ xq4,
                                                                 const float *__restrict__ xs,
                                                                 float *__restrict__ y, int wpp,
-                                                                const FusedIO io) {
+                                                                const FusedIO io,
+                                                                int *__restrict__ d = nullptr) {
+    static_assert(!(PARTIALS && FUSED), "the partials come from the plain GEMV");
     constexpr int CK = (FMT == kFmtCQ2) ? 64 : kW8Chunk;   // k per chunk
     constexpr int CPG = G / CK;                       // chunks per group
     constexpr int RING = (FMT == kFmtCQ2) ? 4 : 256 / G;   // groups in flight per wavefront
@@ -259,6 +262,7 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *_
     const int kc = geom.k / CK;
     const int ng = live ? geom.k / G : 0;
     const int nblk = (geom.k / G + 3) / 4;
+    const int row = p * kPanelRows + lane;
     const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)(live ? p : 0) * kc * 1024,
                                 live ? (uint64_t)kc * 1024 : 0);
     const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)(live ? p : 0) * nblk * 512,
@@ -313,30 +317,37 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *_
                             d4[e] = __builtin_amdgcn_sdot4(ring[s][c][e], xg[4 * c + e], d4[e], false);
                 }
                 const int dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-                const float coef = xssrc[g] * half_bits_to_float(meta[s] & 0xFFFFu);
-                acc = fmaf(coef, static_cast<float>(dot), acc);
+                if (PARTIALS) {
+                    if (row < geom.n) d[(int64_t)row * ng + g] = dot;
+                } else {
+                    const float coef = xssrc[g] * half_bits_to_float(meta[s] & 0xFFFFu);
+                    acc = fmaf(coef, static_cast<float>(dot), acc);
+                }
             }
             load(s, g + RING * wpp);
         }
     }
+    if (PARTIALS) return;                             // (every wavefront: no barrier follows)
     red[wave][lane] = acc;
     __syncthreads();
     if (wsub != 0 || !live) return;
     float s = red[wave][lane];
     for (int w = 1; w < wpp; ++w) s += red[wave + w][lane];
-    const int row = p * kPanelRows + lane;
     if (row < geom.n) y[row] = s;
 }
 
 // One row against the bit-plane formats: a workgroup per panel, 8 wavefronts over the 128-k
 // chunks, lane r on panel row r; a chunk is P 16-byte loads per lane and holds 128 / G groups.
-template <int FMT, int G, bool FUSED, bool ROT>
+// PARTIALS as for gemv_w8_kernel.
+template <int FMT, int G, bool FUSED, bool ROT, bool PARTIALS = false>
 __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t *__restrict__ packed,
                                                                   const Geom geom,
                                                                   const int *__restrict__ xq4,
                                                                   const float *__restrict__ xs,
                                                                   float *__restrict__ y, int wpp,
-                                                                  const FusedIO io) {
+                                                                  const FusedIO io,
+                                                                  int *__restrict__ d = nullptr) {
+    static_assert(!(PARTIALS && FUSED), "the partials come from the plain GEMV");
     constexpr int P = planes<FMT>;
     constexpr int GPC = kBitChunk / G;                // groups per chunk (2 or 1)
     constexpr int RING = FMT == kFmtCQ3 ? 2 : 4;      // chunks in flight per wavefront
@@ -421,14 +432,18 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
                                                                false);
                             }
                     const int dgi = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-                    if (GPC == 2) {
+                    if (GPC == 2 && PARTIALS) {
+                        if (row < geom.n) d[(int64_t)row * ng + g] = dgi;
+                    } else if (GPC == 2) {
                         const float coef = xssrc[g] * half_bits_to_float((meta[s] >> (16 * gi)) & 0xFFFFu);
                         acc = fmaf(coef, static_cast<float>(dgi), acc);
                     } else {
                         dot += dgi;
                     }
                 }
-                if (GPC == 1) {
+                if (GPC == 1 && PARTIALS) {
+                    if (row < geom.n) d[(int64_t)row * ng + c] = dot;
+                } else if (GPC == 1) {
                     const float coef = xssrc[c] * half_bits_to_float(meta[s] & 0xFFFFu);
                     acc = fmaf(coef, static_cast<float>(dot), acc);
                 }
@@ -436,6 +451,7 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
             load(s, c + RING * wpp);
         }
     }
+    if (PARTIALS) return;                             // (every wavefront: no barrier follows)
     red[wave][lane] = acc;
     __syncthreads();
     if (wsub != 0 || !live) return;
@@ -461,13 +477,15 @@ struct W8Stage {
 };                                                    // (row r32 of tile `half`)
 
 // Three workgroups per CU (12 wavefronts) where the registers allow it: the int8 variant keeps
-// its 16-byte weight operands one stage ahead instead of two for that.
-template <int FMT, int G>
+// its 16-byte weight operands one stage ahead instead of two for that.  PARTIALS: each group's
+// int32 tile is stored to d[row][col][g] in place of the fp32 epilogue (xs and y are not used).
+template <int FMT, int G, bool PARTIALS = false>
 __global__ __launch_bounds__(256, 3) void gemm_w8_kernel(const uint8_t *__restrict__ packed,
                                                          const Geom geom, int m,
                                                          const int8_t *__restrict__ xq,
                                                          const float *__restrict__ xs,
-                                                         float *__restrict__ y) {
+                                                         float *__restrict__ y,
+                                                         int *__restrict__ d = nullptr) {
     constexpr int GPS = kW8SK / G;
     constexpr int BPG = G / 32;                       // MFMA blocks per group
     __shared__ __attribute__((aligned(16))) v4i lds[2][64 * 8];   // [buf][row][16-byte unit]
@@ -508,7 +526,7 @@ __global__ __launch_bounds__(256, 3) void gemm_w8_kernel(const uint8_t *__restri
     const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)(wact ? p : 0) * nblk * 512,
                                 wact ? (uint64_t)nblk * 512 : 0);
     const rsrc_t rx = make_rsrc(xq, (uint64_t)m * k);
-    const rsrc_t rs = make_rsrc(xs, (uint64_t)ng * m * 4);
+    const rsrc_t rs = make_rsrc(xs, PARTIALS ? 0 : (uint64_t)ng * m * 4);   // (no xs: zeros)
 
     auto load_stage = [&](int s, W8Stage<FMT, G> &r) {
 #pragma unroll
@@ -627,7 +645,17 @@ __global__ __launch_bounds__(256, 3) void gemm_w8_kernel(const uint8_t *__restri
                                                                 (j % BPG == 0) ? izero : part[t],
                                                                 0, 0, 0);
             }
-            if (j % BPG == BPG - 1) {                 // the group's last block: rescale
+            if (PARTIALS && j % BPG == BPG - 1) {     // the group's last block: store D
+                if (wact && col < geom.n) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int row = m0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+                            if (row < m) d[((int64_t)row * geom.n + col) * ng + g] = part[t][e];
+                        }
+                }
+            } else if (j % BPG == BPG - 1) {          // the group's last block: rescale
                 const int q = j / BPG;
                 const float sw = half_bits_to_float(meta[q] & 0xFFFFu);
                 // both tiles' coefficients in one two-block outer product: block t = tile t
@@ -648,7 +676,7 @@ __global__ __launch_bounds__(256, 3) void gemm_w8_kernel(const uint8_t *__restri
         if (s + 1 < nstage) stage(std::integral_constant<int, 1>{}, s + 1);
     }
 
-    if (!wact || col >= geom.n) return;
+    if (PARTIALS || !wact || col >= geom.n) return;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -717,6 +745,34 @@ void gemv_fused_fmt(const Geom &g, const uint8_t *packed, int hadamard, const Fu
     else gemv_fmt<FMT, true, false>(g, packed, nullptr, nullptr, y, io, stream);
 }
 
+// The partials variants: the plain GEMV (m == 1) or the GEMM with their epilogues replaced by a
+// store of the int32 per-group dot products.
+template <int FMT, int G>
+void partials_go(const Geom &g, const uint8_t *packed, int m, const int8_t *xq, int32_t *d,
+                 hipStream_t stream) {
+    if (m == 1) {
+        int grid;
+        const int wpp = gemv_wpp(g, &grid);
+        const int *x4 = reinterpret_cast<const int *>(xq);
+        if constexpr (bit_plane<FMT>)
+            gemv_bits_kernel<FMT, G, false, false, true><<<grid, 64 * kW8Waves, 0, stream>>>(
+                packed, g, x4, nullptr, nullptr, wpp, FusedIO{}, d);
+        else
+            gemv_w8_kernel<FMT, G, false, false, true><<<grid, 64 * kW8Waves, 0, stream>>>(
+                packed, g, x4, nullptr, nullptr, wpp, FusedIO{}, d);
+        return;
+    }
+    const unsigned grid = static_cast<unsigned>(((m + 63) / 64) * ((g.n_pad + kW8BN - 1) / kW8BN));
+    gemm_w8_kernel<FMT, G, true><<<grid, 256, 0, stream>>>(packed, g, m, xq, nullptr, nullptr, d);
+}
+
+template <int FMT>
+void partials_fmt(const Geom &g, const uint8_t *packed, int m, const int8_t *xq, int32_t *d,
+                  hipStream_t stream) {
+    if (g.group == 64) partials_go<FMT, 64>(g, packed, m, xq, d, stream);
+    else partials_go<FMT, 128>(g, packed, m, xq, d, stream);
+}
+
 template <int FMT>
 hipError_t launch_w8_fmt(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
                          const float *xs, float *y, hipStream_t stream) {
@@ -739,6 +795,16 @@ hipError_t launch_w8(const Geom &g, const uint8_t *packed, int m, const int8_t *
     if (g.fmt == kFmtCQ1) return launch_w8_fmt<kFmtCQ1>(g, packed, m, xq, xs, y, stream);
     if (g.fmt == kFmtCQ3) return launch_w8_fmt<kFmtCQ3>(g, packed, m, xq, xs, y, stream);
     return launch_w8_fmt<kFmtInt8>(g, packed, m, xq, xs, y, stream);
+}
+
+hipError_t launch_w8_partials(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
+                              int32_t *d, hipStream_t stream) {
+    if (m == 0) return hipSuccess;
+    if (g.fmt == kFmtCQ2) partials_fmt<kFmtCQ2>(g, packed, m, xq, d, stream);
+    else if (g.fmt == kFmtCQ1) partials_fmt<kFmtCQ1>(g, packed, m, xq, d, stream);
+    else if (g.fmt == kFmtCQ3) partials_fmt<kFmtCQ3>(g, packed, m, xq, d, stream);
+    else partials_fmt<kFmtInt8>(g, packed, m, xq, d, stream);
+    return hipGetLastError();
 }
 
 int w8_gemv_workgroups(const Geom &g) {

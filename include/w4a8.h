@@ -422,9 +422,10 @@ w4a8_status w4a8_attn_prefill(const w4a8_attn_layout *AL, const void *packed, co
 
 /*
  * The exact int32 partials D[r][n][g] (definitions above) written by the same kernel code as
- * the GEMV (m == 1) or the GEMM (m > 1), with the fp32 epilogue replaced by a store of D.
+ * the GEMV (m == 1) or the GEMM (m > 1) of the layout's format (the 4-bit formats' kernels, or
+ * those of the int8 and CQ1-CQ3 weights), with the fp32 epilogue replaced by a store of D.
  *   xsum  as from w4a8_prep (the AFFINE partial is recovered from the u - 8 codes as
- *         D_u = D_(u-8) + 8 * xsum)
+ *         D_u = D_(u-8) + 8 * xsum; the other formats do not read it, but it must be given)
  *   d     int32 [m][L->n][k/group]
  * Source: "cactus PR #697", review snippet of the per-group leaf contract.
  */

@@ -216,7 +216,7 @@ def test_invalid_calls_are_rejected_on_the_host(lib):
     L2 = w4a8.packed_layout(w4a8.CQ2, 100, 256, 64)
     assert L2.off_meta == 128 * 64 and L2.off_codebook > L2.off_meta and L2.bytes % 256 == 0
     assert lib.w4a8_pack_weights(ctypes.byref(L2), p, p, None, None, p, None) == ERR_ARG   # codebook
-    assert lib.w4a8_debug_partials(ctypes.byref(L2), p, 2, p, p, p, None) == ERR_UNSUPPORTED
+    assert lib.w4a8_debug_partials(ctypes.byref(L2), p, 0, p, p, p, None) == ERR_ARG   # m < 1
     # 1- and 3-bit codebooks: 16 / 48 bytes per 128 k of a row, k padded to a multiple of 128
     L1 = w4a8.packed_layout(w4a8.CQ1, 100, 192, 64)
     L3 = w4a8.packed_layout(w4a8.CQ3, 100, 192, 64)
@@ -230,7 +230,7 @@ def test_invalid_calls_are_rejected_on_the_host(lib):
     assert lib.w4a8_gemm_glu(ctypes.byref(w4a8.packed_layout(w4a8.INT8, 128, 256, 64)), p, 2, p,
                              p, p, silu, p, None) == ERR_UNSUPPORTED
     assert lib.w4a8_gemv_argmax(L8P, p, p, p, p, f(0.0), p, p, p, p, 16, None) == ERR_UNSUPPORTED
-    assert lib.w4a8_debug_partials(L8P, p, 2, p, p, p, None) == ERR_UNSUPPORTED
+    assert lib.w4a8_debug_partials(L8P, p, 2, p, p, None, None) == ERR_ARG     # no d
     assert lib.w4a8_gemm_a16(L8P, p, 2, p, p, p, None) == ERR_UNSUPPORTED
     assert lib.w4a8_gemm(ctypes.byref(w4a8.packed_layout(w4a8.INT8, 64, 1 << 20, 64)), p, 4096,
                          p, p, p, p, None) == ERR_UNSUPPORTED                # m * k above 2^31
@@ -284,6 +284,9 @@ def test_valid_calls_without_a_device_report_device_error(lib):
     assert lib.w4a8_attn_layout_init(1, 64, 64, ctypes.byref(AL)) == 0
     assert lib.w4a8_attn_pack_kv(ctypes.byref(AL), p, p, p, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_linear_a16(ctypes.byref(L), p, 2, p, p, p, p, None) == ERR_DEVICE
+    for fmt in (w4a8.INT8, w4a8.CQ2, w4a8.CQ1, w4a8.CQ3):     # the byte-decoded partials
+        LB = w4a8.packed_layout(fmt, 128, 256, 64)
+        assert lib.w4a8_debug_partials(ctypes.byref(LB), p, 3, p, p, p, None) == ERR_DEVICE
     assert lib.w4a8_last_error().decode() != ""
 
 

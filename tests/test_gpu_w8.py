@@ -1,6 +1,7 @@
 """GPU parity of int8 weights (format 3, W8A8) and 2-, 1- and 3-bit codebook weights (formats 4, 5,
-6: CQ2, CQ1, CQ3) through w4a8_linear / w4a8_gemv / w4a8_gemm against the oracle: the prepass outputs bit-exact, y within
-the linear's bar (relative L2 error <= 1e-5, |err| <= 1e-4 T per element)."""
+6: CQ2, CQ1, CQ3) through w4a8_linear / w4a8_gemv / w4a8_gemm against the oracle: the prepass
+outputs and the int32 per-group partials (w4a8_debug_partials) bit-exact, y within the linear's
+bar (relative L2 error <= 1e-5, |err| <= 1e-4 T per element)."""
 from __future__ import annotations
 
 import numpy as np
@@ -74,6 +75,12 @@ def test_w8_parity(name, over, fmt):
     assert np.array_equal(got["xs"].view(np.uint32), ref["xs"].view(np.uint32))
     assert np.array_equal(got["xsum"], ref["xsum"])     # (written by the fused one-row kernel too)
     check_y(got["y"], ref["y"], ref["t"], f"w8 {name} {over}")
+    # the int32 per-group dot products of the same GEMV / GEMM code, bit for bit
+    w = _w4a8()
+    xq, _, xsum = got["dev"]
+    d = w.debug_partials(got["lay"], got["packed"], xq, xsum).cpu().numpy()
+    dref = oracle.partials(cfg.fmt, L["codes"], ref["xq"], cfg.group, codebook=L["codebook"])
+    assert np.array_equal(d, dref), f"partials differ at {np.argwhere(d != dref)[:5].tolist()}"
 
 
 @pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
