@@ -26,9 +26,10 @@
 //   lane r < 32 combines its gate value with lane r + 32's up value into act(gate) * up.
 //   Greedy tail (ARGMAX).  Wavefront 0 caps each logit, stores it, and turns it into a 64-bit key
 //   (an order-preserving image of the value above, the inverted row below: the largest key is
-//   the largest logit at its smallest row); a butterfly gives the workgroup's largest key, one
-//   atomic max merges it into the buffer the prepass cleared, and the workgroup that counts
-//   last decodes the token and its logit.  Nothing waits on another workgroup.
+//   the largest logit at its smallest row); a butterfly gives the panel's largest key, which
+//   lane 0 stores to the panel's slot of the key buffer.  A one-workgroup kernel (tail.hip)
+//   then reduces the keys and decodes the token and its logit: no atomics, and nothing waits
+//   on another workgroup.
 #include "w4a8_kernels.h"
 
 namespace w4a8 {
