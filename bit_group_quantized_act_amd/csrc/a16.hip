@@ -165,8 +165,8 @@ __global__ __launch_bounds__(64 * kA16Waves) void gemv_a16_kernel(const uint8_t 
 #pragma unroll
     for (int s = 0; s < kA16Ring; ++s) {
         const int g = wave + s * kA16Waves;
-        ring[s][0] = ld128(rc, code_off(g, 0));
-        ring[s][1] = ld128(rc, code_off(g, 1));
+        ring[s][0] = ld128_stream(rc, code_off(g, 0));
+        ring[s][1] = ld128_stream(rc, code_off(g, 1));
         meta[s] = (MB == 4) ? ld32(rm, meta_off(g)) : ld16(rm, meta_off(g));
     }
     const uint32_t *xsrc;                             // the row's halves and sums: LDS when fused
@@ -247,8 +247,8 @@ __global__ __launch_bounds__(64 * kA16Waves) void gemv_a16_kernel(const uint8_t 
                 if (FMT == kFmtAffine) acc = fmaf(half_bits_to_float(meta[s] >> 16), xsfsrc[g], acc);
             }
             const int gn = g + kA16Ring * kA16Waves;
-            ring[s][0] = ld128(rc, code_off(gn, 0));
-            ring[s][1] = ld128(rc, code_off(gn, 1));
+            ring[s][0] = ld128_stream(rc, code_off(gn, 0));
+            ring[s][1] = ld128_stream(rc, code_off(gn, 1));
             meta[s] = (MB == 4) ? ld32(rm, meta_off(gn)) : ld16(rm, meta_off(gn));
         }
     }

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
         }
 #pragma unroll
         for (int c = 0; c < kChunksPerGroup; ++c)
-            v[slot][c] = ld128(rw, in ? ((g * kChunksPerGroup + c) * kPanelRows + lrow) * 16 + wlane
+            v[slot][c] = ld128_stream(rw, in ? ((g * kChunksPerGroup + c) * kPanelRows + lrow) * 16 + wlane
                                       : kOOB);
     };
     // Issue order is pinned with scheduling barriers (loads complete in issue order, and every

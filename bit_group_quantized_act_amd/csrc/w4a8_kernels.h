@@ -47,8 +47,17 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint64_t bytes) {
     void *p = reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo);
     return __builtin_amdgcn_make_buffer_rsrc(p, 0, n, kRsrcCfg);
 }
+// Cache-policy operand of the buffer loads: bit 1 is the non-temporal (nt) hint on gfx950.
+constexpr int kCachePolicyNT = 2;
+
 __device__ __forceinline__ v4i ld128(rsrc_t r, int voff) {
     return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+// The same load with the non-temporal cache policy, for weight streams that one launch reads
+// once (the one-row GEMVs): the lines are not kept in L2 for a reuse that never comes.  Measured
+// on the 262144-row vocabulary head: 32.4 us against 35.3 us for the plain load.
+__device__ __forceinline__ v4i ld128_stream(rsrc_t r, int voff) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCachePolicyNT));
 }
 __device__ __forceinline__ v2i ld64(rsrc_t r, int voff) {
     return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));

@@ -275,7 +275,7 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *_
     auto load = [&](int s, int g) {
 #pragma unroll
         for (int c = 0; c < CPG; ++c)
-            ring[s][c] = ld128(rc, g < ng ? ((g * CPG + c) * 64 + lane) * 16 : kOOB);
+            ring[s][c] = ld128_stream(rc, g < ng ? ((g * CPG + c) * 64 + lane) * 16 : kOOB);
         meta[s] = ld16(rm, g < ng ? (((g >> 2) * 64 + lane) * 4 + (g & 3)) * 2 : kOOB);
     };
 #pragma unroll
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
     auto load = [&](int s, int c) {
 #pragma unroll
         for (int u = 0; u < P; ++u)
-            ring[s][u] = ld128(rc, c < kc ? ((c * P + u) * 64 + lane) * 16 : kOOB);
+            ring[s][u] = ld128_stream(rc, c < kc ? ((c * P + u) * 64 + lane) * 16 : kOOB);
         // the chunk's groups share one block of 4 (GPC * c is even when GPC = 2)
         const int g = c * GPC;
         if (GPC == 2) meta[s] = ld32(rm, c < kc ? (((g >> 2) * 64 + lane) * 4 + (g & 3)) * 2 : kOOB);
