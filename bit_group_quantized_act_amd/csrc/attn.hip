@@ -19,16 +19,19 @@
 //   value codes.
 //   AV with unsigned P on a signed MFMA: u - 128 enters the i8 product and 128 * (the block's
 //   column sum) is added back in int32, exactly.
-//   Queries: a prepass writes the int8 codes and row scales once; the attention kernel loads them.
-//   Kernel: a workgroup of 4 wavefronts per (query head, 32-query tile, slot range); each
-//   wavefront takes every 4th block of the range (head_dim 256: every 2nd block and half of the
-//   value groups, to keep its output state in registers), keeps its own (O, m, l) and skips
-//   blocks no query of the tile sees; the wavefronts merge through LDS, and ranges split over
-//   several workgroups (to fill the chip) merge in a second kernel, both in a fixed order.  The
-//   next value group's scales, codes and column sums load as soon as the current group's are used;
-//   the codes are P' * (255 / max P'), one reciprocal per (row, group, block).  At one wavefront
-//   per SIMD the waits are the cost: a block's positions and key scales load during the
-//   wavefront's previous block, and its first value group right behind its key codes.
+//   Kernel: a workgroup of 8 wavefronts (two per SIMD) per (query head, 32-query tile, slot
+//   range).  It stages 1024 / head_dim consecutive blocks of its key/value head at a time in LDS
+//   (about 145 KiB: key codes, transposed value codes, value-group scales, column sums, slot
+//   positions and key scales) with buffer loads that write LDS directly, and quantizes the
+//   tile's queries into LDS while those copies are in flight (the first range's workgroup also
+//   writes the codes and scales out); one wait and one barrier later every operand is an LDS
+//   read, with the 16-byte units of key, value and query rows XOR-swizzled so that the MFMA
+//   operand reads are free of bank conflicts.  Each wavefront takes every (8 / DS)-th block of
+//   the range (head_dim 256, DS = 2: half of the value groups, to keep its output state in
+//   registers), keeps its own (O, m, l) and skips blocks no query of the tile sees; the
+//   wavefronts merge through LDS, and ranges split over several workgroups (one workgroup per
+//   CU fills the chip) merge in a second kernel, both in a fixed order.  The codes are
+//   P' * (255 / max P'), one reciprocal per (row, group, block).
 #include "w4a8_kernels.h"
 
 namespace w4a8 {
@@ -36,7 +39,7 @@ namespace {
 
 constexpr int kSlots = 64;      // slots per block
 constexpr int kQT = 32;         // queries per tile
-constexpr int kAW = 4;          // wavefronts per workgroup
+constexpr int kAW = 8;          // wavefronts per workgroup (two per SIMD)
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kMergeRegs = 8;  // split states the merge holds in registers at once
 
@@ -120,6 +123,38 @@ __device__ __forceinline__ float wave_max32(float v) {          // max with the 
     return fmaxf(v, __shfl_xor(v, 32, 64));
 }
 
+// LDS staging of NB = 1024 / D consecutive blocks of one key/value head (every region a whole
+// number of KiB, about 142-148 KiB in all): key codes [NB * 64][D] and transposed value codes
+// [NB][D][64] with their 16-byte units XOR-swizzled by row, value-group scales [NB][NG][64],
+// value column sums [NB][D], slot positions and key scales [NB][64].
+template <int D>
+struct AttnStage {
+    static constexpr int NB = 1024 / D;
+    static constexpr int NG = D / 32;
+    static constexpr int kK = NB * kSlots * D;
+    static constexpr int kVT = NB * D * kSlots;
+    static constexpr int kSV = NB * NG * kSlots * 4;
+    static constexpr int kVS = NB * D * 4;
+    static constexpr int kPS = NB * kSlots * 4;
+    static constexpr int oK = 0, oVT = oK + kK, oSV = oVT + kVT, oVS = oSV + kSV;
+    static constexpr int oPos = oVS + kVS, oSk = oPos + kPS, kBytes = oSk + kPS;
+    static_assert(kSV % 1024 == 0 && kVS % 1024 == 0 && kPS % 1024 == 0, "whole copies");
+    // A key row is D bytes (D / 16 units); 256 / D rows share one 256-byte bank period, so the
+    // unit key changes every 256 / D rows: 16 lanes reading one unit of 16 rows hit 16 distinct
+    // 16-byte bank groups.  Value rows are 64 bytes (4 units, 4 rows per period).
+    __device__ static int kkey(int slot) { return (slot / (256 / D)) % (D / 16); }
+    __device__ static int vkey(int row) { return (row >> 2) & 3; }
+};
+
+typedef __attribute__((address_space(3))) void attn_lds_void;
+
+// 64 lanes x 16 bytes from r at the lane's offset to LDS byte address lds_addr + 16 * lane (the
+// destination goes to M0, so it is made a scalar).
+__device__ __forceinline__ void attn_copy16(rsrc_t r, uint32_t lds_addr, int voff) {
+    const uint32_t a = __builtin_amdgcn_readfirstlane(lds_addr);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (attn_lds_void *)(uintptr_t)a, 16, voff, 0, 0, 0);
+}
+
 // DS = 2 (head_dim 256) splits the value groups over wavefront pairs: wavefront w takes groups
 // (w / 2) * NG/2 .. +NG/2-1 of every second block (w % 2), so its output state is half as large
 // (both of a pair compute the block's QK product and softmax, identically).
@@ -128,11 +163,18 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
                                                         const uint8_t *__restrict__ packed,
                                                         const AttnArgs a) {
 #pragma clang fp contract(off)
+    using ST = AttnStage<D>;
     constexpr int NG = D / 32;           // value groups of the head
     constexpr int NGW = NG / DS;         // value groups of this wavefront
     constexpr int BL = kAW / DS;         // wavefronts sharing a group set (one block each)
+    constexpr int NB = ST::NB;
+    __shared__ __attribute__((aligned(16))) uint8_t stage[ST::kBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t qtile[kQT * D];   // the tile's query codes
+    __shared__ float qscl[kQT];                                       // and row scales
     __shared__ float xm[kAW][kQT];
-    __shared__ float xo[kAW - 1][64][16];
+    // the merge's exchange buffer reuses the staged key codes once every block is done
+    static_assert((kAW - 1) * 64 * 16 * 4 <= ST::kK, "merge buffer inside the key region");
+    float(*xo)[64][16] = reinterpret_cast<float(*)[64][16]>(stage + ST::oK);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int dpart = wave / BL, blane = wave % BL;
@@ -149,24 +191,89 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     const uint32_t qpos = static_cast<uint32_t>(a.pos0) + static_cast<uint32_t>(qi);
     const uint32_t window = static_cast<uint32_t>(a.window), sink = static_cast<uint32_t>(a.sink);
 
-    // the query row's int8 codes (from the query prepass), as the B operands of the QK product:
-    // lane (q, h) holds d = 32i + 16h .. +15 of each 32-wide chunk i
-    v4i qb[NG];
-    const int64_t qrow = (int64_t)head * a.nq + (qlive ? qi : 0);
+    // the head's regions in the packed cache (rebased per staged chunk below)
+    const uint8_t *kqh = packed + ag.off_kq + (int64_t)kh * ag.nblk * kSlots * D;
+    const uint8_t *skh = packed + ag.off_sk + (int64_t)kh * ag.nblk * kSlots * 4;
+    const uint8_t *posh = packed + ag.off_pos + (int64_t)kh * ag.nblk * kSlots * 4;
+    const uint8_t *vth = packed + ag.off_vt + (int64_t)kh * ag.nblk * D * kSlots;
+    const uint8_t *svh = packed + ag.off_sv + (int64_t)kh * ag.nblk * NG * kSlots * 4;
+    const uint8_t *vsh = packed + ag.off_vsum + (int64_t)kh * ag.nblk * D * 4;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (attn_lds_void *)&stage[0]));
+
+    // Stage blocks cb .. cb + NB - 1: every wavefront issues every fourth 1-KiB copy of each
+    // region; blocks past the head's last read past the rebased ranges and stage zeros.
+    auto stage_chunk = [&](int cb) __attribute__((always_inline)) {
+        const int nb = ag.nblk - cb;                           // blocks left in the head (>= 1)
+        const rsrc_t rk = make_rsrc(kqh + (int64_t)cb * kSlots * D, (uint64_t)nb * kSlots * D);
+        const rsrc_t rv = make_rsrc(vth + (int64_t)cb * D * kSlots, (uint64_t)nb * D * kSlots);
+        const rsrc_t rsv = make_rsrc(svh + (int64_t)cb * NG * kSlots * 4, (uint64_t)nb * NG * kSlots * 4);
+        const rsrc_t rvs = make_rsrc(vsh + (int64_t)cb * D * 4, (uint64_t)nb * D * 4);
+        const rsrc_t rpos = make_rsrc(posh + (int64_t)cb * kSlots * 4, (uint64_t)nb * kSlots * 4);
+        const rsrc_t rsk = make_rsrc(skh + (int64_t)cb * kSlots * 4, (uint64_t)nb * kSlots * 4);
+        for (int c = wave; c < ST::kK / 1024; c += kAW) {
+            const int pb = c * 1024 + 16 * lane;
+            const int slot = pb / D, u = (pb % D) / 16;
+            attn_copy16(rk, lds0 + ST::oK + c * 1024, slot * D + 16 * (u ^ ST::kkey(slot % kSlots)));
+        }
+        for (int c = wave; c < ST::kVT / 1024; c += kAW) {
+            const int pb = c * 1024 + 16 * lane;
+            const int row = pb / kSlots, u = (pb % kSlots) / 16;
+            attn_copy16(rv, lds0 + ST::oVT + c * 1024, row * kSlots + 16 * (u ^ ST::vkey(row)));
+        }
+        for (int c = wave; c < ST::kSV / 1024; c += kAW)
+            attn_copy16(rsv, lds0 + ST::oSV + c * 1024, c * 1024 + 16 * lane);
+        for (int c = wave; c < ST::kVS / 1024; c += kAW)
+            attn_copy16(rvs, lds0 + ST::oVS + c * 1024, c * 1024 + 16 * lane);
+        for (int c = wave; c < ST::kPS / 1024; c += kAW) {
+            attn_copy16(rpos, lds0 + ST::oPos + c * 1024, c * 1024 + 16 * lane);
+            attn_copy16(rsk, lds0 + ST::oSk + c * 1024, c * 1024 + 16 * lane);
+        }
+    };
+
+    // The tile's query rows quantized into LDS while the first chunk's copies are in flight: a
+    // row is D / 4 consecutive lanes of one wavefront, one float4 each (scale = max|row| / 127 and
+    // codes round-half-even(q / scale) in fp32, as the activation quantization; a zero scale gives
+    // zero codes).  The codes' 16-byte units are swizzled as the key rows'.  The first split's
+    // workgroup also writes them out (q8, sq).
+    auto quantize_queries = [&]() __attribute__((always_inline)) {
+        constexpr int LPR = D / 4;                          // lanes per row
+        constexpr int kQuads = kQT * LPR;
 #pragma unroll
-    for (int i = 0; i < NG; ++i)
-        qb[i] = qlive ? *reinterpret_cast<const v4i *>(a.q8 + qrow * D + 32 * i + 16 * half)
-                      : v4i{0, 0, 0, 0};
-    const float sq = qlive ? a.sq[qrow] : 0.0f;
-    const float qscale = sq * a.scale;
+        for (int j0 = 0; j0 < kQuads; j0 += 64 * kAW) {
+            const int j = j0 + static_cast<int>(threadIdx.x);
+            const int r = j / LPR, c4 = j % LPR;
+            const bool live = j < kQuads && q0 + r < a.nq;
+            const int64_t qidx = ((int64_t)head * a.nq + q0 + r) * LPR + c4;
+            const float4 v = live ? reinterpret_cast<const float4 *>(a.q)[qidx]
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+            float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+            for (int o = 1; o < LPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            const float scale = amax / 127.0f;
+            const float e[4] = {v.x, v.y, v.z, v.w};
+            uint32_t w = 0u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int c = 0;
+                if (scale > 0.0f)
+                    c = static_cast<int>(fminf(fmaxf(rintf(e[i] / scale), -127.0f), 127.0f));
+                w |= (static_cast<uint32_t>(c) & 0xFFu) << (8 * i);
+            }
+            if (j < kQuads) {
+                const int u = c4 / 4;
+                *reinterpret_cast<uint32_t *>(qtile + r * D + 16 * (u ^ ST::kkey(r)) + 4 * (c4 % 4)) = w;
+                if (c4 == 0) qscl[r] = scale;
+            }
+            if (live && split == 0) {
+                reinterpret_cast<uint32_t *>(a.q8)[qidx] = w;
+                if (c4 == 0) a.sq[(int64_t)head * a.nq + q0 + r] = scale;
+            }
+        }
+    };
 
-    const int8_t *kqb = reinterpret_cast<const int8_t *>(packed + ag.off_kq) + (int64_t)kh * ag.nblk * kSlots * D;
-    const float *skb = reinterpret_cast<const float *>(packed + ag.off_sk) + (int64_t)kh * ag.nblk * kSlots;
-    const int32_t *posb = reinterpret_cast<const int32_t *>(packed + ag.off_pos) + (int64_t)kh * ag.nblk * kSlots;
-    const int8_t *vtb = reinterpret_cast<const int8_t *>(packed + ag.off_vt) + (int64_t)kh * ag.nblk * D * kSlots;
-    const float *svb = reinterpret_cast<const float *>(packed + ag.off_sv) + (int64_t)kh * ag.nblk * NG * kSlots;
-    const int32_t *vsb = reinterpret_cast<const int32_t *>(packed + ag.off_vsum) + (int64_t)kh * ag.nblk * D;
-
+    v4i qb[NG];                 // the lane's query codes: d = 32i + 16h .. +15 of chunk i
+    float qscale = 0.0f;
     float mrun = kNegInf, lrun = 0.0f;
     v16f o[NGW];
 #pragma unroll
@@ -174,27 +281,11 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[g][e] = 0.0f;
 
-    const int b_lo = split * a.bps;
-    const int b_hi = min(ag.nblk, b_lo + a.bps);
-    // a block's slot positions and key scales for the lane's 32 slots: loaded while the
-    // wavefront's previous block is processed, so visibility needs no wait at a block's start
-    struct KBlock {
-        int4 pos[2][4];
-        float4 sk[2][4];
-    };
-    auto load_kblock = [&](int b, KBlock &k) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int base = b * kSlots + t * 32 + half * 16;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) k.pos[t][c] = reinterpret_cast<const int4 *>(posb + base)[c];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) k.sk[t][c] = reinterpret_cast<const float4 *>(skb + base)[c];
-        }
-    };
-    // block b with its positions and key scales in kc; the wavefront's next block's load into kn
-    auto block = [&](int b, const KBlock &kc, KBlock &kn) {
-        if (b + BL < b_hi) load_kblock(b + BL, kn);
+    // block b (staged at local index lb): visibility, S^T = K Q^T, the online softmax and the
+    // value products of the wavefront's groups, every operand from LDS
+    auto block = [&](int lb) __attribute__((always_inline)) {
+        const int *posl = reinterpret_cast<const int *>(stage + ST::oPos) + lb * kSlots;
+        const float *skl = reinterpret_cast<const float *>(stage + ST::oSk) + lb * kSlots;
         // visibility of the lane's 32 slots (two subtiles of 16)
         float s[2][16];
         bool any = false;
@@ -203,7 +294,7 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
             int pos16[16];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int4 pv = kc.pos[t][c];
+                const int4 pv = reinterpret_cast<const int4 *>(posl + t * 32 + half * 16)[c];
                 pos16[4 * c] = pv.x; pos16[4 * c + 1] = pv.y; pos16[4 * c + 2] = pv.z;
                 pos16[4 * c + 3] = pv.w;
             }
@@ -217,48 +308,23 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
             }
         }
         if (__builtin_amdgcn_ballot_w64(any) == 0) return;            // no query sees the block
-        // the value side of group g: its scales for the lane's 32 slots, the transposed value
-        // codes (A operands) and the column sums
-        struct VGroup {
-            float4 sv[2][4];
-            v4i va[2];
-            int4 vsum[4];
-        };
-        auto load_group = [&](int g, VGroup &v) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const float4 *svr = reinterpret_cast<const float4 *>(
-                    svb + ((int64_t)b * NG + g) * kSlots + t * 32 + half * 16);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) v.sv[t][c] = svr[c];
-                v.va[t] = *reinterpret_cast<const v4i *>(
-                    vtb + ((int64_t)b * D + 32 * g + col) * kSlots + t * 32 + half * 16);
-            }
-            const int4 *vsr = reinterpret_cast<const int4 *>(vsb + (int64_t)b * D + g * 32 + half * 16);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) v.vsum[c] = vsr[c];
-        };
-        // the key codes of both subtiles, then the first value group: its loads complete while
-        // the QK product and the softmax run
-        v4i ka[2][NG];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int8_t *kr = kqb + ((int64_t)b * kSlots + t * 32 + col) * D + 16 * half;
-#pragma unroll
-            for (int i = 0; i < NG; ++i) ka[t][i] = *reinterpret_cast<const v4i *>(kr + 32 * i);
-        }
-        VGroup cur;
-        load_group(dpart * NGW, cur);
         // S^T = K Q^T for the block's two 32-slot subtiles
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
+            const int slot = t * 32 + col;
+            const uint8_t *kr = stage + ST::oK + (lb * kSlots + slot) * D;
+            const int key = ST::kkey(slot);
+            v4i ka[NG];
+#pragma unroll
+            for (int i = 0; i < NG; ++i)
+                ka[i] = *reinterpret_cast<const v4i *>(kr + 16 * ((2 * i + half) ^ key));
             v16i acc = {};
 #pragma unroll
             for (int i = 0; i < NG; ++i)
-                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[t][i], qb[i], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[i], qb[i], acc, 0, 0, 0);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float4 kv = kc.sk[t][c];
+                const float4 kv = reinterpret_cast<const float4 *>(skl + t * 32 + half * 16)[c];
                 const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -286,19 +352,30 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
         lrun = lrun * alpha + psum;
         mrun = (mb == kNegInf) ? mrun : mnew;
         const float keep = (mb == kNegInf) ? 1.0f : alpha;
-        // one group's operands in flight: the next group's scales and codes load as soon as the
-        // current group's are consumed, overlapping its matrix product and epilogue
 #pragma unroll
-        for (int g = 0; g < NGW; ++g) {
+        for (int gi = 0; gi < NGW; ++gi) {
+            const int g = dpart * NGW + gi;
+            const float *svl = reinterpret_cast<const float *>(stage + ST::oSV) + (lb * NG + g) * kSlots;
+            float4 sv[2][4];
+            v4i va[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    sv[t][c] = reinterpret_cast<const float4 *>(svl + t * 32 + half * 16)[c];
+                const int row = lb * D + 32 * g + col;
+                va[t] = *reinterpret_cast<const v4i *>(stage + ST::oVT + row * kSlots +
+                                                      16 * ((2 * t + half) ^ ST::vkey(row)));
+            }
             // P folded with the value group's scale, quantized to u8 per (row, group, block)
             float mx = 0.0f;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const float4 sv = cur.sv[t][c];
-                    mx = fmaxf(mx, fmaxf(fmaxf(p[t][4 * c] * sv.x, p[t][4 * c + 1] * sv.y),
-                                         fmaxf(p[t][4 * c + 2] * sv.z, p[t][4 * c + 3] * sv.w)));
+                    const float4 v = sv[t][c];
+                    mx = fmaxf(mx, fmaxf(fmaxf(p[t][4 * c] * v.x, p[t][4 * c + 1] * v.y),
+                                         fmaxf(p[t][4 * c + 2] * v.z, p[t][4 * c + 3] * v.w)));
                 }
             mx = wave_max32(mx);
             const float sp = mx / 255.0f;         // 0 when nothing of the row is visible
@@ -311,8 +388,7 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
                 uint32_t w4[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const float sv4[4] = {cur.sv[t][c].x, cur.sv[t][c].y, cur.sv[t][c].z,
-                                          cur.sv[t][c].w};
+                    const float sv4[4] = {sv[t][c].x, sv[t][c].y, sv[t][c].z, sv[t][c].w};
                     // x + (2^23 + 2^22 + 128) rounds x to the nearest integer (ties to even) in
                     // the sum's low bits, already offset by 128: the low byte is u - 128 as int8
                     uint32_t bq[4];
@@ -326,26 +402,44 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
                 }
                 const v4i pb = {static_cast<int>(w4[0]), static_cast<int>(w4[1]),
                                 static_cast<int>(w4[2]), static_cast<int>(w4[3])};
-                iacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.va[t], pb, iacc, 0, 0, 0);
+                iacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(va[t], pb, iacc, 0, 0, 0);
             }
-            const int vs16[16] = {cur.vsum[0].x, cur.vsum[0].y, cur.vsum[0].z, cur.vsum[0].w,
-                                  cur.vsum[1].x, cur.vsum[1].y, cur.vsum[1].z, cur.vsum[1].w,
-                                  cur.vsum[2].x, cur.vsum[2].y, cur.vsum[2].z, cur.vsum[2].w,
-                                  cur.vsum[3].x, cur.vsum[3].y, cur.vsum[3].z, cur.vsum[3].w};
-            if (g + 1 < NGW) load_group(dpart * NGW + g + 1, cur);
+            const int4 *vsr = reinterpret_cast<const int4 *>(stage + ST::oVS) +
+                              (lb * D + g * 32 + half * 16) / 4;
+            int vs16[16];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int4 v = vsr[c];
+                vs16[4 * c] = v.x; vs16[4 * c + 1] = v.y; vs16[4 * c + 2] = v.z;
+                vs16[4 * c + 3] = v.w;
+            }
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const float av = static_cast<float>(iacc[e] + 128 * vs16[e]);
-                o[g][e] = fmaf(o[g][e], keep, sp * av);
+                o[gi][e] = fmaf(o[gi][e], keep, sp * av);
             }
         }
     };
-    // the wavefront's blocks b_lo + blane, + BL, ..., two per turn with the key sides ping-ponged
-    KBlock k0, k1;
-    if (b_lo + blane < b_hi) load_kblock(b_lo + blane, k0);
-    for (int b = b_lo + blane; b < b_hi; b += 2 * BL) {
-        block(b, k0, k1);
-        if (b + BL < b_hi) block(b + BL, k1, k0);
+
+    // The workgroup's blocks in staged chunks of NB; the wavefront takes blocks b_lo + blane,
+    // + BL, ... of each chunk in order.
+    const int b_lo = split * a.bps;
+    const int b_hi = min(ag.nblk, b_lo + a.bps);
+    for (int cb = b_lo; cb < b_hi; cb += NB) {
+        if (cb > b_lo) __syncthreads();                    // every wavefront is done with LDS
+        stage_chunk(cb);
+        if (cb == b_lo) quantize_queries();
+        __builtin_amdgcn_s_waitcnt(0);                     // this wavefront's copies (and loads)
+        __syncthreads();                                   // everybody's
+        if (cb == b_lo) {
+#pragma unroll
+            for (int i = 0; i < NG; ++i)
+                qb[i] = *reinterpret_cast<const v4i *>(qtile + col * D +
+                                                      16 * ((2 * i + half) ^ ST::kkey(col)));
+            qscale = qlive ? qscl[col] * a.scale : 0.0f;
+        }
+        const int ce = min(b_hi, cb + NB);
+        for (int b = cb + ((blane - (cb - b_lo)) % BL + BL) % BL; b < ce; b += BL) block(b - cb);
     }
 
     // merge the states of the BL wavefronts of each group set (fixed order): M = max m_w, each
@@ -403,31 +497,6 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
             orow[32 * (dpart * NGW + g) + 8 * (e >> 2) + 4 * half + (e & 3)] = o[g][e];
 }
 
-// The query prepass: one lane per 4 inputs of a row (a row is D/4 lanes of one wavefront),
-// sq = max|row| / 127 and q8 = round-half-even(q / sq) in fp32, as the activation quantization.
-__global__ __launch_bounds__(256) void attn_quant_q(const float4 *__restrict__ q, int64_t quads,
-                                                    int lanes_per_row, int *__restrict__ q8,
-                                                    float *__restrict__ sq) {
-#pragma clang fp contract(off)
-    const int64_t t = blockIdx.x * (int64_t)256 + threadIdx.x;
-    const bool live = t < quads;
-    const float4 v = live ? q[t] : make_float4(0.f, 0.f, 0.f, 0.f);
-    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    for (int o = 1; o < lanes_per_row; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-    const float scale = amax / 127.0f;
-    const float e[4] = {v.x, v.y, v.z, v.w};
-    uint32_t w = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int c = 0;
-        if (scale > 0.0f) c = static_cast<int>(fminf(fmaxf(rintf(e[i] / scale), -127.0f), 127.0f));
-        w |= (static_cast<uint32_t>(c) & 0xFFu) << (8 * i);
-    }
-    if (!live) return;
-    q8[t] = static_cast<int>(w);
-    if (t % lanes_per_row == 0) sq[t / lanes_per_row] = scale;
-}
-
 // the split states of each (head, query) merged in split order; a thread per 4 columns of a row
 __global__ __launch_bounds__(256) void attn_merge(int nsplit, int64_t rows, int d,
                                                   const float *__restrict__ work,
@@ -478,9 +547,11 @@ __global__ __launch_bounds__(256) void attn_merge(int nsplit, int64_t rows, int 
 }  // namespace
 
 int attn_splits(int nh, int nq, int nblk) {
+    // one workgroup per CU (the staged blocks fill its LDS), at most one block per wavefront of
+    // a group set (four for head_dim 256)
     const int tiles = nh * ((nq + kQT - 1) / kQT);
-    int s = (512 + tiles - 1) / tiles;                 // aim at two workgroups per CU
-    s = max(1, min(s, (nblk + kAW - 1) / kAW));        // about one block per wavefront
+    int s = (256 + tiles - 1) / tiles;
+    s = max(1, min(s, (nblk + kAW / 2 - 1) / (kAW / 2)));
     return s;
 }
 
@@ -501,11 +572,6 @@ hipError_t launch_attn(const AttnGeom &ag, const uint8_t *packed, const float *q
                        int pos0, int window, int sink, float scale, int8_t *q8, float *sq,
                        float *o, float *m, float *l, float *work, hipStream_t stream) {
     if (nq == 0) return hipSuccess;
-    const int64_t quads = (int64_t)nh * nq * ag.d / 4;
-    attn_quant_q<<<static_cast<unsigned>((quads + 255) / 256), 256, 0, stream>>>(
-        reinterpret_cast<const float4 *>(q), quads, ag.d / 4, reinterpret_cast<int *>(q8), sq);
-    hipError_t e0 = hipGetLastError();
-    if (e0 != hipSuccess) return e0;
     AttnArgs a{q, nh, nq, pos0, window, sink, attn_splits(nh, nq, ag.nblk), 0, scale, q8, sq, o, m,
                l, work};
     a.bps = (ag.nblk + a.nsplit - 1) / a.nsplit;
