@@ -174,7 +174,9 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     __shared__ float xm[kAW][kQT];
     // the merge's exchange buffer reuses the staged key codes once every block is done
     static_assert((kAW - 1) * 64 * 16 * 4 <= ST::kK, "merge buffer inside the key region");
-    float(*xo)[64][16] = reinterpret_cast<float(*)[64][16]>(stage + ST::oK);
+    // ([wavefront][element][lane]: a wavefront's 64 lanes write one element as 256 contiguous
+    // bytes, free of bank conflicts)
+    float(*xo)[16][64] = reinterpret_cast<float(*)[16][64]>(stage + ST::oK);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int dpart = wave / BL, blane = wave % BL;
@@ -461,14 +463,14 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     for (int g = 0; g < NGW; ++g) {
         if (blane != 0)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) xo[dpart * (BL - 1) + blane - 1][lane][e] = o[g][e] * mine;
+            for (int e = 0; e < 16; ++e) xo[dpart * (BL - 1) + blane - 1][e][lane] = o[g][e] * mine;
         __syncthreads();
         if (blane == 0) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 float v = o[g][e] * mine;
 #pragma unroll
-                for (int w = 1; w < BL; ++w) v += xo[dpart * (BL - 1) + w - 1][lane][e];
+                for (int w = 1; w < BL; ++w) v += xo[dpart * (BL - 1) + w - 1][e][lane];
                 o[g][e] = v;
             }
         }
