@@ -108,6 +108,17 @@ def w8_gemv_workgroups(cfg):
     return -(-panels // (8 // wpp))
 
 
+def fused_one_row(cfg):
+    """Whether w4a8_linear runs this workload as one kernel (the prepass fused into the GEMV),
+    as the library decides it: one row, k <= 16384, and at most 4096 panels (2048 with the
+    128-block rotation) for the 4-bit formats, 1024 GEMV workgroups for the byte-decoded ones."""
+    if cfg.m != 1 or cfg.k > 16384:
+        return False
+    if cfg.fmt in BYTE_DECODED:
+        return w8_gemv_workgroups(cfg) <= 1024
+    return -(-cfg.n // 64) <= (2048 if cfg.hadamard else 4096)
+
+
 def kernel_source_sha(kernel):
     import hashlib
     h = hashlib.sha256()
@@ -283,8 +294,7 @@ def workload_name(cfg, glu=None, cap=None, a16=False):
     rot = ", 128-block WHT" if cfg.hadamard else ""
     if cfg.extra.get("row_scale"):
         rot += f", one scale per row seen as K/{cfg.group} groups"
-    fused = (cfg.m == 1 and cfg.k <= 16384 and
-             (w8_gemv_workgroups(cfg) <= 1024 if cfg.fmt in BYTE_DECODED else cfg.n <= 262144))
+    fused = fused_one_row(cfg)
     if a16:
         one = cfg.m == 1 and cfg.k <= 16384 and -(-cfg.n // 64) <= 2048
         return (f"{cfg.name} {kind}: M={cfg.m} K={cfg.k} N={cfg.n} G={cfg.group} "
@@ -359,8 +369,7 @@ class LayerBench:
                                      bias=t(layer["bias"]), codebook=t(layer["codebook"]))
         self.lay = lay
         self.wbytes = synth.weight_bytes(cfg)
-        fused = (cfg.m == 1 and cfg.k <= 16384 and                # w4a8_linear's one-kernel
-                 (w8_gemv_workgroups(cfg) <= 1024 if self.byte_decoded else cfg.n <= 262144))
+        fused = fused_one_row(cfg)                          # w4a8_linear's one-kernel path
         self.cap = cap = args.argmax if variants else None
         self.a16 = a16 = args.a16 and variants
         self.glu = args.glu if variants else None

@@ -356,7 +356,7 @@ w4a8_status w4a8_linear(const w4a8_layout *L, const void *packed, int32_t m, con
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!byte_decoded(L) && m == 1 && L->k <= w4a8::kFusedMaxK &&
-        L->n_pad / W4A8_PANEL_ROWS <= w4a8::kFusedMaxPanels)
+        L->n_pad / W4A8_PANEL_ROWS <= w4a8::fused_max_panels(hadamard_block))
         return launched(w4a8::launch_gemv_fused(g, pk, x, hadamard_block, xq, xs, xsum, y, st),
                         "fused gemv launch");
     if (byte_decoded(L) && m == 1 && L->k <= w4a8::kFusedMaxK &&
@@ -410,7 +410,8 @@ w4a8_status w4a8_linear_glu(const w4a8_layout *L, const void *packed, int32_t m,
     const w4a8::Geom g = geom_of(L);
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (m == 1 && L->k <= w4a8::kFusedMaxK && L->n_pad / W4A8_PANEL_ROWS <= w4a8::kFusedMaxPanels)
+    if (m == 1 && L->k <= w4a8::kFusedMaxK &&
+        L->n_pad / W4A8_PANEL_ROWS <= w4a8::fused_max_panels(hadamard_block))
         return launched(w4a8::launch_gemv_glu_fused(g, act, pk, x, hadamard_block, xq, xs, xsum,
                                                     y, st),
                         "fused gated gemv launch");
@@ -606,7 +607,7 @@ w4a8_status w4a8_linear_a16(const w4a8_layout *L, const void *packed, int32_t m,
     if ((s = check_prep_a16(x, m, L->k, L->group, xh, xsf)) != W4A8_OK || m == 0) return s;
     if ((s = check_device()) != W4A8_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (m == 1 && L->k <= w4a8::kFusedMaxK && L->n_pad / W4A8_PANEL_ROWS <= w4a8::kFusedMaxPanels)
+    if (m == 1 && L->k <= w4a8::kFusedMaxK && L->n_pad / W4A8_PANEL_ROWS <= w4a8::kFusedMaxPanelsA16)
         return launched(w4a8::launch_linear_a16_fused(geom_of(L), static_cast<const uint8_t *>(packed),
                                                       x, xh, xsf, y, st),
                         "fused fp16-activation gemv launch");

@@ -191,10 +191,16 @@ hipError_t launch_gemv(const Geom &g, const uint8_t *packed, const int8_t *xq, c
 // The decode GEMV with the prepass of its one activation row fused in: every workgroup
 // quantizes x into LDS; workgroup 0 also writes xq, xs, xsum.  k <= kFusedMaxK.  Each workgroup
 // (one 64-row panel) repeats the quantization of its wavefronts' groups from L2, which costs less
-// than a second launch up to a 262144-row vocabulary head (4096 panels, measured at k 1536: one
-// kernel 35.9 us, prepass + GEMV 37.6 us); beyond kFusedMaxPanels the prepass runs on its own.
+// than a second launch up to a 262144-row vocabulary head without rotation (4096 panels,
+// measured at k 1536: one kernel 35.9 us, prepass + GEMV 37.6 us).  With the 128-block rotation
+// every workgroup also repeats the butterflies, and at 4096 panels the one kernel is slower
+// (45.8 us against 39.4 + the prepass): there the bound stays 2048 panels, as for the
+// fp16-activation path.  Beyond the bound the prepass runs on its own.
 constexpr int kFusedMaxK = 16384;
 constexpr int kFusedMaxPanels = 4096;
+constexpr int kFusedMaxPanelsRot = 2048;
+constexpr int kFusedMaxPanelsA16 = 2048;
+inline int fused_max_panels(int hadamard) { return hadamard ? kFusedMaxPanelsRot : kFusedMaxPanels; }
 constexpr int kFusedQuadsPerLane = 8;   // activation quads one lane of the fused GEMV quantizes
 hipError_t launch_gemv_fused(const Geom &g, const uint8_t *packed, const float *x, int hadamard,
                              int8_t *xq, float *xs, int32_t *xsum, float *y, hipStream_t stream);

@@ -216,11 +216,11 @@ w4a8_status w4a8_gemm(const w4a8_layout *L, const void *packed, int32_t m, const
  *   hadamard_block  0 or 128, as for w4a8_prep
  *   xq, xs, xsum    the prepass outputs, laid out as for w4a8_prep (written; the GEMM reads them)
  *   y               fp32 [m][L->n]
- * m == 1 with L->k <= 16384 and L->n <= 262144 runs one kernel: every workgroup of the GEMV
- * quantizes the row itself into LDS with the prepass's arithmetic (so xq, xs and xsum are the same
- * bits as w4a8_prep's), which removes a launch from each decode layer, up to a 262144-row
- * vocabulary head.  Otherwise the prepass kernel and then the GEMV or GEMM kernel are enqueued on
- * the stream.  m == 0 is a no-op (the pointers may then be NULL).
+ * m == 1 with L->k <= 16384 and L->n <= 262144 (131072 with hadamard_block 128) runs one
+ * kernel: every workgroup of the GEMV quantizes the row itself into LDS with the prepass's
+ * arithmetic (so xq, xs and xsum are the same bits as w4a8_prep's), which removes a launch from
+ * each decode layer.  Otherwise the prepass kernel and then the GEMV or GEMM kernel are enqueued
+ * on the stream.  m == 0 is a no-op (the pointers may then be NULL).
  * Source: "cactus PR #697", section "Quantized matmul" (the fused GEMV's first phase is the
  * Hadamard rotation and int8 quantization of the activations).
  */
@@ -245,8 +245,8 @@ typedef enum {
  *   x, hadamard_block, xq, xs, xsum  as for w4a8_linear (xq, xs and xsum are written)
  *   act   a w4a8_act
  *   y     fp32 [m][L->n / 2]
- * m == 1 with L->k <= 16384 and L->n <= 262144 runs one kernel (the prepass fused, as for
- * w4a8_linear); otherwise the prepass kernel, then the gated GEMV or GEMM.  m == 0 is a no-op.
+ * m == 1 with L->k <= 16384 and L->n <= 262144 (131072 with hadamard_block 128) runs one kernel
+ * (the prepass fused, as for w4a8_linear); otherwise the prepass kernel, then the gated GEMV or GEMM.  m == 0 is a no-op.
  * W4A8_ERR_ARG: L->n % 128 != 0, or act not a w4a8_act.  W4A8_ERR_UNSUPPORTED: the span from a
  * gate row to its up row in the packed codes or metadata ((L->n / 2 + 64) rows) exceeds
  * 2^31 - 16 bytes, or as for w4a8_gemm.
@@ -285,7 +285,8 @@ w4a8_status w4a8_gemm_glu(const w4a8_layout *L, const void *packed, int32_t m, c
  *            that overlap on one work buffer race)
  * Three kernels on the stream: the prepass; the GEMV, which also caps and stores the logits and
  * stores each panel's largest (logit, smaller index) key to work; a one-workgroup kernel that
- * reduces the keys into token and value.  A one-scale-per-row head (the orthogonal lm_head) is
+ * reduces the keys into token and value.  (Fusing the prepass into this GEMV, as w4a8_linear
+ * does, measured slower on the 262144-row head: 39.4 against 38.7 us per call.)  A one-scale-per-row head (the orthogonal lm_head) is
  * packed with that scale repeated over its 128-wide groups (group = 128): the same formula.
  * W4A8_ERR_ARG: softcap negative or not finite, token / value / work NULL or misaligned,
  * work_bytes too small.

@@ -138,6 +138,8 @@ LINEAR_CASES = [
     ("C1", dict(n=64, k=16448), True),
     ("C1", dict(n=262144, k=128), False),          # fused at its row bound, 4096 panels
     ("C1", dict(n=262145, k=128), False),          # one row past it: prepass + GEMV
+    ("C4", dict(m=1, n=131072, k=128), False),     # rotated: fused at its 2048-panel bound
+    ("C4", dict(m=1, n=131073, k=128), False),     # one row past it: prepass + GEMV
     ("C3a", dict(m=65, n=1000, k=1280), True),
     ("C4", dict(m=200, n=448, k=1536), False),
 ]
