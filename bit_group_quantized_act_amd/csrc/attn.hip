@@ -172,11 +172,11 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     __shared__ __attribute__((aligned(16))) uint8_t qtile[kQT * D];   // the tile's query codes
     __shared__ float qscl[kQT];                                       // and row scales
     __shared__ float xm[kAW][kQT];
-    // the merge's exchange buffer reuses the staged key codes once every block is done
-    static_assert((kAW - 1) * 64 * 16 * 4 <= ST::kK, "merge buffer inside the key region");
-    // ([wavefront][element][lane]: a wavefront's 64 lanes write one element as 256 contiguous
-    // bytes, free of bank conflicts)
-    float(*xo)[16][64] = reinterpret_cast<float(*)[16][64]>(stage + ST::oK);
+    // the merge's exchange buffer reuses the staged blocks once every block is done:
+    // [wavefront][group][element][lane] (a wavefront's 64 lanes store one element as 256
+    // contiguous bytes, free of bank conflicts)
+    static_assert(kAW * NGW * 16 * 64 * 4 <= ST::kBytes, "merge buffer inside the staged blocks");
+    float *xst = reinterpret_cast<float *>(stage);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int dpart = wave / BL, blane = wave % BL;
@@ -459,27 +459,18 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     float lsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < BL; ++w) lsum += xm[dpart * BL + w][col];
+    // Every wavefront stores its scaled state; then each of the BL wavefronts of a group set
+    // adds the BL states (in wavefront order) for NGW * 16 / BL of the set's elements and stores
+    // them: the sums and the output stores are spread over all the wavefronts.
 #pragma unroll
-    for (int g = 0; g < NGW; ++g) {
-        if (blane != 0)
+    for (int g = 0; g < NGW; ++g)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) xo[dpart * (BL - 1) + blane - 1][e][lane] = o[g][e] * mine;
-        __syncthreads();
-        if (blane == 0) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float v = o[g][e] * mine;
-#pragma unroll
-                for (int w = 1; w < BL; ++w) v += xo[dpart * (BL - 1) + w - 1][e][lane];
-                o[g][e] = v;
-            }
-        }
-        __syncthreads();
-    }
-    if (blane != 0 || !qlive) return;
+        for (int e = 0; e < 16; ++e) xst[((wave * NGW + g) * 16 + e) * 64 + lane] = o[g][e] * mine;
+    __syncthreads();
+    if (!qlive) return;
     const int64_t row = (int64_t)head * a.nq + qi;
     float *orow;
-    const bool stats = dpart == 0 && half == 0;
+    const bool stats = dpart == 0 && blane == 0 && half == 0;
     if (a.nsplit == 1) {
         orow = a.o + row * D;
         if (stats) { a.m[row] = mall; a.l[row] = lsum; }
@@ -492,11 +483,17 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
             ml[1] = lsum;
         }
     }
+    constexpr int PPW = NGW * 16 / BL;                 // elements each wavefront adds up
+    static_assert(PPW * BL == NGW * 16, "the elements split evenly");
 #pragma unroll
-    for (int g = 0; g < NGW; ++g)
+    for (int i = 0; i < PPW; ++i) {
+        const int pe = blane * PPW + i;
+        const int g = pe >> 4, e = pe & 15;
+        float v = xst[(((dpart * BL) * NGW + g) * 16 + e) * 64 + lane];
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            orow[32 * (dpart * NGW + g) + 8 * (e >> 2) + 4 * half + (e & 3)] = o[g][e];
+        for (int w = 1; w < BL; ++w) v += xst[(((dpart * BL + w) * NGW + g) * 16 + e) * 64 + lane];
+        orow[32 * (dpart * NGW + g) + 8 * (e >> 2) + 4 * half + (e & 3)] = v;
+    }
 }
 
 // the split states of each (head, query) merged in split order; a thread per 4 columns of a row
