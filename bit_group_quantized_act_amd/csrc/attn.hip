@@ -203,21 +203,30 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
         (attn_lds_void *)&stage[0]));
 
-    // Stage blocks cb .. cb + NB - 1: every wavefront issues every fourth 1-KiB copy of each
-    // region; blocks past the head's last read past the rebased ranges and stage zeros.
-    auto stage_chunk = [&](int cb) __attribute__((always_inline)) {
+    // Stage blocks cb .. cb + NB - 1: every wavefront issues every eighth 1-KiB copy of each
+    // region; blocks past the head's last read past the rebased ranges and stage zeros.  The key
+    // side (positions, key scales, key codes) first; the value side is issued once the key side
+    // has landed and arrives while the QK products and the softmax run.
+    auto stage_keys = [&](int cb) __attribute__((always_inline)) {
         const int nb = ag.nblk - cb;                           // blocks left in the head (>= 1)
         const rsrc_t rk = make_rsrc(kqh + (int64_t)cb * kSlots * D, (uint64_t)nb * kSlots * D);
-        const rsrc_t rv = make_rsrc(vth + (int64_t)cb * D * kSlots, (uint64_t)nb * D * kSlots);
-        const rsrc_t rsv = make_rsrc(svh + (int64_t)cb * NG * kSlots * 4, (uint64_t)nb * NG * kSlots * 4);
-        const rsrc_t rvs = make_rsrc(vsh + (int64_t)cb * D * 4, (uint64_t)nb * D * 4);
         const rsrc_t rpos = make_rsrc(posh + (int64_t)cb * kSlots * 4, (uint64_t)nb * kSlots * 4);
         const rsrc_t rsk = make_rsrc(skh + (int64_t)cb * kSlots * 4, (uint64_t)nb * kSlots * 4);
+        for (int c = wave; c < ST::kPS / 1024; c += kAW) {
+            attn_copy16(rpos, lds0 + ST::oPos + c * 1024, c * 1024 + 16 * lane);
+            attn_copy16(rsk, lds0 + ST::oSk + c * 1024, c * 1024 + 16 * lane);
+        }
         for (int c = wave; c < ST::kK / 1024; c += kAW) {
             const int pb = c * 1024 + 16 * lane;
             const int slot = pb / D, u = (pb % D) / 16;
             attn_copy16(rk, lds0 + ST::oK + c * 1024, slot * D + 16 * (u ^ ST::kkey(slot % kSlots)));
         }
+    };
+    auto stage_values = [&](int cb) __attribute__((always_inline)) {
+        const int nb = ag.nblk - cb;
+        const rsrc_t rv = make_rsrc(vth + (int64_t)cb * D * kSlots, (uint64_t)nb * D * kSlots);
+        const rsrc_t rsv = make_rsrc(svh + (int64_t)cb * NG * kSlots * 4, (uint64_t)nb * NG * kSlots * 4);
+        const rsrc_t rvs = make_rsrc(vsh + (int64_t)cb * D * 4, (uint64_t)nb * D * 4);
         for (int c = wave; c < ST::kVT / 1024; c += kAW) {
             const int pb = c * 1024 + 16 * lane;
             const int row = pb / kSlots, u = (pb % kSlots) / 16;
@@ -227,10 +236,6 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
             attn_copy16(rsv, lds0 + ST::oSV + c * 1024, c * 1024 + 16 * lane);
         for (int c = wave; c < ST::kVS / 1024; c += kAW)
             attn_copy16(rvs, lds0 + ST::oVS + c * 1024, c * 1024 + 16 * lane);
-        for (int c = wave; c < ST::kPS / 1024; c += kAW) {
-            attn_copy16(rpos, lds0 + ST::oPos + c * 1024, c * 1024 + 16 * lane);
-            attn_copy16(rsk, lds0 + ST::oSk + c * 1024, c * 1024 + 16 * lane);
-        }
     };
 
     // The tile's query rows quantized into LDS while the first chunk's copies are in flight: a
@@ -283,9 +288,16 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[g][e] = 0.0f;
 
-    // block b (staged at local index lb): visibility, S^T = K Q^T, the online softmax and the
-    // value products of the wavefront's groups, every operand from LDS
-    auto block = [&](int lb) __attribute__((always_inline)) {
+    // Block b (staged at local index lb), every operand from LDS: visibility, S^T = K Q^T and the
+    // online softmax (qk_block, key side only), then the value products of the wavefront's groups
+    // (av_block) from the probabilities and rescale factor qk_block leaves in a BlockP.
+    struct BlockP {
+        float p[2][16];
+        float keep;
+        bool live;                       // some query of the tile sees the block
+    };
+    auto qk_block = [&](int lb, BlockP &bp) __attribute__((always_inline)) {
+        bp.live = false;
         const int *posl = reinterpret_cast<const int *>(stage + ST::oPos) + lb * kSlots;
         const float *skl = reinterpret_cast<const float *>(stage + ST::oSk) + lb * kSlots;
         // visibility of the lane's 32 slots (two subtiles of 16)
@@ -310,6 +322,7 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
             }
         }
         if (__builtin_amdgcn_ballot_w64(any) == 0) return;            // no query sees the block
+        bp.live = true;
         // S^T = K Q^T for the block's two 32-slot subtiles
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -342,18 +355,22 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
         mb = wave_max32(mb);
         const float mnew = fmaxf(mrun, mb);
         const float alpha = (mrun == kNegInf) ? 0.0f : expf(mrun - mnew);
-        float p[2][16];
         float psum = 0.0f;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                p[t][e] = (s[t][e] == kNegInf) ? 0.0f : expf(s[t][e] - mnew);
-                psum += p[t][e];
+                bp.p[t][e] = (s[t][e] == kNegInf) ? 0.0f : expf(s[t][e] - mnew);
+                psum += bp.p[t][e];
             }
         lrun = lrun * alpha + psum;
         mrun = (mb == kNegInf) ? mrun : mnew;
-        const float keep = (mb == kNegInf) ? 1.0f : alpha;
+        bp.keep = (mb == kNegInf) ? 1.0f : alpha;
+    };
+    auto av_block = [&](int lb, const BlockP &bp) __attribute__((always_inline)) {
+        if (!bp.live) return;
+        const float keep = bp.keep;
+        const float(&p)[2][16] = bp.p;
 #pragma unroll
         for (int gi = 0; gi < NGW; ++gi) {
             const int g = dpart * NGW + gi;
@@ -427,12 +444,14 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     // + BL, ... of each chunk in order.
     const int b_lo = split * a.bps;
     const int b_hi = min(ag.nblk, b_lo + a.bps);
+    constexpr int MB = (NB + BL - 1) / BL;               // blocks of a wavefront per chunk
     for (int cb = b_lo; cb < b_hi; cb += NB) {
         if (cb > b_lo) __syncthreads();                    // every wavefront is done with LDS
-        stage_chunk(cb);
+        stage_keys(cb);
         if (cb == b_lo) quantize_queries();
         __builtin_amdgcn_s_waitcnt(0);                     // this wavefront's copies (and loads)
         __syncthreads();                                   // everybody's
+        stage_values(cb);
         if (cb == b_lo) {
 #pragma unroll
             for (int i = 0; i < NG; ++i)
@@ -441,7 +460,18 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
             qscale = qlive ? qscl[col] * a.scale : 0.0f;
         }
         const int ce = min(b_hi, cb + NB);
-        for (int b = cb + ((blane - (cb - b_lo)) % BL + BL) % BL; b < ce; b += BL) block(b - cb);
+        const int bf = cb + ((blane - (cb - b_lo)) % BL + BL) % BL;   // the wavefront's first
+        BlockP bp[MB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            bp[i].live = false;
+            if (bf + i * BL < ce) qk_block(bf + i * BL - cb, bp[i]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);                     // the value side, everybody's
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+            if (bf + i * BL < ce) av_block(bf + i * BL - cb, bp[i]);
     }
 
     // merge the states of the BL wavefronts of each group set (fixed order): M = max m_w, each
