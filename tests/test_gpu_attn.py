@@ -3,10 +3,13 @@ w4a8_attn_prefill) against the oracle's int8 method.
 
 Bit-exact: the query codes and scales, and the requantized keys.  The running state: m within
 2e-5 (1 + |m|) (fp32 logits against fp64), l within 1e-4 relative (fp32 exponentials summed),
-and the normalized output O / l with relative L2 error <= 1e-4 over each case and <= 1e-3 per
-query row.  Row bound: a code of the 8-bit P can differ from the oracle's only where P' / sp
-lies within fp32 rounding of a half-integer, and one such difference moves a row's output by at
-most 1/255 of one value row's share of it, well under 1e-3."""
+and the normalized output O / l with relative L2 error <= 1e-4 over each case; per query row
+<= 1e-3 for all but 0.1% of the rows and <= 4e-3 for every row.  Row bound: a code of the 8-bit
+P can differ from the oracle's only where P' / sp lies within fp32 rounding of a half-integer,
+and one such difference moves a row's output O / l by sp * v / l, at most 1/255 of the row's
+largest P' against its value row; relative to the row (a weighted mean of value rows whose
+largest weight is that slot's) this is at most about 1/255 = 3.9e-3, and it is that large only
+in a row dominated by one slot, so almost every row stays far below 1e-3."""
 from __future__ import annotations
 
 import numpy as np
@@ -67,7 +70,9 @@ def check_attn(got, ref, what):
     row = np.linalg.norm(on - rn, axis=1) / np.maximum(np.linalg.norm(rn, axis=1), 1e-30)
     tot = np.linalg.norm(on - rn) / np.linalg.norm(rn)
     assert tot <= 1e-4, f"{what}: relative L2 error {tot:.3e}"
-    assert row.max() <= 1e-3, f"{what}: worst row {row.max():.3e}"
+    assert row.max() <= 4e-3, f"{what}: worst row {row.max():.3e}"
+    assert (row > 1e-3).sum() <= max(1, row.size // 1000), \
+        f"{what}: {(row > 1e-3).sum()} of {row.size} rows above 1e-3"
     return tot, row.max()
 
 
@@ -81,6 +86,11 @@ CASES = [
                 pos0=300)),
     ("A1", dict(nh=3, nkvh=3, nq=7, nkv=64, d=256)),
     ("A2", dict(nh=2, nkvh=1, nq=20, nkv=90, d=64, window=5, sink=0, rolled=False, pos0=400)),
+    # slot ranges longer than one staged chunk (1024 / head_dim blocks): several chunks per
+    # workgroup, the last one partly past the cache
+    ("A1", dict(nh=8, nkvh=2, nq=256, nkv=2100, d=256)),
+    ("A2", dict(nh=16, nkvh=4, nq=128, nkv=3000, d=128, window=300, sink=2, pos0=3100)),
+    ("A1", dict(nh=32, nkvh=8, nq=256, nkv=1200, d=64)),
 ]
 
 
