@@ -99,25 +99,31 @@ def build(verbose: bool = False, extra_flags=None) -> str:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
                                             text=True)))
-    failed = []
-    for src, p in procs:
-        out, err = p.communicate()
-        err = _quiet(err)
-        if p.returncode != 0:
-            failed.append(f"{src}:\n{err}")
-        elif verbose and err.strip():
-            print(err)
-    if failed:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
-    for asm, kernel in asm_checks:
-        check_no_scratch(asm, kernel)
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + _quiet(r.stderr))
-    os.replace(tmp, LIB)
-    os.replace(probe_tmp, PROBE_LIB)
+    try:
+        failed = []
+        for src, p in procs:
+            out, err = p.communicate()
+            err = _quiet(err)
+            if p.returncode != 0:
+                failed.append(f"{src}:\n{err}")
+            elif verbose and err.strip():
+                print(err)
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+        for asm, kernel in asm_checks:
+            check_no_scratch(asm, kernel)
+        cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + _quiet(r.stderr))
+        os.replace(tmp, LIB)
+        os.replace(probe_tmp, PROBE_LIB)
+    finally:
+        # a failed build leaves no partial library behind
+        for leftover in (tmp, probe_tmp):
+            if os.path.exists(leftover):
+                os.remove(leftover)
     return LIB
 
 

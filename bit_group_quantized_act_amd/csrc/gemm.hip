@@ -31,9 +31,11 @@
 //   at two per SIMD (double-buffered partials, weights three stages ahead, three LDS buffers):
 //   the step is a chain of short dependent phases (unpack, operand reads, MFMAs, epilogue)
 //   that other wavefronts cover better than reordering inside one wavefront does.
-//   Epilogue.  At the last k step of a group the VALU converts the group's int32 partials and
-//   accumulates them with one FMA each (the wait for the MFMA results is covered by the other
-//   wavefronts of the SIMD).  The FMA coefficients
+//   Epilogue.  At the last k step of a group the VALU turns the group's int32 partials into
+//   floats and accumulates them with one FMA each (the wait for the MFMA results is covered by
+//   the other wavefronts of the SIMD).  Where the registers allow, the partials start from the
+//   bit pattern of 1.5 * 2^23 rather than zero, so the float is one exact subtraction instead of
+//   a slower conversion (the same value).  The FMA coefficients
 //   xs[row] * sw[col] come from one fp32 outer-product MFMA (v_mfma_f32_32x32x1_2b: block t =
 //   tile t), which lands each coefficient in the lane and register of its partial; the affine
 //   bias term xs*xsum[row] * (bw + 8 sw)[col] is a second outer product accumulated on the
@@ -114,6 +116,9 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     constexpr int SPG = G / 64;                        // k steps per group
     constexpr int GPS = kSteps / SPG;                  // groups per stage
     constexpr int kMB = (FMT == kFmtAffine) ? 4 : 2;   // metadata bytes per channel and group
+    // Partials start from kPartialBias (16 more registers for the start value) except where that
+    // does not fit the register budget (affine with 128-groups) and in the partials variant.
+    constexpr bool kBiased = !PARTIALS && !(FMT == kFmtAffine && G == 128);
     __shared__ __attribute__((aligned(16))) uint8_t lds[kNS][kStageBytes];
 
     const int tid = threadIdx.x;
@@ -228,9 +233,11 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
                 }
             } else {
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    acc[16 * t + e] = fmaf(static_cast<float>(dt[t][e]), coef[16 * t + e],
-                                           acc[16 * t + e]);
+                for (int e = 0; e < 16; ++e) {
+                    const float df = kBiased ? partial_to_float(dt[t][e])
+                                             : static_cast<float>(dt[t][e]);
+                    acc[16 * t + e] = fmaf(df, coef[16 * t + e], acc[16 * t + e]);
+                }
             }
         }
     };
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
         const v4i a01 = *reinterpret_cast<const v4i *>(buf + a_rd[J][1]);
         const v4i a10 = *reinterpret_cast<const v4i *>(buf + a_rd[J][0] + 32 * kSK);
         const v4i a11 = *reinterpret_cast<const v4i *>(buf + a_rd[J][1] + 32 * kSK);
-        const v16i z = {};
+        const v16i z = kBiased ? partial_start() : v16i{};
         v16i &d0 = dt[0];
         v16i &d1 = dt[1];
         d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a00, blo, first ? z : d0, 0, 0, 0);

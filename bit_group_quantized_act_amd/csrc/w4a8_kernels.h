@@ -98,6 +98,24 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
+// The 4-bit GEMM's int8 matrix products start each group's partial from this bit pattern
+// instead of zero.  0x4B400000 is the float 1.5 * 2^23, whose ulp is 1, so for |D| < 2^22 the integer
+// 0x4B400000 + D read as a float is exactly 1.5 * 2^23 + D, and one exact subtraction gives D as
+// a float: the value an int-to-float conversion gives, for a cheaper instruction.  Every GEMM
+// partial stays far inside that range: |code| <= 127 activations times weights of magnitude at
+// most 128 (16 q and codebook entries) over at most 128 k give |D| <= 2,080,768.  (The int8-
+// weight GEMM keeps the conversion: at its register bound the start value's 16 registers spill.)
+constexpr int kPartialBias = 0x4B400000;
+__device__ __forceinline__ v16i partial_start() {
+    v16i z;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = kPartialBias;
+    return z;
+}
+__device__ __forceinline__ float partial_to_float(int biased) {
+    return __builtin_bit_cast(float, biased) - 12582912.0f;
+}
+
 // ---- the activation prepass of one float4 quad
 //
 // Rotation (optional normalized Walsh-Hadamard transform of 128-wide blocks), per-group int8
