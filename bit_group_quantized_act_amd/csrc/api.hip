@@ -304,7 +304,7 @@ w4a8_status w4a8_gemv(const w4a8_layout *L, const void *packed, const int8_t *xq
     if ((s = check_device()) != W4A8_OK) return s;
     if (byte_decoded(L))
         return launched(w4a8::launch_w8(geom_of(L), static_cast<const uint8_t *>(packed), 1, xq,
-                                        xs, y, static_cast<hipStream_t>(stream)),
+                                        xs, xsum, y, static_cast<hipStream_t>(stream)),
                         "int8-weight gemv launch");
     return launched(w4a8::launch_gemv(geom_of(L), static_cast<const uint8_t *>(packed), xq, xs,
                                       xsum, y, nullptr, static_cast<hipStream_t>(stream)),
@@ -326,7 +326,7 @@ w4a8_status w4a8_gemm(const w4a8_layout *L, const void *packed, int32_t m, const
     if ((s = check_device()) != W4A8_OK) return s;
     if (byte_decoded(L))
         return launched(w4a8::launch_w8(geom_of(L), static_cast<const uint8_t *>(packed), m, xq,
-                                        xs, y, static_cast<hipStream_t>(stream)),
+                                        xs, xsum, y, static_cast<hipStream_t>(stream)),
                         "int8-weight gemm launch");
     return launched(w4a8::launch_gemm(geom_of(L), static_cast<const uint8_t *>(packed), m, xq,
                                       xs, xsum, y, nullptr, static_cast<hipStream_t>(stream)),
@@ -366,7 +366,8 @@ w4a8_status w4a8_linear(const w4a8_layout *L, const void *packed, int32_t m, con
     hipError_t e = w4a8::launch_prep(x, m, L->k, L->group, hadamard_block, xq, xs, xsum, st);
     if (e != hipSuccess) return launched(e, "prep launch");
     if (byte_decoded(L))
-        return launched(w4a8::launch_w8(g, pk, m, xq, xs, y, st), "int8-weight linear launch");
+        return launched(w4a8::launch_w8(g, pk, m, xq, xs, xsum, y, st),
+                        "int8-weight linear launch");
     if (m == 1)
         return launched(w4a8::launch_gemv(g, pk, xq, xs, xsum, y, nullptr, st), "gemv launch");
     return launched(w4a8::launch_gemm(g, pk, m, xq, xs, xsum, y, nullptr, st), "gemm launch");
@@ -739,7 +740,7 @@ w4a8_status w4a8_debug_partials(const w4a8_layout *L, const void *packed, int32_
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (byte_decoded(L))
-        return launched(w4a8::launch_w8_partials(g, pk, m, xq, d, st),
+        return launched(w4a8::launch_w8_partials(g, pk, m, xq, xsum, d, st),
                         "int8-weight partials launch");
     if (m == 1)
         return launched(w4a8::launch_gemv(g, pk, xq, nullptr, xsum, nullptr, d, st),

@@ -282,10 +282,10 @@ hipError_t launch_pack_cq2(const Geom &g, const uint8_t *codes, const int8_t *co
 hipError_t launch_pack_bits(const Geom &g, const uint8_t *codes, const int8_t *codebook,
                             uint8_t *packed, hipStream_t stream);
 hipError_t launch_w8(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
-                     const float *xs, float *y, hipStream_t stream);
+                     const float *xs, const int32_t *xsum, float *y, hipStream_t stream);
 // Their exact int32 partials d [m][n][k/group] from the same GEMV (m == 1) or GEMM code.
 hipError_t launch_w8_partials(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
-                              int32_t *d, hipStream_t stream);
+                              const int32_t *xsum, int32_t *d, hipStream_t stream);
 // Their one-row GEMV with the prepass fused in (k <= kFusedMaxK): every workgroup quantizes x
 // into LDS, workgroup 0 also writes xq, xs and xsum.  w8_gemv_workgroups is its grid size; past
 // kFusedMaxW8Workgroups the separate prepass costs less than the repeats (at 2048 workgroups of

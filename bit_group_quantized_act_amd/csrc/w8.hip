@@ -71,7 +71,9 @@ struct FusedPrep {
     }
     // A wavefront's quads are 64 consecutive ones, so a group's G/4 lanes and a rotation block's
     // 32 are aligned runs that are all active or all inactive (k is a multiple of G and of 128).
-    __device__ __forceinline__ void run(const FusedIO &io, int k, int *lxq, float *lxs) {
+    // lxsum (when not null) also receives the group sums
+    __device__ __forceinline__ void run(const FusedIO &io, int k, int *lxq, float *lxs,
+                                        int *lxsum = nullptr) {
         const int lane = threadIdx.x & 63;
 #pragma unroll
         for (int i = 0; i < kFusedQuads; ++i) {
@@ -85,6 +87,7 @@ struct FusedPrep {
                 lxq[q] = codes;
                 const bool leader = (q & (G / 4 - 1)) == 0;
                 if (leader) lxs[q / (G / 4)] = scale;
+                if (leader && lxsum) lxsum[q / (G / 4)] = sum;
                 if (blockIdx.x == 0) {
                     reinterpret_cast<int *>(io.xq)[q] = codes;
                     if (leader) {
@@ -218,11 +221,16 @@ __device__ __forceinline__ int cq2_dword(uint32_t w, int s, uint32_t cb) {
     return static_cast<int>(__builtin_amdgcn_perm(cb, cb, (w >> (2 * s)) & 0x03030303u));
 }
 
+// The four one-bit selectors at bits 8j + sh of a CQ1 bit word as bytes 0 or 1.
+__device__ __forceinline__ uint32_t cq1_bits(uint32_t bw, int sh) {
+    return (bw >> sh) & 0x01010101u;
+}
+
 // The bit-plane formats: four int8 weights whose one-bit selectors sit at bits 8j + sh of the
 // bit word bw (CQ1), or whose low two bits sit at 8j + 2s of the crumb word w and high bit at
 // 8j + sh of bw (CQ3; cb0 holds entries 0-3, cb1 entries 4-7).
 __device__ __forceinline__ int cq1_dword(uint32_t bw, int sh, uint32_t cb) {
-    return static_cast<int>(__builtin_amdgcn_perm(cb, cb, (bw >> sh) & 0x01010101u));
+    return static_cast<int>(__builtin_amdgcn_perm(cb, cb, cq1_bits(bw, sh)));
 }
 __device__ __forceinline__ int cq3_dword(uint32_t w, int s, uint32_t bw, int sh, uint32_t cb0,
                                          uint32_t cb1) {
@@ -339,11 +347,16 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_w8_kernel(const uint8_t *_
 // One row against the bit-plane formats: a workgroup per panel, 8 wavefronts over the 128-k
 // chunks, lane r on panel row r; a chunk is P 16-byte loads per lane and holds 128 / G groups.
 // PARTIALS as for gemv_w8_kernel.
+// CQ1 uses that a two-entry codebook is affine in its selector bit: with entries e0, e1 the
+// weight is e0 + b (e1 - e0), so a group's dot product is e0 * xsum + (e1 - e0) * (the sum of the
+// codes whose bit is set), the same integer.  The masked sums take one dot4 against the bits as
+// 0/1 bytes, without the byte permute that looks the entries up.
 template <int FMT, int G, bool FUSED, bool ROT, bool PARTIALS = false>
 __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t *__restrict__ packed,
                                                                   const Geom geom,
                                                                   const int *__restrict__ xq4,
                                                                   const float *__restrict__ xs,
+                                                                  const int *__restrict__ xsum,
                                                                   float *__restrict__ y, int wpp,
                                                                   const FusedIO io,
                                                                   int *__restrict__ d = nullptr) {
@@ -351,9 +364,11 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
     constexpr int P = planes<FMT>;
     constexpr int GPC = kBitChunk / G;                // groups per chunk (2 or 1)
     constexpr int RING = FMT == kFmtCQ3 ? 2 : 4;      // chunks in flight per wavefront
+    constexpr bool kAffineBit = FMT == kFmtCQ1;
     __shared__ float red[kW8Waves][64];
     __shared__ __attribute__((aligned(16))) int lxq[FUSED ? kFusedMaxK / 4 : 1];
     __shared__ float lxs[FUSED ? kFusedMaxK / 64 : 1];
+    __shared__ int lxsum[(FUSED && kAffineBit) ? kFusedMaxK / 64 : 1];
     FusedPrep<G, ROT> fp;
     if constexpr (FUSED) fp.issue(io, geom.k);
     __builtin_amdgcn_sched_barrier(0);
@@ -378,6 +393,9 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
     } else if (live) {
         cb0 = reinterpret_cast<const uint32_t *>(packed + geom.off_codebook)[row];
     }
+    // CQ1: entry 0 and the step to entry 1
+    const int e0 = static_cast<int8_t>(cb0 & 0xFFu);
+    const int step = static_cast<int>(static_cast<int8_t>((cb0 >> 8) & 0xFFu)) - e0;
     v4i ring[RING][P];
     uint32_t meta[RING];
     auto load = [&](int s, int c) {
@@ -391,15 +409,18 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
     };
 #pragma unroll
     for (int s = 0; s < RING; ++s) load(s, wsub + s * wpp);
-    const int *xsrc;                                  // the row's codes and scales: LDS when fused
-    const float *xssrc;
+    const int *xsrc;                                  // the row's codes, scales and (CQ1) group
+    const float *xssrc;                               // sums: LDS when fused
+    const int *xsumsrc;
     if constexpr (FUSED) {
-        fp.run(io, geom.k, lxq, lxs);
+        fp.run(io, geom.k, lxq, lxs, kAffineBit ? lxsum : nullptr);
         xsrc = lxq;
         xssrc = lxs;
+        xsumsrc = lxsum;
     } else {
         xsrc = xq4;
         xssrc = xs;
+        xsumsrc = xsum;
     }
     float acc = 0.0f;
     for (int c0 = wsub; c0 < kc; c0 += RING * wpp) {
@@ -426,12 +447,15 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
                                 if (FMT == kFmtCQ3)
                                     wv = cq3_dword(static_cast<uint32_t>(ring[s][gi][pb + 2 * h]), e,
                                                    bw, 4 * pb + e, cb0, cb1);
-                                else
-                                    wv = cq1_dword(bw, 4 * pb + e, cb0);
+                                else   // the bits themselves: d4 sums the selected codes
+                                    wv = static_cast<int>(cq1_bits(bw, 4 * pb + e));
                                 d4[e] = __builtin_amdgcn_sdot4(wv, xg[8 * pb + 4 * h + e], d4[e],
                                                                false);
                             }
-                    const int dgi = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+                    int dgi = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+                    // CQ1 with 64-groups: the group's dot product from its masked sum (with
+                    // 128-groups the chunk's two halves are added first, below)
+                    if (kAffineBit && GPC == 2) dgi = e0 * xsumsrc[g] + step * dgi;
                     if (GPC == 2 && PARTIALS) {
                         if (row < geom.n) d[(int64_t)row * ng + g] = dgi;
                     } else if (GPC == 2) {
@@ -441,6 +465,7 @@ __global__ __launch_bounds__(64 * kW8Waves) void gemv_bits_kernel(const uint8_t 
                         dot += dgi;
                     }
                 }
+                if (kAffineBit && GPC == 1) dot = e0 * xsumsrc[c] + step * dot;
                 if (GPC == 1 && PARTIALS) {
                     if (row < geom.n) d[(int64_t)row * ng + c] = dot;
                 } else if (GPC == 1) {
@@ -718,45 +743,47 @@ int gemv_wpp(const Geom &g, int *grid) {
 
 template <int FMT, int G, bool FUSED, bool ROT>
 void gemv_go(const Geom &g, unsigned grid, int wpp, const uint8_t *packed, const int *x4,
-             const float *xs, float *y, const FusedIO &io, hipStream_t stream) {
+             const float *xs, const int *xsum, float *y, const FusedIO &io, hipStream_t stream) {
     if constexpr (bit_plane<FMT>)
         gemv_bits_kernel<FMT, G, FUSED, ROT><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs,
-                                                                                y, wpp, io);
+                                                                                xsum, y, wpp, io);
     else
         gemv_w8_kernel<FMT, G, FUSED, ROT><<<grid, 64 * kW8Waves, 0, stream>>>(packed, g, x4, xs, y,
                                                                               wpp, io);
 }
 
 template <int FMT, bool FUSED, bool ROT>
-void gemv_fmt(const Geom &g, const uint8_t *packed, const int *x4, const float *xs, float *y,
-              const FusedIO &io, hipStream_t stream) {
+void gemv_fmt(const Geom &g, const uint8_t *packed, const int *x4, const float *xs,
+              const int *xsum, float *y, const FusedIO &io, hipStream_t stream) {
     int grid;
     const int wpp = gemv_wpp(g, &grid);
     if (g.group == 64)
-        gemv_go<FMT, 64, FUSED, ROT>(g, static_cast<unsigned>(grid), wpp, packed, x4, xs, y, io, stream);
+        gemv_go<FMT, 64, FUSED, ROT>(g, static_cast<unsigned>(grid), wpp, packed, x4, xs, xsum, y, io,
+                                     stream);
     else
-        gemv_go<FMT, 128, FUSED, ROT>(g, static_cast<unsigned>(grid), wpp, packed, x4, xs, y, io, stream);
+        gemv_go<FMT, 128, FUSED, ROT>(g, static_cast<unsigned>(grid), wpp, packed, x4, xs, xsum, y,
+                                      io, stream);
 }
 
 template <int FMT>
 void gemv_fused_fmt(const Geom &g, const uint8_t *packed, int hadamard, const FusedIO &io,
                     float *y, hipStream_t stream) {
-    if (hadamard == 128) gemv_fmt<FMT, true, true>(g, packed, nullptr, nullptr, y, io, stream);
-    else gemv_fmt<FMT, true, false>(g, packed, nullptr, nullptr, y, io, stream);
+    if (hadamard == 128) gemv_fmt<FMT, true, true>(g, packed, nullptr, nullptr, nullptr, y, io, stream);
+    else gemv_fmt<FMT, true, false>(g, packed, nullptr, nullptr, nullptr, y, io, stream);
 }
 
 // The partials variants: the plain GEMV (m == 1) or the GEMM with their epilogues replaced by a
 // store of the int32 per-group dot products.
 template <int FMT, int G>
-void partials_go(const Geom &g, const uint8_t *packed, int m, const int8_t *xq, int32_t *d,
-                 hipStream_t stream) {
+void partials_go(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
+                 const int32_t *xsum, int32_t *d, hipStream_t stream) {
     if (m == 1) {
         int grid;
         const int wpp = gemv_wpp(g, &grid);
         const int *x4 = reinterpret_cast<const int *>(xq);
         if constexpr (bit_plane<FMT>)
             gemv_bits_kernel<FMT, G, false, false, true><<<grid, 64 * kW8Waves, 0, stream>>>(
-                packed, g, x4, nullptr, nullptr, wpp, FusedIO{}, d);
+                packed, g, x4, nullptr, xsum, nullptr, wpp, FusedIO{}, d);
         else
             gemv_w8_kernel<FMT, G, false, false, true><<<grid, 64 * kW8Waves, 0, stream>>>(
                 packed, g, x4, nullptr, nullptr, wpp, FusedIO{}, d);
@@ -767,17 +794,17 @@ void partials_go(const Geom &g, const uint8_t *packed, int m, const int8_t *xq, 
 }
 
 template <int FMT>
-void partials_fmt(const Geom &g, const uint8_t *packed, int m, const int8_t *xq, int32_t *d,
-                  hipStream_t stream) {
-    if (g.group == 64) partials_go<FMT, 64>(g, packed, m, xq, d, stream);
-    else partials_go<FMT, 128>(g, packed, m, xq, d, stream);
+void partials_fmt(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
+                  const int32_t *xsum, int32_t *d, hipStream_t stream) {
+    if (g.group == 64) partials_go<FMT, 64>(g, packed, m, xq, xsum, d, stream);
+    else partials_go<FMT, 128>(g, packed, m, xq, xsum, d, stream);
 }
 
 template <int FMT>
 hipError_t launch_w8_fmt(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
-                         const float *xs, float *y, hipStream_t stream) {
+                         const float *xs, const int32_t *xsum, float *y, hipStream_t stream) {
     if (m == 1) {
-        gemv_fmt<FMT, false, false>(g, packed, reinterpret_cast<const int *>(xq), xs, y,
+        gemv_fmt<FMT, false, false>(g, packed, reinterpret_cast<const int *>(xq), xs, xsum, y,
                                     FusedIO{}, stream);
         return hipGetLastError();
     }
@@ -789,21 +816,21 @@ hipError_t launch_w8_fmt(const Geom &g, const uint8_t *packed, int m, const int8
 }  // namespace
 
 hipError_t launch_w8(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
-                     const float *xs, float *y, hipStream_t stream) {
+                     const float *xs, const int32_t *xsum, float *y, hipStream_t stream) {
     if (m == 0) return hipSuccess;
-    if (g.fmt == kFmtCQ2) return launch_w8_fmt<kFmtCQ2>(g, packed, m, xq, xs, y, stream);
-    if (g.fmt == kFmtCQ1) return launch_w8_fmt<kFmtCQ1>(g, packed, m, xq, xs, y, stream);
-    if (g.fmt == kFmtCQ3) return launch_w8_fmt<kFmtCQ3>(g, packed, m, xq, xs, y, stream);
-    return launch_w8_fmt<kFmtInt8>(g, packed, m, xq, xs, y, stream);
+    if (g.fmt == kFmtCQ2) return launch_w8_fmt<kFmtCQ2>(g, packed, m, xq, xs, xsum, y, stream);
+    if (g.fmt == kFmtCQ1) return launch_w8_fmt<kFmtCQ1>(g, packed, m, xq, xs, xsum, y, stream);
+    if (g.fmt == kFmtCQ3) return launch_w8_fmt<kFmtCQ3>(g, packed, m, xq, xs, xsum, y, stream);
+    return launch_w8_fmt<kFmtInt8>(g, packed, m, xq, xs, xsum, y, stream);
 }
 
 hipError_t launch_w8_partials(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
-                              int32_t *d, hipStream_t stream) {
+                              const int32_t *xsum, int32_t *d, hipStream_t stream) {
     if (m == 0) return hipSuccess;
-    if (g.fmt == kFmtCQ2) partials_fmt<kFmtCQ2>(g, packed, m, xq, d, stream);
-    else if (g.fmt == kFmtCQ1) partials_fmt<kFmtCQ1>(g, packed, m, xq, d, stream);
-    else if (g.fmt == kFmtCQ3) partials_fmt<kFmtCQ3>(g, packed, m, xq, d, stream);
-    else partials_fmt<kFmtInt8>(g, packed, m, xq, d, stream);
+    if (g.fmt == kFmtCQ2) partials_fmt<kFmtCQ2>(g, packed, m, xq, xsum, d, stream);
+    else if (g.fmt == kFmtCQ1) partials_fmt<kFmtCQ1>(g, packed, m, xq, xsum, d, stream);
+    else if (g.fmt == kFmtCQ3) partials_fmt<kFmtCQ3>(g, packed, m, xq, xsum, d, stream);
+    else partials_fmt<kFmtInt8>(g, packed, m, xq, xsum, d, stream);
     return hipGetLastError();
 }
 

@@ -426,7 +426,9 @@ w4a8_status w4a8_attn_prefill(const w4a8_attn_layout *AL, const void *packed, co
  * the GEMV (m == 1) or the GEMM (m > 1) of the layout's format (the 4-bit formats' kernels, or
  * those of the int8 and CQ1-CQ3 weights), with the fp32 epilogue replaced by a store of D.
  *   xsum  as from w4a8_prep (the AFFINE partial is recovered from the u - 8 codes as
- *         D_u = D_(u-8) + 8 * xsum; the other formats do not read it, but it must be given)
+ *         D_u = D_(u-8) + 8 * xsum; the one-row CQ1 GEMV forms D = e0 * xsum + (e1 - e0) *
+ *         (sum of the codes whose bit is set); the other formats do not read it, but it must
+ *         be given)
  *   d     int32 [m][L->n][k/group]
  * Source: "cactus PR #697", review snippet of the per-group leaf contract.
  */
