@@ -16,6 +16,13 @@
 //   first 16 activation bytes and its high nibbles (k 16..31) with the next 16: two
 //   v_mfma_i32_32x32x32_i8 per tile per 64-wide k step.  Workgroups are numbered so that each
 //   XCD (one L2) gets a contiguous run of tiles, the M tiles of a channel block adjacent.
+//   Split tiles.  A CU's time follows how many tiles it holds, so a last round that gives only
+//   some CUs one more tile costs a large part of a whole round (measured at 128 rows and k 5120:
+//   512 tiles 51.5 us, 544 tiles 63 us, 768 tiles 73 us).
+//   The launcher therefore splits the tiles of such a partial round: each goes to four
+//   workgroups, one per 32-channel group, whose four wavefronts run one k quarter each (one
+//   64-wide step per stage) and add their outputs in LDS in a fixed order.  Small layers (fewer
+//   tiles than CUs) are split whole, which spreads them over four times the CUs.
 //   Stages.  The k range is cut into stages of 256.  A stage's activation rows, the activation
 //   scales (and sums) of its groups and the weight metadata of the workgroup's two panels are
 //   copied from memory straight into one of two LDS stage buffers by buffer loads with an LDS
@@ -26,7 +33,7 @@
 //   it everybody's have.  Weight chunks go to registers one stage ahead.  A load that may fall
 //   outside its buffer carries its whole offset in the range-checked VGPR operand, and every
 //   load past the data is aimed out of range: it returns zeros and touches no memory.
-//   Occupancy.  At most 168 VGPRs and 40 KiB of LDS per workgroup let three workgroups share a
+//   Occupancy.  At most 168 VGPRs and 44 KiB of LDS per workgroup let three workgroups share a
 //   CU (three wavefronts per SIMD).  Measured on MI355X, that beats a register-hungrier layout
 //   at two per SIMD (double-buffered partials, weights three stages ahead, three LDS buffers):
 //   the step is a chain of short dependent phases (unpack, operand reads, MFMAs, epilogue)
@@ -63,7 +70,8 @@ constexpr int kNS = 2;                      // LDS stage buffers
 constexpr int kAStage = BM * kSK;           // activation bytes of a stage (16 KiB)
 constexpr int kXOff = kAStage;              // xs [4 groups][64 rows] fp32, then xsum the same
 constexpr int kMOff = kAStage + 2048;       // weight metadata of the workgroup's two panels
-constexpr int kStageBytes = kAStage + 4096;
+                                            // (a split workgroup: 1 KiB per wavefront)
+constexpr int kStageBytes = kAStage + 6144;
 // The count is exact only while the kernel makes no other vector memory access in the loop: a
 // register spill (scratch loads and stores count too) would break it, so the build rejects any
 // GEMM kernel that uses scratch.
@@ -72,6 +80,9 @@ constexpr int kStageBytes = kAStage + 4096;
 // a wavefront issues between its copies of stage s and the wait at the top of stage s: the
 // weight chunks of stage s.
 constexpr int kVmAfterStage = kSteps;
+// A split workgroup's wavefront runs one k step per stage, so one weight chunk follows the copies.
+constexpr int kVmAfterSplitStage = 1;
+constexpr int kSplit = 4;                   // k quarters of a split workgroup (its wavefronts)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -111,7 +122,7 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
                                                       const float *__restrict__ xs,
                                                       const int *__restrict__ xsum,
                                                       float *__restrict__ y,
-                                                      int *__restrict__ d, int act) {
+                                                      int *__restrict__ d, int act, int nfull) {
     static_assert(!(GLU && PARTIALS), "the gated output has no partials variant");
     constexpr int SPG = G / 64;                        // k steps per group
     constexpr int GPS = kSteps / SPG;                  // groups per stage
@@ -125,14 +136,26 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // Tile of this workgroup.  When the tile count is a multiple of the 8 XCDs, workgroup b runs
-    // on XCD b % 8 and takes tile (b % 8) * (T / 8) + b / 8, so each XCD walks a contiguous run.
+    // Tile of this workgroup.  Workgroups below nfull take whole tiles: when nfull is a multiple
+    // of the 8 XCDs, workgroup b runs on XCD b % 8 and takes tile (b % 8) * (nfull / 8) + b / 8,
+    // so each XCD walks a contiguous run.  Each tile from nfull on is split over four workgroups,
+    // one per 32-channel group of the tile; a split workgroup's four wavefronts take that
+    // channel group over one k quarter each and add their outputs in LDS at the end (fixed
+    // order).  The launcher splits the tiles of a last, partial round of the CUs, which would
+    // otherwise leave a few CUs a whole extra tile.
     const int tiles_m = (m + BM - 1) / BM;
     const int tiles_n = (geom.n_pad + kBN - 1) / kBN;
-    const int ntiles = tiles_m * tiles_n;
+    const bool split = !GLU && static_cast<int>(blockIdx.x) >= nfull;   // workgroup-uniform
     int bid = blockIdx.x;
-    if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+    int cgrp = 0;                                      // split: the tile's channel group
+    if (split) {
+        cgrp = (bid - nfull) % kSplit;
+        bid = nfull + (bid - nfull) / kSplit;
+    } else if ((nfull & 7) == 0) {
+        bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
+    }
     const int mt = bid % tiles_m, nt = bid / tiles_m;
+    const int wcol = split ? cgrp : wave;              // the wavefront's 32-channel group
 
     const int k = geom.k;
     const int ng = k / G;
@@ -140,12 +163,12 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     const int nstages = (k + kSK - 1) / kSK;
     const int m0 = mt * BM;
     const int rows_wg = min(m - m0, BM);
-    const int c0 = nt * kBN + wave * 32;               // first output channel of the wavefront
-    const bool active = c0 < geom.n_pad;               // wave-uniform
+    const int c0 = nt * kBN + wcol * 32;               // first output channel of the wavefront
+    const bool active = c0 < geom.n_pad;               // wave-uniform (workgroup-uniform: split)
     const int half = lane >> 5;
     const int r32 = lane & 31;
-    const int pnl = wave >> 1;                         // the wavefront's panel in the workgroup
-    const int prow = (wave & 1) * 32 + r32;            // the lane's channel row in that panel
+    const int pnl = wcol >> 1;                         // the wavefront's panel in the workgroup
+    const int prow = (wcol & 1) * 32 + r32;            // the lane's channel row in that panel
     // GLU: gate panel nt (wavefronts 0, 1) and the up panel up_pan panels on (2, 3)
     const int up_pan = GLU ? geom.n_pad / (2 * kPanelRows) : 0;
     const int p = GLU ? nt + (pnl ? up_pan : 0) : (active ? c0 / kPanelRows : 0);
@@ -214,18 +237,20 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     const v32f zf = {};
 
     // The epilogue of group g, whose partials are in dt and coefficients in coef.
-    // (PARTIALS: the int32 partials go to d instead, with the affine sums from xbuf)
-    auto finish = [&](int g, const uint8_t *xbuf) __attribute__((always_inline)) {
+    // (PARTIALS: the int32 partials go to d instead, with the affine sums from slot gi of xbuf;
+    // a split workgroup's stage past its quarter stores nothing: live false)
+    auto finish = [&](int g, const uint8_t *xbuf, int gi, bool live, auto BIASED)
+                      __attribute__((always_inline)) {
+        constexpr bool biased = decltype(BIASED)::value;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             if (PARTIALS) {
                 const int col = c0 + r32;
-                const int gi = g % GPS;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int rl = 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
                     const int row = m0 + rl;
-                    if (!active || g >= ng || row >= m || col >= geom.n) continue;
+                    if (!live || !active || g >= ng || row >= m || col >= geom.n) continue;
                     int v = (FMT == kFmtCodebook) ? dt[t][e] : (dt[t][e] >> 4);
                     if (FMT == kFmtAffine)
                         v += 8 * reinterpret_cast<const int *>(xbuf + kXOff + 1024)[gi * 64 + rl];
@@ -234,24 +259,23 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
             } else {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const float df = kBiased ? partial_to_float(dt[t][e])
-                                             : static_cast<float>(dt[t][e]);
+                    const float df = biased ? partial_to_float(dt[t][e])
+                                            : static_cast<float>(dt[t][e]);
                     acc[16 * t + e] = fmaf(df, coef[16 * t + e], acc[16 * t + e]);
                 }
             }
         }
     };
-    // The outer products of group g from a stage buffer's scales and metadata: its coefficients
-    // (into coef) and, affine, its bias term (into acc).
-    auto group_products = [&](int g, const uint8_t *buf) __attribute__((always_inline)) {
-        const int gi = g % GPS;                        // group inside the stage
-        const int bi = g % 4;                          // group inside the metadata block
+    // The outer products of a group from a stage buffer's scales and metadata: its coefficients
+    // (into coef) and, affine, its bias term (into acc).  gi: the group's slot of scales and sums
+    // in the stage; mi: its metadata entry.
+    auto group_products = [&](const uint8_t *buf, int gi, int mi) __attribute__((always_inline)) {
         const float xsv = reinterpret_cast<const float *>(buf + kXOff)[gi * 64 + lane];
         uint32_t meta;
         if (kMB == 2)
-            meta = reinterpret_cast<const uint16_t *>(buf + kMOff)[(pnl * 64 + prow) * 4 + bi];
+            meta = reinterpret_cast<const uint16_t *>(buf + kMOff)[mi];
         else
-            meta = reinterpret_cast<const uint32_t *>(buf + kMOff)[(pnl * 64 + prow) * 4 + bi];
+            meta = reinterpret_cast<const uint32_t *>(buf + kMOff)[mi];
         const float sw = half_bits_to_float(meta & 0xFFFFu);
         const float sw16 = (FMT == kFmtCodebook) ? sw : sw * 0.0625f;
         coef = __builtin_amdgcn_mfma_f32_32x32x1f32(xsv, sw16, zf, 0, 0, 0);
@@ -299,8 +323,8 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
         d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a01, bhi, d0, 0, 0, 0);
         d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a11, bhi, d1, 0, 0, 0);
         if (last) {   // group g's products (its coefficients and affine bias), then its epilogue
-            if (!PARTIALS) group_products(g, buf);
-            finish(g, buf);
+            if (!PARTIALS) group_products(buf, g % GPS, (pnl * 64 + prow) * 4 + g % 4);
+            finish(g, buf, g % GPS, true, std::integral_constant<bool, kBiased>());
         }
     };
 
@@ -321,6 +345,120 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
         __builtin_amdgcn_sched_barrier(0);
         step(BB, std::integral_constant<int, 3>(), st);
     };
+
+    if (split) {
+        // ---- a split workgroup: wavefront w runs k quarter w, [w k/4, (w+1) k/4), of channel group
+        // cgrp, one 64-wide step per stage (k is a multiple of 4 G and of 256, so a quarter is whole
+        // steps and whole groups).  A stage buffer holds the four quarters' steps side by side: k unit
+        // u of a row is unit u % 4 of quarter u / 4, so wavefront w reads the same operand offsets as
+        // step w of a whole stage.  Slot q of the scales and sums holds quarter q's group, and the
+        // metadata region w (1 KiB) the block of wavefront w's group.  Stages past the quarter's end
+        // (the loop runs two at a time) load their weights, scales and metadata out of range: zero
+        // weights with zero coefficients add nothing, and their partials are not stored.
+        const int qsteps = nstages;                        // steps per quarter: k / 256
+        const int sw0 = wave * qsteps;                     // the wavefront's first step in all of k
+        const int gq0 = (lane >> 4) * (ng / kSplit);       // first group of the lane's copy quarter
+        int sa_off[4];
+    #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * wave + 4 * i + (lane >> 4);
+            const int ku = (lane & 15) ^ (row & 15);
+            sa_off[i] = row * k + (ku >> 2) * (k / kSplit) + 16 * (ku & 3);
+        }
+        const int sx_off = (m0 + 4 * (lane & 15)) * 4;
+        const int sm_off = pnl * nblk * 64 * 4 * kMB + lane * 16;
+        auto issue_split = [&](int st) __attribute__((always_inline)) {
+            const uint32_t buf = lds_base + (st % kNS) * kStageBytes;
+            const bool live = st < qsteps;
+    #pragma unroll
+            for (int i = 0; i < 4; ++i)
+                copy16(ra, buf + (16 * wave + 4 * i) * kSK, sa_off[i] + 64 * st);
+            const int gl = gq0 + (64 * st) / G;
+            copy16(rx, buf + kXOff + (x_is_sum ? 1024 : 0), live ? gl * m * 4 + sx_off : kOOB);
+            const int gw = wave * (ng / kSplit) + (64 * st) / G;
+            copy16(rmeta, buf + kMOff + wave * 1024, live ? sm_off + (gw / 4) * 64 * 4 * kMB : kOOB);
+        };
+        auto load_split = [&](int slot, int st) {
+            rb[slot] = ld128(rw, st < qsteps ? w_off + (sw0 + st) * 2048 : kOOB);
+        };
+        int sa_rd[2];
+    #pragma unroll
+        for (int h = 0; h < 2; ++h) sa_rd[h] = r32 * kSK + 16 * ((4 * wave + 2 * half + h) ^ (r32 & 15));
+        // The wavefront's step of stage st, whose LDS buffer and weight slot B = S = st % 2 are
+        // compile-time (two weight chunks in flight).
+        auto split_step = [&](auto BB, auto SS, int st) __attribute__((always_inline)) {
+            constexpr int B = decltype(BB)::value;
+            constexpr int S = decltype(SS)::value;
+            constexpr int sub = S % SPG;                   // (a quarter starts on a group)
+            constexpr bool first = sub == 0;
+            constexpr bool last = sub == SPG - 1;
+            const int g = (sw0 + st) / SPG;
+            const uint8_t *buf = lds[B];
+            v4i blo, bhi;
+            unpack_b<FMT>(rb[S], cb, blo, bhi);
+            load_split(S, st + 2);                         // the slot's step two stages on
+            const v4i a00 = *reinterpret_cast<const v4i *>(buf + sa_rd[0]);
+            const v4i a01 = *reinterpret_cast<const v4i *>(buf + sa_rd[1]);
+            const v4i a10 = *reinterpret_cast<const v4i *>(buf + sa_rd[0] + 32 * kSK);
+            const v4i a11 = *reinterpret_cast<const v4i *>(buf + sa_rd[1] + 32 * kSK);
+            const v16i z = {};                             // (no start-value registers here)
+            v16i &d0 = dt[0];
+            v16i &d1 = dt[1];
+            d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a00, blo, first ? z : d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a10, blo, first ? z : d1, 0, 0, 0);
+            d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a01, bhi, d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a11, bhi, d1, 0, 0, 0);
+            if (last) {
+                if (!PARTIALS) group_products(buf, wave, wave * (1024 / kMB) + prow * 4 + g % 4);
+                finish(g, buf, wave, st < qsteps, std::false_type());
+            }
+        };
+        auto split_stage = [&](auto BB, auto SS, int st) __attribute__((always_inline)) {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm<kVmAfterSplitStage>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            issue_split(st + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            split_step(BB, SS, st);
+        };
+
+        // ---- prologue: copies of stage 0, then the weight chunks of stages 0 and 1
+        issue_split(0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_split(0, 0);
+        load_split(1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int st = 0; st < qsteps; st += 2) {
+            split_stage(std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), st);
+            split_stage(std::integral_constant<int, 1>(), std::integral_constant<int, 1>(), st + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (PARTIALS || !active) return;                 // (workgroup-uniform)
+        // The quarters' outputs meet in LDS: wavefronts 1-3 store theirs, wavefront 0 adds them
+        // to its own in quarter order and stores the tile.
+        __syncthreads();
+        float *xch = reinterpret_cast<float *>(&lds[0][0]);   // [3][32][64] fp32, 24 KiB
+        if (wave > 0) {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) xch[((wave - 1) * 32 + e) * 64 + lane] = acc[e];
+        }
+        __syncthreads();
+        const int col = c0 + r32;
+        if (wave != 0 || col >= geom.n) return;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+                float v = acc[16 * t + e];
+#pragma unroll
+                for (int w = 0; w < kSplit - 1; ++w) v += xch[(w * 32 + 16 * t + e) * 64 + lane];
+                if (row < m) y[(int64_t)row * geom.n + col] = v;
+            }
+        }
+        return;
+    }
 
     // ---- prologue, in the loop's issue order: copies of stage 0, then its weight chunks
     issue_stage(0);
@@ -376,15 +514,41 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     }
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+// Tiles taken whole; the rest (a last, partial round over the CUs, when it is at most three
+// quarters of one) are split over four workgroups each.  The split needs k to be whole 256-wide
+// stages and each quarter whole groups; the gated output never splits.
+int whole_tiles(int tiles, int k, int group, bool glu) {
+    const int cus = device_cus();
+    if (glu || cus <= 0 || k % 256 != 0 || k % (kSplit * group) != 0) return tiles;
+    const int tail = tiles % cus;
+    if (tail == 0 || tail * kSplit > cus * 3) return tiles;
+    return tiles - tail;
+}
+
 // (the gated output has the same tile count: 64 output channels per workgroup from 128 rows)
 template <int FMT, int G, bool PARTIALS, bool GLU>
 hipError_t launch_bm(const Geom &g, int act, const uint8_t *packed, int m, const int8_t *xq,
                      const float *xs, const int32_t *xsum, float *y, int32_t *d,
                      hipStream_t stream) {
-    const unsigned tiles =
-        static_cast<unsigned>(((g.n_pad + kBN - 1) / kBN) * ((m + BM - 1) / BM));
-    gemm_kernel<FMT, G, PARTIALS, GLU><<<tiles, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y,
-                                                                  d, act);
+    const int tiles = ((g.n_pad + kBN - 1) / kBN) * ((m + BM - 1) / BM);
+    const int nfull = whole_tiles(tiles, g.k, G, GLU);
+    const unsigned grid = static_cast<unsigned>(nfull + kSplit * (tiles - nfull));
+    gemm_kernel<FMT, G, PARTIALS, GLU><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y,
+                                                                 d, act, nfull);
     return hipGetLastError();
 }
 

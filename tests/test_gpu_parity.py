@@ -57,6 +57,8 @@ def _run(L, with_partials=True):
 
 # (config, overrides, full_range codes): every format and group, GEMV and GEMM, M tails
 # {1, 2, 63, 65, 127, 130}, N tails {16, 1000, 2049}, several 64-row panels and 128-row M tiles.
+# GEMMs with k a multiple of 256 (and of 512 for 128-groups) and fewer tiles than the CUs run
+# every tile split over four workgroups; the others take whole tiles.
 CASES = [
     ("C1", dict(), False),
     ("C1", dict(n=1000), True),
@@ -82,6 +84,10 @@ CASES = [
     ("C1", dict(m=257, n=200, k=1024, group=128), True),
     ("C3a", dict(m=513, n=130, k=768, group=128), True),
     ("C3a", dict(m=1024, n=384, k=256, group=128), True),
+    # more tiles than CUs: whole tiles and, for the last partial round, tiles split over four
+    # workgroups (one k quarter per wavefront) in the same launch
+    ("C3a", dict(m=64, n=34816, k=512), True),
+    ("C4", dict(m=64, n=33000, k=512), False),
 ]
 
 
