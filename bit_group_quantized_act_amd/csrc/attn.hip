@@ -41,6 +41,11 @@ constexpr int kSlots = 64;      // slots per block
 constexpr int kQT = 32;         // queries per tile
 constexpr int kAW = 8;          // wavefronts per workgroup (two per SIMD)
 constexpr float kNegInf = -__builtin_inff();
+// Scores are kept in base-2 units (the log2(e) factor is folded into the query scale), so every
+// exponential is one hardware 2^x; the statistic m is returned in natural units (times ln 2).
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2 = 0.693147180559945309f;
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int kMergeRegs = 8;  // split states the merge holds in registers at once
 
 // Position of slot jj (0..63) of a block in the MFMA order: subtile t = jj / 32, row r = jj % 32
@@ -116,7 +121,7 @@ struct AttnArgs {
     float *sq;                 // [nh][nq]
     float *o, *m, *l;          // final [nh][nq][d], [nh][nq] (nsplit == 1) ...
     float *work;               // ... or partial states: o [nsplit][nh][nq][d], then (m, l)
-                               // [nsplit][nh][nq][2]
+                               // [nsplit][nh][nq][2] (m in base-2 units)
 };
 
 __device__ __forceinline__ float wave_max32(float v) {          // max with the other lane half
@@ -342,9 +347,10 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
                 const float4 kv = reinterpret_cast<const float4 *>(skl + t * 32 + half * 16)[c];
                 const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (s[t][4 * c + i] == 0.0f)
-                        s[t][4 * c + i] = static_cast<float>(acc[4 * c + i]) * qscale * k4[i];
+                for (int i = 0; i < 4; ++i) {   // (a select: visible slots hold 0, hidden -inf)
+                    const float sc = static_cast<float>(acc[4 * c + i]) * qscale * k4[i];
+                    s[t][4 * c + i] = (s[t][4 * c + i] == 0.0f) ? sc : kNegInf;
+                }
             }
         }
         float mb = kNegInf;
@@ -354,13 +360,13 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
             for (int e = 0; e < 16; ++e) mb = fmaxf(mb, s[t][e]);
         mb = wave_max32(mb);
         const float mnew = fmaxf(mrun, mb);
-        const float alpha = (mrun == kNegInf) ? 0.0f : expf(mrun - mnew);
+        const float alpha = (mrun == kNegInf) ? 0.0f : exp2_hw(mrun - mnew);
         float psum = 0.0f;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                bp.p[t][e] = (s[t][e] == kNegInf) ? 0.0f : expf(s[t][e] - mnew);
+                bp.p[t][e] = (s[t][e] == kNegInf) ? 0.0f : exp2_hw(s[t][e] - mnew);
                 psum += bp.p[t][e];
             }
         lrun = lrun * alpha + psum;
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
             for (int i = 0; i < NG; ++i)
                 qb[i] = *reinterpret_cast<const v4i *>(qtile + col * D +
                                                       16 * ((2 * i + half) ^ ST::kkey(col)));
-            qscale = qlive ? qscl[col] * a.scale : 0.0f;
+            qscale = qlive ? qscl[col] * (a.scale * kLog2e) : 0.0f;
         }
         const int ce = min(b_hi, cb + NB);
         const int bf = cb + ((blane - (cb - b_lo)) % BL + BL) % BL;   // the wavefront's first
@@ -475,14 +481,14 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     }
 
     // merge the states of the BL wavefronts of each group set (fixed order): M = max m_w, each
-    // scaled by e^(m_w - M); the two group sets of DS = 2 hold the same (m, l)
+    // scaled by 2^(m_w - M) (base-2 scores); the two group sets of DS = 2 hold the same (m, l)
     const float lw = lrun + __shfl_xor(lrun, 32, 64);
     if (half == 0) xm[wave][col] = mrun;
     __syncthreads();
     float mall = xm[dpart * BL][col];
 #pragma unroll
     for (int w = 1; w < BL; ++w) mall = fmaxf(mall, xm[dpart * BL + w][col]);
-    const float mine = (mrun == kNegInf) ? 0.0f : expf(mrun - mall);
+    const float mine = (mrun == kNegInf) ? 0.0f : exp2_hw(mrun - mall);
     __syncthreads();
     if (half == 0) xm[wave][col] = lw * mine;
     __syncthreads();
@@ -503,7 +509,7 @@ __global__ __launch_bounds__(64 * kAW) void attn_kernel(const AttnGeom ag,
     const bool stats = dpart == 0 && blane == 0 && half == 0;
     if (a.nsplit == 1) {
         orow = a.o + row * D;
-        if (stats) { a.m[row] = mall; a.l[row] = lsum; }
+        if (stats) { a.m[row] = mall * kLn2; a.l[row] = lsum; }
     } else {
         const int64_t rows = (int64_t)a.nh * a.nq, srow = (int64_t)split * rows + row;
         orow = a.work + srow * D;
@@ -541,7 +547,7 @@ __global__ __launch_bounds__(256) void attn_merge(int nsplit, int64_t rows, int 
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float mall = kNegInf, lsum = 0.0f;
     auto add = [&](float2 st, float4 v) {
-        const float f = (st.x == kNegInf) ? 0.0f : expf(st.x - mall);
+        const float f = (st.x == kNegInf) ? 0.0f : exp2_hw(st.x - mall);
         acc.x += v.x * f;
         acc.y += v.y * f;
         acc.z += v.z * f;
@@ -570,7 +576,7 @@ __global__ __launch_bounds__(256) void attn_merge(int nsplit, int64_t rows, int 
         for (int s = 0; s < nsplit; ++s) add(ml[s * rows + row], part(s));
     }
     reinterpret_cast<float4 *>(o)[t] = acc;
-    if (c4 == 0) { m[row] = mall; l[row] = lsum; }
+    if (c4 == 0) { m[row] = mall * kLn2; l[row] = lsum; }
 }
 
 }  // namespace
