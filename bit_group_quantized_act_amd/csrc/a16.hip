@@ -35,7 +35,9 @@
 //   of a load under full load).  Each group ends with acc += sw * P (one FMA per element; the
 //   lane's column is fixed, so sw is one register); the affine bias of a stage's two groups is
 //   one update on the matrix unit (v_mfma_f32_32x32x2_f32, k slot h = group 2s + h: rows' sums
-//   times the channel's bias).
+//   times the channel's bias).  The tiles of a last, partial round over the CUs are split over
+//   four workgroups (one k quarter per wavefront, outputs added in LDS in a fixed order), as in
+//   the int8 GEMM.
 #include "w4a8_kernels.h"
 
 #include <type_traits>
@@ -266,6 +268,7 @@ __global__ __launch_bounds__(64 * kA16Waves) void gemv_a16_kernel(const uint8_t 
 
 constexpr int kA16BN = 128;                        // channels per workgroup (4 wavefronts x 32)
 constexpr int kA16SK = 128;                        // k per LDS stage (two groups)
+constexpr int kA16Split = 4;                       // k quarters of a split workgroup
 
 // Everything one LDS stage needs from memory, loaded two stages ahead: the rows' halves (four
 // 16-byte units per thread), the lane's weight chunk of each of the stage's two groups, those
@@ -278,12 +281,15 @@ struct StageRegs {
     float sum[2];
 };
 
+// Workgroups from nfull on take a quarter of a tile each: its 32-channel group cgrp over all of
+// k, the four wavefronts one k quarter each (one 32-wide chunk per stage), their outputs added in
+// LDS in quarter order at the end (the launcher splits the tiles of a last, partial round).
 template <int FMT>
 __global__ __launch_bounds__(256, 2) void gemm_a16_kernel(const uint8_t *__restrict__ packed,
                                                           const Geom geom, int m,
                                                           const uint16_t *__restrict__ xh,
                                                           const float *__restrict__ xsf,
-                                                          float *__restrict__ y) {
+                                                          float *__restrict__ y, int nfull) {
     constexpr int MB = (FMT == kFmtAffine) ? 4 : 2;
     __shared__ __attribute__((aligned(16))) v4i lds[2][64 * 16];   // [buf][row][16-byte unit]
     const int tid = threadIdx.x;
@@ -293,12 +299,18 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_kernel(const uint8_t *__restr
     const int r32 = lane & 31;
 
     const int mtiles = (m + 63) / 64;
+    const bool split = static_cast<int>(blockIdx.x) >= nfull;   // workgroup-uniform
     int bid = blockIdx.x;
-    const int nb = gridDim.x;
-    if (nb % 8 == 0) bid = (bid % 8) * (nb / 8) + bid / 8;   // consecutive tiles on one XCD
+    int cgrp = 0;
+    if (split) {
+        cgrp = (bid - nfull) % kA16Split;
+        bid = nfull + (bid - nfull) / kA16Split;
+    } else if (nfull % 8 == 0) {
+        bid = (bid % 8) * (nfull / 8) + bid / 8;            // consecutive tiles on one XCD
+    }
     const int mt = bid % mtiles, nt = bid / mtiles;
     const int m0 = mt * 64;
-    const int c0 = nt * kA16BN + wave * 32;                 // this wavefront's first channel
+    const int c0 = nt * kA16BN + (split ? cgrp : wave) * 32;   // this wavefront's first channel
     const bool wact = c0 < geom.n_pad;                      // panels are whole: all or none
     const int col = c0 + r32;
     const int p = col / kPanelRows, prow = col % kPanelRows;
@@ -353,6 +365,111 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_kernel(const uint8_t *__restr
         for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
     }
     const v16f zero16 = acc[0];
+
+    if (split) {
+        // Stage s of a split workgroup holds chunk s of each k quarter: LDS unit u of a row is
+        // unit u % 4 of quarter u / 4 (32 k each); wavefront q (quarter q) takes its units
+        // 4q .. 4q+3, chunk q k/128 + s of its channel and group (q k/128 + s) / 2, whose
+        // epilogue follows its second chunk (a quarter starts on a group: k % 256 == 0).
+        const int qchunks = k / (kA16Split * 32);            // chunks per quarter
+        const int c_first = wave * qchunks;
+        auto load_split = [&](int s, StageRegs &r) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = i * 16 + (tid >> 4), u = tid & 15;
+                const int kk = (u >> 2) * (k / kA16Split) + s * 32 + 8 * (u & 3);
+                const bool ok = (m0 + rr < m) && s < qchunks;
+                r.a[i] = ld128(rx, ok ? ((m0 + rr) * k + kk) * 2 : kOOB);
+            }
+            const int c = c_first + s;
+            const int g = c >> 1;
+            const bool okc = s < qchunks;
+            r.b[0] = ld128(rc, okc ? (c * 64 + prow) * 16 : kOOB);
+            const int mo = okc ? (((g >> 2) * 64 + prow) * 4 + (g & 3)) * MB : kOOB;
+            r.meta[0] = (MB == 4) ? ld32(rm, mo) : ld16(rm, mo);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int row = m0 + 32 * t + r32;
+                // the bias update's k slot 0 (lanes 0-31) carries the group, slot 1 nothing
+                const bool ok = FMT == kFmtAffine && okc && half == 0 && row < m;
+                r.sum[t] = __builtin_bit_cast(float, ld32(rs, ok ? (g * m + row) * 4 : kOOB));
+            }
+        };
+        StageRegs sring[2];
+        v16f part[2] = {zero16, zero16};
+        load_split(0, sring[0]);
+        if (qchunks > 1) load_split(1, sring[1]);
+        store_a(0, sring[0]);
+        __syncthreads();
+        auto split_stage = [&](auto slot_c, int s) {
+            constexpr int slot = decltype(slot_c)::value;
+            const v4i bch = sring[slot].b[0];
+            const uint32_t meta = sring[slot].meta[0];
+            const float sum[2] = {sring[slot].sum[0], sring[slot].sum[1]};
+            if (s + 2 < qchunks) load_split(s + 2, sring[slot]);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                // lane half h: dword 2 jj + h of the chunk against unit 4 q + 2 jj + h
+                const uint32_t w = static_cast<uint32_t>(bch[2 * jj + half]) ^ 0x88888888u;
+                const v4i bw4 = {static_cast<int>(half_pair<FMT>(w, 0)),
+                                 static_cast<int>(half_pair<FMT>(w, 1)),
+                                 static_cast<int>(half_pair<FMT>(w, 2)),
+                                 static_cast<int>(half_pair<FMT>(w, 3))};
+                const v8h_t bop = __builtin_bit_cast(v8h_t, bw4);
+                const int unit = 4 * wave + 2 * jj + half;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int rr = 32 * t + r32;
+                    const v8h_t aop =
+                        __builtin_bit_cast(v8h_t, lds[slot][rr * 16 + (unit ^ (rr & 7))]);
+                    part[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop, part[t], 0, 0, 0);
+                }
+            }
+            if (s & 1) {                                   // the group's second chunk
+                const float sw = half_bits_to_float(meta & 0xFFFFu);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[t][e] = fmaf(sw, part[t][e], acc[t][e]);
+                    part[t] = zero16;
+                }
+                if (FMT == kFmtAffine) {
+                    const float bw = half == 0 ? half_bits_to_float(meta >> 16) : 0.0f;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(sum[t], bw, acc[t], 0, 0, 0);
+                }
+            }
+            if (s + 1 < qchunks) store_a(slot ^ 1, sring[slot ^ 1]);
+            __syncthreads();
+        };
+        for (int s = 0; s < qchunks; s += 2) {
+            split_stage(std::integral_constant<int, 0>{}, s);
+            split_stage(std::integral_constant<int, 1>{}, s + 1);
+        }
+        if (!wact) return;                                 // (workgroup-uniform)
+        float *xch = reinterpret_cast<float *>(&lds[0][0]);   // [3][32][64] fp32, 24 KiB
+        if (wave > 0) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) xch[((wave - 1) * 32 + 16 * t + e) * 64 + lane] = acc[t][e];
+        }
+        __syncthreads();
+        if (wave != 0 || col >= geom.n) return;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+                float v = acc[t][e];
+#pragma unroll
+                for (int w = 0; w < kA16Split - 1; ++w) v += xch[(w * 32 + 16 * t + e) * 64 + lane];
+                if (row < m) y[(int64_t)row * geom.n + col] = v;
+            }
+        }
+        return;
+    }
 
     // stage s reads LDS buffer s & 1 and its loads sit in ring slot s & 1; at stage s the slot
     // is refilled with stage s + 2, and at its end stage s + 1's halves go to the other buffer
@@ -449,11 +566,13 @@ hipError_t launch_linear_a16(const Geom &g, const uint8_t *packed, int m, const 
                 packed, g, xw, xsf, y, nullptr, nullptr, nullptr);
         return hipGetLastError();
     }
-    const unsigned grid = static_cast<unsigned>(((m + 63) / 64) * ((g.n_pad + kA16BN - 1) / kA16BN));
+    const int tiles = ((m + 63) / 64) * ((g.n_pad + kA16BN - 1) / kA16BN);
+    const int nfull = (g.k % (kA16Split * kGroupA16) == 0) ? whole_tiles(tiles) : tiles;
+    const unsigned grid = static_cast<unsigned>(nfull + kA16Split * (tiles - nfull));
     if (g.fmt == kFmtAffine)
-        gemm_a16_kernel<kFmtAffine><<<grid, 256, 0, stream>>>(packed, g, m, xh, xsf, y);
+        gemm_a16_kernel<kFmtAffine><<<grid, 256, 0, stream>>>(packed, g, m, xh, xsf, y, nfull);
     else
-        gemm_a16_kernel<kFmtSym><<<grid, 256, 0, stream>>>(packed, g, m, xh, xsf, y);
+        gemm_a16_kernel<kFmtSym><<<grid, 256, 0, stream>>>(packed, g, m, xh, xsf, y, nfull);
     return hipGetLastError();
 }
 

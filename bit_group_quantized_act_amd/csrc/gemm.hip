@@ -514,29 +514,11 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     }
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-    static int cus[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cus[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        cus[dev] = v;
-    }
-    return cus[dev];
-}
-
-// Tiles taken whole; the rest (a last, partial round over the CUs, when it is at most three
-// quarters of one) are split over four workgroups each.  The split needs k to be whole 256-wide
-// stages and each quarter whole groups; the gated output never splits.
-int whole_tiles(int tiles, int k, int group, bool glu) {
-    const int cus = device_cus();
-    if (glu || cus <= 0 || k % 256 != 0 || k % (kSplit * group) != 0) return tiles;
-    const int tail = tiles % cus;
-    if (tail == 0 || tail * kSplit > cus * 3) return tiles;
-    return tiles - tail;
+// The split needs k to be whole 256-wide stages and each quarter whole groups; the gated
+// output never splits.
+int gemm_whole_tiles(int tiles, int k, int group, bool glu) {
+    if (glu || k % 256 != 0 || k % (kSplit * group) != 0) return tiles;
+    return whole_tiles(tiles);
 }
 
 // (the gated output has the same tile count: 64 output channels per workgroup from 128 rows)
@@ -545,7 +527,7 @@ hipError_t launch_bm(const Geom &g, int act, const uint8_t *packed, int m, const
                      const float *xs, const int32_t *xsum, float *y, int32_t *d,
                      hipStream_t stream) {
     const int tiles = ((g.n_pad + kBN - 1) / kBN) * ((m + BM - 1) / BM);
-    const int nfull = whole_tiles(tiles, g.k, G, GLU);
+    const int nfull = gemm_whole_tiles(tiles, g.k, G, GLU);
     const unsigned grid = static_cast<unsigned>(nfull + kSplit * (tiles - nfull));
     gemm_kernel<FMT, G, PARTIALS, GLU><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y,
                                                                  d, act, nfull);
@@ -577,6 +559,27 @@ hipError_t launch_f(const Geom &g, int act, const uint8_t *packed, int m, const 
 }
 
 }  // namespace
+
+int device_cus() {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+int whole_tiles(int tiles) {
+    const int cus = device_cus();
+    if (cus <= 0) return tiles;
+    const int tail = tiles % cus;
+    if (tail == 0 || tail * 4 > cus * 3) return tiles;
+    return tiles - tail;
+}
 
 hipError_t launch_gemm(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
                        const float *xs, const int32_t *xsum, float *y, int32_t *d,

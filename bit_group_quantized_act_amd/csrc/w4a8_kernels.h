@@ -223,6 +223,13 @@ constexpr int kFusedQuadsPerLane = 8;   // activation quads one lane of the fuse
 hipError_t launch_gemv_fused(const Geom &g, const uint8_t *packed, const float *x, int hadamard,
                              int8_t *xq, float *xs, int32_t *xsum, float *y, hipStream_t stream);
 
+// Compute units of the current device (cached per device; 0 if the query fails).
+int device_cus();
+// Split-tile policy of the GEMMs: the number of tiles taken whole by one workgroup each; the rest
+// (the tiles of a last, partial round over the CUs, when that round fills at most three quarters
+// of them) go to four workgroups each, one k quarter per wavefront.  A CU's time follows how
+// many tiles it holds, so such a round would otherwise cost nearly as much as a full one.
+int whole_tiles(int tiles);
 hipError_t launch_gemm(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
                        const float *xs, const int32_t *xsum, float *y, int32_t *d,
                        hipStream_t stream);

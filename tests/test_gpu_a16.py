@@ -61,7 +61,8 @@ def _oracle(L, cols=None):
 
 
 # one row (GEMV) and several (GEMM): ragged n (panel padding, a half-empty 128-channel tile),
-# an odd group count (the last LDS stage holds one group), one group, ragged m tiles
+# an odd group count (the last LDS stage holds one group), one group, ragged m tiles; GEMMs with
+# k a multiple of 256 and fewer tiles than the CUs run every tile split over four workgroups
 CASES = [
     ("C2a", dict(n=1000, k=2048)),
     ("C3a", dict(m=1, n=640, k=640)),
@@ -75,6 +76,8 @@ CASES = [
     ("C2a", dict(m=63, n=640, k=2048)),
     ("C5b", dict(m=64, n=1024, k=1536)),
     ("C3a", dict(m=3, n=64, k=64)),
+    # more tiles than CUs: whole tiles and split tiles (one k quarter per wavefront) in one launch
+    ("C3a", dict(m=64, n=34816, k=512)),
 ]
 
 
