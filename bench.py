@@ -89,9 +89,9 @@ KERNEL_SOURCES = {
     "gemm": ["gemm.hip", "w4a8_kernels.h"],
 }
 TRAFFIC = {
-    "C5a": dict(kernel="gemv", source_sha="c40a12f6a10fb88e", fetch_kib=104503.41,
+    "C5a": dict(kernel="gemv", source_sha="67281c996dacfddd", fetch_kib=104503.43,
                 write_kib=1025.6875, fetch_factor=1.99979, write_factor=1.0),
-    "C3a": dict(kernel="gemm", source_sha="a1bd6050716ceda3", fetch_kib=53360.69,
+    "C3a": dict(kernel="gemm", source_sha="3a840858921469bf", fetch_kib=56123.66,
                 write_kib=17408.0000, fetch_factor=1.99979, write_factor=1.0),
 }
 
