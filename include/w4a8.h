@@ -202,9 +202,12 @@ w4a8_status w4a8_gemv(const w4a8_layout *L, const void *packed, const int8_t *xq
  *   xq int8 [m][k], xs fp32 [k/group][m], xsum int32 [k/group][m] from w4a8_prep
  *   y  fp32 [m][L->n]
  * m == 0 is a no-op (xq, xs, xsum and y may then be NULL).  W4A8_ERR_UNSUPPORTED when
- * m * (k/group + 16) * 4 bytes exceed 2^31 - 16.  Source: "cactus PR #697", section
- * "Quantized matmul" (fused GEMM, M>1, raw int32 partials rescaled per tile); "geistlib issue
- * #500" (native int8 GEMM for prefill).
+ * m * (k/group + 16) * 4 bytes exceed 2^31 - 16.  The int32 group partials are exact; the fp32
+ * sum over groups has a fixed order for given shapes and device (repeated calls give the same
+ * bits), but tiles of a last, partial round over the device's CUs add their k quarters
+ * separately, so the order (and the last bits) can depend on the CU count and on n and m.
+ * Source: "cactus PR #697", section "Quantized matmul" (fused GEMM, M>1, raw int32 partials
+ * rescaled per tile); "geistlib issue #500" (native int8 GEMM for prefill).
  */
 w4a8_status w4a8_gemm(const w4a8_layout *L, const void *packed, int32_t m, const int8_t *xq,
                       const float *xs, const int32_t *xsum, float *y, void *stream);
