@@ -149,8 +149,24 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     int bid = blockIdx.x;
     int cgrp = 0;                                      // split: the tile's channel group
     if (split) {
-        cgrp = (bid - nfull) % kSplit;
-        bid = nfull + (bid - nfull) / kSplit;
+        // Part p of the split tiles.  Workgroup b runs on XCD b % 8 (nfull is a multiple of 8),
+        // so the parts of one channel group of one channel block (its row tiles, whose weights
+        // are the same) are placed 8 apart, on one XCD: for each run of 8 (channel block,
+        // channel group) units, the parts of row tile mt are parts 8 mt .. 8 mt + 7 of the run.
+        // That needs the tail to be whole channel blocks (tiles_m a power of two) and a whole
+        // number of runs; otherwise part p is channel group p % 4 of tile p / 4.
+        const int part = bid - nfull;
+        const int units = (tiles_m * tiles_n - nfull) / tiles_m * kSplit;   // tail units
+        const int run = 8 * tiles_m;                   // parts per run of 8 units
+        if ((tiles_m & (tiles_m - 1)) == 0 && part < (units / 8) * run) {
+            const int u = (part / run) * 8 + part % 8;
+            const int mtp = (part % run) / 8;
+            cgrp = u % kSplit;
+            bid = nfull + (u / kSplit) * tiles_m + mtp;
+        } else {
+            cgrp = part % kSplit;
+            bid = nfull + part / kSplit;
+        }
     } else if ((nfull & 7) == 0) {
         bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
     }
