@@ -22,7 +22,9 @@
 //   The launcher therefore splits the tiles of such a partial round: each goes to four
 //   workgroups, one per 32-channel group, whose four wavefronts run one k quarter each (one
 //   64-wide step per stage) and add their outputs in LDS in a fixed order.  Small layers (fewer
-//   tiles than CUs) are split whole, which spreads them over four times the CUs.
+//   tiles than CUs) are split whole, which spreads them over four times the CUs.  A gated tile
+//   splits in two (32 output channels each): wavefronts 0, 1 take the gate panel over the two k
+//   halves, 2, 3 the up panel, and act(gate) * up is formed after the halves are added.
 //   Stages.  The k range is cut into stages of 256.  A stage's activation rows, the activation
 //   scales (and sums) of its groups and the weight metadata of the workgroup's two panels are
 //   copied from memory straight into one of two LDS stage buffers by buffer loads with an LDS
@@ -138,14 +140,17 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
 
     // Tile of this workgroup.  Workgroups below nfull take whole tiles: when nfull is a multiple
     // of the 8 XCDs, workgroup b runs on XCD b % 8 and takes tile (b % 8) * (nfull / 8) + b / 8,
-    // so each XCD walks a contiguous run.  Each tile from nfull on is split over four workgroups,
-    // one per 32-channel group of the tile; a split workgroup's four wavefronts take that
-    // channel group over one k quarter each and add their outputs in LDS at the end (fixed
-    // order).  The launcher splits the tiles of a last, partial round of the CUs, which would
-    // otherwise leave a few CUs a whole extra tile.
+    // so each XCD walks a contiguous run.  Each tile from nfull on is split over four workgroups
+    // (two, gated), one per 32-channel group of the tile; a split workgroup's four wavefronts
+    // take that channel group over one k quarter each (gated: gate and up over one k half each)
+    // and add their outputs in LDS at the end (fixed order).  The launcher splits the tiles of a
+    // last, partial round of the CUs, which would otherwise leave a few CUs a whole extra tile.
     const int tiles_m = (m + BM - 1) / BM;
     const int tiles_n = (geom.n_pad + kBN - 1) / kBN;
-    const bool split = !GLU && static_cast<int>(blockIdx.x) >= nfull;   // workgroup-uniform
+    // workgroups per split tile: four (one per 32-channel group); two for the gated output (one
+    // per 32 output channels, whose gate and up tiles its wavefronts share)
+    constexpr int kParts = GLU ? 2 : kSplit;
+    const bool split = static_cast<int>(blockIdx.x) >= nfull;   // workgroup-uniform
     int bid = blockIdx.x;
     int cgrp = 0;                                      // split: the tile's channel group
     if (split) {
@@ -156,22 +161,23 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
         // That needs the tail to be whole channel blocks (tiles_m a power of two) and a whole
         // number of runs; otherwise part p is channel group p % 4 of tile p / 4.
         const int part = bid - nfull;
-        const int units = (tiles_m * tiles_n - nfull) / tiles_m * kSplit;   // tail units
+        const int units = (tiles_m * tiles_n - nfull) / tiles_m * kParts;   // tail units
         const int run = 8 * tiles_m;                   // parts per run of 8 units
         if ((tiles_m & (tiles_m - 1)) == 0 && part < (units / 8) * run) {
             const int u = (part / run) * 8 + part % 8;
             const int mtp = (part % run) / 8;
-            cgrp = u % kSplit;
-            bid = nfull + (u / kSplit) * tiles_m + mtp;
+            cgrp = u % kParts;
+            bid = nfull + (u / kParts) * tiles_m + mtp;
         } else {
-            cgrp = part % kSplit;
-            bid = nfull + part / kSplit;
+            cgrp = part % kParts;
+            bid = nfull + part / kParts;
         }
     } else if ((nfull & 7) == 0) {
         bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
     }
     const int mt = bid % tiles_m, nt = bid / tiles_m;
-    const int wcol = split ? cgrp : wave;              // the wavefront's 32-channel group
+    // the wavefront's 32-channel group (gated: bit 1 the gate or up panel, bit 0 the group)
+    const int wcol = !split ? wave : (GLU ? ((wave & 2) | cgrp) : cgrp);
 
     const int k = geom.k;
     const int ng = k / G;
@@ -363,35 +369,43 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     };
 
     if (split) {
-        // ---- a split workgroup: wavefront w runs k quarter w, [w k/4, (w+1) k/4), of channel group
-        // cgrp, one 64-wide step per stage (k is a multiple of 4 G and of 256, so a quarter is whole
-        // steps and whole groups).  A stage buffer holds the four quarters' steps side by side: k unit
-        // u of a row is unit u % 4 of quarter u / 4, so wavefront w reads the same operand offsets as
-        // step w of a whole stage.  Slot q of the scales and sums holds quarter q's group, and the
-        // metadata region w (1 KiB) the block of wavefront w's group.  Stages past the quarter's end
-        // (the loop runs two at a time) load their weights, scales and metadata out of range: zero
-        // weights with zero coefficients add nothing, and their partials are not stored.
-        const int qsteps = nstages;                        // steps per quarter: k / 256
-        const int sw0 = wave * qsteps;                     // the wavefront's first step in all of k
-        const int gq0 = (lane >> 4) * (ng / kSplit);       // first group of the lane's copy quarter
+        // ---- a split workgroup: k is cut into NSL slices (quarters; halves for the gated output,
+        // whose wavefronts 0, 1 take the gate panel and 2, 3 the up panel of the same channels),
+        // and wavefront w runs slice w % NSL of channel group cgrp, one 64-wide step per stage (k
+        // is a multiple of NSL G and of 256, so a slice is whole steps and whole groups).  A stage
+        // buffer holds the slices' steps side by side: k unit u of a row is unit u % 4 of slice
+        // u / 4 (slices past NSL are left empty), so wavefront w reads the same operand offsets as
+        // step w % NSL of a whole stage.  Slot q of the scales and sums holds slice q's group, and
+        // the metadata region w (1 KiB) the block of wavefront w's group in its panel.  Stages
+        // past the slice's end (the loop runs two at a time) load their weights, scales and
+        // metadata out of range: zero weights with zero coefficients add nothing, and their
+        // partials are not stored.
+        constexpr int NSL = GLU ? 2 : kSplit;
+        const int slice = wave % NSL;
+        const int qsteps = k / (64 * NSL);                 // steps per slice
+        const int sw0 = slice * qsteps;                    // the wavefront's first step in all of k
+        const int sq = lane >> 4;                          // the lane's copy slice (>= NSL: empty)
+        const int gq0 = sq * (ng / NSL);                   // first group of the lane's copy slice
         int sa_off[4];
     #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * wave + 4 * i + (lane >> 4);
             const int ku = (lane & 15) ^ (row & 15);
-            sa_off[i] = row * k + (ku >> 2) * (k / kSplit) + 16 * (ku & 3);
+            sa_off[i] = (ku >> 2) < NSL ? row * k + (ku >> 2) * (k / NSL) + 16 * (ku & 3) : kOOB;
         }
         const int sx_off = (m0 + 4 * (lane & 15)) * 4;
-        const int sm_off = pnl * nblk * 64 * 4 * kMB + lane * 16;
+        const int sm_off = pnl * pstep * nblk * 64 * 4 * kMB + lane * 16;
         auto issue_split = [&](int st) __attribute__((always_inline)) {
             const uint32_t buf = lds_base + (st % kNS) * kStageBytes;
             const bool live = st < qsteps;
     #pragma unroll
             for (int i = 0; i < 4; ++i)
-                copy16(ra, buf + (16 * wave + 4 * i) * kSK, sa_off[i] + 64 * st);
+                copy16(ra, buf + (16 * wave + 4 * i) * kSK,
+                       sa_off[i] == kOOB ? kOOB : sa_off[i] + 64 * st);
             const int gl = gq0 + (64 * st) / G;
-            copy16(rx, buf + kXOff + (x_is_sum ? 1024 : 0), live ? gl * m * 4 + sx_off : kOOB);
-            const int gw = wave * (ng / kSplit) + (64 * st) / G;
+            copy16(rx, buf + kXOff + (x_is_sum ? 1024 : 0),
+                   live && sq < NSL ? gl * m * 4 + sx_off : kOOB);
+            const int gw = slice * (ng / NSL) + (64 * st) / G;
             copy16(rmeta, buf + kMOff + wave * 1024, live ? sm_off + (gw / 4) * 64 * 4 * kMB : kOOB);
         };
         auto load_split = [&](int slot, int st) {
@@ -399,13 +413,13 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
         };
         int sa_rd[2];
     #pragma unroll
-        for (int h = 0; h < 2; ++h) sa_rd[h] = r32 * kSK + 16 * ((4 * wave + 2 * half + h) ^ (r32 & 15));
+        for (int h = 0; h < 2; ++h) sa_rd[h] = r32 * kSK + 16 * ((4 * slice + 2 * half + h) ^ (r32 & 15));
         // The wavefront's step of stage st, whose LDS buffer and weight slot B = S = st % 2 are
         // compile-time (two weight chunks in flight).
         auto split_step = [&](auto BB, auto SS, int st) __attribute__((always_inline)) {
             constexpr int B = decltype(BB)::value;
             constexpr int S = decltype(SS)::value;
-            constexpr int sub = S % SPG;                   // (a quarter starts on a group)
+            constexpr int sub = S % SPG;                   // (a slice starts on a group)
             constexpr bool first = sub == 0;
             constexpr bool last = sub == SPG - 1;
             const int g = (sw0 + st) / SPG;
@@ -425,8 +439,8 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
             d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a01, bhi, d0, 0, 0, 0);
             d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a11, bhi, d1, 0, 0, 0);
             if (last) {
-                if (!PARTIALS) group_products(buf, wave, wave * (1024 / kMB) + prow * 4 + g % 4);
-                finish(g, buf, wave, st < qsteps, std::false_type());
+                if (!PARTIALS) group_products(buf, slice, wave * (1024 / kMB) + prow * 4 + g % 4);
+                finish(g, buf, slice, st < qsteps, std::false_type());
             }
         };
         auto split_stage = [&](auto BB, auto SS, int st) __attribute__((always_inline)) {
@@ -451,8 +465,9 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
         }
         __builtin_amdgcn_sched_barrier(0);
         if (PARTIALS || !active) return;                 // (workgroup-uniform)
-        // The quarters' outputs meet in LDS: wavefronts 1-3 store theirs, wavefront 0 adds them
-        // to its own in quarter order and stores the tile.
+        // The slices' outputs meet in LDS: wavefronts 1-3 store theirs, wavefront 0 adds them
+        // to its own in slice order and stores the tile (gated: gate = wavefronts 0 + 1, up =
+        // 2 + 3, then act(gate) * up).
         __syncthreads();
         float *xch = reinterpret_cast<float *>(&lds[0][0]);   // [3][32][64] fp32, 24 KiB
         if (wave > 0) {
@@ -460,6 +475,23 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
             for (int e = 0; e < 32; ++e) xch[((wave - 1) * 32 + e) * 64 + lane] = acc[e];
         }
         __syncthreads();
+        if (GLU) {
+            if (wave != 0) return;
+            const int f_n = geom.n / 2;
+            const int colz = nt * kPanelRows + prow;       // output channel, < F
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int i = 16 * t + e;
+                    const int row = m0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+                    const float gate = acc[i] + xch[i * 64 + lane];
+                    const float up = xch[(32 + i) * 64 + lane] + xch[(64 + i) * 64 + lane];
+                    if (row < m) y[(int64_t)row * f_n + colz] = act_apply(act, gate) * up;
+                }
+            }
+            return;
+        }
         const int col = c0 + r32;
         if (wave != 0 || col >= geom.n) return;
 #pragma unroll
@@ -530,10 +562,9 @@ __global__ __launch_bounds__(256, 3) void gemm_kernel(const uint8_t *__restrict_
     }
 }
 
-// The split needs k to be whole 256-wide stages and each quarter whole groups; the gated
-// output never splits.
+// The split needs k to be whole 256-wide stages and each quarter (each half, gated) whole groups.
 int gemm_whole_tiles(int tiles, int k, int group, bool glu) {
-    if (glu || k % 256 != 0 || k % (kSplit * group) != 0) return tiles;
+    if (k % 256 != 0 || k % ((glu ? 2 : kSplit) * group) != 0) return tiles;
     return whole_tiles(tiles);
 }
 
@@ -544,7 +575,7 @@ hipError_t launch_bm(const Geom &g, int act, const uint8_t *packed, int m, const
                      hipStream_t stream) {
     const int tiles = ((g.n_pad + kBN - 1) / kBN) * ((m + BM - 1) / BM);
     const int nfull = gemm_whole_tiles(tiles, g.k, G, GLU);
-    const unsigned grid = static_cast<unsigned>(nfull + kSplit * (tiles - nfull));
+    const unsigned grid = static_cast<unsigned>(nfull + (GLU ? 2 : kSplit) * (tiles - nfull));
     gemm_kernel<FMT, G, PARTIALS, GLU><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, xsum, y,
                                                                  d, act, nfull);
     return hipGetLastError();

@@ -82,6 +82,8 @@ GLU_CASES = [
     ("C4", dict(m=200, n=384, k=1536), GT),
     ("C5b", dict(m=64, n=512, k=1536), GE),
     ("C1", dict(m=3, n=128, k=1024, group=128), S),
+    # more tiles than CUs: whole gated tiles and split ones (gate and up halves of k) in one launch
+    ("C3a", dict(m=64, n=34816, k=512), GE),
 ]
 
 
