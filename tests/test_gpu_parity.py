@@ -88,6 +88,11 @@ CASES = [
     # workgroups (one k quarter per wavefront) in the same launch
     ("C3a", dict(m=64, n=34816, k=512), True),
     ("C4", dict(m=64, n=33000, k=512), False),
+    # wide layers, few rows: 512 tiles (two whole rounds on 256 CUs), 516 tiles (a tail of four
+    # split tiles, a last row block of 2 rows), 513 tiles (one split tile, a ragged channel tile)
+    ("C5b", dict(m=3, n=65536, k=256), False),
+    ("C3a", dict(m=130, n=22016, k=256), True),
+    ("C4", dict(m=2, n=65600, k=512), False),
 ]
 
 
