@@ -323,7 +323,13 @@ hipError_t launch_wk(const Geom &g, int act, const uint8_t *packed, const float 
 template <int FMT, int G, bool PARTIALS, bool FUSED, bool ROT, bool GLU>
 hipError_t launch_w(const Geom &g, int act, const uint8_t *packed, const float *x, int8_t *xq,
                     float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
-    // W = 8 once there are 6 metadata blocks (some wavefronts may own none), else 4
+    // W = 8 once there are 6 metadata blocks (some wavefronts may own none), else 4.  The fused
+    // kernel at exactly 6 blocks takes W = 6, one block per wavefront, so that every wavefront
+    // quantizes and loads (the 262144-row head at K = 1536: 33.6 -> 33.0 us; the plain kernel
+    // measured no faster with 6)
+    if (FUSED && (g.k / G + 3) / 4 == 6)
+        return launch_wk<FMT, G, 6, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y,
+                                                              d, stream);
     if ((g.k / G + 3) / 4 >= 6)
         return launch_wk<FMT, G, 8, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y,
                                                               d, stream);

@@ -76,6 +76,7 @@ GLU_CASES = [
     ("C1", dict(n=256), S),
     ("C2a", dict(n=640, k=4096), GT),
     ("C4", dict(m=1, n=384, k=1536), GE),
+    ("C1", dict(n=640, k=1536), S),               # six metadata blocks: six wavefronts
     ("C3a", dict(m=1, n=1280, k=640), S),
     ("C1", dict(n=128, k=16448), GT),
     ("C3a", dict(m=65, n=1280, k=1280), S),

@@ -143,6 +143,11 @@ LINEAR_CASES = [
     ("C3a", dict(m=1, n=200, k=640), True),
     ("C4", dict(m=1, n=320, k=768), False),
     ("C4", dict(m=1, n=130, k=1536), True),
+    # fused at six metadata blocks (six wavefronts, one block each): 24 groups of 64, 22 groups
+    # (a last block of two), 24 groups of 128 with rotation
+    ("C1", dict(n=1000, k=1536), True),
+    ("C3a", dict(m=1, n=600, k=1408), True),
+    ("C4", dict(m=1, n=200, k=3072), True),
     ("C2a", dict(n=320, k=4096), True),           # fused, 2 activation quads per lane
     ("C4", dict(m=1, n=130, k=8192), True),        # fused with rotation, 4 quads per lane
     ("C1", dict(n=192, k=16384), True),            # fused at its k bound, 8 quads per lane
