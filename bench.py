@@ -53,10 +53,12 @@ against 1024 cached slots.  value = int8 operations of the two products over the
 (query, slot) pairs per second, against the 5.0 POP/s dense int8 MFMA peak.
 
 --argmax CAP times the greedy tail of a vocabulary head instead (one row; w4a8_lm_head_argmax:
-the prepass, the GEMV that also soft-caps the logits with CAP (0: no cap) and stores each
-64-row panel's largest key, and a one-workgroup reduction of those keys into the token).  The
-timed "kernel" is w4a8_gemv_argmax on prepared activations: the GEMV and the reduction
-together, with the plain GEMV's algorithmic bytes plus the keys (written and read) and the token.
+the GEMV that also soft-caps the logits with CAP (0: no cap) and stores each 64-row panel's
+largest key, with the prepass fused into it where w4a8_linear fuses it, else a prepass kernel
+before it, and a one-workgroup reduction of those keys into the token).  The timed "kernel" is
+the GEMV and the reduction together (with the prepass where it is fused in, else
+w4a8_gemv_argmax on prepared activations), with the GEMV's algorithmic bytes plus the keys
+(written and read) and the token.
 """
 from __future__ import annotations
 
@@ -302,7 +304,7 @@ def workload_name(cfg, glu=None, cap=None, a16=False):
                 + ("prepass (X as half, fp32 group sums) fused into the GEMV" if one else
                    f"prepass writing X as half and its fp32 group sums + "
                    f"{'GEMV' if cfg.m == 1 else 'GEMM'}") + " per step)")
-    how = ("prepass fused into the GEMV" if fused and cap is None else
+    how = ("prepass fused into the GEMV" if fused else
            "prepass + GEMV" if cfg.m == 1 else "prepass + GEMM")
     gated = "" if glu is None else f", gated output {glu}(gate)*up with F={cfg.n // 2}"
     tail = "" if cap is None else (f", greedy tail: logits soft-capped at {cap:g} and their "
@@ -373,8 +375,6 @@ class LayerBench:
         self.cap = cap = args.argmax if variants else None
         self.a16 = a16 = args.a16 and variants
         self.glu = args.glu if variants else None
-        if cap is not None:
-            fused = False                                  # the tail runs in the two-kernel path
         alg_bytes = synth.algorithmic_bytes(cfg, fused_prep=fused)
         # fp16 activations at one row (k <= 16384, at most 2048 panels): w4a8_linear_a16 is one
         # kernel with the prepass fused in
@@ -418,6 +418,10 @@ class LayerBench:
             w.linear_a16(lay, pk, x, out=y, prep_out=(self.xh16, self.xsf16))
         elif self.a16:
             w.gemm_a16(lay, pk, self.xh16, self.xsf16, out=y)
+        elif self.cap is not None and self.fused:
+            w.lm_head_argmax(lay, pk, x, self.cap, self.cfg.hadamard,
+                             out=(y[0], self.token, self.tval), work=self.work,
+                             prep_out=(xq, xs, xsum))
         elif self.cap is not None:
             w.gemv_argmax(lay, pk, xq, xs, xsum, self.cap, out=(y[0], self.token, self.tval),
                           work=self.work)
@@ -450,8 +454,10 @@ class LayerBench:
 
     def kernel_name(self):
         kname = "gemv" if self.cfg.m == 1 else "gemm"  # the fused kernel lives in gemv.hip
-        return ("gemv_argmax (GEMV with the tail + key reduction)" if self.cap is not None else
-                f"{kname}_a16" if self.a16 else f"{kname}_w8" if self.byte_decoded else kname)
+        if self.cap is not None:
+            return ("lm_head_argmax (prepass fused into the GEMV with the tail + key reduction)"
+                    if self.fused else "gemv_argmax (GEMV with the tail + key reduction)")
+        return f"{kname}_a16" if self.a16 else f"{kname}_w8" if self.byte_decoded else kname
 
     def traffic(self):
         kname = "gemv" if self.cfg.m == 1 else "gemm"

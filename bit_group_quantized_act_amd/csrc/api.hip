@@ -446,11 +446,17 @@ w4a8_status lm_head_argmax_checked(const w4a8_layout *L, const void *packed, con
     W4A8_REQUIRE_PTR(logits);
     if ((s = check_device()) != W4A8_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const w4a8::Tail tail{softcap, static_cast<unsigned long long *>(work), token, value};
+    const uint8_t *pk = static_cast<const uint8_t *>(packed);
+    // within the fused GEMV's bounds the prepass runs inside the GEMV, as in w4a8_linear
+    if (L->k <= w4a8::kFusedMaxK &&
+        L->n_pad / W4A8_PANEL_ROWS <= w4a8::fused_max_panels(hadamard_block))
+        return launched(w4a8::launch_gemv_argmax_fused(geom_of(L), pk, x, hadamard_block, xq, xs,
+                                                       xsum, logits, tail, st),
+                        "fused greedy tail gemv launch");
     hipError_t e = w4a8::launch_prep(x, 1, L->k, L->group, hadamard_block, xq, xs, xsum, st);
     if (e != hipSuccess) return launched(e, "prep launch");
-    const w4a8::Tail tail{softcap, static_cast<unsigned long long *>(work), token, value};
-    return launched(w4a8::launch_gemv_argmax(geom_of(L), static_cast<const uint8_t *>(packed), xq,
-                                             xs, xsum, logits, tail, st),
+    return launched(w4a8::launch_gemv_argmax(geom_of(L), pk, xq, xs, xsum, logits, tail, st),
                     "greedy tail gemv launch");
 }
 

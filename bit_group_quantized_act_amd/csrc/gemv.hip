@@ -70,7 +70,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const uint8_t *__restrict_
                                                       float *__restrict__ y,
                                                       int *__restrict__ d, int act, Tail tail) {
     static_assert(!(GLU && PARTIALS), "the gated output has no partials variant");
-    static_assert(!(ARGMAX && (GLU || PARTIALS || FUSED)), "the greedy tail is a plain GEMV's");
+    static_assert(!(ARGMAX && (GLU || PARTIALS)), "the greedy tail has no gated or partials variant");
     constexpr int kChunksPerGroup = G / kChunkK;
     constexpr int kLanesPerGroup = G / 4;
     // Fused: activation quads (4 values) per lane that a wavefront quantizes, at most (the
@@ -296,70 +296,74 @@ hipError_t launch_k(const Geom &g, int act, const uint8_t *packed, const float *
     return hipGetLastError();
 }
 
-template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, bool GLU>
+template <int FMT, int G, int W, bool PARTIALS, bool FUSED, bool ROT, bool GLU, bool ARGMAX>
 hipError_t launch_wk(const Geom &g, int act, const uint8_t *packed, const float *x, int8_t *xq,
-                     float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
+                     float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream,
+                     const Tail &tail) {
     if (!FUSED)
-        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 1, GLU>(g, act, packed, x, xq, xs, xsum,
-                                                                 y, d, stream);
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 1, GLU, ARGMAX>(
+            g, act, packed, x, xq, xs, xsum, y, d, stream, tail);
     // the quads of the largest wavefront share (whole metadata blocks of 4 groups)
     const int nblk = (g.k / G + 3) / 4;
     const int max_quads = (nblk + W - 1) / W * 4 * (G / 4);
     if (max_quads <= 64)
-        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 1, GLU>(g, act, packed, x, xq, xs,
-                                                                  xsum, y, d, stream);
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 1, GLU, ARGMAX>(
+            g, act, packed, x, xq, xs, xsum, y, d, stream, tail);
     if (max_quads <= 128)
-        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 2, GLU>(g, act, packed, x, xq, xs,
-                                                                  xsum, y, d, stream);
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 2, GLU, ARGMAX>(
+            g, act, packed, x, xq, xs, xsum, y, d, stream, tail);
     if (max_quads <= 256)
-        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 4, GLU>(g, act, packed, x, xq, xs,
-                                                                  xsum, y, d, stream);
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, 4, GLU, ARGMAX>(
+            g, act, packed, x, xq, xs, xsum, y, d, stream, tail);
     if (max_quads <= 64 * kFusedQuadsPerLane)
-        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, kFusedQuadsPerLane, GLU>(
-            g, act, packed, x, xq, xs, xsum, y, d, stream);
+        return launch_k<FMT, G, W, PARTIALS, FUSED, ROT, kFusedQuadsPerLane, GLU, ARGMAX>(
+            g, act, packed, x, xq, xs, xsum, y, d, stream, tail);
     return hipErrorInvalidValue;
 }
 
-template <int FMT, int G, bool PARTIALS, bool FUSED, bool ROT, bool GLU>
+template <int FMT, int G, bool PARTIALS, bool FUSED, bool ROT, bool GLU, bool ARGMAX>
 hipError_t launch_w(const Geom &g, int act, const uint8_t *packed, const float *x, int8_t *xq,
-                    float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
+                    float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream,
+                    const Tail &tail) {
     // W = 8 once there are 6 metadata blocks (some wavefronts may own none), else 4.  The fused
     // kernel at exactly 6 blocks takes W = 6, one block per wavefront, so that every wavefront
     // quantizes and loads (the 262144-row head at K = 1536: 33.6 -> 33.0 us; the plain kernel
     // measured no faster with 6)
     if (FUSED && (g.k / G + 3) / 4 == 6)
-        return launch_wk<FMT, G, 6, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y,
-                                                              d, stream);
+        return launch_wk<FMT, G, 6, PARTIALS, FUSED, ROT, GLU, ARGMAX>(g, act, packed, x, xq, xs,
+                                                                      xsum, y, d, stream, tail);
     if ((g.k / G + 3) / 4 >= 6)
-        return launch_wk<FMT, G, 8, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y,
-                                                              d, stream);
-    return launch_wk<FMT, G, 4, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y, d,
-                                                          stream);
+        return launch_wk<FMT, G, 8, PARTIALS, FUSED, ROT, GLU, ARGMAX>(g, act, packed, x, xq, xs,
+                                                                      xsum, y, d, stream, tail);
+    return launch_wk<FMT, G, 4, PARTIALS, FUSED, ROT, GLU, ARGMAX>(g, act, packed, x, xq, xs,
+                                                                  xsum, y, d, stream, tail);
 }
 
-template <int FMT, bool PARTIALS, bool FUSED, bool ROT, bool GLU>
+template <int FMT, bool PARTIALS, bool FUSED, bool ROT, bool GLU, bool ARGMAX>
 hipError_t launch_g(const Geom &g, int act, const uint8_t *packed, const float *x, int8_t *xq,
-                    float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream) {
+                    float *xs, int32_t *xsum, float *y, int32_t *d, hipStream_t stream,
+                    const Tail &tail) {
     if (g.group == 64)
-        return launch_w<FMT, 64, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y, d,
-                                                           stream);
-    return launch_w<FMT, 128, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y, d,
-                                                        stream);
+        return launch_w<FMT, 64, PARTIALS, FUSED, ROT, GLU, ARGMAX>(g, act, packed, x, xq, xs,
+                                                                   xsum, y, d, stream, tail);
+    return launch_w<FMT, 128, PARTIALS, FUSED, ROT, GLU, ARGMAX>(g, act, packed, x, xq, xs, xsum,
+                                                                y, d, stream, tail);
 }
 
-template <bool PARTIALS, bool FUSED, bool ROT, bool GLU = false>
+template <bool PARTIALS, bool FUSED, bool ROT, bool GLU = false, bool ARGMAX = false>
 hipError_t launch_f(const Geom &g, const uint8_t *packed, const float *x, int8_t *xq, float *xs,
-                    int32_t *xsum, float *y, int32_t *d, hipStream_t stream, int act = 0) {
+                    int32_t *xsum, float *y, int32_t *d, hipStream_t stream, int act = 0,
+                    const Tail &tail = Tail{}) {
     switch (g.fmt) {
     case kFmtSym:
-        return launch_g<kFmtSym, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y, d,
-                                                           stream);
+        return launch_g<kFmtSym, PARTIALS, FUSED, ROT, GLU, ARGMAX>(g, act, packed, x, xq, xs,
+                                                                   xsum, y, d, stream, tail);
     case kFmtAffine:
-        return launch_g<kFmtAffine, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum, y,
-                                                              d, stream);
+        return launch_g<kFmtAffine, PARTIALS, FUSED, ROT, GLU, ARGMAX>(g, act, packed, x, xq, xs,
+                                                                      xsum, y, d, stream, tail);
     default:
-        return launch_g<kFmtCodebook, PARTIALS, FUSED, ROT, GLU>(g, act, packed, x, xq, xs, xsum,
-                                                                y, d, stream);
+        return launch_g<kFmtCodebook, PARTIALS, FUSED, ROT, GLU, ARGMAX>(g, act, packed, x, xq, xs,
+                                                                        xsum, y, d, stream, tail);
     }
 }
 
@@ -417,6 +421,18 @@ hipError_t launch_gemv_argmax(const Geom &g, const uint8_t *packed, const int8_t
         break;
     default: e = launch_argmax_g<kFmtCodebook>(g, packed, xq, xs, xsum, y, tail, stream); break;
     }
+    if (e != hipSuccess) return e;
+    return launch_argmax_keys(tail.keys, g.n_pad / kPanelRows, tail.token, tail.value, stream);
+}
+
+hipError_t launch_gemv_argmax_fused(const Geom &g, const uint8_t *packed, const float *x,
+                                    int hadamard, int8_t *xq, float *xs, int32_t *xsum, float *y,
+                                    const Tail &tail, hipStream_t stream) {
+    const hipError_t e =
+        hadamard ? launch_f<false, true, true, false, true>(g, packed, x, xq, xs, xsum, y, nullptr,
+                                                            stream, 0, tail)
+                 : launch_f<false, true, false, false, true>(g, packed, x, xq, xs, xsum, y,
+                                                             nullptr, stream, 0, tail);
     if (e != hipSuccess) return e;
     return launch_argmax_keys(tail.keys, g.n_pad / kPanelRows, tail.token, tail.value, stream);
 }

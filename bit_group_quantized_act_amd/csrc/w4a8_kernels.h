@@ -254,6 +254,11 @@ struct Tail {
 hipError_t launch_gemv_argmax(const Geom &g, const uint8_t *packed, const int8_t *xq,
                               const float *xs, const int32_t *xsum, float *y, const Tail &tail,
                               hipStream_t stream);
+// The same tail with the prepass fused into the GEMV (one row, within the fused GEMV's bounds):
+// x fp32 [k] in, xq / xs / xsum written by workgroup 0, as launch_gemv_fused.
+hipError_t launch_gemv_argmax_fused(const Geom &g, const uint8_t *packed, const float *x,
+                                    int hadamard, int8_t *xq, float *xs, int32_t *xsum, float *y,
+                                    const Tail &tail, hipStream_t stream);
 // The fp16-activation path: the prepass (x fp32 [m][k] -> interleaved halves xh [m][k] and the
 // fp32 group sums xsf [k/64][m]) and the linear on them (GEMV for m == 1, GEMM above), for the
 // symmetric and affine formats with 64-wide groups.

@@ -286,11 +286,13 @@ w4a8_status w4a8_gemm_glu(const w4a8_layout *L, const void *packed, int32_t m, c
  *   work, work_bytes  device scratch of at least W4A8_ARGMAX_WORK_BYTES(L->n) bytes, 8-byte
  *            aligned: one 64-bit key per 64-row panel (no initial contents are needed; calls
  *            that overlap on one work buffer race)
- * Three kernels on the stream: the prepass; the GEMV, which also caps and stores the logits and
- * stores each panel's largest (logit, smaller index) key to work; a one-workgroup kernel that
- * reduces the keys into token and value.  (Fusing the prepass into this GEMV, as w4a8_linear
- * does, measured slower on the 262144-row head: 39.4 against 38.7 us per call.)  A one-scale-per-row head (the orthogonal lm_head) is
- * packed with that scale repeated over its 128-wide groups (group = 128): the same formula.
+ * The kernels on the stream: the GEMV, which also caps and stores the logits and stores each
+ * panel's largest (logit, smaller index) key to work, with the prepass fused into it within the
+ * bounds where w4a8_linear fuses it (k <= 16384 and at most 4096 panels, 2048 with the rotation;
+ * workgroup 0 writes xq, xs and xsum) and a prepass kernel before it otherwise; then a
+ * one-workgroup kernel that reduces the keys into token and value.  The results are the same
+ * bits either way.  A one-scale-per-row head (the orthogonal lm_head) is packed with that scale
+ * repeated over its 128-wide groups (group = 128): the same formula.
  * W4A8_ERR_ARG: softcap negative or not finite, token / value / work NULL or misaligned,
  * work_bytes too small.
  * Source: "cactus-compute/engine PR #750: Metal Support", the commit list (the orthogonal lm_head
@@ -308,7 +310,7 @@ w4a8_status w4a8_lm_head_argmax(const w4a8_layout *L, const void *packed, const 
 /*
  * w4a8_lm_head_argmax for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same validation, the same
- * three kernels and the same results, with the panel keys in a buffer the library holds on each
+ * kernels and the same results, with the panel keys in a buffer the library holds on each
  * GPU it runs on (W4A8_ARGMAX_WORK_BYTES(W4A8_NOALLOC_MAX_N) = 128 KiB, kept until the process
  * ends) instead of a caller's work buffer.  Nothing is allocated or freed: the buffer is a static
  * device array whose address is looked up once per device, on the first call there.
@@ -327,7 +329,7 @@ w4a8_status w4a8_lm_head_argmax_noalloc(const w4a8_layout *L, const void *packed
 
 /*
  * The GEMV and greedy tail of w4a8_lm_head_argmax on activations already quantized by w4a8_prep
- * (m = 1): the same two kernels, so the same logits, token and value.
+ * (m = 1): the GEMV with the tail and the key reduction, with the same logits, token and value.
  * Errors as w4a8_gemv and w4a8_lm_head_argmax.
  * Source: as w4a8_lm_head_argmax.
  */
