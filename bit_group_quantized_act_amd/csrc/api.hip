@@ -100,9 +100,7 @@ w4a8_status launched(hipError_t e, const char *what) {
         if (!aligned((p), 16)) return fail(W4A8_ERR_ARG, #p " is not 16-byte aligned");        \
     } while (0)
 
-// Sizes the GEMM addresses with 32-bit offsets: the activation scales and sums of all rows
-// (m * k/group dwords) and the workgroup count.
-// Int8 and 2-bit codebook weights run through their own GEMV / GEMM.
+// Int8 and 1-, 2- and 3-bit codebook weights (byte-decoded) run through their own GEMV / GEMM.
 bool byte_decoded(const w4a8_layout *L) {
     return L->format >= W4A8_INT8 && L->format <= W4A8_CQ3;
 }
@@ -120,6 +118,9 @@ w4a8_status reject_int8(const w4a8_layout *L, const char *what) {
     return W4A8_OK;
 }
 
+// Sizes the GEMM addresses with 32-bit offsets: the activation scales and sums of all rows
+// (m * k/group dwords), the activation codes of the byte-decoded formats' GEMM, and the
+// workgroup count.
 w4a8_status check_gemm_size(const w4a8_layout *L, int32_t m) {
     // (the GEMM's copies run up to 16 groups past the last one)
     const int64_t scales = static_cast<int64_t>(m) * (L->k / L->group + 16) * 4;
