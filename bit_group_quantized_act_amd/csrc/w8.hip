@@ -504,13 +504,217 @@ struct W8Stage {
 // Three workgroups per CU (12 wavefronts) where the registers allow it: the int8 variant keeps
 // its 16-byte weight operands one stage ahead instead of two for that.  PARTIALS: each group's
 // int32 tile is stored to d[row][col][g] in place of the fp32 epilogue (xs and y are not used).
+// Split tiles (not PARTIALS): workgroups from nfull on each take one 32-channel group of a tile
+// of the last, partial round over the CUs; wavefront w runs k quarter w of it, one 32-wide block
+// per stage (a stage's LDS buffer holds the four quarters' blocks side by side, so wavefront w
+// reads the operand offsets of block w of a whole stage), and the four outputs are added in LDS
+// in quarter order.  k is a multiple of 128 and of 4 G.
+// The kernels with a split path: the codebook formats with 64-groups.  (In the int8 and the
+// 128-group kernels the extra path made the register allocation spill in the whole-tile loop.)
+template <int FMT, int G, bool PARTIALS>
+constexpr bool kW8Split = !PARTIALS && FMT != kFmtInt8 && G == 64;
+
+template <int FMT, int G>
+struct W8Split {
+    v4i a[2];                                         // two 16-byte activation units per thread
+    v4i w;                                            // int8: the lane's 16-byte chunk
+    v2i w2[2];                                        // CQ2: chunk / CQ3: crumb planes (8 bytes)
+    v2i bp;                                           // CQ1 / CQ3: the lane's 8 bytes of bits
+    uint32_t meta;                                    // the block's group: weight metadata
+    float xs;                                         // and the scale of the lane's row
+};
+
+
+// A split workgroup (see gemm_w8_kernel): 32 channels of one tile, wavefront w over k quarter w.
+template <int FMT, int G>
+__device__ __forceinline__ void split_tile(const uint8_t *__restrict__ packed, const Geom &geom,
+                                           int m, const int8_t *__restrict__ xq,
+                                           const float *__restrict__ xs, float *__restrict__ y,
+                                           int nfull, v4i (*lds)[64 * 8]) {
+    constexpr int BPG = G / 32;                       // 32-wide blocks per group
+    constexpr int P = planes<FMT>;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+    const int r32 = lane & 31;
+    const int mtiles = (m + 63) / 64;
+    const int part_id = static_cast<int>(blockIdx.x) - nfull;
+    const int tile = nfull + part_id / 4;
+    const int mt = tile % mtiles, nt = tile / mtiles;
+    const int m0 = mt * 64;
+    const int c0 = nt * kW8BN + (part_id % 4) * 32;   // the workgroup's 32 channels
+    if (c0 >= geom.n_pad) return;                     // (workgroup-uniform)
+    const int col = c0 + r32;
+    const int p = col / kPanelRows, prow = col % kPanelRows;
+    const int k = geom.k;
+    const int kc = bit_plane<FMT> ? (k + kBitChunk - 1) / kBitChunk
+                                  : k / ((FMT == kFmtCQ2) ? 64 : kW8Chunk);
+    const int ng = k / G;
+    const int nblk = (ng + 3) / 4;
+    const int qk = k / 4;                             // k per quarter
+    const int nst = qk / 32;                          // stages: one 32-wide block per wavefront
+    const int gb0 = wave * nst;                       // the wavefront's first block in all of k
+    uint32_t cb = 0u, cb1 = 0u;
+    if (FMT == kFmtCQ2 || FMT == kFmtCQ1)
+        cb = reinterpret_cast<const uint32_t *>(packed + geom.off_codebook)[col];
+    if (FMT == kFmtCQ3) {
+        const uint2 v = reinterpret_cast<const uint2 *>(packed + geom.off_codebook)[col];
+        cb = v.x;
+        cb1 = v.y;
+    }
+    const rsrc_t rc = make_rsrc(packed + geom.off_codes + (uint64_t)p * kc * P * 1024,
+                                (uint64_t)kc * P * 1024);
+    const rsrc_t rm = make_rsrc(packed + geom.off_meta + (uint64_t)p * nblk * 512,
+                                (uint64_t)nblk * 512);
+    const rsrc_t rx = make_rsrc(xq, (uint64_t)m * k);
+    const rsrc_t rs = make_rsrc(xs, (uint64_t)ng * m * 4);
+
+    // Stage s: activation unit u of a row holds quarter u / 2, k 32 s + 16 (u % 2) of it; the
+    // wavefront's weights, metadata and row scale are those of its block gb0 + s.
+    auto load_stage = [&](int s, W8Split<FMT, G> &r) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int rr = i * 32 + (tid >> 3), u = tid & 7;
+            const int kk = (u >> 1) * qk + 32 * s + 16 * (u & 1);
+            const bool ok = (m0 + rr < m) && s < nst;
+            r.a[i] = ld128(rx, ok ? (m0 + rr) * k + kk : kOOB);
+        }
+        const int gb = gb0 + s;
+        const bool okb = s < nst;
+        if (FMT == kFmtInt8) {
+            r.w = ld128(rc, okb ? ((2 * gb + half) * 64 + prow) * 16 : kOOB);
+        } else if (FMT == kFmtCQ2) {
+            r.w2[0] = ld64(rc, okb ? ((gb >> 1) * 64 + prow) * 16 + 8 * half : kOOB);
+        } else {
+            const int c = gb >> 2;
+            if (FMT == kFmtCQ3)
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    r.w2[u] = ld64(rc, okb ? ((c * P + u) * 64 + prow) * 16 + 8 * half : kOOB);
+            r.bp = ld64(rc, okb ? ((c * P + P - 1) * 64 + prow) * 16 + 8 * half : kOOB);
+        }
+        const int g = (gb * 32) / G;
+        r.meta = ld16(rm, okb ? (((g >> 2) * 64 + prow) * 4 + (g & 3)) * 2 : kOOB);
+        const int row = m0 + 32 * half + r32;
+        r.xs = __builtin_bit_cast(float, ld32(rs, (okb && row < m) ? (g * m + row) * 4 : kOOB));
+    };
+    auto store_a = [&](int buf, const W8Split<FMT, G> &r) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int rr = i * 32 + (tid >> 3), u = tid & 7;
+            lds[buf][rr * 8 + (u ^ (rr & 7))] = r.a[i];
+        }
+    };
+
+    v16f acc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+    v32f zero32;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) zero32[e] = 0.0f;
+    const v16i izero = {};
+    v16i part[2] = {};
+    W8Split<FMT, G> ring[2];
+    load_stage(0, ring[0]);
+    if (nst > 1) load_stage(1, ring[1]);
+    store_a(0, ring[0]);
+    __syncthreads();
+
+    auto stage = [&](auto slot_c, int s) {
+        constexpr int slot = decltype(slot_c)::value;
+        const int gb = gb0 + s;
+        // nst is a multiple of BPG (k a multiple of 4 G), so the block's place in its group is
+        // that of s, and s is even in slot 0 and odd in slot 1
+        const bool first = (BPG == 2) ? slot == 0 : s % BPG == 0;
+        const bool last = (BPG == 2) ? slot == 1 : s % BPG == BPG - 1;
+        v4i b;
+        if (FMT == kFmtCQ2) {
+            const uint32_t w = static_cast<uint32_t>(ring[slot].w2[0][slot]);   // word gb % 2
+            b = v4i{cq2_dword(w, 0, cb), cq2_dword(w, 1, cb), cq2_dword(w, 2, cb),
+                    cq2_dword(w, 3, cb)};
+        } else if (bit_plane<FMT>) {
+            // block j = 2q + pb of its chunk (selects, not a runtime index into the registers)
+            const int j = gb & 3;
+            const v2i bpv = ring[slot].bp;
+            const uint32_t bw = static_cast<uint32_t>((j >> 1) ? bpv[1] : bpv[0]);
+            uint32_t cw = 0u;
+            if (FMT == kFmtCQ3) {
+                const v2i c0v = ring[slot].w2[0], c1v = ring[slot].w2[1];
+                const v2i cv = (j >> 1) ? c1v : c0v;
+                cw = static_cast<uint32_t>((j & 1) ? cv[1] : cv[0]);
+            }
+            const int sh = 4 * (j & 1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (FMT == kFmtCQ3)
+                    b[e] = cq3_dword(cw, e, bw, sh + e, cb, cb1);
+                else
+                    b[e] = cq1_dword(bw, sh + e, cb);
+            }
+        } else {
+            b = ring[slot].w;
+        }
+        const uint32_t meta = ring[slot].meta;
+        const float xsv = ring[slot].xs;
+        if (s + 2 < nst) load_stage(s + 2, ring[slot]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int rr = 32 * t + r32;
+            const v4i aop = lds[slot][rr * 8 + ((2 * wave + half) ^ (rr & 7))];
+            part[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, b, first ? izero : part[t],
+                                                            0, 0, 0);
+        }
+        if (last) {                                   // the group's last block: rescale
+            const float sw = half_bits_to_float(meta & 0xFFFFu);
+            const v32f coef = __builtin_amdgcn_mfma_f32_32x32x1f32(xsv, sw, zero32, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[t][e] = fmaf(coef[16 * t + e], static_cast<float>(part[t][e]), acc[t][e]);
+        }
+        if (s + 1 < nst) store_a(slot ^ 1, ring[slot ^ 1]);
+        __syncthreads();
+    };
+    for (int s = 0; s < nst; s += 2) {
+        stage(std::integral_constant<int, 0>{}, s);
+        if (s + 1 < nst) stage(std::integral_constant<int, 1>{}, s + 1);
+    }
+
+    // the quarters' outputs meet in LDS, one tile at a time: wavefronts 1-3 store theirs and
+    // wavefront 0 adds them to its own in quarter order
+    float *xch = reinterpret_cast<float *>(&lds[0][0]);   // [3][16][64] fp32, 12 KiB
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (wave > 0) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) xch[((wave - 1) * 16 + e) * 64 + lane] = acc[t][e];
+        }
+        __syncthreads();
+        if (wave == 0 && col < geom.n) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + 32 * t + 8 * (e / 4) + 4 * half + (e % 4);
+                float v = acc[t][e];
+#pragma unroll
+                for (int w = 0; w < 3; ++w) v += xch[(w * 16 + e) * 64 + lane];
+                if (row < m) y[(int64_t)row * geom.n + col] = v;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 template <int FMT, int G, bool PARTIALS = false>
 __global__ __launch_bounds__(256, 3) void gemm_w8_kernel(const uint8_t *__restrict__ packed,
                                                          const Geom geom, int m,
                                                          const int8_t *__restrict__ xq,
                                                          const float *__restrict__ xs,
                                                          float *__restrict__ y,
-                                                         int *__restrict__ d = nullptr) {
+                                                         int *__restrict__ d, int nfull) {
     constexpr int GPS = kW8SK / G;
     constexpr int BPG = G / 32;                       // MFMA blocks per group
     __shared__ __attribute__((aligned(16))) v4i lds[2][64 * 8];   // [buf][row][16-byte unit]
@@ -521,9 +725,14 @@ __global__ __launch_bounds__(256, 3) void gemm_w8_kernel(const uint8_t *__restri
     const int r32 = lane & 31;
 
     const int mtiles = (m + 63) / 64;
+    if constexpr (kW8Split<FMT, G, PARTIALS>) {
+        if (static_cast<int>(blockIdx.x) >= nfull) {    // (workgroup-uniform)
+            split_tile<FMT, G>(packed, geom, m, xq, xs, y, nfull, lds);
+            return;
+        }
+    }
     int bid = blockIdx.x;
-    const int nb = gridDim.x;
-    if (nb % 8 == 0) bid = (bid % 8) * (nb / 8) + bid / 8;   // consecutive tiles on one XCD
+    if (nfull % 8 == 0) bid = (bid % 8) * (nfull / 8) + bid / 8;   // consecutive tiles on one XCD
     const int mt = bid % mtiles, nt = bid / mtiles;
     const int m0 = mt * 64;
     const int c0 = nt * kW8BN + wave * 32;
@@ -789,8 +998,9 @@ void partials_go(const Geom &g, const uint8_t *packed, int m, const int8_t *xq,
                 packed, g, x4, nullptr, nullptr, wpp, FusedIO{}, d);
         return;
     }
-    const unsigned grid = static_cast<unsigned>(((m + 63) / 64) * ((g.n_pad + kW8BN - 1) / kW8BN));
-    gemm_w8_kernel<FMT, G, true><<<grid, 256, 0, stream>>>(packed, g, m, xq, nullptr, nullptr, d);
+    const int tiles = ((m + 63) / 64) * ((g.n_pad + kW8BN - 1) / kW8BN);
+    gemm_w8_kernel<FMT, G, true><<<static_cast<unsigned>(tiles), 256, 0, stream>>>(
+        packed, g, m, xq, nullptr, nullptr, d, tiles);
 }
 
 template <int FMT>
@@ -808,9 +1018,17 @@ hipError_t launch_w8_fmt(const Geom &g, const uint8_t *packed, int m, const int8
                                     FusedIO{}, stream);
         return hipGetLastError();
     }
-    const unsigned grid = static_cast<unsigned>(((m + 63) / 64) * ((g.n_pad + kW8BN - 1) / kW8BN));
-    if (g.group == 64) gemm_w8_kernel<FMT, 64><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y);
-    else gemm_w8_kernel<FMT, 128><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y);
+    // the tiles of a last, partial round over the CUs split in four (k a multiple of 128 and of
+    // 4 G: whole 32-wide blocks and whole groups per quarter)
+    const int tiles = ((m + 63) / 64) * ((g.n_pad + kW8BN - 1) / kW8BN);
+    const bool can_split = (g.group == 64) ? kW8Split<FMT, 64, false> : kW8Split<FMT, 128, false>;
+    const int nfull = (can_split && g.k % 128 == 0 && g.k % (4 * g.group) == 0)
+                          ? whole_tiles(tiles) : tiles;
+    const unsigned grid = static_cast<unsigned>(nfull + 4 * (tiles - nfull));
+    if (g.group == 64)
+        gemm_w8_kernel<FMT, 64><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y, nullptr, nfull);
+    else
+        gemm_w8_kernel<FMT, 128><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y, nullptr, nfull);
     return hipGetLastError();
 }
 }  // namespace

@@ -52,6 +52,11 @@ CASES = [
     ("C4", dict(m=130, n=384, k=1536)),
     ("C5b", dict(m=64, n=1024, k=1536)),
     ("C1", dict(m=3, n=64, k=64)),
+    # more tiles than CUs: with the 64-group codebook formats the tiles of the last, partial
+    # round run split over four workgroups (one k quarter per wavefront): 272 tiles (16 split,
+    # four stages per quarter) and 516 (4 split, two stages per quarter, a 2-row last row block)
+    ("C3a", dict(m=64, n=34816, k=512)),
+    ("C3a", dict(m=130, n=22016, k=256)),
 ]
 
 
