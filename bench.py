@@ -16,9 +16,12 @@ Timing.  Weights are replicated into a pool of distinct packed buffers totalling
 the 256 MiB last-level cache) and the steps walk through the pool, so every step streams its
 weights from HBM, as a decode does across layers.  The K timed steps are captured once into a HIP
 graph (launch gaps of a Python loop would otherwise dominate microsecond kernels) and replayed
-between stream synchronizations; W warmup steps run first.  The dominant kernel's average
-duration is timed the same way from a graph of launches of that kernel alone over the same pool
-(at one row the fused kernel is the whole step), bracketed by HIP events on the capturing stream.
+between stream synchronizations; W warmup steps run first (by default 1000, a few tens of
+milliseconds, so that the GPU's clocks have settled: after 20 the timed graph's replay ran 4%
+slow on the decode head, the first replays of a run ramping from 35 to 33 us per step).  The
+dominant kernel's average duration is timed the same way from a graph of launches of that kernel
+alone over the same pool (at one row the fused kernel is the whole step), bracketed by HIP events
+on the capturing stream.
 
 value      = weight bytes (nibbles + scales [+ bias] [+ codebook]) per step / step time (GB/s)
 roofline   = algorithmic bytes of one launch of the dominant kernel (weights + xq + xs + xsum + y,
@@ -142,7 +145,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", default="C5a",
                     help="workload (C1, C2a, C2b, C3a, C3b, C4, C5a, C5b, C5o); default C5a")
     ap.add_argument("--secondary", default="C3a",
