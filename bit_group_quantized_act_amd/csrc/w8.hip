@@ -708,7 +708,9 @@ __device__ __forceinline__ void split_tile(const uint8_t *__restrict__ packed, c
     }
 }
 
-template <int FMT, int G, bool PARTIALS = false>
+// SPLIT: the variant with the split path, launched only when there are split tiles (its mere
+// presence slowed the whole-tile loop of some formats, 3-bit codebook 5% on the 64-row head).
+template <int FMT, int G, bool PARTIALS = false, bool SPLIT = false>
 __global__ __launch_bounds__(256, 3) void gemm_w8_kernel(const uint8_t *__restrict__ packed,
                                                          const Geom geom, int m,
                                                          const int8_t *__restrict__ xq,
@@ -725,7 +727,7 @@ __global__ __launch_bounds__(256, 3) void gemm_w8_kernel(const uint8_t *__restri
     const int r32 = lane & 31;
 
     const int mtiles = (m + 63) / 64;
-    if constexpr (kW8Split<FMT, G, PARTIALS>) {
+    if constexpr (SPLIT && kW8Split<FMT, G, PARTIALS>) {
         if (static_cast<int>(blockIdx.x) >= nfull) {    // (workgroup-uniform)
             split_tile<FMT, G>(packed, geom, m, xq, xs, y, nfull, lds);
             return;
@@ -1025,10 +1027,13 @@ hipError_t launch_w8_fmt(const Geom &g, const uint8_t *packed, int m, const int8
     const int nfull = (can_split && g.k % 128 == 0 && g.k % (4 * g.group) == 0)
                           ? whole_tiles(tiles) : tiles;
     const unsigned grid = static_cast<unsigned>(nfull + 4 * (tiles - nfull));
-    if (g.group == 64)
-        gemm_w8_kernel<FMT, 64><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y, nullptr, nfull);
-    else
+    if (g.group == 128)
         gemm_w8_kernel<FMT, 128><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y, nullptr, nfull);
+    else if (nfull < tiles)
+        gemm_w8_kernel<FMT, 64, false, kW8Split<FMT, 64, false>><<<grid, 256, 0, stream>>>(
+            packed, g, m, xq, xs, y, nullptr, nfull);
+    else
+        gemm_w8_kernel<FMT, 64><<<grid, 256, 0, stream>>>(packed, g, m, xq, xs, y, nullptr, nfull);
     return hipGetLastError();
 }
 }  // namespace
