@@ -94,10 +94,10 @@ KERNEL_SOURCES = {
     "gemm": ["gemm.hip", "w4a8_kernels.h"],
 }
 TRAFFIC = {
-    "C5a": dict(kernel="gemv", source_sha="5a1b3107f34bd42d", fetch_kib=104509.42,
-                write_kib=1025.6875, fetch_factor=1.99979, write_factor=1.0),
-    "C3a": dict(kernel="gemm", source_sha="a545c755d06222ad", fetch_kib=53282.87,
-                write_kib=17408.0000, fetch_factor=1.99979, write_factor=1.0),
+    "C5a": dict(kernel="gemv", source_sha="9e7fcf52161c7224", fetch_kib=104509.38,
+                write_kib=1025.6885, fetch_factor=1.99980, write_factor=1.0),
+    "C3a": dict(kernel="gemm", source_sha="38de9063a4a389a3", fetch_kib=53272.42,
+                write_kib=17408.0000, fetch_factor=1.99980, write_factor=1.0),
 }
 
 
