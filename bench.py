@@ -590,8 +590,9 @@ def cpu_baseline(lb, seconds):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (column-parallel "
-              "sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the layer would "
+              "shard by output columns, one slice of the packed panels per GPU); run with "
+              "--gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
