@@ -93,6 +93,10 @@ CASES = [
     ("C5b", dict(m=3, n=65536, k=256), False),
     ("C3a", dict(m=130, n=22016, k=256), True),
     ("C4", dict(m=2, n=65600, k=512), False),
+    # the largest k the ABI takes (2^20): one tile split over four workgroups, 1024 stages per
+    # k quarter; and 2^19 with 128-groups over several whole tiles
+    ("C1", dict(m=2, n=64, k=1 << 20), True),
+    ("C3a", dict(m=5, n=200, k=1 << 19, group=128), True),
 ]
 
 
@@ -158,6 +162,7 @@ LINEAR_CASES = [
     ("C4", dict(m=1, n=131073, k=128), False),     # one row past it: prepass + GEMV
     ("C3a", dict(m=65, n=1000, k=1280), True),
     ("C4", dict(m=200, n=448, k=1536), False),
+    ("C1", dict(n=64, k=1 << 20), True),          # the largest k: prepass + GEMV, 4096 blocks
 ]
 
 

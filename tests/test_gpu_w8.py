@@ -57,6 +57,7 @@ CASES = [
     # four stages per quarter) and 516 (4 split, two stages per quarter, a 2-row last row block)
     ("C3a", dict(m=64, n=34816, k=512)),
     ("C3a", dict(m=130, n=22016, k=256)),
+    ("C1", dict(m=2, n=64, k=1 << 20)),     # the largest k: one tile (split for the codebooks)
 ]
 
 
