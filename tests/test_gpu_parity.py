@@ -97,6 +97,8 @@ CASES = [
     # k quarter; and 2^19 with 128-groups over several whole tiles
     ("C1", dict(m=2, n=64, k=1 << 20), True),
     ("C3a", dict(m=5, n=200, k=1 << 19, group=128), True),
+    # many rows: 128 row blocks of one channel tile, all split (512 workgroups)
+    ("C3a", dict(m=8192, n=64, k=256), True),
 ]
 
 
