@@ -78,6 +78,10 @@ CASES = [
     ("C3a", dict(m=3, n=64, k=64)),
     # more tiles than CUs: whole tiles and split tiles (one k quarter per wavefront) in one launch
     ("C3a", dict(m=64, n=34816, k=512)),
+    # the largest k (2^20): one row past the fused bound (prepass + GEMV), and a one-tile GEMM
+    # split over four workgroups
+    ("C1", dict(n=64, k=1 << 20)),
+    ("C3a", dict(m=2, n=64, k=1 << 20)),
 ]
 
 
