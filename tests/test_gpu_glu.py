@@ -85,6 +85,7 @@ GLU_CASES = [
     ("C1", dict(m=3, n=128, k=1024, group=128), S),
     # more tiles than CUs: whole gated tiles and split ones (gate and up halves of k) in one launch
     ("C3a", dict(m=64, n=34816, k=512), GE),
+    ("C3a", dict(m=2, n=128, k=1 << 20), S),      # the largest k: one gated tile, split in two
 ]
 
 
