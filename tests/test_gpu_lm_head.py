@@ -116,6 +116,7 @@ CASES = [
     ("C3a", dict(m=1, n=1280, k=640), 15.0),
     ("C1", dict(n=300, k=256), 50.0),
     ("C1", dict(n=640, k=1024, group=128), 0.0),
+    ("C1", dict(n=200, k=1 << 20), 30.0),        # the largest k: past the fused bound
 ]
 
 
